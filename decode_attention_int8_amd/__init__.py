@@ -1,0 +1,224 @@
+"""decode_attention_int8_amd -- q8-KV single-query decode attention on MI355X.
+
+A thin ctypes binding over ``libq8kv.so`` (C ABI declared in
+``include/q8kv.h``).  This module only marshals arguments: it checks tensor
+dtypes, devices and contiguity, reads shapes, and passes raw device pointers
+and the current HIP stream to the library.  Every step of the computation runs
+in the library's HIP kernels; there is no fallback of any kind -- if the
+library is not built, importing this package raises.
+
+PyTorch supplies device memory and streams only.
+"""
+import ctypes
+import os
+import re
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libq8kv.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "q8kv.h")
+
+Q8KV_OK, Q8KV_EINVAL, Q8KV_ENULL, Q8KV_EHIP, Q8KV_ENOMEM = 0, -1, -2, -3, -4
+
+
+class Q8KVError(RuntimeError):
+    def __init__(self, code, message):
+        super().__init__(f"q8kv error {code}: {message}")
+        self.code = code
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; build it with `python -m decode_attention_int8_amd.build` "
+            "or __graft_entry__.build()")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    sig = {
+        "q8kv_decode_attn": [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, P],
+        "q8kv_decode_attn_split": [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, P],
+        "q8kv_plan": [I, I, I, I, I, I, P, P],
+        "q8kv_append": [P, P, P, P, P, P, I, P, I, I, I, I, I, P],
+        "q8kv_release": [],
+        "q8kv_debug_quantize_q": [P, P, P, I, I, P],
+        "q8kv_debug_block_dots": [P, I, P, P, P, P, I, I, I, I, I, I, I, P],
+    }
+    for name, args in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = I
+    lib.q8kv_last_error.argtypes = []
+    lib.q8kv_last_error.restype = ctypes.c_char_p
+    return lib
+
+
+lib = _load()
+
+
+def header_symbols():
+    """Names of the functions include/q8kv.h declares."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\w[\w\s\*]*?\b(q8kv_\w+)\s*\(", text, re.M)))
+
+
+def last_error():
+    return lib.q8kv_last_error().decode()
+
+
+def _check(rc):
+    if rc != Q8KV_OK:
+        raise Q8KVError(rc, last_error())
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t, name, dtype, device, ndim):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+class PagedKVCache:
+    """Device page pool of one layer's q8 KV cache.
+
+    k_pages, v_pages int8 [num_blocks][n_kv][kv_bs][hd];
+    k_scale, v_scale fp32 [num_blocks][n_kv][kv_bs].
+    """
+
+    def __init__(self, num_blocks, n_kv, kv_bs, hd, device="cuda"):
+        dev = torch.device(device)
+        self.num_blocks, self.n_kv, self.kv_bs, self.hd = num_blocks, n_kv, kv_bs, hd
+        self.k_pages = torch.empty((num_blocks, n_kv, kv_bs, hd), dtype=torch.int8, device=dev)
+        self.v_pages = torch.empty_like(self.k_pages)
+        self.k_scale = torch.empty((num_blocks, n_kv, kv_bs), dtype=torch.float32, device=dev)
+        self.v_scale = torch.empty_like(self.k_scale)
+
+    @classmethod
+    def wrap(cls, k_pages, v_pages, k_scale, v_scale):
+        self = cls.__new__(cls)
+        self.k_pages, self.v_pages, self.k_scale, self.v_scale = k_pages, v_pages, k_scale, v_scale
+        self.num_blocks, self.n_kv, self.kv_bs, self.hd = k_pages.shape
+        return self
+
+    @property
+    def device(self):
+        return self.k_pages.device
+
+    def validate(self):
+        d = self.device
+        shp = (self.num_blocks, self.n_kv, self.kv_bs, self.hd)
+        for name in ("k_pages", "v_pages"):
+            t = getattr(self, name)
+            _need(t, name, torch.int8, d, 4)
+            if tuple(t.shape) != shp:
+                raise ValueError(f"{name} shape {tuple(t.shape)} != {shp}")
+        for name in ("k_scale", "v_scale"):
+            t = getattr(self, name)
+            _need(t, name, torch.float32, d, 3)
+            if tuple(t.shape) != shp[:3]:
+                raise ValueError(f"{name} shape {tuple(t.shape)} != {shp[:3]}")
+
+    def append(self, k_src, v_src, slot_mapping):
+        """Quantise k_src/v_src [n_tokens][n_kv][hd] (fp32 or bf16) into slots."""
+        self.validate()
+        d = self.device
+        if k_src.dtype not in (torch.float32, torch.bfloat16):
+            raise TypeError("k_src must be float32 or bfloat16")
+        _need(k_src, "k_src", k_src.dtype, d, 3)
+        _need(v_src, "v_src", k_src.dtype, d, 3)
+        _need(slot_mapping, "slot_mapping", torch.int32, d, 1)
+        n = slot_mapping.shape[0]
+        if tuple(k_src.shape) != (n, self.n_kv, self.hd) or v_src.shape != k_src.shape:
+            raise ValueError("k_src/v_src must be [n_tokens][n_kv][hd] matching slot_mapping")
+        with torch.cuda.device(d):
+            _check(lib.q8kv_append(_ptr(self.k_pages), _ptr(self.v_pages), _ptr(self.k_scale),
+                                   _ptr(self.v_scale), _ptr(k_src), _ptr(v_src),
+                                   1 if k_src.dtype == torch.bfloat16 else 0, _ptr(slot_mapping),
+                                   n, self.num_blocks, self.n_kv, self.hd, self.kv_bs, _stream(d)))
+
+
+def decode_attn(q, cache, block_table, seq_lens, scale, out=None, part_tokens=0):
+    """out[b][h] = softmax(q8 scores) @ q8 V for every sequence b and head h.
+
+    q fp32 [batch][n_q][hd]; block_table int32 [batch][max_blocks];
+    seq_lens int32 [batch]; all on the cache's device.  part_tokens 0 picks the
+    automatic split plan.  Returns out (fp32 [batch][n_q][hd]).
+    """
+    cache.validate()
+    d = cache.device
+    _need(q, "q", torch.float32, d, 3)
+    _need(block_table, "block_table", torch.int32, d, 2)
+    _need(seq_lens, "seq_lens", torch.int32, d, 1)
+    batch, n_q, hd = q.shape
+    if hd != cache.hd or block_table.shape[0] != batch or seq_lens.shape[0] != batch:
+        raise ValueError("q / block_table / seq_lens / cache shapes disagree")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need(out, "out", torch.float32, d, 3)
+        if out.shape != q.shape:
+            raise ValueError("out must have q's shape")
+    with torch.cuda.device(d):
+        _check(lib.q8kv_decode_attn_split(
+            _ptr(out), _ptr(q), _ptr(cache.k_pages), _ptr(cache.v_pages), _ptr(cache.k_scale),
+            _ptr(cache.v_scale), _ptr(block_table), _ptr(seq_lens), block_table.shape[1],
+            cache.num_blocks, batch, n_q, cache.n_kv, hd, cache.kv_bs, float(scale),
+            int(part_tokens), _stream(d)))
+    return out
+
+
+def plan(batch, n_q, n_kv, hd, kv_bs, max_blocks):
+    """(tokens per partition, partitions of the longest sequence) of the
+    automatic split plan."""
+    pt, npart = ctypes.c_int(), ctypes.c_int()
+    _check(lib.q8kv_plan(batch, n_q, n_kv, hd, kv_bs, max_blocks, ctypes.byref(pt), ctypes.byref(npart)))
+    return pt.value, npart.value
+
+
+def release():
+    _check(lib.q8kv_release())
+
+
+def debug_quantize_q(q):
+    """Test export: the decode prologue's int8 query and per-32-block scales."""
+    if q.dtype != torch.float32 or not q.is_cuda or not q.is_contiguous():
+        raise ValueError("q must be a contiguous float32 device tensor")
+    hd = q.shape[-1]
+    rows = q.numel() // hd
+    qi = torch.empty(q.shape, dtype=torch.int8, device=q.device)
+    qsc = torch.empty(q.shape[:-1] + (hd // 32,), dtype=torch.float32, device=q.device)
+    with torch.cuda.device(q.device):
+        _check(lib.q8kv_debug_quantize_q(_ptr(qi), _ptr(qsc), _ptr(q), rows, hd, _stream(q.device)))
+    return qi, qsc
+
+
+def debug_block_dots(q, cache, block_table, seq_lens, max_tok):
+    """Test export: int32 dots [batch][n_q][max_tok][hd/32] from the decode
+    kernel's matrix-core scoring step (entries past seq_len stay zero)."""
+    cache.validate()
+    d = cache.device
+    _need(q, "q", torch.float32, d, 3)
+    _need(block_table, "block_table", torch.int32, d, 2)
+    _need(seq_lens, "seq_lens", torch.int32, d, 1)
+    batch, n_q, hd = q.shape
+    dots = torch.zeros((batch, n_q, max_tok, hd // 32), dtype=torch.int32, device=d)
+    with torch.cuda.device(d):
+        _check(lib.q8kv_debug_block_dots(
+            _ptr(dots), max_tok, _ptr(q), _ptr(cache.k_pages), _ptr(block_table), _ptr(seq_lens),
+            block_table.shape[1], cache.num_blocks, batch, n_q, cache.n_kv, hd, cache.kv_bs,
+            _stream(d)))
+    return dots

@@ -1,0 +1,854 @@
+// q8kv: single-query decode attention over a paged int8 KV cache on gfx950.
+//
+// The method is the one walked through on the page "Day 9-2:
+// flash_attn_single_q_q8_neon" (trdm.cn), section 2 (segments 1-3): quantise
+// the query once per 32-block, score every cached token with int8 dot
+// products into int32 per block, rescale in fp32, keep a running max/exp-sum
+// that rescales the int8-V accumulator whenever the max grows, divide once at
+// the end.  Here it is laid out for CDNA4 matrix cores:
+//
+//   * one workgroup (4 waves) owns (sequence b, kv head kh, token partition);
+//     the G = n_q / n_kv query heads of kh share every K/V byte it loads;
+//   * a wave walks tiles of 32 tokens.  Q.K^T runs on v_mfma_i32_16x16x64_i8
+//     with A = 16 K rows x 64 bytes (two 32-blocks) and B = the quantised
+//     queries: columns 0-7 carry head g's even block with zeros under the odd
+//     block's k-slots, columns 8-15 the odd block with zeros under the even
+//     one, so every int32 result is one head's dot over exactly one 32-block
+//     (the per-block scales differ, so blocks must never share a sum);
+//   * the per-block scales are applied in fp32 and the two block parities are
+//     added with one DPP row rotation;
+//   * the tile max is reduced across the wave with permlane16/32 swaps; the
+//     accumulator is rescaled once per tile (the page's rule applied to the
+//     tile's maximum);
+//   * P.V runs on v_mfma_f32_16x16x32_f16: rows 0-7 are the heads' weights
+//     w * v_scale rounded to f16 ("hi"), rows 8-15 the f16 remainder
+//     (w * v_scale - hi), so the fp32-faithful weight is carried by two f16
+//     rows in one instruction; the int8 V bytes are exact in f16;
+//   * ranges longer than one partition are merged by a log-sum-exp combine
+//     kernel in partition order (deterministic).
+// Scores are kept in the log2 domain (softmax scale pre-multiplied by log2 e)
+// so every exponential is one v_exp_f32.
+
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <utility>
+
+#include "q8kv.h"
+
+namespace {
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kQBlock = 32;       // query quantisation block (elements)
+constexpr int kHeadGroup = 8;     // query heads handled by one MFMA column set
+constexpr int kTile = 32;         // tokens per wave tile
+constexpr int kSub = 16;          // tokens per Q.K MFMA
+constexpr int kWaves = 4;         // waves per decode workgroup
+constexpr int kThreads = kWave * kWaves;
+constexpr float kInv127 = 1.0f / 127.0f;
+constexpr float kLog2e = 1.44269504088896340736f;
+
+static_assert(__builtin_bit_cast(uint32_t, kInv127) == 0x3C010204u, "1/127 must round to 0x3C010204");
+
+template <int HD>
+struct Geo {
+    static constexpr int NB = HD / kQBlock;  // 32-blocks per row
+    static constexpr int NPAIR = HD / 64;    // Q.K MFMAs per 16-token sub-tile
+    static constexpr int BPL = HD / 16;      // V bytes per lane per token (= P.V MFMAs)
+    static constexpr int DPT = BPL / 4;      // V dwords per lane per token
+};
+
+// ----------------------------------------------------------------------------
+// quantiser (query blocks and K/V rows share it)
+
+__device__ __forceinline__ float q8_guard(float a) { return a < 1e-6f ? 1.0f : a; }
+
+// clamp(x * inv, -128, 127) then truncate toward zero (v_cvt_i32_f32).
+__device__ __forceinline__ int q8_code(float x, float inv) {
+    float y = x * inv;
+    y = fminf(fmaxf(y, -128.0f), 127.0f);
+    return (int)y;
+}
+
+__device__ __forceinline__ uint32_t q8_pack4(f32x4 x, float inv) {
+    return (uint32_t)(q8_code(x.x, inv) & 0xff) | ((uint32_t)(q8_code(x.y, inv) & 0xff) << 8) |
+           ((uint32_t)(q8_code(x.z, inv) & 0xff) << 16) | ((uint32_t)(q8_code(x.w, inv) & 0xff) << 24);
+}
+
+// Quantise up to kHeadGroup query rows (G of them; the rest are zero) into
+// LDS: lq [kHeadGroup][HD] int8, lqsc [kHeadGroup][HD/32] fp32.  Eight
+// consecutive threads own one 32-block (4 floats each).
+template <int HD>
+__device__ __forceinline__ void quantize_q_rows(const float* __restrict__ q, int G, int8_t* lq,
+                                                float* lqsc, int tid, int nthreads) {
+    constexpr int kChunks = kHeadGroup * HD / 4;
+    for (int c = tid; c < kChunks; c += nthreads) {
+        const int g = c / (HD / 4);
+        const int e = (c % (HD / 4)) * 4;
+        f32x4 x = {0.f, 0.f, 0.f, 0.f};
+        if (g < G) x = *reinterpret_cast<const f32x4*>(q + (size_t)g * HD + e);
+        float a = fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w)));
+        a = fmaxf(a, __shfl_xor(a, 1));
+        a = fmaxf(a, __shfl_xor(a, 2));
+        a = fmaxf(a, __shfl_xor(a, 4));
+        a = q8_guard(a);
+        const float inv = 127.0f / a;
+        *reinterpret_cast<uint32_t*>(lq + g * HD + e) = q8_pack4(x, inv);
+        if ((c & 7) == 0) lqsc[g * (HD / kQBlock) + e / kQBlock] = a * kInv127;
+    }
+}
+
+// ----------------------------------------------------------------------------
+// wave-level helpers
+
+__device__ __forceinline__ float dpp_row_ror8(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, false));
+}
+// x[l] op x[l ^ 16] and x[l] op x[l ^ 32] through the gfx950 permlane swaps.
+__device__ __forceinline__ float swap16_max(float x) {
+    auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float swap32_max(float x) {
+    auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float swap16_sum(float x) {
+    auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float swap32_sum(float x) {
+    auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float lane_read(float x, int src_lane) {
+    return __int_as_float(__builtin_amdgcn_ds_bpermute(src_lane << 2, __float_as_int(x)));
+}
+
+// Query operand of the Q.K MFMA for block pair p (blocks 2p, 2p+1).  Lane
+// l = 16 r + n supplies column n = 8 bp + g and k-slot group r: the 16 bytes
+// of head g's block 2p+bp that the K operand's group r carries when r/2 == bp,
+// zeros otherwise.
+template <int HD>
+struct QOperand {
+    i32x4 op[Geo<HD>::NPAIR];
+    float scl[Geo<HD>::NPAIR];  // scale of block 2p+bp of head g
+};
+
+template <int HD>
+__device__ __forceinline__ void load_q_operand(QOperand<HD>& Q, const int8_t* lq, const float* lqsc,
+                                               int lane) {
+    const int r = lane >> 4, n = lane & 15, bp = n >> 3, g = n & 7;
+#pragma unroll
+    for (int p = 0; p < Geo<HD>::NPAIR; ++p) {
+        const int blk = 2 * p + bp;
+        if ((r >> 1) == bp)
+            Q.op[p] = *reinterpret_cast<const i32x4*>(lq + g * HD + kQBlock * blk + 16 * (r & 1));
+        else
+            Q.op[p] = i32x4{0, 0, 0, 0};
+        Q.scl[p] = lqsc[g * Geo<HD>::NB + blk];
+    }
+}
+
+// K operand: lane l = 16 r + n carries bytes [64p + 16r, +16) of the K row of
+// sub-tile token n (row = base + min(n, nvalid - 1)).
+template <int HD>
+__device__ __forceinline__ void load_k_subtile(i32x4 (&kop)[Geo<HD>::NPAIR], const int8_t* __restrict__ kp,
+                                               size_t base_row, int nvalid, int lane) {
+    const int r = lane >> 4, n = lane & 15;
+    const int tk = min(n, nvalid - 1);
+    const int8_t* row = kp + (base_row + (size_t)tk) * HD + 16 * r;
+#pragma unroll
+    for (int p = 0; p < Geo<HD>::NPAIR; ++p) kop[p] = *reinterpret_cast<const i32x4*>(row + 64 * p);
+}
+
+// int32 block dots of one sub-tile: c[p][j] = dot(token 4r+j, head g, block 2p+bp).
+template <int HD>
+__device__ __forceinline__ void qk_mfma(i32x4 (&c)[Geo<HD>::NPAIR], const i32x4 (&kop)[Geo<HD>::NPAIR],
+                                        const QOperand<HD>& Q) {
+#pragma unroll
+    for (int p = 0; p < Geo<HD>::NPAIR; ++p)
+        c[p] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop[p], Q.op[p], i32x4{0, 0, 0, 0}, 0, 0, 0);
+}
+
+// int8 V bytes -> f16 P.V operands.  raw[k][d] holds bytes [BPL n + 4d, +4) of
+// the V row in k-slot k; out[s] gets element k = V[k-slot k][BPL n + s] as f16.
+// u = v ^ 0x80 is v + 128 in [0, 255]; the f16 with bits 0x6400 | u is
+// 1024 + u exactly, and subtracting 1152 leaves v exactly.
+template <int DPT>
+__device__ __forceinline__ void v_to_f16(const uint32_t (&raw)[8][DPT], f16x8 (&out)[4 * DPT]) {
+    const f16x2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
+#pragma unroll
+    for (int d = 0; d < DPT; ++d) {
+        uint32_t pk[4][4];  // [byte b][token pair k2]
+#pragma unroll
+        for (int k2 = 0; k2 < 4; ++k2) {
+            const uint32_t x0 = raw[2 * k2][d] ^ 0x80808080u;
+            const uint32_t x1 = raw[2 * k2 + 1][d] ^ 0x80808080u;
+            const uint32_t lo = __builtin_amdgcn_perm(x1, x0, 0x05010400u);  // x0b0 x1b0 x0b1 x1b1
+            const uint32_t hi = __builtin_amdgcn_perm(x1, x0, 0x07030602u);  // x0b2 x1b2 x0b3 x1b3
+            pk[0][k2] = __builtin_amdgcn_perm(0x64646464u, lo, 0x04010400u);
+            pk[1][k2] = __builtin_amdgcn_perm(0x64646464u, lo, 0x04030402u);
+            pk[2][k2] = __builtin_amdgcn_perm(0x64646464u, hi, 0x04010400u);
+            pk[3][k2] = __builtin_amdgcn_perm(0x64646464u, hi, 0x04030402u);
+        }
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            u32x4 v;
+#pragma unroll
+            for (int k2 = 0; k2 < 4; ++k2) {
+                f16x2 h = __builtin_bit_cast(f16x2, pk[b][k2]) - bias;
+                v[k2] = __builtin_bit_cast(uint32_t, h);
+            }
+            out[4 * d + b] = __builtin_bit_cast(f16x8, v);
+        }
+    }
+}
+
+template <int N>
+__device__ __forceinline__ void load_dwords(uint32_t (&d)[N], const int8_t* p) {
+    if constexpr (N == 1) {
+        d[0] = *reinterpret_cast<const uint32_t*>(p);
+    } else if constexpr (N == 2) {
+        u32x2 v = *reinterpret_cast<const u32x2*>(p);
+        d[0] = v.x;
+        d[1] = v.y;
+    } else {
+        u32x4 v = *reinterpret_cast<const u32x4*>(p);
+        d[0] = v.x;
+        d[1] = v.y;
+        d[2] = v.z;
+        d[3] = v.w;
+    }
+}
+
+// ----------------------------------------------------------------------------
+// decode kernel
+
+struct DecodeArgs {
+    float* out;
+    const float* q;
+    const int8_t* kp;
+    const int8_t* vp;
+    const float* ks;
+    const float* vs;
+    const int32_t* table;
+    const int32_t* lens;
+    float* ws_acc;  // [batch][n_q][n_parts][hd]
+    float2* ws_ms;  // [batch][n_q][n_parts] (max in log2 units, exp-sum)
+    int max_blocks, num_blocks, n_q, n_kv, kv_bs, group, part_tokens, n_parts;
+    float scale_log2;  // softmax scale * log2(e)
+};
+
+template <int HD>
+__global__ __launch_bounds__(kThreads) void q8kv_decode_kernel(const DecodeArgs a) {
+    using GG = Geo<HD>;
+    __shared__ __attribute__((aligned(16))) int8_t lq[kHeadGroup * HD];
+    __shared__ float lqsc[kHeadGroup * GG::NB];
+    __shared__ float lM[kWaves][kHeadGroup];
+    __shared__ float lS[kWaves][kHeadGroup];
+    __shared__ float lacc[kWaves][kHeadGroup][HD];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int part = blockIdx.x % a.n_parts;
+    const int bk = blockIdx.x / a.n_parts;
+    const int kh = bk % a.n_kv;
+    const int b = bk / a.n_kv;
+    const int G = a.group;
+    const int cap = a.max_blocks * a.kv_bs;
+    int L = a.lens[b];
+    bool bad = false;
+    if (L > cap) {
+        L = cap;
+        bad = true;
+    }
+    float* out_rows = a.out + ((size_t)b * a.n_q + (size_t)kh * G) * HD;
+    if (L <= 0) {
+        if (part == 0)
+            for (int e = tid; e < G * HD; e += kThreads) out_rows[e] = 0.0f;
+        return;
+    }
+    const int t0 = part * a.part_tokens;
+    if (t0 >= L) return;
+    const int t1 = min(L, t0 + a.part_tokens);
+    const int n_parts_b = (L + a.part_tokens - 1) / a.part_tokens;
+
+    quantize_q_rows<HD>(a.q + ((size_t)b * a.n_q + (size_t)kh * G) * HD, G, lq, lqsc, tid, kThreads);
+    __syncthreads();
+
+    const int r = lane >> 4, n = lane & 15;
+    QOperand<HD> Q;
+    load_q_operand<HD>(Q, lq, lqsc, lane);
+
+    f32x4 acc[GG::BPL];
+#pragma unroll
+    for (int s = 0; s < GG::BPL; ++s) acc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float M = -INFINITY, S = 0.0f;
+    const int32_t* trow = a.table + (size_t)b * a.max_blocks;
+
+    for (int ts = t0 + kTile * wid; ts < t1; ts += kTile * kWaves) {
+        // Sub-tile geometry (uniform across the wave).  Partitions start on
+        // multiples of 32 and kv_bs is a multiple of 16, so each 16-token
+        // sub-tile lies inside one page.  An empty second sub-tile reuses the
+        // first one's page so that no table entry past the sequence is read.
+        int nval[2], neff[2];
+        size_t base[2];
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            nval[st] = min(max(t1 - (ts + kSub * st), 0), kSub);
+            const int tst = nval[st] > 0 ? ts + kSub * st : ts;
+            neff[st] = nval[st] > 0 ? nval[st] : nval[0];
+            int blk = trow[tst / a.kv_bs];
+            if ((unsigned)blk >= (unsigned)a.num_blocks) {
+                bad = true;
+                blk = 0;
+            }
+            base[st] = ((size_t)blk * a.n_kv + kh) * a.kv_bs + (size_t)(tst % a.kv_bs);
+        }
+
+        i32x4 kop[2][GG::NPAIR];
+        f32x4 ks4[2], vs4[2];
+        uint32_t vraw[8][GG::DPT];
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            load_k_subtile<HD>(kop[st], a.kp, base[st], neff[st], lane);
+            const int g0 = min(4 * r, (neff[st] - 1) & ~3);
+            ks4[st] = *reinterpret_cast<const f32x4*>(a.ks + base[st] + g0);
+            vs4[st] = *reinterpret_cast<const f32x4*>(a.vs + base[st] + g0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int tv = min(4 * r + j, neff[st] - 1);
+                load_dwords<GG::DPT>(vraw[4 * st + j], a.vp + (base[st] + (size_t)tv) * HD + GG::BPL * n);
+            }
+        }
+
+        // scores (log2 domain); lanes n and n^8 end up with the same values
+        float sc[2][4];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            i32x4 c[GG::NPAIR];
+            qk_mfma<HD>(c, kop[st], Q);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float part_s = 0.0f;
+#pragma unroll
+                for (int p = 0; p < GG::NPAIR; ++p) part_s += (float)c[p][j] * Q.scl[p];
+                const float full = part_s + dpp_row_ror8(part_s);
+                const float sv = (full * ks4[st][j]) * a.scale_log2;
+                sc[st][j] = (4 * r + j) < nval[st] ? sv : -INFINITY;
+                mx = fmaxf(mx, sc[st][j]);
+            }
+        }
+        mx = swap16_max(mx);
+        mx = swap32_max(mx);
+        const float m_new = fmaxf(M, mx);
+        const float alpha = __builtin_amdgcn_exp2f(M - m_new);
+        M = m_new;
+
+        f16x8 aw;
+        float wsum = 0.0f;
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float w = __builtin_amdgcn_exp2f(sc[st][j] - m_new);
+                wsum += w;
+                const float W = (4 * r + j) < nval[st] ? w * vs4[st][j] : 0.0f;
+                const _Float16 hi = (_Float16)W;
+                const _Float16 lo = (_Float16)(W - (float)hi);
+                aw[4 * st + j] = n < 8 ? hi : lo;
+            }
+        }
+        S = S * alpha + wsum;
+
+        // rescale the accumulator rows (head 4(r&1)+j) by that head's alpha
+        float arow[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) arow[j] = lane_read(alpha, 4 * (r & 1) + j);
+#pragma unroll
+        for (int s = 0; s < GG::BPL; ++s) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[s][j] *= arow[j];
+        }
+
+        f16x8 bv[GG::BPL];
+        v_to_f16<GG::DPT>(vraw, bv);
+#pragma unroll
+        for (int s = 0; s < GG::BPL; ++s) acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, bv[s], acc[s], 0, 0, 0);
+    }
+
+    // wave state -> LDS: exp-sum over the four row groups, hi + lo rows
+    S = swap16_sum(S);
+    S = swap32_sum(S);
+#pragma unroll
+    for (int s = 0; s < GG::BPL; ++s) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[s][j] = swap32_sum(acc[s][j]);
+    }
+    if (lane < kHeadGroup) {
+        lM[wid][lane] = M;
+        lS[wid][lane] = S;
+    }
+    if (r < 2) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+#pragma unroll
+            for (int s = 0; s < GG::BPL; ++s) lacc[wid][4 * r + j][GG::BPL * n + s] = acc[s][j];
+        }
+    }
+    const bool any_bad = __syncthreads_or(bad);
+
+    // merge the waves' states (same rescale rule, wave order fixed)
+    for (int e = tid; e < G * HD; e += kThreads) {
+        const int g = e / HD, i = e % HD;
+        float Mx = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) Mx = fmaxf(Mx, lM[w][g]);
+        float St = 0.0f, at = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float ew = __builtin_amdgcn_exp2f(lM[w][g] - Mx);
+            St += lS[w][g] * ew;
+            at += lacc[w][g][i] * ew;
+        }
+        if (any_bad) at = NAN;
+        if (n_parts_b == 1) {
+            out_rows[(size_t)g * HD + i] = at / St;
+        } else {
+            const size_t pidx = ((size_t)b * a.n_q + (size_t)kh * G + g) * a.n_parts + part;
+            a.ws_acc[pidx * HD + i] = at;
+            if (i == 0) a.ws_ms[pidx] = make_float2(Mx, St);
+        }
+    }
+}
+
+struct CombineArgs {
+    float* out;
+    const float* ws_acc;
+    const float2* ws_ms;
+    const int32_t* lens;
+    int n_q, n_parts, part_tokens, cap;
+};
+
+// Merge the partition states of one (sequence, head) in partition order:
+// M* = max M_p, S* = sum S_p 2^(M_p - M*), out = sum acc_p 2^(M_p - M*) / S*.
+template <int HD>
+__global__ __launch_bounds__(HD) void q8kv_combine_kernel(const CombineArgs a) {
+    const int h = blockIdx.x, b = blockIdx.y, i = threadIdx.x;
+    const int L = min(a.lens[b], a.cap);
+    if (L <= 0) return;
+    const int np = (L + a.part_tokens - 1) / a.part_tokens;
+    if (np <= 1) return;
+    const size_t base = ((size_t)b * a.n_q + h) * a.n_parts;
+    float Mx = -INFINITY;
+    for (int p = 0; p < np; ++p) Mx = fmaxf(Mx, a.ws_ms[base + p].x);
+    float St = 0.0f, at = 0.0f;
+    for (int p = 0; p < np; ++p) {
+        const float2 ms = a.ws_ms[base + p];
+        const float e = __builtin_amdgcn_exp2f(ms.x - Mx);
+        St += ms.y * e;
+        at += a.ws_acc[(base + p) * HD + i] * e;
+    }
+    a.out[((size_t)b * a.n_q + h) * HD + i] = at / St;
+}
+
+// ----------------------------------------------------------------------------
+// append kernel: one wave per (token, kv head) row
+
+struct AppendArgs {
+    int8_t* kp;
+    int8_t* vp;
+    float* ks;
+    float* vs;
+    const void* ksrc;
+    const void* vsrc;
+    const int32_t* slots;
+    int n_tokens, n_kv, kv_bs, src_bf16;
+    long long n_slots;
+};
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m));
+    return x;
+}
+
+template <int HD>
+__global__ __launch_bounds__(256) void q8kv_append_kernel(const AppendArgs a) {
+    constexpr int EPL = HD / kWave;  // elements per lane
+    const int lane = threadIdx.x & (kWave - 1);
+    const long long row_id = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row_id >= (long long)a.n_tokens * a.n_kv) return;
+    const int t = (int)(row_id / a.n_kv), kh = (int)(row_id % a.n_kv);
+    const int slot = a.slots[t];
+    if (slot < 0 || (long long)slot >= a.n_slots) return;
+    const int blk = slot / a.kv_bs, rr = slot % a.kv_bs;
+    const size_t dst_row = ((size_t)blk * a.n_kv + kh) * a.kv_bs + rr;
+    const size_t src_off = ((size_t)t * a.n_kv + kh) * HD + (size_t)lane * EPL;
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+        const void* src = pass == 0 ? a.ksrc : a.vsrc;
+        float x[EPL];
+        if (a.src_bf16) {
+            const uint16_t* s16 = static_cast<const uint16_t*>(src) + src_off;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) x[e] = __uint_as_float((uint32_t)s16[e] << 16);
+        } else {
+            const float* s32 = static_cast<const float*>(src) + src_off;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) x[e] = s32[e];
+        }
+        float am = 0.0f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) am = fmaxf(am, fabsf(x[e]));
+        am = q8_guard(wave_max(am));
+        const float inv = 127.0f / am;
+        uint32_t packed = 0;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) packed |= (uint32_t)(q8_code(x[e], inv) & 0xff) << (8 * e);
+        int8_t* dst = (pass == 0 ? a.kp : a.vp) + dst_row * HD + (size_t)lane * EPL;
+        if constexpr (EPL == 1) *reinterpret_cast<uint8_t*>(dst) = (uint8_t)packed;
+        else if constexpr (EPL == 2) *reinterpret_cast<uint16_t*>(dst) = (uint16_t)packed;
+        else *reinterpret_cast<uint32_t*>(dst) = packed;
+        if (lane == 0) (pass == 0 ? a.ks : a.vs)[dst_row] = am * kInv127;
+    }
+}
+
+// ----------------------------------------------------------------------------
+// test exports built from the decode kernel's device functions
+
+template <int HD>
+__global__ __launch_bounds__(kThreads) void q8kv_debug_quantize_kernel(int8_t* qi, float* qsc, const float* q,
+                                                                      int rows) {
+    __shared__ __attribute__((aligned(16))) int8_t lq[kHeadGroup * HD];
+    __shared__ float lqsc[kHeadGroup * Geo<HD>::NB];
+    const int r0 = blockIdx.x * kHeadGroup;
+    const int G = min(kHeadGroup, rows - r0);
+    quantize_q_rows<HD>(q + (size_t)r0 * HD, G, lq, lqsc, threadIdx.x, kThreads);
+    __syncthreads();
+    for (int e = threadIdx.x; e < G * HD; e += kThreads) qi[(size_t)r0 * HD + e] = lq[e];
+    for (int e = threadIdx.x; e < G * Geo<HD>::NB; e += kThreads) qsc[(size_t)r0 * Geo<HD>::NB + e] = lqsc[e];
+}
+
+struct DotsArgs {
+    int32_t* dots;
+    const float* q;
+    const int8_t* kp;
+    const int32_t* table;
+    const int32_t* lens;
+    int max_tok, max_blocks, num_blocks, n_q, n_kv, kv_bs, group;
+};
+
+template <int HD>
+__global__ __launch_bounds__(kThreads) void q8kv_debug_dots_kernel(const DotsArgs a) {
+    using GG = Geo<HD>;
+    __shared__ __attribute__((aligned(16))) int8_t lq[kHeadGroup * HD];
+    __shared__ float lqsc[kHeadGroup * GG::NB];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int kh = blockIdx.x % a.n_kv, b = blockIdx.x / a.n_kv;
+    const int G = a.group;
+    const int Lm = min(min(a.lens[b], a.max_blocks * a.kv_bs), a.max_tok);
+    quantize_q_rows<HD>(a.q + ((size_t)b * a.n_q + (size_t)kh * G) * HD, G, lq, lqsc, tid, kThreads);
+    __syncthreads();
+    QOperand<HD> Q;
+    load_q_operand<HD>(Q, lq, lqsc, lane);
+    const int r = lane >> 4, n = lane & 15, bp = n >> 3, g = n & 7;
+    for (int ts = kSub * wid; ts < Lm; ts += kSub * kWaves) {
+        const int nval = min(Lm - ts, kSub);
+        const int blk = a.table[(size_t)b * a.max_blocks + ts / a.kv_bs];
+        if ((unsigned)blk >= (unsigned)a.num_blocks) continue;
+        const size_t base = ((size_t)blk * a.n_kv + kh) * a.kv_bs + (size_t)(ts % a.kv_bs);
+        i32x4 kop[GG::NPAIR], c[GG::NPAIR];
+        load_k_subtile<HD>(kop, a.kp, base, nval, lane);
+        qk_mfma<HD>(c, kop, Q);
+        if (g >= G) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int t = ts + 4 * r + j;
+            if (t >= Lm) continue;
+#pragma unroll
+            for (int p = 0; p < GG::NPAIR; ++p)
+                a.dots[(((size_t)b * a.n_q + (size_t)kh * G + g) * a.max_tok + t) * GG::NB + 2 * p + bp] = c[p][j];
+        }
+    }
+}
+
+// ----------------------------------------------------------------------------
+// host side
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+    return fail(Q8KV_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+struct Workspace {
+    void* ptr = nullptr;
+    size_t bytes = 0;
+};
+std::mutex g_mu;
+std::map<std::pair<int, void*>, Workspace> g_ws;
+
+bool valid_hd(int hd) { return hd == 64 || hd == 128 || hd == 256; }
+bool valid_kv_bs(int bs) { return bs == 16 || bs == 32 || bs == 64 || bs == 128 || bs == 256; }
+
+int check_cache_shape(int num_blocks, int n_kv, int hd, int kv_bs) {
+    if (num_blocks <= 0 || n_kv <= 0) return fail(Q8KV_EINVAL, "num_blocks (%d) and n_kv_heads (%d) must be positive", num_blocks, n_kv);
+    if (!valid_hd(hd)) return fail(Q8KV_EINVAL, "hd must be 64, 128 or 256 (got %d)", hd);
+    if (!valid_kv_bs(kv_bs)) return fail(Q8KV_EINVAL, "kv_bs must be 16, 32, 64, 128 or 256 (got %d)", kv_bs);
+    const long long rows = (long long)num_blocks * n_kv * kv_bs;
+    if (rows > INT_MAX) return fail(Q8KV_EINVAL, "page pool of %lld rows exceeds 2^31-1", rows);
+    return Q8KV_OK;
+}
+
+// Partition plan: a pure function of the shapes.  Aim for about 2048
+// workgroups over the longest possible context (8 per compute unit on a
+// 256-CU part), with partitions of 128 to 4096 tokens.
+void plan(int batch, int n_kv, int max_tokens, int* part_tokens, int* n_parts) {
+    const long long units = (long long)batch * n_kv * max_tokens;
+    const long long want = (units + 2047) / 2048;
+    int pt = 128;
+    while (pt < 4096 && pt < want) pt *= 2;
+    *part_tokens = pt;
+    *n_parts = (max_tokens + pt - 1) / pt;
+}
+
+int decode_impl(float* out, const float* q, const int8_t* kp, const int8_t* vp, const float* ks,
+                const float* vs, const int32_t* table, const int32_t* lens, int max_blocks,
+                int num_blocks, int batch, int n_q, int n_kv, int hd, int kv_bs, float scale,
+                int part_tokens, void* stream) {
+    if (!out || !q || !kp || !vp || !ks || !vs || !table || !lens)
+        return fail(Q8KV_ENULL, "a tensor pointer is NULL");
+    if (batch <= 0 || n_q <= 0) return fail(Q8KV_EINVAL, "batch (%d) and n_q_heads (%d) must be positive", batch, n_q);
+    int rc = check_cache_shape(num_blocks, n_kv, hd, kv_bs);
+    if (rc) return rc;
+    if (n_q % n_kv) return fail(Q8KV_EINVAL, "n_q_heads (%d) is not a multiple of n_kv_heads (%d)", n_q, n_kv);
+    const int G = n_q / n_kv;
+    if (G > kHeadGroup) return fail(Q8KV_EINVAL, "query heads per kv head must be <= %d (got %d)", kHeadGroup, G);
+    if (max_blocks <= 0) return fail(Q8KV_EINVAL, "max_blocks_per_seq must be positive (got %d)", max_blocks);
+    if ((long long)max_blocks * kv_bs > (INT_MAX / 2)) return fail(Q8KV_EINVAL, "max_blocks_per_seq * kv_bs overflows");
+    if (!std::isfinite(scale)) return fail(Q8KV_EINVAL, "scale must be finite");
+    if (part_tokens < 0 || part_tokens % kTile) return fail(Q8KV_EINVAL, "part_tokens must be 0 or a positive multiple of %d (got %d)", kTile, part_tokens);
+    const int max_tokens = max_blocks * kv_bs;
+    int pt, np;
+    if (part_tokens == 0) {
+        plan(batch, n_kv, max_tokens, &pt, &np);
+    } else {
+        pt = part_tokens;
+        np = (max_tokens + pt - 1) / pt;
+    }
+    const long long grid = (long long)batch * n_kv * np;
+    if (grid > INT_MAX) return fail(Q8KV_EINVAL, "decode grid of %lld workgroups is too large", grid);
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    float* ws_acc = nullptr;
+    float2* ws_ms = nullptr;
+    if (np > 1) {
+        const size_t n_state = (size_t)batch * n_q * np;
+        const size_t need = n_state * ((size_t)hd * sizeof(float) + sizeof(float2));
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+        std::lock_guard<std::mutex> lock(g_mu);
+        Workspace& w = g_ws[{dev, stream}];
+        if (w.bytes < need) {
+            if (w.ptr) {
+                e = hipStreamSynchronize(st);
+                if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+                e = hipFree(w.ptr);
+                w.ptr = nullptr;
+                w.bytes = 0;
+                if (e != hipSuccess) return hip_fail(e, "hipFree");
+            }
+            e = hipMalloc(&w.ptr, need);
+            if (e != hipSuccess) {
+                w.ptr = nullptr;
+                return fail(Q8KV_ENOMEM, "hipMalloc of %zu workspace bytes: %s", need, hipGetErrorString(e));
+            }
+            w.bytes = need;
+        }
+        ws_ms = static_cast<float2*>(w.ptr);
+        ws_acc = reinterpret_cast<float*>(static_cast<char*>(w.ptr) + n_state * sizeof(float2));
+    }
+
+    DecodeArgs da{out, q, kp, vp, ks, vs, table, lens, ws_acc, ws_ms, max_blocks, num_blocks,
+                  n_q, n_kv, kv_bs, G, pt, np, scale * kLog2e};
+    switch (hd) {
+        case 64: hipLaunchKernelGGL(q8kv_decode_kernel<64>, dim3((unsigned)grid), dim3(kThreads), 0, st, da); break;
+        case 128: hipLaunchKernelGGL(q8kv_decode_kernel<128>, dim3((unsigned)grid), dim3(kThreads), 0, st, da); break;
+        default: hipLaunchKernelGGL(q8kv_decode_kernel<256>, dim3((unsigned)grid), dim3(kThreads), 0, st, da); break;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
+    if (np > 1) {
+        CombineArgs ca{out, ws_acc, ws_ms, lens, n_q, np, pt, max_tokens};
+        dim3 cg((unsigned)n_q, (unsigned)batch);
+        switch (hd) {
+            case 64: hipLaunchKernelGGL(q8kv_combine_kernel<64>, cg, dim3(64), 0, st, ca); break;
+            case 128: hipLaunchKernelGGL(q8kv_combine_kernel<128>, cg, dim3(128), 0, st, ca); break;
+            default: hipLaunchKernelGGL(q8kv_combine_kernel<256>, cg, dim3(256), 0, st, ca); break;
+        }
+        e = hipGetLastError();
+        if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
+    }
+    return Q8KV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int q8kv_decode_attn(float* out, const float* q, const int8_t* k_pages, const int8_t* v_pages,
+                     const float* k_scale, const float* v_scale, const int32_t* block_table,
+                     const int32_t* seq_lens, int max_blocks_per_seq, int num_blocks, int batch,
+                     int n_q_heads, int n_kv_heads, int hd, int kv_bs, float scale, void* stream) {
+    g_err.clear();
+    return decode_impl(out, q, k_pages, v_pages, k_scale, v_scale, block_table, seq_lens,
+                       max_blocks_per_seq, num_blocks, batch, n_q_heads, n_kv_heads, hd, kv_bs,
+                       scale, 0, stream);
+}
+
+int q8kv_decode_attn_split(float* out, const float* q, const int8_t* k_pages, const int8_t* v_pages,
+                           const float* k_scale, const float* v_scale, const int32_t* block_table,
+                           const int32_t* seq_lens, int max_blocks_per_seq, int num_blocks, int batch,
+                           int n_q_heads, int n_kv_heads, int hd, int kv_bs, float scale,
+                           int part_tokens, void* stream) {
+    g_err.clear();
+    return decode_impl(out, q, k_pages, v_pages, k_scale, v_scale, block_table, seq_lens,
+                       max_blocks_per_seq, num_blocks, batch, n_q_heads, n_kv_heads, hd, kv_bs,
+                       scale, part_tokens, stream);
+}
+
+int q8kv_plan(int batch, int n_q_heads, int n_kv_heads, int hd, int kv_bs, int max_blocks_per_seq,
+              int* part_tokens, int* n_parts) {
+    g_err.clear();
+    if (!part_tokens || !n_parts) return fail(Q8KV_ENULL, "output pointer is NULL");
+    if (batch <= 0 || n_q_heads <= 0 || n_kv_heads <= 0 || n_q_heads % n_kv_heads)
+        return fail(Q8KV_EINVAL, "bad head/batch shape");
+    if (!valid_hd(hd) || !valid_kv_bs(kv_bs) || max_blocks_per_seq <= 0 ||
+        (long long)max_blocks_per_seq * kv_bs > (INT_MAX / 2))
+        return fail(Q8KV_EINVAL, "bad hd / kv_bs / max_blocks_per_seq");
+    plan(batch, n_kv_heads, max_blocks_per_seq * kv_bs, part_tokens, n_parts);
+    return Q8KV_OK;
+}
+
+int q8kv_append(int8_t* k_pages, int8_t* v_pages, float* k_scale, float* v_scale, const void* k_src,
+                const void* v_src, int src_dtype, const int32_t* slot_mapping, int n_tokens,
+                int num_blocks, int n_kv_heads, int hd, int kv_bs, void* stream) {
+    g_err.clear();
+    if (!k_pages || !v_pages || !k_scale || !v_scale || !k_src || !v_src || !slot_mapping)
+        return fail(Q8KV_ENULL, "a tensor pointer is NULL");
+    if (n_tokens < 0) return fail(Q8KV_EINVAL, "n_tokens must be >= 0 (got %d)", n_tokens);
+    int rc = check_cache_shape(num_blocks, n_kv_heads, hd, kv_bs);
+    if (rc) return rc;
+    if (src_dtype != 0 && src_dtype != 1) return fail(Q8KV_EINVAL, "src_dtype must be 0 (fp32) or 1 (bf16)");
+    if (n_tokens == 0) return Q8KV_OK;
+    const long long rows = (long long)n_tokens * n_kv_heads;
+    const long long grid = (rows + 3) / 4;
+    if (grid > INT_MAX) return fail(Q8KV_EINVAL, "too many rows (%lld)", rows);
+    AppendArgs aa{k_pages, v_pages, k_scale, v_scale, k_src, v_src, slot_mapping, n_tokens,
+                  n_kv_heads, kv_bs, src_dtype, (long long)num_blocks * kv_bs};
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    switch (hd) {
+        case 64: hipLaunchKernelGGL(q8kv_append_kernel<64>, dim3((unsigned)grid), dim3(256), 0, st, aa); break;
+        case 128: hipLaunchKernelGGL(q8kv_append_kernel<128>, dim3((unsigned)grid), dim3(256), 0, st, aa); break;
+        default: hipLaunchKernelGGL(q8kv_append_kernel<256>, dim3((unsigned)grid), dim3(256), 0, st, aa); break;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "append kernel launch");
+    return Q8KV_OK;
+}
+
+const char* q8kv_last_error(void) { return g_err.c_str(); }
+
+int q8kv_release(void) {
+    g_err.clear();
+    std::lock_guard<std::mutex> lock(g_mu);
+    int rc = Q8KV_OK;
+    int cur = 0;
+    if (!g_ws.empty() && hipGetDevice(&cur) != hipSuccess) cur = -1;
+    for (auto& kv : g_ws) {
+        if (!kv.second.ptr) continue;
+        hipError_t e = hipSetDevice(kv.first.first);
+        if (e == hipSuccess) e = hipDeviceSynchronize();
+        if (e == hipSuccess) e = hipFree(kv.second.ptr);
+        if (e != hipSuccess && rc == Q8KV_OK) rc = hip_fail(e, "releasing workspace");
+    }
+    g_ws.clear();
+    if (cur >= 0) (void)hipSetDevice(cur);
+    return rc;
+}
+
+int q8kv_debug_quantize_q(int8_t* qi, float* qsc, const float* q, int rows, int hd, void* stream) {
+    g_err.clear();
+    if (!qi || !qsc || !q) return fail(Q8KV_ENULL, "a tensor pointer is NULL");
+    if (rows < 0 || !valid_hd(hd)) return fail(Q8KV_EINVAL, "bad rows (%d) or hd (%d)", rows, hd);
+    if (rows == 0) return Q8KV_OK;
+    const unsigned grid = (unsigned)((rows + kHeadGroup - 1) / kHeadGroup);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    switch (hd) {
+        case 64: hipLaunchKernelGGL(q8kv_debug_quantize_kernel<64>, dim3(grid), dim3(kThreads), 0, st, qi, qsc, q, rows); break;
+        case 128: hipLaunchKernelGGL(q8kv_debug_quantize_kernel<128>, dim3(grid), dim3(kThreads), 0, st, qi, qsc, q, rows); break;
+        default: hipLaunchKernelGGL(q8kv_debug_quantize_kernel<256>, dim3(grid), dim3(kThreads), 0, st, qi, qsc, q, rows); break;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "quantize kernel launch");
+    return Q8KV_OK;
+}
+
+int q8kv_debug_block_dots(int32_t* dots, int max_tok, const float* q, const int8_t* k_pages,
+                          const int32_t* block_table, const int32_t* seq_lens, int max_blocks_per_seq,
+                          int num_blocks, int batch, int n_q_heads, int n_kv_heads, int hd, int kv_bs,
+                          void* stream) {
+    g_err.clear();
+    if (!dots || !q || !k_pages || !block_table || !seq_lens) return fail(Q8KV_ENULL, "a tensor pointer is NULL");
+    int rc = check_cache_shape(num_blocks, n_kv_heads, hd, kv_bs);
+    if (rc) return rc;
+    if (batch <= 0 || n_q_heads <= 0 || n_q_heads % n_kv_heads || n_q_heads / n_kv_heads > kHeadGroup ||
+        max_tok < 0 || max_blocks_per_seq <= 0 || (long long)max_blocks_per_seq * kv_bs > (INT_MAX / 2))
+        return fail(Q8KV_EINVAL, "bad decode shape");
+    if (max_tok == 0) return Q8KV_OK;
+    DotsArgs da{dots, q, k_pages, block_table, seq_lens, max_tok, max_blocks_per_seq, num_blocks,
+                n_q_heads, n_kv_heads, kv_bs, n_q_heads / n_kv_heads};
+    const unsigned grid = (unsigned)batch * (unsigned)n_kv_heads;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    switch (hd) {
+        case 64: hipLaunchKernelGGL(q8kv_debug_dots_kernel<64>, dim3(grid), dim3(kThreads), 0, st, da); break;
+        case 128: hipLaunchKernelGGL(q8kv_debug_dots_kernel<128>, dim3(grid), dim3(kThreads), 0, st, da); break;
+        default: hipLaunchKernelGGL(q8kv_debug_dots_kernel<256>, dim3(grid), dim3(kThreads), 0, st, da); break;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "dots kernel launch");
+    return Q8KV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,156 @@
+/*
+ * q8kv -- single-query decode attention over a paged int8 ("q8") KV cache,
+ * one online-softmax pass, for AMD Instinct MI355X (gfx950).
+ *
+ * The computation is the one walked through on the page "Day 9-2:
+ * flash_attn_single_q_q8_neon" (trdm.cn), section 2:
+ *   segment 1  each query head is quantised once to int8 in 32-element
+ *              blocks, scale = absmax * fp32(1/127), codes = truncate(clamp(
+ *              q * (127 / absmax), -128, 127)), absmax < 1e-6 treated as 1;
+ *   segment 2  every cached token is scored with int8 x int8 -> int32 dot
+ *              products, one per 32-block, rescaled in fp32 by the block's q
+ *              scale, the token's K scale and the softmax scale; a running
+ *              maximum M and exp-sum S rescale the accumulated
+ *              V_int8 * (weight * v_scale) whenever M grows, so each K/V row
+ *              is read once;
+ *   segment 3  the output is the accumulator divided by S.
+ * The page's per-token rule is applied per tile of tokens and per partition
+ * of the context (the same rescale rule on whole groups), which changes the
+ * fp32 rounding but not the mathematics.
+ *
+ * Memory layouts (all tensors are caller-owned device memory, row-major,
+ * densely packed, naturally aligned -- 16 bytes for pages and scales):
+ *   q, out        fp32  [batch][n_q_heads][hd]
+ *   k_pages,
+ *   v_pages       int8  [num_blocks][n_kv_heads][kv_bs][hd]
+ *   k_scale,
+ *   v_scale       fp32  [num_blocks][n_kv_heads][kv_bs]  dequantisation
+ *                       factor absmax * fp32(1/127) of that row
+ *   block_table   int32 [batch][max_blocks_per_seq]  physical block of each
+ *                       logical block of a sequence; entries past a
+ *                       sequence's last block are never read (-1 by convention)
+ *   seq_lens      int32 [batch]  tokens cached for each sequence
+ * Token t of sequence b lives in physical block block_table[b][t / kv_bs] at
+ * row t % kv_bs.  Query head h reads kv head h / (n_q_heads / n_kv_heads).
+ *
+ * Every entry point checks its arguments on the host before it makes any HIP
+ * call, launches asynchronously on `stream` (a hipStream_t passed as void*,
+ * NULL = the null stream of the current device) and never synchronises.
+ * Faults inside a kernel surface at the caller's next synchronisation.  On a
+ * non-zero return nothing was launched and q8kv_last_error() says why.
+ */
+#ifndef Q8KV_H
+#define Q8KV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    Q8KV_OK = 0,
+    Q8KV_EINVAL = -1, /* a size, shape or value argument is out of range */
+    Q8KV_ENULL = -2,  /* a required pointer is NULL */
+    Q8KV_EHIP = -3,   /* a HIP call failed; the message holds its error string */
+    Q8KV_ENOMEM = -4  /* the split-context workspace could not be allocated */
+};
+
+/*
+ * Decode attention for one query token per sequence.
+ *
+ * out          [batch][n_q_heads][hd] fp32, written in full.  A sequence with
+ *              seq_lens[b] <= 0 gets an all-zero row.  A row whose sequence
+ *              reaches a block_table entry outside [0, num_blocks), or whose
+ *              seq_lens[b] exceeds max_blocks_per_seq * kv_bs, is written as
+ *              NaN (the kernel never reads outside the page pool).
+ * q            [batch][n_q_heads][hd] fp32 query (already rotated).
+ * max_blocks_per_seq  row stride of block_table; bounds every sequence.
+ * num_blocks   physical blocks in the page pool (bounds table entries).
+ * hd           64, 128 or 256.
+ * kv_bs        tokens per page: 16, 32, 64, 128 or 256.
+ * n_q_heads / n_kv_heads must be an integer group size of 1 to 8.
+ * scale        softmax scale (normally 1/sqrt(hd)), finite.
+ *
+ * Contexts longer than one partition are split into fixed ranges of tokens
+ * whose (max, sum, accumulator) states are merged in range order by a second
+ * kernel; the plan depends only on the shapes, so results are deterministic.
+ * Split contexts use a library-owned device workspace (grown on demand with
+ * hipMalloc, one per device and stream, freed by q8kv_release).
+ */
+int q8kv_decode_attn(float* out, const float* q,
+                     const int8_t* k_pages, const int8_t* v_pages,
+                     const float* k_scale, const float* v_scale,
+                     const int32_t* block_table, const int32_t* seq_lens,
+                     int max_blocks_per_seq, int num_blocks,
+                     int batch, int n_q_heads, int n_kv_heads, int hd, int kv_bs,
+                     float scale, void* stream);
+
+/*
+ * q8kv_decode_attn with an explicit partition length in tokens (a positive
+ * multiple of 32), or 0 for the automatic plan.  Same contract otherwise.
+ */
+int q8kv_decode_attn_split(float* out, const float* q,
+                           const int8_t* k_pages, const int8_t* v_pages,
+                           const float* k_scale, const float* v_scale,
+                           const int32_t* block_table, const int32_t* seq_lens,
+                           int max_blocks_per_seq, int num_blocks,
+                           int batch, int n_q_heads, int n_kv_heads, int hd, int kv_bs,
+                           float scale, int part_tokens, void* stream);
+
+/*
+ * The automatic partition plan for a decode shape (host only, no HIP call):
+ * *part_tokens = tokens per partition, *n_parts = partitions of the longest
+ * possible sequence (max_blocks_per_seq * kv_bs tokens).
+ */
+int q8kv_plan(int batch, int n_q_heads, int n_kv_heads, int hd, int kv_bs,
+              int max_blocks_per_seq, int* part_tokens, int* n_parts);
+
+/*
+ * Quantise new K and V rows into the paged cache (page "Day 9-2", section 1
+ * and the kscale argument of section 2: one scale per token and kv head,
+ * computed with the same absmax rule as the query, over the whole hd row).
+ *
+ * k_src, v_src [n_tokens][n_kv_heads][hd], fp32 (src_dtype 0) or bf16
+ *              (src_dtype 1, widened exactly to fp32).
+ * slot_mapping [n_tokens] int32: destination slot block * kv_bs + row of each
+ *              token; a negative slot skips the token, as does a slot at or
+ *              beyond num_blocks * kv_bs.
+ * Rows are written to k_pages/v_pages[block][kh][row][:] and their
+ * dequantisation factors to k_scale/v_scale[block][kh][row].
+ */
+int q8kv_append(int8_t* k_pages, int8_t* v_pages, float* k_scale, float* v_scale,
+                const void* k_src, const void* v_src, int src_dtype,
+                const int32_t* slot_mapping, int n_tokens, int num_blocks,
+                int n_kv_heads, int hd, int kv_bs, void* stream);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* q8kv_last_error(void);
+
+/* Free every library-owned workspace on every device (synchronising first). */
+int q8kv_release(void);
+
+/*
+ * Test exports: the decode kernel's own device functions, so that the int8
+ * parts can be compared bit for bit.
+ *
+ * q8kv_debug_quantize_q: qi [rows][hd] int8 and qsc [rows][hd/32] fp32 from
+ * q [rows][hd] fp32, through the decode kernel's query prologue.
+ *
+ * q8kv_debug_block_dots: dots [batch][n_q_heads][max_tok][hd/32] int32, the
+ * per-32-block int32 dot of the quantised query with each K row, computed by
+ * the decode kernel's matrix-core scoring step, for t < min(seq_lens[b],
+ * max_tok); other entries are left untouched.
+ */
+int q8kv_debug_quantize_q(int8_t* qi, float* qsc, const float* q, int rows, int hd,
+                          void* stream);
+int q8kv_debug_block_dots(int32_t* dots, int max_tok, const float* q, const int8_t* k_pages,
+                          const int32_t* block_table, const int32_t* seq_lens,
+                          int max_blocks_per_seq, int num_blocks, int batch, int n_q_heads,
+                          int n_kv_heads, int hd, int kv_bs, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q8KV_H */

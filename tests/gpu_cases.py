@@ -1,0 +1,63 @@
+"""GPU-side assembly for the parity tests: the same seeded fp32 sources the
+oracle quantises on the host are quantised on the GPU by q8kv_append, then
+decoded by q8kv_decode_attn.  Nothing here computes any part of the method."""
+import sys
+
+import numpy as np
+import torch
+
+import decode_attention_int8_amd as q8
+from cases import POISON_INT8
+
+DEV = torch.device("cuda", 0)
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(a, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    return t if dtype is None else t.to(dtype)
+
+
+def gpu_cache(c, poison=True, src_dtype=torch.float32, seqs=None):
+    """Append every sequence's fp32 (or bf16) source rows into a device cache."""
+    w = c.w
+    cache = q8.PagedKVCache(c.num_blocks, w.n_kv, w.kv_bs, w.hd, device=DEV)
+    cache.k_pages.fill_(POISON_INT8 if poison else 0)
+    cache.v_pages.fill_(POISON_INT8 if poison else 0)
+    cache.k_scale.fill_(float("nan") if poison else 0.0)
+    cache.v_scale.fill_(float("nan") if poison else 0.0)
+    for b in (range(w.batch) if seqs is None else seqs):
+        if len(c.slots[b]) == 0:
+            continue
+        cache.append(to_dev(c.k_src[b], src_dtype), to_dev(c.v_src[b], src_dtype), to_dev(c.slots[b]))
+    return cache
+
+
+def dev_inputs(c):
+    return to_dev(c.q), to_dev(c.table), to_dev(c.lens)
+
+
+def decode(c, cache, part_tokens=0, lens=None):
+    q, bt, sl = dev_inputs(c)
+    if lens is not None:
+        sl = to_dev(np.asarray(lens, np.int32))
+    out = q8.decode_attn(q, cache, bt, sl, c.scale, part_tokens=part_tokens)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def assert_cache_equal(host, dev, blocks=None):
+    """Bitwise equality of pages and scales (NaN == NaN for poisoned rows)."""
+    for f in ("k_pages", "v_pages", "k_scale", "v_scale"):
+        a = getattr(host, f)
+        b = getattr(dev, f).cpu().numpy()
+        if blocks is not None:
+            a, b = a[blocks], b[blocks]
+        if a.dtype == np.float32:
+            assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), f
+        else:
+            assert np.array_equal(a, b), f

@@ -1,0 +1,100 @@
+"""The C-ABI library loads, exports what include/q8kv.h declares, and rejects
+bad arguments on the host before any HIP call (CPU only: no compute call is
+made; every call here returns from argument validation)."""
+import ctypes
+
+import pytest
+
+import decode_attention_int8_amd as q8
+
+L = q8.lib
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+NUL = ctypes.c_void_p(0)
+
+
+def test_exports_every_declared_symbol():
+    names = q8.header_symbols()
+    assert len(names) == 8
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def decode(**kw):
+    a = dict(out=FAKE, q=FAKE, kp=FAKE, vp=FAKE, ks=FAKE, vs=FAKE, bt=FAKE, sl=FAKE,
+             max_blocks=8, num_blocks=16, batch=2, n_q=8, n_kv=2, hd=128, kv_bs=16,
+             scale=0.088, part=0)
+    a.update(kw)
+    return L.q8kv_decode_attn_split(a["out"], a["q"], a["kp"], a["vp"], a["ks"], a["vs"], a["bt"],
+                                    a["sl"], a["max_blocks"], a["num_blocks"], a["batch"], a["n_q"],
+                                    a["n_kv"], a["hd"], a["kv_bs"], a["scale"], a["part"], NUL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(out=NUL), q8.Q8KV_ENULL),
+    (dict(q=NUL), q8.Q8KV_ENULL),
+    (dict(kp=NUL), q8.Q8KV_ENULL),
+    (dict(vs=NUL), q8.Q8KV_ENULL),
+    (dict(bt=NUL), q8.Q8KV_ENULL),
+    (dict(sl=NUL), q8.Q8KV_ENULL),
+    (dict(batch=0), q8.Q8KV_EINVAL),
+    (dict(n_q=0), q8.Q8KV_EINVAL),
+    (dict(n_kv=0), q8.Q8KV_EINVAL),
+    (dict(n_q=6, n_kv=4), q8.Q8KV_EINVAL),
+    (dict(n_q=18, n_kv=1), q8.Q8KV_EINVAL),
+    (dict(hd=96), q8.Q8KV_EINVAL),
+    (dict(hd=512), q8.Q8KV_EINVAL),
+    (dict(kv_bs=8), q8.Q8KV_EINVAL),
+    (dict(kv_bs=48), q8.Q8KV_EINVAL),
+    (dict(max_blocks=0), q8.Q8KV_EINVAL),
+    (dict(max_blocks=1 << 30), q8.Q8KV_EINVAL),
+    (dict(num_blocks=0), q8.Q8KV_EINVAL),
+    (dict(num_blocks=1 << 30), q8.Q8KV_EINVAL),
+    (dict(scale=float("inf")), q8.Q8KV_EINVAL),
+    (dict(scale=float("nan")), q8.Q8KV_EINVAL),
+    (dict(part=48), q8.Q8KV_EINVAL),
+    (dict(part=-32), q8.Q8KV_EINVAL),
+])
+def test_decode_rejects_before_any_hip_call(kw, code):
+    assert decode(**kw) == code
+    assert q8.last_error() != ""
+
+
+def test_append_rejects():
+    def ap(**kw):
+        a = dict(kp=FAKE, vp=FAKE, ks=FAKE, vs=FAKE, ksrc=FAKE, vsrc=FAKE, dt=0, sm=FAKE,
+                 n=4, nb=8, n_kv=2, hd=128, kv_bs=16)
+        a.update(kw)
+        return L.q8kv_append(a["kp"], a["vp"], a["ks"], a["vs"], a["ksrc"], a["vsrc"], a["dt"],
+                             a["sm"], a["n"], a["nb"], a["n_kv"], a["hd"], a["kv_bs"], NUL)
+    assert ap(kp=NUL) == q8.Q8KV_ENULL
+    assert ap(sm=NUL) == q8.Q8KV_ENULL
+    assert ap(dt=2) == q8.Q8KV_EINVAL
+    assert ap(n=-1) == q8.Q8KV_EINVAL
+    assert ap(hd=100) == q8.Q8KV_EINVAL
+    assert ap(kv_bs=24) == q8.Q8KV_EINVAL
+    assert ap(nb=0) == q8.Q8KV_EINVAL
+    assert ap(n=0) == q8.Q8KV_OK  # nothing to do: no launch
+
+
+def test_debug_exports_reject():
+    assert L.q8kv_debug_quantize_q(NUL, FAKE, FAKE, 4, 128, NUL) == q8.Q8KV_ENULL
+    assert L.q8kv_debug_quantize_q(FAKE, FAKE, FAKE, 4, 100, NUL) == q8.Q8KV_EINVAL
+    assert L.q8kv_debug_quantize_q(FAKE, FAKE, FAKE, 0, 128, NUL) == q8.Q8KV_OK
+    assert L.q8kv_debug_block_dots(FAKE, 4, FAKE, FAKE, FAKE, FAKE, 4, 8, 1, 3, 2, 128, 16, NUL) == q8.Q8KV_EINVAL
+    assert L.q8kv_debug_block_dots(NUL, 4, FAKE, FAKE, FAKE, FAKE, 4, 8, 1, 2, 2, 128, 16, NUL) == q8.Q8KV_ENULL
+
+
+def test_plan_is_shape_only_and_sane():
+    for shape in [(1, 32, 4, 128, 64, 2048), (1, 32, 32, 128, 16, 256), (16, 32, 8, 128, 16, 512),
+                  (64, 64, 8, 128, 64, 512), (1, 1, 1, 128, 16, 32), (3, 8, 8, 64, 256, 1)]:
+        pt, npart = q8.plan(*shape)
+        max_tok = shape[4] * shape[5]
+        assert pt % 32 == 0 and 128 <= pt <= 4096
+        assert npart == -(-max_tok // pt)
+        assert q8.plan(*shape) == (pt, npart)
+    with pytest.raises(q8.Q8KVError):
+        q8.plan(1, 3, 2, 128, 16, 4)
+
+
+def test_release_without_workspace_is_ok():
+    q8.release()

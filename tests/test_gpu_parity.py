@@ -1,0 +1,218 @@
+"""GPU parity: the HIP path against the CPU oracle on the same seeded inputs.
+
+* quantisation and integer dot products are compared bit for bit: the paged
+  K/V rows and scales written by q8kv_append, the decode prologue's int8
+  query and block scales, and the int32 per-32-block dots of the matrix-core
+  scoring step;
+* decode outputs are compared element by element with the oracle's fp32
+  single pass, max-abs error <= 2e-4 (unit-scale V);
+* edge cases: lengths around tiles, pages and partitions, every head-group
+  size, every hd x kv_bs, forced split plans, empty sequences, poisoned
+  unreferenced rows, an out-of-range table entry, determinism.
+"""
+import numpy as np
+import pytest
+import torch
+
+import decode_attention_int8_amd as q8
+import oracle
+import workloads
+from cases import build, small
+from gpu_cases import DEV, assert_cache_equal, decode, dev_inputs, gpu_cache, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-4
+
+SMALL = {
+    "tiny": small("tiny", seq_len=200),
+    "mha7b": small("mha7b", n_q=8, n_kv=8, seq_len=300),
+    "gqa_batch": small("gqa_batch", batch=3, n_q=8, n_kv=2, seq_len=170),
+    "long_gqa": small("long_gqa", n_q=16, n_kv=2, seq_len=1000),
+    "ragged": small("ragged", batch=6, n_q=16, n_kv=2, seq_len=400),
+}
+
+
+def check_decode(c, cache=None, part_tokens=0, tol=TOL):
+    if cache is None:
+        cache = gpu_cache(c)
+    got = decode(c, cache, part_tokens=part_tokens)
+    want = oracle.decode(c.q, c.cache, c.table, c.lens, c.scale, threads=8)
+    assert np.all(np.isfinite(got)), "non-finite output"
+    err = float(np.abs(got - want).max()) if got.size else 0.0
+    assert err <= tol, f"max-abs error {err:.3g} > {tol}"
+    return err
+
+
+@pytest.mark.parametrize("hd,kv_bs,n_kv,dtype", [
+    (128, 16, 2, torch.float32), (128, 64, 8, torch.float32), (64, 16, 1, torch.float32),
+    (256, 32, 7, torch.float32), (128, 16, 2, torch.bfloat16), (256, 128, 3, torch.bfloat16),
+])
+def test_append_bit_exact(hd, kv_bs, n_kv, dtype):
+    w = workloads.Workload("app", 3, n_kv, n_kv, hd, kv_bs, 5 * kv_bs + 3, ragged=True,
+                           table="pool", spare_blocks=4, key=300 + hd + kv_bs + n_kv)
+    c = build(w, with_cache=False)
+    if dtype == torch.bfloat16:
+        bits = [to_dev(k).to(torch.bfloat16).cpu().view(torch.int16).numpy().view(np.uint16) for k in c.k_src]
+        vbits = [to_dev(v).to(torch.bfloat16).cpu().view(torch.int16).numpy().view(np.uint16) for v in c.v_src]
+        host = oracle.Cache(c.num_blocks, n_kv, kv_bs, hd, fill_int8=127, fill_scale=np.nan)
+        for b in range(w.batch):
+            host.append(bits[b], vbits[b], c.slots[b])
+    else:
+        from cases import host_cache
+        host = host_cache(c)
+    say(f"append hd={hd} kv_bs={kv_bs} n_kv={n_kv} {dtype}")
+    dev = gpu_cache(c, src_dtype=dtype)
+    torch.cuda.synchronize()
+    assert_cache_equal(host, dev)
+
+
+def test_append_skips_negative_and_out_of_pool_slots():
+    w = workloads.Workload("skip", 1, 2, 2, 128, 16, 40, key=320)
+    c = build(w)
+    slots = c.slots[0].copy()
+    slots[3] = -1
+    slots[7] = c.num_blocks * w.kv_bs  # past the pool
+    dev = q8.PagedKVCache(c.num_blocks, 2, 16, 128, device=DEV)
+    for t in (dev.k_pages, dev.v_pages):
+        t.fill_(127)
+    for t in (dev.k_scale, dev.v_scale):
+        t.fill_(float("nan"))
+    dev.append(to_dev(c.k_src[0]), to_dev(c.v_src[0]), to_dev(slots))
+    host = oracle.Cache(c.num_blocks, 2, 16, 128, fill_int8=127, fill_scale=np.nan)
+    keep = slots >= 0
+    keep &= slots < c.num_blocks * 16
+    host.append(c.k_src[0][keep], c.v_src[0][keep], slots[keep])
+    torch.cuda.synchronize()
+    assert_cache_equal(host, dev)
+
+
+@pytest.mark.parametrize("hd", [64, 128, 256])
+def test_quantize_q_bit_exact(hd):
+    rng = np.random.default_rng(hd)
+    q = rng.standard_normal((37, hd)).astype(np.float32)
+    q[3] = 0.0
+    q[5, :32] = 5e-7
+    q[6] *= 1e-3
+    q[7] *= 1e4
+    q[8, 40] = 0.5 * np.abs(q[8, 32:64]).max()
+    say(f"quantize_q hd={hd}")
+    qi, qsc = q8.debug_quantize_q(to_dev(q))
+    torch.cuda.synchronize()
+    want_qi, want_sc = oracle.quantize_q(q)
+    assert np.array_equal(qi.cpu().numpy(), want_qi)
+    assert np.array_equal(qsc.cpu().numpy().view(np.uint32), want_sc.view(np.uint32))
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_block_dots_bit_exact(name):
+    c = build(SMALL[name])
+    cache = gpu_cache(c)
+    q, bt, sl = dev_inputs(c)
+    max_tok = int(c.lens.max())
+    say(f"block dots {name}")
+    got = q8.debug_block_dots(q, cache, bt, sl, max_tok).cpu().numpy()
+    want = oracle.block_dots(c.q, c.cache, c.table, c.lens, max_tok)
+    for b in range(c.w.batch):
+        L = int(c.lens[b])
+        assert np.array_equal(got[b, :, :L], want[b, :, :L])
+
+
+@pytest.mark.parametrize("hd,G", [(64, 8), (256, 3), (128, 1), (128, 5)])
+def test_block_dots_other_shapes(hd, G):
+    w = workloads.Workload("dots", 2, 2 * G, 2, hd, 32, 77, ragged=True, table="pool", key=400 + hd + G)
+    c = build(w)
+    cache = gpu_cache(c)
+    q, bt, sl = dev_inputs(c)
+    say(f"block dots hd={hd} G={G}")
+    got = q8.debug_block_dots(q, cache, bt, sl, 77).cpu().numpy()
+    want = oracle.block_dots(c.q, c.cache, c.table, c.lens, 77)
+    for b in range(2):
+        L = int(c.lens[b])
+        assert np.array_equal(got[b, :, :L], want[b, :, :L])
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_decode_small_workloads(name):
+    c = build(SMALL[name])
+    say(f"decode {name} lens={c.lens.tolist()[:8]}")
+    dev = gpu_cache(c)
+    torch.cuda.synchronize()
+    assert_cache_equal(c.cache, dev)
+    check_decode(c, dev)
+    for pt in (32, 96):
+        check_decode(c, dev, part_tokens=pt)
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_decode_edge_lengths(G):
+    lens = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257, 300]
+    w = workloads.Workload("edge", len(lens), 2 * G, 2, 128, 16, 320, ragged=True, table="pool",
+                           spare_blocks=5, key=500 + G)
+    c = build(w, lens=lens)
+    say(f"edge lengths G={G}")
+    dev = gpu_cache(c)
+    for pt in (0, 32, 64, 128):
+        check_decode(c, dev, part_tokens=pt)
+
+
+@pytest.mark.parametrize("hd", [64, 128, 256])
+@pytest.mark.parametrize("kv_bs", [16, 32, 64, 128, 256])
+def test_decode_hd_kv_bs(hd, kv_bs):
+    w = workloads.Workload("hdbs", 3, 8, 2, hd, kv_bs, 2 * kv_bs + 37, ragged=True, table="pool",
+                           spare_blocks=2, k_outlier_p=0.05, k_outlier_amp=6.0,
+                           key=600 + hd + kv_bs)
+    c = build(w)
+    say(f"decode hd={hd} kv_bs={kv_bs} lens={c.lens.tolist()}")
+    dev = gpu_cache(c)
+    check_decode(c, dev)
+    check_decode(c, dev, part_tokens=64)
+
+
+def test_decode_empty_sequences_give_zero_rows():
+    w = workloads.Workload("empty", 4, 8, 2, 128, 16, 100, ragged=True, table="pool", key=700)
+    c = build(w, lens=[0, 50, 0, 100])
+    dev = gpu_cache(c)
+    got = decode(c, dev)
+    assert not got[0].any() and not got[2].any()
+    check_decode(c, dev)
+    check_decode(c, dev, part_tokens=32)
+
+
+def test_decode_bad_table_entry_gives_nan_row_only():
+    w = workloads.Workload("bad", 3, 4, 2, 128, 16, 64, key=710)
+    c = build(w)
+    dev = gpu_cache(c)
+    table = c.table.copy()
+    table[1, 2] = c.num_blocks + 5
+    q, _, sl = dev_inputs(c)
+    for pt in (0, 32):
+        out = q8.decode_attn(q, dev, to_dev(table), sl, c.scale, part_tokens=pt).cpu().numpy()
+        assert np.all(np.isnan(out[1]))
+        want = oracle.decode(c.q, c.cache, c.table, c.lens, c.scale)
+        assert np.abs(out[[0, 2]] - want[[0, 2]]).max() <= TOL
+    # a length past the table's capacity is flagged the same way
+    lens = c.lens.copy()
+    lens[2] = w.max_blocks * w.kv_bs + 1
+    out = q8.decode_attn(q, dev, to_dev(c.table), to_dev(lens), c.scale).cpu().numpy()
+    assert np.all(np.isnan(out[2])) and np.all(np.isfinite(out[:2]))
+
+
+def test_decode_deterministic():
+    c = build(SMALL["ragged"])
+    dev = gpu_cache(c)
+    a = decode(c, dev)
+    b = decode(c, dev)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_decode_zero_query_and_dominant_token():
+    w = small("long_gqa", n_q=8, n_kv=1, seq_len=700)
+    c = build(w, with_cache=False)
+    c.q[0, :4] = 0.0
+    c.k_src[0][333, 0] = c.q[0, 5] * np.float32(30.0)
+    from cases import host_cache
+    c.cache = host_cache(c)
+    dev = gpu_cache(c)
+    check_decode(c, dev)
+    check_decode(c, dev, part_tokens=64)
