@@ -1,0 +1,260 @@
+#!/usr/bin/env python3
+"""Benchmark: q8-KV single-query decode attention on one MI355X.
+
+One step = one q8kv_decode_attn call over one batch of the workload (Q
+quantise, page walk, int8 scoring, online softmax, P.V, split combine); the
+KV cache is appended (quantised) beforehand and is resident in HBM when the
+timed region starts.  Cold-cache timing: the step rotates over R copies of
+the page pool so that R copies span >= 1 GB (four times the MI355X's 256 MB
+last-level cache), so each step reads its KV from HBM.
+
+Prints ONE JSON line: value = KV GB/s (int8 K and V rows plus their fp32
+scales, per step, divided by the step time), plus us/step, the roofline of
+the decode launch (algorithmic bytes / mean launch time from HIP events on the
+launch stream, against 8 TB/s), the CPU oracle timed on a bounded sample of
+the same workload, and sampled parity against that oracle.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "q8-KV decode attention µs/step + KV GB/s (% of HBM peak), 1 GPU"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="mha7b", choices=workloads.ORDER)
+    p.add_argument("--cold-bytes", type=float, default=1.0e9,
+                   help="bytes the rotated cache copies must span (0: warm, one copy)")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="target CPU time of the oracle baseline sample")
+    p.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline and parity sample")
+    p.add_argument("--part-tokens", type=int, default=0, help="override the split plan (0: automatic)")
+    return p.parse_args()
+
+
+def build_gpu(w, dev, copies_bytes):
+    import torch
+    import decode_attention_int8_amd as q8
+    lens = workloads.seq_lens(w)
+    table, nb = workloads.block_table(w, lens)
+    cache = q8.PagedKVCache(nb, w.n_kv, w.kv_bs, w.hd, device=dev)
+    for t in (cache.k_pages, cache.v_pages, cache.k_scale, cache.v_scale):
+        t.zero_()
+    t0 = time.time()
+    with ThreadPoolExecutor(8) as ex:
+        chunk = 8
+        for c0 in range(0, w.batch, chunk):
+            bs = list(range(c0, min(c0 + chunk, w.batch)))
+            futs = {b: ex.submit(workloads.kv_rows, w, b, int(lens[b])) for b in bs}
+            for b in bs:
+                k, v = futs[b].result()
+                sm = workloads.slot_mapping(w, table, b, int(lens[b]))
+                cache.append(torch.from_numpy(k).to(dev), torch.from_numpy(v).to(dev),
+                             torch.from_numpy(sm).to(dev))
+    torch.cuda.synchronize()
+    log(f"appended {int(lens.sum())} tokens x {w.n_kv} kv heads in {time.time() - t0:.1f}s")
+    kv = workloads.kv_bytes(w, lens)
+    R = 1 if copies_bytes <= 0 else max(1, math.ceil(copies_bytes / kv))
+    free, _ = torch.cuda.mem_get_info(dev)
+    pool_bytes = 2 * cache.k_pages.numel() + 8 * cache.k_scale.numel()
+    R = max(1, min(R, int(0.8 * free // max(pool_bytes, 1)) + 1, 256))
+    caches = [cache] + [q8.PagedKVCache.wrap(cache.k_pages.clone(), cache.v_pages.clone(),
+                                             cache.k_scale.clone(), cache.v_scale.clone())
+                        for _ in range(R - 1)]
+    q = torch.from_numpy(workloads.query(w)).to(dev)
+    return dict(lens=lens, table=table, nb=nb, caches=caches, q=q,
+                table_d=torch.from_numpy(table).to(dev), lens_d=torch.from_numpy(lens).to(dev))
+
+
+def time_gpu(w, g, steps, warmup, part_tokens):
+    import torch
+    import decode_attention_int8_amd as q8
+    scale = workloads.softmax_scale(w.hd)
+    R = len(g["caches"])
+    out = torch.empty_like(g["q"])
+
+    def step(i):
+        q8.decode_attn(g["q"], g["caches"][i % R], g["table_d"], g["lens_d"], scale, out=out,
+                       part_tokens=part_tokens)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    # whole-loop timing: the step time the metric reports
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    loop_ms = e0.elapsed_time(e1) / steps
+    # per-launch timing: an event pair around every call, on the launch stream
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        pairs[i][0].record(stream)
+        step(i)
+        pairs[i][1].record(stream)
+    torch.cuda.synchronize()
+    launch_ms = float(np.mean([a.elapsed_time(b) for a, b in pairs]))
+    return loop_ms, launch_ms, out
+
+
+def cpu_baseline(w, g, gpu_out_fn, seconds):
+    """Time the oracle (OpenMP over (b, h), all usable host cores, at most 16)
+    on a bounded sample of the workload: whole steps repeated for about
+    `seconds` when a step is short, else the longest sequences (truncated if
+    need be) up to that budget, scaled to a whole step by the token fraction.
+    Also compares the GPU's outputs with the oracle's on that sample."""
+    import oracle
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    lens, table = g["lens"], g["table"]
+    scale = workloads.softmax_scale(w.hd)
+    q = workloads.query(w)
+    tokens_total = int(lens.sum())
+    host = oracle.Cache(g["nb"], w.n_kv, w.kv_bs, w.hd)
+    srcs = {}
+
+    def add(b):
+        if b not in srcs:
+            k, v = workloads.kv_rows(w, b, int(lens[b]))
+            host.append(k, v, workloads.slot_mapping(w, table, b, int(lens[b])))
+            srcs[b] = (k, v)
+
+    order = [int(b) for b in np.argsort(-lens, kind="stable")]
+    add(order[0])
+    probe = np.zeros_like(lens)
+    probe[order[0]] = min(int(lens[order[0]]), 4096)
+    t = time.perf_counter()
+    oracle.decode(q, host, table, probe, scale, threads=threads)
+    sec_per_tok = (time.perf_counter() - t) / int(probe[order[0]])
+    budget = max(1, int(seconds / max(sec_per_tok, 1e-12)))
+    sl = np.zeros_like(lens)
+    acc = 0
+    for b in order:
+        if acc >= budget:
+            break
+        take = min(int(lens[b]), budget - acc)
+        if take > 0:
+            add(b)
+            sl[b] = take
+            acc += take
+    seqs = [b for b in order if sl[b] > 0]
+    whole = acc == tokens_total
+    reps = max(1, int(round(budget / tokens_total))) if whole else 1
+    t = time.perf_counter()
+    for _ in range(reps):
+        want = oracle.decode(q, host, table, sl, scale, threads=threads)
+    secs = time.perf_counter() - t
+    step_s = secs / reps / (acc / tokens_total)
+    kvb = workloads.kv_bytes(w, lens)
+    got = gpu_out_fn(sl)
+    err = float(np.abs(got[seqs] - want[seqs]).max())
+    # q8 vs unquantised fp32 KV on a few heads of the sample
+    q8err, rel = [], []
+    b = seqs[0]
+    Lb = int(sl[b])
+    kb, vb = srcs[b]
+    for h in range(0, w.n_q, max(1, w.n_q // 4)):
+        ex = oracle.exact_f64(q[b, h], kb[:Lb, h // w.group], vb[:Lb, h // w.group], scale)
+        q8err.append(np.abs(want[b, h] - ex).max())
+        rel.append(np.linalg.norm(want[b, h] - ex) / np.linalg.norm(ex))
+    if whole:
+        sample = f"the whole step ({tokens_total} tokens, all {w.n_q} heads) repeated {reps} times"
+    else:
+        sample = (f"{len(seqs)} of {w.batch} sequences, {acc} of {tokens_total} tokens "
+                  f"({100.0 * acc / tokens_total:.2f}%), all {w.n_q} heads; time scaled by the token fraction")
+    cpu = {"value": round(kvb / step_s / 1e9, 4), "unit": "GB/s", "us_per_step": round(step_s * 1e6, 1),
+           "cores": threads, "kind": "oracle", "sample": sample, "sample_seconds": round(secs, 2)}
+    parity = {"max_abs_err_vs_oracle": err, "tol": 2e-4, "ok": bool(err <= 2e-4),
+              "checked": f"{len(seqs)} sequences x {w.n_q} heads (the CPU sample)",
+              "q8_vs_fp32kv_max_abs": float(max(q8err)), "q8_vs_fp32kv_rel_l2": float(max(rel))}
+    return cpu, parity
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import decode_attention_int8_amd as q8
+    w = workloads.WORKLOADS[args.workload]
+    dev = torch.device("cuda", 0)
+    log(f"workload {w.name}: batch {w.batch}, heads {w.n_q}/{w.n_kv}, hd {w.hd}, kv_bs {w.kv_bs}, "
+        f"seq_len {'U{1..%d}' % w.seq_len if w.ragged else w.seq_len}")
+    g = build_gpu(w, dev, args.cold_bytes)
+    lens = g["lens"]
+    kvb = workloads.kv_bytes(w, lens)
+    algo = workloads.step_bytes(w, lens)
+    pt, npart = q8.plan(w.batch, w.n_q, w.n_kv, w.hd, w.kv_bs, w.max_blocks)
+    if args.part_tokens:
+        pt, npart = args.part_tokens, -(-w.max_blocks * w.kv_bs // args.part_tokens)
+    log(f"KV bytes/step {kvb / 1e6:.2f} MB, {len(g['caches'])} rotated copies, plan {pt} tokens x {npart} partitions")
+    loop_ms, launch_ms, _ = time_gpu(w, g, args.steps, args.warmup, args.part_tokens)
+    log(f"step {loop_ms * 1e3:.2f} us (loop), {launch_ms * 1e3:.2f} us (per-launch events)")
+    kv_gbs = kvb / (loop_ms * 1e-3) / 1e9
+    achieved = algo / (launch_ms * 1e-3) / 1e9
+    rec = {
+        "metric": METRIC,
+        "value": round(kv_gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(loop_ms, 5),
+        "us_per_step": round(loop_ms * 1e3, 3),
+        "hbm_frac": round(kv_gbs / HBM_PEAK_GBS, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "n_q_heads": w.n_q, "n_kv_heads": w.n_kv,
+                   "hd": w.hd, "kv_bs": w.kv_bs,
+                   "seq_len": ("U{1..%d}" % w.seq_len) if w.ragged else w.seq_len,
+                   "tokens": int(lens.sum()), "kv_bytes_per_step": kvb, "algorithmic_bytes_per_step": algo,
+                   "part_tokens": pt, "n_parts": npart, "cold_cache_copies": len(g["caches"])},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "launch_us": round(launch_ms * 1e3, 3)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu:
+        scale = workloads.softmax_scale(w.hd)
+
+        def gpu_out(sample_lens):
+            o = q8.decode_attn(g["q"], g["caches"][0], g["table_d"],
+                               torch.from_numpy(np.ascontiguousarray(sample_lens)).to(dev), scale)
+            torch.cuda.synchronize()
+            return o.cpu().numpy()
+
+        cpu, parity = cpu_baseline(w, g, gpu_out, args.cpu_seconds)
+        rec["cpu_baseline"] = cpu
+        rec["parity"] = parity
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

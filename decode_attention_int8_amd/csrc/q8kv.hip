@@ -136,6 +136,19 @@ __device__ __forceinline__ float swap32_sum(float x) {
     auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
+__device__ __forceinline__ int r_of(int lane) { return lane >> 4; }
+
+// Merge states cross workgroups (and XCDs) through agent-scope relaxed
+// atomics: the stores write through and the loads read through the
+// per-XCD caches, so no whole-cache writeback or invalidate is needed.
+__device__ __forceinline__ void state_store(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float state_load(const float* p) {
+    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until this thread's stores have completed (are visible agent-wide).
+__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ float lane_read(float x, int src_lane) {
     return __int_as_float(__builtin_amdgcn_ds_bpermute(src_lane << 2, __float_as_int(x)));
 }
@@ -147,12 +160,12 @@ __device__ __forceinline__ float lane_read(float x, int src_lane) {
 template <int HD>
 struct QOperand {
     i32x4 op[Geo<HD>::NPAIR];
-    float scl[Geo<HD>::NPAIR];  // scale of block 2p+bp of head g
+    float scl[Geo<HD>::NPAIR];  // scale of block 2p+bp of head g (times score_scale)
 };
 
 template <int HD>
 __device__ __forceinline__ void load_q_operand(QOperand<HD>& Q, const int8_t* lq, const float* lqsc,
-                                               int lane) {
+                                               int lane, float score_scale = 1.0f) {
     const int r = lane >> 4, n = lane & 15, bp = n >> 3, g = n & 7;
 #pragma unroll
     for (int p = 0; p < Geo<HD>::NPAIR; ++p) {
@@ -161,7 +174,7 @@ __device__ __forceinline__ void load_q_operand(QOperand<HD>& Q, const int8_t* lq
             Q.op[p] = *reinterpret_cast<const i32x4*>(lq + g * HD + kQBlock * blk + 16 * (r & 1));
         else
             Q.op[p] = i32x4{0, 0, 0, 0};
-        Q.scl[p] = lqsc[g * Geo<HD>::NB + blk];
+        Q.scl[p] = lqsc[g * Geo<HD>::NB + blk] * score_scale;
     }
 }
 
@@ -240,6 +253,15 @@ __device__ __forceinline__ void load_dwords(uint32_t (&d)[N], const int8_t* p) {
 // ----------------------------------------------------------------------------
 // decode kernel
 
+// Partitions of one (sequence, kv head) are merged in a fixed two-level tree:
+// the last workgroup of each run of kMergeFan consecutive partitions merges
+// their states (in partition order) into a level-1 state, and the last of the
+// level-1 mergers merges those (in order) into the output.  Arrival order
+// decides only which workgroup does a merge, never the arithmetic, so the
+// result is deterministic.
+constexpr int kMergeFan = 16;
+constexpr int kMaxParts = 1024;  // kMergeFan * kMaxMerge: at most 64 level-1 states per group
+
 struct DecodeArgs {
     float* out;
     const float* q;
@@ -249,11 +271,211 @@ struct DecodeArgs {
     const float* vs;
     const int32_t* table;
     const int32_t* lens;
-    float* ws_acc;  // [batch][n_q][n_parts][hd]
-    float2* ws_ms;  // [batch][n_q][n_parts] (max in log2 units, exp-sum)
-    int max_blocks, num_blocks, n_q, n_kv, kv_bs, group, part_tokens, n_parts;
+    float* acc0;    // level-0 states [group][n_parts][G][hd]
+    float* ms0;     // [group][n_parts][G][2] (max in log2 units, exp-sum)
+    float* acc1;    // level-1 states [group][n_mid][G][hd]
+    float* ms1;     // [group][n_mid][G][2]
+    int* cnt0;      // [group][n_mid] arrivals per run (zero between calls)
+    int* cnt1;      // [group] arrivals of level-1 mergers (zero between calls)
+    int max_blocks, num_blocks, n_q, n_kv, kv_bs, group, part_tokens, n_parts, n_mid;
     float scale_log2;  // softmax scale * log2(e)
 };
+
+// Registers of one 32-token tile: K operands of both sub-tiles, their K/V
+// scales (4 tokens per lane), and the V bytes of the lane's 8 k-slots.
+template <int HD>
+struct Tile {
+    i32x4 k[2][Geo<HD>::NPAIR];
+    f32x4 ks[2], vs[2];
+    uint32_t v[8][Geo<HD>::DPT];
+    int nval[2];  // valid tokens of each 16-token sub-tile (wave-uniform)
+};
+
+// Issue the loads of the tile starting at token ts (< t1) of sequence b.
+// Partitions start on multiples of 32 and kv_bs is a multiple of 16, so each
+// 16-token sub-tile lies inside one page.  An empty second sub-tile reuses
+// the first one's page, so no table entry past the sequence is read; rows
+// past t1 are redirected to the last valid row of their sub-tile.
+template <int HD>
+__device__ __forceinline__ void tile_load(Tile<HD>& T, const DecodeArgs& a, const int32_t* trow, int kh,
+                                          int ts, int t1, int lane, bool& bad) {
+    using GG = Geo<HD>;
+    const int r = lane >> 4, n = lane & 15;
+    size_t base[2];
+    int neff[2];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+        T.nval[st] = min(max(t1 - (ts + kSub * st), 0), kSub);
+        const int tst = T.nval[st] > 0 ? ts + kSub * st : ts;
+        neff[st] = T.nval[st] > 0 ? T.nval[st] : T.nval[0];
+        int blk = trow[tst / a.kv_bs];
+        if ((unsigned)blk >= (unsigned)a.num_blocks) {
+            bad = true;
+            blk = 0;
+        }
+        base[st] = ((size_t)blk * a.n_kv + kh) * a.kv_bs + (size_t)(tst % a.kv_bs);
+    }
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+        load_k_subtile<HD>(T.k[st], a.kp, base[st], neff[st], lane);
+        const int g0 = min(4 * r, (neff[st] - 1) & ~3);
+        T.ks[st] = *reinterpret_cast<const f32x4*>(a.ks + base[st] + g0);
+        T.vs[st] = *reinterpret_cast<const f32x4*>(a.vs + base[st] + g0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int tv = min(4 * r + j, neff[st] - 1);
+            load_dwords<GG::DPT>(T.v[4 * st + j], a.vp + (base[st] + (size_t)tv) * HD + GG::BPL * n);
+        }
+    }
+}
+
+// One tile of the page's recurrence for the wave's 8 head columns: int8
+// scores on the matrix cores, tile max, rescale of S and the accumulator by
+// 2^(M_old - M_new), weights 2^(s - M_new), P.V on the matrix cores.
+template <int HD>
+__device__ __forceinline__ void tile_compute(const Tile<HD>& T, const QOperand<HD>& Q,
+                                             f32x4 (&acc)[Geo<HD>::BPL], float& M, float& S, int lane) {
+    using GG = Geo<HD>;
+    const int r = lane >> 4, n = lane & 15;
+    float sc[2][4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+        i32x4 c[GG::NPAIR];
+        qk_mfma<HD>(c, T.k[st], Q);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float part_s = 0.0f;
+#pragma unroll
+            for (int p = 0; p < GG::NPAIR; ++p) part_s += (float)c[p][j] * Q.scl[p];
+            const float full = part_s + dpp_row_ror8(part_s);  // add the other block parity
+            const float sv = full * T.ks[st][j];
+            sc[st][j] = (4 * r + j) < T.nval[st] ? sv : -INFINITY;
+            mx = fmaxf(mx, sc[st][j]);
+        }
+    }
+    mx = swap16_max(mx);
+    mx = swap32_max(mx);
+    const float m_new = fmaxf(M, mx);
+    const float alpha = __builtin_amdgcn_exp2f(M - m_new);
+    M = m_new;
+
+    f16x8 aw;
+    float wsum = 0.0f;
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float w = __builtin_amdgcn_exp2f(sc[st][j] - m_new);
+            wsum += w;
+            const float W = (4 * r + j) < T.nval[st] ? w * T.vs[st][j] : 0.0f;
+            const _Float16 hi = (_Float16)W;
+            const _Float16 lo = (_Float16)(W - (float)hi);
+            aw[4 * st + j] = n < 8 ? hi : lo;
+        }
+    }
+    S = S * alpha + wsum;
+
+    // Rescale the accumulator rows (head 4(r&1)+j) by that head's alpha.
+    // alpha is exactly 1 for a head whose maximum did not grow, so the whole
+    // step is skipped (wave-uniformly) when no head's maximum grew.
+    if (__any(alpha != 1.0f)) {
+        float arow[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) arow[j] = lane_read(alpha, 4 * (r & 1) + j);
+#pragma unroll
+        for (int s = 0; s < GG::BPL; ++s) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[s][j] *= arow[j];
+        }
+    }
+
+    f16x8 bv[GG::BPL];
+    v_to_f16<GG::DPT>(T.v, bv);
+#pragma unroll
+    for (int s = 0; s < GG::BPL; ++s) acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, bv[s], acc[s], 0, 0, 0);
+}
+
+// Merge `count` (<= kMaxMerge) consecutive states (G heads each) in order
+// with the rescale rule: M* = max M_k, S* = sum S_k 2^(M_k - M*),
+// acc* = sum acc_k 2^(M_k - M*).  States are (M, S) pairs in ms[k][g][2] and
+// accumulators in acc[k][g][HD].  Writes acc*/S* to out (final) or
+// (M*, S*, acc*) to the destination state.  All loads of a batch are issued
+// before any is used (a merge is a handful of memory round trips, not one per
+// state); the sums still run in state order.  scratch: LDS, >= 2*kMaxMerge*8
+// + 8 floats.
+constexpr int kMaxMerge = 64;
+
+template <int HD>
+__device__ void merge_states(const float* ms, const float* acc, int count, int G, bool final, float* out,
+                             float* dms, float* dacc, float* scratch, int tid) {
+    float* lm = scratch;                          // [kMaxMerge][8] maxima, then weights
+    float* ls = scratch + kMaxMerge * kHeadGroup;  // [kMaxMerge][8] exp-sums
+    float* lsum = ls + kMaxMerge * kHeadGroup;     // [8]
+    const int n = count * G;
+    float mv[2], sv[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int idx = min(tid + u * kThreads, n - 1);
+        mv[u] = state_load(ms + 2 * idx);
+        sv[u] = state_load(ms + 2 * idx + 1);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int idx = tid + u * kThreads;
+        if (idx < n) {
+            lm[(idx / G) * kHeadGroup + idx % G] = mv[u];
+            ls[(idx / G) * kHeadGroup + idx % G] = sv[u];
+        }
+    }
+    __syncthreads();
+    if (tid < G) {
+        float Mx = -INFINITY;
+        for (int k = 0; k < count; ++k) Mx = fmaxf(Mx, lm[k * kHeadGroup + tid]);
+        float St = 0.0f;
+        for (int k = 0; k < count; ++k) {
+            const float w = __builtin_amdgcn_exp2f(lm[k * kHeadGroup + tid] - Mx);
+            lm[k * kHeadGroup + tid] = w;
+            St += ls[k * kHeadGroup + tid] * w;
+        }
+        lsum[tid] = St;
+        if (!final) {
+            state_store(dms + 2 * tid, Mx);
+            state_store(dms + 2 * tid + 1, St);
+        }
+    }
+    __syncthreads();
+    constexpr int EPT = kHeadGroup * HD / kThreads;  // elements per thread
+    constexpr int C = 32 / EPT;                     // states per load batch
+    float at[EPT];
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) at[j] = 0.0f;
+    const int total = G * HD;
+    for (int k0 = 0; k0 < count; k0 += C) {
+        float v[EPT][C];
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) {
+            const int e = min(tid + j * kThreads, total - 1);
+#pragma unroll
+            for (int u = 0; u < C; ++u) v[j][u] = state_load(acc + (size_t)min(k0 + u, count - 1) * G * HD + e);
+        }
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) {
+            const int g = min(tid + j * kThreads, total - 1) / HD;
+#pragma unroll
+            for (int u = 0; u < C; ++u)
+                if (k0 + u < count) at[j] += v[j][u] * lm[(k0 + u) * kHeadGroup + g];
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+        const int e = tid + j * kThreads;
+        if (e < total) {
+            if (final) out[e] = at[j] / lsum[e / HD];
+            else state_store(dacc + e, at[j]);
+        }
+    }
+}
 
 template <int HD>
 __global__ __launch_bounds__(kThreads) void q8kv_decode_kernel(const DecodeArgs a) {
@@ -263,14 +485,15 @@ __global__ __launch_bounds__(kThreads) void q8kv_decode_kernel(const DecodeArgs 
     __shared__ float lM[kWaves][kHeadGroup];
     __shared__ float lS[kWaves][kHeadGroup];
     __shared__ float lacc[kWaves][kHeadGroup][HD];
+    __shared__ int lflag;
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int part = blockIdx.x % a.n_parts;
-    const int bk = blockIdx.x / a.n_parts;
-    const int kh = bk % a.n_kv;
-    const int b = bk / a.n_kv;
+    const int grp = blockIdx.x / a.n_parts;  // (sequence, kv head)
+    const int kh = grp % a.n_kv;
+    const int b = grp / a.n_kv;
     const int G = a.group;
     const int cap = a.max_blocks * a.kv_bs;
     int L = a.lens[b];
@@ -289,110 +512,37 @@ __global__ __launch_bounds__(kThreads) void q8kv_decode_kernel(const DecodeArgs 
     if (t0 >= L) return;
     const int t1 = min(L, t0 + a.part_tokens);
     const int n_parts_b = (L + a.part_tokens - 1) / a.part_tokens;
+    const int32_t* trow = a.table + (size_t)b * a.max_blocks;
+
+    // Start streaming the wave's first tile before the query prologue.
+    constexpr int kStride = kTile * kWaves;
+    int ts = t0 + kTile * wid;
+    Tile<HD> A, B;
+    if (ts < t1) tile_load<HD>(A, a, trow, kh, ts, t1, lane, bad);
 
     quantize_q_rows<HD>(a.q + ((size_t)b * a.n_q + (size_t)kh * G) * HD, G, lq, lqsc, tid, kThreads);
     __syncthreads();
-
-    const int r = lane >> 4, n = lane & 15;
     QOperand<HD> Q;
-    load_q_operand<HD>(Q, lq, lqsc, lane);
+    load_q_operand<HD>(Q, lq, lqsc, lane, a.scale_log2);
 
     f32x4 acc[GG::BPL];
 #pragma unroll
     for (int s = 0; s < GG::BPL; ++s) acc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
     float M = -INFINITY, S = 0.0f;
-    const int32_t* trow = a.table + (size_t)b * a.max_blocks;
 
-    for (int ts = t0 + kTile * wid; ts < t1; ts += kTile * kWaves) {
-        // Sub-tile geometry (uniform across the wave).  Partitions start on
-        // multiples of 32 and kv_bs is a multiple of 16, so each 16-token
-        // sub-tile lies inside one page.  An empty second sub-tile reuses the
-        // first one's page so that no table entry past the sequence is read.
-        int nval[2], neff[2];
-        size_t base[2];
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-            nval[st] = min(max(t1 - (ts + kSub * st), 0), kSub);
-            const int tst = nval[st] > 0 ? ts + kSub * st : ts;
-            neff[st] = nval[st] > 0 ? nval[st] : nval[0];
-            int blk = trow[tst / a.kv_bs];
-            if ((unsigned)blk >= (unsigned)a.num_blocks) {
-                bad = true;
-                blk = 0;
-            }
-            base[st] = ((size_t)blk * a.n_kv + kh) * a.kv_bs + (size_t)(tst % a.kv_bs);
-        }
-
-        i32x4 kop[2][GG::NPAIR];
-        f32x4 ks4[2], vs4[2];
-        uint32_t vraw[8][GG::DPT];
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-            load_k_subtile<HD>(kop[st], a.kp, base[st], neff[st], lane);
-            const int g0 = min(4 * r, (neff[st] - 1) & ~3);
-            ks4[st] = *reinterpret_cast<const f32x4*>(a.ks + base[st] + g0);
-            vs4[st] = *reinterpret_cast<const f32x4*>(a.vs + base[st] + g0);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int tv = min(4 * r + j, neff[st] - 1);
-                load_dwords<GG::DPT>(vraw[4 * st + j], a.vp + (base[st] + (size_t)tv) * HD + GG::BPL * n);
-            }
-        }
-
-        // scores (log2 domain); lanes n and n^8 end up with the same values
-        float sc[2][4];
-        float mx = -INFINITY;
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-            i32x4 c[GG::NPAIR];
-            qk_mfma<HD>(c, kop[st], Q);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                float part_s = 0.0f;
-#pragma unroll
-                for (int p = 0; p < GG::NPAIR; ++p) part_s += (float)c[p][j] * Q.scl[p];
-                const float full = part_s + dpp_row_ror8(part_s);
-                const float sv = (full * ks4[st][j]) * a.scale_log2;
-                sc[st][j] = (4 * r + j) < nval[st] ? sv : -INFINITY;
-                mx = fmaxf(mx, sc[st][j]);
-            }
-        }
-        mx = swap16_max(mx);
-        mx = swap32_max(mx);
-        const float m_new = fmaxf(M, mx);
-        const float alpha = __builtin_amdgcn_exp2f(M - m_new);
-        M = m_new;
-
-        f16x8 aw;
-        float wsum = 0.0f;
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float w = __builtin_amdgcn_exp2f(sc[st][j] - m_new);
-                wsum += w;
-                const float W = (4 * r + j) < nval[st] ? w * vs4[st][j] : 0.0f;
-                const _Float16 hi = (_Float16)W;
-                const _Float16 lo = (_Float16)(W - (float)hi);
-                aw[4 * st + j] = n < 8 ? hi : lo;
-            }
-        }
-        S = S * alpha + wsum;
-
-        // rescale the accumulator rows (head 4(r&1)+j) by that head's alpha
-        float arow[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) arow[j] = lane_read(alpha, 4 * (r & 1) + j);
-#pragma unroll
-        for (int s = 0; s < GG::BPL; ++s) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) acc[s][j] *= arow[j];
-        }
-
-        f16x8 bv[GG::BPL];
-        v_to_f16<GG::DPT>(vraw, bv);
-#pragma unroll
-        for (int s = 0; s < GG::BPL; ++s) acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, bv[s], acc[s], 0, 0, 0);
+    // Two register tiles in flight: load the next tile (clamped to the
+    // current one past the end, so the loads stay unconditional) while
+    // computing this one.
+    while (ts < t1) {
+        int tn = ts + kStride;
+        tile_load<HD>(B, a, trow, kh, tn < t1 ? tn : ts, t1, lane, bad);
+        tile_compute<HD>(A, Q, acc, M, S, lane);
+        ts = tn;
+        if (ts >= t1) break;
+        tn = ts + kStride;
+        tile_load<HD>(A, a, trow, kh, tn < t1 ? tn : ts, t1, lane, bad);
+        tile_compute<HD>(B, Q, acc, M, S, lane);
+        ts = tn;
     }
 
     // wave state -> LDS: exp-sum over the four row groups, hi + lo rows
@@ -407,7 +557,8 @@ __global__ __launch_bounds__(kThreads) void q8kv_decode_kernel(const DecodeArgs 
         lM[wid][lane] = M;
         lS[wid][lane] = S;
     }
-    if (r < 2) {
+    if (r_of(lane) < 2) {
+        const int r = r_of(lane), n = lane & 15;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
 #pragma unroll
@@ -417,6 +568,7 @@ __global__ __launch_bounds__(kThreads) void q8kv_decode_kernel(const DecodeArgs 
     const bool any_bad = __syncthreads_or(bad);
 
     // merge the waves' states (same rescale rule, wave order fixed)
+    const size_t state0 = ((size_t)grp * a.n_parts + part) * G;  // level-0 slot of this partition
     for (int e = tid; e < G * HD; e += kThreads) {
         const int g = e / HD, i = e % HD;
         float Mx = -INFINITY;
@@ -431,43 +583,54 @@ __global__ __launch_bounds__(kThreads) void q8kv_decode_kernel(const DecodeArgs 
         }
         if (any_bad) at = NAN;
         if (n_parts_b == 1) {
-            out_rows[(size_t)g * HD + i] = at / St;
+            out_rows[e] = at / St;
         } else {
-            const size_t pidx = ((size_t)b * a.n_q + (size_t)kh * G + g) * a.n_parts + part;
-            a.ws_acc[pidx * HD + i] = at;
-            if (i == 0) a.ws_ms[pidx] = make_float2(Mx, St);
+            state_store(a.acc0 + state0 * HD + e, at);
+            if (i == 0) {
+                state_store(a.ms0 + (state0 + g) * 2, Mx);
+                state_store(a.ms0 + (state0 + g) * 2 + 1, St);
+            }
         }
     }
-}
+    if (n_parts_b == 1) return;
 
-struct CombineArgs {
-    float* out;
-    const float* ws_acc;
-    const float2* ws_ms;
-    const int32_t* lens;
-    int n_q, n_parts, part_tokens, cap;
-};
-
-// Merge the partition states of one (sequence, head) in partition order:
-// M* = max M_p, S* = sum S_p 2^(M_p - M*), out = sum acc_p 2^(M_p - M*) / S*.
-template <int HD>
-__global__ __launch_bounds__(HD) void q8kv_combine_kernel(const CombineArgs a) {
-    const int h = blockIdx.x, b = blockIdx.y, i = threadIdx.x;
-    const int L = min(a.lens[b], a.cap);
-    if (L <= 0) return;
-    const int np = (L + a.part_tokens - 1) / a.part_tokens;
-    if (np <= 1) return;
-    const size_t base = ((size_t)b * a.n_q + h) * a.n_parts;
-    float Mx = -INFINITY;
-    for (int p = 0; p < np; ++p) Mx = fmaxf(Mx, a.ws_ms[base + p].x);
-    float St = 0.0f, at = 0.0f;
-    for (int p = 0; p < np; ++p) {
-        const float2 ms = a.ws_ms[base + p];
-        const float e = __builtin_amdgcn_exp2f(ms.x - Mx);
-        St += ms.y * e;
-        at += a.ws_acc[(base + p) * HD + i] * e;
+    // level 1: the last arrival of this run of kMergeFan partitions merges it
+    const int run = part / kMergeFan;
+    const int run_len = min(kMergeFan, n_parts_b - run * kMergeFan);
+    const int n_runs = (n_parts_b + kMergeFan - 1) / kMergeFan;
+    wait_stores();
+    __syncthreads();
+    if (tid == 0) {
+        int* c = a.cnt0 + (size_t)grp * a.n_mid + run;
+        const int prev = __hip_atomic_fetch_add(c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const bool last = prev == run_len - 1;
+        if (last) __hip_atomic_store(c, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        lflag = last;
     }
-    a.out[((size_t)b * a.n_q + h) * HD + i] = at / St;
+    __syncthreads();
+    if (!lflag) return;
+    const size_t first = ((size_t)grp * a.n_parts + (size_t)run * kMergeFan) * G;
+    const size_t mid = ((size_t)grp * a.n_mid + run) * G;
+    float* scratch = &lacc[0][0][0];  // free once the waves are merged
+    merge_states<HD>(a.ms0 + first * 2, a.acc0 + first * HD, run_len, G, n_runs == 1, out_rows,
+                     a.ms1 + mid * 2, a.acc1 + mid * HD, scratch, tid);
+    if (n_runs == 1) return;
+
+    // level 2: the last level-1 merger merges the runs into the output
+    wait_stores();
+    __syncthreads();
+    if (tid == 0) {
+        int* c = a.cnt1 + grp;
+        const int prev = __hip_atomic_fetch_add(c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const bool last = prev == n_runs - 1;
+        if (last) __hip_atomic_store(c, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        lflag = last;
+    }
+    __syncthreads();
+    if (!lflag) return;
+    const size_t mid0 = (size_t)grp * a.n_mid * G;
+    merge_states<HD>(a.ms1 + mid0 * 2, a.acc1 + mid0 * HD, n_runs, G, true, out_rows, nullptr, nullptr, scratch,
+                     tid);
 }
 
 // ----------------------------------------------------------------------------
@@ -611,9 +774,15 @@ int hip_fail(hipError_t e, const char* what) {
     return fail(Q8KV_EHIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// Library-owned split-context workspace of one (device, stream): merge states
+// (no initialisation needed) and, in a separate allocation that nothing else
+// writes, the arrival counters, which are zeroed when allocated and which
+// every call leaves at zero again.
 struct Workspace {
     void* ptr = nullptr;
     size_t bytes = 0;
+    int* counters = nullptr;
+    size_t counter_bytes = 0;
 };
 std::mutex g_mu;
 std::map<std::pair<int, void*>, Workspace> g_ws;
@@ -630,16 +799,64 @@ int check_cache_shape(int num_blocks, int n_kv, int hd, int kv_bs) {
     return Q8KV_OK;
 }
 
-// Partition plan: a pure function of the shapes.  Aim for about 2048
-// workgroups over the longest possible context (8 per compute unit on a
-// 256-CU part), with partitions of 128 to 4096 tokens.
+// Partition plan: a pure function of the shapes, so results never depend on
+// the device.  Aim for about 768 workgroups over the longest possible context
+// (3 resident 4-wave workgroups per compute unit on a 256-CU part) with
+// partitions that are multiples of 128 tokens (every wave gets the same
+// number of 32-token tiles), from 128 to 4096 tokens.
 void plan(int batch, int n_kv, int max_tokens, int* part_tokens, int* n_parts) {
     const long long units = (long long)batch * n_kv * max_tokens;
-    const long long want = (units + 2047) / 2048;
-    int pt = 128;
-    while (pt < 4096 && pt < want) pt *= 2;
-    *part_tokens = pt;
-    *n_parts = (max_tokens + pt - 1) / pt;
+    long long pt = (units + 767) / 768;
+    pt = (pt + 127) / 128 * 128;
+    if (pt < 128) pt = 128;
+    if (pt > 4096) pt = 4096;
+    // the merge tree takes at most kMaxParts partitions per sequence
+    const long long min_pt = ((max_tokens + kMaxParts - 1) / kMaxParts + 127) / 128 * 128;
+    if (pt < min_pt) pt = min_pt;
+    *part_tokens = (int)pt;
+    *n_parts = (int)((max_tokens + pt - 1) / pt);
+}
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Offsets of the merge states inside the workspace.
+struct WsLayout {
+    size_t acc0, ms0, acc1, ms1, bytes;
+};
+
+WsLayout ws_layout(size_t groups, int np, int n_mid, int G, int hd) {
+    WsLayout l;
+    size_t off = 0;
+    l.acc0 = off; off = align256(off + groups * np * G * hd * sizeof(float));
+    l.ms0 = off;  off = align256(off + groups * np * G * 2 * sizeof(float));
+    l.acc1 = off; off = align256(off + groups * n_mid * G * hd * sizeof(float));
+    l.ms1 = off;  off = align256(off + groups * n_mid * G * 2 * sizeof(float));
+    l.bytes = off;
+    return l;
+}
+
+int grow(void** ptr, size_t* have, size_t need, hipStream_t st, bool zero) {
+    if (*have >= need) return Q8KV_OK;
+    hipError_t e;
+    if (*ptr) {
+        e = hipStreamSynchronize(st);
+        if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+        e = hipFree(*ptr);
+        *ptr = nullptr;
+        *have = 0;
+        if (e != hipSuccess) return hip_fail(e, "hipFree");
+    }
+    e = hipMalloc(ptr, need);
+    if (e != hipSuccess) {
+        *ptr = nullptr;
+        return fail(Q8KV_ENOMEM, "hipMalloc of %zu workspace bytes: %s", need, hipGetErrorString(e));
+    }
+    if (zero) {
+        e = hipMemsetAsync(*ptr, 0, need, st);
+        if (e != hipSuccess) return hip_fail(e, "hipMemsetAsync");
+    }
+    *have = need;
+    return Q8KV_OK;
 }
 
 int decode_impl(float* out, const float* q, const int8_t* kp, const int8_t* vp, const float* ks,
@@ -665,43 +882,39 @@ int decode_impl(float* out, const float* q, const int8_t* kp, const int8_t* vp, 
     } else {
         pt = part_tokens;
         np = (max_tokens + pt - 1) / pt;
+        if (np > kMaxParts)
+            return fail(Q8KV_EINVAL, "part_tokens %d splits %d tokens into %d > %d partitions", pt, max_tokens, np, kMaxParts);
     }
     const long long grid = (long long)batch * n_kv * np;
     if (grid > INT_MAX) return fail(Q8KV_EINVAL, "decode grid of %lld workgroups is too large", grid);
+    const int n_mid = (np + kMergeFan - 1) / kMergeFan;
 
     hipStream_t st = static_cast<hipStream_t>(stream);
-    float* ws_acc = nullptr;
-    float2* ws_ms = nullptr;
+    DecodeArgs da{out, q, kp, vp, ks, vs, table, lens, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                  max_blocks, num_blocks, n_q, n_kv, kv_bs, G, pt, np, n_mid, scale * kLog2e};
     if (np > 1) {
-        const size_t n_state = (size_t)batch * n_q * np;
-        const size_t need = n_state * ((size_t)hd * sizeof(float) + sizeof(float2));
+        const size_t groups = (size_t)batch * n_kv;
+        const WsLayout lay = ws_layout(groups, np, n_mid, G, hd);
         int dev = 0;
         hipError_t e = hipGetDevice(&dev);
         if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
         std::lock_guard<std::mutex> lock(g_mu);
         Workspace& w = g_ws[{dev, stream}];
-        if (w.bytes < need) {
-            if (w.ptr) {
-                e = hipStreamSynchronize(st);
-                if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
-                e = hipFree(w.ptr);
-                w.ptr = nullptr;
-                w.bytes = 0;
-                if (e != hipSuccess) return hip_fail(e, "hipFree");
-            }
-            e = hipMalloc(&w.ptr, need);
-            if (e != hipSuccess) {
-                w.ptr = nullptr;
-                return fail(Q8KV_ENOMEM, "hipMalloc of %zu workspace bytes: %s", need, hipGetErrorString(e));
-            }
-            w.bytes = need;
-        }
-        ws_ms = static_cast<float2*>(w.ptr);
-        ws_acc = reinterpret_cast<float*>(static_cast<char*>(w.ptr) + n_state * sizeof(float2));
+        rc = grow(&w.ptr, &w.bytes, lay.bytes, st, false);
+        if (rc) return rc;
+        const size_t cnt_bytes = (groups * n_mid + groups) * sizeof(int);
+        void* cptr = w.counters;
+        rc = grow(&cptr, &w.counter_bytes, cnt_bytes, st, true);
+        w.counters = static_cast<int*>(cptr);
+        if (rc) return rc;
+        char* base = static_cast<char*>(w.ptr);
+        da.acc0 = reinterpret_cast<float*>(base + lay.acc0);
+        da.ms0 = reinterpret_cast<float*>(base + lay.ms0);
+        da.acc1 = reinterpret_cast<float*>(base + lay.acc1);
+        da.ms1 = reinterpret_cast<float*>(base + lay.ms1);
+        da.cnt0 = w.counters;
+        da.cnt1 = w.counters + groups * n_mid;
     }
-
-    DecodeArgs da{out, q, kp, vp, ks, vs, table, lens, ws_acc, ws_ms, max_blocks, num_blocks,
-                  n_q, n_kv, kv_bs, G, pt, np, scale * kLog2e};
     switch (hd) {
         case 64: hipLaunchKernelGGL(q8kv_decode_kernel<64>, dim3((unsigned)grid), dim3(kThreads), 0, st, da); break;
         case 128: hipLaunchKernelGGL(q8kv_decode_kernel<128>, dim3((unsigned)grid), dim3(kThreads), 0, st, da); break;
@@ -709,17 +922,6 @@ int decode_impl(float* out, const float* q, const int8_t* kp, const int8_t* vp, 
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
-    if (np > 1) {
-        CombineArgs ca{out, ws_acc, ws_ms, lens, n_q, np, pt, max_tokens};
-        dim3 cg((unsigned)n_q, (unsigned)batch);
-        switch (hd) {
-            case 64: hipLaunchKernelGGL(q8kv_combine_kernel<64>, cg, dim3(64), 0, st, ca); break;
-            case 128: hipLaunchKernelGGL(q8kv_combine_kernel<128>, cg, dim3(128), 0, st, ca); break;
-            default: hipLaunchKernelGGL(q8kv_combine_kernel<256>, cg, dim3(256), 0, st, ca); break;
-        }
-        e = hipGetLastError();
-        if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
-    }
     return Q8KV_OK;
 }
 
@@ -797,10 +999,11 @@ int q8kv_release(void) {
     int cur = 0;
     if (!g_ws.empty() && hipGetDevice(&cur) != hipSuccess) cur = -1;
     for (auto& kv : g_ws) {
-        if (!kv.second.ptr) continue;
+        if (!kv.second.ptr && !kv.second.counters) continue;
         hipError_t e = hipSetDevice(kv.first.first);
         if (e == hipSuccess) e = hipDeviceSynchronize();
-        if (e == hipSuccess) e = hipFree(kv.second.ptr);
+        if (e == hipSuccess && kv.second.ptr) e = hipFree(kv.second.ptr);
+        if (e == hipSuccess && kv.second.counters) e = hipFree(kv.second.counters);
         if (e != hipSuccess && rc == Q8KV_OK) rc = hip_fail(e, "releasing workspace");
     }
     g_ws.clear();
