@@ -138,19 +138,38 @@ __device__ __forceinline__ float swap32_sum(float x) {
 }
 __device__ __forceinline__ int r_of(int lane) { return lane >> 4; }
 
-// Merge states cross workgroups (and XCDs) through agent-scope relaxed
-// atomics: the stores write through and the loads read through the
-// per-XCD caches, so no whole-cache writeback or invalidate is needed.
-__device__ __forceinline__ void state_store(float* p, float v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Merge states cross workgroups (and XCDs).  They move through buffer
+// loads and stores with the SC1 cache policy -- device-scope coherent
+// accesses that write through / read through the per-XCD caches -- so no
+// whole-cache writeback or invalidate is ever needed.
+constexpr int kDeviceCoherent = 16;  // SC1 cache-policy bit of buffer instructions
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t state_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
 }
-__device__ __forceinline__ float state_load(const float* p) {
-    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ f32x4 state_load4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kDeviceCoherent));
+}
+__device__ __forceinline__ float state_load1(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, kDeviceCoherent));
+}
+__device__ __forceinline__ void state_store4(__amdgpu_buffer_rsrc_t r, uint32_t voff, f32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), r, voff, 0, kDeviceCoherent);
+}
+__device__ __forceinline__ void state_store1(__amdgpu_buffer_rsrc_t r, uint32_t voff, float v) {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, v), r, voff, 0, kDeviceCoherent);
 }
 // Wait until this thread's stores have completed (are visible agent-wide).
 __device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ float lane_read(float x, int src_lane) {
     return __int_as_float(__builtin_amdgcn_ds_bpermute(src_lane << 2, __float_as_int(x)));
+}
+
+// Streaming loads of cache bytes (read once): non-temporal, so they do not
+// displace reusable lines from the caches.
+template <typename T>
+__device__ __forceinline__ T stream_load(const void* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const T*>(p));
 }
 
 // Query operand of the Q.K MFMA for block pair p (blocks 2p, 2p+1).  Lane
@@ -185,9 +204,10 @@ __device__ __forceinline__ void load_k_subtile(i32x4 (&kop)[Geo<HD>::NPAIR], con
                                                size_t base_row, int nvalid, int lane) {
     const int r = lane >> 4, n = lane & 15;
     const int tk = min(n, nvalid - 1);
-    const int8_t* row = kp + (base_row + (size_t)tk) * HD + 16 * r;
+    const int8_t* sub = kp + base_row * HD;  // wave-uniform
+    const uint32_t off = (uint32_t)(tk * HD + 16 * r);
 #pragma unroll
-    for (int p = 0; p < Geo<HD>::NPAIR; ++p) kop[p] = *reinterpret_cast<const i32x4*>(row + 64 * p);
+    for (int p = 0; p < Geo<HD>::NPAIR; ++p) kop[p] = stream_load<i32x4>(sub + off + 64 * p);
 }
 
 // int32 block dots of one sub-tile: c[p][j] = dot(token 4r+j, head g, block 2p+bp).
@@ -200,49 +220,54 @@ __device__ __forceinline__ void qk_mfma(i32x4 (&c)[Geo<HD>::NPAIR], const i32x4 
 }
 
 // int8 V bytes -> f16 P.V operands.  raw[k][d] holds bytes [BPL n + 4d, +4) of
-// the V row in k-slot k; out[s] gets element k = V[k-slot k][BPL n + s] as f16.
-// u = v ^ 0x80 is v + 128 in [0, 255]; the f16 with bits 0x6400 | u is
-// 1024 + u exactly, and subtracting 1152 leaves v exactly.
-template <int DPT>
-__device__ __forceinline__ void v_to_f16(const uint32_t (&raw)[8][DPT], f16x8 (&out)[4 * DPT]) {
-    const f16x2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
-#pragma unroll
-    for (int d = 0; d < DPT; ++d) {
-        uint32_t pk[4][4];  // [byte b][token pair k2]
-#pragma unroll
-        for (int k2 = 0; k2 < 4; ++k2) {
-            const uint32_t x0 = raw[2 * k2][d] ^ 0x80808080u;
-            const uint32_t x1 = raw[2 * k2 + 1][d] ^ 0x80808080u;
-            const uint32_t lo = __builtin_amdgcn_perm(x1, x0, 0x05010400u);  // x0b0 x1b0 x0b1 x1b1
-            const uint32_t hi = __builtin_amdgcn_perm(x1, x0, 0x07030602u);  // x0b2 x1b2 x0b3 x1b3
-            pk[0][k2] = __builtin_amdgcn_perm(0x64646464u, lo, 0x04010400u);
-            pk[1][k2] = __builtin_amdgcn_perm(0x64646464u, lo, 0x04030402u);
-            pk[2][k2] = __builtin_amdgcn_perm(0x64646464u, hi, 0x04010400u);
-            pk[3][k2] = __builtin_amdgcn_perm(0x64646464u, hi, 0x04030402u);
-        }
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            u32x4 v;
-#pragma unroll
-            for (int k2 = 0; k2 < 4; ++k2) {
-                f16x2 h = __builtin_bit_cast(f16x2, pk[b][k2]) - bias;
-                v[k2] = __builtin_bit_cast(uint32_t, h);
-            }
-            out[4 * d + b] = __builtin_bit_cast(f16x8, v);
-        }
+// the V row in k-slot k; out[b] gets element k = V[k-slot k][BPL n + 4d + b] as f16.
+// Each f16 comes from one SDWA conversion of a sign-extended byte (exact for
+// int8), written into the low or high half of its destination dword.
+template <int B>
+__device__ __forceinline__ uint32_t i8pair_to_f16x2(uint32_t x0, uint32_t x1) {
+    uint32_t r;
+    if constexpr (B == 0) {
+        asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_0" : "=v"(r) : "v"(x0));
+        asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_0" : "+v"(r) : "v"(x1));
+    } else if constexpr (B == 1) {
+        asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_1" : "=v"(r) : "v"(x0));
+        asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_1" : "+v"(r) : "v"(x1));
+    } else if constexpr (B == 2) {
+        asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_2" : "=v"(r) : "v"(x0));
+        asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_2" : "+v"(r) : "v"(x1));
+    } else {
+        asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_3" : "=v"(r) : "v"(x0));
+        asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_3" : "+v"(r) : "v"(x1));
     }
+    return r;
+}
+
+template <int DPT>
+__device__ __forceinline__ void v_dword_to_f16(const uint32_t (&raw)[8][DPT], int d, f16x8 (&out)[4]) {
+    u32x4 v0, v1, v2, v3;
+#pragma unroll
+    for (int k2 = 0; k2 < 4; ++k2) {
+        v0[k2] = i8pair_to_f16x2<0>(raw[2 * k2][d], raw[2 * k2 + 1][d]);
+        v1[k2] = i8pair_to_f16x2<1>(raw[2 * k2][d], raw[2 * k2 + 1][d]);
+        v2[k2] = i8pair_to_f16x2<2>(raw[2 * k2][d], raw[2 * k2 + 1][d]);
+        v3[k2] = i8pair_to_f16x2<3>(raw[2 * k2][d], raw[2 * k2 + 1][d]);
+    }
+    out[0] = __builtin_bit_cast(f16x8, v0);
+    out[1] = __builtin_bit_cast(f16x8, v1);
+    out[2] = __builtin_bit_cast(f16x8, v2);
+    out[3] = __builtin_bit_cast(f16x8, v3);
 }
 
 template <int N>
 __device__ __forceinline__ void load_dwords(uint32_t (&d)[N], const int8_t* p) {
     if constexpr (N == 1) {
-        d[0] = *reinterpret_cast<const uint32_t*>(p);
+        d[0] = stream_load<uint32_t>(p);
     } else if constexpr (N == 2) {
-        u32x2 v = *reinterpret_cast<const u32x2*>(p);
+        u32x2 v = stream_load<u32x2>(p);
         d[0] = v.x;
         d[1] = v.y;
     } else {
-        u32x4 v = *reinterpret_cast<const u32x4*>(p);
+        u32x4 v = stream_load<u32x4>(p);
         d[0] = v.x;
         d[1] = v.y;
         d[2] = v.z;
@@ -260,7 +285,7 @@ __device__ __forceinline__ void load_dwords(uint32_t (&d)[N], const int8_t* p) {
 // decides only which workgroup does a merge, never the arithmetic, so the
 // result is deterministic.
 constexpr int kMergeFan = 16;
-constexpr int kMaxParts = 1024;  // kMergeFan * kMaxMerge: at most 64 level-1 states per group
+constexpr int kMaxParts = kMergeFan * kMergeFan;  // two merge levels of at most kMergeFan states
 
 struct DecodeArgs {
     float* out;
@@ -281,12 +306,13 @@ struct DecodeArgs {
     float scale_log2;  // softmax scale * log2(e)
 };
 
-// Registers of one 32-token tile: K operands of both sub-tiles, their K/V
-// scales (4 tokens per lane), and the V bytes of the lane's 8 k-slots.
+// Registers of one 32-token tile: K operands of both sub-tiles, the V bytes
+// of the lane's 8 k-slots, and the K/V scales of tile token (lane & 31) --
+// a lane fetches the scales of its own tokens from their owners.
 template <int HD>
 struct Tile {
     i32x4 k[2][Geo<HD>::NPAIR];
-    f32x4 ks[2], vs[2];
+    float ks, vs;
     uint32_t v[8][Geo<HD>::DPT];
     int nval[2];  // valid tokens of each 16-token sub-tile (wave-uniform)
 };
@@ -296,8 +322,16 @@ struct Tile {
 // 16-token sub-tile lies inside one page.  An empty second sub-tile reuses
 // the first one's page, so no table entry past the sequence is read; rows
 // past t1 are redirected to the last valid row of their sub-tile.
+// Physical blocks of the two sub-tiles of the tile at token ts (the table
+// index is clamped into the row, so the read is always in bounds; an entry
+// is only used when its sub-tile holds valid tokens).
+__device__ __forceinline__ void tile_blocks(const int32_t* trow, int ts, int kv_bs, int max_blocks, int (&blk)[2]) {
+    blk[0] = trow[min(ts / kv_bs, max_blocks - 1)];
+    blk[1] = trow[min((ts + kSub) / kv_bs, max_blocks - 1)];
+}
+
 template <int HD>
-__device__ __forceinline__ void tile_load(Tile<HD>& T, const DecodeArgs& a, const int32_t* trow, int kh,
+__device__ __forceinline__ void tile_load(Tile<HD>& T, const DecodeArgs& a, const int (&tblk)[2], int kh,
                                           int ts, int t1, int lane, bool& bad) {
     using GG = Geo<HD>;
     const int r = lane >> 4, n = lane & 15;
@@ -308,23 +342,28 @@ __device__ __forceinline__ void tile_load(Tile<HD>& T, const DecodeArgs& a, cons
         T.nval[st] = min(max(t1 - (ts + kSub * st), 0), kSub);
         const int tst = T.nval[st] > 0 ? ts + kSub * st : ts;
         neff[st] = T.nval[st] > 0 ? T.nval[st] : T.nval[0];
-        int blk = trow[tst / a.kv_bs];
+        int blk = (st == 1 && T.nval[1] > 0) ? tblk[1] : tblk[0];
         if ((unsigned)blk >= (unsigned)a.num_blocks) {
             bad = true;
             blk = 0;
         }
         base[st] = ((size_t)blk * a.n_kv + kh) * a.kv_bs + (size_t)(tst % a.kv_bs);
     }
+    {
+        // scales of tile token (lane & 31): sub-tile (lane >> 4) & 1, row lane & 15
+        const int st = (lane >> 4) & 1;
+        const size_t srow = (st ? base[1] : base[0]) + (size_t)min(lane & 15, (st ? neff[1] : neff[0]) - 1);
+        T.ks = stream_load<float>(a.ks + srow);
+        T.vs = stream_load<float>(a.vs + srow);
+    }
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
         load_k_subtile<HD>(T.k[st], a.kp, base[st], neff[st], lane);
-        const int g0 = min(4 * r, (neff[st] - 1) & ~3);
-        T.ks[st] = *reinterpret_cast<const f32x4*>(a.ks + base[st] + g0);
-        T.vs[st] = *reinterpret_cast<const f32x4*>(a.vs + base[st] + g0);
+        const int8_t* vsub = a.vp + base[st] * HD;  // wave-uniform
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int tv = min(4 * r + j, neff[st] - 1);
-            load_dwords<GG::DPT>(T.v[4 * st + j], a.vp + (base[st] + (size_t)tv) * HD + GG::BPL * n);
+            load_dwords<GG::DPT>(T.v[4 * st + j], vsub + (uint32_t)(tv * HD + GG::BPL * n));
         }
     }
 }
@@ -333,10 +372,13 @@ __device__ __forceinline__ void tile_load(Tile<HD>& T, const DecodeArgs& a, cons
 // scores on the matrix cores, tile max, rescale of S and the accumulator by
 // 2^(M_old - M_new), weights 2^(s - M_new), P.V on the matrix cores.
 template <int HD>
-__device__ __forceinline__ void tile_compute(const Tile<HD>& T, const QOperand<HD>& Q,
+__device__ __forceinline__ void tile_compute(const Tile<HD>& T, const int8_t* lq, const float* lqsc, float score_scale,
                                              f32x4 (&acc)[Geo<HD>::BPL], float& M, float& S, int lane) {
     using GG = Geo<HD>;
     const int r = lane >> 4, n = lane & 15;
+    // the query operand is re-read from LDS each tile rather than pinned in registers
+    QOperand<HD> Q;
+    load_q_operand<HD>(Q, lq, lqsc, lane, score_scale);
     float sc[2][4];
     float mx = -INFINITY;
 #pragma unroll
@@ -349,7 +391,8 @@ __device__ __forceinline__ void tile_compute(const Tile<HD>& T, const QOperand<H
 #pragma unroll
             for (int p = 0; p < GG::NPAIR; ++p) part_s += (float)c[p][j] * Q.scl[p];
             const float full = part_s + dpp_row_ror8(part_s);  // add the other block parity
-            const float sv = full * T.ks[st][j];
+            const float ksj = lane_read(T.ks, 16 * st + 4 * r + j);
+            const float sv = full * ksj;
             sc[st][j] = (4 * r + j) < T.nval[st] ? sv : -INFINITY;
             mx = fmaxf(mx, sc[st][j]);
         }
@@ -368,7 +411,9 @@ __device__ __forceinline__ void tile_compute(const Tile<HD>& T, const QOperand<H
         for (int j = 0; j < 4; ++j) {
             const float w = __builtin_amdgcn_exp2f(sc[st][j] - m_new);
             wsum += w;
-            const float W = (4 * r + j) < T.nval[st] ? w * T.vs[st][j] : 0.0f;
+            // ds_bpermute must run with every lane active: fetch, then select
+            const float vsj = lane_read(T.vs, 16 * st + 4 * r + j);
+            const float W = (4 * r + j) < T.nval[st] ? w * vsj : 0.0f;
             const _Float16 hi = (_Float16)W;
             const _Float16 lo = (_Float16)(W - (float)hi);
             aw[4 * st + j] = n < 8 ? hi : lo;
@@ -390,89 +435,73 @@ __device__ __forceinline__ void tile_compute(const Tile<HD>& T, const QOperand<H
         }
     }
 
-    f16x8 bv[GG::BPL];
-    v_to_f16<GG::DPT>(T.v, bv);
+    // Convert the V bytes one dword (4 slices) at a time, each group followed
+    // by its four MFMAs, so only 16 converted registers are live at once.
 #pragma unroll
-    for (int s = 0; s < GG::BPL; ++s) acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, bv[s], acc[s], 0, 0, 0);
+    for (int d = 0; d < GG::DPT; ++d) {
+        f16x8 bv[4];
+        v_dword_to_f16(T.v, d, bv);
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+            acc[4 * d + b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, bv[b], acc[4 * d + b], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
 }
 
-// Merge `count` (<= kMaxMerge) consecutive states (G heads each) in order
-// with the rescale rule: M* = max M_k, S* = sum S_k 2^(M_k - M*),
-// acc* = sum acc_k 2^(M_k - M*).  States are (M, S) pairs in ms[k][g][2] and
-// accumulators in acc[k][g][HD].  Writes acc*/S* to out (final) or
-// (M*, S*, acc*) to the destination state.  All loads of a batch are issued
-// before any is used (a merge is a handful of memory round trips, not one per
-// state); the sums still run in state order.  scratch: LDS, >= 2*kMaxMerge*8
-// + 8 floats.
-constexpr int kMaxMerge = 64;
-
+// Merge `count` (<= kMergeFan) consecutive states of G heads in order with
+// the rescale rule: M* = max M_k, S* = sum S_k 2^(M_k - M*),
+// acc* = sum acc_k 2^(M_k - M*).  States are (M, S) pairs ms[k][g][2] and
+// accumulators acc[k][g][HD].  Every thread owns float4 slices of the
+// accumulator, loads all `count` states' slices and its heads' (M, S) at
+// once (one memory round trip), and reduces them in state order.  Writes
+// acc*/S* to out (final) or (M*, S*, acc*) to the destination state.
 template <int HD>
 __device__ void merge_states(const float* ms, const float* acc, int count, int G, bool final, float* out,
-                             float* dms, float* dacc, float* scratch, int tid) {
-    float* lm = scratch;                          // [kMaxMerge][8] maxima, then weights
-    float* ls = scratch + kMaxMerge * kHeadGroup;  // [kMaxMerge][8] exp-sums
-    float* lsum = ls + kMaxMerge * kHeadGroup;     // [8]
-    const int n = count * G;
-    float mv[2], sv[2];
+                             float* dms, float* dacc, int tid) {
+    constexpr int Q4 = HD / 4;                                     // float4 per head row
+    constexpr int J = (kHeadGroup * Q4 + kThreads - 1) / kThreads;  // float4 slices per thread
+    const uint32_t acc_stride = (uint32_t)(G * HD * 4), ms_stride = (uint32_t)(G * 8);
+    const __amdgpu_buffer_rsrc_t racc = state_rsrc(acc, (uint32_t)count * acc_stride);
+    const __amdgpu_buffer_rsrc_t rms = state_rsrc(ms, (uint32_t)count * ms_stride);
+    const __amdgpu_buffer_rsrc_t rdacc = state_rsrc(dacc, acc_stride);
+    const __amdgpu_buffer_rsrc_t rdms = state_rsrc(dms, ms_stride);
+    const int total4 = G * Q4;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int idx = min(tid + u * kThreads, n - 1);
-        mv[u] = state_load(ms + 2 * idx);
-        sv[u] = state_load(ms + 2 * idx + 1);
-    }
+    for (int j = 0; j < J; ++j) {
+        const int e4 = tid + j * kThreads;
+        if (e4 >= total4) break;
+        const int g = e4 / Q4;
+        f32x4 v[kMergeFan];
+        float m[kMergeFan], sm[kMergeFan];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int idx = tid + u * kThreads;
-        if (idx < n) {
-            lm[(idx / G) * kHeadGroup + idx % G] = mv[u];
-            ls[(idx / G) * kHeadGroup + idx % G] = sv[u];
+        for (int k = 0; k < kMergeFan; ++k) {
+            const uint32_t kk = (uint32_t)min(k, count - 1);
+            v[k] = state_load4(racc, (uint32_t)e4 * 16, kk * acc_stride);
+            m[k] = state_load1(rms, (uint32_t)g * 8, kk * ms_stride);
+            sm[k] = state_load1(rms, (uint32_t)g * 8 + 4, kk * ms_stride);
         }
-    }
-    __syncthreads();
-    if (tid < G) {
         float Mx = -INFINITY;
-        for (int k = 0; k < count; ++k) Mx = fmaxf(Mx, lm[k * kHeadGroup + tid]);
+#pragma unroll
+        for (int k = 0; k < kMergeFan; ++k)
+            if (k < count) Mx = fmaxf(Mx, m[k]);
         float St = 0.0f;
-        for (int k = 0; k < count; ++k) {
-            const float w = __builtin_amdgcn_exp2f(lm[k * kHeadGroup + tid] - Mx);
-            lm[k * kHeadGroup + tid] = w;
-            St += ls[k * kHeadGroup + tid] * w;
+        f32x4 at = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < kMergeFan; ++k) {
+            if (k < count) {
+                const float w = __builtin_amdgcn_exp2f(m[k] - Mx);
+                St += sm[k] * w;
+                at += v[k] * w;
+            }
         }
-        lsum[tid] = St;
-        if (!final) {
-            state_store(dms + 2 * tid, Mx);
-            state_store(dms + 2 * tid + 1, St);
-        }
-    }
-    __syncthreads();
-    constexpr int EPT = kHeadGroup * HD / kThreads;  // elements per thread
-    constexpr int C = 32 / EPT;                     // states per load batch
-    float at[EPT];
-#pragma unroll
-    for (int j = 0; j < EPT; ++j) at[j] = 0.0f;
-    const int total = G * HD;
-    for (int k0 = 0; k0 < count; k0 += C) {
-        float v[EPT][C];
-#pragma unroll
-        for (int j = 0; j < EPT; ++j) {
-            const int e = min(tid + j * kThreads, total - 1);
-#pragma unroll
-            for (int u = 0; u < C; ++u) v[j][u] = state_load(acc + (size_t)min(k0 + u, count - 1) * G * HD + e);
-        }
-#pragma unroll
-        for (int j = 0; j < EPT; ++j) {
-            const int g = min(tid + j * kThreads, total - 1) / HD;
-#pragma unroll
-            for (int u = 0; u < C; ++u)
-                if (k0 + u < count) at[j] += v[j][u] * lm[(k0 + u) * kHeadGroup + g];
-        }
-    }
-#pragma unroll
-    for (int j = 0; j < EPT; ++j) {
-        const int e = tid + j * kThreads;
-        if (e < total) {
-            if (final) out[e] = at[j] / lsum[e / HD];
-            else state_store(dacc + e, at[j]);
+        if (final) {
+            *reinterpret_cast<f32x4*>(out + (size_t)e4 * 4) = at / St;
+        } else {
+            state_store4(rdacc, (uint32_t)e4 * 16, at);
+            if (e4 % Q4 == 0) {
+                state_store1(rdms, (uint32_t)g * 8, Mx);
+                state_store1(rdms, (uint32_t)g * 8 + 4, St);
+            }
         }
     }
 }
@@ -496,6 +525,12 @@ __global__ __launch_bounds__(kThreads) void q8kv_decode_kernel(const DecodeArgs 
     const int b = grp / a.n_kv;
     const int G = a.group;
     const int cap = a.max_blocks * a.kv_bs;
+    const int32_t* trow = a.table + (size_t)b * a.max_blocks;
+    const int t0 = part * a.part_tokens;
+    // issue the first tile's table reads together with the length read
+    int ts = t0 + kTile * wid;
+    int blk_first[2];
+    tile_blocks(trow, ts, a.kv_bs, a.max_blocks, blk_first);
     int L = a.lens[b];
     bool bad = false;
     if (L > cap) {
@@ -508,41 +543,33 @@ __global__ __launch_bounds__(kThreads) void q8kv_decode_kernel(const DecodeArgs 
             for (int e = tid; e < G * HD; e += kThreads) out_rows[e] = 0.0f;
         return;
     }
-    const int t0 = part * a.part_tokens;
     if (t0 >= L) return;
     const int t1 = min(L, t0 + a.part_tokens);
     const int n_parts_b = (L + a.part_tokens - 1) / a.part_tokens;
-    const int32_t* trow = a.table + (size_t)b * a.max_blocks;
 
     // Start streaming the wave's first tile before the query prologue.
     constexpr int kStride = kTile * kWaves;
-    int ts = t0 + kTile * wid;
-    Tile<HD> A, B;
-    if (ts < t1) tile_load<HD>(A, a, trow, kh, ts, t1, lane, bad);
+    Tile<HD> A;
+    if (ts < t1) tile_load<HD>(A, a, blk_first, kh, ts, t1, lane, bad);
 
     quantize_q_rows<HD>(a.q + ((size_t)b * a.n_q + (size_t)kh * G) * HD, G, lq, lqsc, tid, kThreads);
     __syncthreads();
-    QOperand<HD> Q;
-    load_q_operand<HD>(Q, lq, lqsc, lane, a.scale_log2);
 
     f32x4 acc[GG::BPL];
 #pragma unroll
     for (int s = 0; s < GG::BPL; ++s) acc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
     float M = -INFINITY, S = 0.0f;
 
-    // Two register tiles in flight: load the next tile (clamped to the
-    // current one past the end, so the loads stay unconditional) while
-    // computing this one.
+    // One register tile per wave; latency is hidden by the other resident
+    // waves (the tile loads of one wave overlap the others' compute).
     while (ts < t1) {
-        int tn = ts + kStride;
-        tile_load<HD>(B, a, trow, kh, tn < t1 ? tn : ts, t1, lane, bad);
-        tile_compute<HD>(A, Q, acc, M, S, lane);
-        ts = tn;
-        if (ts >= t1) break;
-        tn = ts + kStride;
-        tile_load<HD>(A, a, trow, kh, tn < t1 ? tn : ts, t1, lane, bad);
-        tile_compute<HD>(B, Q, acc, M, S, lane);
-        ts = tn;
+        tile_compute<HD>(A, lq, lqsc, a.scale_log2, acc, M, S, lane);
+        ts += kStride;
+        if (ts < t1) {
+            int blk[2];
+            tile_blocks(trow, ts, a.kv_bs, a.max_blocks, blk);
+            tile_load<HD>(A, a, blk, kh, ts, t1, lane, bad);
+        }
     }
 
     // wave state -> LDS: exp-sum over the four row groups, hi + lo rows
@@ -569,26 +596,33 @@ __global__ __launch_bounds__(kThreads) void q8kv_decode_kernel(const DecodeArgs 
 
     // merge the waves' states (same rescale rule, wave order fixed)
     const size_t state0 = ((size_t)grp * a.n_parts + part) * G;  // level-0 slot of this partition
-    for (int e = tid; e < G * HD; e += kThreads) {
-        const int g = e / HD, i = e % HD;
+    __amdgpu_buffer_rsrc_t r_acc0, r_ms0;
+    if (n_parts_b > 1) {
+        r_acc0 = state_rsrc(a.acc0 + state0 * HD, (uint32_t)(G * HD * 4));
+        r_ms0 = state_rsrc(a.ms0 + state0 * 2, (uint32_t)(G * 8));
+    }
+    constexpr int Q4 = HD / 4;
+    for (int e4 = tid; e4 < G * Q4; e4 += kThreads) {
+        const int g = e4 / Q4, i4 = e4 % Q4;
         float Mx = -INFINITY;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) Mx = fmaxf(Mx, lM[w][g]);
-        float St = 0.0f, at = 0.0f;
+        float St = 0.0f;
+        f32x4 at = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
             const float ew = __builtin_amdgcn_exp2f(lM[w][g] - Mx);
             St += lS[w][g] * ew;
-            at += lacc[w][g][i] * ew;
+            at += *reinterpret_cast<const f32x4*>(&lacc[w][g][4 * i4]) * ew;
         }
-        if (any_bad) at = NAN;
+        if (any_bad) at = f32x4{NAN, NAN, NAN, NAN};
         if (n_parts_b == 1) {
-            out_rows[e] = at / St;
+            *reinterpret_cast<f32x4*>(out_rows + (size_t)e4 * 4) = at / St;
         } else {
-            state_store(a.acc0 + state0 * HD + e, at);
-            if (i == 0) {
-                state_store(a.ms0 + (state0 + g) * 2, Mx);
-                state_store(a.ms0 + (state0 + g) * 2 + 1, St);
+            state_store4(r_acc0, (uint32_t)e4 * 16, at);
+            if (i4 == 0) {
+                state_store1(r_ms0, (uint32_t)g * 8, Mx);
+                state_store1(r_ms0, (uint32_t)g * 8 + 4, St);
             }
         }
     }
@@ -611,9 +645,8 @@ __global__ __launch_bounds__(kThreads) void q8kv_decode_kernel(const DecodeArgs 
     if (!lflag) return;
     const size_t first = ((size_t)grp * a.n_parts + (size_t)run * kMergeFan) * G;
     const size_t mid = ((size_t)grp * a.n_mid + run) * G;
-    float* scratch = &lacc[0][0][0];  // free once the waves are merged
     merge_states<HD>(a.ms0 + first * 2, a.acc0 + first * HD, run_len, G, n_runs == 1, out_rows,
-                     a.ms1 + mid * 2, a.acc1 + mid * HD, scratch, tid);
+                     a.ms1 + mid * 2, a.acc1 + mid * HD, tid);
     if (n_runs == 1) return;
 
     // level 2: the last level-1 merger merges the runs into the output
@@ -629,8 +662,8 @@ __global__ __launch_bounds__(kThreads) void q8kv_decode_kernel(const DecodeArgs 
     __syncthreads();
     if (!lflag) return;
     const size_t mid0 = (size_t)grp * a.n_mid * G;
-    merge_states<HD>(a.ms1 + mid0 * 2, a.acc1 + mid0 * HD, n_runs, G, true, out_rows, nullptr, nullptr, scratch,
-                     tid);
+    merge_states<HD>(a.ms1 + mid0 * 2, a.acc1 + mid0 * HD, n_runs, G, true, out_rows, a.ms1 + mid0 * 2,
+                     a.acc1 + mid0 * HD, tid);
 }
 
 // ----------------------------------------------------------------------------
@@ -803,14 +836,14 @@ int check_cache_shape(int num_blocks, int n_kv, int hd, int kv_bs) {
 // the device.  Aim for about 768 workgroups over the longest possible context
 // (3 resident 4-wave workgroups per compute unit on a 256-CU part) with
 // partitions that are multiples of 128 tokens (every wave gets the same
-// number of 32-token tiles), from 128 to 4096 tokens.
+// number of 32-token tiles), from 128 to 2048 tokens, and never more than
+// kMaxParts partitions per sequence.
 void plan(int batch, int n_kv, int max_tokens, int* part_tokens, int* n_parts) {
     const long long units = (long long)batch * n_kv * max_tokens;
     long long pt = (units + 767) / 768;
     pt = (pt + 127) / 128 * 128;
     if (pt < 128) pt = 128;
-    if (pt > 4096) pt = 4096;
-    // the merge tree takes at most kMaxParts partitions per sequence
+    if (pt > 2048) pt = 2048;
     const long long min_pt = ((max_tokens + kMaxParts - 1) / kMaxParts + 127) / 128 * 128;
     if (pt < min_pt) pt = min_pt;
     *part_tokens = (int)pt;
