@@ -10,9 +10,11 @@ last-level cache), so each step reads its KV from HBM.
 
 Prints ONE JSON line: value = KV GB/s (int8 K and V rows plus their fp32
 scales, per step, divided by the step time), plus us/step, the roofline of
-the decode launch (algorithmic bytes / mean launch time from HIP events on the
-launch stream, against 8 TB/s), the CPU oracle timed on a bounded sample of
-the same workload, and sampled parity against that oracle.
+the decode launch (algorithmic bytes / mean launch time, from HIP events on
+the launch stream around the timed launches, against 8 TB/s; traffic = HBM
+bytes per launch from the committed counter summary when it matches the
+kernel source), the CPU oracle timed on a bounded sample of the same
+workload, and sampled parity against that oracle.
 """
 import argparse
 import json
@@ -49,6 +51,9 @@ def parse():
                    help="target CPU time of the oracle baseline sample")
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline and parity sample")
     p.add_argument("--part-tokens", type=int, default=0, help="override the split plan (0: automatic)")
+    p.add_argument("--copy-mb", type=float, default=0.0,
+                   help="after timing, run one device-to-device copy of this many MiB (a known-size "
+                        "kernel that scales hardware byte counters)")
     return p.parse_args()
 
 
@@ -100,24 +105,33 @@ def time_gpu(w, g, steps, warmup, part_tokens):
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
+    # HIP events on the launch stream bracket the K back-to-back launches of
+    # the timed region; their mean is the per-launch (= per-step) duration
     stream = torch.cuda.current_stream()
-    # whole-loop timing: the step time the metric reports
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for i in range(steps):
         step(i)
     e1.record(stream)
     torch.cuda.synchronize()
-    loop_ms = e0.elapsed_time(e1) / steps
-    # per-launch timing: an event pair around every call, on the launch stream
-    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for i in range(steps):
-        pairs[i][0].record(stream)
-        step(i)
-        pairs[i][1].record(stream)
-    torch.cuda.synchronize()
-    launch_ms = float(np.mean([a.elapsed_time(b) for a, b in pairs]))
-    return loop_ms, launch_ms, out
+    return e0.elapsed_time(e1) / steps, out
+
+
+def profiled_traffic(w):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel source (else None)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "decode_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(w.name)
+    if not rec:
+        return None
+    src = b"".join(open(os.path.join(ROOT, f), "rb").read()
+                   for f in ("decode_attention_int8_amd/csrc/q8kv.hip", "include/q8kv.h"))
+    if hashlib.sha256(src).hexdigest() != rec["source_sha256"]:
+        return None
+    return rec["traffic_bytes"]
 
 
 def cpu_baseline(w, g, gpu_out_fn, seconds):
@@ -212,10 +226,10 @@ def main():
     if args.part_tokens:
         pt, npart = args.part_tokens, -(-w.max_blocks * w.kv_bs // args.part_tokens)
     log(f"KV bytes/step {kvb / 1e6:.2f} MB, {len(g['caches'])} rotated copies, plan {pt} tokens x {npart} partitions")
-    loop_ms, launch_ms, _ = time_gpu(w, g, args.steps, args.warmup, args.part_tokens)
-    log(f"step {loop_ms * 1e3:.2f} us (loop), {launch_ms * 1e3:.2f} us (per-launch events)")
+    loop_ms, _ = time_gpu(w, g, args.steps, args.warmup, args.part_tokens)
+    log(f"step {loop_ms * 1e3:.2f} us")
     kv_gbs = kvb / (loop_ms * 1e-3) / 1e9
-    achieved = algo / (launch_ms * 1e-3) / 1e9
+    achieved = algo / (loop_ms * 1e-3) / 1e9
     rec = {
         "metric": METRIC,
         "value": round(kv_gbs, 2),
@@ -237,10 +251,19 @@ def main():
                    "tokens": int(lens.sum()), "kv_bytes_per_step": kvb, "algorithmic_bytes_per_step": algo,
                    "part_tokens": pt, "n_parts": npart, "cold_cache_copies": len(g["caches"])},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "launch_us": round(launch_ms * 1e3, 3)},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": profiled_traffic(w),
+                     "algorithmic_bytes": algo, "launch_us": round(loop_ms * 1e3, 3)},
         "cpu_baseline": None,
     }
+    if args.copy_mb > 0:
+        n = int(args.copy_mb * 2 ** 20)
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: {n} bytes read, {n} bytes written")
+        del src, dst
     if not args.no_cpu:
         scale = workloads.softmax_scale(w.hd)
 

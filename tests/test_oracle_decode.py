@@ -262,3 +262,24 @@ def test_exact_f64_closed_forms():
     k2 = rng.standard_normal((9, 16))
     k2[4] = q * 1e3
     assert np.allclose(oracle.exact_f64(q, k2, v, 1.0), v[4], atol=1e-12)
+
+
+def test_three_pass_reference_closed_forms():
+    # the float64 three-pass reference on its own: one token returns the
+    # dequantised V row; q = 0 gives the plain mean of the dequantised rows
+    w = small("gqa_batch", batch=2, n_q=4, n_kv=2, seq_len=1)
+    c = build(w)
+    ref = oracle.three_pass_f64(c.q, c.cache, c.table, c.lens, c.scale)
+    for b in range(2):
+        for h in range(4):
+            _, v, _, vs = oracle.gather_rows(c.cache, c.table, b, h // 2, 1)
+            assert np.allclose(ref[b, h], v[0].astype(np.float64) * float(vs[0]), rtol=0, atol=1e-12)
+    w = small("ragged", batch=2, n_q=4, n_kv=2, seq_len=90)
+    c = build(w)
+    c.q[:] = 0.0
+    ref = oracle.three_pass_f64(c.q, c.cache, c.table, c.lens, c.scale)
+    for b in range(2):
+        for kh in range(2):
+            _, v, _, vs = oracle.gather_rows(c.cache, c.table, b, kh, int(c.lens[b]))
+            mean = (v.astype(np.float64) * vs.astype(np.float64)[:, None]).mean(axis=0)
+            assert np.allclose(ref[b, 2 * kh], mean, rtol=0, atol=1e-12)
