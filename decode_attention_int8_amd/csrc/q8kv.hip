@@ -37,6 +37,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <algorithm>
 #include <map>
 #include <mutex>
 #include <string>
@@ -137,30 +138,6 @@ __device__ __forceinline__ float swap32_sum(float x) {
     return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 __device__ __forceinline__ int r_of(int lane) { return lane >> 4; }
-
-// Merge states cross workgroups (and XCDs).  They move through buffer
-// loads and stores with the SC1 cache policy -- device-scope coherent
-// accesses that write through / read through the per-XCD caches -- so no
-// whole-cache writeback or invalidate is ever needed.
-constexpr int kDeviceCoherent = 16;  // SC1 cache-policy bit of buffer instructions
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t state_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ f32x4 state_load4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kDeviceCoherent));
-}
-__device__ __forceinline__ float state_load1(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, kDeviceCoherent));
-}
-__device__ __forceinline__ void state_store4(__amdgpu_buffer_rsrc_t r, uint32_t voff, f32x4 v) {
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), r, voff, 0, kDeviceCoherent);
-}
-__device__ __forceinline__ void state_store1(__amdgpu_buffer_rsrc_t r, uint32_t voff, float v) {
-    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, v), r, voff, 0, kDeviceCoherent);
-}
-// Wait until this thread's stores have completed (are visible agent-wide).
-__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ float lane_read(float x, int src_lane) {
     return __int_as_float(__builtin_amdgcn_ds_bpermute(src_lane << 2, __float_as_int(x)));
 }
@@ -278,14 +255,16 @@ __device__ __forceinline__ void load_dwords(uint32_t (&d)[N], const int8_t* p) {
 // ----------------------------------------------------------------------------
 // decode kernel
 
-// Partitions of one (sequence, kv head) are merged in a fixed two-level tree:
-// the last workgroup of each run of kMergeFan consecutive partitions merges
-// their states (in partition order) into a level-1 state, and the last of the
-// level-1 mergers merges those (in order) into the output.  Arrival order
-// decides only which workgroup does a merge, never the arithmetic, so the
-// result is deterministic.
-constexpr int kMergeFan = 16;
-constexpr int kMaxParts = kMergeFan * kMergeFan;  // two merge levels of at most kMergeFan states
+// The decode grid is persistent: each workgroup takes work items
+// (sequence b, kv head kh, token partition p) from an atomic ticket until none
+// are left, so no workgroup idles while work remains.  Items are numbered
+// through an exclusive prefix sum of n_kv * ceil(L / pt) items per sequence
+// built in LDS from seq_lens.  An item's arithmetic does not depend on which
+// workgroup runs it, so results are deterministic.  A sequence with one partition
+// writes its output directly; longer ones store each partition's state
+// (M, S, acc) and q8kv_combine_kernel merges them in partition order.
+constexpr int kMaxBatch = 2048;   // sequences per call (LDS prefix sums)
+constexpr int kMaxParts = 256;    // partitions per sequence (combine LDS)
 
 struct DecodeArgs {
     float* out;
@@ -296,13 +275,11 @@ struct DecodeArgs {
     const float* vs;
     const int32_t* table;
     const int32_t* lens;
-    float* acc0;    // level-0 states [group][n_parts][G][hd]
-    float* ms0;     // [group][n_parts][G][2] (max in log2 units, exp-sum)
-    float* acc1;    // level-1 states [group][n_mid][G][hd]
-    float* ms1;     // [group][n_mid][G][2]
-    int* cnt0;      // [group][n_mid] arrivals per run (zero between calls)
-    int* cnt1;      // [group] arrivals of level-1 mergers (zero between calls)
-    int max_blocks, num_blocks, n_q, n_kv, kv_bs, group, part_tokens, n_parts, n_mid;
+    float* st_acc;  // partition states: accumulators [batch][n_kv][n_parts][G][hd]
+    float* st_ms;   // [batch][n_kv][n_parts][G][2] (max in log2 units, exp-sum)
+    int* ticket;    // [2]: next work item, workgroups done (zero between calls);
+                    // NULL when every item has its own workgroup
+    int batch, max_blocks, num_blocks, n_q, n_kv, kv_bs, group, part_tokens, n_parts;
     float scale_log2;  // softmax scale * log2(e)
 };
 
@@ -322,12 +299,20 @@ struct Tile {
 // 16-token sub-tile lies inside one page.  An empty second sub-tile reuses
 // the first one's page, so no table entry past the sequence is read; rows
 // past t1 are redirected to the last valid row of their sub-tile.
+// Wave-uniform read of a table that the kernel never writes, through the
+// constant address space so that it is a scalar load: a vector load would
+// queue behind the in-flight tile loads and wait for all of them.
+typedef const __attribute__((address_space(4))) int32_t const_i32;
+__device__ __forceinline__ int uniform_read(const int32_t* p, int idx) {
+    return ((const_i32*)p)[idx];
+}
+
 // Physical blocks of the two sub-tiles of the tile at token ts (the table
 // index is clamped into the row, so the read is always in bounds; an entry
 // is only used when its sub-tile holds valid tokens).
 __device__ __forceinline__ void tile_blocks(const int32_t* trow, int ts, int kv_bs, int max_blocks, int (&blk)[2]) {
-    blk[0] = trow[min(ts / kv_bs, max_blocks - 1)];
-    blk[1] = trow[min((ts + kSub) / kv_bs, max_blocks - 1)];
+    blk[0] = uniform_read(trow, min(ts / kv_bs, max_blocks - 1));
+    blk[1] = uniform_read(trow, min((ts + kSub) / kv_bs, max_blocks - 1));
 }
 
 template <int HD>
@@ -448,222 +433,294 @@ __device__ __forceinline__ void tile_compute(const Tile<HD>& T, const int8_t* lq
     }
 }
 
-// Merge `count` (<= kMergeFan) consecutive states of G heads in order with
-// the rescale rule: M* = max M_k, S* = sum S_k 2^(M_k - M*),
-// acc* = sum acc_k 2^(M_k - M*).  States are (M, S) pairs ms[k][g][2] and
-// accumulators acc[k][g][HD].  Every thread owns float4 slices of the
-// accumulator, loads all `count` states' slices and its heads' (M, S) at
-// once (one memory round trip), and reduces them in state order.  Writes
-// acc*/S* to out (final) or (M*, S*, acc*) to the destination state.
-template <int HD>
-__device__ void merge_states(const float* ms, const float* acc, int count, int G, bool final, float* out,
-                             float* dms, float* dacc, int tid) {
-    constexpr int Q4 = HD / 4;                                     // float4 per head row
-    constexpr int J = (kHeadGroup * Q4 + kThreads - 1) / kThreads;  // float4 slices per thread
-    const uint32_t acc_stride = (uint32_t)(G * HD * 4), ms_stride = (uint32_t)(G * 8);
-    const __amdgpu_buffer_rsrc_t racc = state_rsrc(acc, (uint32_t)count * acc_stride);
-    const __amdgpu_buffer_rsrc_t rms = state_rsrc(ms, (uint32_t)count * ms_stride);
-    const __amdgpu_buffer_rsrc_t rdacc = state_rsrc(dacc, acc_stride);
-    const __amdgpu_buffer_rsrc_t rdms = state_rsrc(dms, ms_stride);
-    const int total4 = G * Q4;
-#pragma unroll
-    for (int j = 0; j < J; ++j) {
-        const int e4 = tid + j * kThreads;
-        if (e4 >= total4) break;
-        const int g = e4 / Q4;
-        f32x4 v[kMergeFan];
-        float m[kMergeFan], sm[kMergeFan];
-#pragma unroll
-        for (int k = 0; k < kMergeFan; ++k) {
-            const uint32_t kk = (uint32_t)min(k, count - 1);
-            v[k] = state_load4(racc, (uint32_t)e4 * 16, kk * acc_stride);
-            m[k] = state_load1(rms, (uint32_t)g * 8, kk * ms_stride);
-            sm[k] = state_load1(rms, (uint32_t)g * 8 + 4, kk * ms_stride);
-        }
-        float Mx = -INFINITY;
-#pragma unroll
-        for (int k = 0; k < kMergeFan; ++k)
-            if (k < count) Mx = fmaxf(Mx, m[k]);
-        float St = 0.0f;
-        f32x4 at = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int k = 0; k < kMergeFan; ++k) {
-            if (k < count) {
-                const float w = __builtin_amdgcn_exp2f(m[k] - Mx);
-                St += sm[k] * w;
-                at += v[k] * w;
-            }
-        }
-        if (final) {
-            *reinterpret_cast<f32x4*>(out + (size_t)e4 * 4) = at / St;
-        } else {
-            state_store4(rdacc, (uint32_t)e4 * 16, at);
-            if (e4 % Q4 == 0) {
-                state_store1(rdms, (uint32_t)g * 8, Mx);
-                state_store1(rdms, (uint32_t)g * 8 + 4, St);
-            }
-        }
-    }
+// Work items of one sequence: n_kv * ceil(L / pt); none for L <= 0.
+__device__ __forceinline__ int seq_items(int L, int cap, int pt, int n_kv) {
+    L = min(L, cap);
+    return L > 0 ? n_kv * ((L + pt - 1) / pt) : 0;
 }
 
-template <int HD>
-__global__ __launch_bounds__(kThreads) void q8kv_decode_kernel(const DecodeArgs a) {
+// PF: each wave keeps two register tiles and loads the next while computing
+// the current one (for grids of at most two workgroups per compute unit,
+// where registers are not what limits occupancy).  Occupancy asked of the
+// register allocator: 3 waves per SIMD fits hd 64 and 128 without spills
+// (single buffer), 2 with prefetch; hd 256 keeps a whole register file.
+template <int HD, bool PF>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(HD == 256 ? 1 : (PF ? 2 : 3)))) void
+q8kv_decode_kernel(const DecodeArgs a) {
     using GG = Geo<HD>;
     __shared__ __attribute__((aligned(16))) int8_t lq[kHeadGroup * HD];
     __shared__ float lqsc[kHeadGroup * GG::NB];
     __shared__ float lM[kWaves][kHeadGroup];
     __shared__ float lS[kWaves][kHeadGroup];
     __shared__ float lacc[kWaves][kHeadGroup][HD];
-    __shared__ int lflag;
+    __shared__ int lpre[kMaxBatch + 1];  // exclusive prefix of items per sequence
+    __shared__ int lscan[kWaves];
+    __shared__ int litem;
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int part = blockIdx.x % a.n_parts;
-    const int grp = blockIdx.x / a.n_parts;  // (sequence, kv head)
-    const int kh = grp % a.n_kv;
-    const int b = grp / a.n_kv;
     const int G = a.group;
     const int cap = a.max_blocks * a.kv_bs;
-    const int32_t* trow = a.table + (size_t)b * a.max_blocks;
-    const int t0 = part * a.part_tokens;
-    // issue the first tile's table reads together with the length read
-    int ts = t0 + kTile * wid;
-    int blk_first[2];
-    tile_blocks(trow, ts, a.kv_bs, a.max_blocks, blk_first);
-    int L = a.lens[b];
-    bool bad = false;
-    if (L > cap) {
-        L = cap;
-        bad = true;
-    }
-    float* out_rows = a.out + ((size_t)b * a.n_q + (size_t)kh * G) * HD;
-    if (L <= 0) {
-        if (part == 0)
-            for (int e = tid; e < G * HD; e += kThreads) out_rows[e] = 0.0f;
-        return;
-    }
-    if (t0 >= L) return;
-    const int t1 = min(L, t0 + a.part_tokens);
-    const int n_parts_b = (L + a.part_tokens - 1) / a.part_tokens;
 
-    // Start streaming the wave's first tile before the query prologue.
-    constexpr int kStride = kTile * kWaves;
-    Tile<HD> A;
-    if (ts < t1) tile_load<HD>(A, a, blk_first, kh, ts, t1, lane, bad);
-
-    quantize_q_rows<HD>(a.q + ((size_t)b * a.n_q + (size_t)kh * G) * HD, G, lq, lqsc, tid, kThreads);
+    // ---- item numbering: each thread sums a contiguous chunk of sequences;
+    // the chunk totals are scanned with wave shuffles and one LDS round
+    const int per = (a.batch + kThreads - 1) / kThreads;
+    const int c0 = min(tid * per, a.batch), c1 = min(c0 + per, a.batch);
+    int local = 0;
+    for (int bb = c0; bb < c1; ++bb) local += seq_items(a.lens[bb], cap, a.part_tokens, a.n_kv);
+    int incl = local;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int v = __shfl_up(incl, off);
+        if (lane >= off) incl += v;
+    }
+    if (lane == kWave - 1) lscan[wid] = incl;
     __syncthreads();
+    int run = incl - local;
+    for (int w = 0; w < wid; ++w) run += lscan[w];
+    for (int bb = c0; bb < c1; ++bb) {
+        lpre[bb] = run;
+        run += seq_items(a.lens[bb], cap, a.part_tokens, a.n_kv);
+    }
+    if (tid == kThreads - 1) lpre[a.batch] = run;
+    __syncthreads();
+    const int total = lpre[a.batch];
 
-    f32x4 acc[GG::BPL];
-#pragma unroll
-    for (int s = 0; s < GG::BPL; ++s) acc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float M = -INFINITY, S = 0.0f;
-
-    // One register tile per wave; latency is hidden by the other resident
-    // waves (the tile loads of one wave overlap the others' compute).
-    while (ts < t1) {
-        tile_compute<HD>(A, lq, lqsc, a.scale_log2, acc, M, S, lane);
-        ts += kStride;
-        if (ts < t1) {
-            int blk[2];
-            tile_blocks(trow, ts, a.kv_bs, a.max_blocks, blk);
-            tile_load<HD>(A, a, blk, kh, ts, t1, lane, bad);
+    // empty sequences get zero rows (R11); sequence b is zeroed by workgroup b mod grid
+    for (int bb = blockIdx.x; bb < a.batch; bb += gridDim.x) {
+        if (lpre[bb + 1] == lpre[bb]) {
+            float* o = a.out + (size_t)bb * a.n_q * HD;
+            for (int e = tid; e < a.n_q * HD; e += kThreads) o[e] = 0.0f;
         }
     }
 
-    // wave state -> LDS: exp-sum over the four row groups, hi + lo rows
-    S = swap16_sum(S);
-    S = swap32_sum(S);
-#pragma unroll
-    for (int s = 0; s < GG::BPL; ++s) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[s][j] = swap32_sum(acc[s][j]);
-    }
-    if (lane < kHeadGroup) {
-        lM[wid][lane] = M;
-        lS[wid][lane] = S;
-    }
-    if (r_of(lane) < 2) {
-        const int r = r_of(lane), n = lane & 15;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-#pragma unroll
-            for (int s = 0; s < GG::BPL; ++s) lacc[wid][4 * r + j][GG::BPL * n + s] = acc[s][j];
-        }
-    }
-    const bool any_bad = __syncthreads_or(bad);
-
-    // merge the waves' states (same rescale rule, wave order fixed)
-    const size_t state0 = ((size_t)grp * a.n_parts + part) * G;  // level-0 slot of this partition
-    __amdgpu_buffer_rsrc_t r_acc0, r_ms0;
-    if (n_parts_b > 1) {
-        r_acc0 = state_rsrc(a.acc0 + state0 * HD, (uint32_t)(G * HD * 4));
-        r_ms0 = state_rsrc(a.ms0 + state0 * 2, (uint32_t)(G * 8));
-    }
+    constexpr int kStride = kTile * kWaves;
     constexpr int Q4 = HD / 4;
-    for (int e4 = tid; e4 < G * Q4; e4 += kThreads) {
-        const int g = e4 / Q4, i4 = e4 % Q4;
-        float Mx = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) Mx = fmaxf(Mx, lM[w][g]);
-        float St = 0.0f;
-        f32x4 at = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-            const float ew = __builtin_amdgcn_exp2f(lM[w][g] - Mx);
-            St += lS[w][g] * ew;
-            at += *reinterpret_cast<const f32x4*>(&lacc[w][g][4 * i4]) * ew;
+    // The first item of a workgroup is its own index; later ones come from the
+    // ticket (offset by the grid size) when items can outnumber workgroups.
+    int item = blockIdx.x;
+    for (;;) {
+        if (item >= total) break;
+        // sequence of the item: the last b with lpre[b] <= item
+        int lo = 0, hi = a.batch;
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (lpre[mid] <= item) lo = mid;
+            else hi = mid;
         }
-        if (any_bad) at = f32x4{NAN, NAN, NAN, NAN};
-        if (n_parts_b == 1) {
-            *reinterpret_cast<f32x4*>(out_rows + (size_t)e4 * 4) = at / St;
+        // Item coordinates are wave-uniform; saying so keeps the block-table
+        // and length reads on the scalar path (a vector load would queue
+        // behind the in-flight tile loads and wait for all of them).
+        const int b = __builtin_amdgcn_readfirstlane(lo);
+        const int first_item = __builtin_amdgcn_readfirstlane(lpre[b]);
+        const int np_b = (__builtin_amdgcn_readfirstlane(lpre[b + 1]) - first_item) / a.n_kv;
+        const int rr = __builtin_amdgcn_readfirstlane(item) - first_item;
+        const int kh = rr / np_b, part = rr % np_b;
+        const int32_t* trow = a.table + (size_t)b * a.max_blocks;
+        const int t0 = part * a.part_tokens;
+        // issue the first tile's table reads together with the length read
+        int ts = t0 + kTile * wid;
+        int blk_first[2];
+        tile_blocks(trow, ts, a.kv_bs, a.max_blocks, blk_first);
+        int L = uniform_read(a.lens, b);
+        bool bad = false;
+        if (L > cap) {
+            L = cap;
+            bad = true;
+        }
+        const int t1 = min(L, t0 + a.part_tokens);
+        float* out_rows = a.out + ((size_t)b * a.n_q + (size_t)kh * G) * HD;
+
+        // Start streaming the wave's first tile before the query prologue.
+        Tile<HD> A;
+        if (ts < t1) tile_load<HD>(A, a, blk_first, kh, ts, t1, lane, bad);
+
+        quantize_q_rows<HD>(a.q + ((size_t)b * a.n_q + (size_t)kh * G) * HD, G, lq, lqsc, tid, kThreads);
+        __syncthreads();
+
+        f32x4 acc[GG::BPL];
+#pragma unroll
+        for (int s = 0; s < GG::BPL; ++s) acc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+        float M = -INFINITY, S = 0.0f;
+
+        if constexpr (PF) {
+            // Two register tiles: the next tile's loads (clamped to the current
+            // tile past the end, so they are unconditional) are in flight while
+            // this one is computed.
+            Tile<HD> B;
+            while (ts < t1) {
+                int tn = ts + kStride < t1 ? ts + kStride : ts;
+                int blk[2];
+                tile_blocks(trow, tn, a.kv_bs, a.max_blocks, blk);
+                tile_load<HD>(B, a, blk, kh, tn, t1, lane, bad);
+                tile_compute<HD>(A, lq, lqsc, a.scale_log2, acc, M, S, lane);
+                ts += kStride;
+                if (ts >= t1) break;
+                tn = ts + kStride < t1 ? ts + kStride : ts;
+                tile_blocks(trow, tn, a.kv_bs, a.max_blocks, blk);
+                tile_load<HD>(A, a, blk, kh, tn, t1, lane, bad);
+                tile_compute<HD>(B, lq, lqsc, a.scale_log2, acc, M, S, lane);
+                ts += kStride;
+            }
         } else {
-            state_store4(r_acc0, (uint32_t)e4 * 16, at);
-            if (i4 == 0) {
-                state_store1(r_ms0, (uint32_t)g * 8, Mx);
-                state_store1(r_ms0, (uint32_t)g * 8 + 4, St);
+            // One register tile per wave; latency is hidden by the other
+            // resident waves (one wave's loads overlap the others' compute).
+            while (ts < t1) {
+                tile_compute<HD>(A, lq, lqsc, a.scale_log2, acc, M, S, lane);
+                ts += kStride;
+                if (ts < t1) {
+                    int blk[2];
+                    tile_blocks(trow, ts, a.kv_bs, a.max_blocks, blk);
+                    tile_load<HD>(A, a, blk, kh, ts, t1, lane, bad);
+                }
             }
         }
-    }
-    if (n_parts_b == 1) return;
 
-    // level 1: the last arrival of this run of kMergeFan partitions merges it
-    const int run = part / kMergeFan;
-    const int run_len = min(kMergeFan, n_parts_b - run * kMergeFan);
-    const int n_runs = (n_parts_b + kMergeFan - 1) / kMergeFan;
-    wait_stores();
-    __syncthreads();
-    if (tid == 0) {
-        int* c = a.cnt0 + (size_t)grp * a.n_mid + run;
-        const int prev = __hip_atomic_fetch_add(c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const bool last = prev == run_len - 1;
-        if (last) __hip_atomic_store(c, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        lflag = last;
-    }
-    __syncthreads();
-    if (!lflag) return;
-    const size_t first = ((size_t)grp * a.n_parts + (size_t)run * kMergeFan) * G;
-    const size_t mid = ((size_t)grp * a.n_mid + run) * G;
-    merge_states<HD>(a.ms0 + first * 2, a.acc0 + first * HD, run_len, G, n_runs == 1, out_rows,
-                     a.ms1 + mid * 2, a.acc1 + mid * HD, tid);
-    if (n_runs == 1) return;
+        // wave state -> LDS: exp-sum over the four row groups, hi + lo rows
+        S = swap16_sum(S);
+        S = swap32_sum(S);
+#pragma unroll
+        for (int s = 0; s < GG::BPL; ++s) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[s][j] = swap32_sum(acc[s][j]);
+        }
+        if (lane < kHeadGroup) {
+            lM[wid][lane] = M;
+            lS[wid][lane] = S;
+        }
+        if (r_of(lane) < 2) {
+            const int r = r_of(lane), n = lane & 15;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+#pragma unroll
+                for (int s = 0; s < GG::BPL; ++s) lacc[wid][4 * r + j][GG::BPL * n + s] = acc[s][j];
+            }
+        }
+        const bool any_bad = __syncthreads_or(bad);
 
-    // level 2: the last level-1 merger merges the runs into the output
-    wait_stores();
-    __syncthreads();
-    if (tid == 0) {
-        int* c = a.cnt1 + grp;
-        const int prev = __hip_atomic_fetch_add(c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const bool last = prev == n_runs - 1;
-        if (last) __hip_atomic_store(c, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        lflag = last;
+        // merge the waves' states (same rescale rule, wave order fixed); write
+        // the output (one partition) or this partition's state
+        const size_t state0 = (((size_t)b * a.n_kv + kh) * a.n_parts + part) * G;
+        for (int e4 = tid; e4 < G * Q4; e4 += kThreads) {
+            const int g = e4 / Q4, i4 = e4 % Q4;
+            float Mx = -INFINITY;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) Mx = fmaxf(Mx, lM[w][g]);
+            float St = 0.0f;
+            f32x4 at = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) {
+                const float ew = __builtin_amdgcn_exp2f(lM[w][g] - Mx);
+                St += lS[w][g] * ew;
+                at += *reinterpret_cast<const f32x4*>(&lacc[w][g][4 * i4]) * ew;
+            }
+            if (any_bad) at = f32x4{NAN, NAN, NAN, NAN};
+            if (np_b == 1) {
+                *reinterpret_cast<f32x4*>(out_rows + (size_t)e4 * 4) = at / St;
+            } else {
+                *reinterpret_cast<f32x4*>(a.st_acc + state0 * HD + (size_t)e4 * 4) = at;
+                if (i4 == 0) *reinterpret_cast<float2*>(a.st_ms + (state0 + g) * 2) = make_float2(Mx, St);
+            }
+        }
+        // next item (the barrier also keeps LDS from being reused too early)
+        if (!a.ticket) break;
+        if (tid == 0) litem = (int)gridDim.x + __hip_atomic_fetch_add(a.ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        item = litem;
+        __syncthreads();
     }
+    if (!a.ticket) return;
+    // the last workgroup to finish resets the ticket for the next call (all
+    // others have taken their final ticket before counting themselves done)
+    if (tid == 0) {
+        const int done = __hip_atomic_fetch_add(a.ticket + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (done == (int)gridDim.x - 1) {
+            __hip_atomic_store(a.ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(a.ticket + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
+struct CombineArgs {
+    float* out;
+    const float* st_acc;
+    const float* st_ms;
+    const int32_t* lens;
+    int n_q, n_kv, group, cap, part_tokens, n_parts;
+};
+
+// Merge the partition states of one (sequence, query head) with the rescale
+// rule: M* = max M_p, S* = sum S_p 2^(M_p - M*), out = sum acc_p 2^(M_p - M*) / S*.
+// Thread (row r, slice i4) owns partitions p = r, r + R, ... and sums them in
+// increasing order; the R row sums are then added in row order, so the result
+// is deterministic.  All state loads are issued at once, together with the
+// length read (slots past the sequence's partitions are read but never used).
+template <int HD>
+__global__ __launch_bounds__(kThreads) void q8kv_combine_kernel(const CombineArgs a) {
+    constexpr int Q4 = HD / 4;          // float4 slices per head row
+    constexpr int R = kThreads / Q4;    // partitions summed in parallel
+    constexpr int PER = kMaxParts / R;  // partitions per thread at most
+    __shared__ f32x4 lpart[R][Q4];
+    __shared__ float lsp[R];
+    __shared__ float lmax[kWaves];
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid >> 6;
+    const int h = blockIdx.x % a.n_q, b = blockIdx.x / a.n_q;
+    const int kh = h / a.group, g = h % a.group;
+    const size_t first = (((size_t)b * a.n_kv + kh) * a.n_parts) * a.group + g;  // state of p = 0
+    const size_t pstride = (size_t)a.group;                                        // states per partition
+    const int i4 = tid % Q4, r = tid / Q4;
+
+    f32x4 v[PER];
+    float2 ms[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        const int p = r + k * R;
+        if (p < a.n_parts) {
+            v[k] = *reinterpret_cast<const f32x4*>(a.st_acc + (first + p * pstride) * HD + 4 * i4);
+            ms[k] = *reinterpret_cast<const float2*>(a.st_ms + (first + p * pstride) * 2);
+        }
+    }
+    const int L = min(a.lens[b], a.cap);
+    if (L <= 0) return;
+    const int np = (L + a.part_tokens - 1) / a.part_tokens;
+    if (np <= 1) return;
+
+    float mx = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < PER; ++k)
+        if (r + k * R < np) mx = fmaxf(mx, ms[k].x);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    if (lane == 0) lmax[wid] = mx;
     __syncthreads();
-    if (!lflag) return;
-    const size_t mid0 = (size_t)grp * a.n_mid * G;
-    merge_states<HD>(a.ms1 + mid0 * 2, a.acc1 + mid0 * HD, n_runs, G, true, out_rows, a.ms1 + mid0 * 2,
-                     a.acc1 + mid0 * HD, tid);
+    float Mx = lmax[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) Mx = fmaxf(Mx, lmax[w]);
+
+    f32x4 at = {0.f, 0.f, 0.f, 0.f};
+    float sp = 0.0f;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        if (r + k * R < np) {
+            const float w = __builtin_amdgcn_exp2f(ms[k].x - Mx);
+            at += v[k] * w;
+            sp += ms[k].y * w;
+        }
+    }
+    lpart[r][i4] = at;
+    if (i4 == 0) lsp[r] = sp;
+    __syncthreads();
+    if (r == 0) {
+        f32x4 t = lpart[0][i4];
+        float St = lsp[0];
+#pragma unroll
+        for (int rr = 1; rr < R; ++rr) {
+            t += lpart[rr][i4];
+            St += lsp[rr];
+        }
+        *reinterpret_cast<f32x4*>(a.out + ((size_t)b * a.n_q + h) * HD + 4 * i4) = t / St;
+    }
 }
 
 // ----------------------------------------------------------------------------
@@ -807,18 +864,17 @@ int hip_fail(hipError_t e, const char* what) {
     return fail(Q8KV_EHIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-// Library-owned split-context workspace of one (device, stream): merge states
-// (no initialisation needed) and, in a separate allocation that nothing else
-// writes, the arrival counters, which are zeroed when allocated and which
-// every call leaves at zero again.
+// Library-owned split-context workspace of one (device, stream): the
+// partition states written by the decode kernel and read by the combine
+// kernel (no initialisation needed).
 struct Workspace {
     void* ptr = nullptr;
     size_t bytes = 0;
-    int* counters = nullptr;
-    size_t counter_bytes = 0;
+    int* ticket = nullptr;  // [2] zeroed at allocation, left at zero by every call
 };
 std::mutex g_mu;
 std::map<std::pair<int, void*>, Workspace> g_ws;
+std::map<std::pair<int, int>, int> g_resident;  // (device, hd) -> resident decode workgroups
 
 bool valid_hd(int hd) { return hd == 64 || hd == 128 || hd == 256; }
 bool valid_kv_bs(int bs) { return bs == 16 || bs == 32 || bs == 64 || bs == 128 || bs == 256; }
@@ -833,17 +889,19 @@ int check_cache_shape(int num_blocks, int n_kv, int hd, int kv_bs) {
 }
 
 // Partition plan: a pure function of the shapes, so results never depend on
-// the device.  Aim for about 768 workgroups over the longest possible context
-// (3 resident 4-wave workgroups per compute unit on a 256-CU part) with
-// partitions that are multiples of 128 tokens (every wave gets the same
-// number of 32-token tiles), from 128 to 2048 tokens, and never more than
-// kMaxParts partitions per sequence.
+// the device.  When the longest possible step spreads over about 512 work
+// items of at most 2048 tokens, use that (one item per workgroup: every
+// resident workgroup streams one long partition).  Larger steps use
+// 1024-token partitions and many items per workgroup, which the persistent
+// grid balances to within one item.  Partitions are multiples of 128 tokens
+// (every wave gets the same number of 32-token tiles) and a sequence has at
+// most kMaxParts of them.
 void plan(int batch, int n_kv, int max_tokens, int* part_tokens, int* n_parts) {
     const long long units = (long long)batch * n_kv * max_tokens;
-    long long pt = (units + 767) / 768;
+    long long pt = (units + 511) / 512;
+    if (pt > 2048) pt = 1024;
     pt = (pt + 127) / 128 * 128;
     if (pt < 128) pt = 128;
-    if (pt > 2048) pt = 2048;
     const long long min_pt = ((max_tokens + kMaxParts - 1) / kMaxParts + 127) / 128 * 128;
     if (pt < min_pt) pt = min_pt;
     *part_tokens = (int)pt;
@@ -852,43 +910,24 @@ void plan(int batch, int n_kv, int max_tokens, int* part_tokens, int* n_parts) {
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
-// Offsets of the merge states inside the workspace.
-struct WsLayout {
-    size_t acc0, ms0, acc1, ms1, bytes;
-};
-
-WsLayout ws_layout(size_t groups, int np, int n_mid, int G, int hd) {
-    WsLayout l;
-    size_t off = 0;
-    l.acc0 = off; off = align256(off + groups * np * G * hd * sizeof(float));
-    l.ms0 = off;  off = align256(off + groups * np * G * 2 * sizeof(float));
-    l.acc1 = off; off = align256(off + groups * n_mid * G * hd * sizeof(float));
-    l.ms1 = off;  off = align256(off + groups * n_mid * G * 2 * sizeof(float));
-    l.bytes = off;
-    return l;
-}
-
-int grow(void** ptr, size_t* have, size_t need, hipStream_t st, bool zero) {
-    if (*have >= need) return Q8KV_OK;
-    hipError_t e;
-    if (*ptr) {
-        e = hipStreamSynchronize(st);
-        if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
-        e = hipFree(*ptr);
-        *ptr = nullptr;
-        *have = 0;
-        if (e != hipSuccess) return hip_fail(e, "hipFree");
+// Workgroups of the (single-buffer) decode kernel that fit on the device at once.
+int resident_workgroups(int dev, int hd, int* out) {
+    std::lock_guard<std::mutex> lock(g_mu);
+    auto it = g_resident.find({dev, hd});
+    if (it != g_resident.end()) {
+        *out = it->second;
+        return Q8KV_OK;
     }
-    e = hipMalloc(ptr, need);
-    if (e != hipSuccess) {
-        *ptr = nullptr;
-        return fail(Q8KV_ENOMEM, "hipMalloc of %zu workspace bytes: %s", need, hipGetErrorString(e));
-    }
-    if (zero) {
-        e = hipMemsetAsync(*ptr, 0, need, st);
-        if (e != hipSuccess) return hip_fail(e, "hipMemsetAsync");
-    }
-    *have = need;
+    int cus = 0, per_cu = 0;
+    hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+    const void* k = hd == 64 ? reinterpret_cast<const void*>(q8kv_decode_kernel<64, false>)
+                  : hd == 128 ? reinterpret_cast<const void*>(q8kv_decode_kernel<128, false>)
+                              : reinterpret_cast<const void*>(q8kv_decode_kernel<256, false>);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kThreads, 0);
+    if (e != hipSuccess) return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
+    *out = std::max(1, cus * std::max(1, per_cu));
+    g_resident[{dev, hd}] = *out;
     return Q8KV_OK;
 }
 
@@ -899,6 +938,7 @@ int decode_impl(float* out, const float* q, const int8_t* kp, const int8_t* vp, 
     if (!out || !q || !kp || !vp || !ks || !vs || !table || !lens)
         return fail(Q8KV_ENULL, "a tensor pointer is NULL");
     if (batch <= 0 || n_q <= 0) return fail(Q8KV_EINVAL, "batch (%d) and n_q_heads (%d) must be positive", batch, n_q);
+    if (batch > kMaxBatch) return fail(Q8KV_EINVAL, "batch (%d) exceeds %d sequences per call", batch, kMaxBatch);
     int rc = check_cache_shape(num_blocks, n_kv, hd, kv_bs);
     if (rc) return rc;
     if (n_q % n_kv) return fail(Q8KV_EINVAL, "n_q_heads (%d) is not a multiple of n_kv_heads (%d)", n_q, n_kv);
@@ -918,43 +958,91 @@ int decode_impl(float* out, const float* q, const int8_t* kp, const int8_t* vp, 
         if (np > kMaxParts)
             return fail(Q8KV_EINVAL, "part_tokens %d splits %d tokens into %d > %d partitions", pt, max_tokens, np, kMaxParts);
     }
-    const long long grid = (long long)batch * n_kv * np;
-    if (grid > INT_MAX) return fail(Q8KV_EINVAL, "decode grid of %lld workgroups is too large", grid);
-    const int n_mid = (np + kMergeFan - 1) / kMergeFan;
+    const long long items = (long long)batch * n_kv * np;
+    if ((long long)batch * n_q > INT_MAX || items > INT_MAX) return fail(Q8KV_EINVAL, "decode shape too large");
 
     hipStream_t st = static_cast<hipStream_t>(stream);
-    DecodeArgs da{out, q, kp, vp, ks, vs, table, lens, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
-                  max_blocks, num_blocks, n_q, n_kv, kv_bs, G, pt, np, n_mid, scale * kLog2e};
-    if (np > 1) {
-        const size_t groups = (size_t)batch * n_kv;
-        const WsLayout lay = ws_layout(groups, np, n_mid, G, hd);
-        int dev = 0;
-        hipError_t e = hipGetDevice(&dev);
-        if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    int resident = 0;
+    rc = resident_workgroups(dev, hd, &resident);
+    if (rc) return rc;
+    const unsigned grid = (unsigned)std::min<long long>(items, resident);
+    DecodeArgs da{out, q, kp, vp, ks, vs, table, lens, nullptr, nullptr, nullptr,
+                  batch, max_blocks, num_blocks, n_q, n_kv, kv_bs, G, pt, np, scale * kLog2e};
+    if (items > (long long)grid) {
         std::lock_guard<std::mutex> lock(g_mu);
         Workspace& w = g_ws[{dev, stream}];
-        rc = grow(&w.ptr, &w.bytes, lay.bytes, st, false);
-        if (rc) return rc;
-        const size_t cnt_bytes = (groups * n_mid + groups) * sizeof(int);
-        void* cptr = w.counters;
-        rc = grow(&cptr, &w.counter_bytes, cnt_bytes, st, true);
-        w.counters = static_cast<int*>(cptr);
-        if (rc) return rc;
-        char* base = static_cast<char*>(w.ptr);
-        da.acc0 = reinterpret_cast<float*>(base + lay.acc0);
-        da.ms0 = reinterpret_cast<float*>(base + lay.ms0);
-        da.acc1 = reinterpret_cast<float*>(base + lay.acc1);
-        da.ms1 = reinterpret_cast<float*>(base + lay.ms1);
-        da.cnt0 = w.counters;
-        da.cnt1 = w.counters + groups * n_mid;
+        if (!w.ticket) {
+            void* t = nullptr;
+            e = hipMalloc(&t, 256);
+            if (e != hipSuccess) return fail(Q8KV_ENOMEM, "hipMalloc of the work ticket: %s", hipGetErrorString(e));
+            e = hipMemsetAsync(t, 0, 256, st);
+            if (e != hipSuccess) {
+                (void)hipFree(t);
+                return hip_fail(e, "hipMemsetAsync");
+            }
+            w.ticket = static_cast<int*>(t);
+        }
+        da.ticket = w.ticket;
     }
-    switch (hd) {
-        case 64: hipLaunchKernelGGL(q8kv_decode_kernel<64>, dim3((unsigned)grid), dim3(kThreads), 0, st, da); break;
-        case 128: hipLaunchKernelGGL(q8kv_decode_kernel<128>, dim3((unsigned)grid), dim3(kThreads), 0, st, da); break;
-        default: hipLaunchKernelGGL(q8kv_decode_kernel<256>, dim3((unsigned)grid), dim3(kThreads), 0, st, da); break;
+    if (np > 1) {
+        const size_t n_state = (size_t)batch * n_kv * np * G;
+        const size_t acc_bytes = align256(n_state * hd * sizeof(float));
+        const size_t need = acc_bytes + n_state * 2 * sizeof(float);
+        std::lock_guard<std::mutex> lock(g_mu);
+        Workspace& w = g_ws[{dev, stream}];
+        if (w.bytes < need) {
+            if (w.ptr) {
+                e = hipStreamSynchronize(st);
+                if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+                e = hipFree(w.ptr);
+                w.ptr = nullptr;
+                w.bytes = 0;
+                if (e != hipSuccess) return hip_fail(e, "hipFree");
+            }
+            e = hipMalloc(&w.ptr, need);
+            if (e != hipSuccess) {
+                w.ptr = nullptr;
+                return fail(Q8KV_ENOMEM, "hipMalloc of %zu workspace bytes: %s", need, hipGetErrorString(e));
+            }
+            w.bytes = need;
+        }
+        da.st_acc = static_cast<float*>(w.ptr);
+        da.st_ms = reinterpret_cast<float*>(static_cast<char*>(w.ptr) + acc_bytes);
     }
-    hipError_t e = hipGetLastError();
+    // every item in its own workgroup, at most two per compute unit: prefetch
+    int cus = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+    const bool pf = items <= (long long)grid && grid <= 2u * (unsigned)cus;
+    if (pf) {
+        switch (hd) {
+            case 64: hipLaunchKernelGGL((q8kv_decode_kernel<64, true>), dim3(grid), dim3(kThreads), 0, st, da); break;
+            case 128: hipLaunchKernelGGL((q8kv_decode_kernel<128, true>), dim3(grid), dim3(kThreads), 0, st, da); break;
+            default: hipLaunchKernelGGL((q8kv_decode_kernel<256, true>), dim3(grid), dim3(kThreads), 0, st, da); break;
+        }
+    } else {
+        switch (hd) {
+            case 64: hipLaunchKernelGGL((q8kv_decode_kernel<64, false>), dim3(grid), dim3(kThreads), 0, st, da); break;
+            case 128: hipLaunchKernelGGL((q8kv_decode_kernel<128, false>), dim3(grid), dim3(kThreads), 0, st, da); break;
+            default: hipLaunchKernelGGL((q8kv_decode_kernel<256, false>), dim3(grid), dim3(kThreads), 0, st, da); break;
+        }
+    }
+    e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
+    if (np > 1) {
+        CombineArgs ca{out, da.st_acc, da.st_ms, lens, n_q, n_kv, G, max_tokens, pt, np};
+        const unsigned cgrid = (unsigned)(batch * n_q);
+        switch (hd) {
+            case 64: hipLaunchKernelGGL(q8kv_combine_kernel<64>, dim3(cgrid), dim3(kThreads), 0, st, ca); break;
+            case 128: hipLaunchKernelGGL(q8kv_combine_kernel<128>, dim3(cgrid), dim3(kThreads), 0, st, ca); break;
+            default: hipLaunchKernelGGL(q8kv_combine_kernel<256>, dim3(cgrid), dim3(kThreads), 0, st, ca); break;
+        }
+        e = hipGetLastError();
+        if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
+    }
     return Q8KV_OK;
 }
 
@@ -1032,11 +1120,11 @@ int q8kv_release(void) {
     int cur = 0;
     if (!g_ws.empty() && hipGetDevice(&cur) != hipSuccess) cur = -1;
     for (auto& kv : g_ws) {
-        if (!kv.second.ptr && !kv.second.counters) continue;
+        if (!kv.second.ptr && !kv.second.ticket) continue;
         hipError_t e = hipSetDevice(kv.first.first);
         if (e == hipSuccess) e = hipDeviceSynchronize();
         if (e == hipSuccess && kv.second.ptr) e = hipFree(kv.second.ptr);
-        if (e == hipSuccess && kv.second.counters) e = hipFree(kv.second.counters);
+        if (e == hipSuccess && kv.second.ticket) e = hipFree(kv.second.ticket);
         if (e != hipSuccess && rc == Q8KV_OK) rc = hip_fail(e, "releasing workspace");
     }
     g_ws.clear();
