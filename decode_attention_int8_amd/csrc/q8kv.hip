@@ -174,17 +174,35 @@ __device__ __forceinline__ void load_q_operand(QOperand<HD>& Q, const int8_t* lq
     }
 }
 
-// K operand: lane l = 16 r + n carries bytes [64p + 16r, +16) of the K row of
-// sub-tile token n (row = base + min(n, nvalid - 1)).
+// Page byte order.  Each page (one physical block of one kv head, kv_bs
+// rows of HD bytes) is a run of 16-row sub-tiles of 16 * HD bytes, and each
+// sub-tile is HD / 64 chunks of 1 KB in which lane slot l (0..63) owns bytes
+// [16 l, 16 l + 16).  One dwordx4 load per lane therefore reads a whole chunk
+// with consecutive lanes on consecutive 16-byte pieces, and what a lane gets
+// is exactly its matrix-core operand:
+//   K chunk c, slot l = 16 r + n: row n, columns [64 c + 16 r, +16);
+//   V slot l = 16 r + n owns rows 4r .. 4r+3, columns [BPL n, BPL n + BPL)
+//     (BPL = HD / 16); its 4 BPL bytes in (row, column) order are cut into
+//     16-byte pieces, piece c going to chunk c.
+__device__ __forceinline__ size_t k_swizzle(int row, int col) {
+    return (size_t)(col >> 6) * 1024 + 16 * (16 * ((col & 63) >> 4) + row) + (col & 15);
+}
+template <int HD>
+__device__ __forceinline__ size_t v_swizzle(int row, int col) {
+    constexpr int BPL = Geo<HD>::BPL;
+    const int slot = 16 * (row >> 2) + col / BPL;
+    const int qb = (row & 3) * BPL + col % BPL;  // byte of the slot's 4 BPL
+    return (size_t)(qb >> 4) * 1024 + 16 * slot + (qb & 15);
+}
+
+// K operands of one sub-tile whose first row is base_row: chunk p is the A
+// operand of the pair-p MFMA (lane 16 r + n: row n, bytes [64p + 16r, +16)).
 template <int HD>
 __device__ __forceinline__ void load_k_subtile(i32x4 (&kop)[Geo<HD>::NPAIR], const int8_t* __restrict__ kp,
-                                               size_t base_row, int nvalid, int lane) {
-    const int r = lane >> 4, n = lane & 15;
-    const int tk = min(n, nvalid - 1);
+                                               size_t base_row, int lane) {
     const int8_t* sub = kp + base_row * HD;  // wave-uniform
-    const uint32_t off = (uint32_t)(tk * HD + 16 * r);
 #pragma unroll
-    for (int p = 0; p < Geo<HD>::NPAIR; ++p) kop[p] = stream_load<i32x4>(sub + off + 64 * p);
+    for (int p = 0; p < Geo<HD>::NPAIR; ++p) kop[p] = stream_load<i32x4>(sub + 1024 * p + 16 * lane);
 }
 
 // int32 block dots of one sub-tile: c[p][j] = dot(token 4r+j, head g, block 2p+bp).
@@ -196,10 +214,18 @@ __device__ __forceinline__ void qk_mfma(i32x4 (&c)[Geo<HD>::NPAIR], const i32x4 
         c[p] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop[p], Q.op[p], i32x4{0, 0, 0, 0}, 0, 0, 0);
 }
 
-// int8 V bytes -> f16 P.V operands.  raw[k][d] holds bytes [BPL n + 4d, +4) of
-// the V row in k-slot k; out[b] gets element k = V[k-slot k][BPL n + 4d + b] as f16.
-// Each f16 comes from one SDWA conversion of a sign-extended byte (exact for
-// int8), written into the low or high half of its destination dword.
+// int8 V bytes -> f16 P.V operands.  The lane's V bytes of a tile are the
+// chunks v[st][c] of its two sub-tiles; k-slot k = 4 st + j is row 4r + j of
+// sub-tile st, and dword d of that row's BPL bytes is dword j DPT + d of the
+// lane's bytes of the sub-tile.  out[b] gets element k = V[k-slot k][BPL n +
+// 4d + b] as f16.  Each f16 comes from one SDWA conversion of a sign-extended
+// byte (exact for int8), written into the low or high half of its dword.
+template <int HD>
+__device__ __forceinline__ uint32_t v_raw(const u32x4 (&v)[2][Geo<HD>::NPAIR], int k, int d) {
+    const int st = k >> 2, w = (k & 3) * Geo<HD>::DPT + d;
+    return v[st][w >> 2][w & 3];
+}
+
 template <int B>
 __device__ __forceinline__ uint32_t i8pair_to_f16x2(uint32_t x0, uint32_t x1) {
     uint32_t r;
@@ -219,15 +245,16 @@ __device__ __forceinline__ uint32_t i8pair_to_f16x2(uint32_t x0, uint32_t x1) {
     return r;
 }
 
-template <int DPT>
-__device__ __forceinline__ void v_dword_to_f16(const uint32_t (&raw)[8][DPT], int d, f16x8 (&out)[4]) {
+template <int HD>
+__device__ __forceinline__ void v_dword_to_f16(const u32x4 (&vch)[2][Geo<HD>::NPAIR], int d, f16x8 (&out)[4]) {
     u32x4 v0, v1, v2, v3;
 #pragma unroll
     for (int k2 = 0; k2 < 4; ++k2) {
-        v0[k2] = i8pair_to_f16x2<0>(raw[2 * k2][d], raw[2 * k2 + 1][d]);
-        v1[k2] = i8pair_to_f16x2<1>(raw[2 * k2][d], raw[2 * k2 + 1][d]);
-        v2[k2] = i8pair_to_f16x2<2>(raw[2 * k2][d], raw[2 * k2 + 1][d]);
-        v3[k2] = i8pair_to_f16x2<3>(raw[2 * k2][d], raw[2 * k2 + 1][d]);
+        const uint32_t x0 = v_raw<HD>(vch, 2 * k2, d), x1 = v_raw<HD>(vch, 2 * k2 + 1, d);
+        v0[k2] = i8pair_to_f16x2<0>(x0, x1);
+        v1[k2] = i8pair_to_f16x2<1>(x0, x1);
+        v2[k2] = i8pair_to_f16x2<2>(x0, x1);
+        v3[k2] = i8pair_to_f16x2<3>(x0, x1);
     }
     out[0] = __builtin_bit_cast(f16x8, v0);
     out[1] = __builtin_bit_cast(f16x8, v1);
@@ -235,34 +262,16 @@ __device__ __forceinline__ void v_dword_to_f16(const uint32_t (&raw)[8][DPT], in
     out[3] = __builtin_bit_cast(f16x8, v3);
 }
 
-template <int N>
-__device__ __forceinline__ void load_dwords(uint32_t (&d)[N], const int8_t* p) {
-    if constexpr (N == 1) {
-        d[0] = stream_load<uint32_t>(p);
-    } else if constexpr (N == 2) {
-        u32x2 v = stream_load<u32x2>(p);
-        d[0] = v.x;
-        d[1] = v.y;
-    } else {
-        u32x4 v = stream_load<u32x4>(p);
-        d[0] = v.x;
-        d[1] = v.y;
-        d[2] = v.z;
-        d[3] = v.w;
-    }
-}
-
 // ----------------------------------------------------------------------------
 // decode kernel
 
-// The decode grid is persistent: each workgroup takes work items
-// (sequence b, kv head kh, token partition p) from an atomic ticket until none
-// are left, so no workgroup idles while work remains.  Items are numbered
-// through an exclusive prefix sum of n_kv * ceil(L / pt) items per sequence
-// built in LDS from seq_lens.  An item's arithmetic does not depend on which
-// workgroup runs it, so results are deterministic.  A sequence with one partition
-// writes its output directly; longer ones store each partition's state
-// (M, S, acc) and q8kv_combine_kernel merges them in partition order.
+// A work item is (sequence b, kv head kh, token partition p).  When the
+// shape's items fit on the device at once, each has its own workgroup;
+// otherwise a persistent grid takes them from an atomic ticket (see
+// GridMode).  An item's arithmetic does not depend on which workgroup runs
+// it, so results are deterministic.  A sequence with one partition writes
+// its output directly; longer ones store each partition's state (M, S, acc)
+// and q8kv_combine_kernel merges them in partition order.
 constexpr int kMaxBatch = 2048;   // sequences per call (LDS prefix sums)
 constexpr int kMaxParts = 256;    // partitions per sequence (combine LDS)
 
@@ -283,22 +292,22 @@ struct DecodeArgs {
     float scale_log2;  // softmax scale * log2(e)
 };
 
-// Registers of one 32-token tile: K operands of both sub-tiles, the V bytes
-// of the lane's 8 k-slots, and the K/V scales of tile token (lane & 31) --
-// a lane fetches the scales of its own tokens from their owners.
+// Registers of one 32-token tile: the K and V chunks of both sub-tiles and
+// the K/V scales of the lane's rows 4r..4r+3 of each sub-tile (one 16-byte
+// load, shared by the 16 lanes of a row group).
 template <int HD>
 struct Tile {
     i32x4 k[2][Geo<HD>::NPAIR];
-    float ks, vs;
-    uint32_t v[8][Geo<HD>::DPT];
+    u32x4 v[2][Geo<HD>::NPAIR];
+    f32x4 ks[2], vs[2];
     int nval[2];  // valid tokens of each 16-token sub-tile (wave-uniform)
 };
 
 // Issue the loads of the tile starting at token ts (< t1) of sequence b.
 // Partitions start on multiples of 32 and kv_bs is a multiple of 16, so each
-// 16-token sub-tile lies inside one page.  An empty second sub-tile reuses
-// the first one's page, so no table entry past the sequence is read; rows
-// past t1 are redirected to the last valid row of their sub-tile.
+// 16-token sub-tile lies inside one page and is read whole (rows past t1 are
+// masked in tile_compute).  An empty second sub-tile re-reads the first one,
+// so no table entry past the sequence is read.
 // Wave-uniform read of a table that the kernel never writes, through the
 // constant address space so that it is a scalar load: a vector load would
 // queue behind the in-flight tile loads and wait for all of them.
@@ -318,38 +327,22 @@ __device__ __forceinline__ void tile_blocks(const int32_t* trow, int ts, int kv_
 template <int HD>
 __device__ __forceinline__ void tile_load(Tile<HD>& T, const DecodeArgs& a, const int (&tblk)[2], int kh,
                                           int ts, int t1, int lane, bool& bad) {
-    using GG = Geo<HD>;
-    const int r = lane >> 4, n = lane & 15;
-    size_t base[2];
-    int neff[2];
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
         T.nval[st] = min(max(t1 - (ts + kSub * st), 0), kSub);
         const int tst = T.nval[st] > 0 ? ts + kSub * st : ts;
-        neff[st] = T.nval[st] > 0 ? T.nval[st] : T.nval[0];
         int blk = (st == 1 && T.nval[1] > 0) ? tblk[1] : tblk[0];
         if ((unsigned)blk >= (unsigned)a.num_blocks) {
             bad = true;
             blk = 0;
         }
-        base[st] = ((size_t)blk * a.n_kv + kh) * a.kv_bs + (size_t)(tst % a.kv_bs);
-    }
-    {
-        // scales of tile token (lane & 31): sub-tile (lane >> 4) & 1, row lane & 15
-        const int st = (lane >> 4) & 1;
-        const size_t srow = (st ? base[1] : base[0]) + (size_t)min(lane & 15, (st ? neff[1] : neff[0]) - 1);
-        T.ks = stream_load<float>(a.ks + srow);
-        T.vs = stream_load<float>(a.vs + srow);
-    }
+        const size_t base = ((size_t)blk * a.n_kv + kh) * a.kv_bs + (size_t)(tst % a.kv_bs);
+        T.ks[st] = stream_load<f32x4>(a.ks + base + 4 * (lane >> 4));
+        T.vs[st] = stream_load<f32x4>(a.vs + base + 4 * (lane >> 4));
+        load_k_subtile<HD>(T.k[st], a.kp, base, lane);
+        const int8_t* vsub = a.vp + base * HD;  // wave-uniform
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-        load_k_subtile<HD>(T.k[st], a.kp, base[st], neff[st], lane);
-        const int8_t* vsub = a.vp + base[st] * HD;  // wave-uniform
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int tv = min(4 * r + j, neff[st] - 1);
-            load_dwords<GG::DPT>(T.v[4 * st + j], vsub + (uint32_t)(tv * HD + GG::BPL * n));
-        }
+        for (int c = 0; c < Geo<HD>::NPAIR; ++c) T.v[st][c] = stream_load<u32x4>(vsub + 1024 * c + 16 * lane);
     }
 }
 
@@ -376,7 +369,7 @@ __device__ __forceinline__ void tile_compute(const Tile<HD>& T, const int8_t* lq
 #pragma unroll
             for (int p = 0; p < GG::NPAIR; ++p) part_s += (float)c[p][j] * Q.scl[p];
             const float full = part_s + dpp_row_ror8(part_s);  // add the other block parity
-            const float ksj = lane_read(T.ks, 16 * st + 4 * r + j);
+            const float ksj = T.ks[st][j];
             const float sv = full * ksj;
             sc[st][j] = (4 * r + j) < T.nval[st] ? sv : -INFINITY;
             mx = fmaxf(mx, sc[st][j]);
@@ -396,8 +389,7 @@ __device__ __forceinline__ void tile_compute(const Tile<HD>& T, const int8_t* lq
         for (int j = 0; j < 4; ++j) {
             const float w = __builtin_amdgcn_exp2f(sc[st][j] - m_new);
             wsum += w;
-            // ds_bpermute must run with every lane active: fetch, then select
-            const float vsj = lane_read(T.vs, 16 * st + 4 * r + j);
+            const float vsj = T.vs[st][j];
             const float W = (4 * r + j) < T.nval[st] ? w * vsj : 0.0f;
             const _Float16 hi = (_Float16)W;
             const _Float16 lo = (_Float16)(W - (float)hi);
@@ -425,7 +417,7 @@ __device__ __forceinline__ void tile_compute(const Tile<HD>& T, const int8_t* lq
 #pragma unroll
     for (int d = 0; d < GG::DPT; ++d) {
         f16x8 bv[4];
-        v_dword_to_f16(T.v, d, bv);
+        v_dword_to_f16<HD>(T.v, d, bv);
 #pragma unroll
         for (int b = 0; b < 4; ++b)
             acc[4 * d + b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, bv[b], acc[4 * d + b], 0, 0, 0);
@@ -439,21 +431,28 @@ __device__ __forceinline__ int seq_items(int L, int cap, int pt, int n_kv) {
     return L > 0 ? n_kv * ((L + pt - 1) / pt) : 0;
 }
 
-// PF: each wave keeps two register tiles and loads the next while computing
-// the current one (for grids of at most two workgroups per compute unit,
-// where registers are not what limits occupancy).  Occupancy asked of the
-// register allocator: 3 waves per SIMD fits hd 64 and 128 without spills
-// (single buffer), 2 with prefetch; hd 256 keeps a whole register file.
-template <int HD, bool PF>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(HD == 256 ? 1 : (PF ? 2 : 3)))) void
+// Grid modes.  kPersistent: fewer workgroups than items; items are numbered
+// through an exclusive prefix sum of n_kv * ceil(L / pt) per sequence built in
+// LDS from seq_lens, and each workgroup takes its next item from an atomic
+// ticket.  kStatic: one workgroup per (sequence, kv head, partition) slot of
+// the shape's upper bound, read straight off blockIdx; a slot past its
+// sequence's end exits at once.  Each wave holds one register tile; latency
+// is hidden by the other resident waves (one wave's loads overlap the
+// others' compute).  3 waves per SIMD fit hd 64 and 128 without spills; hd
+// 256 keeps a whole register file.
+enum GridMode { kPersistent = 0, kStatic = 1 };
+
+template <int HD, int MODE>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(HD == 256 ? 1 : 3))) void
 q8kv_decode_kernel(const DecodeArgs a) {
     using GG = Geo<HD>;
+    constexpr bool STATIC = MODE == kStatic;
     __shared__ __attribute__((aligned(16))) int8_t lq[kHeadGroup * HD];
     __shared__ float lqsc[kHeadGroup * GG::NB];
     __shared__ float lM[kWaves][kHeadGroup];
     __shared__ float lS[kWaves][kHeadGroup];
     __shared__ float lacc[kWaves][kHeadGroup][HD];
-    __shared__ int lpre[kMaxBatch + 1];  // exclusive prefix of items per sequence
+    __shared__ int lpre[STATIC ? 1 : kMaxBatch + 1];  // exclusive prefix of items per sequence
     __shared__ int lscan[kWaves];
     __shared__ int litem;
 
@@ -463,35 +462,38 @@ q8kv_decode_kernel(const DecodeArgs a) {
     const int G = a.group;
     const int cap = a.max_blocks * a.kv_bs;
 
-    // ---- item numbering: each thread sums a contiguous chunk of sequences;
-    // the chunk totals are scanned with wave shuffles and one LDS round
-    const int per = (a.batch + kThreads - 1) / kThreads;
-    const int c0 = min(tid * per, a.batch), c1 = min(c0 + per, a.batch);
-    int local = 0;
-    for (int bb = c0; bb < c1; ++bb) local += seq_items(a.lens[bb], cap, a.part_tokens, a.n_kv);
-    int incl = local;
+    int total = 0;
+    if constexpr (!STATIC) {
+        // item numbering: each thread sums a contiguous chunk of sequences;
+        // the chunk totals are scanned with wave shuffles and one LDS round
+        const int per = (a.batch + kThreads - 1) / kThreads;
+        const int c0 = min(tid * per, a.batch), c1 = min(c0 + per, a.batch);
+        int local = 0;
+        for (int bb = c0; bb < c1; ++bb) local += seq_items(a.lens[bb], cap, a.part_tokens, a.n_kv);
+        int incl = local;
 #pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        const int v = __shfl_up(incl, off);
-        if (lane >= off) incl += v;
-    }
-    if (lane == kWave - 1) lscan[wid] = incl;
-    __syncthreads();
-    int run = incl - local;
-    for (int w = 0; w < wid; ++w) run += lscan[w];
-    for (int bb = c0; bb < c1; ++bb) {
-        lpre[bb] = run;
-        run += seq_items(a.lens[bb], cap, a.part_tokens, a.n_kv);
-    }
-    if (tid == kThreads - 1) lpre[a.batch] = run;
-    __syncthreads();
-    const int total = lpre[a.batch];
+        for (int off = 1; off < kWave; off <<= 1) {
+            const int v = __shfl_up(incl, off);
+            if (lane >= off) incl += v;
+        }
+        if (lane == kWave - 1) lscan[wid] = incl;
+        __syncthreads();
+        int run = incl - local;
+        for (int w = 0; w < wid; ++w) run += lscan[w];
+        for (int bb = c0; bb < c1; ++bb) {
+            lpre[bb] = run;
+            run += seq_items(a.lens[bb], cap, a.part_tokens, a.n_kv);
+        }
+        if (tid == kThreads - 1) lpre[a.batch] = run;
+        __syncthreads();
+        total = lpre[a.batch];
 
-    // empty sequences get zero rows (R11); sequence b is zeroed by workgroup b mod grid
-    for (int bb = blockIdx.x; bb < a.batch; bb += gridDim.x) {
-        if (lpre[bb + 1] == lpre[bb]) {
-            float* o = a.out + (size_t)bb * a.n_q * HD;
-            for (int e = tid; e < a.n_q * HD; e += kThreads) o[e] = 0.0f;
+        // empty sequences get zero rows; sequence b is zeroed by workgroup b mod grid
+        for (int bb = blockIdx.x; bb < a.batch; bb += gridDim.x) {
+            if (lpre[bb + 1] == lpre[bb]) {
+                float* o = a.out + (size_t)bb * a.n_q * HD;
+                for (int e = tid; e < a.n_q * HD; e += kThreads) o[e] = 0.0f;
+            }
         }
     }
 
@@ -501,22 +503,31 @@ q8kv_decode_kernel(const DecodeArgs a) {
     // ticket (offset by the grid size) when items can outnumber workgroups.
     int item = blockIdx.x;
     for (;;) {
-        if (item >= total) break;
-        // sequence of the item: the last b with lpre[b] <= item
-        int lo = 0, hi = a.batch;
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (lpre[mid] <= item) lo = mid;
-            else hi = mid;
-        }
         // Item coordinates are wave-uniform; saying so keeps the block-table
         // and length reads on the scalar path (a vector load would queue
         // behind the in-flight tile loads and wait for all of them).
-        const int b = __builtin_amdgcn_readfirstlane(lo);
-        const int first_item = __builtin_amdgcn_readfirstlane(lpre[b]);
-        const int np_b = (__builtin_amdgcn_readfirstlane(lpre[b + 1]) - first_item) / a.n_kv;
-        const int rr = __builtin_amdgcn_readfirstlane(item) - first_item;
-        const int kh = rr / np_b, part = rr % np_b;
+        int b, kh, part, first_item = 0, np_b = 0;
+        if constexpr (STATIC) {
+            const int id = __builtin_amdgcn_readfirstlane(item);
+            part = id % a.n_parts;
+            kh = (id / a.n_parts) % a.n_kv;
+            b = id / (a.n_parts * a.n_kv);
+        } else {
+            if (item >= total) break;
+            // sequence of the item: the last b with lpre[b] <= item
+            int lo = 0, hi = a.batch;
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (lpre[mid] <= item) lo = mid;
+                else hi = mid;
+            }
+            b = __builtin_amdgcn_readfirstlane(lo);
+            first_item = __builtin_amdgcn_readfirstlane(lpre[b]);
+            np_b = (__builtin_amdgcn_readfirstlane(lpre[b + 1]) - first_item) / a.n_kv;
+            const int rr = __builtin_amdgcn_readfirstlane(item) - first_item;
+            kh = rr / np_b;
+            part = rr % np_b;
+        }
         const int32_t* trow = a.table + (size_t)b * a.max_blocks;
         const int t0 = part * a.part_tokens;
         // issue the first tile's table reads together with the length read
@@ -529,8 +540,18 @@ q8kv_decode_kernel(const DecodeArgs a) {
             L = cap;
             bad = true;
         }
-        const int t1 = min(L, t0 + a.part_tokens);
         float* out_rows = a.out + ((size_t)b * a.n_q + (size_t)kh * G) * HD;
+        if constexpr (STATIC) {
+            // a slot past the sequence's end has nothing to do; an empty
+            // sequence's rows are zeroed by its partition-0 slots
+            if (t0 >= L) {
+                if (part == 0)
+                    for (int e = tid; e < G * HD; e += kThreads) out_rows[e] = 0.0f;
+                return;
+            }
+            np_b = (L + a.part_tokens - 1) / a.part_tokens;
+        }
+        const int t1 = min(L, t0 + a.part_tokens);
 
         // Start streaming the wave's first tile before the query prologue.
         Tile<HD> A;
@@ -544,36 +565,13 @@ q8kv_decode_kernel(const DecodeArgs a) {
         for (int s = 0; s < GG::BPL; ++s) acc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
         float M = -INFINITY, S = 0.0f;
 
-        if constexpr (PF) {
-            // Two register tiles: the next tile's loads (clamped to the current
-            // tile past the end, so they are unconditional) are in flight while
-            // this one is computed.
-            Tile<HD> B;
-            while (ts < t1) {
-                int tn = ts + kStride < t1 ? ts + kStride : ts;
+        while (ts < t1) {
+            tile_compute<HD>(A, lq, lqsc, a.scale_log2, acc, M, S, lane);
+            ts += kStride;
+            if (ts < t1) {
                 int blk[2];
-                tile_blocks(trow, tn, a.kv_bs, a.max_blocks, blk);
-                tile_load<HD>(B, a, blk, kh, tn, t1, lane, bad);
-                tile_compute<HD>(A, lq, lqsc, a.scale_log2, acc, M, S, lane);
-                ts += kStride;
-                if (ts >= t1) break;
-                tn = ts + kStride < t1 ? ts + kStride : ts;
-                tile_blocks(trow, tn, a.kv_bs, a.max_blocks, blk);
-                tile_load<HD>(A, a, blk, kh, tn, t1, lane, bad);
-                tile_compute<HD>(B, lq, lqsc, a.scale_log2, acc, M, S, lane);
-                ts += kStride;
-            }
-        } else {
-            // One register tile per wave; latency is hidden by the other
-            // resident waves (one wave's loads overlap the others' compute).
-            while (ts < t1) {
-                tile_compute<HD>(A, lq, lqsc, a.scale_log2, acc, M, S, lane);
-                ts += kStride;
-                if (ts < t1) {
-                    int blk[2];
-                    tile_blocks(trow, ts, a.kv_bs, a.max_blocks, blk);
-                    tile_load<HD>(A, a, blk, kh, ts, t1, lane, bad);
-                }
+                tile_blocks(trow, ts, a.kv_bs, a.max_blocks, blk);
+                tile_load<HD>(A, a, blk, kh, ts, t1, lane, bad);
             }
         }
 
@@ -624,13 +622,13 @@ q8kv_decode_kernel(const DecodeArgs a) {
             }
         }
         // next item (the barrier also keeps LDS from being reused too early)
-        if (!a.ticket) break;
+        if (STATIC || !a.ticket) break;
         if (tid == 0) litem = (int)gridDim.x + __hip_atomic_fetch_add(a.ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __syncthreads();
         item = litem;
         __syncthreads();
     }
-    if (!a.ticket) return;
+    if (STATIC || !a.ticket) return;
     // the last workgroup to finish resets the ticket for the next call (all
     // others have taken their final ticket before counting themselves done)
     if (tid == 0) {
@@ -777,7 +775,10 @@ __global__ __launch_bounds__(256) void q8kv_append_kernel(const AppendArgs a) {
         uint32_t packed = 0;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) packed |= (uint32_t)(q8_code(x[e], inv) & 0xff) << (8 * e);
-        int8_t* dst = (pass == 0 ? a.kp : a.vp) + dst_row * HD + (size_t)lane * EPL;
+        // the lane's EPL columns stay adjacent in both page byte orders
+        const int row = rr % kSub, col = lane * EPL;
+        int8_t* dst = (pass == 0 ? a.kp : a.vp) + (dst_row - row) * HD +
+                      (pass == 0 ? k_swizzle(row, col) : v_swizzle<HD>(row, col));
         if constexpr (EPL == 1) *reinterpret_cast<uint8_t*>(dst) = (uint8_t)packed;
         else if constexpr (EPL == 2) *reinterpret_cast<uint16_t*>(dst) = (uint16_t)packed;
         else *reinterpret_cast<uint32_t*>(dst) = packed;
@@ -826,12 +827,11 @@ __global__ __launch_bounds__(kThreads) void q8kv_debug_dots_kernel(const DotsArg
     load_q_operand<HD>(Q, lq, lqsc, lane);
     const int r = lane >> 4, n = lane & 15, bp = n >> 3, g = n & 7;
     for (int ts = kSub * wid; ts < Lm; ts += kSub * kWaves) {
-        const int nval = min(Lm - ts, kSub);
         const int blk = a.table[(size_t)b * a.max_blocks + ts / a.kv_bs];
         if ((unsigned)blk >= (unsigned)a.num_blocks) continue;
         const size_t base = ((size_t)blk * a.n_kv + kh) * a.kv_bs + (size_t)(ts % a.kv_bs);
         i32x4 kop[GG::NPAIR], c[GG::NPAIR];
-        load_k_subtile<HD>(kop, a.kp, base, nval, lane);
+        load_k_subtile<HD>(kop, a.kp, base, lane);
         qk_mfma<HD>(c, kop, Q);
         if (g >= G) continue;
 #pragma unroll
@@ -921,14 +921,26 @@ int resident_workgroups(int dev, int hd, int* out) {
     int cus = 0, per_cu = 0;
     hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
-    const void* k = hd == 64 ? reinterpret_cast<const void*>(q8kv_decode_kernel<64, false>)
-                  : hd == 128 ? reinterpret_cast<const void*>(q8kv_decode_kernel<128, false>)
-                              : reinterpret_cast<const void*>(q8kv_decode_kernel<256, false>);
+    const void* k = hd == 64 ? reinterpret_cast<const void*>(q8kv_decode_kernel<64, kPersistent>)
+                  : hd == 128 ? reinterpret_cast<const void*>(q8kv_decode_kernel<128, kPersistent>)
+                              : reinterpret_cast<const void*>(q8kv_decode_kernel<256, kPersistent>);
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kThreads, 0);
     if (e != hipSuccess) return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
     *out = std::max(1, cus * std::max(1, per_cu));
     g_resident[{dev, hd}] = *out;
     return Q8KV_OK;
+}
+
+template <int HD>
+void launch_decode_hd(int mode, unsigned grid, hipStream_t st, const DecodeArgs& da) {
+    if (mode == kPersistent) hipLaunchKernelGGL((q8kv_decode_kernel<HD, kPersistent>), dim3(grid), dim3(kThreads), 0, st, da);
+    else hipLaunchKernelGGL((q8kv_decode_kernel<HD, kStatic>), dim3(grid), dim3(kThreads), 0, st, da);
+}
+
+void launch_decode(int hd, int mode, unsigned grid, hipStream_t st, const DecodeArgs& da) {
+    if (hd == 64) launch_decode_hd<64>(mode, grid, st, da);
+    else if (hd == 128) launch_decode_hd<128>(mode, grid, st, da);
+    else launch_decode_hd<256>(mode, grid, st, da);
 }
 
 int decode_impl(float* out, const float* q, const int8_t* kp, const int8_t* vp, const float* ks,
@@ -1012,24 +1024,8 @@ int decode_impl(float* out, const float* q, const int8_t* kp, const int8_t* vp, 
         da.st_acc = static_cast<float*>(w.ptr);
         da.st_ms = reinterpret_cast<float*>(static_cast<char*>(w.ptr) + acc_bytes);
     }
-    // every item in its own workgroup, at most two per compute unit: prefetch
-    int cus = 0;
-    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
-    const bool pf = items <= (long long)grid && grid <= 2u * (unsigned)cus;
-    if (pf) {
-        switch (hd) {
-            case 64: hipLaunchKernelGGL((q8kv_decode_kernel<64, true>), dim3(grid), dim3(kThreads), 0, st, da); break;
-            case 128: hipLaunchKernelGGL((q8kv_decode_kernel<128, true>), dim3(grid), dim3(kThreads), 0, st, da); break;
-            default: hipLaunchKernelGGL((q8kv_decode_kernel<256, true>), dim3(grid), dim3(kThreads), 0, st, da); break;
-        }
-    } else {
-        switch (hd) {
-            case 64: hipLaunchKernelGGL((q8kv_decode_kernel<64, false>), dim3(grid), dim3(kThreads), 0, st, da); break;
-            case 128: hipLaunchKernelGGL((q8kv_decode_kernel<128, false>), dim3(grid), dim3(kThreads), 0, st, da); break;
-            default: hipLaunchKernelGGL((q8kv_decode_kernel<256, false>), dim3(grid), dim3(kThreads), 0, st, da); break;
-        }
-    }
+    // every item in its own workgroup: static grid
+    launch_decode(hd, items > (long long)grid ? kPersistent : kStatic, grid, st, da);
     e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
     if (np > 1) {

@@ -18,11 +18,16 @@
  * of the context (the same rescale rule on whole groups), which changes the
  * fp32 rounding but not the mathematics.
  *
- * Memory layouts (all tensors are caller-owned device memory, row-major,
- * densely packed, naturally aligned -- 16 bytes for pages and scales):
- *   q, out        fp32  [batch][n_q_heads][hd]
+ * Memory layouts (all tensors are caller-owned device memory, densely
+ * packed, naturally aligned -- 16 bytes for pages and scales):
+ *   q, out        fp32  [batch][n_q_heads][hd] row-major
  *   k_pages,
- *   v_pages       int8  [num_blocks][n_kv_heads][kv_bs][hd]
+ *   v_pages       int8  [num_blocks][n_kv_heads][kv_bs / 16][16 * hd]: each
+ *                       page (block, kv head) is a run of 16-row sub-tiles,
+ *                       and a sub-tile's 16 x hd bytes are stored in the
+ *                       matrix-core operand order below, so that one 16-byte
+ *                       load per lane of a 64-lane wave reads 1 KB of
+ *                       consecutive bytes;
  *   k_scale,
  *   v_scale       fp32  [num_blocks][n_kv_heads][kv_bs]  dequantisation
  *                       factor absmax * fp32(1/127) of that row
@@ -32,6 +37,16 @@
  *   seq_lens      int32 [batch]  tokens cached for each sequence
  * Token t of sequence b lives in physical block block_table[b][t / kv_bs] at
  * row t % kv_bs.  Query head h reads kv head h / (n_q_heads / n_kv_heads).
+ *
+ * Sub-tile byte order.  A sub-tile is hd / 64 chunks of 1024 bytes; byte
+ * 16 * l + i of chunk c belongs to lane slot l = 16 * r + n (r in 0..3, n in
+ * 0..15) and is, for row t (0..15) and column x (0..hd-1) of the sub-tile:
+ *   K: t = n, x = 64 * c + 16 * r + i;
+ *   V: with BPL = hd / 16, slot l holds rows 4r..4r+3, columns
+ *      BPL*n .. BPL*n + BPL - 1, as 4 * BPL bytes in (row, column) order;
+ *      byte j * BPL + e of that run (row 4r + j, column BPL*n + e) is byte
+ *      i of chunk c where c * 16 + i = j * BPL + e.
+ * q8kv_append writes this order; a caller that fills pages itself must too.
  *
  * Every entry point checks its arguments on the host before it makes any HIP
  * call, launches asynchronously on `stream` (a hipStream_t passed as void*,
@@ -116,8 +131,9 @@ int q8kv_plan(int batch, int n_q_heads, int n_kv_heads, int hd, int kv_bs,
  * slot_mapping [n_tokens] int32: destination slot block * kv_bs + row of each
  *              token; a negative slot skips the token, as does a slot at or
  *              beyond num_blocks * kv_bs.
- * Rows are written to k_pages/v_pages[block][kh][row][:] and their
- * dequantisation factors to k_scale/v_scale[block][kh][row].
+ * Row `row` of page (block, kh) is written in the sub-tile byte order above
+ * (sub-tile row / 16, row row % 16 of it) and its dequantisation factors to
+ * k_scale/v_scale[block][kh][row].
  */
 int q8kv_append(int8_t* k_pages, int8_t* v_pages, float* k_scale, float* v_scale,
                 const void* k_src, const void* v_src, int src_dtype,

@@ -50,11 +50,38 @@ def decode(c, cache, part_tokens=0, lens=None):
     return out.cpu().numpy()
 
 
+def chunk_offsets(hd, which):
+    """Byte offset, inside a 16-row sub-tile of a device page, of element
+    (row, column) -- the page byte order include/q8kv.h documents: 1 KB chunks
+    of 64 lane slots x 16 bytes; K chunk c slot 16r+n holds row n, columns
+    64c+16r..+16; V slot 16r+n holds rows 4r..4r+3 x columns BPL n..+BPL
+    (BPL = hd/16) in (row, column) order, cut into 16-byte pieces, piece c in
+    chunk c."""
+    row = np.arange(16)[:, None]
+    col = np.arange(hd)[None, :]
+    if which == "k":
+        return (col // 64) * 1024 + 16 * (16 * ((col % 64) // 16) + row) + col % 16
+    bpl = hd // 16
+    slot = 16 * (row // 4) + col // bpl
+    qb = (row % 4) * bpl + col % bpl
+    return (qb // 16) * 1024 + 16 * slot + qb % 16
+
+
+def natural_pages(pages, which):
+    """Device pages [nb][n_kv][kv_bs][hd] in chunk order -> row-major rows."""
+    nb, n_kv, kv_bs, hd = pages.shape
+    sub = pages.reshape(nb, n_kv, kv_bs // 16, 16 * hd)
+    return sub[..., chunk_offsets(hd, which).reshape(-1)].reshape(nb, n_kv, kv_bs, hd)
+
+
 def assert_cache_equal(host, dev, blocks=None):
-    """Bitwise equality of pages and scales (NaN == NaN for poisoned rows)."""
+    """Bitwise equality of pages (in row order) and scales (NaN == NaN for
+    poisoned rows)."""
     for f in ("k_pages", "v_pages", "k_scale", "v_scale"):
         a = getattr(host, f)
         b = getattr(dev, f).cpu().numpy()
+        if f.endswith("pages"):
+            b = natural_pages(b, f[0])
         if blocks is not None:
             a, b = a[blocks], b[blocks]
         if a.dtype == np.float32:
