@@ -288,9 +288,118 @@ struct DecodeArgs {
     float* st_ms;   // [batch][n_kv][n_parts][G][2] (max in log2 units, exp-sum)
     int* ticket;    // [2]: next work item, workgroups done (zero between calls);
                     // NULL when every item has its own workgroup
+    int* arrive;    // [batch][n_kv]: partitions of a (sequence, kv head) stored so far
+                    // (zero between calls); NULL when q8kv_combine_kernel merges
     int batch, max_blocks, num_blocks, n_q, n_kv, kv_bs, group, part_tokens, n_parts;
     float scale_log2;  // softmax scale * log2(e)
 };
+
+// Partition states cross workgroups (and XCDs) through buffer loads and
+// stores with the SC1 cache policy: device-scope coherent accesses that
+// write through / read through the per-XCD caches, so no whole-cache
+// writeback or invalidate is needed between a state's store and its load.
+constexpr int kDeviceCoherent = 16;  // SC1 cache-policy bit of buffer instructions
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t state_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ f32x4 state_load4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kDeviceCoherent));
+}
+__device__ __forceinline__ float2 state_load2(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+    return __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, kDeviceCoherent));
+}
+__device__ __forceinline__ void state_store4(__amdgpu_buffer_rsrc_t r, uint32_t voff, f32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), r, voff, 0, kDeviceCoherent);
+}
+__device__ __forceinline__ void state_store2(__amdgpu_buffer_rsrc_t r, uint32_t voff, float2 v) {
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, voff, 0, kDeviceCoherent);
+}
+// Wait until this thread's stores have completed (are visible device-wide).
+__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// In-kernel merge: when a (sequence, kv head) has at most kFuseRows partition
+// states (partitions x query heads), the workgroup that stores the last of
+// them merges them all, so no second kernel is needed.  A thread holds at most
+// kFusePer partitions of one float4 slice.
+constexpr int kFuseRows = 64;
+constexpr int kFusePer = 8;
+
+// Accumulator slice e4 of partitions r, r + R, ... (< np), all loads at once.
+__device__ __forceinline__ void load_slices(f32x4 (&v)[kFusePer], __amdgpu_buffer_rsrc_t racc, uint32_t pstride,
+                                            int e4, int r, int R, int np) {
+#pragma unroll
+    for (int k = 0; k < kFusePer; ++k) {
+        const int p = r + k * R;
+        if (p < np) v[k] = state_load4(racc, (uint32_t)e4 * 16, (uint32_t)p * pstride);
+    }
+}
+
+// sum_k v[k] 2^(M_p - M*) over this thread's partitions, in order.
+__device__ __forceinline__ f32x4 weigh_slices(const f32x4 (&v)[kFusePer], const float2* lms, int G, int g,
+                                              float Mx, int r, int R, int np) {
+    f32x4 at = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < kFusePer; ++k) {
+        const int p = r + k * R;
+        if (p < np) at += v[k] * __builtin_amdgcn_exp2f(lms[p * G + g].x - Mx);
+    }
+    return at;
+}
+
+// M* and S* of head g over the np partitions (states in LDS, partition order).
+__device__ __forceinline__ void group_max_sum(const float2* lms, int G, int g, int np, float& Mx, float& St) {
+    Mx = -INFINITY;
+    St = 0.0f;
+    for (int p = 0; p < np; ++p) Mx = fmaxf(Mx, lms[p * G + g].x);
+    for (int p = 0; p < np; ++p) St += lms[p * G + g].y * __builtin_amdgcn_exp2f(lms[p * G + g].x - Mx);
+}
+
+// Merge the np partition states of (b, kh) into the output rows, in
+// partition order: M* = max M_p, S* = sum S_p 2^(M_p - M*), out = sum acc_p
+// 2^(M_p - M*) / S*.  Thread (row r, slice e4) sums partitions r, r + R, ...
+// in order; the R row sums are then added in row order, so the result does
+// not depend on which workgroup merges.
+template <int HD>
+__device__ void merge_group(const DecodeArgs& a, int b, int kh, int np, float* out_rows, int tid, float2* lms,
+                            f32x4* lred) {
+    constexpr int Q4 = HD / 4;
+    const int G = a.group;
+    const int slices = G * Q4;
+    const size_t first = ((size_t)b * a.n_kv + kh) * a.n_parts * G;  // state of (partition 0, head 0)
+    const __amdgpu_buffer_rsrc_t racc = state_rsrc(a.st_acc + first * HD, (uint32_t)(np * G * HD * 4));
+    const __amdgpu_buffer_rsrc_t rms = state_rsrc(a.st_ms + first * 2, (uint32_t)(np * G * 8));
+    const uint32_t pstride = (uint32_t)(G * HD * 4);  // bytes between partitions
+    const int R = slices >= kThreads ? 1 : kThreads / slices;
+    const int r = tid / slices;
+    const bool active = r < R;
+    int e4 = active ? tid - r * slices : 0;
+    // the accumulator loads go out before the (M, S) round trip
+    f32x4 v[kFusePer];
+    if (active) load_slices(v, racc, pstride, e4, r, R, np);
+    for (int i = tid; i < np * G; i += kThreads) lms[i] = state_load2(rms, (uint32_t)i * 8);
+    __syncthreads();
+    float Mx, St;
+    group_max_sum(lms, G, e4 / Q4, np, Mx, St);
+    f32x4 at = weigh_slices(v, lms, G, e4 / Q4, Mx, r, R, np);
+    if (R > 1) {
+        if (active) lred[tid] = at;
+        __syncthreads();
+        if (r == 0) {
+            for (int rr = 1; rr < R; ++rr) at += lred[rr * slices + e4];
+            *reinterpret_cast<f32x4*>(out_rows + (size_t)e4 * 4) = at / St;
+        }
+        return;
+    }
+    if (active) *reinterpret_cast<f32x4*>(out_rows + (size_t)e4 * 4) = at / St;
+    // slices > kThreads (hd 256 with five or more heads): further slices
+    for (e4 += kThreads; active && e4 < slices; e4 += kThreads) {
+        load_slices(v, racc, pstride, e4, 0, 1, np);
+        group_max_sum(lms, G, e4 / Q4, np, Mx, St);
+        at = weigh_slices(v, lms, G, e4 / Q4, Mx, 0, 1, np);
+        *reinterpret_cast<f32x4*>(out_rows + (size_t)e4 * 4) = at / St;
+    }
+}
 
 // Registers of one 32-token tile: the K and V chunks of both sub-tiles and
 // the K/V scales of the lane's rows 4r..4r+3 of each sub-tile (one 16-byte
@@ -455,6 +564,9 @@ q8kv_decode_kernel(const DecodeArgs a) {
     __shared__ int lpre[STATIC ? 1 : kMaxBatch + 1];  // exclusive prefix of items per sequence
     __shared__ int lscan[kWaves];
     __shared__ int litem;
+    __shared__ int lflag;
+    __shared__ float2 lms[kFuseRows];
+    __shared__ f32x4 lred[kThreads];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -600,6 +712,8 @@ q8kv_decode_kernel(const DecodeArgs a) {
         // merge the waves' states (same rescale rule, wave order fixed); write
         // the output (one partition) or this partition's state
         const size_t state0 = (((size_t)b * a.n_kv + kh) * a.n_parts + part) * G;
+        const __amdgpu_buffer_rsrc_t racc = state_rsrc(a.st_acc + state0 * HD, (uint32_t)(G * HD * 4));
+        const __amdgpu_buffer_rsrc_t rms = state_rsrc(a.st_ms + state0 * 2, (uint32_t)(G * 8));
         for (int e4 = tid; e4 < G * Q4; e4 += kThreads) {
             const int g = e4 / Q4, i4 = e4 % Q4;
             float Mx = -INFINITY;
@@ -617,9 +731,23 @@ q8kv_decode_kernel(const DecodeArgs a) {
             if (np_b == 1) {
                 *reinterpret_cast<f32x4*>(out_rows + (size_t)e4 * 4) = at / St;
             } else {
-                *reinterpret_cast<f32x4*>(a.st_acc + state0 * HD + (size_t)e4 * 4) = at;
-                if (i4 == 0) *reinterpret_cast<float2*>(a.st_ms + (state0 + g) * 2) = make_float2(Mx, St);
+                state_store4(racc, (uint32_t)e4 * 16, at);
+                if (i4 == 0) state_store2(rms, (uint32_t)g * 8, make_float2(Mx, St));
             }
+        }
+        if (a.arrive && np_b > 1) {
+            // the workgroup storing the group's last state merges the group
+            wait_stores();
+            __syncthreads();
+            if (tid == 0) {
+                int* c = a.arrive + (size_t)b * a.n_kv + kh;
+                const int prev = __hip_atomic_fetch_add(c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const bool last = prev == np_b - 1;
+                if (last) __hip_atomic_store(c, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                lflag = last;
+            }
+            __syncthreads();
+            if (lflag) merge_group<HD>(a, b, kh, np_b, out_rows, tid, lms, lred);
         }
         // next item (the barrier also keeps LDS from being reused too early)
         if (STATIC || !a.ticket) break;
@@ -865,12 +993,15 @@ int hip_fail(hipError_t e, const char* what) {
 }
 
 // Library-owned split-context workspace of one (device, stream): the
-// partition states written by the decode kernel and read by the combine
-// kernel (no initialisation needed).
+// partition states (no initialisation needed), the persistent grid's work
+// ticket and the in-kernel merge's arrival counters (zeroed at allocation,
+// left at zero by every call).
 struct Workspace {
     void* ptr = nullptr;
     size_t bytes = 0;
-    int* ticket = nullptr;  // [2] zeroed at allocation, left at zero by every call
+    int* ticket = nullptr;  // [2]
+    int* arrive = nullptr;  // [arrive_n]
+    size_t arrive_n = 0;
 };
 std::mutex g_mu;
 std::map<std::pair<int, void*>, Workspace> g_ws;
@@ -891,15 +1022,16 @@ int check_cache_shape(int num_blocks, int n_kv, int hd, int kv_bs) {
 // Partition plan: a pure function of the shapes, so results never depend on
 // the device.  When the longest possible step spreads over about 512 work
 // items of at most 2048 tokens, use that (one item per workgroup: every
-// resident workgroup streams one long partition).  Larger steps use
-// 1024-token partitions and many items per workgroup, which the persistent
-// grid balances to within one item.  Partitions are multiples of 128 tokens
-// (every wave gets the same number of 32-token tiles) and a sequence has at
-// most kMaxParts of them.
+// resident workgroup streams one long partition).  Larger steps run on the
+// persistent grid with partitions of 2048-4096 tokens (about 4096 items):
+// long enough that the partition states stay a small fraction of the
+// traffic, short enough that the grid stays balanced to within one item.
+// Partitions are multiples of 128 tokens (every wave gets the same number of
+// 32-token tiles) and a sequence has at most kMaxParts of them.
 void plan(int batch, int n_kv, int max_tokens, int* part_tokens, int* n_parts) {
     const long long units = (long long)batch * n_kv * max_tokens;
     long long pt = (units + 511) / 512;
-    if (pt > 2048) pt = 1024;
+    if (pt > 2048) pt = std::min(4096LL, std::max(2048LL, (units + 4095) / 4096));
     pt = (pt + 127) / 128 * 128;
     if (pt < 128) pt = 128;
     const long long min_pt = ((max_tokens + kMaxParts - 1) / kMaxParts + 127) / 128 * 128;
@@ -981,7 +1113,7 @@ int decode_impl(float* out, const float* q, const int8_t* kp, const int8_t* vp, 
     rc = resident_workgroups(dev, hd, &resident);
     if (rc) return rc;
     const unsigned grid = (unsigned)std::min<long long>(items, resident);
-    DecodeArgs da{out, q, kp, vp, ks, vs, table, lens, nullptr, nullptr, nullptr,
+    DecodeArgs da{out, q, kp, vp, ks, vs, table, lens, nullptr, nullptr, nullptr, nullptr,
                   batch, max_blocks, num_blocks, n_q, n_kv, kv_bs, G, pt, np, scale * kLog2e};
     if (items > (long long)grid) {
         std::lock_guard<std::mutex> lock(g_mu);
@@ -1024,11 +1156,41 @@ int decode_impl(float* out, const float* q, const int8_t* kp, const int8_t* vp, 
         da.st_acc = static_cast<float*>(w.ptr);
         da.st_ms = reinterpret_cast<float*>(static_cast<char*>(w.ptr) + acc_bytes);
     }
+    // small groups of partition states are merged inside the decode kernel
+    const int slices = G * hd / 4;
+    const int rows_par = slices >= kThreads ? 1 : kThreads / slices;
+    const bool fuse = np > 1 && np * G <= kFuseRows && (np + rows_par - 1) / rows_par <= kFusePer;
+    if (fuse) {
+        const size_t need = (size_t)batch * n_kv;
+        std::lock_guard<std::mutex> lock(g_mu);
+        Workspace& w = g_ws[{dev, stream}];
+        if (w.arrive_n < need) {
+            if (w.arrive) {
+                e = hipStreamSynchronize(st);
+                if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+                e = hipFree(w.arrive);
+                w.arrive = nullptr;
+                w.arrive_n = 0;
+                if (e != hipSuccess) return hip_fail(e, "hipFree");
+            }
+            void* t = nullptr;
+            e = hipMalloc(&t, need * sizeof(int));
+            if (e != hipSuccess) return fail(Q8KV_ENOMEM, "hipMalloc of the merge counters: %s", hipGetErrorString(e));
+            e = hipMemsetAsync(t, 0, need * sizeof(int), st);
+            if (e != hipSuccess) {
+                (void)hipFree(t);
+                return hip_fail(e, "hipMemsetAsync");
+            }
+            w.arrive = static_cast<int*>(t);
+            w.arrive_n = need;
+        }
+        da.arrive = w.arrive;
+    }
     // every item in its own workgroup: static grid
     launch_decode(hd, items > (long long)grid ? kPersistent : kStatic, grid, st, da);
     e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
-    if (np > 1) {
+    if (np > 1 && !fuse) {
         CombineArgs ca{out, da.st_acc, da.st_ms, lens, n_q, n_kv, G, max_tokens, pt, np};
         const unsigned cgrid = (unsigned)(batch * n_q);
         switch (hd) {
@@ -1116,11 +1278,12 @@ int q8kv_release(void) {
     int cur = 0;
     if (!g_ws.empty() && hipGetDevice(&cur) != hipSuccess) cur = -1;
     for (auto& kv : g_ws) {
-        if (!kv.second.ptr && !kv.second.ticket) continue;
+        if (!kv.second.ptr && !kv.second.ticket && !kv.second.arrive) continue;
         hipError_t e = hipSetDevice(kv.first.first);
         if (e == hipSuccess) e = hipDeviceSynchronize();
         if (e == hipSuccess && kv.second.ptr) e = hipFree(kv.second.ptr);
         if (e == hipSuccess && kv.second.ticket) e = hipFree(kv.second.ticket);
+        if (e == hipSuccess && kv.second.arrive) e = hipFree(kv.second.arrive);
         if (e != hipSuccess && rc == Q8KV_OK) rc = hip_fail(e, "releasing workspace");
     }
     g_ws.clear();

@@ -169,6 +169,28 @@ def test_decode_hd_kv_bs(hd, kv_bs):
     check_decode(c, dev, part_tokens=64)
 
 
+@pytest.mark.parametrize("hd,G", [(64, 1), (64, 8), (128, 1), (128, 3), (128, 5), (128, 8),
+                                  (256, 2), (256, 5), (256, 8)])
+def test_decode_split_merge_paths(hd, G):
+    """Partition states of a (sequence, kv head) are merged inside the decode
+    kernel by the workgroup that stores the last one when there are at most
+    64 of them (partitions x query heads), else by the combine kernel.  The
+    partition lengths here give 3 to 19 partitions, so each shape takes one or
+    both paths, the in-kernel one with one or several float4 slices per
+    thread; each call is made twice, since the merge leaves its arrival
+    counters at zero for the next call."""
+    w = workloads.Workload("merge", 3, 2 * G, 2, hd, 32, 600, ragged=True, table="pool",
+                           key=800 + hd + G)
+    c = build(w)
+    say(f"split merge hd={hd} G={G} lens={c.lens.tolist()}")
+    dev = gpu_cache(c)
+    for pt in (32, 64, 128, 192):
+        first = decode(c, dev, part_tokens=pt)
+        again = decode(c, dev, part_tokens=pt)
+        assert np.array_equal(first.view(np.uint32), again.view(np.uint32))
+        check_decode(c, dev, part_tokens=pt)
+
+
 def test_decode_empty_sequences_give_zero_rows():
     w = workloads.Workload("empty", 4, 8, 2, 128, 16, 100, ragged=True, table="pool", key=700)
     c = build(w, lens=[0, 50, 0, 100])
