@@ -93,16 +93,39 @@ __device__ __forceinline__ uint32_t q8_pack4(f32x4 x, float inv) {
 
 // Quantise up to kHeadGroup query rows (G of them; the rest are zero) into
 // LDS: lq [kHeadGroup][HD] int8, lqsc [kHeadGroup][HD/32] fp32.  Eight
-// consecutive threads own one 32-block (4 floats each).
-template <int HD>
-__device__ __forceinline__ void quantize_q_rows(const float* __restrict__ q, int G, int8_t* lq,
-                                                float* lqsc, int tid, int nthreads) {
-    constexpr int kChunks = kHeadGroup * HD / 4;
-    for (int c = tid; c < kChunks; c += nthreads) {
+// consecutive threads own one 32-block (4 floats each).  The rows are loaded
+// into registers first (load_q_rows) so the loads can be issued early and
+// the quantisation done once they have arrived.
+template <int HD, int NT>
+struct QRows {
+    static constexpr int kChunks = kHeadGroup * HD / 4;
+    static constexpr int kPer = (kChunks + NT - 1) / NT;
+    f32x4 x[kPer];
+};
+
+// Every thread issues its loads unconditionally (rows past G re-read row
+// G - 1 and are zeroed), so no branch makes a later wait conservative.
+template <int HD, int NT>
+__device__ __forceinline__ void load_q_rows(QRows<HD, NT>& Q, const float* __restrict__ q, int G, int tid) {
+#pragma unroll
+    for (int i = 0; i < QRows<HD, NT>::kPer; ++i) {
+        const int c = min(tid + i * NT, QRows<HD, NT>::kChunks - 1);
         const int g = c / (HD / 4);
         const int e = (c % (HD / 4)) * 4;
-        f32x4 x = {0.f, 0.f, 0.f, 0.f};
-        if (g < G) x = *reinterpret_cast<const f32x4*>(q + (size_t)g * HD + e);
+        const f32x4 x = *reinterpret_cast<const f32x4*>(q + (size_t)min(g, G - 1) * HD + e);
+        Q.x[i] = g < G ? x : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+}
+
+template <int HD, int NT>
+__device__ __forceinline__ void quantize_q_regs(const QRows<HD, NT>& Q, int8_t* lq, float* lqsc, int tid) {
+#pragma unroll
+    for (int i = 0; i < QRows<HD, NT>::kPer; ++i) {
+        const int c = tid + i * NT;
+        if (QRows<HD, NT>::kChunks % NT != 0 && c >= QRows<HD, NT>::kChunks) break;  // same for all 8 of a block
+        const int g = c / (HD / 4);
+        const int e = (c % (HD / 4)) * 4;
+        const f32x4 x = Q.x[i];
         float a = fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w)));
         a = fmaxf(a, __shfl_xor(a, 1));
         a = fmaxf(a, __shfl_xor(a, 2));
@@ -112,6 +135,13 @@ __device__ __forceinline__ void quantize_q_rows(const float* __restrict__ q, int
         *reinterpret_cast<uint32_t*>(lq + g * HD + e) = q8_pack4(x, inv);
         if ((c & 7) == 0) lqsc[g * (HD / kQBlock) + e / kQBlock] = a * kInv127;
     }
+}
+
+template <int HD, int NT>
+__device__ __forceinline__ void quantize_q_rows(const float* __restrict__ q, int G, int8_t* lq, float* lqsc, int tid) {
+    QRows<HD, NT> Q;
+    load_q_rows<HD, NT>(Q, q, G, tid);
+    quantize_q_regs<HD, NT>(Q, lq, lqsc, tid);
 }
 
 // ----------------------------------------------------------------------------
@@ -640,13 +670,22 @@ q8kv_decode_kernel(const DecodeArgs a) {
             kh = rr / np_b;
             part = rr % np_b;
         }
+        // the query rows' loads go out first: the quantisation then waits for
+        // them alone, not for the first tile queued behind them
+        QRows<HD, kThreads> qrows;
+        load_q_rows<HD, kThreads>(qrows, a.q + ((size_t)b * a.n_q + (size_t)kh * G) * HD, G, tid);
         const int32_t* trow = a.table + (size_t)b * a.max_blocks;
         const int t0 = part * a.part_tokens;
-        // issue the first tile's table reads together with the length read
+        // The first tile's table reads, those of the item's first tile (a
+        // wave with no tile of its own loads that one, unused, so that every
+        // wave has the same loads in flight) and the length read are issued
+        // together and waited for once.
         int ts = t0 + kTile * wid;
-        int blk_first[2];
+        int blk_first[2], blk_t0[2];
         tile_blocks(trow, ts, a.kv_bs, a.max_blocks, blk_first);
+        tile_blocks(trow, t0, a.kv_bs, a.max_blocks, blk_t0);
         int L = uniform_read(a.lens, b);
+        asm volatile("" : "+s"(blk_first[0]), "+s"(blk_first[1]), "+s"(blk_t0[0]), "+s"(blk_t0[1]), "+s"(L));
         bool bad = false;
         if (L > cap) {
             L = cap;
@@ -667,9 +706,13 @@ q8kv_decode_kernel(const DecodeArgs a) {
 
         // Start streaming the wave's first tile before the query prologue.
         Tile<HD> A;
-        if (ts < t1) tile_load<HD>(A, a, blk_first, kh, ts, t1, lane, bad);
+        {
+            const bool own = ts < t1;
+            const int blk0[2] = {own ? blk_first[0] : blk_t0[0], own ? blk_first[1] : blk_t0[1]};
+            tile_load<HD>(A, a, blk0, kh, own ? ts : t0, t1, lane, bad);
+        }
 
-        quantize_q_rows<HD>(a.q + ((size_t)b * a.n_q + (size_t)kh * G) * HD, G, lq, lqsc, tid, kThreads);
+        quantize_q_regs<HD, kThreads>(qrows, lq, lqsc, tid);
         __syncthreads();
 
         f32x4 acc[GG::BPL];
@@ -924,7 +967,7 @@ __global__ __launch_bounds__(kThreads) void q8kv_debug_quantize_kernel(int8_t* q
     __shared__ float lqsc[kHeadGroup * Geo<HD>::NB];
     const int r0 = blockIdx.x * kHeadGroup;
     const int G = min(kHeadGroup, rows - r0);
-    quantize_q_rows<HD>(q + (size_t)r0 * HD, G, lq, lqsc, threadIdx.x, kThreads);
+    quantize_q_rows<HD, kThreads>(q + (size_t)r0 * HD, G, lq, lqsc, threadIdx.x);
     __syncthreads();
     for (int e = threadIdx.x; e < G * HD; e += kThreads) qi[(size_t)r0 * HD + e] = lq[e];
     for (int e = threadIdx.x; e < G * Geo<HD>::NB; e += kThreads) qsc[(size_t)r0 * Geo<HD>::NB + e] = lqsc[e];
@@ -949,7 +992,7 @@ __global__ __launch_bounds__(kThreads) void q8kv_debug_dots_kernel(const DotsArg
     const int kh = blockIdx.x % a.n_kv, b = blockIdx.x / a.n_kv;
     const int G = a.group;
     const int Lm = min(min(a.lens[b], a.max_blocks * a.kv_bs), a.max_tok);
-    quantize_q_rows<HD>(a.q + ((size_t)b * a.n_q + (size_t)kh * G) * HD, G, lq, lqsc, tid, kThreads);
+    quantize_q_rows<HD, kThreads>(a.q + ((size_t)b * a.n_q + (size_t)kh * G) * HD, G, lq, lqsc, tid);
     __syncthreads();
     QOperand<HD> Q;
     load_q_operand<HD>(Q, lq, lqsc, lane);
@@ -1005,7 +1048,13 @@ struct Workspace {
 };
 std::mutex g_mu;
 std::map<std::pair<int, void*>, Workspace> g_ws;
-std::map<std::pair<int, int>, int> g_resident;  // (device, hd) -> resident decode workgroups
+// Launch facts of the decode kernels on one device for one hd.
+struct LaunchInfo {
+    int cus = 0;          // compute units
+    int resident = 0;     // persistent-grid workgroups that fit at once
+    int static_lds = 0;   // dynamic LDS that keeps a static grid at two workgroups per CU
+};
+std::map<std::pair<int, int>, LaunchInfo> g_launch;  // (device, hd)
 
 bool valid_hd(int hd) { return hd == 64 || hd == 128 || hd == 256; }
 bool valid_kv_bs(int bs) { return bs == 16 || bs == 32 || bs == 64 || bs == 128 || bs == 256; }
@@ -1042,37 +1091,53 @@ void plan(int batch, int n_kv, int max_tokens, int* part_tokens, int* n_parts) {
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
-// Workgroups of the (single-buffer) decode kernel that fit on the device at once.
-int resident_workgroups(int dev, int hd, int* out) {
+template <int HD>
+int launch_info_hd(int dev, LaunchInfo& li) {
+    int per_cu = 0, lds_cu = 0;
+    hipError_t e = hipDeviceGetAttribute(&li.cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &per_cu, reinterpret_cast<const void*>(q8kv_decode_kernel<HD, kPersistent>), kThreads, 0);
+    if (e != hipSuccess) return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
+    li.resident = std::max(1, li.cus * std::max(1, per_cu));
+    // A static grid of at most two workgroups per CU is spread evenly when a
+    // third cannot fit: ask for just over a third of the CU's LDS.
+    hipFuncAttributes fa;
+    e = hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(q8kv_decode_kernel<HD, kStatic>));
+    if (e != hipSuccess) return hip_fail(e, "hipFuncGetAttributes");
+    const int need = (lds_cu / 3 + 256) / 256 * 256;
+    const int dyn = need - (int)fa.sharedSizeBytes;
+    li.static_lds = (dyn > 0 && need <= 65536) ? dyn : 0;
+    return Q8KV_OK;
+}
+
+int launch_info(int dev, int hd, LaunchInfo* out) {
     std::lock_guard<std::mutex> lock(g_mu);
-    auto it = g_resident.find({dev, hd});
-    if (it != g_resident.end()) {
+    auto it = g_launch.find({dev, hd});
+    if (it != g_launch.end()) {
         *out = it->second;
         return Q8KV_OK;
     }
-    int cus = 0, per_cu = 0;
-    hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
-    const void* k = hd == 64 ? reinterpret_cast<const void*>(q8kv_decode_kernel<64, kPersistent>)
-                  : hd == 128 ? reinterpret_cast<const void*>(q8kv_decode_kernel<128, kPersistent>)
-                              : reinterpret_cast<const void*>(q8kv_decode_kernel<256, kPersistent>);
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kThreads, 0);
-    if (e != hipSuccess) return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
-    *out = std::max(1, cus * std::max(1, per_cu));
-    g_resident[{dev, hd}] = *out;
+    LaunchInfo li;
+    const int rc = hd == 64 ? launch_info_hd<64>(dev, li) : hd == 128 ? launch_info_hd<128>(dev, li)
+                                                                      : launch_info_hd<256>(dev, li);
+    if (rc) return rc;
+    g_launch[{dev, hd}] = li;
+    *out = li;
     return Q8KV_OK;
 }
 
 template <int HD>
-void launch_decode_hd(int mode, unsigned grid, hipStream_t st, const DecodeArgs& da) {
+void launch_decode_hd(int mode, unsigned grid, size_t lds, hipStream_t st, const DecodeArgs& da) {
     if (mode == kPersistent) hipLaunchKernelGGL((q8kv_decode_kernel<HD, kPersistent>), dim3(grid), dim3(kThreads), 0, st, da);
-    else hipLaunchKernelGGL((q8kv_decode_kernel<HD, kStatic>), dim3(grid), dim3(kThreads), 0, st, da);
+    else hipLaunchKernelGGL((q8kv_decode_kernel<HD, kStatic>), dim3(grid), dim3(kThreads), lds, st, da);
 }
 
-void launch_decode(int hd, int mode, unsigned grid, hipStream_t st, const DecodeArgs& da) {
-    if (hd == 64) launch_decode_hd<64>(mode, grid, st, da);
-    else if (hd == 128) launch_decode_hd<128>(mode, grid, st, da);
-    else launch_decode_hd<256>(mode, grid, st, da);
+void launch_decode(int hd, int mode, unsigned grid, size_t lds, hipStream_t st, const DecodeArgs& da) {
+    if (hd == 64) launch_decode_hd<64>(mode, grid, lds, st, da);
+    else if (hd == 128) launch_decode_hd<128>(mode, grid, lds, st, da);
+    else launch_decode_hd<256>(mode, grid, lds, st, da);
 }
 
 int decode_impl(float* out, const float* q, const int8_t* kp, const int8_t* vp, const float* ks,
@@ -1109,10 +1174,10 @@ int decode_impl(float* out, const float* q, const int8_t* kp, const int8_t* vp, 
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-    int resident = 0;
-    rc = resident_workgroups(dev, hd, &resident);
+    LaunchInfo li;
+    rc = launch_info(dev, hd, &li);
     if (rc) return rc;
-    const unsigned grid = (unsigned)std::min<long long>(items, resident);
+    const unsigned grid = (unsigned)std::min<long long>(items, li.resident);
     DecodeArgs da{out, q, kp, vp, ks, vs, table, lens, nullptr, nullptr, nullptr, nullptr,
                   batch, max_blocks, num_blocks, n_q, n_kv, kv_bs, G, pt, np, scale * kLog2e};
     if (items > (long long)grid) {
@@ -1186,8 +1251,11 @@ int decode_impl(float* out, const float* q, const int8_t* kp, const int8_t* vp, 
         }
         da.arrive = w.arrive;
     }
-    // every item in its own workgroup: static grid
-    launch_decode(hd, items > (long long)grid ? kPersistent : kStatic, grid, st, da);
+    // every item in its own workgroup: static grid (two per CU at most when
+    // that is enough)
+    const int mode = items > (long long)grid ? kPersistent : kStatic;
+    const size_t lds = mode == kStatic && grid <= 2u * (unsigned)li.cus ? (size_t)li.static_lds : 0;
+    launch_decode(hd, mode, grid, lds, st, da);
     e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
     if (np > 1 && !fuse) {
