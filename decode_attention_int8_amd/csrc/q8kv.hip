@@ -303,6 +303,8 @@ __device__ __forceinline__ void v_dword_to_f16(const u32x4 (&vch)[2][Geo<HD>::NP
 // its output directly; longer ones store each partition's state (M, S, acc)
 // and q8kv_combine_kernel merges them in partition order.
 constexpr int kMaxBatch = 2048;   // sequences per call (LDS prefix sums)
+constexpr int kClasses = 16;      // remainder classes of the persistent grid's item order
+constexpr int kNoPartial = 255;   // class of a sequence without a partial partition
 constexpr int kMaxParts = 256;    // partitions per sequence (combine LDS)
 
 struct DecodeArgs {
@@ -564,12 +566,6 @@ __device__ __forceinline__ void tile_compute(const Tile<HD>& T, const int8_t* lq
     }
 }
 
-// Work items of one sequence: n_kv * ceil(L / pt); none for L <= 0.
-__device__ __forceinline__ int seq_items(int L, int cap, int pt, int n_kv) {
-    L = min(L, cap);
-    return L > 0 ? n_kv * ((L + pt - 1) / pt) : 0;
-}
-
 // Grid modes.  kPersistent: fewer workgroups than items; items are numbered
 // through an exclusive prefix sum of n_kv * ceil(L / pt) per sequence built in
 // LDS from seq_lens, and each workgroup takes its next item from an atomic
@@ -591,7 +587,12 @@ q8kv_decode_kernel(const DecodeArgs a) {
     __shared__ float lM[kWaves][kHeadGroup];
     __shared__ float lS[kWaves][kHeadGroup];
     __shared__ float lacc[kWaves][kHeadGroup][HD];
-    __shared__ int lpre[STATIC ? 1 : kMaxBatch + 1];  // exclusive prefix of items per sequence
+    // persistent grids: exclusive prefix of full-partition items per sequence,
+    // the sequences that end in a partial partition (longest remainder
+    // first) and each sequence's remainder class
+    __shared__ int lfull[STATIC ? 1 : kMaxBatch + 1];
+    __shared__ int lorder[STATIC ? 1 : kMaxBatch];
+    __shared__ uint8_t lcls[STATIC ? 1 : kMaxBatch];
     __shared__ int lscan[kWaves];
     __shared__ int litem;
     __shared__ int lflag;
@@ -604,14 +605,29 @@ q8kv_decode_kernel(const DecodeArgs a) {
     const int G = a.group;
     const int cap = a.max_blocks * a.kv_bs;
 
-    int total = 0;
+    // Persistent grids number their items longest first, so that the ones
+    // handed out last are short and the grid drains evenly: every full
+    // partition (in sequence, kv head, partition order), then the sequences'
+    // partial last partitions by decreasing remainder class (kClasses classes
+    // of part_tokens / kClasses tokens; ties by sequence index).
+    int nfull = 0, total = 0;
     if constexpr (!STATIC) {
-        // item numbering: each thread sums a contiguous chunk of sequences;
-        // the chunk totals are scanned with wave shuffles and one LDS round
+        const int pt = a.part_tokens;
+        // each thread counts a contiguous chunk of sequences; the chunk
+        // totals are scanned with wave shuffles and one LDS round
         const int per = (a.batch + kThreads - 1) / kThreads;
         const int c0 = min(tid * per, a.batch), c1 = min(c0 + per, a.batch);
         int local = 0;
-        for (int bb = c0; bb < c1; ++bb) local += seq_items(a.lens[bb], cap, a.part_tokens, a.n_kv);
+        for (int bb = c0; bb < c1; ++bb) {
+            const int L = min(a.lens[bb], cap);
+            int cls = kNoPartial;
+            if (L > 0) {
+                local += L / pt;
+                if (L % pt) cls = (kClasses - 1) - (int)((long long)(L % pt) * kClasses / pt);
+            }
+            lcls[bb] = (uint8_t)cls;
+        }
+        local *= a.n_kv;
         int incl = local;
 #pragma unroll
         for (int off = 1; off < kWave; off <<= 1) {
@@ -623,16 +639,50 @@ q8kv_decode_kernel(const DecodeArgs a) {
         int run = incl - local;
         for (int w = 0; w < wid; ++w) run += lscan[w];
         for (int bb = c0; bb < c1; ++bb) {
-            lpre[bb] = run;
-            run += seq_items(a.lens[bb], cap, a.part_tokens, a.n_kv);
+            lfull[bb] = run;
+            run += a.n_kv * (max(min(a.lens[bb], cap), 0) / pt);
         }
-        if (tid == kThreads - 1) lpre[a.batch] = run;
+        if (tid == kThreads - 1) lfull[a.batch] = run;
         __syncthreads();
-        total = lpre[a.batch];
+        // wave 0 ranks the partial sequences: class counts, then positions
+        // (class start + earlier sequences of the class) from wave ballots
+        if (wid == 0) {
+            int start[kClasses];
+#pragma unroll
+            for (int k = 0; k < kClasses; ++k) start[k] = 0;
+            for (int b0 = 0; b0 < a.batch; b0 += kWave) {
+                const int cls = b0 + lane < a.batch ? lcls[b0 + lane] : kNoPartial;
+#pragma unroll
+                for (int k = 0; k < kClasses; ++k) start[k] += __popcll(__ballot(cls == k));
+            }
+            int npart = 0;
+#pragma unroll
+            for (int k = 0; k < kClasses; ++k) {
+                const int c = start[k];
+                start[k] = npart;
+                npart += c;
+            }
+            const unsigned long long below = (1ull << lane) - 1;
+            for (int b0 = 0; b0 < a.batch; b0 += kWave) {
+                const int cls = b0 + lane < a.batch ? lcls[b0 + lane] : kNoPartial;
+                int pos = 0;
+#pragma unroll
+                for (int k = 0; k < kClasses; ++k) {
+                    const unsigned long long m = __ballot(cls == k);
+                    if (cls == k) pos = start[k] + __popcll(m & below);
+                    start[k] += __popcll(m);
+                }
+                if (cls != kNoPartial) lorder[pos] = b0 + lane;
+            }
+            if (lane == 0) lscan[0] = npart;
+        }
+        __syncthreads();
+        nfull = lfull[a.batch];
+        total = nfull + lscan[0] * a.n_kv;
 
         // empty sequences get zero rows; sequence b is zeroed by workgroup b mod grid
         for (int bb = blockIdx.x; bb < a.batch; bb += gridDim.x) {
-            if (lpre[bb + 1] == lpre[bb]) {
+            if (lfull[bb + 1] == lfull[bb] && lcls[bb] == kNoPartial) {
                 float* o = a.out + (size_t)bb * a.n_q * HD;
                 for (int e = tid; e < a.n_q * HD; e += kThreads) o[e] = 0.0f;
             }
@@ -648,7 +698,7 @@ q8kv_decode_kernel(const DecodeArgs a) {
         // Item coordinates are wave-uniform; saying so keeps the block-table
         // and length reads on the scalar path (a vector load would queue
         // behind the in-flight tile loads and wait for all of them).
-        int b, kh, part, first_item = 0, np_b = 0;
+        int b, kh, part;
         if constexpr (STATIC) {
             const int id = __builtin_amdgcn_readfirstlane(item);
             part = id % a.n_parts;
@@ -656,19 +706,27 @@ q8kv_decode_kernel(const DecodeArgs a) {
             b = id / (a.n_parts * a.n_kv);
         } else {
             if (item >= total) break;
-            // sequence of the item: the last b with lpre[b] <= item
-            int lo = 0, hi = a.batch;
-            while (hi - lo > 1) {
-                const int mid = (lo + hi) >> 1;
-                if (lpre[mid] <= item) lo = mid;
-                else hi = mid;
+            const int id = __builtin_amdgcn_readfirstlane(item);
+            if (id < nfull) {
+                // full partition: the last b with lfull[b] <= id
+                int lo = 0, hi = a.batch;
+                while (hi - lo > 1) {
+                    const int mid = (lo + hi) >> 1;
+                    if (lfull[mid] <= id) lo = mid;
+                    else hi = mid;
+                }
+                b = __builtin_amdgcn_readfirstlane(lo);
+                const int f0 = __builtin_amdgcn_readfirstlane(lfull[b]);
+                const int nf = (__builtin_amdgcn_readfirstlane(lfull[b + 1]) - f0) / a.n_kv;
+                kh = (id - f0) / nf;
+                part = (id - f0) % nf;
+            } else {
+                // partial last partition of the sequence ranked (id - nfull) / n_kv
+                const int j = id - nfull;
+                b = __builtin_amdgcn_readfirstlane(lorder[j / a.n_kv]);
+                kh = j % a.n_kv;
+                part = (__builtin_amdgcn_readfirstlane(lfull[b + 1]) - __builtin_amdgcn_readfirstlane(lfull[b])) / a.n_kv;
             }
-            b = __builtin_amdgcn_readfirstlane(lo);
-            first_item = __builtin_amdgcn_readfirstlane(lpre[b]);
-            np_b = (__builtin_amdgcn_readfirstlane(lpre[b + 1]) - first_item) / a.n_kv;
-            const int rr = __builtin_amdgcn_readfirstlane(item) - first_item;
-            kh = rr / np_b;
-            part = rr % np_b;
         }
         // the query rows' loads go out first: the quantisation then waits for
         // them alone, not for the first tile queued behind them
@@ -700,8 +758,8 @@ q8kv_decode_kernel(const DecodeArgs a) {
                     for (int e = tid; e < G * HD; e += kThreads) out_rows[e] = 0.0f;
                 return;
             }
-            np_b = (L + a.part_tokens - 1) / a.part_tokens;
         }
+        const int np_b = (L + a.part_tokens - 1) / a.part_tokens;
         const int t1 = min(L, t0 + a.part_tokens);
 
         // Start streaming the wave's first tile before the query prologue.

@@ -191,6 +191,31 @@ def test_decode_split_merge_paths(hd, G):
         check_decode(c, dev, part_tokens=pt)
 
 
+@pytest.mark.parametrize("G,kv_bs", [(4, 16), (1, 32), (8, 64)])
+def test_decode_persistent_grid(G, kv_bs):
+    """Shapes with more (sequence, kv head, partition) items than fit on the
+    device at once run on the persistent grid, whose item order puts every
+    full partition first and the partial last partitions after them by
+    decreasing length.  64 sequences of up to 1024 tokens split into 32-96
+    token partitions give 1300-4100 items; the lengths include empty
+    sequences, exact multiples of the partition length and sequences shorter
+    than one partition."""
+    rng = np.random.default_rng(900 + G + kv_bs)
+    lens = rng.integers(1, 1025, size=64)
+    lens[:12] = [0, 1, 31, 32, 33, 96, 192, 1024, 0, 95, 97, 1000]
+    w = workloads.Workload("persist", 64, 2 * G, 2, 128, kv_bs, 1024, ragged=True, table="pool",
+                           spare_blocks=3, key=900 + G + kv_bs)
+    c = build(w, lens=[int(x) for x in lens])
+    say(f"persistent grid G={G} kv_bs={kv_bs} tokens={int(c.lens.sum())}")
+    dev = gpu_cache(c)
+    for pt in (32, 64, 96):
+        got = decode(c, dev, part_tokens=pt)
+        assert not got[0].any() and not got[8].any()
+        again = decode(c, dev, part_tokens=pt)
+        assert np.array_equal(got.view(np.uint32), again.view(np.uint32))
+        check_decode(c, dev, part_tokens=pt)
+
+
 def test_decode_empty_sequences_give_zero_rows():
     w = workloads.Workload("empty", 4, 8, 2, 128, 16, 100, ragged=True, table="pool", key=700)
     c = build(w, lens=[0, 50, 0, 100])
