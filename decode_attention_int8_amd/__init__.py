@@ -79,6 +79,13 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+def _ok(t, dtype, dev, ndim):
+    """The per-call check of a tensor argument, kept to a few attribute reads
+    (decode calls are issued every few microseconds)."""
+    return (isinstance(t, torch.Tensor) and t.dtype is dtype and t.is_cuda and t.get_device() == dev
+            and t.dim() == ndim and t.is_contiguous())
+
+
 def _need(t, name, dtype, device, ndim):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
@@ -99,6 +106,14 @@ class PagedKVCache:
     k_scale, v_scale fp32 [num_blocks][n_kv][kv_bs].
     """
 
+    _TENSORS = ("k_pages", "v_pages", "k_scale", "v_scale")
+
+    def __setattr__(self, name, value):
+        # replacing a tensor drops the checked pointers
+        if name in PagedKVCache._TENSORS:
+            object.__setattr__(self, "_meta", None)
+        object.__setattr__(self, name, value)
+
     def __init__(self, num_blocks, n_kv, kv_bs, hd, device="cuda"):
         dev = torch.device(device)
         self.num_blocks, self.n_kv, self.kv_bs, self.hd = num_blocks, n_kv, kv_bs, hd
@@ -110,6 +125,7 @@ class PagedKVCache:
     @classmethod
     def wrap(cls, k_pages, v_pages, k_scale, v_scale):
         self = cls.__new__(cls)
+        object.__setattr__(self, "_meta", None)
         self.k_pages, self.v_pages, self.k_scale, self.v_scale = k_pages, v_pages, k_scale, v_scale
         self.num_blocks, self.n_kv, self.kv_bs, self.hd = k_pages.shape
         return self
@@ -131,6 +147,18 @@ class PagedKVCache:
             _need(t, name, torch.float32, d, 3)
             if tuple(t.shape) != shp[:3]:
                 raise ValueError(f"{name} shape {tuple(t.shape)} != {shp[:3]}")
+
+    def _pointers(self):
+        """(device index, k_pages, v_pages, k_scale, v_scale pointers), checked
+        once and kept until a tensor is replaced."""
+        meta = getattr(self, "_meta", None)
+        if meta is None:
+            self.validate()
+            if not self.k_pages.is_cuda:
+                raise ValueError("the cache must live on a GPU")
+            meta = (self.k_pages.get_device(),) + tuple(getattr(self, n).data_ptr() for n in PagedKVCache._TENSORS)
+            object.__setattr__(self, "_meta", meta)
+        return meta
 
     def append(self, k_src, v_src, slot_mapping):
         """Quantise k_src/v_src [n_tokens][n_kv][hd] (fp32 or bf16) into slots."""
@@ -158,26 +186,30 @@ def decode_attn(q, cache, block_table, seq_lens, scale, out=None, part_tokens=0)
     seq_lens int32 [batch]; all on the cache's device.  part_tokens 0 picks the
     automatic split plan.  Returns out (fp32 [batch][n_q][hd]).
     """
-    cache.validate()
-    d = cache.device
-    _need(q, "q", torch.float32, d, 3)
-    _need(block_table, "block_table", torch.int32, d, 2)
-    _need(seq_lens, "seq_lens", torch.int32, d, 1)
+    dev, kp, vp, ks, vs = cache._pointers()
+    if not (_ok(q, torch.float32, dev, 3) and _ok(block_table, torch.int32, dev, 2)
+            and _ok(seq_lens, torch.int32, dev, 1)):
+        d = cache.device
+        _need(q, "q", torch.float32, d, 3)
+        _need(block_table, "block_table", torch.int32, d, 2)
+        _need(seq_lens, "seq_lens", torch.int32, d, 1)
     batch, n_q, hd = q.shape
     if hd != cache.hd or block_table.shape[0] != batch or seq_lens.shape[0] != batch:
         raise ValueError("q / block_table / seq_lens / cache shapes disagree")
     if out is None:
         out = torch.empty_like(q)
+    elif not (_ok(out, torch.float32, dev, 3) and out.shape == q.shape):
+        _need(out, "out", torch.float32, cache.device, 3)
+        raise ValueError("out must have q's shape")
+    args = (out.data_ptr(), q.data_ptr(), kp, vp, ks, vs, block_table.data_ptr(), seq_lens.data_ptr(),
+            block_table.shape[1], cache.num_blocks, batch, n_q, cache.n_kv, hd, cache.kv_bs, float(scale),
+            int(part_tokens))
+    # the library allocates its workspace on the current device
+    if torch.cuda.current_device() == dev:
+        _check(lib.q8kv_decode_attn_split(*args, torch.cuda.current_stream(dev).cuda_stream))
     else:
-        _need(out, "out", torch.float32, d, 3)
-        if out.shape != q.shape:
-            raise ValueError("out must have q's shape")
-    with torch.cuda.device(d):
-        _check(lib.q8kv_decode_attn_split(
-            _ptr(out), _ptr(q), _ptr(cache.k_pages), _ptr(cache.v_pages), _ptr(cache.k_scale),
-            _ptr(cache.v_scale), _ptr(block_table), _ptr(seq_lens), block_table.shape[1],
-            cache.num_blocks, batch, n_q, cache.n_kv, hd, cache.kv_bs, float(scale),
-            int(part_tokens), _stream(d)))
+        with torch.cuda.device(dev):
+            _check(lib.q8kv_decode_attn_split(*args, torch.cuda.current_stream(dev).cuda_stream))
     return out
 
 
