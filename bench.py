@@ -184,6 +184,9 @@ def cpu_baseline(w, g, gpu_out_fn, seconds):
     kvb = workloads.kv_bytes(w, lens)
     got = gpu_out_fn(sl)
     err = float(np.abs(got[seqs] - want[seqs]).max())
+    want64 = oracle.decode(q, host, table, sl, scale, use_f64=True, threads=threads)
+    err64 = float(np.abs(got[seqs] - want64[seqs]).max())
+    oracle_drift = float(np.abs(want[seqs] - want64[seqs]).max())
     # q8 vs unquantised fp32 KV on a few heads of the sample
     q8err, rel = [], []
     b = seqs[0]
@@ -201,6 +204,7 @@ def cpu_baseline(w, g, gpu_out_fn, seconds):
     cpu = {"value": round(kvb / step_s / 1e9, 4), "unit": "GB/s", "us_per_step": round(step_s * 1e6, 1),
            "cores": threads, "kind": "oracle", "sample": sample, "sample_seconds": round(secs, 2)}
     parity = {"max_abs_err_vs_oracle": err, "tol": 2e-4, "ok": bool(err <= 2e-4),
+              "max_abs_err_vs_oracle_f64": err64, "oracle_f32_vs_f64": oracle_drift,
               "checked": f"{len(seqs)} sequences x {w.n_q} heads (the CPU sample)",
               "q8_vs_fp32kv_max_abs": float(max(q8err)), "q8_vs_fp32kv_rel_l2": float(max(rel))}
     return cpu, parity

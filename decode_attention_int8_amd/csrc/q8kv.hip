@@ -23,7 +23,10 @@
 //   * P.V runs on v_mfma_f32_16x16x32_f16: rows 0-7 are the heads' weights
 //     w * v_scale rounded to f16 ("hi"), rows 8-15 the f16 remainder
 //     (w * v_scale - hi), so the fp32-faithful weight is carried by two f16
-//     rows in one instruction; the int8 V bytes are exact in f16;
+//     rows in one instruction; the int8 V bytes are exact in f16.  The
+//     weights are taken as 2^(s - M + kWeightShift), so that small ones stay
+//     clear of the f16 subnormals; the shift is common to the accumulator
+//     and the exp-sum and cancels in their quotient;
 //   * ranges longer than one partition are merged by a log-sum-exp combine
 //     kernel in partition order (deterministic).
 // Scores are kept in the log2 domain (softmax scale pre-multiplied by log2 e)
@@ -63,6 +66,12 @@ constexpr int kWaves = 4;         // waves per decode workgroup
 constexpr int kThreads = kWave * kWaves;
 constexpr float kInv127 = 1.0f / 127.0f;
 constexpr float kLog2e = 1.44269504088896340736f;
+// Exponent offset of the P.V weights (see the file comment).  A weight is at
+// most 2^8 * v_scale, within f16 range for v_scale < 255, and the f16
+// subnormal step 2^-24 becomes 2^-32 of a unit weight: the rounding of
+// many small weights no longer adds up to ~1e-4 of the output when one token
+// dominates a long context.
+constexpr float kWeightShift = 8.0f;
 
 static_assert(__builtin_bit_cast(uint32_t, kInv127) == 0x3C010204u, "1/127 must round to 0x3C010204");
 
@@ -489,7 +498,8 @@ __device__ __forceinline__ void tile_load(Tile<HD>& T, const DecodeArgs& a, cons
 
 // One tile of the page's recurrence for the wave's 8 head columns: int8
 // scores on the matrix cores, tile max, rescale of S and the accumulator by
-// 2^(M_old - M_new), weights 2^(s - M_new), P.V on the matrix cores.
+// 2^(M_old - M_new), weights 2^(s - M_new + kWeightShift), P.V on the matrix
+// cores.
 template <int HD>
 __device__ __forceinline__ void tile_compute(const Tile<HD>& T, const int8_t* lq, const float* lqsc, float score_scale,
                                              f32x4 (&acc)[Geo<HD>::BPL], float& M, float& S, int lane) {
@@ -521,6 +531,7 @@ __device__ __forceinline__ void tile_compute(const Tile<HD>& T, const int8_t* lq
     const float m_new = fmaxf(M, mx);
     const float alpha = __builtin_amdgcn_exp2f(M - m_new);
     M = m_new;
+    const float m_shift = m_new - kWeightShift;
 
     f16x8 aw;
     float wsum = 0.0f;
@@ -528,7 +539,7 @@ __device__ __forceinline__ void tile_compute(const Tile<HD>& T, const int8_t* lq
     for (int st = 0; st < 2; ++st) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const float w = __builtin_amdgcn_exp2f(sc[st][j] - m_new);
+            const float w = __builtin_amdgcn_exp2f(sc[st][j] - m_shift);
             wsum += w;
             const float vsj = T.vs[st][j];
             const float W = (4 * r + j) < T.nval[st] ? w * vsj : 0.0f;
