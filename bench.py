@@ -13,8 +13,11 @@ scales, per step, divided by the step time), plus us/step, the roofline of
 the decode launch (algorithmic bytes / mean launch time, from HIP events on
 the launch stream around the timed launches, against 8 TB/s; traffic = HBM
 bytes per launch from the committed counter summary when it matches the
-kernel source), the CPU oracle timed on a bounded sample of the same
-workload, and sampled parity against that oracle.
+kernel source), the per-call distribution (events around each call of a
+second pass: median, min, p90), a plain linear read of the same K+V pools in
+one launch (the streaming ceiling the decode is compared with), the CPU
+oracle timed on a bounded sample of the same workload, and sampled parity
+against that oracle and its fp64 twin.
 """
 import argparse
 import json
@@ -114,7 +117,40 @@ def time_gpu(w, g, steps, warmup, part_tokens):
         step(i)
     e1.record(stream)
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps, out
+    loop_ms = e0.elapsed_time(e1) / steps
+    # the per-call distribution: events around every call of a second pass
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    calls = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+    per_call = {"median": round(float(np.median(calls)), 3), "min": round(float(calls.min()), 3),
+                "p90": round(float(np.percentile(calls, 90)), 3)}
+    return loop_ms, per_call, out
+
+
+def time_stream_read(g, steps):
+    """A plain linear read of the same page pools (K and V) in one launch per
+    step, rotated like the decode steps: the streaming ceiling the decode is
+    compared with.  Returns (us per read, bytes per read)."""
+    import torch
+    import decode_attention_int8_amd as q8
+    R = len(g["caches"])
+    pairs = [(c.k_pages, c.v_pages) for c in g["caches"]]
+    nbytes = sum(t.numel() * t.element_size() for t in pairs[0])
+    for i in range(3):
+        q8.debug_stream_read(*pairs[i % R])
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        q8.debug_stream_read(*pairs[i % R])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / steps, nbytes
 
 
 def profiled_traffic(w):
@@ -230,8 +266,12 @@ def main():
     if args.part_tokens:
         pt, npart = args.part_tokens, -(-w.max_blocks * w.kv_bs // args.part_tokens)
     log(f"KV bytes/step {kvb / 1e6:.2f} MB, {len(g['caches'])} rotated copies, plan {pt} tokens x {npart} partitions")
-    loop_ms, _ = time_gpu(w, g, args.steps, args.warmup, args.part_tokens)
-    log(f"step {loop_ms * 1e3:.2f} us")
+    loop_ms, per_call, _ = time_gpu(w, g, args.steps, args.warmup, args.part_tokens)
+    log(f"step {loop_ms * 1e3:.2f} us (per call: median {per_call['median']}, min {per_call['min']}, "
+        f"p90 {per_call['p90']} us)")
+    read_us, read_bytes = time_stream_read(g, args.steps)
+    read_gbs = read_bytes / (read_us * 1e-6) / 1e9
+    log(f"streaming read of the K+V pools: {read_us:.2f} us, {read_gbs:.0f} GB/s")
     kv_gbs = kvb / (loop_ms * 1e-3) / 1e9
     achieved = algo / (loop_ms * 1e-3) / 1e9
     rec = {
@@ -257,6 +297,10 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": profiled_traffic(w),
                      "algorithmic_bytes": algo, "launch_us": round(loop_ms * 1e3, 3)},
+        "per_call_us": per_call,
+        "stream_read_ceiling": {"gbs": round(read_gbs, 1), "bytes": read_bytes, "us": round(read_us, 3),
+                                "frac_of_peak": round(read_gbs / HBM_PEAK_GBS, 4),
+                                "decode_frac_of_ceiling": round(achieved / read_gbs, 4)},
         "cpu_baseline": None,
     }
     if args.copy_mb > 0:

@@ -31,7 +31,7 @@ class Q8KVError(RuntimeError):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is not built; build it with `python -m decode_attention_int8_amd.build` "
+            f"{LIB_PATH} is not built; build it with `python decode_attention_int8_amd/build.py` "
             "or __graft_entry__.build()")
     lib = ctypes.CDLL(LIB_PATH)
     P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
@@ -43,6 +43,7 @@ def _load():
         "q8kv_release": [],
         "q8kv_debug_quantize_q": [P, P, P, I, I, P],
         "q8kv_debug_block_dots": [P, I, P, P, P, P, I, I, I, I, I, I, I, P],
+        "q8kv_debug_stream_read": [P, ctypes.c_size_t, P, ctypes.c_size_t, P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -219,6 +220,18 @@ def plan(batch, n_q, n_kv, hd, kv_bs, max_blocks):
     pt, npart = ctypes.c_int(), ctypes.c_int()
     _check(lib.q8kv_plan(batch, n_q, n_kv, hd, kv_bs, max_blocks, ctypes.byref(pt), ctypes.byref(npart)))
     return pt.value, npart.value
+
+
+def debug_stream_read(a, b):
+    """Measurement export: one plain linear read of the device tensors a and b
+    (contiguous, sizes multiples of 16 bytes) on the current stream."""
+    for t in (a, b):
+        if not (isinstance(t, torch.Tensor) and t.is_cuda and t.is_contiguous()):
+            raise ValueError("stream-read buffers must be contiguous device tensors")
+    nb = lambda t: t.numel() * t.element_size()
+    with torch.cuda.device(a.device):
+        _check(lib.q8kv_debug_stream_read(a.data_ptr(), nb(a), b.data_ptr(), nb(b),
+                                          torch.cuda.current_stream(a.device).cuda_stream))
 
 
 def release():

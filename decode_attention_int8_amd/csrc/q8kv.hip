@@ -1086,6 +1086,39 @@ __global__ __launch_bounds__(kThreads) void q8kv_debug_dots_kernel(const DotsArg
 }
 
 // ----------------------------------------------------------------------------
+// streaming-read reference: the same bytes as a decode call's page pools,
+// read linearly with non-temporal dwordx4 loads and folded away, so a
+// benchmark can state the decode's rate against what a plain read reaches
+// on the same device in the same run.  The first half of the grid reads
+// buffer a, the second half buffer b; a workgroup reads 32 KB per step
+// (eight 4 KB rows of its 256 threads).
+
+__device__ unsigned g_stream_sink;
+
+__global__ __launch_bounds__(256) void q8kv_stream_read_kernel(const u32x4* __restrict__ a, size_t a16,
+                                                               const u32x4* __restrict__ b, size_t b16) {
+    constexpr int L = 8;
+    const unsigned half = gridDim.x / 2;
+    const bool second = blockIdx.x >= half;
+    const u32x4* p = second ? b : a;
+    const size_t n16 = second ? b16 : a16;
+    const size_t wg = second ? blockIdx.x - half : blockIdx.x;
+    unsigned acc = 0;
+    for (size_t base = wg * 256 * L; base < n16; base += (size_t)half * 256 * L) {
+        u32x4 v[L];
+#pragma unroll
+        for (int k = 0; k < L; ++k) {
+            const size_t i = base + threadIdx.x + 256 * k;
+            v[k] = i < n16 ? __builtin_nontemporal_load(p + i) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int k = 0; k < L; ++k) acc ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
+    }
+    // a volatile store (almost never taken) keeps the reads from being dropped
+    if (acc == 0x9e3779b9u) *reinterpret_cast<volatile unsigned*>(&g_stream_sink) = acc;
+}
+
+// ----------------------------------------------------------------------------
 // host side
 
 thread_local std::string g_err;
@@ -1468,6 +1501,23 @@ int q8kv_debug_block_dots(int32_t* dots, int max_tok, const float* q, const int8
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "dots kernel launch");
+    return Q8KV_OK;
+}
+
+int q8kv_debug_stream_read(const void* a, size_t a_bytes, const void* b, size_t b_bytes, void* stream) {
+    g_err.clear();
+    if (!a || !b) return fail(Q8KV_ENULL, "a buffer pointer is NULL");
+    if (a_bytes % 16 || b_bytes % 16) return fail(Q8KV_EINVAL, "buffer sizes must be multiples of 16 bytes");
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice / hipDeviceGetAttribute");
+    // two workgroups per CU on each buffer: 16 MB in flight on 256 CUs
+    const unsigned grid = 4u * (unsigned)cus;
+    hipLaunchKernelGGL(q8kv_stream_read_kernel, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream),
+                       static_cast<const u32x4*>(a), a_bytes / 16, static_cast<const u32x4*>(b), b_bytes / 16);
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "stream read launch");
     return Q8KV_OK;
 }
 

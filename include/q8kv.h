@@ -57,6 +57,7 @@
 #ifndef Q8KV_H
 #define Q8KV_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -164,6 +165,16 @@ int q8kv_debug_block_dots(int32_t* dots, int max_tok, const float* q, const int8
                           const int32_t* block_table, const int32_t* seq_lens,
                           int max_blocks_per_seq, int num_blocks, int batch, int n_q_heads,
                           int n_kv_heads, int hd, int kv_bs, void* stream);
+
+/*
+ * Measurement export: read a_bytes of device buffer a and b_bytes of device
+ * buffer b (both multiples of 16) in one launch with plain linear
+ * non-temporal loads and discard the data.  A benchmark times it over a
+ * decode call's page pools to state the decode's rate against a plain
+ * streaming read of the same bytes on the same device.  No output; never
+ * writes either buffer.
+ */
+int q8kv_debug_stream_read(const void* a, size_t a_bytes, const void* b, size_t b_bytes, void* stream);
 
 #ifdef __cplusplus
 }

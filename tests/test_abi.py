@@ -14,7 +14,7 @@ NUL = ctypes.c_void_p(0)
 
 def test_exports_every_declared_symbol():
     names = q8.header_symbols()
-    assert len(names) == 8
+    assert len(names) == 9
     for n in names:
         assert hasattr(L, n), n
 
@@ -82,6 +82,11 @@ def test_debug_exports_reject():
     assert L.q8kv_debug_quantize_q(FAKE, FAKE, FAKE, 0, 128, NUL) == q8.Q8KV_OK
     assert L.q8kv_debug_block_dots(FAKE, 4, FAKE, FAKE, FAKE, FAKE, 4, 8, 1, 3, 2, 128, 16, NUL) == q8.Q8KV_EINVAL
     assert L.q8kv_debug_block_dots(NUL, 4, FAKE, FAKE, FAKE, FAKE, 4, 8, 1, 2, 2, 128, 16, NUL) == q8.Q8KV_ENULL
+
+
+def test_stream_read_rejects():
+    assert L.q8kv_debug_stream_read(NUL, 16, FAKE, 16, NUL) == q8.Q8KV_ENULL
+    assert L.q8kv_debug_stream_read(FAKE, 17, FAKE, 16, NUL) == q8.Q8KV_EINVAL
 
 
 def test_plan_is_shape_only_and_sane():
