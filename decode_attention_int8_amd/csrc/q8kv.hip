@@ -1173,7 +1173,9 @@ int check_cache_shape(int num_blocks, int n_kv, int hd, int kv_bs) {
 // Partition plan: a pure function of the shapes, so results never depend on
 // the device.  When the longest possible step spreads over about 512 work
 // items of at most 2048 tokens, use that (one item per workgroup: every
-// resident workgroup streams one long partition).  Larger steps run on the
+// resident workgroup streams one long partition); small steps take up to 512
+// tokens per item (four tiles per wave) while that still leaves 256 items,
+// which halves their merge and startup costs.  Larger steps run on the
 // persistent grid with partitions of 2048-4096 tokens (about 4096 items):
 // long enough that the partition states stay a small fraction of the
 // traffic, short enough that the grid stays balanced to within one item.
@@ -1182,6 +1184,7 @@ int check_cache_shape(int num_blocks, int n_kv, int hd, int kv_bs) {
 void plan(int batch, int n_kv, int max_tokens, int* part_tokens, int* n_parts) {
     const long long units = (long long)batch * n_kv * max_tokens;
     long long pt = (units + 511) / 512;
+    if (pt < 512) pt = std::max(pt, std::min(512LL, units / 256));
     if (pt > 2048) pt = std::min(4096LL, std::max(2048LL, (units + 4095) / 4096));
     pt = (pt + 127) / 128 * 128;
     if (pt < 128) pt = 128;
