@@ -38,6 +38,7 @@ def _load():
     sig = {
         "q8kv_decode_attn": [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, P],
         "q8kv_decode_attn_split": [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, P],
+        "q8kv_append_decode_attn": [P, P, P, P, I, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, P],
         "q8kv_plan": [I, I, I, I, I, I, P, P],
         "q8kv_append": [P, P, P, P, P, P, I, P, I, I, I, I, I, P],
         "q8kv_release": [],
@@ -211,6 +212,51 @@ def decode_attn(q, cache, block_table, seq_lens, scale, out=None, part_tokens=0)
     else:
         with torch.cuda.device(dev):
             _check(lib.q8kv_decode_attn_split(*args, torch.cuda.current_stream(dev).cuda_stream))
+    return out
+
+
+def append_decode_attn(q, cache, k_new, v_new, block_table, seq_lens, scale, out=None, part_tokens=0):
+    """One decode step that also stores the step's own token, in one launch.
+
+    k_new, v_new [batch][n_kv][hd] fp32 or bf16: the new token's K and V
+    rows.  For every sequence with seq_lens[b] >= 1 they are quantised into
+    the cache at position seq_lens[b] - 1 (seq_lens already counts the new
+    token), then out is decode_attn over positions 0 .. seq_lens[b] - 1.
+    Same result, cache bytes and output bits, as cache.append at those slots
+    followed by decode_attn.  Returns out (fp32 [batch][n_q][hd]).
+    """
+    dev, kp, vp, ks, vs = cache._pointers()
+    nd = k_new.dtype if isinstance(k_new, torch.Tensor) else None
+    if not (_ok(q, torch.float32, dev, 3) and _ok(block_table, torch.int32, dev, 2)
+            and _ok(seq_lens, torch.int32, dev, 1) and nd in (torch.float32, torch.bfloat16)
+            and _ok(k_new, nd, dev, 3) and _ok(v_new, nd, dev, 3)):
+        d = cache.device
+        _need(q, "q", torch.float32, d, 3)
+        _need(block_table, "block_table", torch.int32, d, 2)
+        _need(seq_lens, "seq_lens", torch.int32, d, 1)
+        if nd not in (torch.float32, torch.bfloat16):
+            raise TypeError("k_new must be a float32 or bfloat16 tensor")
+        _need(k_new, "k_new", nd, d, 3)
+        _need(v_new, "v_new", nd, d, 3)
+    batch, n_q, hd = q.shape
+    if hd != cache.hd or block_table.shape[0] != batch or seq_lens.shape[0] != batch:
+        raise ValueError("q / block_table / seq_lens / cache shapes disagree")
+    if tuple(k_new.shape) != (batch, cache.n_kv, hd) or v_new.shape != k_new.shape:
+        raise ValueError("k_new / v_new must be [batch][n_kv][hd]")
+    if out is None:
+        out = torch.empty_like(q)
+    elif not (_ok(out, torch.float32, dev, 3) and out.shape == q.shape):
+        _need(out, "out", torch.float32, cache.device, 3)
+        raise ValueError("out must have q's shape")
+    args = (out.data_ptr(), q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
+            1 if nd is torch.bfloat16 else 0, kp, vp, ks, vs, block_table.data_ptr(),
+            seq_lens.data_ptr(), block_table.shape[1], cache.num_blocks, batch, n_q, cache.n_kv, hd,
+            cache.kv_bs, float(scale), int(part_tokens))
+    if torch.cuda.current_device() == dev:
+        _check(lib.q8kv_append_decode_attn(*args, torch.cuda.current_stream(dev).cuda_stream))
+    else:
+        with torch.cuda.device(dev):
+            _check(lib.q8kv_append_decode_attn(*args, torch.cuda.current_stream(dev).cuda_stream))
     return out
 
 

@@ -333,6 +333,12 @@ struct DecodeArgs {
                     // (zero between calls); NULL when q8kv_combine_kernel merges
     int batch, max_blocks, num_blocks, n_q, n_kv, kv_bs, group, part_tokens, n_parts;
     float scale_log2;  // softmax scale * log2(e)
+    // fused append (kernels instantiated with NEW): the new token's K and V
+    // rows [batch][n_kv][hd], fp32 or bf16 (new_bf16), quantised into the
+    // cache at position seq_lens[b] - 1 before it is attended to
+    const void* knew;
+    const void* vnew;
+    int new_bf16;
 };
 
 // Partition states cross workgroups (and XCDs) through buffer loads and
@@ -445,6 +451,85 @@ __device__ void merge_group(const DecodeArgs& a, int b, int kh, int np, float* o
 // Registers of one 32-token tile: the K and V chunks of both sub-tiles and
 // the K/V scales of the lane's rows 4r..4r+3 of each sub-tile (one 16-byte
 // load, shared by the 16 lanes of a row group).
+// ----------------------------------------------------------------------------
+// K/V row quantiser (page "Day 9-2", section 1, and the kscale of section 2:
+// one scale per token and kv head over the whole hd row, the query's absmax
+// rule).  One wave per row, EPL = HD / 64 consecutive elements per lane.
+// q8kv_append and the fused append of the decode kernel both use these, so
+// the two write identical bytes.
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m));
+    return x;
+}
+
+template <int HD>
+struct NewRow {
+    static constexpr int EPL = HD / kWave;
+    float x[EPL];
+};
+
+// The lane's EPL elements of source row `row` ([rows][HD], fp32, or bf16
+// widened exactly).
+template <int HD>
+__device__ __forceinline__ void row_load(NewRow<HD>& r, const void* src, size_t row, int bf16, int lane) {
+    constexpr int EPL = NewRow<HD>::EPL;
+    const size_t off = row * HD + (size_t)lane * EPL;
+    if (bf16) {
+        const uint16_t* s16 = static_cast<const uint16_t*>(src) + off;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) r.x[e] = __uint_as_float((uint32_t)s16[e] << 16);
+    } else {
+        const float* s32 = static_cast<const float*>(src) + off;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) r.x[e] = s32[e];
+    }
+}
+
+// Codes truncate(clamp(x * 127 / absmax, -128, 127)) of the lane's elements,
+// packed little-endian; dq = absmax * fp32(1/127), the row's dequantisation
+// factor (absmax < 1e-6 counts as 1).
+template <int HD>
+__device__ __forceinline__ uint32_t row_quantize(const NewRow<HD>& r, float& dq) {
+    constexpr int EPL = NewRow<HD>::EPL;
+    float am = 0.0f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) am = fmaxf(am, fabsf(r.x[e]));
+    am = q8_guard(wave_max(am));
+    const float inv = 127.0f / am;
+    uint32_t packed = 0;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) packed |= (uint32_t)(q8_code(r.x[e], inv) & 0xff) << (8 * e);
+    dq = am * kInv127;
+    return packed;
+}
+
+// Write a quantised row to page row dst_row (= (block * n_kv + kh) * kv_bs +
+// row_in_page) in the sub-tile byte order, and its factor to scales[dst_row].
+// The lane's EPL columns stay adjacent in both byte orders.
+template <int HD, bool V>
+__device__ __forceinline__ void row_store(int8_t* pages, float* scales, size_t dst_row, int row_in_page,
+                                          uint32_t packed, float dq, int lane) {
+    constexpr int EPL = NewRow<HD>::EPL;
+    const int row = row_in_page % kSub, col = lane * EPL;
+    int8_t* dst = pages + (dst_row - row) * HD + (V ? v_swizzle<HD>(row, col) : k_swizzle(row, col));
+    if constexpr (EPL == 1) *reinterpret_cast<uint8_t*>(dst) = (uint8_t)packed;
+    else if constexpr (EPL == 2) *reinterpret_cast<uint16_t*>(dst) = (uint16_t)packed;
+    else *reinterpret_cast<uint32_t*>(dst) = packed;
+    if (lane == 0) scales[dst_row] = dq;
+}
+
+// The lane's codes in natural column order (for the tile patch below).
+template <int HD>
+__device__ __forceinline__ void row_to_lds(int8_t* row, uint32_t packed, int lane) {
+    constexpr int EPL = NewRow<HD>::EPL;
+    int8_t* d = row + lane * EPL;
+    if constexpr (EPL == 1) *reinterpret_cast<uint8_t*>(d) = (uint8_t)packed;
+    else if constexpr (EPL == 2) *reinterpret_cast<uint16_t*>(d) = (uint16_t)packed;
+    else *reinterpret_cast<uint32_t*>(d) = packed;
+}
+
 template <int HD>
 struct Tile {
     i32x4 k[2][Geo<HD>::NPAIR];
@@ -493,6 +578,48 @@ __device__ __forceinline__ void tile_load(Tile<HD>& T, const DecodeArgs& a, cons
         const int8_t* vsub = a.vp + base * HD;  // wave-uniform
 #pragma unroll
         for (int c = 0; c < Geo<HD>::NPAIR; ++c) T.v[st][c] = stream_load<u32x4>(vsub + 1024 * c + 16 * lane);
+    }
+}
+
+// Fused append: replace row `row32` (0..31) of a loaded tile by the new
+// token's quantised K and V rows, held in LDS in natural column order (lk,
+// lv), and their factors dk, dv.  The tile's own load of that row (the old
+// page bytes) is discarded, so nothing waits for the new row's stores.
+// Register positions follow the sub-tile byte order: K lane 16 r + n holds
+// row n, columns 64 c + 16 r + [0, 16) in chunk c; V lanes of row group r
+// hold rows 4 r .. 4 r + 3, the BPL columns BPL n .. of row 4 r + j being
+// dwords j DPT .. j DPT + DPT - 1 of the lane's 4 DPT dwords (dword u is
+// element u % 4 of chunk u / 4); scales: element j of lane group r.
+template <int HD>
+__device__ __forceinline__ void tile_patch(Tile<HD>& T, const int8_t* lk, const int8_t* lv, float dk, float dv,
+                                           int row32, int lane) {
+    using GG = Geo<HD>;
+    const int r = lane >> 4, n = lane & 15;
+    const int row = row32 & (kSub - 1), j = row & 3;
+    i32x4 knew[GG::NPAIR];
+#pragma unroll
+    for (int c = 0; c < GG::NPAIR; ++c) knew[c] = *reinterpret_cast<const i32x4*>(lk + 64 * c + 16 * r);
+    uint32_t vnew[GG::DPT];
+#pragma unroll
+    for (int d = 0; d < GG::DPT; ++d) vnew[d] = *reinterpret_cast<const uint32_t*>(lv + GG::BPL * n + 4 * d);
+    const bool own_k = n == row, own_v = r == (row >> 2);
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+        if (st != (row32 >> 4)) continue;  // wave-uniform
+#pragma unroll
+        for (int c = 0; c < GG::NPAIR; ++c) T.k[st][c] = own_k ? knew[c] : T.k[st][c];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            T.ks[st][e] = (own_v && e == j) ? dk : T.ks[st][e];
+            T.vs[st][e] = (own_v && e == j) ? dv : T.vs[st][e];
+        }
+#pragma unroll
+        for (int u = 0; u < 4 * GG::NPAIR; ++u) {
+#pragma unroll
+            for (int d = 0; d < GG::DPT; ++d) {
+                if (own_v && u == j * GG::DPT + d) T.v[st][u / 4][u % 4] = vnew[d];
+            }
+        }
     }
 }
 
@@ -588,7 +715,7 @@ __device__ __forceinline__ void tile_compute(const Tile<HD>& T, const int8_t* lq
 // 256 keeps a whole register file.
 enum GridMode { kPersistent = 0, kStatic = 1 };
 
-template <int HD, int MODE>
+template <int HD, int MODE, bool NEW>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(HD == 256 ? 1 : 3))) void
 q8kv_decode_kernel(const DecodeArgs a) {
     using GG = Geo<HD>;
@@ -609,6 +736,7 @@ q8kv_decode_kernel(const DecodeArgs a) {
     __shared__ int lflag;
     __shared__ float2 lms[kFuseRows];
     __shared__ f32x4 lred[kThreads];
+    __shared__ __attribute__((aligned(16))) int8_t lnew[NEW ? 2 * HD : 16];  // fused append: new K, V codes
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -773,6 +901,25 @@ q8kv_decode_kernel(const DecodeArgs a) {
         const int np_b = (L + a.part_tokens - 1) / a.part_tokens;
         const int t1 = min(L, t0 + a.part_tokens);
 
+        // Fused append: the new token is the sequence's last, L - 1.  The
+        // wave whose tile holds it loads its K and V rows now, quantises them
+        // after the query prologue, writes them to the cache and patches
+        // them into that tile's registers.
+        int tail_ts = INT_MIN, tail_blk = -1;
+        NewRow<HD> nk, nv;
+        if constexpr (NEW) {
+            if (!bad && L > t0 && L <= t1) {
+                const int off = L - 1 - t0;
+                if (wid == ((off / kTile) % kWaves)) {
+                    tail_ts = t0 + off / kTile * kTile;
+                    tail_blk = uniform_read(trow, (L - 1) / a.kv_bs);
+                    const size_t src_row = (size_t)b * a.n_kv + kh;
+                    row_load<HD>(nk, a.knew, src_row, a.new_bf16, lane);
+                    row_load<HD>(nv, a.vnew, src_row, a.new_bf16, lane);
+                }
+            }
+        }
+
         // Start streaming the wave's first tile before the query prologue.
         Tile<HD> A;
         {
@@ -784,12 +931,33 @@ q8kv_decode_kernel(const DecodeArgs a) {
         quantize_q_regs<HD, kThreads>(qrows, lq, lqsc, tid);
         __syncthreads();
 
+        float new_dk = 0.0f, new_dv = 0.0f;
+        if constexpr (NEW) {
+            if (tail_ts != INT_MIN) {
+                const uint32_t pk = row_quantize<HD>(nk, new_dk);
+                const uint32_t pv = row_quantize<HD>(nv, new_dv);
+                row_to_lds<HD>(lnew, pk, lane);
+                row_to_lds<HD>(lnew + HD, pv, lane);
+                // an invalid table entry leaves the cache alone (the tile
+                // load has already flagged the row)
+                if ((unsigned)tail_blk < (unsigned)a.num_blocks) {
+                    const int rr = (L - 1) % a.kv_bs;
+                    const size_t dst_row = ((size_t)tail_blk * a.n_kv + kh) * a.kv_bs + rr;
+                    row_store<HD, false>(const_cast<int8_t*>(a.kp), const_cast<float*>(a.ks), dst_row, rr, pk, new_dk, lane);
+                    row_store<HD, true>(const_cast<int8_t*>(a.vp), const_cast<float*>(a.vs), dst_row, rr, pv, new_dv, lane);
+                }
+            }
+        }
+
         f32x4 acc[GG::BPL];
 #pragma unroll
         for (int s = 0; s < GG::BPL; ++s) acc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
         float M = -INFINITY, S = 0.0f;
 
         while (ts < t1) {
+            if constexpr (NEW) {
+                if (ts == tail_ts) tile_patch<HD>(A, lnew, lnew + HD, new_dk, new_dv, L - 1 - ts, lane);
+            }
             tile_compute<HD>(A, lq, lqsc, a.scale_log2, acc, M, S, lane);
             ts += kStride;
             if (ts < t1) {
@@ -976,15 +1144,8 @@ struct AppendArgs {
     long long n_slots;
 };
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m));
-    return x;
-}
-
 template <int HD>
 __global__ __launch_bounds__(256) void q8kv_append_kernel(const AppendArgs a) {
-    constexpr int EPL = HD / kWave;  // elements per lane
     const int lane = threadIdx.x & (kWave - 1);
     const long long row_id = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row_id >= (long long)a.n_tokens * a.n_kv) return;
@@ -993,37 +1154,15 @@ __global__ __launch_bounds__(256) void q8kv_append_kernel(const AppendArgs a) {
     if (slot < 0 || (long long)slot >= a.n_slots) return;
     const int blk = slot / a.kv_bs, rr = slot % a.kv_bs;
     const size_t dst_row = ((size_t)blk * a.n_kv + kh) * a.kv_bs + rr;
-    const size_t src_off = ((size_t)t * a.n_kv + kh) * HD + (size_t)lane * EPL;
-#pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
-        const void* src = pass == 0 ? a.ksrc : a.vsrc;
-        float x[EPL];
-        if (a.src_bf16) {
-            const uint16_t* s16 = static_cast<const uint16_t*>(src) + src_off;
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) x[e] = __uint_as_float((uint32_t)s16[e] << 16);
-        } else {
-            const float* s32 = static_cast<const float*>(src) + src_off;
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) x[e] = s32[e];
-        }
-        float am = 0.0f;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) am = fmaxf(am, fabsf(x[e]));
-        am = q8_guard(wave_max(am));
-        const float inv = 127.0f / am;
-        uint32_t packed = 0;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) packed |= (uint32_t)(q8_code(x[e], inv) & 0xff) << (8 * e);
-        // the lane's EPL columns stay adjacent in both page byte orders
-        const int row = rr % kSub, col = lane * EPL;
-        int8_t* dst = (pass == 0 ? a.kp : a.vp) + (dst_row - row) * HD +
-                      (pass == 0 ? k_swizzle(row, col) : v_swizzle<HD>(row, col));
-        if constexpr (EPL == 1) *reinterpret_cast<uint8_t*>(dst) = (uint8_t)packed;
-        else if constexpr (EPL == 2) *reinterpret_cast<uint16_t*>(dst) = (uint16_t)packed;
-        else *reinterpret_cast<uint32_t*>(dst) = packed;
-        if (lane == 0) (pass == 0 ? a.ks : a.vs)[dst_row] = am * kInv127;
-    }
+    const size_t src_row = (size_t)t * a.n_kv + kh;
+    NewRow<HD> k, v;
+    row_load<HD>(k, a.ksrc, src_row, a.src_bf16, lane);
+    row_load<HD>(v, a.vsrc, src_row, a.src_bf16, lane);
+    float dk, dv;
+    const uint32_t pk = row_quantize<HD>(k, dk);
+    const uint32_t pv = row_quantize<HD>(v, dv);
+    row_store<HD, false>(a.kp, a.ks, dst_row, rr, pk, dk, lane);
+    row_store<HD, true>(a.vp, a.vs, dst_row, rr, pv, dv, lane);
 }
 
 // ----------------------------------------------------------------------------
@@ -1156,7 +1295,7 @@ struct LaunchInfo {
     int resident = 0;     // persistent-grid workgroups that fit at once
     int static_lds = 0;   // dynamic LDS that keeps a static grid at two workgroups per CU
 };
-std::map<std::pair<int, int>, LaunchInfo> g_launch;  // (device, hd)
+std::map<std::pair<int, int>, LaunchInfo> g_launch;  // (device, hd * 2 + fused append)
 
 bool valid_hd(int hd) { return hd == 64 || hd == 128 || hd == 256; }
 bool valid_kv_bs(int bs) { return bs == 16 || bs == 32 || bs == 64 || bs == 128 || bs == 256; }
@@ -1196,20 +1335,20 @@ void plan(int batch, int n_kv, int max_tokens, int* part_tokens, int* n_parts) {
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
-template <int HD>
+template <int HD, bool NEW>
 int launch_info_hd(int dev, LaunchInfo& li) {
     int per_cu = 0, lds_cu = 0;
     hipError_t e = hipDeviceGetAttribute(&li.cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev);
     if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &per_cu, reinterpret_cast<const void*>(q8kv_decode_kernel<HD, kPersistent>), kThreads, 0);
+        &per_cu, reinterpret_cast<const void*>(q8kv_decode_kernel<HD, kPersistent, NEW>), kThreads, 0);
     if (e != hipSuccess) return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
     li.resident = std::max(1, li.cus * std::max(1, per_cu));
     // A static grid of at most two workgroups per CU is spread evenly when a
     // third cannot fit: ask for just over a third of the CU's LDS.
     hipFuncAttributes fa;
-    e = hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(q8kv_decode_kernel<HD, kStatic>));
+    e = hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(q8kv_decode_kernel<HD, kStatic, NEW>));
     if (e != hipSuccess) return hip_fail(e, "hipFuncGetAttributes");
     const int need = (lds_cu / 3 + 256) / 256 * 256;
     const int dyn = need - (int)fa.sharedSizeBytes;
@@ -1217,40 +1356,55 @@ int launch_info_hd(int dev, LaunchInfo& li) {
     return Q8KV_OK;
 }
 
-int launch_info(int dev, int hd, LaunchInfo* out) {
+template <bool NEW>
+int launch_info_new(int dev, int hd, LaunchInfo& li) {
+    return hd == 64 ? launch_info_hd<64, NEW>(dev, li) : hd == 128 ? launch_info_hd<128, NEW>(dev, li)
+                                                                   : launch_info_hd<256, NEW>(dev, li);
+}
+
+int launch_info(int dev, int hd, bool fused, LaunchInfo* out) {
     std::lock_guard<std::mutex> lock(g_mu);
-    auto it = g_launch.find({dev, hd});
+    const std::pair<int, int> key{dev, hd * 2 + (fused ? 1 : 0)};
+    auto it = g_launch.find(key);
     if (it != g_launch.end()) {
         *out = it->second;
         return Q8KV_OK;
     }
     LaunchInfo li;
-    const int rc = hd == 64 ? launch_info_hd<64>(dev, li) : hd == 128 ? launch_info_hd<128>(dev, li)
-                                                                      : launch_info_hd<256>(dev, li);
+    const int rc = fused ? launch_info_new<true>(dev, hd, li) : launch_info_new<false>(dev, hd, li);
     if (rc) return rc;
-    g_launch[{dev, hd}] = li;
+    g_launch[key] = li;
     *out = li;
     return Q8KV_OK;
 }
 
-template <int HD>
+template <int HD, bool NEW>
 void launch_decode_hd(int mode, unsigned grid, size_t lds, hipStream_t st, const DecodeArgs& da) {
-    if (mode == kPersistent) hipLaunchKernelGGL((q8kv_decode_kernel<HD, kPersistent>), dim3(grid), dim3(kThreads), 0, st, da);
-    else hipLaunchKernelGGL((q8kv_decode_kernel<HD, kStatic>), dim3(grid), dim3(kThreads), lds, st, da);
+    if (mode == kPersistent) hipLaunchKernelGGL((q8kv_decode_kernel<HD, kPersistent, NEW>), dim3(grid), dim3(kThreads), 0, st, da);
+    else hipLaunchKernelGGL((q8kv_decode_kernel<HD, kStatic, NEW>), dim3(grid), dim3(kThreads), lds, st, da);
+}
+
+template <bool NEW>
+void launch_decode_new(int hd, int mode, unsigned grid, size_t lds, hipStream_t st, const DecodeArgs& da) {
+    if (hd == 64) launch_decode_hd<64, NEW>(mode, grid, lds, st, da);
+    else if (hd == 128) launch_decode_hd<128, NEW>(mode, grid, lds, st, da);
+    else launch_decode_hd<256, NEW>(mode, grid, lds, st, da);
 }
 
 void launch_decode(int hd, int mode, unsigned grid, size_t lds, hipStream_t st, const DecodeArgs& da) {
-    if (hd == 64) launch_decode_hd<64>(mode, grid, lds, st, da);
-    else if (hd == 128) launch_decode_hd<128>(mode, grid, lds, st, da);
-    else launch_decode_hd<256>(mode, grid, lds, st, da);
+    if (da.knew) launch_decode_new<true>(hd, mode, grid, lds, st, da);
+    else launch_decode_new<false>(hd, mode, grid, lds, st, da);
 }
 
 int decode_impl(float* out, const float* q, const int8_t* kp, const int8_t* vp, const float* ks,
                 const float* vs, const int32_t* table, const int32_t* lens, int max_blocks,
                 int num_blocks, int batch, int n_q, int n_kv, int hd, int kv_bs, float scale,
-                int part_tokens, void* stream) {
+                int part_tokens, void* stream, const void* knew = nullptr, const void* vnew = nullptr,
+                int new_dtype = 0) {
     if (!out || !q || !kp || !vp || !ks || !vs || !table || !lens)
         return fail(Q8KV_ENULL, "a tensor pointer is NULL");
+    if ((knew == nullptr) != (vnew == nullptr)) return fail(Q8KV_ENULL, "k_new and v_new must both be given");
+    if (knew && new_dtype != 0 && new_dtype != 1) return fail(Q8KV_EINVAL, "src_dtype must be 0 (fp32) or 1 (bf16)");
     if (batch <= 0 || n_q <= 0) return fail(Q8KV_EINVAL, "batch (%d) and n_q_heads (%d) must be positive", batch, n_q);
     if (batch > kMaxBatch) return fail(Q8KV_EINVAL, "batch (%d) exceeds %d sequences per call", batch, kMaxBatch);
     int rc = check_cache_shape(num_blocks, n_kv, hd, kv_bs);
@@ -1280,11 +1434,12 @@ int decode_impl(float* out, const float* q, const int8_t* kp, const int8_t* vp, 
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
     LaunchInfo li;
-    rc = launch_info(dev, hd, &li);
+    rc = launch_info(dev, hd, knew != nullptr, &li);
     if (rc) return rc;
     const unsigned grid = (unsigned)std::min<long long>(items, li.resident);
     DecodeArgs da{out, q, kp, vp, ks, vs, table, lens, nullptr, nullptr, nullptr, nullptr,
-                  batch, max_blocks, num_blocks, n_q, n_kv, kv_bs, G, pt, np, scale * kLog2e};
+                  batch, max_blocks, num_blocks, n_q, n_kv, kv_bs, G, pt, np, scale * kLog2e,
+                  knew, vnew, new_dtype};
     if (items > (long long)grid) {
         std::lock_guard<std::mutex> lock(g_mu);
         Workspace& w = g_ws[{dev, stream}];
@@ -1400,6 +1555,19 @@ int q8kv_decode_attn_split(float* out, const float* q, const int8_t* k_pages, co
     return decode_impl(out, q, k_pages, v_pages, k_scale, v_scale, block_table, seq_lens,
                        max_blocks_per_seq, num_blocks, batch, n_q_heads, n_kv_heads, hd, kv_bs,
                        scale, part_tokens, stream);
+}
+
+int q8kv_append_decode_attn(float* out, const float* q, const void* k_new, const void* v_new,
+                            int src_dtype, int8_t* k_pages, int8_t* v_pages, float* k_scale,
+                            float* v_scale, const int32_t* block_table, const int32_t* seq_lens,
+                            int max_blocks_per_seq, int num_blocks, int batch, int n_q_heads,
+                            int n_kv_heads, int hd, int kv_bs, float scale, int part_tokens,
+                            void* stream) {
+    g_err.clear();
+    if (!k_new || !v_new) return fail(Q8KV_ENULL, "k_new / v_new is NULL");
+    return decode_impl(out, q, k_pages, v_pages, k_scale, v_scale, block_table, seq_lens,
+                       max_blocks_per_seq, num_blocks, batch, n_q_heads, n_kv_heads, hd, kv_bs,
+                       scale, part_tokens, stream, k_new, v_new, src_dtype);
 }
 
 int q8kv_plan(int batch, int n_q_heads, int n_kv_heads, int hd, int kv_bs, int max_blocks_per_seq,

@@ -115,6 +115,34 @@ int q8kv_decode_attn_split(float* out, const float* q,
                            float scale, int part_tokens, void* stream);
 
 /*
+ * Append the step's new token and attend to it in one launch: for every
+ * sequence b with 1 <= seq_lens[b] <= max_blocks_per_seq * kv_bs, the new
+ * token's K and V rows are quantised exactly as q8kv_append does and written
+ * at position seq_lens[b] - 1, i.e. slot block_table[b][(L-1) / kv_bs] * kv_bs
+ * + (L-1) % kv_bs with L = seq_lens[b] (the page-table slot rule of the page
+ * "deepseek-attention-div64" (beaiera.top), section on top-k indices and slot
+ * mapping); then out is what q8kv_decode_attn_split returns over positions
+ * 0 .. L-1 of the updated cache, the new token included.  The fused-kernel
+ * idea follows the same page's section on its fused quantise-and-cache-write
+ * kernel.  The result equals q8kv_append with that slot mapping followed by
+ * q8kv_decode_attn_split, bit for bit (cache and output).
+ *
+ * k_new, v_new [batch][n_kv_heads][hd], fp32 (src_dtype 0) or bf16
+ *              (src_dtype 1), the new token's rows (q's token).
+ * Sequences with seq_lens[b] <= 0 get a zero row and nothing is written; a
+ * sequence whose new slot's table entry lies outside [0, num_blocks), or
+ * whose length exceeds max_blocks_per_seq * kv_bs, gets a NaN row and
+ * nothing is written.  The new slots of different sequences must be
+ * distinct.  Other arguments as for q8kv_decode_attn_split.
+ */
+int q8kv_append_decode_attn(float* out, const float* q, const void* k_new, const void* v_new,
+                            int src_dtype, int8_t* k_pages, int8_t* v_pages, float* k_scale,
+                            float* v_scale, const int32_t* block_table, const int32_t* seq_lens,
+                            int max_blocks_per_seq, int num_blocks, int batch, int n_q_heads,
+                            int n_kv_heads, int hd, int kv_bs, float scale, int part_tokens,
+                            void* stream);
+
+/*
  * The automatic partition plan for a decode shape (host only, no HIP call):
  * *part_tokens = tokens per partition, *n_parts = partitions of the longest
  * possible sequence (max_blocks_per_seq * kv_bs tokens).

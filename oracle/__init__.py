@@ -216,6 +216,38 @@ def block_dots(q, cache, block_table, seq_lens, max_tok=None):
     return dots
 
 
+def new_token_slots(block_table, seq_lens, kv_bs, num_blocks):
+    """Cache slot of each sequence's newest token, position L - 1 with
+    L = seq_lens[b]: physical block block_table[b][(L-1) // kv_bs] times kv_bs
+    plus the row (L-1) % kv_bs -- the block-number x block-size + offset rule
+    for turning a sequence position into a global cache slot (page
+    "deepseek-attention-div64", beaiera.top, section on mapping top-k indices
+    to global slot ids).  -1 (skip) where L <= 0, where L - 1 lies past the
+    table row, or where the entry is outside [0, num_blocks)."""
+    bt = np.asarray(block_table)
+    slots = np.full(bt.shape[0], -1, np.int32)
+    for b in range(bt.shape[0]):
+        L = int(seq_lens[b])
+        if L <= 0 or (L - 1) // kv_bs >= bt.shape[1]:
+            continue
+        blk = int(bt[b, (L - 1) // kv_bs])
+        if 0 <= blk < num_blocks:
+            slots[b] = blk * kv_bs + (L - 1) % kv_bs
+    return slots
+
+
+def append_decode(q, cache, k_new, v_new, block_table, seq_lens, scale, part_tokens=0,
+                  use_f64=False, threads=1):
+    """One decode step that first stores the step's own token: quantise the
+    new K/V rows k_new, v_new [batch][n_kv][hd] into ``cache`` (in place) at
+    each sequence's newest slot (``new_token_slots``), then ``decode`` over
+    positions 0 .. seq_lens[b] - 1, the new token included.  Returns out."""
+    slots = new_token_slots(block_table, seq_lens, cache.kv_bs, cache.num_blocks)
+    cache.append(k_new, v_new, slots)
+    return decode(q, cache, block_table, seq_lens, scale, part_tokens=part_tokens,
+                  use_f64=use_f64, threads=threads)
+
+
 # ----------------------------------------------------------------------------
 # float64 references in plain numpy
 

@@ -14,7 +14,7 @@ NUL = ctypes.c_void_p(0)
 
 def test_exports_every_declared_symbol():
     names = q8.header_symbols()
-    assert len(names) == 9
+    assert len(names) == 10
     for n in names:
         assert hasattr(L, n), n
 
@@ -27,6 +27,34 @@ def decode(**kw):
     return L.q8kv_decode_attn_split(a["out"], a["q"], a["kp"], a["vp"], a["ks"], a["vs"], a["bt"],
                                     a["sl"], a["max_blocks"], a["num_blocks"], a["batch"], a["n_q"],
                                     a["n_kv"], a["hd"], a["kv_bs"], a["scale"], a["part"], NUL)
+
+
+def append_decode(**kw):
+    a = dict(out=FAKE, q=FAKE, kn=FAKE, vn=FAKE, dt=0, kp=FAKE, vp=FAKE, ks=FAKE, vs=FAKE, bt=FAKE,
+             sl=FAKE, max_blocks=8, num_blocks=16, batch=2, n_q=8, n_kv=2, hd=128, kv_bs=16,
+             scale=0.088, part=0)
+    a.update(kw)
+    return L.q8kv_append_decode_attn(a["out"], a["q"], a["kn"], a["vn"], a["dt"], a["kp"], a["vp"],
+                                     a["ks"], a["vs"], a["bt"], a["sl"], a["max_blocks"],
+                                     a["num_blocks"], a["batch"], a["n_q"], a["n_kv"], a["hd"],
+                                     a["kv_bs"], a["scale"], a["part"], NUL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kn=NUL), q8.Q8KV_ENULL),
+    (dict(vn=NUL), q8.Q8KV_ENULL),
+    (dict(kp=NUL), q8.Q8KV_ENULL),
+    (dict(out=NUL), q8.Q8KV_ENULL),
+    (dict(dt=2), q8.Q8KV_EINVAL),
+    (dict(dt=-1), q8.Q8KV_EINVAL),
+    (dict(hd=96), q8.Q8KV_EINVAL),
+    (dict(n_q=6, n_kv=4), q8.Q8KV_EINVAL),
+    (dict(batch=0), q8.Q8KV_EINVAL),
+    (dict(part=48), q8.Q8KV_EINVAL),
+])
+def test_append_decode_rejects_before_any_hip_call(kw, code):
+    assert append_decode(**kw) == code
+    assert q8.last_error() != ""
 
 
 @pytest.mark.parametrize("kw,code", [
