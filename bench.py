@@ -17,7 +17,9 @@ kernel source), the per-call distribution (events around each call of a
 second pass: median, min, p90), a plain linear read of the same K+V pools in
 one launch (the streaming ceiling the decode is compared with), the CPU
 oracle timed on a bounded sample of the same workload, and sampled parity
-against that oracle and its fp64 twin.
+against that oracle and its fp64 twin.  A last leg times the fused step
+that also stores each sequence's new token (q8kv_append_decode_attn) against
+the same work as two launches (q8kv_append, then q8kv_decode_attn).
 """
 import argparse
 import json
@@ -53,6 +55,7 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="target CPU time of the oracle baseline sample")
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline and parity sample")
+    p.add_argument("--no-fused", action="store_true", help="skip the fused append + decode leg")
     p.add_argument("--part-tokens", type=int, default=0, help="override the split plan (0: automatic)")
     p.add_argument("--copy-mb", type=float, default=0.0,
                    help="after timing, run one device-to-device copy of this many MiB (a known-size "
@@ -131,6 +134,55 @@ def time_gpu(w, g, steps, warmup, part_tokens):
     return loop_ms, per_call, out
 
 
+def time_append_decode(w, g, steps, warmup, part_tokens):
+    """The fused step (q8kv_append_decode_attn: store each sequence's new
+    token at position L-1, then attend over 0..L-1) against the same work as
+    two launches (q8kv_append at those slots, then q8kv_decode_attn), both
+    rotated over the cold copies.  The new rows are seeded N(0,1) draws.
+    Returns a dict of per-step times in us."""
+    import torch
+    import decode_attention_int8_amd as q8
+    scale = workloads.softmax_scale(w.hd)
+    R = len(g["caches"])
+    dev = g["q"].device
+    rng = np.random.default_rng(w.key + 7000)
+    k_new = torch.from_numpy(rng.standard_normal((w.batch, w.n_kv, w.hd), dtype=np.float32)).to(dev)
+    v_new = torch.from_numpy(rng.standard_normal((w.batch, w.n_kv, w.hd), dtype=np.float32)).to(dev)
+    lens, table = g["lens"], g["table"]
+    slots = np.array([int(table[b, (L - 1) // w.kv_bs]) * w.kv_bs + (L - 1) % w.kv_bs if L > 0 else -1
+                      for b, L in enumerate(lens.tolist())], np.int32)
+    slots_d = torch.from_numpy(slots).to(dev)
+    out = torch.empty_like(g["q"])
+    stream = torch.cuda.current_stream()
+
+    def fused(i):
+        q8.append_decode_attn(g["q"], g["caches"][i % R], k_new, v_new, g["table_d"], g["lens_d"], scale,
+                              out=out, part_tokens=part_tokens)
+
+    def append(i):
+        g["caches"][i % R].append(k_new, v_new, slots_d)
+
+    def two(i):
+        append(i)
+        q8.decode_attn(g["q"], g["caches"][i % R], g["table_d"], g["lens_d"], scale, out=out,
+                       part_tokens=part_tokens)
+
+    def timed(fn):
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(steps):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / steps
+
+    res = {"fused_us": timed(fused), "two_launch_us": timed(two), "append_us": timed(append)}
+    return {k: round(v, 3) for k, v in res.items()}
+
+
 def time_stream_read(g, steps):
     """A plain linear read of the same page pools (K and V) in one launch per
     step, rotated like the decode steps: the streaming ceiling the decode is
@@ -153,14 +205,14 @@ def time_stream_read(g, steps):
     return e0.elapsed_time(e1) * 1e3 / steps, nbytes
 
 
-def profiled_traffic(w):
+def profiled_traffic(w, key=None):
     """HBM bytes per launch from the committed counter summary, if it was
     taken on the current kernel source (else None)."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "decode_traffic.json")
     if not os.path.exists(path):
         return None
-    rec = json.load(open(path)).get(w.name)
+    rec = json.load(open(path)).get(key or w.name)
     if not rec:
         return None
     src = b"".join(open(os.path.join(ROOT, f), "rb").read()
@@ -324,6 +376,17 @@ def main():
         cpu, parity = cpu_baseline(w, g, gpu_out, args.cpu_seconds)
         rec["cpu_baseline"] = cpu
         rec["parity"] = parity
+    if not args.no_fused:
+        # last: it rewrites each sequence's newest row with the seeded new rows
+        fa = time_append_decode(w, g, args.steps, args.warmup, args.part_tokens)
+        new_bytes = w.batch * w.n_kv * (2 * w.hd * 4 + 2 * (w.hd + 4))
+        fa["algorithmic_bytes"] = algo + new_bytes
+        fa["gbs"] = round((algo + new_bytes) / (fa["fused_us"] * 1e-6) / 1e9, 2)
+        fa["saved_us"] = round(fa["two_launch_us"] - fa["fused_us"], 3)
+        fa["traffic"] = profiled_traffic(w, f"{w.name}:append_decode")
+        log(f"append+decode: fused {fa['fused_us']} us, append then decode {fa['two_launch_us']} us "
+            f"(append alone {fa['append_us']} us)")
+        rec["append_decode"] = fa
     print(json.dumps(rec), flush=True)
 
 

@@ -164,21 +164,26 @@ class PagedKVCache:
 
     def append(self, k_src, v_src, slot_mapping):
         """Quantise k_src/v_src [n_tokens][n_kv][hd] (fp32 or bf16) into slots."""
-        self.validate()
-        d = self.device
-        if k_src.dtype not in (torch.float32, torch.bfloat16):
-            raise TypeError("k_src must be float32 or bfloat16")
-        _need(k_src, "k_src", k_src.dtype, d, 3)
-        _need(v_src, "v_src", k_src.dtype, d, 3)
-        _need(slot_mapping, "slot_mapping", torch.int32, d, 1)
+        dev, kp, vp, ks, vs = self._pointers()
+        sd = k_src.dtype if isinstance(k_src, torch.Tensor) else None
+        if not (sd in (torch.float32, torch.bfloat16) and _ok(k_src, sd, dev, 3) and _ok(v_src, sd, dev, 3)
+                and _ok(slot_mapping, torch.int32, dev, 1)):
+            d = self.device
+            if sd not in (torch.float32, torch.bfloat16):
+                raise TypeError("k_src must be a float32 or bfloat16 tensor")
+            _need(k_src, "k_src", sd, d, 3)
+            _need(v_src, "v_src", sd, d, 3)
+            _need(slot_mapping, "slot_mapping", torch.int32, d, 1)
         n = slot_mapping.shape[0]
         if tuple(k_src.shape) != (n, self.n_kv, self.hd) or v_src.shape != k_src.shape:
             raise ValueError("k_src/v_src must be [n_tokens][n_kv][hd] matching slot_mapping")
-        with torch.cuda.device(d):
-            _check(lib.q8kv_append(_ptr(self.k_pages), _ptr(self.v_pages), _ptr(self.k_scale),
-                                   _ptr(self.v_scale), _ptr(k_src), _ptr(v_src),
-                                   1 if k_src.dtype == torch.bfloat16 else 0, _ptr(slot_mapping),
-                                   n, self.num_blocks, self.n_kv, self.hd, self.kv_bs, _stream(d)))
+        args = (kp, vp, ks, vs, k_src.data_ptr(), v_src.data_ptr(), 1 if sd is torch.bfloat16 else 0,
+                slot_mapping.data_ptr(), n, self.num_blocks, self.n_kv, self.hd, self.kv_bs)
+        if torch.cuda.current_device() == dev:
+            _check(lib.q8kv_append(*args, torch.cuda.current_stream(dev).cuda_stream))
+        else:
+            with torch.cuda.device(dev):
+                _check(lib.q8kv_append(*args, torch.cuda.current_stream(dev).cuda_stream))
 
 
 def decode_attn(q, cache, block_table, seq_lens, scale, out=None, part_tokens=0):

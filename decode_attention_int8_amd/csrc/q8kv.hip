@@ -623,6 +623,66 @@ __device__ __forceinline__ void tile_patch(Tile<HD>& T, const int8_t* lk, const 
     }
 }
 
+// Fused append, by the wave whose tile holds the new token L - 1 of sequence
+// b: load the token's K and V rows, quantise them as q8kv_append does into
+// LDS (codes in natural column order, factors, the page's block) for
+// tile_patch, and write them to the cache after the tile loop.  On static
+// grids the rows are loaded behind the item's first tile and quantised after
+// the query prologue; on persistent grids (whose item loop leaves fewer
+// registers) they are loaded and quantised before the first tile is issued.
+__device__ __forceinline__ const DecodeArgs* kernel_args() {
+    // read here from the kernel argument segment rather than kept in
+    // registers from the kernel's start: only this rare path needs them
+    const DecodeArgs* ka = (const DecodeArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+    asm volatile("" : "+s"(ka));
+    return ka;
+}
+
+template <int HD>
+__device__ __forceinline__ void load_new_rows(NewRow<HD>& nk, NewRow<HD>& nv, const void* knew, const void* vnew,
+                                              int bf16, int b, int n_kv, int kh, int lane) {
+    const size_t src_row = (size_t)b * n_kv + kh;
+    row_load<HD>(nk, knew, src_row, bf16, lane);
+    row_load<HD>(nv, vnew, src_row, bf16, lane);
+}
+
+// lnew [2][HD] codes, lsc [2] factors, *lblk the new token's physical block.
+template <int HD>
+__device__ __forceinline__ void prepare_new_token(const NewRow<HD>& nk, const NewRow<HD>& nv, int blk, int8_t* lnew,
+                                                  float* lsc, int* lblk, int lane) {
+    float dk, dv;
+    const uint32_t pk = row_quantize<HD>(nk, dk);
+    const uint32_t pv = row_quantize<HD>(nv, dv);
+    row_to_lds<HD>(lnew, pk, lane);
+    row_to_lds<HD>(lnew + HD, pv, lane);
+    if (lane == 0) {
+        lsc[0] = dk;
+        lsc[1] = dv;
+        *lblk = blk;
+    }
+}
+
+// After the tile loop: write the quantised rows to the cache in its byte
+// order, unless the block lies outside the pool.
+template <int HD>
+__device__ __forceinline__ void store_new_token(const DecodeArgs& a, int kh, int L, const int8_t* lnew,
+                                                const float* lsc, const int* lblk, int lane) {
+    const int n_kv = a.n_kv, kv_bs = a.kv_bs, num_blocks = a.num_blocks;
+    constexpr int EPL = NewRow<HD>::EPL;
+    const int blk = __builtin_amdgcn_readfirstlane(*lblk);
+    if ((unsigned)blk >= (unsigned)num_blocks) return;
+    uint32_t pk = 0, pv = 0;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+        pk |= (uint32_t)(uint8_t)lnew[lane * EPL + e] << (8 * e);
+        pv |= (uint32_t)(uint8_t)lnew[HD + lane * EPL + e] << (8 * e);
+    }
+    const int rr = (L - 1) % kv_bs;
+    const size_t dst_row = ((size_t)blk * n_kv + kh) * kv_bs + rr;
+    row_store<HD, false>(const_cast<int8_t*>(a.kp), const_cast<float*>(a.ks), dst_row, rr, pk, lsc[0], lane);
+    row_store<HD, true>(const_cast<int8_t*>(a.vp), const_cast<float*>(a.vs), dst_row, rr, pv, lsc[1], lane);
+}
+
 // One tile of the page's recurrence for the wave's 8 head columns: int8
 // scores on the matrix cores, tile max, rescale of S and the accumulator by
 // 2^(M_old - M_new), weights 2^(s - M_new + kWeightShift), P.V on the matrix
@@ -736,7 +796,10 @@ q8kv_decode_kernel(const DecodeArgs a) {
     __shared__ int lflag;
     __shared__ float2 lms[kFuseRows];
     __shared__ f32x4 lred[kThreads];
-    __shared__ __attribute__((aligned(16))) int8_t lnew[NEW ? 2 * HD : 16];  // fused append: new K, V codes
+    // fused append: the new token's codes, factors and block
+    __shared__ __attribute__((aligned(16))) int8_t lnew[NEW ? 2 * HD : 16];
+    __shared__ float lnew_sc[2];
+    __shared__ int lnew_blk;
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -834,6 +897,12 @@ q8kv_decode_kernel(const DecodeArgs a) {
     // ticket (offset by the grid size) when items can outnumber workgroups.
     int item = blockIdx.x;
     for (;;) {
+        // The lane-derived values of an item are derived afresh from an
+        // opaque copy of the thread index in every item: hoisted out of the
+        // item loop, they would be held (and spilled) across the tile loop.
+        int itid = tid;
+        if constexpr (!STATIC) asm volatile("" : "+v"(itid));
+        const int ilane = itid & (kWave - 1);
         // Item coordinates are wave-uniform; saying so keeps the block-table
         // and length reads on the scalar path (a vector load would queue
         // behind the in-flight tile loads and wait for all of them).
@@ -870,7 +939,7 @@ q8kv_decode_kernel(const DecodeArgs a) {
         // the query rows' loads go out first: the quantisation then waits for
         // them alone, not for the first tile queued behind them
         QRows<HD, kThreads> qrows;
-        load_q_rows<HD, kThreads>(qrows, a.q + ((size_t)b * a.n_q + (size_t)kh * G) * HD, G, tid);
+        load_q_rows<HD, kThreads>(qrows, a.q + ((size_t)b * a.n_q + (size_t)kh * G) * HD, G, itid);
         const int32_t* trow = a.table + (size_t)b * a.max_blocks;
         const int t0 = part * a.part_tokens;
         // The first tile's table reads, those of the item's first tile (a
@@ -894,17 +963,15 @@ q8kv_decode_kernel(const DecodeArgs a) {
             // sequence's rows are zeroed by its partition-0 slots
             if (t0 >= L) {
                 if (part == 0)
-                    for (int e = tid; e < G * HD; e += kThreads) out_rows[e] = 0.0f;
+                    for (int e = itid; e < G * HD; e += kThreads) out_rows[e] = 0.0f;
                 return;
             }
         }
         const int np_b = (L + a.part_tokens - 1) / a.part_tokens;
         const int t1 = min(L, t0 + a.part_tokens);
 
-        // Fused append: the new token is the sequence's last, L - 1.  The
-        // wave whose tile holds it loads its K and V rows now, quantises them
-        // after the query prologue, writes them to the cache and patches
-        // them into that tile's registers.
+        // Fused append: the new token is the sequence's last, L - 1; the wave
+        // whose tile holds it stores it and patches it into that tile.
         int tail_ts = INT_MIN, tail_blk = -1;
         NewRow<HD> nk, nv;
         if constexpr (NEW) {
@@ -913,10 +980,17 @@ q8kv_decode_kernel(const DecodeArgs a) {
                 if (wid == ((off / kTile) % kWaves)) {
                     tail_ts = t0 + off / kTile * kTile;
                     tail_blk = uniform_read(trow, (L - 1) / a.kv_bs);
-                    const size_t src_row = (size_t)b * a.n_kv + kh;
-                    row_load<HD>(nk, a.knew, src_row, a.new_bf16, lane);
-                    row_load<HD>(nv, a.vnew, src_row, a.new_bf16, lane);
                 }
+            }
+        }
+        if constexpr (NEW && !STATIC) {
+            // persistent grids: the tail wave loads and quantises the new
+            // rows before it issues its first tile loads, while few
+            // registers are live (the item loop leaves few to spare)
+            if (tail_ts != INT_MIN) {
+                const DecodeArgs* ka = kernel_args();
+                load_new_rows<HD>(nk, nv, ka->knew, ka->vnew, ka->new_bf16, b, a.n_kv, kh, ilane);
+                prepare_new_token<HD>(nk, nv, tail_blk, lnew, lnew_sc, &lnew_blk, ilane);
             }
         }
 
@@ -925,28 +999,22 @@ q8kv_decode_kernel(const DecodeArgs a) {
         {
             const bool own = ts < t1;
             const int blk0[2] = {own ? blk_first[0] : blk_t0[0], own ? blk_first[1] : blk_t0[1]};
-            tile_load<HD>(A, a, blk0, kh, own ? ts : t0, t1, lane, bad);
+            tile_load<HD>(A, a, blk0, kh, own ? ts : t0, t1, ilane, bad);
+        }
+        if constexpr (NEW && STATIC) {
+            // static grids: the new rows' loads go out behind the first tile
+            if (tail_ts != INT_MIN) load_new_rows<HD>(nk, nv, a.knew, a.vnew, a.new_bf16, b, a.n_kv, kh, ilane);
         }
 
-        quantize_q_regs<HD, kThreads>(qrows, lq, lqsc, tid);
+        quantize_q_regs<HD, kThreads>(qrows, lq, lqsc, itid);
         __syncthreads();
-
-        float new_dk = 0.0f, new_dv = 0.0f;
-        if constexpr (NEW) {
-            if (tail_ts != INT_MIN) {
-                const uint32_t pk = row_quantize<HD>(nk, new_dk);
-                const uint32_t pv = row_quantize<HD>(nv, new_dv);
-                row_to_lds<HD>(lnew, pk, lane);
-                row_to_lds<HD>(lnew + HD, pv, lane);
-                // an invalid table entry leaves the cache alone (the tile
-                // load has already flagged the row)
-                if ((unsigned)tail_blk < (unsigned)a.num_blocks) {
-                    const int rr = (L - 1) % a.kv_bs;
-                    const size_t dst_row = ((size_t)tail_blk * a.n_kv + kh) * a.kv_bs + rr;
-                    row_store<HD, false>(const_cast<int8_t*>(a.kp), const_cast<float*>(a.ks), dst_row, rr, pk, new_dk, lane);
-                    row_store<HD, true>(const_cast<int8_t*>(a.vp), const_cast<float*>(a.vs), dst_row, rr, pv, new_dv, lane);
-                }
-            }
+        // static grids: the tail wave quantises the new rows (which arrive
+        // with its first tile) while its second tile is in flight, or here
+        // when the new token is in its first tile
+        const int ts_second = ts + kStride;
+        if constexpr (NEW && STATIC) {
+            if (tail_ts != INT_MIN && tail_ts < ts_second)
+                prepare_new_token<HD>(nk, nv, tail_blk, lnew, lnew_sc, &lnew_blk, ilane);
         }
 
         f32x4 acc[GG::BPL];
@@ -956,15 +1024,23 @@ q8kv_decode_kernel(const DecodeArgs a) {
 
         while (ts < t1) {
             if constexpr (NEW) {
-                if (ts == tail_ts) tile_patch<HD>(A, lnew, lnew + HD, new_dk, new_dv, L - 1 - ts, lane);
+                if (ts == tail_ts) tile_patch<HD>(A, lnew, lnew + HD, lnew_sc[0], lnew_sc[1], L - 1 - ts, ilane);
             }
-            tile_compute<HD>(A, lq, lqsc, a.scale_log2, acc, M, S, lane);
+            tile_compute<HD>(A, lq, lqsc, a.scale_log2, acc, M, S, ilane);
             ts += kStride;
             if (ts < t1) {
                 int blk[2];
                 tile_blocks(trow, ts, a.kv_bs, a.max_blocks, blk);
-                tile_load<HD>(A, a, blk, kh, ts, t1, lane, bad);
+                tile_load<HD>(A, a, blk, kh, ts, t1, ilane, bad);
+                if constexpr (NEW && STATIC) {
+                    if (tail_ts != INT_MIN && ts == ts_second)
+                        prepare_new_token<HD>(nk, nv, tail_blk, lnew, lnew_sc, &lnew_blk, ilane);
+                }
             }
+        }
+
+        if constexpr (NEW) {
+            if (tail_ts != INT_MIN) store_new_token<HD>(a, kh, L, lnew, lnew_sc, &lnew_blk, ilane);
         }
 
         // wave state -> LDS: exp-sum over the four row groups, hi + lo rows
@@ -975,12 +1051,12 @@ q8kv_decode_kernel(const DecodeArgs a) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[s][j] = swap32_sum(acc[s][j]);
         }
-        if (lane < kHeadGroup) {
-            lM[wid][lane] = M;
-            lS[wid][lane] = S;
+        if (ilane < kHeadGroup) {
+            lM[wid][ilane] = M;
+            lS[wid][ilane] = S;
         }
-        if (r_of(lane) < 2) {
-            const int r = r_of(lane), n = lane & 15;
+        if (r_of(ilane) < 2) {
+            const int r = r_of(ilane), n = ilane & 15;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
 #pragma unroll
@@ -994,7 +1070,7 @@ q8kv_decode_kernel(const DecodeArgs a) {
         const size_t state0 = (((size_t)b * a.n_kv + kh) * a.n_parts + part) * G;
         const __amdgpu_buffer_rsrc_t racc = state_rsrc(a.st_acc + state0 * HD, (uint32_t)(G * HD * 4));
         const __amdgpu_buffer_rsrc_t rms = state_rsrc(a.st_ms + state0 * 2, (uint32_t)(G * 8));
-        for (int e4 = tid; e4 < G * Q4; e4 += kThreads) {
+        for (int e4 = itid; e4 < G * Q4; e4 += kThreads) {
             const int g = e4 / Q4, i4 = e4 % Q4;
             float Mx = -INFINITY;
 #pragma unroll
@@ -1019,7 +1095,7 @@ q8kv_decode_kernel(const DecodeArgs a) {
             // the workgroup storing the group's last state merges the group
             wait_stores();
             __syncthreads();
-            if (tid == 0) {
+            if (itid == 0) {
                 int* c = a.arrive + (size_t)b * a.n_kv + kh;
                 const int prev = __hip_atomic_fetch_add(c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 const bool last = prev == np_b - 1;
@@ -1027,7 +1103,7 @@ q8kv_decode_kernel(const DecodeArgs a) {
                 lflag = last;
             }
             __syncthreads();
-            if (lflag) merge_group<HD>(a, b, kh, np_b, out_rows, tid, lms, lred);
+            if (lflag) merge_group<HD>(a, b, kh, np_b, out_rows, itid, lms, lred);
         }
         // next item (the barrier also keeps LDS from being reused too early)
         if (STATIC || !a.ticket) break;
