@@ -19,7 +19,9 @@ one launch (the streaming ceiling the decode is compared with), the CPU
 oracle timed on a bounded sample of the same workload, and sampled parity
 against that oracle and its fp64 twin.  A last leg times the fused step
 that also stores each sequence's new token (q8kv_append_decode_attn) against
-the same work as two launches (q8kv_append, then q8kv_decode_attn).
+the same work as two launches (q8kv_append, then q8kv_decode_attn), and
+another the same step over the FP8 codec (q8kv_fp8_decode_attn), with a
+sampled parity check against its oracle.
 """
 import argparse
 import json
@@ -56,6 +58,7 @@ def parse():
                    help="target CPU time of the oracle baseline sample")
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline and parity sample")
     p.add_argument("--no-fused", action="store_true", help="skip the fused append + decode leg")
+    p.add_argument("--no-fp8", action="store_true", help="skip the FP8-codec leg")
     p.add_argument("--part-tokens", type=int, default=0, help="override the split plan (0: automatic)")
     p.add_argument("--copy-mb", type=float, default=0.0,
                    help="after timing, run one device-to-device copy of this many MiB (a known-size "
@@ -63,7 +66,7 @@ def parse():
     return p.parse_args()
 
 
-def build_gpu(w, dev, copies_bytes):
+def build_gpu(w, dev, copies_bytes, fp8=False):
     import torch
     import decode_attention_int8_amd as q8
     lens = workloads.seq_lens(w)
@@ -71,7 +74,15 @@ def build_gpu(w, dev, copies_bytes):
     cache = q8.PagedKVCache(nb, w.n_kv, w.kv_bs, w.hd, device=dev)
     for t in (cache.k_pages, cache.v_pages, cache.k_scale, cache.v_scale):
         t.zero_()
+    cache8 = None
+    if fp8:
+        cache8 = q8.Fp8KVCache(nb, w.n_kv, w.kv_bs, w.hd, device=dev)
+        for t in (cache8.k_pages, cache8.v_pages, cache8.k_scale, cache8.v_scale):
+            t.zero_()
     t0 = time.time()
+    # each sequence's newest rows, which the fused-append leg stores again
+    k_last = np.zeros((w.batch, w.n_kv, w.hd), np.float32)
+    v_last = np.zeros_like(k_last)
     with ThreadPoolExecutor(8) as ex:
         chunk = 8
         for c0 in range(0, w.batch, chunk):
@@ -79,9 +90,13 @@ def build_gpu(w, dev, copies_bytes):
             futs = {b: ex.submit(workloads.kv_rows, w, b, int(lens[b])) for b in bs}
             for b in bs:
                 k, v = futs[b].result()
+                if int(lens[b]) > 0:
+                    k_last[b], v_last[b] = k[-1], v[-1]
                 sm = workloads.slot_mapping(w, table, b, int(lens[b]))
-                cache.append(torch.from_numpy(k).to(dev), torch.from_numpy(v).to(dev),
-                             torch.from_numpy(sm).to(dev))
+                kd, vd, smd = torch.from_numpy(k).to(dev), torch.from_numpy(v).to(dev), torch.from_numpy(sm).to(dev)
+                cache.append(kd, vd, smd)
+                if cache8 is not None:
+                    cache8.append(kd, vd, smd)
     torch.cuda.synchronize()
     log(f"appended {int(lens.sum())} tokens x {w.n_kv} kv heads in {time.time() - t0:.1f}s")
     kv = workloads.kv_bytes(w, lens)
@@ -92,8 +107,16 @@ def build_gpu(w, dev, copies_bytes):
     caches = [cache] + [q8.PagedKVCache.wrap(cache.k_pages.clone(), cache.v_pages.clone(),
                                              cache.k_scale.clone(), cache.v_scale.clone())
                         for _ in range(R - 1)]
+    caches8 = []
+    if cache8 is not None:
+        R8 = 1 if copies_bytes <= 0 else max(1, math.ceil(copies_bytes / workloads.fp8_kv_bytes(w, lens)))
+        free, _ = torch.cuda.mem_get_info(dev)
+        R8 = max(1, min(R8, int(0.8 * free // max(pool_bytes, 1)) + 1, 256))
+        caches8 = [cache8] + [q8.Fp8KVCache.wrap(cache8.k_pages.clone(), cache8.v_pages.clone(),
+                                                 cache8.k_scale.clone(), cache8.v_scale.clone())
+                              for _ in range(R8 - 1)]
     q = torch.from_numpy(workloads.query(w)).to(dev)
-    return dict(lens=lens, table=table, nb=nb, caches=caches, q=q,
+    return dict(lens=lens, table=table, nb=nb, caches=caches, caches8=caches8, q=q, k_last=k_last, v_last=v_last,
                 table_d=torch.from_numpy(table).to(dev), lens_d=torch.from_numpy(lens).to(dev))
 
 
@@ -138,16 +161,16 @@ def time_append_decode(w, g, steps, warmup, part_tokens):
     """The fused step (q8kv_append_decode_attn: store each sequence's new
     token at position L-1, then attend over 0..L-1) against the same work as
     two launches (q8kv_append at those slots, then q8kv_decode_attn), both
-    rotated over the cold copies.  The new rows are seeded N(0,1) draws.
-    Returns a dict of per-step times in us."""
+    rotated over the cold copies.  The new rows are the rows each sequence's
+    newest token already holds, so the cache bytes do not change.  Returns a
+    dict of per-step times in us."""
     import torch
     import decode_attention_int8_amd as q8
     scale = workloads.softmax_scale(w.hd)
     R = len(g["caches"])
     dev = g["q"].device
-    rng = np.random.default_rng(w.key + 7000)
-    k_new = torch.from_numpy(rng.standard_normal((w.batch, w.n_kv, w.hd), dtype=np.float32)).to(dev)
-    v_new = torch.from_numpy(rng.standard_normal((w.batch, w.n_kv, w.hd), dtype=np.float32)).to(dev)
+    k_new = torch.from_numpy(g["k_last"]).to(dev)
+    v_new = torch.from_numpy(g["v_last"]).to(dev)
     lens, table = g["lens"], g["table"]
     slots = np.array([int(table[b, (L - 1) // w.kv_bs]) * w.kv_bs + (L - 1) % w.kv_bs if L > 0 else -1
                       for b, L in enumerate(lens.tolist())], np.int32)
@@ -181,6 +204,62 @@ def time_append_decode(w, g, steps, warmup, part_tokens):
 
     res = {"fused_us": timed(fused), "two_launch_us": timed(two), "append_us": timed(append)}
     return {k: round(v, 3) for k, v in res.items()}
+
+
+def time_fp8(w, g, steps, warmup, part_tokens):
+    """The same decode step over the FP8 codec (q8kv_fp8_decode_attn),
+    rotated over its own cold copies.  Returns (us per step, out)."""
+    import torch
+    import decode_attention_int8_amd as q8
+    scale = workloads.softmax_scale(w.hd)
+    R = len(g["caches8"])
+    out = torch.empty_like(g["q"])
+
+    def step(i):
+        q8.fp8_decode_attn(g["q"], g["caches8"][i % R], g["table_d"], g["lens_d"], scale, out=out,
+                           part_tokens=part_tokens)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / steps
+
+
+def fp8_parity(w, g, max_seqs=2, max_tokens=16384):
+    """Max-abs difference of the FP8 decode against the FP8 oracle (fp64
+    definition) on a bounded sample of the workload's sequences: the sampled
+    sequences' rows are re-quantised on the host by the oracle."""
+    import torch
+    import decode_attention_int8_amd as q8
+    from oracle import fp8kv
+    lens = g["lens"]
+    seqs, tot = [], 0
+    sample_lens = np.zeros_like(lens)
+    for b in np.argsort(lens, kind="stable"):
+        if len(seqs) >= max_seqs or (seqs and tot + lens[b] > max_tokens):
+            break
+        # a sequence longer than the whole budget is sampled as its prefix
+        sample_lens[b] = min(int(lens[b]), max_tokens)
+        seqs.append(int(b))
+        tot += int(sample_lens[b])
+    scale = workloads.softmax_scale(w.hd)
+    out = q8.fp8_decode_attn(g["q"], g["caches8"][0], g["table_d"], torch.from_numpy(sample_lens).to(g["q"].device),
+                             scale).cpu().numpy()
+    host = fp8kv.Fp8Cache(g["nb"], w.n_kv, w.kv_bs, w.hd)
+    for b in seqs:
+        n = int(sample_lens[b])
+        k, v = workloads.kv_rows(w, b, int(lens[b]))
+        host.append(k[:n], v[:n], workloads.slot_mapping(w, g["table"], b, n))
+    want = fp8kv.decode(workloads.query(w), host, g["table"], sample_lens, scale)
+    return {"max_abs_err_vs_oracle_f64": float(np.abs(out[seqs] - want[seqs]).max()),
+            "sample": f"{len(seqs)} sequences, {tot} tokens"}
 
 
 def time_stream_read(g, steps):
@@ -310,7 +389,7 @@ def main():
     dev = torch.device("cuda", 0)
     log(f"workload {w.name}: batch {w.batch}, heads {w.n_q}/{w.n_kv}, hd {w.hd}, kv_bs {w.kv_bs}, "
         f"seq_len {'U{1..%d}' % w.seq_len if w.ragged else w.seq_len}")
-    g = build_gpu(w, dev, args.cold_bytes)
+    g = build_gpu(w, dev, args.cold_bytes, fp8=not args.no_fp8)
     lens = g["lens"]
     kvb = workloads.kv_bytes(w, lens)
     algo = workloads.step_bytes(w, lens)
@@ -355,6 +434,26 @@ def main():
                                 "decode_frac_of_ceiling": round(achieved / read_gbs, 4)},
         "cpu_baseline": None,
     }
+    if not args.no_fp8:
+        fp8_us = time_fp8(w, g, args.steps, args.warmup, args.part_tokens)
+        algo8 = workloads.step_bytes(w, lens, codec="fp8")
+        rec["fp8"] = {"us_per_step": round(fp8_us, 3), "kv_bytes_per_step": workloads.fp8_kv_bytes(w, lens),
+                      "algorithmic_bytes": algo8,
+                      "achieved_gbs": round(algo8 / (fp8_us * 1e-6) / 1e9, 2),
+                      "frac": round(algo8 / (fp8_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                      "traffic": profiled_traffic(w, f"{w.name}:fp8"),
+                      "cold_cache_copies": len(g["caches8"])}
+        log(f"fp8 codec: {fp8_us:.2f} us/step, {rec['fp8']['achieved_gbs']:.0f} GB/s")
+    if not args.no_fused:
+        fa = time_append_decode(w, g, args.steps, args.warmup, args.part_tokens)
+        new_bytes = w.batch * w.n_kv * (2 * w.hd * 4 + 2 * (w.hd + 4))
+        fa["algorithmic_bytes"] = algo + new_bytes
+        fa["gbs"] = round((algo + new_bytes) / (fa["fused_us"] * 1e-6) / 1e9, 2)
+        fa["saved_us"] = round(fa["two_launch_us"] - fa["fused_us"], 3)
+        fa["traffic"] = profiled_traffic(w, f"{w.name}:append_decode")
+        log(f"append+decode: fused {fa['fused_us']} us, append then decode {fa['two_launch_us']} us "
+            f"(append alone {fa['append_us']} us)")
+        rec["append_decode"] = fa
     if args.copy_mb > 0:
         n = int(args.copy_mb * 2 ** 20)
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
@@ -376,17 +475,8 @@ def main():
         cpu, parity = cpu_baseline(w, g, gpu_out, args.cpu_seconds)
         rec["cpu_baseline"] = cpu
         rec["parity"] = parity
-    if not args.no_fused:
-        # last: it rewrites each sequence's newest row with the seeded new rows
-        fa = time_append_decode(w, g, args.steps, args.warmup, args.part_tokens)
-        new_bytes = w.batch * w.n_kv * (2 * w.hd * 4 + 2 * (w.hd + 4))
-        fa["algorithmic_bytes"] = algo + new_bytes
-        fa["gbs"] = round((algo + new_bytes) / (fa["fused_us"] * 1e-6) / 1e9, 2)
-        fa["saved_us"] = round(fa["two_launch_us"] - fa["fused_us"], 3)
-        fa["traffic"] = profiled_traffic(w, f"{w.name}:append_decode")
-        log(f"append+decode: fused {fa['fused_us']} us, append then decode {fa['two_launch_us']} us "
-            f"(append alone {fa['append_us']} us)")
-        rec["append_decode"] = fa
+        if "fp8" in rec:
+            rec["fp8"]["parity"] = fp8_parity(w, g)
     print(json.dumps(rec), flush=True)
 
 

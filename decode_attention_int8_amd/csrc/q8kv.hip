@@ -42,6 +42,7 @@
 #include <cstring>
 #include <algorithm>
 #include <map>
+#include <type_traits>
 #include <mutex>
 #include <string>
 #include <utility>
@@ -339,6 +340,10 @@ struct DecodeArgs {
     const void* knew;
     const void* vnew;
     int new_bf16;
+    // FP8 codec (kernels instantiated with kFp8): UE8M0 scale bytes
+    // [num_blocks][n_kv][kv_bs][hd/64] (ks / vs are then unused)
+    const uint8_t* ks8;
+    const uint8_t* vs8;
 };
 
 // Partition states cross workgroups (and XCDs) through buffer loads and
@@ -764,6 +769,227 @@ __device__ __forceinline__ void tile_compute(const Tile<HD>& T, const int8_t* lq
     }
 }
 
+// ----------------------------------------------------------------------------
+// FP8 KV codec (page "deepseek-attention-div64", beaiera.top, section on the
+// FP8 quantisation scaling): K and V rows are E4M3 codes, every 64 elements
+// of a row share one UE8M0 byte, the exponent e of the scale 2^e
+// (byte = e + 127).  Pages use the same sub-tile chunks as the int8 codec;
+// K keeps the int8 byte order, V is laid out for 16-column P.V blocks:
+//   V slot l = 16 r + n owns rows 4r .. 4r+3 of the columns 16 s + n
+//     (s = 0 .. HD/16 - 1); dword s of its 4 HD/16 bytes is those four rows
+//     of column 16 s + n (row order), dword s lying in chunk s / 4.
+// Scales: uint8 [num_blocks][n_kv][kv_bs][HD/64].
+//
+// Q.K runs on v_mfma_f32_16x16x32_f16: K codes convert exactly to f16, the
+// query is carried as f16 hi and lo rows (B columns 0-7 and 8-15, ~22
+// significant bits), one accumulator per 64-column block, and the block's
+// K scale 2^e multiplies the block's dot afterwards.  P.V runs on
+// v_mfma_f32_16x16x32_bf16: V codes convert exactly to bf16; the V scale
+// depends on the token and the 64-column block, so each P.V matrix (16
+// columns inside one block) takes the weights times that block's 2^e as bf16
+// hi and lo rows.
+
+constexpr int kFp8Block = 64;  // elements per scale byte
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+template <int HD>
+__device__ __forceinline__ size_t fp8_v_swizzle(int row, int col) {
+    const int slot = 16 * (row >> 2) + (col & 15);
+    const int qb = 4 * (col >> 4) + (row & 3);
+    return (size_t)(qb >> 4) * 1024 + 16 * slot + (qb & 15);
+}
+
+// 2^(byte - 127) as fp32 (bytes 1 .. 254 give normal numbers).
+__device__ __forceinline__ float ue8m0_value(uint32_t byte) { return __uint_as_float(byte << 23); }
+
+template <int NB>
+struct ScaleBytes {
+    uint32_t w[NB];  // 4 rows x NB blocks, byte j * NB + c
+    __device__ __forceinline__ uint32_t byte(int j, int c) const {
+        const int i = j * NB + c;
+        return (w[i >> 2] >> (8 * (i & 3))) & 0xff;
+    }
+};
+
+template <int NB>
+__device__ __forceinline__ void load_scale_bytes(ScaleBytes<NB>& s, const uint8_t* p) {
+    if constexpr (NB == 1) {
+        s.w[0] = stream_load<uint32_t>(p);
+    } else if constexpr (NB == 2) {
+        const u32x2 x = stream_load<u32x2>(p);
+        s.w[0] = x[0];
+        s.w[1] = x[1];
+    } else {
+        const u32x4 x = stream_load<u32x4>(p);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s.w[i] = x[i];
+    }
+}
+
+template <int HD>
+struct Fp8Tile {
+    static constexpr int NB = HD / kFp8Block;
+    i32x4 k[2][Geo<HD>::NPAIR];
+    u32x4 v[2][Geo<HD>::NPAIR];
+    ScaleBytes<NB> ke[2], ve[2];  // rows 4r .. 4r+3 of each sub-tile
+    int nval[2];
+};
+
+template <int HD>
+__device__ __forceinline__ void fp8_tile_load(Fp8Tile<HD>& T, const DecodeArgs& a, const int (&tblk)[2], int kh,
+                                              int ts, int t1, int lane, bool& bad) {
+    constexpr int NB = Fp8Tile<HD>::NB;
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+        T.nval[st] = min(max(t1 - (ts + kSub * st), 0), kSub);
+        const int tst = T.nval[st] > 0 ? ts + kSub * st : ts;
+        int blk = (st == 1 && T.nval[1] > 0) ? tblk[1] : tblk[0];
+        if ((unsigned)blk >= (unsigned)a.num_blocks) {
+            bad = true;
+            blk = 0;
+        }
+        const size_t base = ((size_t)blk * a.n_kv + kh) * a.kv_bs + (size_t)(tst % a.kv_bs);
+        load_scale_bytes<NB>(T.ke[st], a.ks8 + (base + 4 * (lane >> 4)) * NB);
+        load_scale_bytes<NB>(T.ve[st], a.vs8 + (base + 4 * (lane >> 4)) * NB);
+        load_k_subtile<HD>(T.k[st], a.kp, base, lane);
+        const int8_t* vsub = a.vp + base * HD;
+#pragma unroll
+        for (int c = 0; c < Geo<HD>::NPAIR; ++c) T.v[st][c] = stream_load<u32x4>(vsub + 1024 * c + 16 * lane);
+    }
+}
+
+// Query rows -> f16 hi and lo rows in LDS: lq16 [2][kHeadGroup][HD].
+template <int HD, int NT>
+__device__ __forceinline__ void split_q_regs(const QRows<HD, NT>& Q, _Float16* lq16, int tid) {
+#pragma unroll
+    for (int i = 0; i < QRows<HD, NT>::kPer; ++i) {
+        const int c = tid + i * NT;
+        if (QRows<HD, NT>::kChunks % NT != 0 && c >= QRows<HD, NT>::kChunks) break;
+        const int g = c / (HD / 4);
+        const int e = (c % (HD / 4)) * 4;
+        _Float16 hi[4], lo[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            hi[k] = (_Float16)Q.x[i][k];
+            lo[k] = (_Float16)(Q.x[i][k] - (float)hi[k]);
+        }
+        *reinterpret_cast<u32x2*>(lq16 + g * HD + e) = __builtin_bit_cast(u32x2, hi);
+        *reinterpret_cast<u32x2*>(lq16 + (kHeadGroup + g) * HD + e) = __builtin_bit_cast(u32x2, lo);
+    }
+}
+
+// Eight fp8 codes (two dwords) -> f16x8, exactly.
+__device__ __forceinline__ f16x8 fp8x8_to_f16(uint32_t x0, uint32_t x1) {
+    u32x4 r;
+    r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x0, 1.0f, false));
+    r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x0, 1.0f, true));
+    r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x1, 1.0f, false));
+    r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x1, 1.0f, true));
+    return __builtin_bit_cast(f16x8, r);
+}
+
+// Eight fp8 codes (two dwords) -> bf16x8, exactly.
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t x0, uint32_t x1) {
+    u32x4 r;
+    r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x0, 1.0f, false));
+    r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x0, 1.0f, true));
+    r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x1, 1.0f, false));
+    r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x1, 1.0f, true));
+    return __builtin_bit_cast(bf16x8, r);
+}
+
+// One tile of the recurrence over FP8 K/V (same softmax steps as
+// tile_compute; acc[s] holds output columns 16 s + n).
+template <int HD>
+__device__ __forceinline__ void fp8_tile_compute(const Fp8Tile<HD>& T, const _Float16* lq16, float score_scale,
+                                                 f32x4 (&acc)[Geo<HD>::BPL], float& M, float& S, int lane) {
+    using GG = Geo<HD>;
+    constexpr int NB = Fp8Tile<HD>::NB;
+    const int r = lane >> 4, n = lane & 15;
+    const _Float16* qrow = lq16 + ((n >> 3) * kHeadGroup + (n & 7)) * HD + 16 * r;
+    float sc[2][4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+        f32x4 cb[NB];
+#pragma unroll
+        for (int c = 0; c < NB; ++c) {
+            cb[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const f16x8 kop = fp8x8_to_f16((uint32_t)T.k[st][c][2 * h], (uint32_t)T.k[st][c][2 * h + 1]);
+                const f16x8 qop = *reinterpret_cast<const f16x8*>(qrow + 64 * c + 8 * h);
+                cb[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qop, cb[c], 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float part = 0.0f;
+#pragma unroll
+            for (int c = 0; c < NB; ++c) part += cb[c][j] * ue8m0_value(T.ke[st].byte(j, c));
+            const float full = (part + dpp_row_ror8(part)) * score_scale;  // hi + lo query rows
+            sc[st][j] = (4 * r + j) < T.nval[st] ? full : -INFINITY;
+            mx = fmaxf(mx, sc[st][j]);
+        }
+    }
+    mx = swap16_max(mx);
+    mx = swap32_max(mx);
+    const float m_new = fmaxf(M, mx);
+    const float alpha = __builtin_amdgcn_exp2f(M - m_new);
+    M = m_new;
+    const float m_shift = m_new - kWeightShift;
+
+    // Rows past the range (read with their sub-tile) may hold any byte, NaN
+    // codes and scales included: their weights are selected to zero after
+    // the scale multiply and their V codes are zeroed before conversion.
+    float W[8];
+    bool ok[8];
+    uint32_t vmask[2];
+    float wsum = 0.0f;
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+        const int vr = min(max(T.nval[st] - 4 * r, 0), 4);
+        vmask[st] = vr >= 4 ? 0xffffffffu : (1u << (8 * vr)) - 1u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float w = __builtin_amdgcn_exp2f(sc[st][j] - m_shift);
+            wsum += w;
+            ok[4 * st + j] = (4 * r + j) < T.nval[st];
+            W[4 * st + j] = w;
+        }
+    }
+    S = S * alpha + wsum;
+
+    if (__any(alpha != 1.0f)) {
+        float arow[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) arow[j] = lane_read(alpha, 4 * (r & 1) + j);
+#pragma unroll
+        for (int s = 0; s < GG::BPL; ++s) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[s][j] *= arow[j];
+        }
+    }
+
+    // P.V, one 64-column block (four 16-column matrices) at a time
+#pragma unroll
+    for (int c = 0; c < NB; ++c) {
+        bf16x8 aw;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const float x = ok[k] ? W[k] * ue8m0_value(T.ve[k >> 2].byte(k & 3, c)) : 0.0f;
+            const __bf16 hi = (__bf16)x;
+            aw[k] = n < 8 ? hi : (__bf16)(x - (float)hi);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int s = 4 * c + q;
+            const bf16x8 bv = fp8x8_to_bf16(T.v[0][s >> 2][s & 3] & vmask[0], T.v[1][s >> 2][s & 3] & vmask[1]);
+            acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw, bv, acc[s], 0, 0, 0);
+        }
+    }
+}
+
 // Grid modes.  kPersistent: fewer workgroups than items; items are numbered
 // through an exclusive prefix sum of n_kv * ceil(L / pt) per sequence built in
 // LDS from seq_lens, and each workgroup takes its next item from an atomic
@@ -774,14 +1000,19 @@ __device__ __forceinline__ void tile_compute(const Tile<HD>& T, const int8_t* lq
 // others' compute).  3 waves per SIMD fit hd 64 and 128 without spills; hd
 // 256 keeps a whole register file.
 enum GridMode { kPersistent = 0, kStatic = 1 };
+enum CodecKind { kQ8 = 0, kFp8 = 1 };
 
-template <int HD, int MODE, bool NEW>
+template <int HD, int MODE, bool NEW, int CODEC = kQ8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(HD == 256 ? 1 : 3))) void
 q8kv_decode_kernel(const DecodeArgs a) {
     using GG = Geo<HD>;
     constexpr bool STATIC = MODE == kStatic;
-    __shared__ __attribute__((aligned(16))) int8_t lq[kHeadGroup * HD];
-    __shared__ float lqsc[kHeadGroup * GG::NB];
+    constexpr bool FP8 = CODEC == kFp8;
+    static_assert(!(NEW && FP8), "the fused append is an int8-codec path");
+    using TileT = std::conditional_t<FP8, Fp8Tile<HD>, Tile<HD>>;
+    __shared__ __attribute__((aligned(16))) int8_t lq[FP8 ? 16 : kHeadGroup * HD];
+    __shared__ float lqsc[FP8 ? 1 : kHeadGroup * GG::NB];
+    __shared__ __attribute__((aligned(16))) _Float16 lq16[FP8 ? 2 * kHeadGroup * HD : 8];  // FP8: query hi, lo rows
     __shared__ float lM[kWaves][kHeadGroup];
     __shared__ float lS[kWaves][kHeadGroup];
     __shared__ float lacc[kWaves][kHeadGroup][HD];
@@ -995,18 +1226,20 @@ q8kv_decode_kernel(const DecodeArgs a) {
         }
 
         // Start streaming the wave's first tile before the query prologue.
-        Tile<HD> A;
+        TileT A;
         {
             const bool own = ts < t1;
             const int blk0[2] = {own ? blk_first[0] : blk_t0[0], own ? blk_first[1] : blk_t0[1]};
-            tile_load<HD>(A, a, blk0, kh, own ? ts : t0, t1, ilane, bad);
+            if constexpr (FP8) fp8_tile_load<HD>(A, a, blk0, kh, own ? ts : t0, t1, ilane, bad);
+            else tile_load<HD>(A, a, blk0, kh, own ? ts : t0, t1, ilane, bad);
         }
         if constexpr (NEW && STATIC) {
             // static grids: the new rows' loads go out behind the first tile
             if (tail_ts != INT_MIN) load_new_rows<HD>(nk, nv, a.knew, a.vnew, a.new_bf16, b, a.n_kv, kh, ilane);
         }
 
-        quantize_q_regs<HD, kThreads>(qrows, lq, lqsc, itid);
+        if constexpr (FP8) split_q_regs<HD, kThreads>(qrows, lq16, itid);
+        else quantize_q_regs<HD, kThreads>(qrows, lq, lqsc, itid);
         __syncthreads();
         // static grids: the tail wave quantises the new rows (which arrive
         // with its first tile) while its second tile is in flight, or here
@@ -1026,12 +1259,14 @@ q8kv_decode_kernel(const DecodeArgs a) {
             if constexpr (NEW) {
                 if (ts == tail_ts) tile_patch<HD>(A, lnew, lnew + HD, lnew_sc[0], lnew_sc[1], L - 1 - ts, ilane);
             }
-            tile_compute<HD>(A, lq, lqsc, a.scale_log2, acc, M, S, ilane);
+            if constexpr (FP8) fp8_tile_compute<HD>(A, lq16, a.scale_log2, acc, M, S, ilane);
+            else tile_compute<HD>(A, lq, lqsc, a.scale_log2, acc, M, S, ilane);
             ts += kStride;
             if (ts < t1) {
                 int blk[2];
                 tile_blocks(trow, ts, a.kv_bs, a.max_blocks, blk);
-                tile_load<HD>(A, a, blk, kh, ts, t1, ilane, bad);
+                if constexpr (FP8) fp8_tile_load<HD>(A, a, blk, kh, ts, t1, ilane, bad);
+                else tile_load<HD>(A, a, blk, kh, ts, t1, ilane, bad);
                 if constexpr (NEW && STATIC) {
                     if (tail_ts != INT_MIN && ts == ts_second)
                         prepare_new_token<HD>(nk, nv, tail_blk, lnew, lnew_sc, &lnew_blk, ilane);
@@ -1060,7 +1295,7 @@ q8kv_decode_kernel(const DecodeArgs a) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
 #pragma unroll
-                for (int s = 0; s < GG::BPL; ++s) lacc[wid][4 * r + j][GG::BPL * n + s] = acc[s][j];
+                for (int s = 0; s < GG::BPL; ++s) lacc[wid][4 * r + j][FP8 ? 16 * s + n : GG::BPL * n + s] = acc[s][j];
             }
         }
         const bool any_bad = __syncthreads_or(bad);
@@ -1241,6 +1476,81 @@ __global__ __launch_bounds__(256) void q8kv_append_kernel(const AppendArgs a) {
     row_store<HD, true>(a.vp, a.vs, dst_row, rr, pv, dv, lane);
 }
 
+// FP8 append: one wave per (token, kv head) row, EPL = HD / 64 elements per
+// lane, so one 64-element scale block spans 64 / EPL lanes.  Per block: the
+// absmax, e = ceil(log2(absmax / 448)) read off the bits of the fp32
+// quotient (clamped to [-126, 127]; 0 for an all-zero block), codes
+// E4M3(clamp(x * 2^-e, -448, 448)) rounded to nearest even by the hardware
+// conversion, scale byte e + 127.
+__device__ __forceinline__ int fp8_block_exponent(float am) {
+    if (am == 0.0f) return 0;
+    const uint32_t b = __float_as_uint(am / 448.0f);
+    const int ef = (int)((b >> 23) & 0xff);
+    if (ef == 0) return -126;  // a subnormal quotient lies below 2^-126
+    const int e = ef - 127 + ((b & 0x7fffffu) != 0 ? 1 : 0);
+    return min(max(e, -126), 127);
+}
+
+template <int HD, bool V>
+__device__ __forceinline__ void fp8_row_store(uint8_t* pages, uint8_t* scales, size_t dst_row, int row_in_page,
+                                              const NewRow<HD>& x, int lane) {
+    constexpr int EPL = NewRow<HD>::EPL, LPB = kFp8Block / EPL, NB = HD / kFp8Block;
+    float am = 0.0f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) am = fmaxf(am, fabsf(x.x[e]));
+#pragma unroll
+    for (int off = 1; off < LPB; off <<= 1) am = fmaxf(am, __shfl_xor(am, off));
+    const int ex = fp8_block_exponent(am);
+    const float inv = ldexpf(1.0f, -ex);
+    float y[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) y[e] = fminf(fmaxf(x.x[e] * inv, -448.0f), 448.0f);
+    uint32_t packed = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0u, false);
+    if constexpr (EPL == 4) packed = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], packed, true);
+    const int row = row_in_page % kSub, col = lane * EPL;
+    uint8_t* sub = pages + (dst_row - row) * HD;
+    if constexpr (V) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) sub[fp8_v_swizzle<HD>(row, col + e)] = (uint8_t)(packed >> (8 * e));
+    } else {
+        uint8_t* dst = sub + k_swizzle(row, col);
+        if constexpr (EPL == 1) *dst = (uint8_t)packed;
+        else if constexpr (EPL == 2) *reinterpret_cast<uint16_t*>(dst) = (uint16_t)packed;
+        else *reinterpret_cast<uint32_t*>(dst) = packed;
+    }
+    if (lane % LPB == 0) scales[dst_row * NB + lane / LPB] = (uint8_t)(ex + 127);
+}
+
+struct Fp8AppendArgs {
+    uint8_t* kp;
+    uint8_t* vp;
+    uint8_t* ks;
+    uint8_t* vs;
+    const void* ksrc;
+    const void* vsrc;
+    const int32_t* slots;
+    int n_tokens, n_kv, kv_bs, src_bf16;
+    long long n_slots;
+};
+
+template <int HD>
+__global__ __launch_bounds__(256) void q8kv_fp8_append_kernel(const Fp8AppendArgs a) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const long long row_id = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row_id >= (long long)a.n_tokens * a.n_kv) return;
+    const int t = (int)(row_id / a.n_kv), kh = (int)(row_id % a.n_kv);
+    const int slot = a.slots[t];
+    if (slot < 0 || (long long)slot >= a.n_slots) return;
+    const int blk = slot / a.kv_bs, rr = slot % a.kv_bs;
+    const size_t dst_row = ((size_t)blk * a.n_kv + kh) * a.kv_bs + rr;
+    const size_t src_row = (size_t)t * a.n_kv + kh;
+    NewRow<HD> k, v;
+    row_load<HD>(k, a.ksrc, src_row, a.src_bf16, lane);
+    row_load<HD>(v, a.vsrc, src_row, a.src_bf16, lane);
+    fp8_row_store<HD, false>(a.kp, a.ks, dst_row, rr, k, lane);
+    fp8_row_store<HD, true>(a.vp, a.vs, dst_row, rr, v, lane);
+}
+
 // ----------------------------------------------------------------------------
 // test exports built from the decode kernel's device functions
 
@@ -1411,20 +1721,29 @@ void plan(int batch, int n_kv, int max_tokens, int* part_tokens, int* n_parts) {
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
-template <int HD, bool NEW>
+// Decode kernel variants: the int8 codec, the int8 codec with the fused
+// append of the new token, the FP8 codec.
+enum Variant { kVarQ8 = 0, kVarQ8New = 1, kVarFp8 = 2 };
+
+template <int HD, int VAR, int MODE>
+constexpr auto decode_kernel_ptr() {
+    return q8kv_decode_kernel<HD, MODE, VAR == kVarQ8New, VAR == kVarFp8 ? kFp8 : kQ8>;
+}
+
+template <int HD, int VAR>
 int launch_info_hd(int dev, LaunchInfo& li) {
     int per_cu = 0, lds_cu = 0;
     hipError_t e = hipDeviceGetAttribute(&li.cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev);
     if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &per_cu, reinterpret_cast<const void*>(q8kv_decode_kernel<HD, kPersistent, NEW>), kThreads, 0);
+        &per_cu, reinterpret_cast<const void*>(decode_kernel_ptr<HD, VAR, kPersistent>()), kThreads, 0);
     if (e != hipSuccess) return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
     li.resident = std::max(1, li.cus * std::max(1, per_cu));
     // A static grid of at most two workgroups per CU is spread evenly when a
     // third cannot fit: ask for just over a third of the CU's LDS.
     hipFuncAttributes fa;
-    e = hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(q8kv_decode_kernel<HD, kStatic, NEW>));
+    e = hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(decode_kernel_ptr<HD, VAR, kStatic>()));
     if (e != hipSuccess) return hip_fail(e, "hipFuncGetAttributes");
     const int need = (lds_cu / 3 + 256) / 256 * 256;
     const int dyn = need - (int)fa.sharedSizeBytes;
@@ -1432,52 +1751,56 @@ int launch_info_hd(int dev, LaunchInfo& li) {
     return Q8KV_OK;
 }
 
-template <bool NEW>
-int launch_info_new(int dev, int hd, LaunchInfo& li) {
-    return hd == 64 ? launch_info_hd<64, NEW>(dev, li) : hd == 128 ? launch_info_hd<128, NEW>(dev, li)
-                                                                   : launch_info_hd<256, NEW>(dev, li);
+template <int VAR>
+int launch_info_var(int dev, int hd, LaunchInfo& li) {
+    return hd == 64 ? launch_info_hd<64, VAR>(dev, li) : hd == 128 ? launch_info_hd<128, VAR>(dev, li)
+                                                                   : launch_info_hd<256, VAR>(dev, li);
 }
 
-int launch_info(int dev, int hd, bool fused, LaunchInfo* out) {
+int launch_info(int dev, int hd, int var, LaunchInfo* out) {
     std::lock_guard<std::mutex> lock(g_mu);
-    const std::pair<int, int> key{dev, hd * 2 + (fused ? 1 : 0)};
+    const std::pair<int, int> key{dev, hd * 4 + var};
     auto it = g_launch.find(key);
     if (it != g_launch.end()) {
         *out = it->second;
         return Q8KV_OK;
     }
     LaunchInfo li;
-    const int rc = fused ? launch_info_new<true>(dev, hd, li) : launch_info_new<false>(dev, hd, li);
+    const int rc = var == kVarQ8New ? launch_info_var<kVarQ8New>(dev, hd, li)
+                   : var == kVarFp8 ? launch_info_var<kVarFp8>(dev, hd, li)
+                                    : launch_info_var<kVarQ8>(dev, hd, li);
     if (rc) return rc;
     g_launch[key] = li;
     *out = li;
     return Q8KV_OK;
 }
 
-template <int HD, bool NEW>
+template <int HD, int VAR>
 void launch_decode_hd(int mode, unsigned grid, size_t lds, hipStream_t st, const DecodeArgs& da) {
-    if (mode == kPersistent) hipLaunchKernelGGL((q8kv_decode_kernel<HD, kPersistent, NEW>), dim3(grid), dim3(kThreads), 0, st, da);
-    else hipLaunchKernelGGL((q8kv_decode_kernel<HD, kStatic, NEW>), dim3(grid), dim3(kThreads), lds, st, da);
+    if (mode == kPersistent) hipLaunchKernelGGL((decode_kernel_ptr<HD, VAR, kPersistent>()), dim3(grid), dim3(kThreads), 0, st, da);
+    else hipLaunchKernelGGL((decode_kernel_ptr<HD, VAR, kStatic>()), dim3(grid), dim3(kThreads), lds, st, da);
 }
 
-template <bool NEW>
-void launch_decode_new(int hd, int mode, unsigned grid, size_t lds, hipStream_t st, const DecodeArgs& da) {
-    if (hd == 64) launch_decode_hd<64, NEW>(mode, grid, lds, st, da);
-    else if (hd == 128) launch_decode_hd<128, NEW>(mode, grid, lds, st, da);
-    else launch_decode_hd<256, NEW>(mode, grid, lds, st, da);
+template <int VAR>
+void launch_decode_var(int hd, int mode, unsigned grid, size_t lds, hipStream_t st, const DecodeArgs& da) {
+    if (hd == 64) launch_decode_hd<64, VAR>(mode, grid, lds, st, da);
+    else if (hd == 128) launch_decode_hd<128, VAR>(mode, grid, lds, st, da);
+    else launch_decode_hd<256, VAR>(mode, grid, lds, st, da);
 }
 
-void launch_decode(int hd, int mode, unsigned grid, size_t lds, hipStream_t st, const DecodeArgs& da) {
-    if (da.knew) launch_decode_new<true>(hd, mode, grid, lds, st, da);
-    else launch_decode_new<false>(hd, mode, grid, lds, st, da);
+void launch_decode(int hd, int var, int mode, unsigned grid, size_t lds, hipStream_t st, const DecodeArgs& da) {
+    if (var == kVarQ8New) launch_decode_var<kVarQ8New>(hd, mode, grid, lds, st, da);
+    else if (var == kVarFp8) launch_decode_var<kVarFp8>(hd, mode, grid, lds, st, da);
+    else launch_decode_var<kVarQ8>(hd, mode, grid, lds, st, da);
 }
 
 int decode_impl(float* out, const float* q, const int8_t* kp, const int8_t* vp, const float* ks,
                 const float* vs, const int32_t* table, const int32_t* lens, int max_blocks,
                 int num_blocks, int batch, int n_q, int n_kv, int hd, int kv_bs, float scale,
                 int part_tokens, void* stream, const void* knew = nullptr, const void* vnew = nullptr,
-                int new_dtype = 0) {
-    if (!out || !q || !kp || !vp || !ks || !vs || !table || !lens)
+                int new_dtype = 0, const uint8_t* ks8 = nullptr, const uint8_t* vs8 = nullptr) {
+    const bool fp8 = ks8 != nullptr || vs8 != nullptr;
+    if (!out || !q || !kp || !vp || !table || !lens || (fp8 ? (!ks8 || !vs8) : (!ks || !vs)))
         return fail(Q8KV_ENULL, "a tensor pointer is NULL");
     if ((knew == nullptr) != (vnew == nullptr)) return fail(Q8KV_ENULL, "k_new and v_new must both be given");
     if (knew && new_dtype != 0 && new_dtype != 1) return fail(Q8KV_EINVAL, "src_dtype must be 0 (fp32) or 1 (bf16)");
@@ -1510,12 +1833,13 @@ int decode_impl(float* out, const float* q, const int8_t* kp, const int8_t* vp, 
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
     LaunchInfo li;
-    rc = launch_info(dev, hd, knew != nullptr, &li);
+    const int var = fp8 ? kVarFp8 : knew ? kVarQ8New : kVarQ8;
+    rc = launch_info(dev, hd, var, &li);
     if (rc) return rc;
     const unsigned grid = (unsigned)std::min<long long>(items, li.resident);
     DecodeArgs da{out, q, kp, vp, ks, vs, table, lens, nullptr, nullptr, nullptr, nullptr,
                   batch, max_blocks, num_blocks, n_q, n_kv, kv_bs, G, pt, np, scale * kLog2e,
-                  knew, vnew, new_dtype};
+                  knew, vnew, new_dtype, ks8, vs8};
     if (items > (long long)grid) {
         std::lock_guard<std::mutex> lock(g_mu);
         Workspace& w = g_ws[{dev, stream}];
@@ -1591,7 +1915,7 @@ int decode_impl(float* out, const float* q, const int8_t* kp, const int8_t* vp, 
     // that is enough)
     const int mode = items > (long long)grid ? kPersistent : kStatic;
     const size_t lds = mode == kStatic && grid <= 2u * (unsigned)li.cus ? (size_t)li.static_lds : 0;
-    launch_decode(hd, mode, grid, lds, st, da);
+    launch_decode(hd, var, mode, grid, lds, st, da);
     e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
     if (np > 1 && !fuse) {
@@ -1684,6 +2008,45 @@ int q8kv_append(int8_t* k_pages, int8_t* v_pages, float* k_scale, float* v_scale
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "append kernel launch");
     return Q8KV_OK;
+}
+
+int q8kv_fp8_append(uint8_t* k_pages, uint8_t* v_pages, uint8_t* k_scale, uint8_t* v_scale, const void* k_src,
+                    const void* v_src, int src_dtype, const int32_t* slot_mapping, int n_tokens,
+                    int num_blocks, int n_kv_heads, int hd, int kv_bs, void* stream) {
+    g_err.clear();
+    if (!k_pages || !v_pages || !k_scale || !v_scale || !k_src || !v_src || !slot_mapping)
+        return fail(Q8KV_ENULL, "a tensor pointer is NULL");
+    if (n_tokens < 0) return fail(Q8KV_EINVAL, "n_tokens must be >= 0 (got %d)", n_tokens);
+    int rc = check_cache_shape(num_blocks, n_kv_heads, hd, kv_bs);
+    if (rc) return rc;
+    if (src_dtype != 0 && src_dtype != 1) return fail(Q8KV_EINVAL, "src_dtype must be 0 (fp32) or 1 (bf16)");
+    if (n_tokens == 0) return Q8KV_OK;
+    const long long rows = (long long)n_tokens * n_kv_heads;
+    const long long grid = (rows + 3) / 4;
+    if (grid > INT_MAX) return fail(Q8KV_EINVAL, "too many rows (%lld)", rows);
+    Fp8AppendArgs aa{k_pages, v_pages, k_scale, v_scale, k_src, v_src, slot_mapping, n_tokens,
+                     n_kv_heads, kv_bs, src_dtype, (long long)num_blocks * kv_bs};
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    switch (hd) {
+        case 64: hipLaunchKernelGGL(q8kv_fp8_append_kernel<64>, dim3((unsigned)grid), dim3(256), 0, st, aa); break;
+        case 128: hipLaunchKernelGGL(q8kv_fp8_append_kernel<128>, dim3((unsigned)grid), dim3(256), 0, st, aa); break;
+        default: hipLaunchKernelGGL(q8kv_fp8_append_kernel<256>, dim3((unsigned)grid), dim3(256), 0, st, aa); break;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "fp8 append kernel launch");
+    return Q8KV_OK;
+}
+
+int q8kv_fp8_decode_attn(float* out, const float* q, const uint8_t* k_pages, const uint8_t* v_pages,
+                         const uint8_t* k_scale, const uint8_t* v_scale, const int32_t* block_table,
+                         const int32_t* seq_lens, int max_blocks_per_seq, int num_blocks, int batch,
+                         int n_q_heads, int n_kv_heads, int hd, int kv_bs, float scale, int part_tokens,
+                         void* stream) {
+    g_err.clear();
+    if (!k_scale || !v_scale) return fail(Q8KV_ENULL, "a tensor pointer is NULL");
+    return decode_impl(out, q, reinterpret_cast<const int8_t*>(k_pages), reinterpret_cast<const int8_t*>(v_pages),
+                       nullptr, nullptr, block_table, seq_lens, max_blocks_per_seq, num_blocks, batch, n_q_heads,
+                       n_kv_heads, hd, kv_bs, scale, part_tokens, stream, nullptr, nullptr, 0, k_scale, v_scale);
 }
 
 const char* q8kv_last_error(void) { return g_err.c_str(); }

@@ -169,6 +169,52 @@ int q8kv_append(int8_t* k_pages, int8_t* v_pages, float* k_scale, float* v_scale
                 const int32_t* slot_mapping, int n_tokens, int num_blocks,
                 int n_kv_heads, int hd, int kv_bs, void* stream);
 
+/*
+ * FP8 KV codec (page "deepseek-attention-div64" (beaiera.top), section on the
+ * FP8 quantisation scaling): every K and V row is stored as E4M3 codes (sign,
+ * 4 exponent bits with bias 7, 3 mantissa bits; largest finite value 448; no
+ * infinity), and every 64 consecutive elements of a row share one UE8M0
+ * scale byte s, the exponent of the power-of-two scale 2^(s - 127).  A
+ * block's absolute maximum a fixes e = ceil(log2(a / 448)) -- the exact
+ * ceiling for the fp32 quotient a / 448, clamped to [-126, 127], and 0 for
+ * an all-zero block -- and the codes are E4M3(clamp(x * 2^-e, -448, 448)),
+ * rounded to nearest, ties to even; s = e + 127.  An element's value is
+ * code value * 2^e.
+ *
+ * Layouts (caller-owned device memory):
+ *   k_pages,
+ *   v_pages   uint8 [num_blocks][n_kv_heads][kv_bs / 16][16 * hd]: E4M3
+ *             codes in 16-row sub-tiles of hd / 64 chunks of 1024 bytes
+ *             (lane slot l = 16 r + n owns bytes [16 l, 16 l + 16) of each);
+ *             K in the int8 codec's K order (chunk c, slot l: row n,
+ *             columns 64 c + 16 r .. + 16); V: slot l holds rows 4r .. 4r+3
+ *             of the columns 16 s + n (s = 0 .. hd/16 - 1) as hd / 16
+ *             dwords, dword s = those four rows of column 16 s + n in row
+ *             order, dword s lying in chunk s / 4 at bytes 4 (s % 4) ..;
+ *   k_scale,
+ *   v_scale   uint8 [num_blocks][n_kv_heads][kv_bs][hd / 64] UE8M0 bytes.
+ * Other arguments, errors and behaviour as for q8kv_append and
+ * q8kv_decode_attn_split.
+ */
+int q8kv_fp8_append(uint8_t* k_pages, uint8_t* v_pages, uint8_t* k_scale, uint8_t* v_scale,
+                    const void* k_src, const void* v_src, int src_dtype,
+                    const int32_t* slot_mapping, int n_tokens, int num_blocks,
+                    int n_kv_heads, int hd, int kv_bs, void* stream);
+
+/*
+ * Decode attention over an FP8 cache: out[b][h] = softmax(scale * q[b][h] .
+ * K) V over tokens 0 .. seq_lens[b] - 1, with K and V the dequantised
+ * values above and q used as given (carried as two f16 parts, about 22
+ * significant bits).  One pass with the same online-softmax recurrence,
+ * partitions and merges as q8kv_decode_attn_split.
+ */
+int q8kv_fp8_decode_attn(float* out, const float* q, const uint8_t* k_pages,
+                         const uint8_t* v_pages, const uint8_t* k_scale,
+                         const uint8_t* v_scale, const int32_t* block_table,
+                         const int32_t* seq_lens, int max_blocks_per_seq, int num_blocks,
+                         int batch, int n_q_heads, int n_kv_heads, int hd, int kv_bs,
+                         float scale, int part_tokens, void* stream);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* q8kv_last_error(void);
 

@@ -67,6 +67,27 @@ def chunk_offsets(hd, which):
     return (qb // 16) * 1024 + 16 * slot + qb % 16
 
 
+def fp8_v_offsets(hd):
+    """Byte offset, inside a 16-row sub-tile of an FP8 V page, of element
+    (row, column), as include/q8kv.h defines it: slot 16r+n holds rows
+    4r..4r+3 of columns 16s+n; dword s (those four rows in row order) lies in
+    chunk s/4 at bytes 4(s%4)..."""
+    row = np.arange(16)[:, None]
+    col = np.arange(hd)[None, :]
+    slot = 16 * (row // 4) + col % 16
+    qb = 4 * (col // 16) + row % 4
+    return (qb // 16) * 1024 + 16 * slot + qb % 16
+
+
+def natural_fp8_pages(pages, which):
+    """FP8 device pages [nb][n_kv][kv_bs][hd] in chunk order -> row-major rows
+    (K uses the int8 K order)."""
+    nb, n_kv, kv_bs, hd = pages.shape
+    sub = pages.reshape(nb, n_kv, kv_bs // 16, 16 * hd)
+    off = chunk_offsets(hd, "k") if which == "k" else fp8_v_offsets(hd)
+    return sub[..., off.reshape(-1)].reshape(nb, n_kv, kv_bs, hd)
+
+
 def natural_pages(pages, which):
     """Device pages [nb][n_kv][kv_bs][hd] in chunk order -> row-major rows."""
     nb, n_kv, kv_bs, hd = pages.shape

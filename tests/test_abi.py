@@ -14,7 +14,7 @@ NUL = ctypes.c_void_p(0)
 
 def test_exports_every_declared_symbol():
     names = q8.header_symbols()
-    assert len(names) == 10
+    assert len(names) == 12
     for n in names:
         assert hasattr(L, n), n
 
@@ -27,6 +27,51 @@ def decode(**kw):
     return L.q8kv_decode_attn_split(a["out"], a["q"], a["kp"], a["vp"], a["ks"], a["vs"], a["bt"],
                                     a["sl"], a["max_blocks"], a["num_blocks"], a["batch"], a["n_q"],
                                     a["n_kv"], a["hd"], a["kv_bs"], a["scale"], a["part"], NUL)
+
+
+def fp8_decode(**kw):
+    a = dict(out=FAKE, q=FAKE, kp=FAKE, vp=FAKE, ks=FAKE, vs=FAKE, bt=FAKE, sl=FAKE,
+             max_blocks=8, num_blocks=16, batch=2, n_q=8, n_kv=2, hd=128, kv_bs=16,
+             scale=0.088, part=0)
+    a.update(kw)
+    return L.q8kv_fp8_decode_attn(a["out"], a["q"], a["kp"], a["vp"], a["ks"], a["vs"], a["bt"],
+                                  a["sl"], a["max_blocks"], a["num_blocks"], a["batch"], a["n_q"],
+                                  a["n_kv"], a["hd"], a["kv_bs"], a["scale"], a["part"], NUL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ks=NUL), q8.Q8KV_ENULL),
+    (dict(vs=NUL), q8.Q8KV_ENULL),
+    (dict(kp=NUL), q8.Q8KV_ENULL),
+    (dict(sl=NUL), q8.Q8KV_ENULL),
+    (dict(hd=96), q8.Q8KV_EINVAL),
+    (dict(kv_bs=8), q8.Q8KV_EINVAL),
+    (dict(n_q=18, n_kv=1), q8.Q8KV_EINVAL),
+    (dict(scale=float("nan")), q8.Q8KV_EINVAL),
+    (dict(part=48), q8.Q8KV_EINVAL),
+])
+def test_fp8_decode_rejects_before_any_hip_call(kw, code):
+    assert fp8_decode(**kw) == code
+    assert q8.last_error() != ""
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kp=NUL), q8.Q8KV_ENULL),
+    (dict(ks=NUL), q8.Q8KV_ENULL),
+    (dict(sm=NUL), q8.Q8KV_ENULL),
+    (dict(n=-1), q8.Q8KV_EINVAL),
+    (dict(hd=96), q8.Q8KV_EINVAL),
+    (dict(dt=3), q8.Q8KV_EINVAL),
+    (dict(num_blocks=0), q8.Q8KV_EINVAL),
+])
+def test_fp8_append_rejects_before_any_hip_call(kw, code):
+    a = dict(kp=FAKE, vp=FAKE, ks=FAKE, vs=FAKE, kx=FAKE, vx=FAKE, dt=0, sm=FAKE, n=4, num_blocks=16,
+             n_kv=2, hd=128, kv_bs=16)
+    a.update(kw)
+    rc = L.q8kv_fp8_append(a["kp"], a["vp"], a["ks"], a["vs"], a["kx"], a["vx"], a["dt"], a["sm"], a["n"],
+                           a["num_blocks"], a["n_kv"], a["hd"], a["kv_bs"], NUL)
+    assert rc == code
+    assert q8.last_error() != ""
 
 
 def append_decode(**kw):

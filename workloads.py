@@ -150,8 +150,16 @@ def kv_bytes(w, lens):
     return int(np.sum(lens, dtype=np.int64)) * w.n_kv * (2 * w.hd + 8)
 
 
-def step_bytes(w, lens):
+def fp8_kv_bytes(w, lens):
+    """Algorithmic KV bytes of one decode step over the FP8 codec: per (token,
+    kv head) one E4M3 K row, one E4M3 V row and one scale byte per 64
+    elements of each."""
+    return int(np.sum(lens, dtype=np.int64)) * w.n_kv * (2 * w.hd + 2 * (w.hd // 64))
+
+
+def step_bytes(w, lens, codec="q8"):
     """All algorithmic bytes of one step: KV + scales, q and out (fp32), the
     used block-table entries and the seq_lens array."""
     used_blocks = sum(-(-int(L) // w.kv_bs) for L in lens)
-    return (kv_bytes(w, lens) + 2 * w.batch * w.n_q * w.hd * 4 + 4 * used_blocks + 4 * w.batch)
+    kv = kv_bytes(w, lens) if codec == "q8" else fp8_kv_bytes(w, lens)
+    return (kv + 2 * w.batch * w.n_q * w.hd * 4 + 4 * used_blocks + 4 * w.batch)
