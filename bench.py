@@ -21,7 +21,8 @@ against that oracle and its fp64 twin.  A last leg times the fused step
 that also stores each sequence's new token (q8kv_append_decode_attn) against
 the same work as two launches (q8kv_append, then q8kv_decode_attn), and
 another the same step over the FP8 codec (q8kv_fp8_decode_attn), with a
-sampled parity check against its oracle.
+sampled parity check against its oracle, and a QUEST leg (block metadata,
+top-k block selection, decode over the kept blocks).
 """
 import argparse
 import json
@@ -59,6 +60,7 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline and parity sample")
     p.add_argument("--no-fused", action="store_true", help="skip the fused append + decode leg")
     p.add_argument("--no-fp8", action="store_true", help="skip the FP8-codec leg")
+    p.add_argument("--no-quest", action="store_true", help="skip the QUEST metadata / selection leg")
     p.add_argument("--part-tokens", type=int, default=0, help="override the split plan (0: automatic)")
     p.add_argument("--copy-mb", type=float, default=0.0,
                    help="after timing, run one device-to-device copy of this many MiB (a known-size "
@@ -262,6 +264,54 @@ def fp8_parity(w, g, max_seqs=2, max_tokens=16384):
             "sample": f"{len(seqs)} sequences, {tot} tokens"}
 
 
+def time_quest(w, g, steps, warmup, top_k):
+    """QUEST legs on the int8 cache: the metadata pass over every referenced
+    block (a prefill-time op), and one decode step that selects top_k blocks
+    per kv head (bounds + top-k kernels) and attends over them
+    (q8kv_decode_attn_heads), against the dense step.  Timed with events
+    around back-to-back calls on caches[0] (the metadata and the selection
+    are small beside the cache)."""
+    import torch
+    import decode_attention_int8_amd as q8
+    scale = workloads.softmax_scale(w.hd)
+    cache = g["caches"][0]
+    q, bt, sl = g["q"], g["table_d"], g["lens_d"]
+    kmax, kmin = q8.quest_metadata(cache, bt, sl)
+    sel, sel_lens = q8.quest_select(q, cache, kmax, kmin, bt, sl, top_k)
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, n):
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(n):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n
+
+    R = len(g["caches"])
+    meta_us = timed(lambda i: q8.quest_metadata(g["caches"][i % R], bt, sl, kmax, kmin), max(steps // 4, 5))
+    select_us = timed(lambda i: q8.quest_select(q, cache, kmax, kmin, bt, sl, top_k, sel, sel_lens), steps)
+    sparse_us = timed(lambda i: q8.decode_attn_heads(q, g["caches"][i % R], sel, sel_lens, scale, out=out), steps)
+    step_us = timed(lambda i: (q8.quest_select(q, g["caches"][i % R], kmax, kmin, bt, sl, top_k, sel, sel_lens),
+                               q8.decode_attn_heads(q, g["caches"][i % R], sel, sel_lens, scale, out=out)), steps)
+    lens = g["lens"]
+    nblk = [-(-int(L) // w.kv_bs) for L in lens]
+    meta_bytes = sum(nblk) * w.n_kv * (w.kv_bs * (w.hd + 4) + 2 * w.hd * 4)
+    kept_tokens = int(sel_lens.sum().item()) * w.n_kv
+    sparse_bytes = kept_tokens * (2 * w.hd + 8) + 2 * w.batch * w.n_q * w.hd * 4
+    return {"top_k": top_k, "kept_tokens_per_kv_head": int(sel_lens.sum().item()),
+            "metadata_us": round(meta_us, 3), "metadata_bytes": meta_bytes,
+            "metadata_gbs": round(meta_bytes / (meta_us * 1e-6) / 1e9, 1),
+            "select_us": round(select_us, 3), "sparse_decode_us": round(sparse_us, 3),
+            "sparse_decode_gbs": round(sparse_bytes / (sparse_us * 1e-6) / 1e9, 1),
+            "quest_step_us": round(step_us, 3)}
+
+
 def time_stream_read(g, steps):
     """A plain linear read of the same page pools (K and V) in one launch per
     step, rotated like the decode steps: the streaming ceiling the decode is
@@ -444,6 +494,13 @@ def main():
                       "traffic": profiled_traffic(w, f"{w.name}:fp8"),
                       "cold_cache_copies": len(g["caches8"])}
         log(f"fp8 codec: {fp8_us:.2f} us/step, {rec['fp8']['achieved_gbs']:.0f} GB/s")
+    if not args.no_quest:
+        top_k = max(1, -(-w.max_blocks // 8))
+        qs = time_quest(w, g, args.steps, args.warmup, top_k)
+        qs["dense_us"] = round(loop_ms * 1e3, 3)
+        log(f"quest: metadata {qs['metadata_us']} us ({qs['metadata_gbs']} GB/s), select {qs['select_us']} us, "
+            f"sparse decode {qs['sparse_decode_us']} us, step {qs['quest_step_us']} us vs dense {qs['dense_us']} us")
+        rec["quest"] = qs
     if not args.no_fused:
         fa = time_append_decode(w, g, args.steps, args.warmup, args.part_tokens)
         new_bytes = w.batch * w.n_kv * (2 * w.hd * 4 + 2 * (w.hd + 4))

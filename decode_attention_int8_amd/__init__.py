@@ -41,6 +41,9 @@ def _load():
         "q8kv_append_decode_attn": [P, P, P, P, I, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, P],
         "q8kv_plan": [I, I, I, I, I, I, P, P],
         "q8kv_fp8_append": [P, P, P, P, P, P, I, P, I, I, I, I, I, P],
+        "q8kv_quest_metadata": [P, P, P, P, P, P, I, I, I, I, I, I, P],
+        "q8kv_quest_select": [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, P],
+        "q8kv_decode_attn_heads": [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, P],
         "q8kv_fp8_decode_attn": [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, P],
         "q8kv_append": [P, P, P, P, P, P, I, P, I, I, I, I, I, P],
         "q8kv_release": [],
@@ -354,6 +357,96 @@ def fp8_decode_attn(q, cache, block_table, seq_lens, scale, out=None, part_token
     else:
         with torch.cuda.device(dev):
             _check(lib.q8kv_fp8_decode_attn(*args, torch.cuda.current_stream(dev).cuda_stream))
+    return out
+
+
+def quest_metadata(cache, block_table, seq_lens, kmax=None, kmin=None):
+    """Per-block channel max / min of the dequantised K cache (QUEST
+    metadata): kmax, kmin fp32 [num_blocks][n_kv][hd], filled for the blocks
+    the table references below each sequence's length.  Returns (kmax, kmin)."""
+    dev, kp, vp, ks, vs = cache._pointers()
+    d = cache.device
+    _need(block_table, "block_table", torch.int32, d, 2)
+    _need(seq_lens, "seq_lens", torch.int32, d, 1)
+    shp = (cache.num_blocks, cache.n_kv, cache.hd)
+    if kmax is None:
+        kmax = torch.full(shp, float("nan"), dtype=torch.float32, device=d)
+    if kmin is None:
+        kmin = torch.full(shp, float("nan"), dtype=torch.float32, device=d)
+    for t, name in ((kmax, "kmax"), (kmin, "kmin")):
+        _need(t, name, torch.float32, d, 3)
+        if tuple(t.shape) != shp:
+            raise ValueError(f"{name} must be {shp}")
+    if block_table.shape[0] != seq_lens.shape[0]:
+        raise ValueError("block_table / seq_lens batch sizes disagree")
+    with torch.cuda.device(dev):
+        _check(lib.q8kv_quest_metadata(kmax.data_ptr(), kmin.data_ptr(), kp, ks, block_table.data_ptr(),
+                                       seq_lens.data_ptr(), block_table.shape[1], cache.num_blocks,
+                                       block_table.shape[0], cache.n_kv, cache.hd, cache.kv_bs,
+                                       torch.cuda.current_stream(dev).cuda_stream))
+    return kmax, kmin
+
+
+def quest_select(q, cache, kmax, kmin, block_table, seq_lens, top_k, sel_table=None, sel_lens=None):
+    """QUEST block selection: (sel_table int32 [batch][n_kv][top_k] kept
+    physical blocks per kv head in logical order, -1 padded; sel_lens int32
+    [batch] tokens they hold)."""
+    dev = cache._pointers()[0]
+    d = cache.device
+    _need(q, "q", torch.float32, d, 3)
+    _need(block_table, "block_table", torch.int32, d, 2)
+    _need(seq_lens, "seq_lens", torch.int32, d, 1)
+    _need(kmax, "kmax", torch.float32, d, 3)
+    _need(kmin, "kmin", torch.float32, d, 3)
+    batch, n_q, hd = q.shape
+    if hd != cache.hd or block_table.shape[0] != batch or seq_lens.shape[0] != batch:
+        raise ValueError("q / block_table / seq_lens / cache shapes disagree")
+    if tuple(kmax.shape) != (cache.num_blocks, cache.n_kv, hd) or kmin.shape != kmax.shape:
+        raise ValueError("kmax / kmin must be [num_blocks][n_kv][hd]")
+    if sel_table is None:
+        sel_table = torch.empty((batch, cache.n_kv, top_k), dtype=torch.int32, device=d)
+    if sel_lens is None:
+        sel_lens = torch.empty((batch,), dtype=torch.int32, device=d)
+    _need(sel_table, "sel_table", torch.int32, d, 3)
+    _need(sel_lens, "sel_lens", torch.int32, d, 1)
+    if tuple(sel_table.shape) != (batch, cache.n_kv, top_k) or tuple(sel_lens.shape) != (batch,):
+        raise ValueError("sel_table must be [batch][n_kv][top_k] and sel_lens [batch]")
+    with torch.cuda.device(dev):
+        _check(lib.q8kv_quest_select(sel_table.data_ptr(), sel_lens.data_ptr(), q.data_ptr(), kmax.data_ptr(),
+                                     kmin.data_ptr(), block_table.data_ptr(), seq_lens.data_ptr(),
+                                     block_table.shape[1], cache.num_blocks, batch, n_q, cache.n_kv, hd,
+                                     cache.kv_bs, int(top_k), torch.cuda.current_stream(dev).cuda_stream))
+    return sel_table, sel_lens
+
+
+def decode_attn_heads(q, cache, head_table, seq_lens, scale, out=None, part_tokens=0):
+    """decode_attn with one block list per kv head: head_table int32
+    [batch][n_kv][max_blocks] (e.g. quest_select's sel_table), seq_lens int32
+    [batch].  Returns out (fp32 [batch][n_q][hd])."""
+    dev, kp, vp, ks, vs = cache._pointers()
+    if not (_ok(q, torch.float32, dev, 3) and _ok(head_table, torch.int32, dev, 3)
+            and _ok(seq_lens, torch.int32, dev, 1)):
+        d = cache.device
+        _need(q, "q", torch.float32, d, 3)
+        _need(head_table, "head_table", torch.int32, d, 3)
+        _need(seq_lens, "seq_lens", torch.int32, d, 1)
+    batch, n_q, hd = q.shape
+    if (hd != cache.hd or head_table.shape[0] != batch or head_table.shape[1] != cache.n_kv
+            or seq_lens.shape[0] != batch):
+        raise ValueError("q / head_table / seq_lens / cache shapes disagree")
+    if out is None:
+        out = torch.empty_like(q)
+    elif not (_ok(out, torch.float32, dev, 3) and out.shape == q.shape):
+        _need(out, "out", torch.float32, cache.device, 3)
+        raise ValueError("out must have q's shape")
+    args = (out.data_ptr(), q.data_ptr(), kp, vp, ks, vs, head_table.data_ptr(), seq_lens.data_ptr(),
+            head_table.shape[2], cache.num_blocks, batch, n_q, cache.n_kv, hd, cache.kv_bs, float(scale),
+            int(part_tokens))
+    if torch.cuda.current_device() == dev:
+        _check(lib.q8kv_decode_attn_heads(*args, torch.cuda.current_stream(dev).cuda_stream))
+    else:
+        with torch.cuda.device(dev):
+            _check(lib.q8kv_decode_attn_heads(*args, torch.cuda.current_stream(dev).cuda_stream))
     return out
 
 

@@ -344,6 +344,9 @@ struct DecodeArgs {
     // [num_blocks][n_kv][kv_bs][hd/64] (ks / vs are then unused)
     const uint8_t* ks8;
     const uint8_t* vs8;
+    // 1: block_table is [batch][max_blocks]; n_kv: [batch][n_kv][max_blocks]
+    // (a block list per kv head, as the QUEST selection produces)
+    int table_rows;
 };
 
 // Partition states cross workgroups (and XCDs) through buffer loads and
@@ -1171,7 +1174,7 @@ q8kv_decode_kernel(const DecodeArgs a) {
         // them alone, not for the first tile queued behind them
         QRows<HD, kThreads> qrows;
         load_q_rows<HD, kThreads>(qrows, a.q + ((size_t)b * a.n_q + (size_t)kh * G) * HD, G, itid);
-        const int32_t* trow = a.table + (size_t)b * a.max_blocks;
+        const int32_t* trow = a.table + ((size_t)b * a.table_rows + (a.table_rows > 1 ? kh : 0)) * a.max_blocks;
         const int t0 = part * a.part_tokens;
         // The first tile's table reads, those of the item's first tile (a
         // wave with no tile of its own loads that one, unused, so that every
@@ -1521,6 +1524,349 @@ __device__ __forceinline__ void fp8_row_store(uint8_t* pages, uint8_t* scales, s
     if (lane % LPB == 0) scales[dst_row * NB + lane / LPB] = (uint8_t)(ex + 127);
 }
 
+// ----------------------------------------------------------------------------
+// QUEST block metadata and selection (page "CANN ops-transformer Quest
+// Prefill Metadata" (xdnf.cn), section on the experiment background: per KV
+// block, the channel-wise maximum and minimum of its tokens' K rows; at
+// decode, the query against that metadata picks the top-k blocks).
+
+struct QuestArgs {
+    float* kmax;               // [num_blocks][n_kv][hd]
+    float* kmin;
+    const int8_t* kp;          // int8 K pages, sub-tile order
+    const float* ks;           // [num_blocks][n_kv][kv_bs]
+    const int32_t* table;      // [batch][max_blocks]
+    const int32_t* lens;       // [batch]
+    const float* q;            // [batch][n_q][hd]
+    float* bounds;             // [batch][n_kv][max_blocks]
+    int32_t* sel_table;        // [batch][n_kv][top_k]
+    int32_t* sel_lens;         // [batch]
+    int batch, max_blocks, num_blocks, n_q, n_kv, kv_bs, top_k;
+};
+
+// Inclusive max / min over the 16 lanes of a DPP row; lane 15 of the row
+// ends with the row's value.
+__device__ __forceinline__ float row16_max(float x) {
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), 0x111, 0xf, 0xf, false)));
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), 0x112, 0xf, 0xf, false)));
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), 0x114, 0xf, 0xf, false)));
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), 0x118, 0xf, 0xf, false)));
+    return x;
+}
+__device__ __forceinline__ float row16_min(float x) {
+    x = fminf(x, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), 0x111, 0xf, 0xf, false)));
+    x = fminf(x, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), 0x112, 0xf, 0xf, false)));
+    x = fminf(x, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), 0x114, 0xf, 0xf, false)));
+    x = fminf(x, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), 0x118, 0xf, 0xf, false)));
+    return x;
+}
+
+// Metadata: one wave per (sequence, logical block, kv head).  The wave reads
+// the page's 16-row sub-tiles (lane 16 r + n: row n, columns 64 c + 16 r ..
+// +16 of chunk c), dequantises each element as float(code) * k_scale of its
+// row, keeps running maxima and minima per column over its rows (rows past
+// the sequence's length are skipped), reduces them over the 16 rows of a DPP
+// row, and lane 15 of each row writes its 16 columns.
+template <int HD>
+__global__ __launch_bounds__(256) void q8kv_quest_metadata_kernel(const QuestArgs a) {
+    constexpr int NPAIR = Geo<HD>::NPAIR;
+    const int lane = threadIdx.x & (kWave - 1);
+    const long long wave = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (wave >= (long long)a.batch * a.max_blocks * a.n_kv) return;
+    const int kh = (int)(wave % a.n_kv);
+    const int j = (int)((wave / a.n_kv) % a.max_blocks);
+    const int b = (int)(wave / ((long long)a.n_kv * a.max_blocks));
+    const int L = min(a.lens[b], a.max_blocks * a.kv_bs);
+    if (j * a.kv_bs >= L) return;
+    const int p = a.table[(size_t)b * a.max_blocks + j];
+    if ((unsigned)p >= (unsigned)a.num_blocks) return;
+    const int rows = min(a.kv_bs, L - j * a.kv_bs);
+    const int n = lane & 15, r = lane >> 4;
+    float mx[NPAIR][16], mn[NPAIR][16];
+#pragma unroll
+    for (int c = 0; c < NPAIR; ++c) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            mx[c][i] = -INFINITY;
+            mn[c][i] = INFINITY;
+        }
+    }
+    const size_t page_row = ((size_t)p * a.n_kv + kh) * a.kv_bs;
+    for (int r0 = 0; r0 < rows; r0 += kSub) {
+        const bool ok = r0 + n < rows;
+        const float sc = a.ks[page_row + r0 + min(n, rows - 1 - r0)];
+        i32x4 ch[NPAIR];
+        load_k_subtile<HD>(ch, a.kp, page_row + r0, lane);
+#pragma unroll
+        for (int c = 0; c < NPAIR; ++c) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int8_t code = (int8_t)((uint32_t)ch[c][i >> 2] >> (8 * (i & 3)));
+                const float v = (float)code * sc;
+                mx[c][i] = ok ? fmaxf(mx[c][i], v) : mx[c][i];
+                mn[c][i] = ok ? fminf(mn[c][i], v) : mn[c][i];
+            }
+        }
+    }
+    const size_t out = ((size_t)p * a.n_kv + kh) * HD;
+#pragma unroll
+    for (int c = 0; c < NPAIR; ++c) {
+        f32x4 vx[4], vn[4];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            vx[i >> 2][i & 3] = row16_max(mx[c][i]);
+            vn[i >> 2][i & 3] = row16_min(mn[c][i]);
+        }
+        if (n == 15) {
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+                *reinterpret_cast<f32x4*>(a.kmax + out + 64 * c + 16 * r + 4 * i4) = vx[i4];
+                *reinterpret_cast<f32x4*>(a.kmin + out + 64 * c + 16 * r + 4 * i4) = vn[i4];
+            }
+        }
+    }
+}
+
+// Bounds: one workgroup per (sequence, kv head, run of kQuestRun logical
+// blocks); its waves take the run's blocks in turn.  A wave holds the query
+// rows of the kv head (lanes over channels, EPL = HD / 64 each) and, per
+// block j < last, forms for every query head h the lane's part of
+// sum_c max(q_h[c] * kmax[c], q_h[c] * kmin[c]); the eight heads' sums are
+// reduced across the wave with a reduce-scatter butterfly (13 exchanges
+// instead of 48), and the largest over the heads is the block's bound.
+constexpr int kQuestRun = 16;
+
+template <int HD>
+__global__ __launch_bounds__(256) void q8kv_quest_bounds_kernel(const QuestArgs a) {
+    constexpr int EPL = HD / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int runs = (a.max_blocks + kQuestRun - 1) / kQuestRun;
+    const int run = blockIdx.x % runs;
+    const int kh = (blockIdx.x / runs) % a.n_kv;
+    const int b = blockIdx.x / (runs * a.n_kv);
+    const int L = min(a.lens[b], a.max_blocks * a.kv_bs);
+    const int nblk = (max(L, 0) + a.kv_bs - 1) / a.kv_bs;
+    const int j0 = run * kQuestRun;
+    if (j0 >= nblk - 1) return;  // the last block is always kept
+    const int G = a.n_q / a.n_kv;
+    float qv[kHeadGroup][EPL];
+#pragma unroll
+    for (int g = 0; g < kHeadGroup; ++g) {
+        const float* qh = a.q + ((size_t)b * a.n_q + (size_t)kh * G + min(g, G - 1)) * HD + (size_t)lane * EPL;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) qv[g][e] = qh[e];
+    }
+    // head whose full sum this lane ends with after the butterfly
+    const int hl = 4 * ((lane >> 5) & 1) + 2 * ((lane >> 4) & 1) + ((lane >> 3) & 1);
+    const int j1 = min(j0 + kQuestRun, nblk - 1);
+    // the wave's blocks (at most kQuestRun / kWaves) are loaded before any
+    // is reduced, so their latencies overlap
+    constexpr int PW = kQuestRun / kWaves;
+    float bmx[PW][EPL], bmn[PW][EPL];
+    int bp[PW];
+#pragma unroll
+    for (int w = 0; w < PW; ++w) {
+        const int j = min(j0 + wid + kWaves * w, j1 - 1);
+        bp[w] = a.table[(size_t)b * a.max_blocks + j];
+        const int pc = (unsigned)bp[w] < (unsigned)a.num_blocks ? bp[w] : 0;
+        const size_t m0 = ((size_t)pc * a.n_kv + kh) * HD + (size_t)lane * EPL;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+            bmx[w][e] = a.kmax[m0 + e];
+            bmn[w][e] = a.kmin[m0 + e];
+        }
+    }
+#pragma unroll
+    for (int w = 0; w < PW; ++w) {
+        const int j = j0 + wid + kWaves * w;
+        if (j >= j1) break;  // wave-uniform
+        const int p = bp[w];
+        float u;
+        if ((unsigned)p < (unsigned)a.num_blocks) {
+            const float* mx = bmx[w];
+            const float* mn = bmn[w];
+            float t[kHeadGroup];
+#pragma unroll
+            for (int g = 0; g < kHeadGroup; ++g) {
+                t[g] = 0.0f;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) t[g] += fmaxf(qv[g][e] * mx[e], qv[g][e] * mn[e]);
+            }
+            // reduce-scatter: 8 sums -> 4 (xor 32) -> 2 (xor 16) -> 1 (xor 8)
+            const bool hi32 = (lane & 32) != 0, hi16 = (lane & 16) != 0, hi8 = (lane & 8) != 0;
+            float s4[4], s2[2];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float keep = hi32 ? t[i + 4] : t[i], give = hi32 ? t[i] : t[i + 4];
+                s4[i] = keep + __shfl_xor(give, 32);
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const float keep = hi16 ? s4[i + 2] : s4[i], give = hi16 ? s4[i] : s4[i + 2];
+                s2[i] = keep + __shfl_xor(give, 16);
+            }
+            float v;
+            {
+                const float keep = hi8 ? s2[1] : s2[0], give = hi8 ? s2[0] : s2[1];
+                v = keep + __shfl_xor(give, 8);
+            }
+            v += __shfl_xor(v, 4);
+            v += __shfl_xor(v, 2);
+            v += __shfl_xor(v, 1);
+            float m = hl < G ? v : -INFINITY;
+            m = fmaxf(m, __shfl_xor(m, 8));
+            m = fmaxf(m, __shfl_xor(m, 16));
+            m = fmaxf(m, __shfl_xor(m, 32));
+            u = m;
+        } else {
+            u = NAN;  // an entry outside the pool: see the top-k kernel
+        }
+        if (lane == 0) a.bounds[((size_t)b * a.n_kv + kh) * a.max_blocks + j] = u;
+    }
+}
+
+// Order-preserving map of a float to uint32 (larger float, larger key; NaN
+// above +inf).
+__device__ __forceinline__ uint32_t order_key(float x) {
+    const uint32_t u = __float_as_uint(x);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+constexpr int kQuestPer = 16;  // candidate blocks per thread of the top-k workgroup (<= 4096 blocks)
+
+// Inclusive prefix sum over the wave with DPP: shifts by 1, 2, 4, 8 inside
+// each row of 16 lanes, then the row_bcast steps carry lane 15 of a row into
+// the next row and lane 31 into the upper half (no LDS round trips).
+__device__ __forceinline__ int wave_inclusive(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+    return v;
+}
+
+// Workgroup-wide inclusive prefix of one int per thread (thread order) and
+// the total; lsum holds kWaves ints.
+__device__ __forceinline__ int block_inclusive(int v, int* lsum, int& total) {
+    const int w = threadIdx.x >> 6;
+    const int incl = wave_inclusive(v);
+    __syncthreads();  // lsum's previous readers are done
+    if ((threadIdx.x & 63) == 63) lsum[w] = incl;
+    __syncthreads();
+    int base = 0;
+    total = 0;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) {
+        base += i < w ? lsum[i] : 0;
+        total += lsum[i];
+    }
+    return base + incl;
+}
+
+// Top-k: one workgroup per (sequence, kv head).  The k = top_k - 1 largest
+// bounds among blocks 0 .. nblk-2 (ties to the lower index) plus the last
+// block are listed in logical order as physical blocks; -1 pads.  Each
+// thread holds a contiguous run of at most kQuestPer candidates' keys.  The
+// k-th largest key T is found one byte at a time, most significant first:
+// a 256-bin LDS histogram of the candidates that match the bytes fixed so
+// far, scanned from the top bin down, fixes the next byte and how many keys
+// equal to T must still be taken (the lowest-indexed ones).  Two prefix sums
+// then place the blocks above T and those ties in logical order.
+__global__ __launch_bounds__(kThreads) void q8kv_quest_topk_kernel(const QuestArgs a) {
+    __shared__ int lhist[256];
+    __shared__ int lsum[kWaves];
+    __shared__ int lpick[2];
+    const int b = blockIdx.x / a.n_kv, kh = blockIdx.x % a.n_kv;
+    const int tid = threadIdx.x;
+    const int L = min(a.lens[b], a.max_blocks * a.kv_bs);
+    const int nblk = (max(L, 0) + a.kv_bs - 1) / a.kv_bs;
+    const int32_t* trow = a.table + (size_t)b * a.max_blocks;
+    int32_t* srow = a.sel_table + ((size_t)b * a.n_kv + kh) * a.top_k;
+    if (kh == 0 && tid == 0) a.sel_lens[b] = nblk == 0 ? 0 : (min(nblk, a.top_k) - 1) * a.kv_bs + (L - (nblk - 1) * a.kv_bs);
+    if (nblk <= a.top_k) {
+        for (int i = tid; i < a.top_k; i += kThreads) srow[i] = i < nblk ? trow[i] : -1;
+        return;
+    }
+    const int m = nblk - 1, k = a.top_k - 1;
+    const int per = (m + kThreads - 1) / kThreads;  // <= kQuestPer (checked on the host)
+    const int j0 = tid * per;
+    const int cnt_in = max(min(per, m - j0), 0);
+    const float* brow = a.bounds + ((size_t)b * a.n_kv + kh) * a.max_blocks;
+    // A NaN bound (a table entry outside the pool) maps above +inf, so that
+    // block is selected and the decode over the selection meets the bad
+    // entry and writes a NaN row, as the dense decode would.  Slots past the
+    // thread's run hold key 0, below every key the bounds can have (they
+    // never count: T >= 1 whenever k > 0).
+    uint32_t key[kQuestPer];
+    int32_t phys[kQuestPer];
+#pragma unroll
+    for (int i = 0; i < kQuestPer; ++i) {
+        const int jj = min(j0 + i, m - 1);
+        key[i] = __float_as_uint(brow[jj]);
+        phys[i] = trow[jj];
+    }
+#pragma unroll
+    for (int i = 0; i < kQuestPer; ++i) key[i] = i < cnt_in ? order_key(__uint_as_float(key[i])) : 0u;
+
+    uint32_t T = 0xffffffffu;  // k == 0: nothing but the last block
+    int krem = 0;              // keys equal to T still to take
+    if (k > 0) {
+        uint32_t prefix = 0;
+        krem = k;
+        for (int shift = 24; shift >= 0; shift -= 8) {
+            lhist[tid] = 0;
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < kQuestPer; ++i) {
+                const bool match = shift == 24 || (key[i] >> (shift + 8)) == prefix;
+                if (key[i] != 0u && match) atomicAdd(&lhist[(key[i] >> shift) & 255], 1);
+            }
+            __syncthreads();
+            const int c = lhist[255 - tid];  // thread t holds bin 255 - t
+            int total;
+            const int cum = block_inclusive(c, lsum, total);  // keys in bins >= 255 - t
+            if (cum >= krem && cum - c < krem) {
+                lpick[0] = 255 - tid;
+                lpick[1] = krem - (cum - c);
+            }
+            __syncthreads();
+            prefix = (prefix << 8) | (uint32_t)lpick[0];
+            krem = lpick[1];
+        }
+        T = prefix;
+    }
+    // every block above T, then the first krem ties in index order
+    int ties = 0;
+#pragma unroll
+    for (int i = 0; i < kQuestPer; ++i) ties += key[i] == T ? 1 : 0;
+    int dummy;
+    const int tie0 = block_inclusive(ties, lsum, dummy) - ties;
+    int mine = 0;
+    {
+        int t = tie0;
+#pragma unroll
+        for (int i = 0; i < kQuestPer; ++i) {
+            const bool tie = key[i] == T;
+            mine += (key[i] > T || (tie && t < krem)) ? 1 : 0;
+            t += tie ? 1 : 0;
+        }
+    }
+    int pos = block_inclusive(mine, lsum, dummy) - mine;
+    {
+        int t = tie0;
+#pragma unroll
+        for (int i = 0; i < kQuestPer; ++i) {
+            const bool tie = key[i] == T;
+            if (key[i] > T || (tie && t < krem)) srow[pos++] = phys[i];
+            t += tie ? 1 : 0;
+        }
+    }
+    if (tid == 0) srow[k] = trow[nblk - 1];
+}
+
 struct Fp8AppendArgs {
     uint8_t* kp;
     uint8_t* vp;
@@ -1672,6 +2018,8 @@ struct Workspace {
     int* ticket = nullptr;  // [2]
     int* arrive = nullptr;  // [arrive_n]
     size_t arrive_n = 0;
+    float* bounds = nullptr;  // QUEST block bounds [bounds_n]
+    size_t bounds_n = 0;
 };
 std::mutex g_mu;
 std::map<std::pair<int, void*>, Workspace> g_ws;
@@ -1798,12 +2146,14 @@ int decode_impl(float* out, const float* q, const int8_t* kp, const int8_t* vp, 
                 const float* vs, const int32_t* table, const int32_t* lens, int max_blocks,
                 int num_blocks, int batch, int n_q, int n_kv, int hd, int kv_bs, float scale,
                 int part_tokens, void* stream, const void* knew = nullptr, const void* vnew = nullptr,
-                int new_dtype = 0, const uint8_t* ks8 = nullptr, const uint8_t* vs8 = nullptr) {
+                int new_dtype = 0, const uint8_t* ks8 = nullptr, const uint8_t* vs8 = nullptr,
+                bool head_tables = false) {
     const bool fp8 = ks8 != nullptr || vs8 != nullptr;
     if (!out || !q || !kp || !vp || !table || !lens || (fp8 ? (!ks8 || !vs8) : (!ks || !vs)))
         return fail(Q8KV_ENULL, "a tensor pointer is NULL");
     if ((knew == nullptr) != (vnew == nullptr)) return fail(Q8KV_ENULL, "k_new and v_new must both be given");
     if (knew && new_dtype != 0 && new_dtype != 1) return fail(Q8KV_EINVAL, "src_dtype must be 0 (fp32) or 1 (bf16)");
+    if (knew && head_tables) return fail(Q8KV_EINVAL, "the fused append takes a per-sequence block table");
     if (batch <= 0 || n_q <= 0) return fail(Q8KV_EINVAL, "batch (%d) and n_q_heads (%d) must be positive", batch, n_q);
     if (batch > kMaxBatch) return fail(Q8KV_EINVAL, "batch (%d) exceeds %d sequences per call", batch, kMaxBatch);
     int rc = check_cache_shape(num_blocks, n_kv, hd, kv_bs);
@@ -1839,7 +2189,7 @@ int decode_impl(float* out, const float* q, const int8_t* kp, const int8_t* vp, 
     const unsigned grid = (unsigned)std::min<long long>(items, li.resident);
     DecodeArgs da{out, q, kp, vp, ks, vs, table, lens, nullptr, nullptr, nullptr, nullptr,
                   batch, max_blocks, num_blocks, n_q, n_kv, kv_bs, G, pt, np, scale * kLog2e,
-                  knew, vnew, new_dtype, ks8, vs8};
+                  knew, vnew, new_dtype, ks8, vs8, head_tables ? n_kv : 1};
     if (items > (long long)grid) {
         std::lock_guard<std::mutex> lock(g_mu);
         Workspace& w = g_ws[{dev, stream}];
@@ -2049,6 +2399,107 @@ int q8kv_fp8_decode_attn(float* out, const float* q, const uint8_t* k_pages, con
                        n_kv_heads, hd, kv_bs, scale, part_tokens, stream, nullptr, nullptr, 0, k_scale, v_scale);
 }
 
+int q8kv_decode_attn_heads(float* out, const float* q, const int8_t* k_pages, const int8_t* v_pages,
+                           const float* k_scale, const float* v_scale, const int32_t* head_table,
+                           const int32_t* seq_lens, int max_blocks_per_seq, int num_blocks, int batch,
+                           int n_q_heads, int n_kv_heads, int hd, int kv_bs, float scale, int part_tokens,
+                           void* stream) {
+    g_err.clear();
+    return decode_impl(out, q, k_pages, v_pages, k_scale, v_scale, head_table, seq_lens, max_blocks_per_seq,
+                       num_blocks, batch, n_q_heads, n_kv_heads, hd, kv_bs, scale, part_tokens, stream, nullptr,
+                       nullptr, 0, nullptr, nullptr, true);
+}
+
+int q8kv_quest_metadata(float* kmax, float* kmin, const int8_t* k_pages, const float* k_scale,
+                        const int32_t* block_table, const int32_t* seq_lens, int max_blocks_per_seq,
+                        int num_blocks, int batch, int n_kv_heads, int hd, int kv_bs, void* stream) {
+    g_err.clear();
+    if (!kmax || !kmin || !k_pages || !k_scale || !block_table || !seq_lens)
+        return fail(Q8KV_ENULL, "a tensor pointer is NULL");
+    if (batch <= 0) return fail(Q8KV_EINVAL, "batch must be positive (got %d)", batch);
+    int rc = check_cache_shape(num_blocks, n_kv_heads, hd, kv_bs);
+    if (rc) return rc;
+    if (max_blocks_per_seq <= 0 || (long long)max_blocks_per_seq * kv_bs > (INT_MAX / 2))
+        return fail(Q8KV_EINVAL, "bad max_blocks_per_seq (%d)", max_blocks_per_seq);
+    const long long waves = (long long)batch * max_blocks_per_seq * n_kv_heads;
+    const long long grid = (waves + 3) / 4;
+    if (grid > INT_MAX) return fail(Q8KV_EINVAL, "metadata shape too large");
+    QuestArgs qa{kmax, kmin, k_pages, k_scale, block_table, seq_lens, nullptr, nullptr, nullptr, nullptr,
+                 batch, max_blocks_per_seq, num_blocks, 0, n_kv_heads, kv_bs, 0};
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    switch (hd) {
+        case 64: hipLaunchKernelGGL(q8kv_quest_metadata_kernel<64>, dim3((unsigned)grid), dim3(256), 0, st, qa); break;
+        case 128: hipLaunchKernelGGL(q8kv_quest_metadata_kernel<128>, dim3((unsigned)grid), dim3(256), 0, st, qa); break;
+        default: hipLaunchKernelGGL(q8kv_quest_metadata_kernel<256>, dim3((unsigned)grid), dim3(256), 0, st, qa); break;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "metadata kernel launch");
+    return Q8KV_OK;
+}
+
+int q8kv_quest_select(int32_t* sel_table, int32_t* sel_lens, const float* q, const float* kmax,
+                      const float* kmin, const int32_t* block_table, const int32_t* seq_lens,
+                      int max_blocks_per_seq, int num_blocks, int batch, int n_q_heads, int n_kv_heads,
+                      int hd, int kv_bs, int top_k, void* stream) {
+    g_err.clear();
+    if (!sel_table || !sel_lens || !q || !kmax || !kmin || !block_table || !seq_lens)
+        return fail(Q8KV_ENULL, "a tensor pointer is NULL");
+    if (batch <= 0 || n_q_heads <= 0) return fail(Q8KV_EINVAL, "batch and n_q_heads must be positive");
+    int rc = check_cache_shape(num_blocks, n_kv_heads, hd, kv_bs);
+    if (rc) return rc;
+    if (n_q_heads % n_kv_heads) return fail(Q8KV_EINVAL, "n_q_heads (%d) is not a multiple of n_kv_heads (%d)", n_q_heads, n_kv_heads);
+    if (max_blocks_per_seq <= 0 || (long long)max_blocks_per_seq * kv_bs > (INT_MAX / 2))
+        return fail(Q8KV_EINVAL, "bad max_blocks_per_seq (%d)", max_blocks_per_seq);
+    if (max_blocks_per_seq - 1 > kThreads * kQuestPer)
+        return fail(Q8KV_EINVAL, "selection supports at most %d blocks per sequence (got %d)", kThreads * kQuestPer + 1, max_blocks_per_seq);
+    if (top_k <= 0) return fail(Q8KV_EINVAL, "top_k must be positive (got %d)", top_k);
+    if (n_q_heads / n_kv_heads > kHeadGroup)
+        return fail(Q8KV_EINVAL, "query heads per kv head must be <= %d", kHeadGroup);
+    const long long waves = (long long)batch * n_kv_heads * max_blocks_per_seq;
+    if ((waves + 3) / 4 > INT_MAX || (long long)batch * n_kv_heads > INT_MAX) return fail(Q8KV_EINVAL, "selection shape too large");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    float* bounds = nullptr;
+    {
+        const size_t need = (size_t)waves;
+        std::lock_guard<std::mutex> lock(g_mu);
+        Workspace& w = g_ws[{dev, stream}];
+        if (w.bounds_n < need) {
+            if (w.bounds) {
+                e = hipStreamSynchronize(st);
+                if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+                e = hipFree(w.bounds);
+                w.bounds = nullptr;
+                w.bounds_n = 0;
+                if (e != hipSuccess) return hip_fail(e, "hipFree");
+            }
+            void* t = nullptr;
+            e = hipMalloc(&t, need * sizeof(float));
+            if (e != hipSuccess) return fail(Q8KV_ENOMEM, "hipMalloc of the selection bounds: %s", hipGetErrorString(e));
+            w.bounds = static_cast<float*>(t);
+            w.bounds_n = need;
+        }
+        bounds = w.bounds;
+    }
+    QuestArgs qa{const_cast<float*>(kmax), const_cast<float*>(kmin), nullptr, nullptr, block_table, seq_lens, q,
+                 bounds, sel_table, sel_lens, batch, max_blocks_per_seq, num_blocks, n_q_heads, n_kv_heads,
+                 kv_bs, top_k};
+    const unsigned grid = (unsigned)((long long)batch * n_kv_heads * ((max_blocks_per_seq + kQuestRun - 1) / kQuestRun));
+    switch (hd) {
+        case 64: hipLaunchKernelGGL(q8kv_quest_bounds_kernel<64>, dim3(grid), dim3(256), 0, st, qa); break;
+        case 128: hipLaunchKernelGGL(q8kv_quest_bounds_kernel<128>, dim3(grid), dim3(256), 0, st, qa); break;
+        default: hipLaunchKernelGGL(q8kv_quest_bounds_kernel<256>, dim3(grid), dim3(256), 0, st, qa); break;
+    }
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "bounds kernel launch");
+    hipLaunchKernelGGL(q8kv_quest_topk_kernel, dim3((unsigned)(batch * n_kv_heads)), dim3(kThreads), 0, st, qa);
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "top-k kernel launch");
+    return Q8KV_OK;
+}
+
 const char* q8kv_last_error(void) { return g_err.c_str(); }
 
 int q8kv_release(void) {
@@ -2058,12 +2509,13 @@ int q8kv_release(void) {
     int cur = 0;
     if (!g_ws.empty() && hipGetDevice(&cur) != hipSuccess) cur = -1;
     for (auto& kv : g_ws) {
-        if (!kv.second.ptr && !kv.second.ticket && !kv.second.arrive) continue;
+        if (!kv.second.ptr && !kv.second.ticket && !kv.second.arrive && !kv.second.bounds) continue;
         hipError_t e = hipSetDevice(kv.first.first);
         if (e == hipSuccess) e = hipDeviceSynchronize();
         if (e == hipSuccess && kv.second.ptr) e = hipFree(kv.second.ptr);
         if (e == hipSuccess && kv.second.ticket) e = hipFree(kv.second.ticket);
         if (e == hipSuccess && kv.second.arrive) e = hipFree(kv.second.arrive);
+        if (e == hipSuccess && kv.second.bounds) e = hipFree(kv.second.bounds);
         if (e != hipSuccess && rc == Q8KV_OK) rc = hip_fail(e, "releasing workspace");
     }
     g_ws.clear();

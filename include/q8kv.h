@@ -215,6 +215,66 @@ int q8kv_fp8_decode_attn(float* out, const float* q, const uint8_t* k_pages,
                          int batch, int n_q_heads, int n_kv_heads, int hd, int kv_bs,
                          float scale, int part_tokens, void* stream);
 
+/*
+ * QUEST block metadata (page "CANN ops-transformer Quest Prefill Metadata"
+ * (xdnf.cn), section on the experiment background: for every KV block, the
+ * per-channel maximum and minimum over the block's tokens of the K cache).
+ *
+ * kmax, kmin  fp32 [num_blocks][n_kv_heads][hd], caller-owned.  For every
+ *             sequence b and logical block j < ceil(L / kv_bs) with
+ *             L = seq_lens[b], physical block p = block_table[b][j]:
+ *             kmax[p][kh][c] / kmin[p][kh][c] = max / min over the block's
+ *             rows r < min(kv_bs, L - j kv_bs) of float(k code) * k_scale
+ *             of that row (an fp32 product).  Other blocks, and table entries
+ *             outside [0, num_blocks), are left untouched.
+ * Other arguments as for q8kv_decode_attn.  A block shared by several
+ * sequences must cover the same rows in each.
+ */
+int q8kv_quest_metadata(float* kmax, float* kmin, const int8_t* k_pages, const float* k_scale,
+                        const int32_t* block_table, const int32_t* seq_lens,
+                        int max_blocks_per_seq, int num_blocks, int batch, int n_kv_heads,
+                        int hd, int kv_bs, void* stream);
+
+/*
+ * Query-aware block selection over that metadata (same page: at decode the
+ * query is matched against each block's metadata and the top-k blocks take
+ * part in attention).  The bound of block j for query head h is the largest
+ * dot product any vector inside the block's [kmin, kmax] box can have with
+ * q_h: sum over c of max(q_h[c] kmax[c], q_h[c] kmin[c]), computed in fp32;
+ * a kv head takes the largest bound over its query heads.  For each
+ * sequence with nblk = ceil(L / kv_bs) blocks: if nblk <= top_k every block
+ * is kept; else the last block (which holds the newest token) plus the
+ * top_k - 1 blocks of largest bound among the others, ties to the lower
+ * logical index.
+ *
+ * sel_table  int32 [batch][n_kv_heads][top_k]: the kept physical blocks of
+ *            each kv head in logical order, -1 past the kept count.
+ * sel_lens   int32 [batch]: tokens the kept blocks hold
+ *            ((kept - 1) * kv_bs + the last block's rows), the same for every
+ *            kv head; 0 for an empty sequence.
+ * max_blocks_per_seq may be at most 4097.  The bounds go through a
+ * library-owned workspace (grown on demand, freed by q8kv_release).
+ * q8kv_decode_attn_heads(sel_table, sel_lens, max_blocks_per_seq = top_k)
+ * then attends over the kept tokens only.
+ */
+int q8kv_quest_select(int32_t* sel_table, int32_t* sel_lens, const float* q, const float* kmax,
+                      const float* kmin, const int32_t* block_table, const int32_t* seq_lens,
+                      int max_blocks_per_seq, int num_blocks, int batch, int n_q_heads,
+                      int n_kv_heads, int hd, int kv_bs, int top_k, void* stream);
+
+/*
+ * q8kv_decode_attn_split with one block list per kv head: head_table is
+ * int32 [batch][n_kv_heads][max_blocks_per_seq]; kv head kh of sequence b
+ * reads token t from block head_table[b][kh][t / kv_bs].  seq_lens[b] is the
+ * token count of every kv head's list.  Same contract otherwise.
+ */
+int q8kv_decode_attn_heads(float* out, const float* q, const int8_t* k_pages,
+                           const int8_t* v_pages, const float* k_scale, const float* v_scale,
+                           const int32_t* head_table, const int32_t* seq_lens,
+                           int max_blocks_per_seq, int num_blocks, int batch, int n_q_heads,
+                           int n_kv_heads, int hd, int kv_bs, float scale, int part_tokens,
+                           void* stream);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* q8kv_last_error(void);
 

@@ -14,7 +14,7 @@ NUL = ctypes.c_void_p(0)
 
 def test_exports_every_declared_symbol():
     names = q8.header_symbols()
-    assert len(names) == 12
+    assert len(names) == 15
     for n in names:
         assert hasattr(L, n), n
 
@@ -176,3 +176,49 @@ def test_plan_is_shape_only_and_sane():
 
 def test_release_without_workspace_is_ok():
     q8.release()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(sel=NUL), q8.Q8KV_ENULL),
+    (dict(kmax=NUL), q8.Q8KV_ENULL),
+    (dict(top_k=0), q8.Q8KV_EINVAL),
+    (dict(max_blocks=5000), q8.Q8KV_EINVAL),
+    (dict(n_q=18, n_kv=2), q8.Q8KV_EINVAL),
+    (dict(n_q=6, n_kv=4), q8.Q8KV_EINVAL),
+    (dict(hd=96), q8.Q8KV_EINVAL),
+])
+def test_quest_select_rejects_before_any_hip_call(kw, code):
+    a = dict(sel=FAKE, sl_out=FAKE, q=FAKE, kmax=FAKE, kmin=FAKE, bt=FAKE, sl=FAKE, max_blocks=8,
+             num_blocks=16, batch=2, n_q=8, n_kv=2, hd=128, kv_bs=16, top_k=4)
+    a.update(kw)
+    rc = L.q8kv_quest_select(a["sel"], a["sl_out"], a["q"], a["kmax"], a["kmin"], a["bt"], a["sl"],
+                             a["max_blocks"], a["num_blocks"], a["batch"], a["n_q"], a["n_kv"], a["hd"],
+                             a["kv_bs"], a["top_k"], NUL)
+    assert rc == code
+    assert q8.last_error() != ""
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kmax=NUL), q8.Q8KV_ENULL),
+    (dict(kp=NUL), q8.Q8KV_ENULL),
+    (dict(batch=0), q8.Q8KV_EINVAL),
+    (dict(max_blocks=0), q8.Q8KV_EINVAL),
+    (dict(kv_bs=24), q8.Q8KV_EINVAL),
+])
+def test_quest_metadata_rejects_before_any_hip_call(kw, code):
+    a = dict(kmax=FAKE, kmin=FAKE, kp=FAKE, ks=FAKE, bt=FAKE, sl=FAKE, max_blocks=8, num_blocks=16, batch=2,
+             n_kv=2, hd=128, kv_bs=16)
+    a.update(kw)
+    rc = L.q8kv_quest_metadata(a["kmax"], a["kmin"], a["kp"], a["ks"], a["bt"], a["sl"], a["max_blocks"],
+                               a["num_blocks"], a["batch"], a["n_kv"], a["hd"], a["kv_bs"], NUL)
+    assert rc == code
+    assert q8.last_error() != ""
+
+
+def test_decode_heads_rejects_before_any_hip_call():
+    rc = L.q8kv_decode_attn_heads(FAKE, FAKE, FAKE, FAKE, FAKE, NUL, FAKE, FAKE, 8, 16, 2, 8, 2, 128, 16,
+                                  0.088, 0, NUL)
+    assert rc == q8.Q8KV_ENULL
+    rc = L.q8kv_decode_attn_heads(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 16, 2, 8, 2, 100, 16,
+                                  0.088, 0, NUL)
+    assert rc == q8.Q8KV_EINVAL
