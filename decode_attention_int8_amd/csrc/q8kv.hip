@@ -177,6 +177,16 @@ __device__ __forceinline__ float swap32_sum(float x) {
     auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
+// Sum over all 64 lanes, left in every lane: quad_perm swaps (xor 1, 2),
+// row_half_mirror (xor 7) and row_mirror (xor 15) inside each row of 16,
+// then the permlane16 / permlane32 swaps across rows.
+__device__ __forceinline__ float wave_allsum(float x) {
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xb1, 0xf, 0xf, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4e, 0xf, 0xf, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xf, 0xf, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xf, 0xf, false));
+    return swap32_sum(swap16_sum(x));
+}
 __device__ __forceinline__ int r_of(int lane) { return lane >> 4; }
 __device__ __forceinline__ float lane_read(float x, int src_lane) {
     return __int_as_float(__builtin_amdgcn_ds_bpermute(src_lane << 2, __float_as_int(x)));
@@ -1631,9 +1641,9 @@ __global__ __launch_bounds__(256) void q8kv_quest_metadata_kernel(const QuestArg
 // blocks); its waves take the run's blocks in turn.  A wave holds the query
 // rows of the kv head (lanes over channels, EPL = HD / 64 each) and, per
 // block j < last, forms for every query head h the lane's part of
-// sum_c max(q_h[c] * kmax[c], q_h[c] * kmin[c]); the eight heads' sums are
-// reduced across the wave with a reduce-scatter butterfly (13 exchanges
-// instead of 48), and the largest over the heads is the block's bound.
+// sum_c max(q_h[c] * kmax[c], q_h[c] * kmin[c]); each head's sum is reduced
+// across the wave with DPP and permlane swaps (no LDS), and the largest over
+// the heads is the block's bound.
 constexpr int kQuestRun = 16;
 
 template <int HD>
@@ -1657,8 +1667,6 @@ __global__ __launch_bounds__(256) void q8kv_quest_bounds_kernel(const QuestArgs 
 #pragma unroll
         for (int e = 0; e < EPL; ++e) qv[g][e] = qh[e];
     }
-    // head whose full sum this lane ends with after the butterfly
-    const int hl = 4 * ((lane >> 5) & 1) + 2 * ((lane >> 4) & 1) + ((lane >> 3) & 1);
     const int j1 = min(j0 + kQuestRun, nblk - 1);
     // the wave's blocks (at most kQuestRun / kWaves) are loaded before any
     // is reduced, so their latencies overlap
@@ -1693,31 +1701,11 @@ __global__ __launch_bounds__(256) void q8kv_quest_bounds_kernel(const QuestArgs 
 #pragma unroll
                 for (int e = 0; e < EPL; ++e) t[g] += fmaxf(qv[g][e] * mx[e], qv[g][e] * mn[e]);
             }
-            // reduce-scatter: 8 sums -> 4 (xor 32) -> 2 (xor 16) -> 1 (xor 8)
-            const bool hi32 = (lane & 32) != 0, hi16 = (lane & 16) != 0, hi8 = (lane & 8) != 0;
-            float s4[4], s2[2];
+            // the kv head's rows past G repeat row G - 1, so the largest
+            // over all eight is the largest over the kv head's query heads
+            float m = -INFINITY;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float keep = hi32 ? t[i + 4] : t[i], give = hi32 ? t[i] : t[i + 4];
-                s4[i] = keep + __shfl_xor(give, 32);
-            }
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const float keep = hi16 ? s4[i + 2] : s4[i], give = hi16 ? s4[i] : s4[i + 2];
-                s2[i] = keep + __shfl_xor(give, 16);
-            }
-            float v;
-            {
-                const float keep = hi8 ? s2[1] : s2[0], give = hi8 ? s2[0] : s2[1];
-                v = keep + __shfl_xor(give, 8);
-            }
-            v += __shfl_xor(v, 4);
-            v += __shfl_xor(v, 2);
-            v += __shfl_xor(v, 1);
-            float m = hl < G ? v : -INFINITY;
-            m = fmaxf(m, __shfl_xor(m, 8));
-            m = fmaxf(m, __shfl_xor(m, 16));
-            m = fmaxf(m, __shfl_xor(m, 32));
+            for (int g = 0; g < kHeadGroup; ++g) m = fmaxf(m, wave_allsum(t[g]));
             u = m;
         } else {
             u = NAN;  // an entry outside the pool: see the top-k kernel
