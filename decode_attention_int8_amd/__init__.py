@@ -42,6 +42,8 @@ def _load():
         "q8kv_plan": [I, I, I, I, I, I, P, P],
         "q8kv_fp8_append": [P, P, P, P, P, P, I, P, I, I, I, I, I, P],
         "q8kv_quest_metadata": [P, P, P, P, P, P, I, I, I, I, I, I, P],
+        "q8kv_q40_append": [P, P, P, P, P, P, I, P, I, I, I, I, I, P],
+        "q8kv_q40_decode_attn": [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, P],
         "q8kv_quest_select": [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, P],
         "q8kv_decode_attn_heads": [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, P],
         "q8kv_fp8_decode_attn": [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, P],
@@ -327,6 +329,96 @@ class Fp8KVCache(PagedKVCache):
                 slot_mapping.data_ptr(), n, self.num_blocks, self.n_kv, self.hd, self.kv_bs)
         with torch.cuda.device(dev):
             _check(lib.q8kv_fp8_append(*args, torch.cuda.current_stream(dev).cuda_stream))
+
+
+class Q40KVCache(PagedKVCache):
+    """Device page pool of one layer's q4_0 KV cache (4-bit codes, one fp16
+    scale per 32 elements of a row).
+
+    k_pages, v_pages uint8 [num_blocks][n_kv][kv_bs][hd/2] (sub-tile nibble order);
+    k_scale, v_scale float16 [num_blocks][n_kv][kv_bs][hd/32].
+    """
+
+    def __init__(self, num_blocks, n_kv, kv_bs, hd, device="cuda"):
+        dev = torch.device(device)
+        self.num_blocks, self.n_kv, self.kv_bs, self.hd = num_blocks, n_kv, kv_bs, hd
+        self.k_pages = torch.empty((num_blocks, n_kv, kv_bs, hd // 2), dtype=torch.uint8, device=dev)
+        self.v_pages = torch.empty_like(self.k_pages)
+        self.k_scale = torch.empty((num_blocks, n_kv, kv_bs, hd // 32), dtype=torch.float16, device=dev)
+        self.v_scale = torch.empty_like(self.k_scale)
+
+    @classmethod
+    def wrap(cls, k_pages, v_pages, k_scale, v_scale):
+        self = cls.__new__(cls)
+        object.__setattr__(self, "_meta", None)
+        self.k_pages, self.v_pages, self.k_scale, self.v_scale = k_pages, v_pages, k_scale, v_scale
+        nb, n_kv, kv_bs, half = k_pages.shape
+        self.num_blocks, self.n_kv, self.kv_bs, self.hd = nb, n_kv, kv_bs, 2 * half
+        return self
+
+    def validate(self):
+        d = self.device
+        shp = (self.num_blocks, self.n_kv, self.kv_bs)
+        for name in ("k_pages", "v_pages"):
+            t = getattr(self, name)
+            _need(t, name, torch.uint8, d, 4)
+            if tuple(t.shape) != shp + (self.hd // 2,):
+                raise ValueError(f"{name} shape {tuple(t.shape)} != {shp + (self.hd // 2,)}")
+        for name in ("k_scale", "v_scale"):
+            t = getattr(self, name)
+            _need(t, name, torch.float16, d, 4)
+            if tuple(t.shape) != shp + (self.hd // 32,):
+                raise ValueError(f"{name} shape {tuple(t.shape)} != {shp + (self.hd // 32,)}")
+
+    def append(self, k_src, v_src, slot_mapping):
+        """Quantise k_src/v_src [n_tokens][n_kv][hd] (fp32 or bf16) into slots."""
+        dev, kp, vp, ks, vs = self._pointers()
+        sd = k_src.dtype if isinstance(k_src, torch.Tensor) else None
+        if not (sd in (torch.float32, torch.bfloat16) and _ok(k_src, sd, dev, 3) and _ok(v_src, sd, dev, 3)
+                and _ok(slot_mapping, torch.int32, dev, 1)):
+            d = self.device
+            if sd not in (torch.float32, torch.bfloat16):
+                raise TypeError("k_src must be a float32 or bfloat16 tensor")
+            _need(k_src, "k_src", sd, d, 3)
+            _need(v_src, "v_src", sd, d, 3)
+            _need(slot_mapping, "slot_mapping", torch.int32, d, 1)
+        n = slot_mapping.shape[0]
+        if tuple(k_src.shape) != (n, self.n_kv, self.hd) or v_src.shape != k_src.shape:
+            raise ValueError("k_src/v_src must be [n_tokens][n_kv][hd] matching slot_mapping")
+        args = (kp, vp, ks, vs, k_src.data_ptr(), v_src.data_ptr(), 1 if sd is torch.bfloat16 else 0,
+                slot_mapping.data_ptr(), n, self.num_blocks, self.n_kv, self.hd, self.kv_bs)
+        with torch.cuda.device(dev):
+            _check(lib.q8kv_q40_append(*args, torch.cuda.current_stream(dev).cuda_stream))
+
+
+def q40_decode_attn(q, cache, block_table, seq_lens, scale, out=None, part_tokens=0):
+    """decode_attn over a Q40KVCache.  Returns out (fp32 [batch][n_q][hd])."""
+    if not isinstance(cache, Q40KVCache):
+        raise TypeError("cache must be a Q40KVCache")
+    dev, kp, vp, ks, vs = cache._pointers()
+    if not (_ok(q, torch.float32, dev, 3) and _ok(block_table, torch.int32, dev, 2)
+            and _ok(seq_lens, torch.int32, dev, 1)):
+        d = cache.device
+        _need(q, "q", torch.float32, d, 3)
+        _need(block_table, "block_table", torch.int32, d, 2)
+        _need(seq_lens, "seq_lens", torch.int32, d, 1)
+    batch, n_q, hd = q.shape
+    if hd != cache.hd or block_table.shape[0] != batch or seq_lens.shape[0] != batch:
+        raise ValueError("q / block_table / seq_lens / cache shapes disagree")
+    if out is None:
+        out = torch.empty_like(q)
+    elif not (_ok(out, torch.float32, dev, 3) and out.shape == q.shape):
+        _need(out, "out", torch.float32, cache.device, 3)
+        raise ValueError("out must have q's shape")
+    args = (out.data_ptr(), q.data_ptr(), kp, vp, ks, vs, block_table.data_ptr(), seq_lens.data_ptr(),
+            block_table.shape[1], cache.num_blocks, batch, n_q, cache.n_kv, hd, cache.kv_bs, float(scale),
+            int(part_tokens))
+    if torch.cuda.current_device() == dev:
+        _check(lib.q8kv_q40_decode_attn(*args, torch.cuda.current_stream(dev).cuda_stream))
+    else:
+        with torch.cuda.device(dev):
+            _check(lib.q8kv_q40_decode_attn(*args, torch.cuda.current_stream(dev).cuda_stream))
+    return out
 
 
 def fp8_decode_attn(q, cache, block_table, seq_lens, scale, out=None, part_tokens=0):

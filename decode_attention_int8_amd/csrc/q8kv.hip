@@ -128,7 +128,8 @@ __device__ __forceinline__ void load_q_rows(QRows<HD, NT>& Q, const float* __res
 }
 
 template <int HD, int NT>
-__device__ __forceinline__ void quantize_q_regs(const QRows<HD, NT>& Q, int8_t* lq, float* lqsc, int tid) {
+__device__ __forceinline__ void quantize_q_regs(const QRows<HD, NT>& Q, int8_t* lq, float* lqsc, int tid,
+                                                int* lqsum = nullptr) {
 #pragma unroll
     for (int i = 0; i < QRows<HD, NT>::kPer; ++i) {
         const int c = tid + i * NT;
@@ -142,8 +143,18 @@ __device__ __forceinline__ void quantize_q_regs(const QRows<HD, NT>& Q, int8_t* 
         a = fmaxf(a, __shfl_xor(a, 4));
         a = q8_guard(a);
         const float inv = 127.0f / a;
-        *reinterpret_cast<uint32_t*>(lq + g * HD + e) = q8_pack4(x, inv);
+        const uint32_t packed = q8_pack4(x, inv);
+        *reinterpret_cast<uint32_t*>(lq + g * HD + e) = packed;
         if ((c & 7) == 0) lqsc[g * (HD / kQBlock) + e / kQBlock] = a * kInv127;
+        if (lqsum) {
+            // the block's code sum (the q4_0 codec's -8 offset correction)
+            int sum = (int)(int8_t)packed + (int)(int8_t)(packed >> 8) + (int)(int8_t)(packed >> 16) +
+                      (int)(int8_t)(packed >> 24);
+            sum += __shfl_xor(sum, 1);
+            sum += __shfl_xor(sum, 2);
+            sum += __shfl_xor(sum, 4);
+            if ((c & 7) == 0) lqsum[g * (HD / kQBlock) + e / kQBlock] = sum;
+        }
     }
 }
 
@@ -1003,6 +1014,199 @@ __device__ __forceinline__ void fp8_tile_compute(const Fp8Tile<HD>& T, const _Fl
     }
 }
 
+// ----------------------------------------------------------------------------
+// q4_0 KV codec (llama.cpp's block format; the page "FlashAttention" tag,
+// baguaai.com, names the q4_0 KV cache type): every 32 consecutive elements
+// of a row share one fp16 scale d, elements are 4-bit codes c with value
+// (c - 8) * d.  A 16-row sub-tile is 16 * HD / 2 bytes; lane slot l = 16 r + n
+// owns HD / 8 bytes at 8 l ... of it:
+//   K: bytes [8 c, 8 c + 8) of the slot hold row n, columns 64 c + 16 r + i
+//      (low nibble) and 64 c + 16 r + 8 + i (high nibble) in byte i;
+//   V: the slot holds rows 4r .. 4r+3 of the columns 16 s + n (s = 0 ..
+//      HD/16 - 1); byte 4 (s / 2) + j holds row 4r + j of column 16 s + n
+//      for the even s in its low nibble and of the odd s in its high one.
+// Scales: fp16 [num_blocks][n_kv][kv_bs][HD/32].
+// Q.K reuses the int8 path: the unsigned codes feed v_mfma_i32_16x16x64_i8
+// directly and the -8 offset comes off as 8 * (the query block's code sum);
+// the block's d multiplies its dot.  P.V is the FP8 codec's bf16 path with
+// per-32-column-block weights w * d.
+
+constexpr int kQ4Block = 32;
+
+template <int HD>
+struct Q4Geo {
+    static constexpr int SLOT = HD / 8;          // bytes per lane slot of a sub-tile
+    static constexpr int SW = SLOT / 4;          // dwords per lane slot
+    static constexpr int NB = HD / kQ4Block;     // 32-blocks (scales) per row
+    static constexpr int SCW = 4 * NB / 2;       // dwords of fp16 scales for 4 rows
+};
+
+template <int N>
+__device__ __forceinline__ void load_dwords(uint32_t (&d)[N], const void* p) {
+    static_assert(N == 2 || N % 4 == 0, "load size");
+    if constexpr (N == 2) {
+        const u32x2 x = stream_load<u32x2>(p);
+        d[0] = x[0];
+        d[1] = x[1];
+    } else {
+#pragma unroll
+        for (int i = 0; i < N; i += 4) {
+            const u32x4 x = stream_load<u32x4>(static_cast<const uint8_t*>(p) + 4 * i);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) d[i + k] = x[k];
+        }
+    }
+}
+
+template <int HD>
+struct Q4Tile {
+    uint32_t k[2][Q4Geo<HD>::SW];
+    uint32_t v[2][Q4Geo<HD>::SW];
+    uint32_t kd[2][Q4Geo<HD>::SCW];  // fp16 scales of rows 4r .. 4r+3, row-major
+    uint32_t vd[2][Q4Geo<HD>::SCW];
+    int nval[2];
+    __device__ __forceinline__ float kscale(int st, int j, int blk) const {
+        const int i = j * Q4Geo<HD>::NB + blk;
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)(kd[st][i >> 1] >> (16 * (i & 1))));
+    }
+    __device__ __forceinline__ float vscale(int st, int j, int blk) const {
+        const int i = j * Q4Geo<HD>::NB + blk;
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)(vd[st][i >> 1] >> (16 * (i & 1))));
+    }
+};
+
+template <int HD>
+__device__ __forceinline__ void q4_tile_load(Q4Tile<HD>& T, const DecodeArgs& a, const int (&tblk)[2], int kh,
+                                             int ts, int t1, int lane, bool& bad) {
+    using QG = Q4Geo<HD>;
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+        T.nval[st] = min(max(t1 - (ts + kSub * st), 0), kSub);
+        const int tst = T.nval[st] > 0 ? ts + kSub * st : ts;
+        int blk = (st == 1 && T.nval[1] > 0) ? tblk[1] : tblk[0];
+        if ((unsigned)blk >= (unsigned)a.num_blocks) {
+            bad = true;
+            blk = 0;
+        }
+        const size_t base = ((size_t)blk * a.n_kv + kh) * a.kv_bs + (size_t)(tst % a.kv_bs);
+        const size_t srow = (base + 4 * (lane >> 4)) * QG::NB * 2;  // byte offset of row 4r's scales
+        load_dwords<QG::SCW>(T.kd[st], a.ks8 + srow);
+        load_dwords<QG::SCW>(T.vd[st], a.vs8 + srow);
+        load_dwords<QG::SW>(T.k[st], a.kp + base * (HD / 2) + (size_t)lane * QG::SLOT);
+        load_dwords<QG::SW>(T.v[st], a.vp + base * (HD / 2) + (size_t)lane * QG::SLOT);
+    }
+}
+
+// Two fp32 values -> packed bf16x2 (each rounded to nearest even).
+__device__ __forceinline__ uint32_t pack_bf16x2(float x, float y) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)y) << 16);
+}
+
+template <int HD>
+__device__ __forceinline__ void q4_tile_compute(const Q4Tile<HD>& T, const int8_t* lq, const float* lqsc,
+                                                const int* lqsum, float score_scale, f32x4 (&acc)[Geo<HD>::BPL],
+                                                float& M, float& S, int lane) {
+    using GG = Geo<HD>;
+    using QG = Q4Geo<HD>;
+    const int r = lane >> 4, n = lane & 15, bp = n >> 3, g = n & 7;
+    QOperand<HD> Q;
+    load_q_operand<HD>(Q, lq, lqsc, lane, score_scale);
+    int qs8[GG::NPAIR];
+#pragma unroll
+    for (int p = 0; p < GG::NPAIR; ++p) qs8[p] = 8 * lqsum[g * GG::NB + 2 * p + bp];
+    float sc[2][4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+        i32x4 c[GG::NPAIR];
+#pragma unroll
+        for (int p = 0; p < GG::NPAIR; ++p) {
+            const uint32_t x0 = T.k[st][2 * p], x1 = T.k[st][2 * p + 1];
+            const i32x4 kop = {(int)(x0 & 0x0f0f0f0fu), (int)(x1 & 0x0f0f0f0fu), (int)((x0 >> 4) & 0x0f0f0f0fu),
+                               (int)((x1 >> 4) & 0x0f0f0f0fu)};
+            c[p] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop, Q.op[p], i32x4{0, 0, 0, 0}, 0, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float part = 0.0f;
+#pragma unroll
+            for (int p = 0; p < GG::NPAIR; ++p)
+                part += (float)(c[p][j] - qs8[p]) * Q.scl[p] * T.kscale(st, j, 2 * p + bp);
+            const float full = part + dpp_row_ror8(part);  // add the other block parity
+            sc[st][j] = (4 * r + j) < T.nval[st] ? full : -INFINITY;
+            mx = fmaxf(mx, sc[st][j]);
+        }
+    }
+    mx = swap16_max(mx);
+    mx = swap32_max(mx);
+    const float m_new = fmaxf(M, mx);
+    const float alpha = __builtin_amdgcn_exp2f(M - m_new);
+    M = m_new;
+    const float m_shift = m_new - kWeightShift;
+
+    // rows past the range may hold any scale bytes: their weights are
+    // selected to zero after the scale multiply (their codes are finite)
+    float W[8];
+    bool ok[8];
+    float wsum = 0.0f;
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float w = __builtin_amdgcn_exp2f(sc[st][j] - m_shift);
+            wsum += w;
+            ok[4 * st + j] = (4 * r + j) < T.nval[st];
+            W[4 * st + j] = w;
+        }
+    }
+    S = S * alpha + wsum;
+
+    if (__any(alpha != 1.0f)) {
+        float arow[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) arow[j] = lane_read(alpha, 4 * (r & 1) + j);
+#pragma unroll
+        for (int s = 0; s < GG::BPL; ++s) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[s][j] *= arow[j];
+        }
+    }
+
+    // P.V, one 32-column block (two 16-column matrices) at a time; codes
+    // c -> c - 8 as the signed 4-bit value of c ^ 8, exact in bf16
+    uint32_t vx[2][QG::SW];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+#pragma unroll
+        for (int i = 0; i < QG::SW; ++i) vx[st][i] = T.v[st][i] ^ 0x88888888u;
+    }
+#pragma unroll
+    for (int b = 0; b < QG::NB; ++b) {
+        bf16x8 aw;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const float x = ok[k] ? W[k] * T.vscale(k >> 2, k & 3, b) : 0.0f;
+            const __bf16 hi = (__bf16)x;
+            aw[k] = n < 8 ? hi : (__bf16)(x - (float)hi);
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int s = 2 * b + h;
+            u32x4 bv;
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+                const uint32_t d = vx[st][s >> 1];
+                float f[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) f[j] = (float)(int)__builtin_amdgcn_sbfe(d, 8 * j + 4 * h, 4);
+                bv[2 * st] = pack_bf16x2(f[0], f[1]);
+                bv[2 * st + 1] = pack_bf16x2(f[2], f[3]);
+            }
+            acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw, __builtin_bit_cast(bf16x8, bv), acc[s], 0, 0, 0);
+        }
+    }
+}
+
 // Grid modes.  kPersistent: fewer workgroups than items; items are numbered
 // through an exclusive prefix sum of n_kv * ceil(L / pt) per sequence built in
 // LDS from seq_lens, and each workgroup takes its next item from an atomic
@@ -1013,7 +1217,7 @@ __device__ __forceinline__ void fp8_tile_compute(const Fp8Tile<HD>& T, const _Fl
 // others' compute).  3 waves per SIMD fit hd 64 and 128 without spills; hd
 // 256 keeps a whole register file.
 enum GridMode { kPersistent = 0, kStatic = 1 };
-enum CodecKind { kQ8 = 0, kFp8 = 1 };
+enum CodecKind { kQ8 = 0, kFp8 = 1, kQ40 = 2 };
 
 template <int HD, int MODE, bool NEW, int CODEC = kQ8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(HD == 256 ? 1 : 3))) void
@@ -1021,10 +1225,12 @@ q8kv_decode_kernel(const DecodeArgs a) {
     using GG = Geo<HD>;
     constexpr bool STATIC = MODE == kStatic;
     constexpr bool FP8 = CODEC == kFp8;
-    static_assert(!(NEW && FP8), "the fused append is an int8-codec path");
-    using TileT = std::conditional_t<FP8, Fp8Tile<HD>, Tile<HD>>;
+    constexpr bool Q40 = CODEC == kQ40;
+    static_assert(!(NEW && CODEC != kQ8), "the fused append is an int8-codec path");
+    using TileT = std::conditional_t<FP8, Fp8Tile<HD>, std::conditional_t<Q40, Q4Tile<HD>, Tile<HD>>>;
     __shared__ __attribute__((aligned(16))) int8_t lq[FP8 ? 16 : kHeadGroup * HD];
     __shared__ float lqsc[FP8 ? 1 : kHeadGroup * GG::NB];
+    __shared__ int lqsum[Q40 ? kHeadGroup * GG::NB : 1];  // q4_0: query block code sums
     __shared__ __attribute__((aligned(16))) _Float16 lq16[FP8 ? 2 * kHeadGroup * HD : 8];  // FP8: query hi, lo rows
     __shared__ float lM[kWaves][kHeadGroup];
     __shared__ float lS[kWaves][kHeadGroup];
@@ -1244,6 +1450,7 @@ q8kv_decode_kernel(const DecodeArgs a) {
             const bool own = ts < t1;
             const int blk0[2] = {own ? blk_first[0] : blk_t0[0], own ? blk_first[1] : blk_t0[1]};
             if constexpr (FP8) fp8_tile_load<HD>(A, a, blk0, kh, own ? ts : t0, t1, ilane, bad);
+            else if constexpr (Q40) q4_tile_load<HD>(A, a, blk0, kh, own ? ts : t0, t1, ilane, bad);
             else tile_load<HD>(A, a, blk0, kh, own ? ts : t0, t1, ilane, bad);
         }
         if constexpr (NEW && STATIC) {
@@ -1252,6 +1459,7 @@ q8kv_decode_kernel(const DecodeArgs a) {
         }
 
         if constexpr (FP8) split_q_regs<HD, kThreads>(qrows, lq16, itid);
+        else if constexpr (Q40) quantize_q_regs<HD, kThreads>(qrows, lq, lqsc, itid, lqsum);
         else quantize_q_regs<HD, kThreads>(qrows, lq, lqsc, itid);
         __syncthreads();
         // static grids: the tail wave quantises the new rows (which arrive
@@ -1273,12 +1481,14 @@ q8kv_decode_kernel(const DecodeArgs a) {
                 if (ts == tail_ts) tile_patch<HD>(A, lnew, lnew + HD, lnew_sc[0], lnew_sc[1], L - 1 - ts, ilane);
             }
             if constexpr (FP8) fp8_tile_compute<HD>(A, lq16, a.scale_log2, acc, M, S, ilane);
+            else if constexpr (Q40) q4_tile_compute<HD>(A, lq, lqsc, lqsum, a.scale_log2, acc, M, S, ilane);
             else tile_compute<HD>(A, lq, lqsc, a.scale_log2, acc, M, S, ilane);
             ts += kStride;
             if (ts < t1) {
                 int blk[2];
                 tile_blocks(trow, ts, a.kv_bs, a.max_blocks, blk);
                 if constexpr (FP8) fp8_tile_load<HD>(A, a, blk, kh, ts, t1, ilane, bad);
+                else if constexpr (Q40) q4_tile_load<HD>(A, a, blk, kh, ts, t1, ilane, bad);
                 else tile_load<HD>(A, a, blk, kh, ts, t1, ilane, bad);
                 if constexpr (NEW && STATIC) {
                     if (tail_ts != INT_MIN && ts == ts_second)
@@ -1308,7 +1518,7 @@ q8kv_decode_kernel(const DecodeArgs a) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
 #pragma unroll
-                for (int s = 0; s < GG::BPL; ++s) lacc[wid][4 * r + j][FP8 ? 16 * s + n : GG::BPL * n + s] = acc[s][j];
+                for (int s = 0; s < GG::BPL; ++s) lacc[wid][4 * r + j][CODEC != kQ8 ? 16 * s + n : GG::BPL * n + s] = acc[s][j];
             }
         }
         const bool any_bad = __syncthreads_or(bad);
@@ -1855,6 +2065,109 @@ __global__ __launch_bounds__(kThreads) void q8kv_quest_topk_kernel(const QuestAr
     if (tid == 0) srow[k] = trow[nblk - 1];
 }
 
+// q4_0 append: one wave per (token, kv head) row, EPL = HD / 64 elements per
+// lane, a 32-element block on 32 / EPL lanes.  Per block: m = the element of
+// largest magnitude (sign kept, the lowest column on ties), d = m / -8,
+// id = 1 / d (0 for d = 0), codes min(15, trunc(x * id + 8.5)) with two fp32
+// roundings, scale fp16(d).  A byte holds two nibbles of one row, so the lane
+// holding the low nibble's columns fetches the high nibble's codes from its
+// partner lane and writes whole bytes.
+template <int HD, bool V>
+__device__ __forceinline__ void q4_row_store(uint8_t* pages, uint16_t* scales, size_t dst_row, int row_in_page,
+                                             const NewRow<HD>& x, int lane) {
+    constexpr int EPL = NewRow<HD>::EPL, LPB = kQ4Block / EPL, NB = HD / kQ4Block;
+    float am = -1.0f, mv = 0.0f;
+    int mc = 0;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+        if (fabsf(x.x[e]) > am) {
+            am = fabsf(x.x[e]);
+            mv = x.x[e];
+            mc = lane * EPL + e;
+        }
+    }
+#pragma unroll
+    for (int off = 1; off < LPB; off <<= 1) {
+        const float pa = __shfl_xor(am, off), pv = __shfl_xor(mv, off);
+        const int pc = __shfl_xor(mc, off);
+        if (pa > am || (pa == am && pc < mc)) {
+            am = pa;
+            mv = pv;
+            mc = pc;
+        }
+    }
+    const float d = mv / -8.0f;
+    const float id = d != 0.0f ? 1.0f / d : 0.0f;
+    uint32_t codes = 0;  // EPL nibbles, column order
+    {
+        // x * id and + 8.5 round separately: no fused multiply-add here
+#pragma clang fp contract(off)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+            const float y = x.x[e] * id;
+            const int c = min(15, (int)(y + 8.5f));
+            codes |= (uint32_t)c << (4 * e);
+        }
+    }
+    const int row = row_in_page % kSub, col = lane * EPL;
+    uint8_t* sub = pages + (dst_row - row) * (HD / 2);
+    if constexpr (!V) {
+        // byte i of chunk ch: columns 64 ch + 16 rr + i (low) and + 8 (high)
+        const uint32_t partner = (uint32_t)__shfl(codes, lane + 8 / EPL);
+        const int ch = col / 64, cc = col % 64, rr = cc / 16, i = cc % 16;
+        if (i < 8) {
+            uint8_t* dst = sub + (16 * rr + row) * (HD / 8) + 8 * ch + i;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) dst[e] = (uint8_t)(((codes >> (4 * e)) & 15) | (((partner >> (4 * e)) & 15) << 4));
+        }
+    } else {
+        // byte 4 (s / 2) + j of slot 16 (row / 4) + nn: column 16 s + nn of
+        // row 4 (row / 4) + j, even s low, odd s high
+        const uint32_t partner = (uint32_t)__shfl(codes, lane + 16 / EPL);
+        const int sblk = col / 16;
+        if ((sblk & 1) == 0) {
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+                const int nn = (col + e) % 16;
+                uint8_t* dst = sub + (16 * (row >> 2) + nn) * (HD / 8) + 4 * (sblk >> 1) + (row & 3);
+                *dst = (uint8_t)(((codes >> (4 * e)) & 15) | (((partner >> (4 * e)) & 15) << 4));
+            }
+        }
+    }
+    if (lane % LPB == 0)
+        scales[dst_row * NB + lane / LPB] = __builtin_bit_cast(uint16_t, (_Float16)d);
+}
+
+struct Q4AppendArgs {
+    uint8_t* kp;
+    uint8_t* vp;
+    uint16_t* ks;
+    uint16_t* vs;
+    const void* ksrc;
+    const void* vsrc;
+    const int32_t* slots;
+    int n_tokens, n_kv, kv_bs, src_bf16;
+    long long n_slots;
+};
+
+template <int HD>
+__global__ __launch_bounds__(256) void q8kv_q40_append_kernel(const Q4AppendArgs a) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const long long row_id = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row_id >= (long long)a.n_tokens * a.n_kv) return;
+    const int t = (int)(row_id / a.n_kv), kh = (int)(row_id % a.n_kv);
+    const int slot = a.slots[t];
+    if (slot < 0 || (long long)slot >= a.n_slots) return;
+    const int blk = slot / a.kv_bs, rr = slot % a.kv_bs;
+    const size_t dst_row = ((size_t)blk * a.n_kv + kh) * a.kv_bs + rr;
+    const size_t src_row = (size_t)t * a.n_kv + kh;
+    NewRow<HD> k, v;
+    row_load<HD>(k, a.ksrc, src_row, a.src_bf16, lane);
+    row_load<HD>(v, a.vsrc, src_row, a.src_bf16, lane);
+    q4_row_store<HD, false>(a.kp, a.ks, dst_row, rr, k, lane);
+    q4_row_store<HD, true>(a.vp, a.vs, dst_row, rr, v, lane);
+}
+
 struct Fp8AppendArgs {
     uint8_t* kp;
     uint8_t* vp;
@@ -2059,11 +2372,11 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 // Decode kernel variants: the int8 codec, the int8 codec with the fused
 // append of the new token, the FP8 codec.
-enum Variant { kVarQ8 = 0, kVarQ8New = 1, kVarFp8 = 2 };
+enum Variant { kVarQ8 = 0, kVarQ8New = 1, kVarFp8 = 2, kVarQ40 = 3 };
 
 template <int HD, int VAR, int MODE>
 constexpr auto decode_kernel_ptr() {
-    return q8kv_decode_kernel<HD, MODE, VAR == kVarQ8New, VAR == kVarFp8 ? kFp8 : kQ8>;
+    return q8kv_decode_kernel<HD, MODE, VAR == kVarQ8New, VAR == kVarFp8 ? kFp8 : VAR == kVarQ40 ? kQ40 : kQ8>;
 }
 
 template <int HD, int VAR>
@@ -2104,6 +2417,7 @@ int launch_info(int dev, int hd, int var, LaunchInfo* out) {
     LaunchInfo li;
     const int rc = var == kVarQ8New ? launch_info_var<kVarQ8New>(dev, hd, li)
                    : var == kVarFp8 ? launch_info_var<kVarFp8>(dev, hd, li)
+                   : var == kVarQ40 ? launch_info_var<kVarQ40>(dev, hd, li)
                                     : launch_info_var<kVarQ8>(dev, hd, li);
     if (rc) return rc;
     g_launch[key] = li;
@@ -2127,6 +2441,7 @@ void launch_decode_var(int hd, int mode, unsigned grid, size_t lds, hipStream_t 
 void launch_decode(int hd, int var, int mode, unsigned grid, size_t lds, hipStream_t st, const DecodeArgs& da) {
     if (var == kVarQ8New) launch_decode_var<kVarQ8New>(hd, mode, grid, lds, st, da);
     else if (var == kVarFp8) launch_decode_var<kVarFp8>(hd, mode, grid, lds, st, da);
+    else if (var == kVarQ40) launch_decode_var<kVarQ40>(hd, mode, grid, lds, st, da);
     else launch_decode_var<kVarQ8>(hd, mode, grid, lds, st, da);
 }
 
@@ -2135,7 +2450,7 @@ int decode_impl(float* out, const float* q, const int8_t* kp, const int8_t* vp, 
                 int num_blocks, int batch, int n_q, int n_kv, int hd, int kv_bs, float scale,
                 int part_tokens, void* stream, const void* knew = nullptr, const void* vnew = nullptr,
                 int new_dtype = 0, const uint8_t* ks8 = nullptr, const uint8_t* vs8 = nullptr,
-                bool head_tables = false) {
+                bool head_tables = false, bool q40 = false) {
     const bool fp8 = ks8 != nullptr || vs8 != nullptr;
     if (!out || !q || !kp || !vp || !table || !lens || (fp8 ? (!ks8 || !vs8) : (!ks || !vs)))
         return fail(Q8KV_ENULL, "a tensor pointer is NULL");
@@ -2171,7 +2486,7 @@ int decode_impl(float* out, const float* q, const int8_t* kp, const int8_t* vp, 
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
     LaunchInfo li;
-    const int var = fp8 ? kVarFp8 : knew ? kVarQ8New : kVarQ8;
+    const int var = q40 ? kVarQ40 : fp8 ? kVarFp8 : knew ? kVarQ8New : kVarQ8;
     rc = launch_info(dev, hd, var, &li);
     if (rc) return rc;
     const unsigned grid = (unsigned)std::min<long long>(items, li.resident);
@@ -2385,6 +2700,47 @@ int q8kv_fp8_decode_attn(float* out, const float* q, const uint8_t* k_pages, con
     return decode_impl(out, q, reinterpret_cast<const int8_t*>(k_pages), reinterpret_cast<const int8_t*>(v_pages),
                        nullptr, nullptr, block_table, seq_lens, max_blocks_per_seq, num_blocks, batch, n_q_heads,
                        n_kv_heads, hd, kv_bs, scale, part_tokens, stream, nullptr, nullptr, 0, k_scale, v_scale);
+}
+
+int q8kv_q40_append(uint8_t* k_pages, uint8_t* v_pages, uint16_t* k_scale, uint16_t* v_scale, const void* k_src,
+                    const void* v_src, int src_dtype, const int32_t* slot_mapping, int n_tokens,
+                    int num_blocks, int n_kv_heads, int hd, int kv_bs, void* stream) {
+    g_err.clear();
+    if (!k_pages || !v_pages || !k_scale || !v_scale || !k_src || !v_src || !slot_mapping)
+        return fail(Q8KV_ENULL, "a tensor pointer is NULL");
+    if (n_tokens < 0) return fail(Q8KV_EINVAL, "n_tokens must be >= 0 (got %d)", n_tokens);
+    int rc = check_cache_shape(num_blocks, n_kv_heads, hd, kv_bs);
+    if (rc) return rc;
+    if (src_dtype != 0 && src_dtype != 1) return fail(Q8KV_EINVAL, "src_dtype must be 0 (fp32) or 1 (bf16)");
+    if (n_tokens == 0) return Q8KV_OK;
+    const long long rows = (long long)n_tokens * n_kv_heads;
+    const long long grid = (rows + 3) / 4;
+    if (grid > INT_MAX) return fail(Q8KV_EINVAL, "too many rows (%lld)", rows);
+    Q4AppendArgs aa{k_pages, v_pages, k_scale, v_scale, k_src, v_src, slot_mapping, n_tokens,
+                    n_kv_heads, kv_bs, src_dtype, (long long)num_blocks * kv_bs};
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    switch (hd) {
+        case 64: hipLaunchKernelGGL(q8kv_q40_append_kernel<64>, dim3((unsigned)grid), dim3(256), 0, st, aa); break;
+        case 128: hipLaunchKernelGGL(q8kv_q40_append_kernel<128>, dim3((unsigned)grid), dim3(256), 0, st, aa); break;
+        default: hipLaunchKernelGGL(q8kv_q40_append_kernel<256>, dim3((unsigned)grid), dim3(256), 0, st, aa); break;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "q4_0 append kernel launch");
+    return Q8KV_OK;
+}
+
+int q8kv_q40_decode_attn(float* out, const float* q, const uint8_t* k_pages, const uint8_t* v_pages,
+                         const uint16_t* k_scale, const uint16_t* v_scale, const int32_t* block_table,
+                         const int32_t* seq_lens, int max_blocks_per_seq, int num_blocks, int batch,
+                         int n_q_heads, int n_kv_heads, int hd, int kv_bs, float scale, int part_tokens,
+                         void* stream) {
+    g_err.clear();
+    if (!k_scale || !v_scale) return fail(Q8KV_ENULL, "a tensor pointer is NULL");
+    return decode_impl(out, q, reinterpret_cast<const int8_t*>(k_pages), reinterpret_cast<const int8_t*>(v_pages),
+                       nullptr, nullptr, block_table, seq_lens, max_blocks_per_seq, num_blocks, batch, n_q_heads,
+                       n_kv_heads, hd, kv_bs, scale, part_tokens, stream, nullptr, nullptr, 0,
+                       reinterpret_cast<const uint8_t*>(k_scale), reinterpret_cast<const uint8_t*>(v_scale),
+                       false, true);
 }
 
 int q8kv_decode_attn_heads(float* out, const float* q, const int8_t* k_pages, const int8_t* v_pages,

@@ -216,6 +216,47 @@ int q8kv_fp8_decode_attn(float* out, const float* q, const uint8_t* k_pages,
                          float scale, int part_tokens, void* stream);
 
 /*
+ * q4_0 KV codec.  The pages name it only (page "FlashAttention" tag
+ * (baguaai.com), news item on llama.cpp's SYCL decode path for q4_0 / q8_0
+ * KV caches); this is llama.cpp's block format: every 32 consecutive
+ * elements of a K or V row share one fp16 scale d and are stored as 4-bit
+ * codes c, element value (c - 8) * d.  Quantisation of a block: m = its
+ * element of largest magnitude (sign kept, the first on ties), d = m / -8
+ * in fp32, id = 1 / d (0 when d = 0), c = min(15, trunc(x * id + 8.5)) with
+ * two fp32 roundings (no fused multiply-add), stored d = fp16(d).
+ *
+ * Layouts (caller-owned device memory):
+ *   k_pages,
+ *   v_pages   uint8 [num_blocks][n_kv_heads][kv_bs / 16][8 * hd]: 16-row
+ *             sub-tiles of 8 hd bytes; lane slot l = 16 r + n (r in 0..3, n in
+ *             0..15) owns hd / 8 bytes at byte (hd / 8) * l:
+ *             K: byte 8 c + i of the slot holds row n, column 64 c + 16 r + i
+ *                in its low nibble and column 64 c + 16 r + 8 + i in its high
+ *                nibble (c < hd / 64, i < 8);
+ *             V: byte 4 (s / 2) + j holds row 4 r + j of column 16 s + n, the
+ *                even s in the low nibble and the odd s in the high one
+ *                (s < hd / 16, j < 4);
+ *   k_scale,
+ *   v_scale   fp16 bits, uint16 [num_blocks][n_kv_heads][kv_bs][hd / 32].
+ * Decode: the query is quantised per 32-block to int8 as for the int8 cache
+ * (codes qi, scales qsc); a token's score is scale * sum over blocks b of
+ * qsc[b] * d_K[b] * sum_{i in b} qi[i] * (c_K[i] - 8), and the output is the
+ * softmax-weighted sum of the dequantised V rows, one pass as in
+ * q8kv_decode_attn_split.  Other arguments, errors and behaviour as for
+ * q8kv_append and q8kv_decode_attn_split.
+ */
+int q8kv_q40_append(uint8_t* k_pages, uint8_t* v_pages, uint16_t* k_scale, uint16_t* v_scale,
+                    const void* k_src, const void* v_src, int src_dtype,
+                    const int32_t* slot_mapping, int n_tokens, int num_blocks,
+                    int n_kv_heads, int hd, int kv_bs, void* stream);
+int q8kv_q40_decode_attn(float* out, const float* q, const uint8_t* k_pages,
+                         const uint8_t* v_pages, const uint16_t* k_scale,
+                         const uint16_t* v_scale, const int32_t* block_table,
+                         const int32_t* seq_lens, int max_blocks_per_seq, int num_blocks,
+                         int batch, int n_q_heads, int n_kv_heads, int hd, int kv_bs,
+                         float scale, int part_tokens, void* stream);
+
+/*
  * QUEST block metadata (page "CANN ops-transformer Quest Prefill Metadata"
  * (xdnf.cn), section on the experiment background: for every KV block, the
  * per-channel maximum and minimum over the block's tokens of the K cache).

@@ -88,6 +88,33 @@ def natural_fp8_pages(pages, which):
     return sub[..., off.reshape(-1)].reshape(nb, n_kv, kv_bs, hd)
 
 
+def q40_codes(pages, which):
+    """q4_0 device pages [nb][n_kv][kv_bs][hd/2] (sub-tile nibble order) ->
+    codes [nb][n_kv][kv_bs][hd] in row order, as include/q8kv.h defines the
+    order: slot 16r+n owns hd/8 bytes; K byte 8c+i = row n, columns
+    64c+16r+i (low nibble) and 64c+16r+8+i (high); V byte 4(s/2)+j = row
+    4r+j, column 16s+n, even s low nibble, odd s high."""
+    nb, n_kv, kv_bs, half = pages.shape
+    hd = 2 * half
+    sub = pages.reshape(nb, n_kv, kv_bs // 16, 16 * half)
+    out = np.empty((nb, n_kv, kv_bs // 16, 16, hd), np.uint8)
+    for row in range(16):
+        for col in range(hd):
+            if which == "k":
+                r, n = (col % 64) // 16, row
+                i = col % 16
+                byte = (16 * r + n) * (hd // 8) + 8 * (col // 64) + (i % 8)
+                hi = i >= 8
+            else:
+                r, n = row // 4, col % 16
+                s_ = col // 16
+                byte = (16 * r + n) * (hd // 8) + 4 * (s_ // 2) + row % 4
+                hi = (s_ % 2) == 1
+            b = sub[..., byte]
+            out[:, :, :, row, col] = (b >> 4) if hi else (b & 15)
+    return out.reshape(nb, n_kv, kv_bs, hd)
+
+
 def natural_pages(pages, which):
     """Device pages [nb][n_kv][kv_bs][hd] in chunk order -> row-major rows."""
     nb, n_kv, kv_bs, hd = pages.shape

@@ -14,7 +14,7 @@ NUL = ctypes.c_void_p(0)
 
 def test_exports_every_declared_symbol():
     names = q8.header_symbols()
-    assert len(names) == 15
+    assert len(names) == 17
     for n in names:
         assert hasattr(L, n), n
 
