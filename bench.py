@@ -20,9 +20,10 @@ oracle timed on a bounded sample of the same workload, and sampled parity
 against that oracle and its fp64 twin.  A last leg times the fused step
 that also stores each sequence's new token (q8kv_append_decode_attn) against
 the same work as two launches (q8kv_append, then q8kv_decode_attn), and
-another the same step over the FP8 codec (q8kv_fp8_decode_attn), with a
-sampled parity check against its oracle, and a QUEST leg (block metadata,
-top-k block selection, decode over the kept blocks).
+others the same step over the FP8 codec (q8kv_fp8_decode_attn) and the
+q4_0 codec (q8kv_q40_decode_attn), each with a sampled parity check against
+its oracle, and a QUEST leg (block metadata, top-k block selection, decode
+over the kept blocks).
 """
 import argparse
 import json
@@ -60,6 +61,7 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline and parity sample")
     p.add_argument("--no-fused", action="store_true", help="skip the fused append + decode leg")
     p.add_argument("--no-fp8", action="store_true", help="skip the FP8-codec leg")
+    p.add_argument("--no-q40", action="store_true", help="skip the q4_0-codec leg")
     p.add_argument("--no-quest", action="store_true", help="skip the QUEST metadata / selection leg")
     p.add_argument("--part-tokens", type=int, default=0, help="override the split plan (0: automatic)")
     p.add_argument("--copy-mb", type=float, default=0.0,
@@ -68,18 +70,39 @@ def parse():
     return p.parse_args()
 
 
-def build_gpu(w, dev, copies_bytes, fp8=False):
+CODECS = ("fp8", "q40")
+
+
+def codec_api(name):
+    """(cache class, decode call, algorithmic KV bytes) of a KV codec."""
+    import decode_attention_int8_amd as q8
+    return {"fp8": (q8.Fp8KVCache, q8.fp8_decode_attn, workloads.fp8_kv_bytes),
+            "q40": (q8.Q40KVCache, q8.q40_decode_attn, workloads.q40_kv_bytes)}[name]
+
+
+def cold_copies(cache, wrap, kv_bytes, copies_bytes, dev):
+    """The cache plus clones, so that the copies span copies_bytes of
+    algorithmic KV (bounded by 80% of free memory and 256 copies)."""
+    import torch
+    R = 1 if copies_bytes <= 0 else max(1, math.ceil(copies_bytes / kv_bytes))
+    free, _ = torch.cuda.mem_get_info(dev)
+    pool_bytes = sum(t.numel() * t.element_size() for t in (cache.k_pages, cache.v_pages, cache.k_scale, cache.v_scale))
+    R = max(1, min(R, int(0.8 * free // max(pool_bytes, 1)) + 1, 256))
+    return [cache] + [wrap(cache.k_pages.clone(), cache.v_pages.clone(), cache.k_scale.clone(), cache.v_scale.clone())
+                      for _ in range(R - 1)]
+
+
+def build_gpu(w, dev, copies_bytes, codecs=CODECS):
     import torch
     import decode_attention_int8_amd as q8
     lens = workloads.seq_lens(w)
     table, nb = workloads.block_table(w, lens)
     cache = q8.PagedKVCache(nb, w.n_kv, w.kv_bs, w.hd, device=dev)
-    for t in (cache.k_pages, cache.v_pages, cache.k_scale, cache.v_scale):
-        t.zero_()
-    cache8 = None
-    if fp8:
-        cache8 = q8.Fp8KVCache(nb, w.n_kv, w.kv_bs, w.hd, device=dev)
-        for t in (cache8.k_pages, cache8.v_pages, cache8.k_scale, cache8.v_scale):
+    others = {}
+    for name in codecs:
+        others[name] = codec_api(name)[0](nb, w.n_kv, w.kv_bs, w.hd, device=dev)
+    for c in [cache] + list(others.values()):
+        for t in (c.k_pages, c.v_pages, c.k_scale, c.v_scale):
             t.zero_()
     t0 = time.time()
     # each sequence's newest rows, which the fused-append leg stores again
@@ -97,28 +120,15 @@ def build_gpu(w, dev, copies_bytes, fp8=False):
                 sm = workloads.slot_mapping(w, table, b, int(lens[b]))
                 kd, vd, smd = torch.from_numpy(k).to(dev), torch.from_numpy(v).to(dev), torch.from_numpy(sm).to(dev)
                 cache.append(kd, vd, smd)
-                if cache8 is not None:
-                    cache8.append(kd, vd, smd)
+                for c in others.values():
+                    c.append(kd, vd, smd)
     torch.cuda.synchronize()
     log(f"appended {int(lens.sum())} tokens x {w.n_kv} kv heads in {time.time() - t0:.1f}s")
-    kv = workloads.kv_bytes(w, lens)
-    R = 1 if copies_bytes <= 0 else max(1, math.ceil(copies_bytes / kv))
-    free, _ = torch.cuda.mem_get_info(dev)
-    pool_bytes = 2 * cache.k_pages.numel() + 8 * cache.k_scale.numel()
-    R = max(1, min(R, int(0.8 * free // max(pool_bytes, 1)) + 1, 256))
-    caches = [cache] + [q8.PagedKVCache.wrap(cache.k_pages.clone(), cache.v_pages.clone(),
-                                             cache.k_scale.clone(), cache.v_scale.clone())
-                        for _ in range(R - 1)]
-    caches8 = []
-    if cache8 is not None:
-        R8 = 1 if copies_bytes <= 0 else max(1, math.ceil(copies_bytes / workloads.fp8_kv_bytes(w, lens)))
-        free, _ = torch.cuda.mem_get_info(dev)
-        R8 = max(1, min(R8, int(0.8 * free // max(pool_bytes, 1)) + 1, 256))
-        caches8 = [cache8] + [q8.Fp8KVCache.wrap(cache8.k_pages.clone(), cache8.v_pages.clone(),
-                                                 cache8.k_scale.clone(), cache8.v_scale.clone())
-                              for _ in range(R8 - 1)]
+    caches = cold_copies(cache, q8.PagedKVCache.wrap, workloads.kv_bytes(w, lens), copies_bytes, dev)
+    codec_caches = {name: cold_copies(c, codec_api(name)[0].wrap, codec_api(name)[2](w, lens), copies_bytes, dev)
+                    for name, c in others.items()}
     q = torch.from_numpy(workloads.query(w)).to(dev)
-    return dict(lens=lens, table=table, nb=nb, caches=caches, caches8=caches8, q=q, k_last=k_last, v_last=v_last,
+    return dict(lens=lens, table=table, nb=nb, caches=caches, codec=codec_caches, q=q, k_last=k_last, v_last=v_last,
                 table_d=torch.from_numpy(table).to(dev), lens_d=torch.from_numpy(lens).to(dev))
 
 
@@ -208,18 +218,18 @@ def time_append_decode(w, g, steps, warmup, part_tokens):
     return {k: round(v, 3) for k, v in res.items()}
 
 
-def time_fp8(w, g, steps, warmup, part_tokens):
-    """The same decode step over the FP8 codec (q8kv_fp8_decode_attn),
-    rotated over its own cold copies.  Returns (us per step, out)."""
+def time_codec(w, g, name, steps, warmup, part_tokens):
+    """The same decode step over another KV codec (FP8 or q4_0), rotated over
+    its own cold copies.  Returns us per step."""
     import torch
-    import decode_attention_int8_amd as q8
+    decode = codec_api(name)[1]
     scale = workloads.softmax_scale(w.hd)
-    R = len(g["caches8"])
+    caches = g["codec"][name]
+    R = len(caches)
     out = torch.empty_like(g["q"])
 
     def step(i):
-        q8.fp8_decode_attn(g["q"], g["caches8"][i % R], g["table_d"], g["lens_d"], scale, out=out,
-                           part_tokens=part_tokens)
+        decode(g["q"], caches[i % R], g["table_d"], g["lens_d"], scale, out=out, part_tokens=part_tokens)
 
     for i in range(warmup):
         step(i)
@@ -234,13 +244,13 @@ def time_fp8(w, g, steps, warmup, part_tokens):
     return e0.elapsed_time(e1) * 1e3 / steps
 
 
-def fp8_parity(w, g, max_seqs=2, max_tokens=16384):
-    """Max-abs difference of the FP8 decode against the FP8 oracle (fp64
+def codec_parity(w, g, name, max_seqs=2, max_tokens=16384):
+    """Max-abs difference of a codec's decode against its oracle (fp64
     definition) on a bounded sample of the workload's sequences: the sampled
     sequences' rows are re-quantised on the host by the oracle."""
     import torch
-    import decode_attention_int8_amd as q8
-    from oracle import fp8kv
+    from oracle import fp8kv, q40
+    host_cls, ref = {"fp8": (fp8kv.Fp8Cache, fp8kv.decode), "q40": (q40.Q40Cache, q40.decode)}[name]
     lens = g["lens"]
     seqs, tot = [], 0
     sample_lens = np.zeros_like(lens)
@@ -252,14 +262,14 @@ def fp8_parity(w, g, max_seqs=2, max_tokens=16384):
         seqs.append(int(b))
         tot += int(sample_lens[b])
     scale = workloads.softmax_scale(w.hd)
-    out = q8.fp8_decode_attn(g["q"], g["caches8"][0], g["table_d"], torch.from_numpy(sample_lens).to(g["q"].device),
-                             scale).cpu().numpy()
-    host = fp8kv.Fp8Cache(g["nb"], w.n_kv, w.kv_bs, w.hd)
+    out = codec_api(name)[1](g["q"], g["codec"][name][0], g["table_d"],
+                             torch.from_numpy(sample_lens).to(g["q"].device), scale).cpu().numpy()
+    host = host_cls(g["nb"], w.n_kv, w.kv_bs, w.hd)
     for b in seqs:
         n = int(sample_lens[b])
         k, v = workloads.kv_rows(w, b, int(lens[b]))
         host.append(k[:n], v[:n], workloads.slot_mapping(w, g["table"], b, n))
-    want = fp8kv.decode(workloads.query(w), host, g["table"], sample_lens, scale)
+    want = ref(workloads.query(w), host, g["table"], sample_lens, scale)
     return {"max_abs_err_vs_oracle_f64": float(np.abs(out[seqs] - want[seqs]).max()),
             "sample": f"{len(seqs)} sequences, {tot} tokens"}
 
@@ -439,7 +449,8 @@ def main():
     dev = torch.device("cuda", 0)
     log(f"workload {w.name}: batch {w.batch}, heads {w.n_q}/{w.n_kv}, hd {w.hd}, kv_bs {w.kv_bs}, "
         f"seq_len {'U{1..%d}' % w.seq_len if w.ragged else w.seq_len}")
-    g = build_gpu(w, dev, args.cold_bytes, fp8=not args.no_fp8)
+    codecs = tuple(c for c in CODECS if not (c == "fp8" and args.no_fp8) and not (c == "q40" and args.no_q40))
+    g = build_gpu(w, dev, args.cold_bytes, codecs)
     lens = g["lens"]
     kvb = workloads.kv_bytes(w, lens)
     algo = workloads.step_bytes(w, lens)
@@ -484,16 +495,16 @@ def main():
                                 "decode_frac_of_ceiling": round(achieved / read_gbs, 4)},
         "cpu_baseline": None,
     }
-    if not args.no_fp8:
-        fp8_us = time_fp8(w, g, args.steps, args.warmup, args.part_tokens)
-        algo8 = workloads.step_bytes(w, lens, codec="fp8")
-        rec["fp8"] = {"us_per_step": round(fp8_us, 3), "kv_bytes_per_step": workloads.fp8_kv_bytes(w, lens),
-                      "algorithmic_bytes": algo8,
-                      "achieved_gbs": round(algo8 / (fp8_us * 1e-6) / 1e9, 2),
-                      "frac": round(algo8 / (fp8_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                      "traffic": profiled_traffic(w, f"{w.name}:fp8"),
-                      "cold_cache_copies": len(g["caches8"])}
-        log(f"fp8 codec: {fp8_us:.2f} us/step, {rec['fp8']['achieved_gbs']:.0f} GB/s")
+    for name in codecs:
+        c_us = time_codec(w, g, name, args.steps, args.warmup, args.part_tokens)
+        c_algo = workloads.step_bytes(w, lens, codec=name)
+        rec[name] = {"us_per_step": round(c_us, 3), "kv_bytes_per_step": codec_api(name)[2](w, lens),
+                     "algorithmic_bytes": c_algo,
+                     "achieved_gbs": round(c_algo / (c_us * 1e-6) / 1e9, 2),
+                     "frac": round(c_algo / (c_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": profiled_traffic(w, f"{w.name}:{name}"),
+                     "cold_cache_copies": len(g["codec"][name])}
+        log(f"{name} codec: {c_us:.2f} us/step, {rec[name]['achieved_gbs']:.0f} GB/s")
     if not args.no_quest:
         top_k = max(1, -(-w.max_blocks // 8))
         qs = time_quest(w, g, args.steps, args.warmup, top_k)
@@ -532,8 +543,8 @@ def main():
         cpu, parity = cpu_baseline(w, g, gpu_out, args.cpu_seconds)
         rec["cpu_baseline"] = cpu
         rec["parity"] = parity
-        if "fp8" in rec:
-            rec["fp8"]["parity"] = fp8_parity(w, g)
+        for name in codecs:
+            rec[name]["parity"] = codec_parity(w, g, name)
     print(json.dumps(rec), flush=True)
 
 

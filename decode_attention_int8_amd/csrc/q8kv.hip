@@ -1065,13 +1065,12 @@ struct Q4Tile {
     uint32_t kd[2][Q4Geo<HD>::SCW];  // fp16 scales of rows 4r .. 4r+3, row-major
     uint32_t vd[2][Q4Geo<HD>::SCW];
     int nval[2];
-    __device__ __forceinline__ float kscale(int st, int j, int blk) const {
+    // the fp16 scale of row 4r + j, 32-block blk, widened to fp32
+    __device__ __forceinline__ float kscale(int st, int j, int blk) const { return half_at(kd[st], j, blk); }
+    __device__ __forceinline__ float vscale(int st, int j, int blk) const { return half_at(vd[st], j, blk); }
+    static __device__ __forceinline__ float half_at(const uint32_t (&d)[Q4Geo<HD>::SCW], int j, int blk) {
         const int i = j * Q4Geo<HD>::NB + blk;
-        return (float)__builtin_bit_cast(_Float16, (uint16_t)(kd[st][i >> 1] >> (16 * (i & 1))));
-    }
-    __device__ __forceinline__ float vscale(int st, int j, int blk) const {
-        const int i = j * Q4Geo<HD>::NB + blk;
-        return (float)__builtin_bit_cast(_Float16, (uint16_t)(vd[st][i >> 1] >> (16 * (i & 1))));
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)(d[i >> 1] >> (16 * (i & 1))));
     }
 };
 
@@ -1097,23 +1096,34 @@ __device__ __forceinline__ void q4_tile_load(Q4Tile<HD>& T, const DecodeArgs& a,
     }
 }
 
-// Two fp32 values -> packed bf16x2 (each rounded to nearest even).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 values -> packed bf16x2, each rounded to nearest even (one
+// v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float x, float y) {
-    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)y) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){x, y}, bf16x2));
 }
 
+// The value a q4_0 code c carries into P.V is 128 + c: the bf16 whose high
+// byte is 0x43 (exponent of 128, one unit per mantissa step) and whose low
+// byte is c.  The 136 = 128 + 8 offset comes off once per item, from the
+// weight sums (q4_offset_fix).
+constexpr float kQ4Offset = 136.0f;
+
 template <int HD>
-__device__ __forceinline__ void q4_tile_compute(const Q4Tile<HD>& T, const int8_t* lq, const float* lqsc,
+__device__ __forceinline__ void q4_tile_compute(Q4Tile<HD>& T, const int8_t* lq, const float* lqsc,
                                                 const int* lqsum, float score_scale, f32x4 (&acc)[Geo<HD>::BPL],
-                                                float& M, float& S, int lane) {
+                                                f32x4& wsums, float& M, float& S, int lane) {
     using GG = Geo<HD>;
     using QG = Q4Geo<HD>;
     const int r = lane >> 4, n = lane & 15, bp = n >> 3, g = n & 7;
     QOperand<HD> Q;
     load_q_operand<HD>(Q, lq, lqsc, lane, score_scale);
+    // the -8 offset of the K codes: the dot starts at -8 * (the query block's code sum)
     int qs8[GG::NPAIR];
 #pragma unroll
-    for (int p = 0; p < GG::NPAIR; ++p) qs8[p] = 8 * lqsum[g * GG::NB + 2 * p + bp];
+    for (int p = 0; p < GG::NPAIR; ++p) qs8[p] = -8 * lqsum[g * GG::NB + 2 * p + bp];
     float sc[2][4];
     float mx = -INFINITY;
 #pragma unroll
@@ -1124,14 +1134,14 @@ __device__ __forceinline__ void q4_tile_compute(const Q4Tile<HD>& T, const int8_
             const uint32_t x0 = T.k[st][2 * p], x1 = T.k[st][2 * p + 1];
             const i32x4 kop = {(int)(x0 & 0x0f0f0f0fu), (int)(x1 & 0x0f0f0f0fu), (int)((x0 >> 4) & 0x0f0f0f0fu),
                                (int)((x1 >> 4) & 0x0f0f0f0fu)};
-            c[p] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop, Q.op[p], i32x4{0, 0, 0, 0}, 0, 0, 0);
+            c[p] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop, Q.op[p], i32x4{qs8[p], qs8[p], qs8[p], qs8[p]}, 0, 0, 0);
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             float part = 0.0f;
 #pragma unroll
             for (int p = 0; p < GG::NPAIR; ++p)
-                part += (float)(c[p][j] - qs8[p]) * Q.scl[p] * T.kscale(st, j, 2 * p + bp);
+                part += (float)c[p][j] * __builtin_fmaf(Q.scl[p], T.kscale(st, j, 2 * p + bp), 0.0f);
             const float full = part + dpp_row_ror8(part);  // add the other block parity
             sc[st][j] = (4 * r + j) < T.nval[st] ? full : -INFINITY;
             mx = fmaxf(mx, sc[st][j]);
@@ -1144,19 +1154,15 @@ __device__ __forceinline__ void q4_tile_compute(const Q4Tile<HD>& T, const int8_
     M = m_new;
     const float m_shift = m_new - kWeightShift;
 
-    // rows past the range may hold any scale bytes: their weights are
-    // selected to zero after the scale multiply (their codes are finite)
+    // rows past the range have weight exactly 0 (exp2 of -inf)
     float W[8];
-    bool ok[8];
     float wsum = 0.0f;
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const float w = __builtin_amdgcn_exp2f(sc[st][j] - m_shift);
-            wsum += w;
-            ok[4 * st + j] = (4 * r + j) < T.nval[st];
-            W[4 * st + j] = w;
+            W[4 * st + j] = __builtin_amdgcn_exp2f(sc[st][j] - m_shift);
+            wsum += W[4 * st + j];
         }
     }
     S = S * alpha + wsum;
@@ -1170,39 +1176,74 @@ __device__ __forceinline__ void q4_tile_compute(const Q4Tile<HD>& T, const int8_
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[s][j] *= arow[j];
         }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) wsums[j] *= arow[j];
     }
 
-    // P.V, one 32-column block (two 16-column matrices) at a time; codes
-    // c -> c - 8 as the signed 4-bit value of c ^ 8, exact in bf16
-    uint32_t vx[2][QG::SW];
+    // Rows past the range (a partly filled sub-tile's tail, or an empty
+    // sub-tile, which re-reads the first one's rows) may hold any scale
+    // bytes: zero their V scales in the tile so that their zero weights stay
+    // zero.
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
+        if (T.nval[st] < kSub) {
 #pragma unroll
-        for (int i = 0; i < QG::SW; ++i) vx[st][i] = T.v[st][i] ^ 0x88888888u;
+            for (int i = 0; i < QG::SCW; ++i) {
+                const int j = 2 * i / QG::NB;  // row 4r + j of dword i
+                T.vd[st][i] = (4 * r + j) < T.nval[st] ? T.vd[st][i] : 0u;
+            }
+        }
     }
+
+    // weight rows: lanes n < 8 carry bf16(x), lanes n >= 8 the remainder
+    // bf16(x - bf16(x)); a lane of the first kind subtracts zero
+    const uint32_t lo_sel = n < 8 ? 0x0c0c0c0cu : 0x01000c0cu;  // v_perm: (t << 16) or 0
+    const uint32_t lo_mask = n < 8 ? 0u : 0xffff0000u;
 #pragma unroll
     for (int b = 0; b < QG::NB; ++b) {
-        bf16x8 aw;
+        uint32_t aw[4];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const float x = ok[k] ? W[k] * T.vscale(k >> 2, k & 3, b) : 0.0f;
-            const __bf16 hi = (__bf16)x;
-            aw[k] = n < 8 ? hi : (__bf16)(x - (float)hi);
+        for (int i = 0; i < 4; ++i) {
+            const int k0 = 2 * i, k1 = 2 * i + 1;
+            const float x0 = __builtin_fmaf(W[k0], T.vscale(k0 >> 2, k0 & 3, b), 0.0f);
+            const float x1 = __builtin_fmaf(W[k1], T.vscale(k1 >> 2, k1 & 3, b), 0.0f);
+            const uint32_t t = pack_bf16x2(x0, x1);
+            const float h0 = __uint_as_float(__builtin_amdgcn_perm(t, t, lo_sel));
+            const float h1 = __uint_as_float(t & lo_mask);
+            aw[i] = pack_bf16x2(x0 - h0, x1 - h1);
         }
+        const bf16x8 awv = __builtin_bit_cast(bf16x8, aw);
+        // this block's weight sums go to column b of the sums matrix
+        const uint32_t one = n == b ? 0x3f803f80u : 0u;
+        wsums = __builtin_amdgcn_mfma_f32_16x16x32_bf16(awv, __builtin_bit_cast(bf16x8, (u32x4){one, one, one, one}),
+                                                        wsums, 0, 0, 0);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const int s = 2 * b + h;
             u32x4 bv;
 #pragma unroll
             for (int st = 0; st < 2; ++st) {
-                const uint32_t d = vx[st][s >> 1];
-                float f[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) f[j] = (float)(int)__builtin_amdgcn_sbfe(d, 8 * j + 4 * h, 4);
-                bv[2 * st] = pack_bf16x2(f[0], f[1]);
-                bv[2 * st + 1] = pack_bf16x2(f[2], f[3]);
+                const uint32_t d = (T.v[st][b] >> (4 * h)) & 0x0f0f0f0fu;
+                bv[2 * st] = __builtin_amdgcn_perm(0x43434343u, d, 0x04010400u);
+                bv[2 * st + 1] = __builtin_amdgcn_perm(0x43434343u, d, 0x04030402u);
             }
-            acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw, __builtin_bit_cast(bf16x8, bv), acc[s], 0, 0, 0);
+            acc[2 * b + h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(awv, __builtin_bit_cast(bf16x8, bv), acc[2 * b + h],
+                                                                     0, 0, 0);
+        }
+    }
+}
+
+// acc holds sum_k w_k (128 + c_k) per block; the weight sums of block b sit
+// in column b of wsums (lane 16 r + b): subtract 136 times them.
+template <int HD>
+__device__ __forceinline__ void q4_offset_fix(f32x4 (&acc)[Geo<HD>::BPL], const f32x4& wsums, int lane) {
+    const int r = lane >> 4;
+#pragma unroll
+    for (int b = 0; b < Q4Geo<HD>::NB; ++b) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float t = kQ4Offset * __shfl(wsums[j], 16 * r + b);
+            acc[2 * b][j] -= t;
+            acc[2 * b + 1][j] -= t;
         }
     }
 }
@@ -1475,13 +1516,14 @@ q8kv_decode_kernel(const DecodeArgs a) {
 #pragma unroll
         for (int s = 0; s < GG::BPL; ++s) acc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
         float M = -INFINITY, S = 0.0f;
+        f32x4 wsums = {0.f, 0.f, 0.f, 0.f};  // q4_0: per-block weight sums
 
         while (ts < t1) {
             if constexpr (NEW) {
                 if (ts == tail_ts) tile_patch<HD>(A, lnew, lnew + HD, lnew_sc[0], lnew_sc[1], L - 1 - ts, ilane);
             }
             if constexpr (FP8) fp8_tile_compute<HD>(A, lq16, a.scale_log2, acc, M, S, ilane);
-            else if constexpr (Q40) q4_tile_compute<HD>(A, lq, lqsc, lqsum, a.scale_log2, acc, M, S, ilane);
+            else if constexpr (Q40) q4_tile_compute<HD>(A, lq, lqsc, lqsum, a.scale_log2, acc, wsums, M, S, ilane);
             else tile_compute<HD>(A, lq, lqsc, a.scale_log2, acc, M, S, ilane);
             ts += kStride;
             if (ts < t1) {
@@ -1501,6 +1543,7 @@ q8kv_decode_kernel(const DecodeArgs a) {
             if (tail_ts != INT_MIN) store_new_token<HD>(a, kh, L, lnew, lnew_sc, &lnew_blk, ilane);
         }
 
+        if constexpr (Q40) q4_offset_fix<HD>(acc, wsums, ilane);
         // wave state -> LDS: exp-sum over the four row groups, hi + lo rows
         S = swap16_sum(S);
         S = swap32_sum(S);

@@ -157,9 +157,16 @@ def fp8_kv_bytes(w, lens):
     return int(np.sum(lens, dtype=np.int64)) * w.n_kv * (2 * w.hd + 2 * (w.hd // 64))
 
 
+def q40_kv_bytes(w, lens):
+    """Algorithmic KV bytes of one decode step over the q4_0 codec: per
+    (token, kv head) hd / 2 bytes of 4-bit K codes, as many of V codes, and
+    one fp16 scale per 32 elements of each."""
+    return int(np.sum(lens, dtype=np.int64)) * w.n_kv * (w.hd + 4 * (w.hd // 32))
+
+
 def step_bytes(w, lens, codec="q8"):
     """All algorithmic bytes of one step: KV + scales, q and out (fp32), the
     used block-table entries and the seq_lens array."""
     used_blocks = sum(-(-int(L) // w.kv_bs) for L in lens)
-    kv = kv_bytes(w, lens) if codec == "q8" else fp8_kv_bytes(w, lens)
+    kv = {"q8": kv_bytes, "fp8": fp8_kv_bytes, "q40": q40_kv_bytes}[codec](w, lens)
     return (kv + 2 * w.batch * w.n_q * w.hd * 4 + 4 * used_blocks + 4 * w.batch)
