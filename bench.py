@@ -386,6 +386,7 @@ def cpu_baseline(w, g, gpu_out_fn, seconds):
     add(order[0])
     probe = np.zeros_like(lens)
     probe[order[0]] = min(int(lens[order[0]]), 4096)
+    oracle.decode(q, host, table, probe, scale, threads=threads)  # warm: threads, first touches
     t = time.perf_counter()
     oracle.decode(q, host, table, probe, scale, threads=threads)
     sec_per_tok = (time.perf_counter() - t) / int(probe[order[0]])
@@ -402,11 +403,15 @@ def cpu_baseline(w, g, gpu_out_fn, seconds):
             acc += take
     seqs = [b for b in order if sl[b] > 0]
     whole = acc == tokens_total
-    reps = max(1, int(round(budget / tokens_total))) if whole else 1
+    # a whole step that is short repeats until the time budget is spent
+    reps = 0
     t = time.perf_counter()
-    for _ in range(reps):
+    while True:
         want = oracle.decode(q, host, table, sl, scale, threads=threads)
-    secs = time.perf_counter() - t
+        reps += 1
+        secs = time.perf_counter() - t
+        if not whole or secs >= seconds:
+            break
     step_s = secs / reps / (acc / tokens_total)
     kvb = workloads.kv_bytes(w, lens)
     got = gpu_out_fn(sl)
