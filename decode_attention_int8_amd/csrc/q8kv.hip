@@ -111,10 +111,14 @@ struct QRows {
     static constexpr int kChunks = kHeadGroup * HD / 4;
     static constexpr int kPer = (kChunks + NT - 1) / NT;
     f32x4 x[kPer];
+    bool keep[kPer];  // row g < G (rows past G are zero)
+    // the chunk, zero for rows past G: read only where it is quantised, so
+    // that the wait for the load is not placed ahead of later loads
+    __device__ __forceinline__ f32x4 at(int i) const { return keep[i] ? x[i] : f32x4{0.f, 0.f, 0.f, 0.f}; }
 };
 
 // Every thread issues its loads unconditionally (rows past G re-read row
-// G - 1 and are zeroed), so no branch makes a later wait conservative.
+// G - 1), so no branch makes a later wait conservative.
 template <int HD, int NT>
 __device__ __forceinline__ void load_q_rows(QRows<HD, NT>& Q, const float* __restrict__ q, int G, int tid) {
 #pragma unroll
@@ -122,8 +126,8 @@ __device__ __forceinline__ void load_q_rows(QRows<HD, NT>& Q, const float* __res
         const int c = min(tid + i * NT, QRows<HD, NT>::kChunks - 1);
         const int g = c / (HD / 4);
         const int e = (c % (HD / 4)) * 4;
-        const f32x4 x = *reinterpret_cast<const f32x4*>(q + (size_t)min(g, G - 1) * HD + e);
-        Q.x[i] = g < G ? x : f32x4{0.f, 0.f, 0.f, 0.f};
+        Q.x[i] = *reinterpret_cast<const f32x4*>(q + (size_t)min(g, G - 1) * HD + e);
+        Q.keep[i] = g < G;
     }
 }
 
@@ -136,7 +140,7 @@ __device__ __forceinline__ void quantize_q_regs(const QRows<HD, NT>& Q, int8_t* 
         if (QRows<HD, NT>::kChunks % NT != 0 && c >= QRows<HD, NT>::kChunks) break;  // same for all 8 of a block
         const int g = c / (HD / 4);
         const int e = (c % (HD / 4)) * 4;
-        const f32x4 x = Q.x[i];
+        const f32x4 x = Q.at(i);
         float a = fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w)));
         a = fmaxf(a, __shfl_xor(a, 1));
         a = fmaxf(a, __shfl_xor(a, 2));
@@ -891,11 +895,12 @@ __device__ __forceinline__ void split_q_regs(const QRows<HD, NT>& Q, _Float16* l
         if (QRows<HD, NT>::kChunks % NT != 0 && c >= QRows<HD, NT>::kChunks) break;
         const int g = c / (HD / 4);
         const int e = (c % (HD / 4)) * 4;
+        const f32x4 x = Q.at(i);
         _Float16 hi[4], lo[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            hi[k] = (_Float16)Q.x[i][k];
-            lo[k] = (_Float16)(Q.x[i][k] - (float)hi[k]);
+            hi[k] = (_Float16)x[k];
+            lo[k] = (_Float16)(x[k] - (float)hi[k]);
         }
         *reinterpret_cast<u32x2*>(lq16 + g * HD + e) = __builtin_bit_cast(u32x2, hi);
         *reinterpret_cast<u32x2*>(lq16 + (kHeadGroup + g) * HD + e) = __builtin_bit_cast(u32x2, lo);
@@ -1498,6 +1503,10 @@ q8kv_decode_kernel(const DecodeArgs a) {
             // static grids: the new rows' loads go out behind the first tile
             if (tail_ts != INT_MIN) load_new_rows<HD>(nk, nv, a.knew, a.vnew, a.new_bf16, b, a.n_kv, kh, ilane);
         }
+        // keep the query quantisation (which waits for the query rows) behind
+        // the tile loads: the scheduler would otherwise fill the address
+        // latency with it and delay the loads by a memory round trip
+        __builtin_amdgcn_sched_barrier(0);
 
         if constexpr (FP8) split_q_regs<HD, kThreads>(qrows, lq16, itid);
         else if constexpr (Q40) quantize_q_regs<HD, kThreads>(qrows, lq, lqsc, itid, lqsum);
