@@ -1,0 +1,125 @@
+"""GPU parity at the five workloads' full sizes, in the launch configuration
+the benchmark times (the default partition plan; static or persistent grid,
+in-kernel merge or combine kernel as the shape decides), for the int8 codec
+and the FP8 and q4_0 codecs.
+
+The whole workload is appended on the GPU and decoded in one call.  The
+oracle then computes a sample of the outputs: a few sequences (the longest
+and the shortest non-empty one, plus the first and last) and, of those, the
+query heads of the first and the last kv head.  It runs on a host cache that
+holds only the sampled rows of one kv head, addressed through the same block
+table; the other sequences are given length 0 there.
+"""
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import pytest
+import torch
+
+import decode_attention_int8_amd as q8
+import oracle
+import workloads
+from gpu_cases import DEV, say, to_dev
+from oracle import fp8kv, q40
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-4    # GPU vs the fp32 oracle (int8 codec), or vs the fp64 definition (FP8, q4_0)
+TOL64 = 2e-5  # int8 codec: GPU vs the oracle's fp64 twin
+
+CODECS = {
+    "q8": (q8.PagedKVCache, q8.decode_attn),
+    "fp8": (q8.Fp8KVCache, q8.fp8_decode_attn),
+    "q40": (q8.Q40KVCache, q8.q40_decode_attn),
+}
+
+
+def sample_seqs(lens):
+    nz = [int(b) for b in np.flatnonzero(lens > 0)]
+    pick = {nz[0], nz[-1], int(np.argmax(lens)), min(nz, key=lambda b: (int(lens[b]), b))}
+    return sorted(pick)
+
+
+_built = {}
+
+
+def full_case(name):
+    """Device caches of every codec holding the whole workload, the outputs
+    of one decode call each, and the sampled sequences' source rows."""
+    if name in _built:
+        return _built[name]
+    w = workloads.WORKLOADS[name]
+    lens = workloads.seq_lens(w)
+    table, nb = workloads.block_table(w, lens)
+    seqs = sample_seqs(lens)
+    caches = {}
+    for codec, (cls, _) in CODECS.items():
+        c = cls(nb, w.n_kv, w.kv_bs, w.hd, device=DEV)
+        for t in (c.k_pages, c.v_pages, c.k_scale, c.v_scale):
+            t.zero_()
+        caches[codec] = c
+    rows = {}
+    say(f"full size {name}: {int(lens.sum())} tokens, sampled sequences {seqs}")
+    with ThreadPoolExecutor(8) as ex:
+        for c0 in range(0, w.batch, 8):
+            bs = list(range(c0, min(c0 + 8, w.batch)))
+            futs = {b: ex.submit(workloads.kv_rows, w, b, int(lens[b])) for b in bs}
+            for b in bs:
+                k, v = futs[b].result()
+                if int(lens[b]) == 0:
+                    continue
+                sm = workloads.slot_mapping(w, table, b, int(lens[b]))
+                kd, vd, smd = to_dev(k), to_dev(v), to_dev(sm)
+                for c in caches.values():
+                    c.append(kd, vd, smd)
+                if b in seqs:
+                    rows[b] = (k, v, sm)
+    q = workloads.query(w)
+    scale = workloads.softmax_scale(w.hd)
+    qd, td, ld = to_dev(q), to_dev(table), to_dev(lens)
+    outs = {}
+    for codec, (_, fn) in CODECS.items():
+        outs[codec] = fn(qd, caches[codec], td, ld, scale).cpu().numpy()
+    torch.cuda.synchronize()
+    del caches
+    torch.cuda.empty_cache()
+    _built.clear()  # keep one workload's state at a time
+    _built[name] = (w, lens, table, nb, seqs, rows, q, scale, outs)
+    return _built[name]
+
+
+def sampled_reference(codec, w, lens, table, nb, seqs, rows, q, scale, kh):
+    """Oracle outputs [batch][G][hd] of kv head kh for the sampled sequences."""
+    G = w.n_q // w.n_kv
+    host = {"q8": oracle.Cache, "fp8": fp8kv.Fp8Cache, "q40": q40.Q40Cache}[codec](nb, 1, w.kv_bs, w.hd)
+    sl = np.zeros_like(lens)
+    for b in seqs:
+        k, v, sm = rows[b]
+        host.append(k[:, kh:kh + 1], v[:, kh:kh + 1], sm)
+        sl[b] = lens[b]
+    qs = np.ascontiguousarray(q[:, kh * G:(kh + 1) * G])
+    if codec == "q8":
+        return (oracle.decode(qs, host, table, sl, scale, threads=8),
+                oracle.decode(qs, host, table, sl, scale, use_f64=True, threads=8))
+    ref = fp8kv.decode if codec == "fp8" else q40.decode
+    return ref(qs, host, table, sl, scale), None
+
+
+@pytest.mark.parametrize("name,codec", [(n, c) for n in workloads.ORDER for c in CODECS])
+def test_full_size_sampled(name, codec):
+    w, lens, table, nb, seqs, rows, q, scale, outs = full_case(name)
+    got = outs[codec]
+    G = w.n_q // w.n_kv
+    assert np.all(np.isfinite(got))
+    for kh in sorted({0, w.n_kv - 1}):
+        say(f"  {name} {codec}: kv head {kh}, sequences {seqs}")
+        want, want64 = sampled_reference(codec, w, lens, table, nb, seqs, rows, q, scale, kh)
+        g = got[seqs][:, kh * G:(kh + 1) * G]
+        err = float(np.abs(g - want[seqs]).max())
+        assert err <= TOL, f"{name} {codec} kv head {kh}: max-abs error {err:.3g} > {TOL}"
+        if want64 is not None:
+            err64 = float(np.abs(g - want64[seqs]).max())
+            assert err64 <= TOL64, f"{name} {codec} kv head {kh}: max-abs error {err64:.3g} vs fp64 > {TOL64}"
+    # sequences of length 0 give zero rows
+    for b in np.flatnonzero(lens == 0):
+        assert not got[b].any()
