@@ -1,7 +1,7 @@
 """GPU parity at the five workloads' full sizes, in the launch configuration
 the benchmark times (the default partition plan; static or persistent grid,
 in-kernel merge or combine kernel as the shape decides), for the int8 codec
-and the FP8 and q4_0 codecs.
+and the FP8 and q4_0 codecs, the fused append + decode and QUEST.
 
 The whole workload is appended on the GPU and decoded in one call.  The
 oracle then computes a sample of the outputs: a few sequences (the longest
@@ -9,6 +9,13 @@ and the shortest non-empty one, plus the first and last) and, of those, the
 query heads of the first and the last kv head.  It runs on a host cache that
 holds only the sampled rows of one kv head, addressed through the same block
 table; the other sequences are given length 0 there.
+
+The fused step re-stores every sequence's newest token with its own values,
+as the benchmark's fused leg does: the cache must come back unchanged and
+the output must be the plain decode's, bit for bit.  QUEST runs as the
+benchmark's leg does (top_k = ceil(max_blocks / 8)); on the sample its
+metadata is compared bit for bit, its selection checked for validity against
+fp64 bounds, and the decode over the selected blocks against the oracle.
 """
 from concurrent.futures import ThreadPoolExecutor
 
@@ -20,7 +27,8 @@ import decode_attention_int8_amd as q8
 import oracle
 import workloads
 from gpu_cases import DEV, say, to_dev
-from oracle import fp8kv, q40
+from oracle import fp8kv, q40, quest
+from test_oracle_quest import quest_decode
 
 pytestmark = pytest.mark.gpu
 
@@ -59,6 +67,8 @@ def full_case(name):
             t.zero_()
         caches[codec] = c
     rows = {}
+    k_last = np.zeros((w.batch, w.n_kv, w.hd), np.float32)
+    v_last = np.zeros_like(k_last)
     say(f"full size {name}: {int(lens.sum())} tokens, sampled sequences {seqs}")
     with ThreadPoolExecutor(8) as ex:
         for c0 in range(0, w.batch, 8):
@@ -68,6 +78,7 @@ def full_case(name):
                 k, v = futs[b].result()
                 if int(lens[b]) == 0:
                     continue
+                k_last[b], v_last[b] = k[-1], v[-1]
                 sm = workloads.slot_mapping(w, table, b, int(lens[b]))
                 kd, vd, smd = to_dev(k), to_dev(v), to_dev(sm)
                 for c in caches.values():
@@ -80,8 +91,21 @@ def full_case(name):
     outs = {}
     for codec, (_, fn) in CODECS.items():
         outs[codec] = fn(qd, caches[codec], td, ld, scale).cpu().numpy()
+    # the fused step, storing each sequence's newest token again
+    c8 = caches["q8"]
+    before = [t.clone() for t in (c8.k_pages, c8.v_pages, c8.k_scale, c8.v_scale)]
+    outs["fused"] = q8.append_decode_attn(qd, c8, to_dev(k_last), to_dev(v_last), td, ld, scale).cpu().numpy()
+    outs["fused_cache_same"] = all(torch.equal(a, b) for a, b in zip(before, (c8.k_pages, c8.v_pages, c8.k_scale, c8.v_scale)))
+    del before
+    # QUEST
+    top_k = max(1, -(-w.max_blocks // 8))
+    kmax, kmin = q8.quest_metadata(c8, td, ld)
+    sel, sel_lens = q8.quest_select(qd, c8, kmax, kmin, td, ld, top_k)
+    outs["quest"] = dict(kmax=kmax.cpu().numpy(), kmin=kmin.cpu().numpy(), sel=sel.cpu().numpy(),
+                         sel_lens=sel_lens.cpu().numpy(), top_k=top_k,
+                         out=q8.decode_attn_heads(qd, c8, sel, sel_lens, scale).cpu().numpy())
     torch.cuda.synchronize()
-    del caches
+    del caches, c8, kmax, kmin, sel, sel_lens
     torch.cuda.empty_cache()
     _built.clear()  # keep one workload's state at a time
     _built[name] = (w, lens, table, nb, seqs, rows, q, scale, outs)
@@ -105,8 +129,21 @@ def sampled_reference(codec, w, lens, table, nb, seqs, rows, q, scale, kh):
     return ref(qs, host, table, sl, scale), None
 
 
-@pytest.mark.parametrize("name,codec", [(n, c) for n in workloads.ORDER for c in CODECS])
-def test_full_size_sampled(name, codec):
+# one list ordered by workload, so each workload is built once
+CHECKS = [(n, c) for n in workloads.ORDER for c in list(CODECS) + ["fused", "quest"]]
+
+
+@pytest.mark.parametrize("name,check", CHECKS)
+def test_full_size(name, check):
+    if check == "fused":
+        full_size_fused_append_decode(name)
+    elif check == "quest":
+        full_size_quest(name)
+    else:
+        full_size_sampled(name, check)
+
+
+def full_size_sampled(name, codec):
     w, lens, table, nb, seqs, rows, q, scale, outs = full_case(name)
     got = outs[codec]
     G = w.n_q // w.n_kv
@@ -123,3 +160,53 @@ def test_full_size_sampled(name, codec):
     # sequences of length 0 give zero rows
     for b in np.flatnonzero(lens == 0):
         assert not got[b].any()
+
+
+def full_size_fused_append_decode(name):
+    w, lens, table, nb, seqs, rows, q, scale, outs = full_case(name)
+    say(f"  {name} fused append + decode")
+    assert outs["fused_cache_same"], "re-storing the newest tokens changed the cache"
+    assert np.array_equal(outs["fused"].view(np.uint32), outs["q8"].view(np.uint32))
+
+
+def full_size_quest(name):
+    w, lens, table, nb, seqs, rows, q, scale, outs = full_case(name)
+    qs_ = outs["quest"]
+    top_k, kmax, kmin, sel, sel_lens, got = (qs_[k] for k in ("top_k", "kmax", "kmin", "sel", "sel_lens", "out"))
+    G = w.n_q // w.n_kv
+    logical_len = np.minimum(-(-lens // w.kv_bs), top_k)
+    assert np.array_equal(sel_lens, np.where(lens > 0, (logical_len - 1) * w.kv_bs + lens - (-(-lens // w.kv_bs) - 1) * w.kv_bs, 0))
+    for kh in sorted({0, w.n_kv - 1}):
+        say(f"  {name} quest: kv head {kh}, top_k {top_k}, sequences {seqs}")
+        host = oracle.Cache(nb, 1, w.kv_bs, w.hd)
+        sl = np.zeros_like(lens)
+        for b in seqs:
+            k, v, sm = rows[b]
+            host.append(k[:, kh:kh + 1], v[:, kh:kh + 1], sm)
+            sl[b] = lens[b]
+        wmax, wmin = quest.metadata(host.k_pages, host.k_scale, table, sl, w.kv_bs)
+        qs = np.ascontiguousarray(q[:, kh * G:(kh + 1) * G])
+        U = quest.bounds(qs, wmax, wmin, table, sl, 1, w.kv_bs)
+        for b in seqs:
+            nblk = -(-int(lens[b]) // w.kv_bs)
+            blocks = table[b, :nblk]
+            assert np.array_equal(kmax[blocks, kh].view(np.uint32), wmax[blocks, 0].view(np.uint32))
+            assert np.array_equal(kmin[blocks, kh].view(np.uint32), wmin[blocks, 0].view(np.uint32))
+            logical = {int(p): j for j, p in enumerate(blocks)}
+            row = sel[b, kh]
+            kept = [logical[int(x)] for x in row if x >= 0]
+            assert len(kept) == min(nblk, top_k) and np.all(row[len(kept):] == -1)
+            assert kept == sorted(kept) and kept[-1] == nblk - 1
+            if nblk > top_k > 1:
+                chosen = set(kept[:-1])
+                dropped = [j for j in range(nblk - 1) if j not in chosen]
+                mag = max(np.abs(np.maximum(qs[b, g].astype(np.float64) * wmax[blocks[j], 0],
+                                            qs[b, g].astype(np.float64) * wmin[blocks[j], 0])).sum()
+                          for g in range(G) for j in range(nblk - 1))
+                eps = mag * 2.0 ** -20
+                assert min(U[b, 0, j] for j in chosen) >= max(U[b, 0, j] for j in dropped) - eps
+        # decode over the GPU's own selection
+        head_table = np.ascontiguousarray(sel[:, kh:kh + 1])
+        want = quest_decode(qs, host, head_table, np.where(sl > 0, sel_lens, 0), scale)
+        err = float(np.abs(got[seqs][:, kh * G:(kh + 1) * G] - want[seqs]).max())
+        assert err <= TOL, f"{name} quest kv head {kh}: max-abs error {err:.3g} > {TOL}"
