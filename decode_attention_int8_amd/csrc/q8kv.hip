@@ -1899,18 +1899,61 @@ __global__ __launch_bounds__(256) void q8kv_quest_metadata_kernel(const QuestArg
     }
 }
 
+// x[l] + x[l ^ 8] inside rows of 16 lanes, lane l keeping the sum of a (l % 16
+// < 8) or of b (l % 16 >= 8): one rotation by 8 carries the value the partner
+// keeps.
+__device__ __forceinline__ float row_pair_sum(float a, float b, int lane) {
+    const bool lo = (lane & 8) == 0;
+    const float send = lo ? b : a;
+    return (lo ? a : b) + dpp_row_ror8(send);
+}
+
+// Eight per-lane partial sums t[0..7] -> in every lane, the largest over h of
+// the wave-wide sum of t[h].  Transposed butterfly: each exchange halves the
+// values a lane carries (permlane32 swaps: heads h and h + 4 split between
+// the wave halves; permlane16 swaps: h and h + 2 between odd and even rows;
+// a row rotation by 8: h and h + 1 between row halves), then three DPP steps
+// sum the eight lanes of a half row that hold the same head; the largest over
+// the heads then takes three steps (l ^ 8, l ^ 16, l ^ 32).
+__device__ __forceinline__ float max_of_wave_sums8(const float (&t)[kHeadGroup], int lane) {
+    static_assert(kHeadGroup == 8, "eight query rows");
+    float s4[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(t[i]), __float_as_uint(t[i + 4]), false, false);
+        s4[i] = __uint_as_float(p[0]) + __uint_as_float(p[1]);  // head i (lanes < 32) or i + 4
+    }
+    float s2[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(s4[i]), __float_as_uint(s4[i + 2]), false, false);
+        s2[i] = __uint_as_float(p[0]) + __uint_as_float(p[1]);  // + 2 in odd rows
+    }
+    float x = row_pair_sum(s2[0], s2[1], lane);  // + 1 in the upper half of a row
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xb1, 0xf, 0xf, false));   // quad_perm 1,0,3,2
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4e, 0xf, 0xf, false));   // quad_perm 2,3,0,1
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xf, 0xf, false));  // row_half_mirror
+    x = fmaxf(x, dpp_row_ror8(x));
+    x = swap16_max(x);
+    return swap32_max(x);
+}
+
 // Bounds: one workgroup per (sequence, kv head, run of kQuestRun logical
-// blocks); its waves take the run's blocks in turn.  A wave holds the query
-// rows of the kv head (lanes over channels, EPL = HD / 64 each) and, per
-// block j < last, forms for every query head h the lane's part of
-// sum_c max(q_h[c] * kmax[c], q_h[c] * kmin[c]); each head's sum is reduced
-// across the wave with DPP and permlane swaps (no LDS), and the largest over
-// the heads is the block's bound.
-constexpr int kQuestRun = 16;
+// blocks); its waves take the run's blocks in turn.  The kv head's query
+// rows are staged once in LDS; a wave holds them in registers (lanes over
+// channels, EPL = HD / 64 each).  For a >= b, max(q a, q b) = q (a + b) / 2 +
+// |q| (a - b) / 2, so a head's bound sum_c max(q_h[c] kmax[c], q_h[c] kmin[c])
+// is two dot products, with the block's mid (kmax + kmin) / 2 and radius
+// (kmax - kmin) / 2; the eight heads' lane sums are reduced together
+// (max_of_wave_sums8).  A wave issues the metadata loads of all its blocks
+// before it reduces any.
+constexpr int kQuestRun = 32;
 
 template <int HD>
 __global__ __launch_bounds__(256) void q8kv_quest_bounds_kernel(const QuestArgs a) {
     constexpr int EPL = HD / kWave;
+    constexpr int PW = kQuestRun / kWaves;  // blocks per wave
+    __shared__ __attribute__((aligned(16))) float lqv[kHeadGroup][HD];
     const int lane = threadIdx.x & (kWave - 1);
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int runs = (a.max_blocks + kQuestRun - 1) / kQuestRun;
@@ -1920,19 +1963,11 @@ __global__ __launch_bounds__(256) void q8kv_quest_bounds_kernel(const QuestArgs 
     const int L = min(a.lens[b], a.max_blocks * a.kv_bs);
     const int nblk = (max(L, 0) + a.kv_bs - 1) / a.kv_bs;
     const int j0 = run * kQuestRun;
-    if (j0 >= nblk - 1) return;  // the last block is always kept
+    if (j0 >= nblk - 1) return;  // the last block is always kept (uniform over the workgroup)
     const int G = a.n_q / a.n_kv;
-    float qv[kHeadGroup][EPL];
-#pragma unroll
-    for (int g = 0; g < kHeadGroup; ++g) {
-        const float* qh = a.q + ((size_t)b * a.n_q + (size_t)kh * G + min(g, G - 1)) * HD + (size_t)lane * EPL;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) qv[g][e] = qh[e];
-    }
     const int j1 = min(j0 + kQuestRun, nblk - 1);
-    // the wave's blocks (at most kQuestRun / kWaves) are loaded before any
-    // is reduced, so their latencies overlap
-    constexpr int PW = kQuestRun / kWaves;
+    // the wave's metadata loads go out first (blocks past the run re-read
+    // the run's last block and are not used)
     float bmx[PW][EPL], bmn[PW][EPL];
     int bp[PW];
 #pragma unroll
@@ -1947,6 +1982,22 @@ __global__ __launch_bounds__(256) void q8kv_quest_bounds_kernel(const QuestArgs 
             bmn[w][e] = a.kmin[m0 + e];
         }
     }
+    // the kv head's query rows (rows past G repeat row G - 1) into LDS
+    for (int i = threadIdx.x; i < kHeadGroup * HD / 4; i += 256) {
+        const int g = i / (HD / 4), c4 = i % (HD / 4);
+        const float* qh = a.q + ((size_t)b * a.n_q + (size_t)kh * G + min(g, G - 1)) * HD;
+        *reinterpret_cast<f32x4*>(&lqv[g][4 * c4]) = *reinterpret_cast<const f32x4*>(qh + 4 * c4);
+    }
+    __syncthreads();
+    float qv[kHeadGroup][EPL], qa[kHeadGroup][EPL];
+#pragma unroll
+    for (int g = 0; g < kHeadGroup; ++g) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+            qv[g][e] = lqv[g][lane * EPL + e];
+            qa[g][e] = fabsf(qv[g][e]);
+        }
+    }
 #pragma unroll
     for (int w = 0; w < PW; ++w) {
         const int j = j0 + wid + kWaves * w;
@@ -1954,21 +2005,22 @@ __global__ __launch_bounds__(256) void q8kv_quest_bounds_kernel(const QuestArgs 
         const int p = bp[w];
         float u;
         if ((unsigned)p < (unsigned)a.num_blocks) {
-            const float* mx = bmx[w];
-            const float* mn = bmn[w];
+            float mid[EPL], rad[EPL];
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+                mid[e] = 0.5f * (bmx[w][e] + bmn[w][e]);
+                rad[e] = 0.5f * (bmx[w][e] - bmn[w][e]);
+            }
             float t[kHeadGroup];
 #pragma unroll
             for (int g = 0; g < kHeadGroup; ++g) {
                 t[g] = 0.0f;
 #pragma unroll
-                for (int e = 0; e < EPL; ++e) t[g] += fmaxf(qv[g][e] * mx[e], qv[g][e] * mn[e]);
+                for (int e = 0; e < EPL; ++e) t[g] = __builtin_fmaf(qa[g][e], rad[e], __builtin_fmaf(qv[g][e], mid[e], t[g]));
             }
-            // the kv head's rows past G repeat row G - 1, so the largest
-            // over all eight is the largest over the kv head's query heads
-            float m = -INFINITY;
-#pragma unroll
-            for (int g = 0; g < kHeadGroup; ++g) m = fmaxf(m, wave_allsum(t[g]));
-            u = m;
+            // the largest over all eight rows is the largest over the kv
+            // head's query heads
+            u = max_of_wave_sums8(t, lane);
         } else {
             u = NAN;  // an entry outside the pool: see the top-k kernel
         }
