@@ -1865,18 +1865,24 @@ __global__ __launch_bounds__(256) void q8kv_quest_metadata_kernel(const QuestArg
     }
     const size_t page_row = ((size_t)p * a.n_kv + kh) * a.kv_bs;
     for (int r0 = 0; r0 < rows; r0 += kSub) {
-        const bool ok = r0 + n < rows;
-        const float sc = a.ks[page_row + r0 + min(n, rows - 1 - r0)];
+        // rows past the sequence's length (only in its last sub-tile) read
+        // the last valid row again: a repeat changes no maximum or minimum
+        const int rn = min(n, rows - 1 - r0);
+        const float sc = a.ks[page_row + r0 + rn];
+        const float off = -128.0f * sc;  // exact
         i32x4 ch[NPAIR];
-        load_k_subtile<HD>(ch, a.kp, page_row + r0, lane);
+        load_k_subtile<HD>(ch, a.kp, page_row + r0, 16 * r + rn);
+        // code * sc as fma(code + 128, sc, -128 sc): the byte with its sign
+        // bit flipped converts to code + 128 in one instruction, and the
+        // fused result rounds the exact product once, as the product does
 #pragma unroll
         for (int c = 0; c < NPAIR; ++c) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const int8_t code = (int8_t)((uint32_t)ch[c][i >> 2] >> (8 * (i & 3)));
-                const float v = (float)code * sc;
-                mx[c][i] = ok ? fmaxf(mx[c][i], v) : mx[c][i];
-                mn[c][i] = ok ? fminf(mn[c][i], v) : mn[c][i];
+                const uint32_t u = ((uint32_t)ch[c][i >> 2] ^ 0x80808080u) >> (8 * (i & 3));
+                const float v = __builtin_fmaf((float)(uint8_t)u, sc, off);
+                mx[c][i] = fmaxf(mx[c][i], v);
+                mn[c][i] = fminf(mn[c][i], v);
             }
         }
     }
