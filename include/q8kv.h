@@ -89,10 +89,17 @@ enum {
  * scale        softmax scale (normally 1/sqrt(hd)), finite.
  *
  * Contexts longer than one partition are split into fixed ranges of tokens
- * whose (max, sum, accumulator) states are merged in range order by a second
- * kernel; the plan depends only on the shapes, so results are deterministic.
- * Split contexts use a library-owned device workspace (grown on demand with
- * hipMalloc, one per device and stream, freed by q8kv_release).
+ * whose (max, sum, accumulator) states are merged in range order: inside the
+ * decode kernel, by the workgroup that stores a (sequence, kv head)'s last
+ * state, when there are at most 64 states (partitions x query heads), else
+ * by a second kernel.  The plan depends only on the shapes, so results are
+ * deterministic.  Split contexts use a library-owned device workspace (grown
+ * on demand with hipMalloc, one per device and stream, freed by
+ * q8kv_release, which waits for the device first).  Calls on one stream run
+ * in order; calls on different streams use different workspaces.  The
+ * workspace holds per-(sequence, kv head) arrival counters that each call
+ * leaves at zero, so a call that is aborted mid-kernel leaves the workspace
+ * unusable until q8kv_release.
  */
 int q8kv_decode_attn(float* out, const float* q,
                      const int8_t* k_pages, const int8_t* v_pages,
