@@ -27,10 +27,19 @@
 //     weights are taken as 2^(s - M + kWeightShift), so that small ones stay
 //     clear of the f16 subnormals; the shift is common to the accumulator
 //     and the exp-sum and cancels in their quotient;
-//   * ranges longer than one partition are merged by a log-sum-exp combine
-//     kernel in partition order (deterministic).
+//   * ranges longer than one partition are merged with the log-sum-exp rule
+//     in partition order (deterministic): inside the decode kernel by the
+//     workgroup that stores a group's last state when the group is small,
+//     else by a combine kernel.
 // Scores are kept in the log2 domain (softmax scale pre-multiplied by log2 e)
 // so every exponential is one v_exp_f32.
+//
+// The same kernel, with the codec's own tile load and tile compute, serves
+// the FP8 E4M3 codec (UE8M0 scale per 64 elements) and the q4_0 codec (4-bit
+// codes, fp16 scale per 32 elements), and, with the step's new token stored
+// and patched into its tile, the fused append + decode.  QUEST adds per-block
+// channel max / min metadata, a bounds kernel and a top-k kernel that select
+// blocks per kv head, and the decode over per-head block lists.
 
 #include <hip/hip_runtime.h>
 
@@ -191,16 +200,6 @@ __device__ __forceinline__ float swap16_sum(float x) {
 __device__ __forceinline__ float swap32_sum(float x) {
     auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(p[0]) + __uint_as_float(p[1]);
-}
-// Sum over all 64 lanes, left in every lane: quad_perm swaps (xor 1, 2),
-// row_half_mirror (xor 7) and row_mirror (xor 15) inside each row of 16,
-// then the permlane16 / permlane32 swaps across rows.
-__device__ __forceinline__ float wave_allsum(float x) {
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xb1, 0xf, 0xf, false));
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4e, 0xf, 0xf, false));
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xf, 0xf, false));
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xf, 0xf, false));
-    return swap32_sum(swap16_sum(x));
 }
 __device__ __forceinline__ int r_of(int lane) { return lane >> 4; }
 __device__ __forceinline__ float lane_read(float x, int src_lane) {
