@@ -86,6 +86,7 @@ enum {
  * hd           64, 128 or 256.
  * kv_bs        tokens per page: 16, 32, 64, 128 or 256.
  * n_q_heads / n_kv_heads must be an integer group size of 1 to 8.
+ * batch        1 to 2048 sequences per call.
  * scale        softmax scale (normally 1/sqrt(hd)), finite.
  *
  * Contexts longer than one partition are split into fixed ranges of tokens

@@ -110,6 +110,7 @@ def test_append_decode_rejects_before_any_hip_call(kw, code):
     (dict(bt=NUL), q8.Q8KV_ENULL),
     (dict(sl=NUL), q8.Q8KV_ENULL),
     (dict(batch=0), q8.Q8KV_EINVAL),
+    (dict(batch=2049), q8.Q8KV_EINVAL),  # at most 2048 sequences per call
     (dict(n_q=0), q8.Q8KV_EINVAL),
     (dict(n_kv=0), q8.Q8KV_EINVAL),
     (dict(n_q=6, n_kv=4), q8.Q8KV_EINVAL),

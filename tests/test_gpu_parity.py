@@ -224,6 +224,23 @@ def test_decode_persistent_grid(G, kv_bs):
         check_decode(c, dev, part_tokens=pt)
 
 
+def test_decode_max_batch():
+    """2048 sequences, the most one call takes: the persistent grid's
+    per-sequence prefix sums and remainder classes in LDS at their full size,
+    with empty sequences and a spread of lengths."""
+    rng = np.random.default_rng(950)
+    lens = rng.integers(0, 97, size=2048)
+    lens[:6] = [0, 1, 32, 33, 96, 64]
+    w = workloads.Workload("maxbatch", 2048, 8, 2, 128, 16, 96, ragged=True, table="pool", key=950)
+    c = build(w, lens=[int(x) for x in lens])
+    say(f"max batch 2048 tokens={int(c.lens.sum())}")
+    dev = gpu_cache(c)
+    for pt in (0, 32):
+        got = decode(c, dev, part_tokens=pt)
+        assert not got[0].any()
+        check_decode(c, dev, part_tokens=pt)
+
+
 def test_decode_long_peaked_tail_precision():
     """Long contexts whose softmax is dominated by a few tokens put most of
     the sequence into tiny weights.  Their P.V weights must not fall into the
