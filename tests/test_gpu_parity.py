@@ -241,6 +241,17 @@ def test_decode_max_batch():
         check_decode(c, dev, part_tokens=pt)
 
 
+@pytest.mark.parametrize("hd,G", [(64, 1), (128, 8), (256, 4)])
+def test_decode_max_partitions(hd, G):
+    """256 partitions of one sequence, the most a call plans: the combine
+    kernel's per-thread state arrays at their full length for every hd."""
+    w = workloads.Workload("maxparts", 2, 2 * G, 2, hd, 32, 256 * 32, ragged=True, table="pool", key=960 + hd)
+    c = build(w, lens=[256 * 32, 5000])
+    say(f"max partitions hd={hd} G={G}")
+    dev = gpu_cache(c)
+    check_decode(c, dev, part_tokens=32)
+
+
 def test_decode_long_peaked_tail_precision():
     """Long contexts whose softmax is dominated by a few tokens put most of
     the sequence into tiny weights.  Their P.V weights must not fall into the

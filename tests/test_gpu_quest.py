@@ -134,3 +134,15 @@ def test_quest_ties_keep_lower_blocks():
     _, kmax, kmin, sel, sel_lens, _ = run(c, top_k=4)
     logical = {int(c.table[0, j]): j for j in range(10)}
     assert [logical[int(p)] for p in sel[0, 0]] == [0, 1, 2, 9]
+
+
+def test_quest_max_blocks():
+    """4097 blocks in one sequence, the most the selection takes (16
+    candidates per thread of the top-k workgroup), keeping 64."""
+    w = workloads.Workload("questmax", 1, 4, 1, 128, 16, 4097 * 16, table="pool", key=3500)
+    c = build(w)
+    assert c.table.shape[1] == 4097
+    cache, kmax, kmin, sel, sel_lens, out = run(c, top_k=64)
+    check_selection(c, kmax, kmin, sel, sel_lens, 64)
+    want = quest_decode(c.q, c.cache, sel, sel_lens, c.scale)
+    assert float(np.abs(out - want).max()) <= TOL
