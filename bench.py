@@ -51,8 +51,10 @@ def log(*a):
 def parse():
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=100)
-    p.add_argument("--warmup", type=int, default=10)
+    # a short step needs ~1000 untimed steps (~15 ms) before the clocks settle;
+    # 100 steps after 10 read ~3% slow on the 7B-like workload
+    p.add_argument("--steps", type=int, default=1000)
+    p.add_argument("--warmup", type=int, default=1000)
     p.add_argument("--workload", default="mha7b", choices=workloads.ORDER)
     p.add_argument("--cold-bytes", type=float, default=1.0e9,
                    help="bytes the rotated cache copies must span (0: warm, one copy)")
