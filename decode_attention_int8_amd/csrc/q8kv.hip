@@ -2468,7 +2468,7 @@ void plan(int batch, int n_kv, int max_tokens, int* part_tokens, int* n_parts) {
     const long long units = (long long)batch * n_kv * max_tokens;
     long long pt = (units + 511) / 512;
     if (pt < 512) pt = std::max(pt, std::min(512LL, units / 256));
-    if (pt > 2048) pt = std::min(4096LL, std::max(2048LL, (units + 4095) / 4096));
+    if (pt > 4096) pt = std::min(4096LL, std::max(2048LL, (units + 4095) / 4096));
     pt = (pt + 127) / 128 * 128;
     if (pt < 128) pt = 128;
     const long long min_pt = ((max_tokens + kMaxParts - 1) / kMaxParts + 127) / 128 * 128;
