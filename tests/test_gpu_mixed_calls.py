@@ -4,8 +4,8 @@ counters and the QUEST bounds buffer must all be left ready for any next
 call.  A sequence of calls of different shapes and entry points (static and
 persistent grids, in-kernel and combine-kernel merges, a workspace that has
 to grow, the fused step, both codecs, QUEST) is run once, checked against the
-oracle, then run again in reverse order and on a second stream: every output
-must repeat bit for bit.
+oracle, then run again in reverse order, on a second stream, on two streams
+at once and after q8kv_release: every output must repeat bit for bit.
 """
 import numpy as np
 import pytest
@@ -32,12 +32,28 @@ def test_mixed_calls_repeat_bitwise():
     deep = case(4102, 2, 8, 64, 64, 9000, lens=[9000, 4500])      # combine kernel, large workspace
     caches = {id(c): gpu_cache(c) for c in (small, wide, deep)}
 
+    def codec_cache(cls, c):
+        cache = cls(c.num_blocks, c.w.n_kv, c.w.kv_bs, c.w.hd, device=DEV)
+        for t in (cache.k_pages, cache.v_pages, cache.k_scale, cache.v_scale):
+            t.zero_()
+        for b in range(c.w.batch):
+            if len(c.slots[b]):
+                cache.append(to_dev(c.k_src[b]), to_dev(c.v_src[b]), to_dev(c.slots[b]))
+        return cache
+
+    fp8 = {id(c): codec_cache(q8.Fp8KVCache, c) for c in (small, deep)}
+    q40 = {id(c): codec_cache(q8.Q40KVCache, c) for c in (small, deep)}
+
     def dev_in(c):
         return to_dev(c.q), to_dev(c.table), to_dev(c.lens)
 
     def plain(c, pt):
         q, bt, sl = dev_in(c)
         return q8.decode_attn(q, caches[id(c)], bt, sl, c.scale, part_tokens=pt)
+
+    def codec(fn, store, c, pt):
+        q, bt, sl = dev_in(c)
+        return fn(q, store[id(c)], bt, sl, c.scale, part_tokens=pt)
 
     def quest(c):
         q, bt, sl = dev_in(c)
@@ -63,7 +79,11 @@ def test_mixed_calls_repeat_bitwise():
         ("small split 32", lambda: plain(small, 32)),
         ("deep split 64 (grows the workspace)", lambda: plain(deep, 64)),
         ("small fused", lambda: fused(small)),
+        ("deep fp8 (combine)", lambda: codec(q8.fp8_decode_attn, fp8, deep, 0)),
+        ("small q4_0 split 32", lambda: codec(q8.q40_decode_attn, q40, small, 32)),
         ("wide quest", lambda: quest(wide)),
+        ("deep q4_0 split 64", lambda: codec(q8.q40_decode_attn, q40, deep, 64)),
+        ("small fp8", lambda: codec(q8.fp8_decode_attn, fp8, small, 0)),
         ("deep quest", lambda: quest(deep)),
         ("wide plain again", lambda: plain(wide, 0)),
     ]
@@ -85,6 +105,21 @@ def test_mixed_calls_repeat_bitwise():
     side.synchronize()
     for name in outs:
         assert np.array_equal(outs[name].cpu().numpy().view(np.uint32), first[name].view(np.uint32)), name
+    # two streams at once, each with its own ticket, counters and workspace
+    s1, s2 = torch.cuda.Stream(device=DEV), torch.cuda.Stream(device=DEV)
+    torch.cuda.synchronize()
+    conc = {}
+    for _ in range(3):
+        with torch.cuda.stream(s1):
+            conc["wide plain (persistent)"] = plain(wide, 32)
+            conc["deep plain (combine)"] = plain(deep, 0)
+        with torch.cuda.stream(s2):
+            conc["deep split 64 (grows the workspace)"] = plain(deep, 64)
+            conc["small split 32"] = plain(small, 32)
+        s1.synchronize()
+        s2.synchronize()
+        for name, t in conc.items():
+            assert np.array_equal(t.cpu().numpy().view(np.uint32), first[name].view(np.uint32)), name
     q8.release()
     # and after the workspaces are released
     got = plain(deep, 64).cpu().numpy()
