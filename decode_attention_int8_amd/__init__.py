@@ -52,6 +52,7 @@ def _load():
         "q8kv_debug_quantize_q": [P, P, P, I, I, P],
         "q8kv_debug_block_dots": [P, I, P, P, P, P, I, I, I, I, I, I, I, P],
         "q8kv_debug_stream_read": [P, ctypes.c_size_t, P, ctypes.c_size_t, P],
+        "q8kv_debug_set_wide": [I],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -564,6 +565,12 @@ def debug_stream_read(a, b):
 
 def release():
     _check(lib.q8kv_release())
+
+
+def debug_set_wide(enable):
+    """Test export: allow (True, the default) or forbid the 8-wave workgroups
+    of static grids of at most one workgroup per CU."""
+    _check(lib.q8kv_debug_set_wide(1 if enable else 0))
 
 
 def debug_quantize_q(q):

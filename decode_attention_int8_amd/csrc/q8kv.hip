@@ -50,6 +50,7 @@
 #include <cstdio>
 #include <cstring>
 #include <algorithm>
+#include <atomic>
 #include <map>
 #include <type_traits>
 #include <mutex>
@@ -74,6 +75,7 @@ constexpr int kTile = 32;         // tokens per wave tile
 constexpr int kSub = 16;          // tokens per Q.K MFMA
 constexpr int kWaves = 4;         // waves per decode workgroup
 constexpr int kThreads = kWave * kWaves;
+constexpr int kWideWaves = 8;     // waves per workgroup of a static grid of one workgroup per CU
 constexpr float kInv127 = 1.0f / 127.0f;
 constexpr float kLog2e = 1.44269504088896340736f;
 // Exponent offset of the P.V weights (see the file comment).  A weight is at
@@ -439,7 +441,7 @@ __device__ __forceinline__ void group_max_sum(const float2* lms, int G, int g, i
 // 2^(M_p - M*) / S*.  Thread (row r, slice e4) sums partitions r, r + R, ...
 // in order; the R row sums are then added in row order, so the result does
 // not depend on which workgroup merges.
-template <int HD>
+template <int HD, int NT>
 __device__ void merge_group(const DecodeArgs& a, int b, int kh, int np, float* out_rows, int tid, float2* lms,
                             f32x4* lred) {
     constexpr int Q4 = HD / 4;
@@ -449,14 +451,14 @@ __device__ void merge_group(const DecodeArgs& a, int b, int kh, int np, float* o
     const __amdgpu_buffer_rsrc_t racc = state_rsrc(a.st_acc + first * HD, (uint32_t)(np * G * HD * 4));
     const __amdgpu_buffer_rsrc_t rms = state_rsrc(a.st_ms + first * 2, (uint32_t)(np * G * 8));
     const uint32_t pstride = (uint32_t)(G * HD * 4);  // bytes between partitions
-    const int R = slices >= kThreads ? 1 : kThreads / slices;
+    const int R = slices >= NT ? 1 : NT / slices;
     const int r = tid / slices;
     const bool active = r < R;
     int e4 = active ? tid - r * slices : 0;
     // the accumulator loads go out before the (M, S) round trip
     f32x4 v[kFusePer];
     if (active) load_slices(v, racc, pstride, e4, r, R, np);
-    for (int i = tid; i < np * G; i += kThreads) lms[i] = state_load2(rms, (uint32_t)i * 8);
+    for (int i = tid; i < np * G; i += NT) lms[i] = state_load2(rms, (uint32_t)i * 8);
     __syncthreads();
     float Mx, St;
     group_max_sum(lms, G, e4 / Q4, np, Mx, St);
@@ -471,8 +473,8 @@ __device__ void merge_group(const DecodeArgs& a, int b, int kh, int np, float* o
         return;
     }
     if (active) *reinterpret_cast<f32x4*>(out_rows + (size_t)e4 * 4) = at / St;
-    // slices > kThreads (hd 256 with five or more heads): further slices
-    for (e4 += kThreads; active && e4 < slices; e4 += kThreads) {
+    // slices > NT (hd 256 with five or more heads): further slices
+    for (e4 += NT; active && e4 < slices; e4 += NT) {
         load_slices(v, racc, pstride, e4, 0, 1, np);
         group_max_sum(lms, G, e4 / Q4, np, Mx, St);
         at = weigh_slices(v, lms, G, e4 / Q4, Mx, 0, 1, np);
@@ -1264,10 +1266,11 @@ __device__ __forceinline__ void q4_offset_fix(f32x4 (&acc)[Geo<HD>::BPL], const 
 enum GridMode { kPersistent = 0, kStatic = 1 };
 enum CodecKind { kQ8 = 0, kFp8 = 1, kQ40 = 2 };
 
-template <int HD, int MODE, bool NEW, int CODEC = kQ8>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(HD == 256 ? 1 : 3))) void
+template <int HD, int MODE, bool NEW, int CODEC = kQ8, int NW = kWaves>
+__global__ __launch_bounds__(kWave * NW) __attribute__((amdgpu_waves_per_eu(HD == 256 ? 1 : 3))) void
 q8kv_decode_kernel(const DecodeArgs a) {
     using GG = Geo<HD>;
+    constexpr int NT = kWave * NW;  // threads per workgroup
     constexpr bool STATIC = MODE == kStatic;
     constexpr bool FP8 = CODEC == kFp8;
     constexpr bool Q40 = CODEC == kQ40;
@@ -1277,20 +1280,20 @@ q8kv_decode_kernel(const DecodeArgs a) {
     __shared__ float lqsc[FP8 ? 1 : kHeadGroup * GG::NB];
     __shared__ int lqsum[Q40 ? kHeadGroup * GG::NB : 1];  // q4_0: query block code sums
     __shared__ __attribute__((aligned(16))) _Float16 lq16[FP8 ? 2 * kHeadGroup * HD : 8];  // FP8: query hi, lo rows
-    __shared__ float lM[kWaves][kHeadGroup];
-    __shared__ float lS[kWaves][kHeadGroup];
-    __shared__ float lacc[kWaves][kHeadGroup][HD];
+    __shared__ float lM[NW][kHeadGroup];
+    __shared__ float lS[NW][kHeadGroup];
+    __shared__ float lacc[NW][kHeadGroup][HD];
     // persistent grids: exclusive prefix of full-partition items per sequence,
     // the sequences that end in a partial partition (longest remainder
     // first) and each sequence's remainder class
     __shared__ int lfull[STATIC ? 1 : kMaxBatch + 1];
     __shared__ int lorder[STATIC ? 1 : kMaxBatch];
     __shared__ uint8_t lcls[STATIC ? 1 : kMaxBatch];
-    __shared__ int lscan[kWaves];
+    __shared__ int lscan[NW];
     __shared__ int litem;
     __shared__ int lflag;
     __shared__ float2 lms[kFuseRows];
-    __shared__ f32x4 lred[kThreads];
+    __shared__ f32x4 lred[NT];
     // fused append: the new token's codes, factors and block
     __shared__ __attribute__((aligned(16))) int8_t lnew[NEW ? 2 * HD : 16];
     __shared__ float lnew_sc[2];
@@ -1312,7 +1315,7 @@ q8kv_decode_kernel(const DecodeArgs a) {
         const int pt = a.part_tokens;
         // each thread counts a contiguous chunk of sequences; the chunk
         // totals are scanned with wave shuffles and one LDS round
-        const int per = (a.batch + kThreads - 1) / kThreads;
+        const int per = (a.batch + NT - 1) / NT;
         const int c0 = min(tid * per, a.batch), c1 = min(c0 + per, a.batch);
         int local = 0;
         for (int bb = c0; bb < c1; ++bb) {
@@ -1339,7 +1342,7 @@ q8kv_decode_kernel(const DecodeArgs a) {
             lfull[bb] = run;
             run += a.n_kv * (max(min(a.lens[bb], cap), 0) / pt);
         }
-        if (tid == kThreads - 1) lfull[a.batch] = run;
+        if (tid == NT - 1) lfull[a.batch] = run;
         __syncthreads();
         // wave 0 ranks the partial sequences: class counts, then positions
         // (class start + earlier sequences of the class) from wave ballots
@@ -1381,12 +1384,12 @@ q8kv_decode_kernel(const DecodeArgs a) {
         for (int bb = blockIdx.x; bb < a.batch; bb += gridDim.x) {
             if (lfull[bb + 1] == lfull[bb] && lcls[bb] == kNoPartial) {
                 float* o = a.out + (size_t)bb * a.n_q * HD;
-                for (int e = tid; e < a.n_q * HD; e += kThreads) o[e] = 0.0f;
+                for (int e = tid; e < a.n_q * HD; e += NT) o[e] = 0.0f;
             }
         }
     }
 
-    constexpr int kStride = kTile * kWaves;
+    constexpr int kStride = kTile * NW;
     constexpr int Q4 = HD / 4;
     // The first item of a workgroup is its own index; later ones come from the
     // ticket (offset by the grid size) when items can outnumber workgroups.
@@ -1433,8 +1436,8 @@ q8kv_decode_kernel(const DecodeArgs a) {
         }
         // the query rows' loads go out first: the quantisation then waits for
         // them alone, not for the first tile queued behind them
-        QRows<HD, kThreads> qrows;
-        load_q_rows<HD, kThreads>(qrows, a.q + ((size_t)b * a.n_q + (size_t)kh * G) * HD, G, itid);
+        QRows<HD, NT> qrows;
+        load_q_rows<HD, NT>(qrows, a.q + ((size_t)b * a.n_q + (size_t)kh * G) * HD, G, itid);
         const int32_t* trow = a.table + ((size_t)b * a.table_rows + (a.table_rows > 1 ? kh : 0)) * a.max_blocks;
         const int t0 = part * a.part_tokens;
         // The first tile's table reads, those of the item's first tile (a
@@ -1458,7 +1461,7 @@ q8kv_decode_kernel(const DecodeArgs a) {
             // sequence's rows are zeroed by its partition-0 slots
             if (t0 >= L) {
                 if (part == 0)
-                    for (int e = itid; e < G * HD; e += kThreads) out_rows[e] = 0.0f;
+                    for (int e = itid; e < G * HD; e += NT) out_rows[e] = 0.0f;
                 return;
             }
         }
@@ -1472,7 +1475,7 @@ q8kv_decode_kernel(const DecodeArgs a) {
         if constexpr (NEW) {
             if (!bad && L > t0 && L <= t1) {
                 const int off = L - 1 - t0;
-                if (wid == ((off / kTile) % kWaves)) {
+                if (wid == ((off / kTile) % NW)) {
                     tail_ts = t0 + off / kTile * kTile;
                     tail_blk = uniform_read(trow, (L - 1) / a.kv_bs);
                 }
@@ -1507,9 +1510,9 @@ q8kv_decode_kernel(const DecodeArgs a) {
         // latency with it and delay the loads by a memory round trip
         __builtin_amdgcn_sched_barrier(0);
 
-        if constexpr (FP8) split_q_regs<HD, kThreads>(qrows, lq16, itid);
-        else if constexpr (Q40) quantize_q_regs<HD, kThreads>(qrows, lq, lqsc, itid, lqsum);
-        else quantize_q_regs<HD, kThreads>(qrows, lq, lqsc, itid);
+        if constexpr (FP8) split_q_regs<HD, NT>(qrows, lq16, itid);
+        else if constexpr (Q40) quantize_q_regs<HD, NT>(qrows, lq, lqsc, itid, lqsum);
+        else quantize_q_regs<HD, NT>(qrows, lq, lqsc, itid);
         __syncthreads();
         // static grids: the tail wave quantises the new rows (which arrive
         // with its first tile) while its second tile is in flight, or here
@@ -1579,15 +1582,15 @@ q8kv_decode_kernel(const DecodeArgs a) {
         const size_t state0 = (((size_t)b * a.n_kv + kh) * a.n_parts + part) * G;
         const __amdgpu_buffer_rsrc_t racc = state_rsrc(a.st_acc + state0 * HD, (uint32_t)(G * HD * 4));
         const __amdgpu_buffer_rsrc_t rms = state_rsrc(a.st_ms + state0 * 2, (uint32_t)(G * 8));
-        for (int e4 = itid; e4 < G * Q4; e4 += kThreads) {
+        for (int e4 = itid; e4 < G * Q4; e4 += NT) {
             const int g = e4 / Q4, i4 = e4 % Q4;
             float Mx = -INFINITY;
 #pragma unroll
-            for (int w = 0; w < kWaves; ++w) Mx = fmaxf(Mx, lM[w][g]);
+            for (int w = 0; w < NW; ++w) Mx = fmaxf(Mx, lM[w][g]);
             float St = 0.0f;
             f32x4 at = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int w = 0; w < kWaves; ++w) {
+            for (int w = 0; w < NW; ++w) {
                 const float ew = __builtin_amdgcn_exp2f(lM[w][g] - Mx);
                 St += lS[w][g] * ew;
                 at += *reinterpret_cast<const f32x4*>(&lacc[w][g][4 * i4]) * ew;
@@ -1612,7 +1615,7 @@ q8kv_decode_kernel(const DecodeArgs a) {
                 lflag = last;
             }
             __syncthreads();
-            if (lflag) merge_group<HD>(a, b, kh, np_b, out_rows, itid, lms, lred);
+            if (lflag) merge_group<HD, NT>(a, b, kh, np_b, out_rows, itid, lms, lred);
         }
         // next item (the barrier also keeps LDS from being reused too early)
         if (STATIC || !a.ticket) break;
@@ -1953,11 +1956,12 @@ __device__ __forceinline__ float max_of_wave_sums8(const float (&t)[kHeadGroup],
 // (max_of_wave_sums8).  A wave issues the metadata loads of all its blocks
 // before it reduces any.
 constexpr int kQuestRun = 32;
+constexpr int kQuestWaves = 4;  // waves per bounds workgroup
 
 template <int HD>
-__global__ __launch_bounds__(256) void q8kv_quest_bounds_kernel(const QuestArgs a) {
+__global__ __launch_bounds__(kWave * kQuestWaves) void q8kv_quest_bounds_kernel(const QuestArgs a) {
     constexpr int EPL = HD / kWave;
-    constexpr int PW = kQuestRun / kWaves;  // blocks per wave
+    constexpr int PW = kQuestRun / kQuestWaves;  // blocks per wave
     __shared__ __attribute__((aligned(16))) float lqv[kHeadGroup][HD];
     const int lane = threadIdx.x & (kWave - 1);
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1977,7 +1981,7 @@ __global__ __launch_bounds__(256) void q8kv_quest_bounds_kernel(const QuestArgs 
     int bp[PW];
 #pragma unroll
     for (int w = 0; w < PW; ++w) {
-        const int j = min(j0 + wid + kWaves * w, j1 - 1);
+        const int j = min(j0 + wid + kQuestWaves * w, j1 - 1);
         bp[w] = a.table[(size_t)b * a.max_blocks + j];
         const int pc = (unsigned)bp[w] < (unsigned)a.num_blocks ? bp[w] : 0;
         const size_t m0 = ((size_t)pc * a.n_kv + kh) * HD + (size_t)lane * EPL;
@@ -1988,7 +1992,7 @@ __global__ __launch_bounds__(256) void q8kv_quest_bounds_kernel(const QuestArgs 
         }
     }
     // the kv head's query rows (rows past G repeat row G - 1) into LDS
-    for (int i = threadIdx.x; i < kHeadGroup * HD / 4; i += 256) {
+    for (int i = threadIdx.x; i < kHeadGroup * HD / 4; i += kWave * kQuestWaves) {
         const int g = i / (HD / 4), c4 = i % (HD / 4);
         const float* qh = a.q + ((size_t)b * a.n_q + (size_t)kh * G + min(g, G - 1)) * HD;
         *reinterpret_cast<f32x4*>(&lqv[g][4 * c4]) = *reinterpret_cast<const f32x4*>(qh + 4 * c4);
@@ -2005,7 +2009,7 @@ __global__ __launch_bounds__(256) void q8kv_quest_bounds_kernel(const QuestArgs 
     }
 #pragma unroll
     for (int w = 0; w < PW; ++w) {
-        const int j = j0 + wid + kWaves * w;
+        const int j = j0 + wid + kQuestWaves * w;
         if (j >= j1) break;  // wave-uniform
         const int p = bp[w];
         float u;
@@ -2438,8 +2442,10 @@ struct LaunchInfo {
     int cus = 0;          // compute units
     int resident = 0;     // persistent-grid workgroups that fit at once
     int static_lds = 0;   // dynamic LDS that keeps a static grid at two workgroups per CU
+    int wide_lds = 0;     // dynamic LDS that keeps a wide static grid at one workgroup per CU
 };
-std::map<std::pair<int, int>, LaunchInfo> g_launch;  // (device, hd * 2 + fused append)
+std::map<std::pair<int, int>, LaunchInfo> g_launch;  // (device, hd * 4 + kernel variant)
+std::atomic<int> g_wide{1};  // wide workgroups allowed (a test export turns them off)
 
 bool valid_hd(int hd) { return hd == 64 || hd == 128 || hd == 256; }
 bool valid_kv_bs(int bs) { return bs == 16 || bs == 32 || bs == 64 || bs == 128 || bs == 256; }
@@ -2483,10 +2489,16 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 // append of the new token, the FP8 codec.
 enum Variant { kVarQ8 = 0, kVarQ8New = 1, kVarFp8 = 2, kVarQ40 = 3 };
 
-template <int HD, int VAR, int MODE>
+template <int HD, int VAR, int MODE, int NW = kWaves>
 constexpr auto decode_kernel_ptr() {
-    return q8kv_decode_kernel<HD, MODE, VAR == kVarQ8New, VAR == kVarFp8 ? kFp8 : VAR == kVarQ40 ? kQ40 : kQ8>;
+    return q8kv_decode_kernel<HD, MODE, VAR == kVarQ8New, VAR == kVarFp8 ? kFp8 : VAR == kVarQ40 ? kQ40 : kQ8, NW>;
 }
+
+// Wide (kWideWaves) workgroups serve static grids of at most one workgroup
+// per CU at hd 64 and 128: with 4 waves such a grid leaves one wave per SIMD,
+// too few loads in flight to cover the memory latency.  (At hd 256 the wave
+// keeps a whole register file, so 8 waves would not fit on a CU.)
+constexpr bool wide_hd(int hd) { return hd <= 128; }
 
 template <int HD, int VAR>
 int launch_info_hd(int dev, LaunchInfo& li) {
@@ -2506,6 +2518,15 @@ int launch_info_hd(int dev, LaunchInfo& li) {
     const int need = (lds_cu / 3 + 256) / 256 * 256;
     const int dyn = need - (int)fa.sharedSizeBytes;
     li.static_lds = (dyn > 0 && need <= 65536) ? dyn : 0;
+    if constexpr (wide_hd(HD)) {
+        // a wide workgroup asks for just over half of the CU's LDS, so that
+        // the dispatcher cannot stack two on one CU
+        e = hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(decode_kernel_ptr<HD, VAR, kStatic, kWideWaves>()));
+        if (e != hipSuccess) return hip_fail(e, "hipFuncGetAttributes");
+        const int need_w = (lds_cu / 2 + 256) / 256 * 256;
+        const int dyn_w = need_w - (int)fa.sharedSizeBytes;
+        li.wide_lds = (dyn_w > 0 && dyn_w <= 65536) ? dyn_w : 0;
+    }
     return Q8KV_OK;
 }
 
@@ -2535,23 +2556,34 @@ int launch_info(int dev, int hd, int var, LaunchInfo* out) {
 }
 
 template <int HD, int VAR>
-void launch_decode_hd(int mode, unsigned grid, size_t lds, hipStream_t st, const DecodeArgs& da) {
-    if (mode == kPersistent) hipLaunchKernelGGL((decode_kernel_ptr<HD, VAR, kPersistent>()), dim3(grid), dim3(kThreads), 0, st, da);
-    else hipLaunchKernelGGL((decode_kernel_ptr<HD, VAR, kStatic>()), dim3(grid), dim3(kThreads), lds, st, da);
+void launch_decode_hd(int mode, bool wide, unsigned grid, size_t lds, hipStream_t st, const DecodeArgs& da) {
+    if (mode == kPersistent) {
+        hipLaunchKernelGGL((decode_kernel_ptr<HD, VAR, kPersistent>()), dim3(grid), dim3(kThreads), 0, st, da);
+        return;
+    }
+    if constexpr (wide_hd(HD)) {
+        if (wide) {
+            hipLaunchKernelGGL((decode_kernel_ptr<HD, VAR, kStatic, kWideWaves>()), dim3(grid), dim3(kWave * kWideWaves),
+                               lds, st, da);
+            return;
+        }
+    }
+    hipLaunchKernelGGL((decode_kernel_ptr<HD, VAR, kStatic>()), dim3(grid), dim3(kThreads), lds, st, da);
 }
 
 template <int VAR>
-void launch_decode_var(int hd, int mode, unsigned grid, size_t lds, hipStream_t st, const DecodeArgs& da) {
-    if (hd == 64) launch_decode_hd<64, VAR>(mode, grid, lds, st, da);
-    else if (hd == 128) launch_decode_hd<128, VAR>(mode, grid, lds, st, da);
-    else launch_decode_hd<256, VAR>(mode, grid, lds, st, da);
+void launch_decode_var(int hd, int mode, bool wide, unsigned grid, size_t lds, hipStream_t st, const DecodeArgs& da) {
+    if (hd == 64) launch_decode_hd<64, VAR>(mode, wide, grid, lds, st, da);
+    else if (hd == 128) launch_decode_hd<128, VAR>(mode, wide, grid, lds, st, da);
+    else launch_decode_hd<256, VAR>(mode, wide, grid, lds, st, da);
 }
 
-void launch_decode(int hd, int var, int mode, unsigned grid, size_t lds, hipStream_t st, const DecodeArgs& da) {
-    if (var == kVarQ8New) launch_decode_var<kVarQ8New>(hd, mode, grid, lds, st, da);
-    else if (var == kVarFp8) launch_decode_var<kVarFp8>(hd, mode, grid, lds, st, da);
-    else if (var == kVarQ40) launch_decode_var<kVarQ40>(hd, mode, grid, lds, st, da);
-    else launch_decode_var<kVarQ8>(hd, mode, grid, lds, st, da);
+void launch_decode(int hd, int var, int mode, bool wide, unsigned grid, size_t lds, hipStream_t st,
+                   const DecodeArgs& da) {
+    if (var == kVarQ8New) launch_decode_var<kVarQ8New>(hd, mode, wide, grid, lds, st, da);
+    else if (var == kVarFp8) launch_decode_var<kVarFp8>(hd, mode, wide, grid, lds, st, da);
+    else if (var == kVarQ40) launch_decode_var<kVarQ40>(hd, mode, wide, grid, lds, st, da);
+    else launch_decode_var<kVarQ8>(hd, mode, wide, grid, lds, st, da);
 }
 
 int decode_impl(float* out, const float* q, const int8_t* kp, const int8_t* vp, const float* ks,
@@ -2643,9 +2675,14 @@ int decode_impl(float* out, const float* q, const int8_t* kp, const int8_t* vp, 
         da.st_acc = static_cast<float*>(w.ptr);
         da.st_ms = reinterpret_cast<float*>(static_cast<char*>(w.ptr) + acc_bytes);
     }
+    // every item in its own workgroup: static grid (two per CU at most when
+    // that is enough; wide workgroups when one per CU is)
+    const int mode = items > (long long)grid ? kPersistent : kStatic;
+    const bool wide = mode == kStatic && wide_hd(hd) && grid <= (unsigned)li.cus && g_wide.load() != 0;
+    const int nt = wide ? kWave * kWideWaves : kThreads;
     // small groups of partition states are merged inside the decode kernel
     const int slices = G * hd / 4;
-    const int rows_par = slices >= kThreads ? 1 : kThreads / slices;
+    const int rows_par = slices >= nt ? 1 : nt / slices;
     const bool fuse = np > 1 && np * G <= kFuseRows && (np + rows_par - 1) / rows_par <= kFusePer;
     if (fuse) {
         const size_t need = (size_t)batch * n_kv;
@@ -2673,11 +2710,9 @@ int decode_impl(float* out, const float* q, const int8_t* kp, const int8_t* vp, 
         }
         da.arrive = w.arrive;
     }
-    // every item in its own workgroup: static grid (two per CU at most when
-    // that is enough)
-    const int mode = items > (long long)grid ? kPersistent : kStatic;
-    const size_t lds = mode == kStatic && grid <= 2u * (unsigned)li.cus ? (size_t)li.static_lds : 0;
-    launch_decode(hd, var, mode, grid, lds, st, da);
+    const size_t lds = wide ? (size_t)li.wide_lds
+                       : mode == kStatic && grid <= 2u * (unsigned)li.cus ? (size_t)li.static_lds : 0;
+    launch_decode(hd, var, mode, wide, grid, lds, st, da);
     e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
     if (np > 1 && !fuse) {
@@ -2941,9 +2976,9 @@ int q8kv_quest_select(int32_t* sel_table, int32_t* sel_lens, const float* q, con
                  kv_bs, top_k};
     const unsigned grid = (unsigned)((long long)batch * n_kv_heads * ((max_blocks_per_seq + kQuestRun - 1) / kQuestRun));
     switch (hd) {
-        case 64: hipLaunchKernelGGL(q8kv_quest_bounds_kernel<64>, dim3(grid), dim3(256), 0, st, qa); break;
-        case 128: hipLaunchKernelGGL(q8kv_quest_bounds_kernel<128>, dim3(grid), dim3(256), 0, st, qa); break;
-        default: hipLaunchKernelGGL(q8kv_quest_bounds_kernel<256>, dim3(grid), dim3(256), 0, st, qa); break;
+        case 64: hipLaunchKernelGGL(q8kv_quest_bounds_kernel<64>, dim3(grid), dim3(kWave * kQuestWaves), 0, st, qa); break;
+        case 128: hipLaunchKernelGGL(q8kv_quest_bounds_kernel<128>, dim3(grid), dim3(kWave * kQuestWaves), 0, st, qa); break;
+        default: hipLaunchKernelGGL(q8kv_quest_bounds_kernel<256>, dim3(grid), dim3(kWave * kQuestWaves), 0, st, qa); break;
     }
     e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "bounds kernel launch");
@@ -3016,6 +3051,13 @@ int q8kv_debug_block_dots(int32_t* dots, int max_tok, const float* q, const int8
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "dots kernel launch");
+    return Q8KV_OK;
+}
+
+int q8kv_debug_set_wide(int enable) {
+    g_err.clear();
+    if (enable != 0 && enable != 1) return fail(Q8KV_EINVAL, "enable must be 0 or 1 (got %d)", enable);
+    g_wide.store(enable);
     return Q8KV_OK;
 }
 

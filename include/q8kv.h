@@ -350,6 +350,17 @@ int q8kv_debug_block_dots(int32_t* dots, int max_tok, const float* q, const int8
                           int n_kv_heads, int hd, int kv_bs, void* stream);
 
 /*
+ * Test export: enable (1, the default) or disable (0) the 8-wave workgroups
+ * that the decode entry points use for a static grid of at most one
+ * workgroup per CU at hd 64 and 128.  With 0 such grids run the 4-wave
+ * kernel, as larger grids do, so that tests can compare the two.  Applies to
+ * every later call in the process; Q8KV_EINVAL for other values.  The two
+ * kernels merge their waves' states in different orders, so their outputs
+ * agree to rounding, not bit for bit.
+ */
+int q8kv_debug_set_wide(int enable);
+
+/*
  * Measurement export: read a_bytes of device buffer a and b_bytes of device
  * buffer b (both multiples of 16) in one launch with plain linear
  * non-temporal loads and discard the data.  A benchmark times it over a

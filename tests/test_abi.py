@@ -14,7 +14,7 @@ NUL = ctypes.c_void_p(0)
 
 def test_exports_every_declared_symbol():
     names = q8.header_symbols()
-    assert len(names) == 17
+    assert len(names) == 18
     for n in names:
         assert hasattr(L, n), n
 
@@ -156,6 +156,13 @@ def test_debug_exports_reject():
     assert L.q8kv_debug_quantize_q(FAKE, FAKE, FAKE, 0, 128, NUL) == q8.Q8KV_OK
     assert L.q8kv_debug_block_dots(FAKE, 4, FAKE, FAKE, FAKE, FAKE, 4, 8, 1, 3, 2, 128, 16, NUL) == q8.Q8KV_EINVAL
     assert L.q8kv_debug_block_dots(NUL, 4, FAKE, FAKE, FAKE, FAKE, 4, 8, 1, 2, 2, 128, 16, NUL) == q8.Q8KV_ENULL
+
+
+def test_set_wide_accepts_only_0_and_1():
+    assert L.q8kv_debug_set_wide(2) == q8.Q8KV_EINVAL
+    assert L.q8kv_debug_set_wide(-1) == q8.Q8KV_EINVAL
+    assert L.q8kv_debug_set_wide(0) == q8.Q8KV_OK
+    assert L.q8kv_debug_set_wide(1) == q8.Q8KV_OK  # the default again
 
 
 def test_stream_read_rejects():
