@@ -7,8 +7,9 @@
 // that rescales the int8-V accumulator whenever the max grows, divide once at
 // the end.  Here it is laid out for CDNA4 matrix cores:
 //
-//   * one workgroup (4 waves) owns (sequence b, kv head kh, token partition);
-//     the G = n_q / n_kv query heads of kh share every K/V byte it loads;
+//   * one workgroup (4 waves; 8 for a static grid of one workgroup per CU)
+//     owns (sequence b, kv head kh, token partition); the G = n_q / n_kv
+//     query heads of kh share every K/V byte it loads;
 //   * a wave walks tiles of 32 tokens.  Q.K^T runs on v_mfma_i32_16x16x64_i8
 //     with A = 16 K rows x 64 bytes (two 32-blocks) and B = the quantised
 //     queries: columns 0-7 carry head g's even block with zeros under the odd
