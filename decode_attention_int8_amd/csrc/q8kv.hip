@@ -589,9 +589,14 @@ __device__ __forceinline__ int uniform_read(const int32_t* p, int idx) {
 // Physical blocks of the two sub-tiles of the tile at token ts (the table
 // index is clamped into the row, so the read is always in bounds; an entry
 // is only used when its sub-tile holds valid tokens).
+// kv_bs is a power of two (checked on the host), so token positions split
+// into (block, row) with a shift and a mask.
+__device__ __forceinline__ int log2_pow2(int x) { return 31 - __builtin_clz(x); }
+
 __device__ __forceinline__ void tile_blocks(const int32_t* trow, int ts, int kv_bs, int max_blocks, int (&blk)[2]) {
-    blk[0] = uniform_read(trow, min(ts / kv_bs, max_blocks - 1));
-    blk[1] = uniform_read(trow, min((ts + kSub) / kv_bs, max_blocks - 1));
+    const int sh = log2_pow2(kv_bs);
+    blk[0] = uniform_read(trow, min(ts >> sh, max_blocks - 1));
+    blk[1] = uniform_read(trow, min((ts + kSub) >> sh, max_blocks - 1));
 }
 
 template <int HD>
@@ -606,7 +611,7 @@ __device__ __forceinline__ void tile_load(Tile<HD>& T, const DecodeArgs& a, cons
             bad = true;
             blk = 0;
         }
-        const size_t base = ((size_t)blk * a.n_kv + kh) * a.kv_bs + (size_t)(tst % a.kv_bs);
+        const size_t base = (((size_t)blk * a.n_kv + kh) << log2_pow2(a.kv_bs)) + (size_t)(tst & (a.kv_bs - 1));
         T.ks[st] = stream_load<f32x4>(a.ks + base + 4 * (lane >> 4));
         T.vs[st] = stream_load<f32x4>(a.vs + base + 4 * (lane >> 4));
         load_k_subtile<HD>(T.k[st], a.kp, base, lane);
@@ -878,7 +883,7 @@ __device__ __forceinline__ void fp8_tile_load(Fp8Tile<HD>& T, const DecodeArgs& 
             bad = true;
             blk = 0;
         }
-        const size_t base = ((size_t)blk * a.n_kv + kh) * a.kv_bs + (size_t)(tst % a.kv_bs);
+        const size_t base = (((size_t)blk * a.n_kv + kh) << log2_pow2(a.kv_bs)) + (size_t)(tst & (a.kv_bs - 1));
         load_scale_bytes<NB>(T.ke[st], a.ks8 + (base + 4 * (lane >> 4)) * NB);
         load_scale_bytes<NB>(T.ve[st], a.vs8 + (base + 4 * (lane >> 4)) * NB);
         load_k_subtile<HD>(T.k[st], a.kp, base, lane);
@@ -1094,7 +1099,7 @@ __device__ __forceinline__ void q4_tile_load(Q4Tile<HD>& T, const DecodeArgs& a,
             bad = true;
             blk = 0;
         }
-        const size_t base = ((size_t)blk * a.n_kv + kh) * a.kv_bs + (size_t)(tst % a.kv_bs);
+        const size_t base = (((size_t)blk * a.n_kv + kh) << log2_pow2(a.kv_bs)) + (size_t)(tst & (a.kv_bs - 1));
         const size_t srow = (base + 4 * (lane >> 4)) * QG::NB * 2;  // byte offset of row 4r's scales
         load_dwords<QG::SCW>(T.kd[st], a.ks8 + srow);
         load_dwords<QG::SCW>(T.vd[st], a.vs8 + srow);
