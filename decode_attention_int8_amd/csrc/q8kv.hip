@@ -1851,14 +1851,17 @@ template <int HD>
 __global__ __launch_bounds__(256) void q8kv_quest_metadata_kernel(const QuestArgs a) {
     constexpr int NPAIR = Geo<HD>::NPAIR;
     const int lane = threadIdx.x & (kWave - 1);
-    const long long wave = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const long long wave = (long long)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (wave >= (long long)a.batch * a.max_blocks * a.n_kv) return;
     const int kh = (int)(wave % a.n_kv);
     const int j = (int)((wave / a.n_kv) % a.max_blocks);
     const int b = (int)(wave / ((long long)a.n_kv * a.max_blocks));
-    const int L = min(a.lens[b], a.max_blocks * a.kv_bs);
+    // the length and the table entry are read together (j < max_blocks, so
+    // the entry is inside the table whether or not the block is in use)
+    const int len = uniform_read(a.lens, b);
+    const int p = uniform_read(a.table + (size_t)b * a.max_blocks, j);
+    const int L = min(len, a.max_blocks * a.kv_bs);
     if (j * a.kv_bs >= L) return;
-    const int p = a.table[(size_t)b * a.max_blocks + j];
     if ((unsigned)p >= (unsigned)a.num_blocks) return;
     const int rows = min(a.kv_bs, L - j * a.kv_bs);
     const int n = lane & 15, r = lane >> 4;
@@ -1872,14 +1875,24 @@ __global__ __launch_bounds__(256) void q8kv_quest_metadata_kernel(const QuestArg
         }
     }
     const size_t page_row = ((size_t)p * a.n_kv + kh) * a.kv_bs;
+    // rows past the sequence's length (only in its last sub-tile) read the
+    // last valid row again: a repeat changes no maximum or minimum.  The next
+    // sub-tile's loads go out before the current one is reduced.
+    i32x4 ch[NPAIR];
+    int rn = min(n, rows - 1);
+    float sc = a.ks[page_row + rn];
+    load_k_subtile<HD>(ch, a.kp, page_row, 16 * r + rn);
     for (int r0 = 0; r0 < rows; r0 += kSub) {
-        // rows past the sequence's length (only in its last sub-tile) read
-        // the last valid row again: a repeat changes no maximum or minimum
-        const int rn = min(n, rows - 1 - r0);
-        const float sc = a.ks[page_row + r0 + rn];
-        const float off = -128.0f * sc;  // exact
-        i32x4 ch[NPAIR];
-        load_k_subtile<HD>(ch, a.kp, page_row + r0, 16 * r + rn);
+        i32x4 cu[NPAIR];
+#pragma unroll
+        for (int c = 0; c < NPAIR; ++c) cu[c] = ch[c];
+        const float sc_cur = sc;
+        if (r0 + kSub < rows) {
+            rn = min(n, rows - 1 - (r0 + kSub));
+            sc = a.ks[page_row + r0 + kSub + rn];
+            load_k_subtile<HD>(ch, a.kp, page_row + r0 + kSub, 16 * r + rn);
+        }
+        const float off = -128.0f * sc_cur;  // exact
         // code * sc as fma(code + 128, sc, -128 sc): the byte with its sign
         // bit flipped converts to code + 128 in one instruction, and the
         // fused result rounds the exact product once, as the product does
@@ -1887,8 +1900,8 @@ __global__ __launch_bounds__(256) void q8kv_quest_metadata_kernel(const QuestArg
         for (int c = 0; c < NPAIR; ++c) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const uint32_t u = ((uint32_t)ch[c][i >> 2] ^ 0x80808080u) >> (8 * (i & 3));
-                const float v = __builtin_fmaf((float)(uint8_t)u, sc, off);
+                const uint32_t u = ((uint32_t)cu[c][i >> 2] ^ 0x80808080u) >> (8 * (i & 3));
+                const float v = __builtin_fmaf((float)(uint8_t)u, sc_cur, off);
                 mx[c][i] = fmaxf(mx[c][i], v);
                 mn[c][i] = fminf(mn[c][i], v);
             }
