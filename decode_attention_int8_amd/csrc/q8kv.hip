@@ -1824,29 +1824,40 @@ struct QuestArgs {
     int batch, max_blocks, num_blocks, n_q, n_kv, kv_bs, top_k;
 };
 
-// Inclusive max / min over the 16 lanes of a DPP row; lane 15 of the row
-// ends with the row's value.
-__device__ __forceinline__ float row16_max(float x) {
-    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), 0x111, 0xf, 0xf, false)));
-    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), 0x112, 0xf, 0xf, false)));
-    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), 0x114, 0xf, 0xf, false)));
-    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), 0x118, 0xf, 0xf, false)));
-    return x;
+// A DPP row of 16 lanes holds 16 values per lane, lane n's slot s carrying
+// column s ^ n.  Four exchange steps leave lane n with column n's maximum
+// (minimum) over the row: partner lanes n ^ 8 (row rotation by 8), n ^ 7
+// (half-row mirror), n ^ 2 and n ^ 1 (quad permutations).  With that
+// layout the partner holds the lane's column s in slot s ^ x, so each step
+// combines slot s with the partner's slot s ^ x and keeps the lower half:
+// 8 + 4 + 2 + 1 operations instead of 4 per value.
+template <bool MAX>
+__device__ __forceinline__ float dpp_combine(float x, float y_from_partner) {
+    return MAX ? fmaxf(x, y_from_partner) : fminf(x, y_from_partner);
 }
-__device__ __forceinline__ float row16_min(float x) {
-    x = fminf(x, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), 0x111, 0xf, 0xf, false)));
-    x = fminf(x, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), 0x112, 0xf, 0xf, false)));
-    x = fminf(x, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), 0x114, 0xf, 0xf, false)));
-    x = fminf(x, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), 0x118, 0xf, 0xf, false)));
-    return x;
+template <int CTRL>
+__device__ __forceinline__ float dpp_take(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+template <bool MAX>
+__device__ __forceinline__ float row16_reduce_xor(float (&v)[16]) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) v[s] = dpp_combine<MAX>(v[s], dpp_take<0x128>(v[s ^ 8]));  // row_ror:8
+#pragma unroll
+    for (int s = 0; s < 4; ++s) v[s] = dpp_combine<MAX>(v[s], dpp_take<0x141>(v[s ^ 7]));  // row_half_mirror
+#pragma unroll
+    for (int s = 0; s < 2; ++s) v[s] = dpp_combine<MAX>(v[s], dpp_take<0x4e>(v[s ^ 2]));   // quad_perm 2,3,0,1
+    return dpp_combine<MAX>(v[0], dpp_take<0xb1>(v[1]));                                     // quad_perm 1,0,3,2
 }
 
 // Metadata: one wave per (sequence, logical block, kv head).  The wave reads
 // the page's 16-row sub-tiles (lane 16 r + n: row n, columns 64 c + 16 r ..
-// +16 of chunk c), dequantises each element as float(code) * k_scale of its
-// row, keeps running maxima and minima per column over its rows (rows past
-// the sequence's length are skipped), reduces them over the 16 rows of a DPP
-// row, and lane 15 of each row writes its 16 columns.
+// +16 of chunk c), puts column 64 c + 16 r + (s ^ n) in slot s (a dword
+// exchange and a byte permute per dword), dequantises each element as
+// float(code) * k_scale of its row, keeps running maxima and minima per slot
+// over its rows (rows past the sequence's length are skipped), reduces them
+// over the 16 rows of a DPP row (row16_reduce_xor), and lane n of each row
+// writes column 64 c + 16 r + n.
 template <int HD>
 __global__ __launch_bounds__(256) void q8kv_quest_metadata_kernel(const QuestArgs a) {
     constexpr int NPAIR = Geo<HD>::NPAIR;
@@ -1865,6 +1876,8 @@ __global__ __launch_bounds__(256) void q8kv_quest_metadata_kernel(const QuestArg
     if ((unsigned)p >= (unsigned)a.num_blocks) return;
     const int rows = min(a.kv_bs, L - j * a.kv_bs);
     const int n = lane & 15, r = lane >> 4;
+    const uint32_t bsel = 0x03020100u ^ ((uint32_t)(n & 3) * 0x01010101u);  // byte e <- byte e ^ (n & 3)
+    const bool dx1 = (n & 4) != 0, dx2 = (n & 8) != 0;                         // dword D <- dword D ^ (n >> 2)
     float mx[NPAIR][16], mn[NPAIR][16];
 #pragma unroll
     for (int c = 0; c < NPAIR; ++c) {
@@ -1883,9 +1896,15 @@ __global__ __launch_bounds__(256) void q8kv_quest_metadata_kernel(const QuestArg
     float sc = a.ks[page_row + rn];
     load_k_subtile<HD>(ch, a.kp, page_row, 16 * r + rn);
     for (int r0 = 0; r0 < rows; r0 += kSub) {
-        i32x4 cu[NPAIR];
+        uint32_t cu[NPAIR][4];
 #pragma unroll
-        for (int c = 0; c < NPAIR; ++c) cu[c] = ch[c];
+        for (int c = 0; c < NPAIR; ++c) {
+            uint32_t t[4];
+#pragma unroll
+            for (int d = 0; d < 4; ++d) t[d] = dx1 ? (uint32_t)ch[c][d ^ 1] : (uint32_t)ch[c][d];
+#pragma unroll
+            for (int d = 0; d < 4; ++d) cu[c][d] = __builtin_amdgcn_perm(0u, dx2 ? t[d ^ 2] : t[d], bsel);
+        }
         const float sc_cur = sc;
         if (r0 + kSub < rows) {
             rn = min(n, rows - 1 - (r0 + kSub));
@@ -1900,7 +1919,7 @@ __global__ __launch_bounds__(256) void q8kv_quest_metadata_kernel(const QuestArg
         for (int c = 0; c < NPAIR; ++c) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const uint32_t u = ((uint32_t)cu[c][i >> 2] ^ 0x80808080u) >> (8 * (i & 3));
+                const uint32_t u = (cu[c][i >> 2] ^ 0x80808080u) >> (8 * (i & 3));
                 const float v = __builtin_fmaf((float)(uint8_t)u, sc_cur, off);
                 mx[c][i] = fmaxf(mx[c][i], v);
                 mn[c][i] = fminf(mn[c][i], v);
@@ -1910,19 +1929,10 @@ __global__ __launch_bounds__(256) void q8kv_quest_metadata_kernel(const QuestArg
     const size_t out = ((size_t)p * a.n_kv + kh) * HD;
 #pragma unroll
     for (int c = 0; c < NPAIR; ++c) {
-        f32x4 vx[4], vn[4];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            vx[i >> 2][i & 3] = row16_max(mx[c][i]);
-            vn[i >> 2][i & 3] = row16_min(mn[c][i]);
-        }
-        if (n == 15) {
-#pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4) {
-                *reinterpret_cast<f32x4*>(a.kmax + out + 64 * c + 16 * r + 4 * i4) = vx[i4];
-                *reinterpret_cast<f32x4*>(a.kmin + out + 64 * c + 16 * r + 4 * i4) = vn[i4];
-            }
-        }
+        const float vx = row16_reduce_xor<true>(mx[c]);
+        const float vn = row16_reduce_xor<false>(mn[c]);
+        a.kmax[out + 64 * c + 16 * r + n] = vx;
+        a.kmin[out + 64 * c + 16 * r + n] = vn;
     }
 }
 
