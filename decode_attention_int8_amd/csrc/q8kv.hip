@@ -1855,7 +1855,7 @@ __device__ __forceinline__ float row16_reduce_xor(float (&v)[16]) {
 // +16 of chunk c), puts column 64 c + 16 r + (s ^ n) in slot s (a dword
 // exchange and a byte permute per dword), dequantises each element as
 // float(code) * k_scale of its row, keeps running maxima and minima per slot
-// over its rows (rows past the sequence's length are skipped), reduces them
+// over its rows (rows past the sequence's length repeat its last row), reduces them
 // over the 16 rows of a DPP row (row16_reduce_xor), and lane n of each row
 // writes column 64 c + 16 r + n.
 template <int HD>
