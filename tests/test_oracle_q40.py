@@ -7,6 +7,17 @@
   where the top code saturates at 15); an all-zero block is code 8 with
   d = 0; a block made of exact multiples (c - 8) * d of an fp16-exact d
   returns its codes; negating a block keeps d's magnitude.
+* The rounding of the code (reading of llama.cpp's q4_0 rule): x * id and
+  + 8.5 are two fp32 roundings and the sum is truncated.  Elements whose
+  x * id is exactly a half step (k + 1/2, with d a power of two) take the
+  codes written out by hand below (trunc(k + 9) = k + 9; rounding x * id to
+  nearest even, then adding 8, gives k + 8 for even k); elements whose
+  exact x * id + 8.5 lies within half an ulp of an integer (found by an
+  exact-rational search) take the code of the two roundings, which differs
+  there from a single fused rounding.  Both are checked against the rule
+  evaluated in exact rational arithmetic, and a battery of planted mistakes
+  (round-half-even, a fused multiply-add, no clamp at 15, the scale's sign,
+  ties to the last element) must each fail one of these pins.
 * Decode: a cache whose rows use one fp16-exact scale for all their blocks is
   the same attention as an int8 cache with codes c - 8 and that scale, so
   the q4_0 decode must equal the independent three-pass fp64 reference of
@@ -14,13 +25,16 @@
   dequantised V row; a zero query gives the mean of the dequantised rows;
   Decimal brute force on a tiny case.
 """
+import math
 from decimal import Decimal, getcontext
+from fractions import Fraction
 
 import numpy as np
 import pytest
 
 import oracle
 from oracle import q40
+from test_oracle_quant import F, f32_round
 
 
 @pytest.mark.parametrize("seed", range(6))
@@ -153,3 +167,157 @@ def test_decode_decimal_brute_force():
         vv = [(int(c4.v_codes[0, 0, t, i]) - 8) * Decimal(float(c4.v_d[0, 0, t, i // 32])) for t in range(6)]
         ref = sum(w[t] * vv[t] for t in range(6)) / W
         assert abs(float(ref) - out[0, 0, i]) < 1e-13
+
+
+# ---------------------------------------------------------------------------
+# the code's rounding
+
+def exact_q40_block(xs, fused=False):
+    """The q4_0 rule in exact rational arithmetic, one fp32 rounding per
+    operation: m = the first element of largest magnitude, d = rn(m / -8),
+    id = rn(1 / d) (0 for d = 0), code = min(15, trunc(rn(rn(x id) + 17/2)))
+    -- or, with fused, a single rounding of x id + 17/2.  The sum is at
+    least 1/2, so truncation is the floor."""
+    a, m = Fraction(0), Fraction(0)
+    for x in xs:
+        if abs(F(x)) > a:
+            a, m = abs(F(x)), F(x)
+    d = f32_round(m / -8)
+    idv = f32_round(1 / d) if d != 0 else Fraction(0)
+    codes = []
+    for x in xs:
+        y = F(x) * idv
+        y = f32_round(y + Fraction(17, 2)) if fused else f32_round(f32_round(y) + Fraction(17, 2))
+        codes.append(min(15, math.floor(y)))
+    return codes, d
+
+
+# (x, code) with d = 1: x * id = x exactly; code = trunc(x + 8.5), written out
+HALF_STEPS = [(-8.0, 0), (0.5, 9), (2.5, 11), (4.5, 13), (6.5, 15), (-1.5, 7), (-3.5, 5), (-5.5, 3),
+              (-7.5, 1), (1.5, 10), (3.5, 12), (-0.5, 8), (-2.5, 6), (0.0, 8), (7.5, 15), (-6.5, 2)]
+
+
+def half_step_blocks():
+    xs = np.zeros(32, np.float32)
+    want = np.full(32, 8, np.uint8)
+    for i, (x, c) in enumerate(HALF_STEPS):
+        xs[i], want[i] = x, c
+    for k in (0, -20, -3, 5, 20):   # d = 2^k: the same codes
+        yield (xs * np.float32(2.0 ** k)).astype(np.float32), want
+
+
+def test_half_steps_truncate():
+    for xs, want in half_step_blocks():
+        codes, d16 = q40.quantize_block(xs)
+        assert np.array_equal(codes, want), (xs[:4], codes[:16], want[:16])
+        assert list(want) == exact_q40_block(xs)[0]
+
+
+def two_rounding_blocks(n=4):
+    """Blocks in which x * id + 8.5 falls where the two fp32 roundings and
+    a fused one disagree: x * id just past -1/2 - 2^-22 (so x * id rounds to
+    exactly -1/2 - 2^-22 and the sum to the tie 8 - 2^-22, which goes to the
+    even 8, while the exact sum rounds down to 8 - 2^-21).  Found by an
+    exact-rational search over seeded block maxima."""
+    rng = np.random.default_rng(2024)
+    target = -Fraction(1, 2) - Fraction(17, 4) * Fraction(1, 2 ** 24)
+    found = []
+    while len(found) < n:
+        m = np.float32(-rng.uniform(1.0, 8.0) * 2.0 ** int(rng.integers(-6, 7)))
+        d = f32_round(F(m) / -8)
+        idv = f32_round(1 / d)
+        x0 = np.float32(float(target / idv))
+        for cand in (x0, np.nextafter(x0, np.float32(-np.inf)), np.nextafter(x0, np.float32(np.inf))):
+            xs = np.zeros(32, np.float32)
+            xs[0], xs[1 + len(found) % 31] = m, cand
+            two, _ = exact_q40_block(xs)
+            fused, _ = exact_q40_block(xs, fused=True)
+            if two != fused:
+                found.append((xs, two))
+                break
+    return found
+
+
+def test_two_roundings_not_fused():
+    blocks = two_rounding_blocks()
+    assert len(blocks) == 4
+    for xs, want in blocks:
+        codes, _ = q40.quantize_block(xs)
+        assert list(codes) == want
+        rows, _ = q40.quantize_rows(xs[None])
+        assert list(rows[0]) == want
+
+
+def test_rule_exact_on_random_blocks():
+    """The oracle's codes and scales equal the rule evaluated exactly, on
+    random blocks of several magnitudes (scale: fp16 of the exact d)."""
+    rng = np.random.default_rng(77)
+    for scale in (1.0, 3e-4, 250.0):
+        for _ in range(20):
+            xs = (rng.standard_normal(32) * scale).astype(np.float32)
+            codes, d16 = q40.quantize_block(xs)
+            want, d = exact_q40_block(xs)
+            assert list(codes) == want and d16 == np.float16(float(d))
+
+
+# planted mistakes in the quantiser; each must fail one of the pins above
+
+def _mutant(kind):
+    def block(x):
+        x = np.asarray(x, np.float32)
+        amax, m = np.float32(0), np.float32(0)
+        for v in x:
+            if abs(v) > amax or (kind == "ties_last" and abs(v) == amax and amax > 0):
+                amax, m = np.float32(abs(v)), v
+        d = np.float32(m / np.float32(8.0 if kind == "d_sign" else -8.0))
+        idv = np.float32(1.0) / d if d != 0 else np.float32(0.0)
+        codes = np.empty(32, np.uint8)
+        for i, v in enumerate(x):
+            if kind == "round_half_even":
+                c = int(np.rint(np.float32(v * idv))) + 8
+            elif kind == "fused":
+                c = math.floor(f32_round(F(v) * F(idv) + Fraction(17, 2)))
+            else:
+                c = int(np.float32(np.float32(v * idv) + np.float32(8.5)))
+            codes[i] = c if kind == "no_clamp" else min(15, c)
+        return codes, np.float16(d)
+
+    def rows(x):
+        x = np.asarray(x, np.float32)
+        n = x.shape[-1]
+        flat = x.reshape(-1, n)
+        codes = np.empty(flat.shape, np.uint8)
+        d16 = np.empty((flat.shape[0], n // 32), np.float16)
+        for r in range(flat.shape[0]):
+            for b in range(n // 32):
+                codes[r, 32 * b:32 * b + 32], d16[r, b] = block(flat[r, 32 * b:32 * b + 32])
+        return codes.reshape(x.shape), d16.reshape(x.shape[:-1] + (n // 32,))
+    return block, rows
+
+
+PINS = [lambda: test_block_properties(0), test_zero_block_and_exact_multiples, test_ties_take_the_first_largest,
+        test_half_steps_truncate, test_two_roundings_not_fused, test_rule_exact_on_random_blocks]
+
+
+@pytest.mark.parametrize("kind", ["round_half_even", "fused", "no_clamp", "d_sign", "ties_last"])
+def test_mutants_fail_a_pin(kind, monkeypatch):
+    block, rows = _mutant(kind)
+    monkeypatch.setattr(q40, "quantize_block", block)
+    monkeypatch.setattr(q40, "quantize_rows", rows)
+    failed = []
+    for pin in PINS:
+        try:
+            pin()
+        except (AssertionError, OverflowError, ValueError):
+            failed.append(pin)
+    assert failed, f"mutant {kind} passes every pin"
+
+
+def test_unmutated_blockwise_passes_every_pin(monkeypatch):
+    """The battery's own control: the rule written the same way as the
+    mutants, unchanged, passes every pin."""
+    block, rows = _mutant("none")
+    monkeypatch.setattr(q40, "quantize_block", block)
+    monkeypatch.setattr(q40, "quantize_rows", rows)
+    for pin in PINS:
+        pin()
