@@ -14,6 +14,10 @@ FLAGS = [
     "-Wall", "-Wno-unused-result",
     # keep the compiler from forming packed fp32 instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # every atomic here is issued by one thread: the atomic optimizer's
+    # cross-lane reduction only adds a wait for each atomic's result before
+    # the next one can go out
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-I", os.path.join(ROOT, "include"),
 ]
 

@@ -27,11 +27,15 @@
 //     rows in one instruction; the int8 V bytes are exact in f16.  The
 //     weights are taken as 2^(s - M + kWeightShift), so that small ones stay
 //     clear of the f16 subnormals; the shift is common to the accumulator
-//     and the exp-sum and cancels in their quotient;
+//     and the exp-sum and cancels in their quotient.  For the int8 codec
+//     the shift also takes out 2^E, a per-wave power of two that follows
+//     the largest V scale seen, so the f16 weights w * v_scale neither
+//     overflow nor sink into the subnormals whatever the V amplitude (the
+//     state's normalisation point moves with E, as it does with the max);
 //   * ranges longer than one partition are merged with the log-sum-exp rule
-//     in partition order (deterministic): inside the decode kernel by the
-//     workgroup that stores a group's last state when the group is small,
-//     else by a combine kernel.
+//     in a fixed order (deterministic), inside the decode kernel: by the
+//     workgroup that stores a group's last state, in one level for small
+//     groups and in two (runs of partitions, then the runs) for large ones.
 // Scores are kept in the log2 domain (softmax scale pre-multiplied by log2 e)
 // so every exponential is one v_exp_f32.
 //
@@ -79,12 +83,23 @@ constexpr int kThreads = kWave * kWaves;
 constexpr int kWideWaves = 8;     // waves per workgroup of a static grid of one workgroup per CU
 constexpr float kInv127 = 1.0f / 127.0f;
 constexpr float kLog2e = 1.44269504088896340736f;
-// Exponent offset of the P.V weights (see the file comment).  A weight is at
-// most 2^8 * v_scale, within f16 range for v_scale < 255, and the f16
-// subnormal step 2^-24 becomes 2^-32 of a unit weight: the rounding of
-// many small weights no longer adds up to ~1e-4 of the output when one token
+// Exponent offset of the P.V weights (see the file comment): the f16
+// subnormal step 2^-24 becomes 2^-32 of a unit weight, so the rounding of
+// many small weights does not add up to ~1e-4 of the output when one token
 // dominates a long context.
 constexpr float kWeightShift = 8.0f;
+// The int8 codec's weights are 2^(s - P) with the normalisation point
+// P = M - kWeightShift + E, where E >= e - kVsHeadroom for every V scale
+// below 2^e seen so far: a weight times its V scale is then below
+// 2^(kWeightShift + kVsHeadroom) = 2^14, clear of the f16 maximum (65504),
+// and stays large enough that small weights do not sink into the f16
+// subnormals when the V scales are tiny.  E is kept in [kVsEMin, kVsEMax]
+// (V scales below 2^(kVsEMin + 6) only lose relative precision, far below
+// that of the largest ones).
+constexpr int kVsHeadroom = 6;
+constexpr int kVsEMin = -60;
+constexpr int kVsEMax = 120;
+constexpr int kVsEInit = kVsEMin;
 
 static_assert(__builtin_bit_cast(uint32_t, kInv127) == 0x3C010204u, "1/127 must round to 0x3C010204");
 
@@ -338,11 +353,13 @@ __device__ __forceinline__ void v_dword_to_f16(const u32x4 (&vch)[2][Geo<HD>::NP
 // GridMode).  An item's arithmetic does not depend on which workgroup runs
 // it, so results are deterministic.  A sequence with one partition writes
 // its output directly; longer ones store each partition's state (M, S, acc)
-// and q8kv_combine_kernel merges them in partition order.
+// and the workgroup that stores the last of them merges them in a fixed
+// order (one level for small groups, two levels -- runs of partitions, then
+// the runs -- for large ones).
 constexpr int kMaxBatch = 2048;   // sequences per call (LDS prefix sums)
 constexpr int kClasses = 16;      // remainder classes of the persistent grid's item order
 constexpr int kNoPartial = 255;   // class of a sequence without a partial partition
-constexpr int kMaxParts = 256;    // partitions per sequence (combine LDS)
+constexpr int kMaxParts = 256;    // partitions per sequence
 
 struct DecodeArgs {
     float* out;
@@ -353,13 +370,29 @@ struct DecodeArgs {
     const float* vs;
     const int32_t* table;
     const int32_t* lens;
-    float* st_acc;  // partition states: accumulators [batch][n_kv][n_parts][G][hd]
-    float* st_ms;   // [batch][n_kv][n_parts][G][2] (max in log2 units, exp-sum)
+    // Partition states: accumulators [batch][n_kv][n_parts + n_runs][G][hd]
+    // and (max in log2 units, exp-sum) [batch][n_kv][n_parts + n_runs][G][2];
+    // a group's run states (two-level merge) follow its partition states.
+    float* st_acc;
+    float* st_ms;
     int* ticket;    // [2]: next work item, workgroups done (zero between calls);
                     // NULL when every item has its own workgroup
-    int* arrive;    // [batch][n_kv]: partitions of a (sequence, kv head) stored so far
-                    // (zero between calls); NULL when q8kv_combine_kernel merges
+    // Merge counters, all zero between calls (every call leaves them zero).
+    // merge 1: arrive [batch][n_hk] int, partitions of a (sequence, head group)
+    // stored so far.  merge 2: arrive holds one 64-bit word per (sequence,
+    // head group) -- bits 0-15 partitions stored, bits 32-63 runs whose
+    // merged state is stored -- followed by int run counters
+    // [batch][n_hk][n_runs], partitions of the run stored so far.
+    int* arrive;
+    int merge;       // 0: no group spans several partitions; 1: one level; 2: two levels
+    int run;         // merge 2: partitions per run
+    int n_runs;      // merge 2: runs of the longest possible sequence (else 0)
     int batch, max_blocks, num_blocks, n_q, n_kv, kv_bs, group, part_tokens, n_parts;
+    // Query heads per kv head above kHeadGroup: they are split into hgs
+    // groups of `group` heads, each its own work item (reading the kv head's
+    // K/V again); n_hk = n_kv * hgs work items per (sequence, partition).
+    // group * hgs = n_q / n_kv; hgs is 1 for group sizes up to kHeadGroup.
+    int hgs, n_hk;
     float scale_log2;  // softmax scale * log2(e)
     // fused append (kernels instantiated with NEW): the new token's K and V
     // rows [batch][n_kv][hd], fp32 or bf16 (new_bf16), quantised into the
@@ -375,6 +408,20 @@ struct DecodeArgs {
     // (a block list per kv head, as the QUEST selection produces)
     int table_rows;
 };
+
+// The kernel's arguments read afresh from the kernel argument segment, for
+// code off the tile loop (the fused append's tail wave, the merges): values
+// read there are not kept in scalar registers across the tile loop.  The
+// pointer is in the constant address space, so the reads are scalar loads
+// through the scalar cache; the empty asm keeps them where they are used.
+// The segment's address is defined only in the kernel itself: every caller
+// must be inlined into it.
+typedef const __attribute__((address_space(4))) DecodeArgs ConstArgs;
+__device__ __forceinline__ ConstArgs* kernel_args() {
+    ConstArgs* ka = (ConstArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+    asm volatile("" : "+s"(ka));
+    return ka;
+}
 
 // Partition states cross workgroups (and XCDs) through buffer loads and
 // stores with the SC1 cache policy: device-scope coherent accesses that
@@ -437,18 +484,18 @@ __device__ __forceinline__ void group_max_sum(const float2* lms, int G, int g, i
     for (int p = 0; p < np; ++p) St += lms[p * G + g].y * __builtin_amdgcn_exp2f(lms[p * G + g].x - Mx);
 }
 
-// Merge the np partition states of (b, kh) into the output rows, in
-// partition order: M* = max M_p, S* = sum S_p 2^(M_p - M*), out = sum acc_p
-// 2^(M_p - M*) / S*.  Thread (row r, slice e4) sums partitions r, r + R, ...
+// Merge the np partition states of group gi (a sequence's head group) into
+// the output rows, in partition order: M* = max M_p, S* = sum S_p
+// 2^(M_p - M*), out = sum acc_p 2^(M_p - M*) / S*.  Thread (row r, slice e4) sums partitions r, r + R, ...
 // in order; the R row sums are then added in row order, so the result does
 // not depend on which workgroup merges.
 template <int HD, int NT>
-__device__ void merge_group(const DecodeArgs& a, int b, int kh, int np, float* out_rows, int tid, float2* lms,
+__device__ void merge_group(const DecodeArgs& a, size_t gi, int np, float* out_rows, int tid, float2* lms,
                             f32x4* lred) {
     constexpr int Q4 = HD / 4;
     const int G = a.group;
     const int slices = G * Q4;
-    const size_t first = ((size_t)b * a.n_kv + kh) * a.n_parts * G;  // state of (partition 0, head 0)
+    const size_t first = gi * (a.n_parts + a.n_runs) * G;  // state of (partition 0, head 0)
     const __amdgpu_buffer_rsrc_t racc = state_rsrc(a.st_acc + first * HD, (uint32_t)(np * G * HD * 4));
     const __amdgpu_buffer_rsrc_t rms = state_rsrc(a.st_ms + first * 2, (uint32_t)(np * G * 8));
     const uint32_t pstride = (uint32_t)(G * HD * 4);  // bytes between partitions
@@ -480,6 +527,166 @@ __device__ void merge_group(const DecodeArgs& a, int b, int kh, int np, float* o
         group_max_sum(lms, G, e4 / Q4, np, Mx, St);
         at = weigh_slices(v, lms, G, e4 / Q4, Mx, 0, 1, np);
         *reinterpret_cast<f32x4*>(out_rows + (size_t)e4 * 4) = at / St;
+    }
+}
+
+// Two-level merge of large groups (more partition states than one workgroup
+// merges at once).  The partitions of a (sequence, kv head) form runs of
+// a.run consecutive partitions.  The workgroup that stores a run's last
+// partition state folds the run into a run state
+//   M_j = max_p M_p,  S_j = sum_p S_p f_p,  acc_j = sum_p acc_p f_p,
+//   f_p = 2^(M_p - M_j)   (partition order),
+// stores it and sets the run's bit in the group's word.  The workgroup that
+// stores the group's last partition state writes
+//   out = sum_j acc_j 2^(M_j - M*) / sum_j S_j 2^(M_j - M*),  M* = max_j M_j
+// (run order), reading the run states whose bits it saw and folding every
+// other run from its partition states itself, with the same code: every
+// sum is an explicit fused multiply-add, so a run state has the same bits
+// whichever workgroup folds it, and the output does not depend on which run
+// merges had finished.  This is the page's rescale rule applied to whole
+// partitions and runs.
+constexpr int kRunMax = 16;      // partitions per run
+constexpr int kRunsMax = 32;     // runs per group (the word's 32 mask bits)
+// State slices a thread has in flight in the two-level merge: static grids
+// run two waves per SIMD, so their kernels have registers for a batch that
+// covers a whole final merge; persistent grids (three waves per SIMD) take
+// smaller batches.
+constexpr int kMergeBatch = 24;
+constexpr int kMergeBatchPersistent = 8;
+constexpr int kSlotMerged = 1 << 30;  // slot word: a stored run state (else a partition state)
+constexpr int kSlotLast = 1 << 29;    // slot word: the run's last slot
+
+__device__ __forceinline__ f32x4 fma4(f32x4 x, float f, f32x4 y) {
+    return f32x4{__builtin_fmaf(x.x, f, y.x), __builtin_fmaf(x.y, f, y.y), __builtin_fmaf(x.z, f, y.z),
+                 __builtin_fmaf(x.w, f, y.w)};
+}
+
+// Merge runs j0 .. j1-1 of group gi (np_b partitions).  mask: runs whose
+// stored state may be read.  final: write the output rows; else (one run)
+// store the run's state.  LDS: lf [np_b][G] partition factors, lrm
+// [j1-j0][G] run (M, S), lslot [kMaxParts + 1] the slot list and its length.
+// Every load of a batch is issued unconditionally, so that all are in
+// flight at once (a load under a branch is preceded by a wait for the ones
+// before it); a slot past the list loads from past the buffer's end, which a
+// buffer load returns as zeros, and its value is not used.
+template <int B>
+__device__ __forceinline__ void load_slot_batch(f32x4 (&v)[B], __amdgpu_buffer_rsrc_t racc, const int* lslot,
+                                                int base, int nslot, uint32_t voff, uint32_t sstride, bool live) {
+#pragma unroll
+    for (int i = 0; i < B; ++i) {
+        const int sw = lslot[min(base + i, nslot - 1)];
+        v[i] = state_load4(racc, live && base + i < nslot ? voff + (uint32_t)(sw & 0xffff) * sstride : 0xfffffff0u, 0);
+    }
+}
+
+template <int HD, int NT, int B>
+__device__ __forceinline__ void merge_runs(size_t gi, int np_b, int j0, int j1, uint32_t mask, bool final,
+                                           float* out_rows, int tid, float* lf, float2* lrm, int* lslot) {
+    constexpr int Q4 = HD / 4;
+    ConstArgs& a = *kernel_args();
+    const int G = a.group, RUN = a.run;
+    const int nst = a.n_parts + a.n_runs;  // states per group: partitions, then runs
+    const size_t first = gi * nst * G;     // state (partition 0, head 0) of the group
+    const __amdgpu_buffer_rsrc_t racc = state_rsrc(a.st_acc + first * HD, (uint32_t)(nst * G * HD * 4));
+    const __amdgpu_buffer_rsrc_t rms = state_rsrc(a.st_ms + first * 2, (uint32_t)(nst * G * 8));
+    const int nrun = j1 - j0;
+    const int slices = G * Q4;
+    const uint32_t sstride = (uint32_t)(G * HD * 4);  // bytes between consecutive states
+    // The slot list (wave 0, one lane per run): a read run state is one slot,
+    // any other run one slot per partition, all in run order.  Slot word:
+    // bits 0-15 the state index, 16-23 the run (from j0), flags above.
+    if (tid < kWave) {
+        const int j = j0 + tid;
+        const bool live = tid < nrun;
+        const bool merged = live && ((mask >> j) & 1u);
+        const int c = !live ? 0 : merged ? 1 : min(RUN, np_b - j * RUN);
+        int incl = c;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            const int v = __shfl_up(incl, off);
+            if (tid >= off) incl += v;
+        }
+        const int start = incl - c;
+        if (merged) lslot[start] = kSlotMerged | kSlotLast | (tid << 16) | (a.n_parts + j);
+        else
+            for (int i = 0; i < c; ++i) lslot[start + i] = (i == c - 1 ? kSlotLast : 0) | (tid << 16) | (j * RUN + i);
+        if (tid == kWave - 1) lslot[kMaxParts] = incl;
+    }
+    __syncthreads();
+    const int nslot = __builtin_amdgcn_readfirstlane(lslot[kMaxParts]);
+    // The first slice's accumulator loads go out before the (M, S) round
+    // trip, so the two overlap.
+    auto slice_off = [&](int e4) {
+        const int g = e4 / Q4;
+        return (uint32_t)(g * HD * 4 + (e4 - g * Q4) * 16);  // the slice inside a state
+    };
+    f32x4 v[B];
+    load_slot_batch<B>(v, racc, lslot, 0, nslot, slice_off(min(tid, slices - 1)), sstride, tid < slices);
+    // Run (M_j, S_j) and partition factors: one thread per (run, head).
+    for (int t = tid; t < nrun * G; t += NT) {
+        const int j = j0 + t / G, g = t - (t / G) * G;
+        float Mj, Sj;
+        if ((mask >> j) & 1u) {
+            const float2 ms = state_load2(rms, (uint32_t)((a.n_parts + j) * G + g) * 8);
+            Mj = ms.x;
+            Sj = ms.y;
+        } else {
+            const int p0 = j * RUN, rs = min(RUN, np_b - p0);
+            float2 ms[kRunMax];
+#pragma unroll
+            for (int i = 0; i < kRunMax; ++i)
+                ms[i] = state_load2(rms, i < rs ? (uint32_t)((p0 + i) * G + g) * 8 : 0xfffffff0u);
+            Mj = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < kRunMax; ++i) Mj = i < rs ? fmaxf(Mj, ms[i].x) : Mj;
+            Sj = 0.0f;
+#pragma unroll
+            for (int i = 0; i < kRunMax; ++i) {
+                const float f = __builtin_amdgcn_exp2f(ms[i].x - Mj);
+                Sj = i < rs ? __builtin_fmaf(ms[i].y, f, Sj) : Sj;
+                if (i < rs) lf[(p0 + i) * G + g] = f;
+            }
+        }
+        lrm[(j - j0) * G + g] = make_float2(Mj, Sj);
+    }
+    __syncthreads();
+    for (int e4 = tid; e4 < slices; e4 += NT) {
+        const int g = e4 / Q4;
+        const uint32_t voff = slice_off(e4);
+        float Mx = -INFINITY, St = 0.0f;
+        if (final) {
+            for (int j = 0; j < nrun; ++j) Mx = fmaxf(Mx, lrm[j * G + g].x);
+            for (int j = 0; j < nrun; ++j)
+                St = __builtin_fmaf(lrm[j * G + g].y, __builtin_amdgcn_exp2f(lrm[j * G + g].x - Mx), St);
+        }
+        f32x4 at = {0.f, 0.f, 0.f, 0.f}, accj = {0.f, 0.f, 0.f, 0.f};
+        for (int base = 0; base < nslot; base += B) {
+            if (base > 0 || e4 != tid) load_slot_batch<B>(v, racc, lslot, base, nslot, voff, sstride, true);
+#pragma unroll
+            for (int i = 0; i < B; ++i) {
+                // branch-free: the slot words are uniform, but held in vector registers
+                const int sw = lslot[min(base + i, nslot - 1)];
+                const bool use = base + i < nslot;
+                const int src = sw & 0xffff;
+                const bool merged = (sw & kSlotMerged) != 0;
+                const float f = lf[merged ? 0 : src * G + g];
+                const f32x4 na = merged ? v[i] : fma4(v[i], f, accj);
+                accj = use ? na : accj;
+                if (final) {
+                    const bool last = use && (sw & kSlotLast) != 0;
+                    const float e = __builtin_amdgcn_exp2f(lrm[((sw >> 16) & 0xff) * G + g].x - Mx);
+                    const f32x4 nat = fma4(accj, e, at);
+                    at = last ? nat : at;
+                    accj = last ? f32x4{0.f, 0.f, 0.f, 0.f} : accj;
+                }
+            }
+        }
+        if (final) {
+            *reinterpret_cast<f32x4*>(out_rows + (size_t)e4 * 4) = at / St;
+        } else {
+            state_store4(racc, voff + (uint32_t)(a.n_parts + j0) * sstride, accj);
+            if (e4 == g * Q4) state_store2(rms, (uint32_t)((a.n_parts + j0) * G + g) * 8, lrm[g]);
+        }
     }
 }
 
@@ -670,13 +877,6 @@ __device__ __forceinline__ void tile_patch(Tile<HD>& T, const int8_t* lk, const 
 // grids the rows are loaded behind the item's first tile and quantised after
 // the query prologue; on persistent grids (whose item loop leaves fewer
 // registers) they are loaded and quantised before the first tile is issued.
-__device__ __forceinline__ const DecodeArgs* kernel_args() {
-    // read here from the kernel argument segment rather than kept in
-    // registers from the kernel's start: only this rare path needs them
-    const DecodeArgs* ka = (const DecodeArgs*)__builtin_amdgcn_kernarg_segment_ptr();
-    asm volatile("" : "+s"(ka));
-    return ka;
-}
 
 template <int HD>
 __device__ __forceinline__ void load_new_rows(NewRow<HD>& nk, NewRow<HD>& nv, const void* knew, const void* vnew,
@@ -726,10 +926,11 @@ __device__ __forceinline__ void store_new_token(const DecodeArgs& a, int kh, int
 // One tile of the page's recurrence for the wave's 8 head columns: int8
 // scores on the matrix cores, tile max, rescale of S and the accumulator by
 // 2^(M_old - M_new), weights 2^(s - M_new + kWeightShift), P.V on the matrix
-// cores.
+// cores.  E: the wave's V-scale exponent (S and the accumulator are
+// normalised at P = M - kWeightShift + E).
 template <int HD>
 __device__ __forceinline__ void tile_compute(const Tile<HD>& T, const int8_t* lq, const float* lqsc, float score_scale,
-                                             f32x4 (&acc)[Geo<HD>::BPL], float& M, float& S, int lane) {
+                                             f32x4 (&acc)[Geo<HD>::BPL], float& M, float& S, int& E, int lane) {
     using GG = Geo<HD>;
     const int r = lane >> 4, n = lane & 15;
     // the query operand is re-read from LDS each tile rather than pinned in registers
@@ -753,12 +954,25 @@ __device__ __forceinline__ void tile_compute(const Tile<HD>& T, const int8_t* lq
             mx = fmaxf(mx, sc[st][j]);
         }
     }
+    // the tile's largest V scale (valid rows; the 16 lanes of a row group
+    // share its rows) -> the exponent offset E
+    float vmx = 0.0f;
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) vmx = fmaxf(vmx, (4 * r + j) < T.nval[st] ? T.vs[st][j] : 0.0f);
+    }
     mx = swap16_max(mx);
+    vmx = swap16_max(vmx);
     mx = swap32_max(mx);
+    vmx = swap32_max(vmx);
+    const int et = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_frexp_expf(vmx)) - kVsHeadroom;
+    const int e_new = max(E, min(et, kVsEMax));
     const float m_new = fmaxf(M, mx);
-    const float alpha = __builtin_amdgcn_exp2f(M - m_new);
+    const float m_shift = m_new - (kWeightShift - (float)e_new);  // the new normalisation point
+    const float alpha = __builtin_amdgcn_exp2f((M - (kWeightShift - (float)E)) - m_shift);
     M = m_new;
-    const float m_shift = m_new - kWeightShift;
+    E = e_new;
 
     f16x8 aw;
     float wsum = 0.0f;
@@ -778,8 +992,9 @@ __device__ __forceinline__ void tile_compute(const Tile<HD>& T, const int8_t* lq
     S = S * alpha + wsum;
 
     // Rescale the accumulator rows (head 4(r&1)+j) by that head's alpha.
-    // alpha is exactly 1 for a head whose maximum did not grow, so the whole
-    // step is skipped (wave-uniformly) when no head's maximum grew.
+    // alpha is exactly 1 for a head whose normalisation point did not move
+    // (its maximum and the wave's V-scale exponent did not grow), so the
+    // whole step is skipped (wave-uniformly) when none moved.
     if (__any(alpha != 1.0f)) {
         float arow[4];
 #pragma unroll
@@ -1272,12 +1487,17 @@ __device__ __forceinline__ void q4_offset_fix(f32x4 (&acc)[Geo<HD>::BPL], const 
 enum GridMode { kPersistent = 0, kStatic = 1 };
 enum CodecKind { kQ8 = 0, kFp8 = 1, kQ40 = 2 };
 
-template <int HD, int MODE, bool NEW, int CODEC = kQ8, int NW = kWaves>
-__global__ __launch_bounds__(kWave * NW) __attribute__((amdgpu_waves_per_eu(HD == 256 ? 1 : 3))) void
+// M2: the kernel carries the two-level merge (a persistent grid whose
+// groups all fit the one-level merge runs without it: its registers are
+// then allocated for the tile loop alone).
+template <int HD, int MODE, bool NEW, int CODEC = kQ8, int NW = kWaves, bool M2 = true>
+__global__ __launch_bounds__(kWave * NW)
+__attribute__((amdgpu_waves_per_eu(HD == 256 ? 1 : MODE == kStatic ? 2 : 3))) void
 q8kv_decode_kernel(const DecodeArgs a) {
     using GG = Geo<HD>;
     constexpr int NT = kWave * NW;  // threads per workgroup
     constexpr bool STATIC = MODE == kStatic;
+    constexpr int kMB = STATIC ? kMergeBatch : kMergeBatchPersistent;
     constexpr bool FP8 = CODEC == kFp8;
     constexpr bool Q40 = CODEC == kQ40;
     static_assert(!(NEW && CODEC != kQ8), "the fused append is an int8-codec path");
@@ -1298,8 +1518,15 @@ q8kv_decode_kernel(const DecodeArgs a) {
     __shared__ int lscan[NW];
     __shared__ int litem;
     __shared__ int lflag;
+    __shared__ uint32_t lmask;
     __shared__ float2 lms[kFuseRows];
     __shared__ f32x4 lred[NT];
+    // the two-level merge reuses LDS that is free once the partition state is
+    // stored: lacc for the partition factors, lred for the run (M, S) and
+    // the slot list
+    static_assert(sizeof(lacc) >= sizeof(float) * kMaxParts * kHeadGroup, "partition factors do not fit");
+    static_assert(sizeof(lred) >= sizeof(float2) * kRunsMax * kHeadGroup + sizeof(int) * (kMaxParts + 1),
+                  "run states and slots do not fit");
     // fused append: the new token's codes, factors and block
     __shared__ __attribute__((aligned(16))) int8_t lnew[NEW ? 2 * HD : 16];
     __shared__ float lnew_sc[2];
@@ -1333,7 +1560,7 @@ q8kv_decode_kernel(const DecodeArgs a) {
             }
             lcls[bb] = (uint8_t)cls;
         }
-        local *= a.n_kv;
+        local *= a.n_hk;
         int incl = local;
 #pragma unroll
         for (int off = 1; off < kWave; off <<= 1) {
@@ -1346,7 +1573,7 @@ q8kv_decode_kernel(const DecodeArgs a) {
         for (int w = 0; w < wid; ++w) run += lscan[w];
         for (int bb = c0; bb < c1; ++bb) {
             lfull[bb] = run;
-            run += a.n_kv * (max(min(a.lens[bb], cap), 0) / pt);
+            run += a.n_hk * (max(min(a.lens[bb], cap), 0) / pt);
         }
         if (tid == NT - 1) lfull[a.batch] = run;
         __syncthreads();
@@ -1384,7 +1611,7 @@ q8kv_decode_kernel(const DecodeArgs a) {
         }
         __syncthreads();
         nfull = lfull[a.batch];
-        total = nfull + lscan[0] * a.n_kv;
+        total = nfull + lscan[0] * a.n_hk;
 
         // empty sequences get zero rows; sequence b is zeroed by workgroup b mod grid
         for (int bb = blockIdx.x; bb < a.batch; bb += gridDim.x) {
@@ -1410,12 +1637,13 @@ q8kv_decode_kernel(const DecodeArgs a) {
         // Item coordinates are wave-uniform; saying so keeps the block-table
         // and length reads on the scalar path (a vector load would queue
         // behind the in-flight tile loads and wait for all of them).
-        int b, kh, part;
+        // ih: the item's head group (0 .. n_hk - 1), of kv head kh = ih / hgs
+        int b, ih, part;
         if constexpr (STATIC) {
             const int id = __builtin_amdgcn_readfirstlane(item);
             part = id % a.n_parts;
-            kh = (id / a.n_parts) % a.n_kv;
-            b = id / (a.n_parts * a.n_kv);
+            ih = (id / a.n_parts) % a.n_hk;
+            b = id / (a.n_parts * a.n_hk);
         } else {
             if (item >= total) break;
             const int id = __builtin_amdgcn_readfirstlane(item);
@@ -1429,21 +1657,22 @@ q8kv_decode_kernel(const DecodeArgs a) {
                 }
                 b = __builtin_amdgcn_readfirstlane(lo);
                 const int f0 = __builtin_amdgcn_readfirstlane(lfull[b]);
-                const int nf = (__builtin_amdgcn_readfirstlane(lfull[b + 1]) - f0) / a.n_kv;
-                kh = (id - f0) / nf;
+                const int nf = (__builtin_amdgcn_readfirstlane(lfull[b + 1]) - f0) / a.n_hk;
+                ih = (id - f0) / nf;
                 part = (id - f0) % nf;
             } else {
-                // partial last partition of the sequence ranked (id - nfull) / n_kv
+                // partial last partition of the sequence ranked (id - nfull) / n_hk
                 const int j = id - nfull;
-                b = __builtin_amdgcn_readfirstlane(lorder[j / a.n_kv]);
-                kh = j % a.n_kv;
-                part = (__builtin_amdgcn_readfirstlane(lfull[b + 1]) - __builtin_amdgcn_readfirstlane(lfull[b])) / a.n_kv;
+                b = __builtin_amdgcn_readfirstlane(lorder[j / a.n_hk]);
+                ih = j % a.n_hk;
+                part = (__builtin_amdgcn_readfirstlane(lfull[b + 1]) - __builtin_amdgcn_readfirstlane(lfull[b])) / a.n_hk;
             }
         }
+        const int kh = a.hgs == 1 ? ih : ih / a.hgs;
         // the query rows' loads go out first: the quantisation then waits for
         // them alone, not for the first tile queued behind them
         QRows<HD, NT> qrows;
-        load_q_rows<HD, NT>(qrows, a.q + ((size_t)b * a.n_q + (size_t)kh * G) * HD, G, itid);
+        load_q_rows<HD, NT>(qrows, a.q + ((size_t)b * a.n_q + (size_t)ih * G) * HD, G, itid);
         const int32_t* trow = a.table + ((size_t)b * a.table_rows + (a.table_rows > 1 ? kh : 0)) * a.max_blocks;
         const int t0 = part * a.part_tokens;
         // The first tile's table reads, those of the item's first tile (a
@@ -1461,7 +1690,7 @@ q8kv_decode_kernel(const DecodeArgs a) {
             L = cap;
             bad = true;
         }
-        float* out_rows = a.out + ((size_t)b * a.n_q + (size_t)kh * G) * HD;
+        float* out_rows = a.out + ((size_t)b * a.n_q + (size_t)ih * G) * HD;
         if constexpr (STATIC) {
             // a slot past the sequence's end has nothing to do; an empty
             // sequence's rows are zeroed by its partition-0 slots
@@ -1492,7 +1721,7 @@ q8kv_decode_kernel(const DecodeArgs a) {
             // rows before it issues its first tile loads, while few
             // registers are live (the item loop leaves few to spare)
             if (tail_ts != INT_MIN) {
-                const DecodeArgs* ka = kernel_args();
+                ConstArgs* ka = kernel_args();
                 load_new_rows<HD>(nk, nv, ka->knew, ka->vnew, ka->new_bf16, b, a.n_kv, kh, ilane);
                 prepare_new_token<HD>(nk, nv, tail_blk, lnew, lnew_sc, &lnew_blk, ilane);
             }
@@ -1533,6 +1762,7 @@ q8kv_decode_kernel(const DecodeArgs a) {
 #pragma unroll
         for (int s = 0; s < GG::BPL; ++s) acc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
         float M = -INFINITY, S = 0.0f;
+        int E = kVsEInit;  // int8 codec: the V-scale exponent offset
         f32x4 wsums = {0.f, 0.f, 0.f, 0.f};  // q4_0: per-block weight sums
 
         while (ts < t1) {
@@ -1541,7 +1771,7 @@ q8kv_decode_kernel(const DecodeArgs a) {
             }
             if constexpr (FP8) fp8_tile_compute<HD>(A, lq16, a.scale_log2, acc, M, S, ilane);
             else if constexpr (Q40) q4_tile_compute<HD>(A, lq, lqsc, lqsum, a.scale_log2, acc, wsums, M, S, ilane);
-            else tile_compute<HD>(A, lq, lqsc, a.scale_log2, acc, M, S, ilane);
+            else tile_compute<HD>(A, lq, lqsc, a.scale_log2, acc, M, S, E, ilane);
             ts += kStride;
             if (ts < t1) {
                 int blk[2];
@@ -1557,10 +1787,12 @@ q8kv_decode_kernel(const DecodeArgs a) {
         }
 
         if constexpr (NEW) {
-            if (tail_ts != INT_MIN) store_new_token<HD>(a, kh, L, lnew, lnew_sc, &lnew_blk, ilane);
+            // (one head group of the kv head stores it; every one patches its tile)
+            if (tail_ts != INT_MIN && ih == kh * a.hgs) store_new_token<HD>(a, kh, L, lnew, lnew_sc, &lnew_blk, ilane);
         }
 
         if constexpr (Q40) q4_offset_fix<HD>(acc, wsums, ilane);
+
         // wave state -> LDS: exp-sum over the four row groups, hi + lo rows
         S = swap16_sum(S);
         S = swap32_sum(S);
@@ -1570,7 +1802,10 @@ q8kv_decode_kernel(const DecodeArgs a) {
             for (int j = 0; j < 4; ++j) acc[s][j] = swap32_sum(acc[s][j]);
         }
         if (ilane < kHeadGroup) {
-            lM[wid][ilane] = M;
+            // the wave's normalisation point: S and acc are sums of 2^(s - P)
+            // terms (the int8 codec's P moves with its V-scale exponent; the
+            // other codecs' is M - kWeightShift in every wave, so M serves)
+            lM[wid][ilane] = CODEC == kQ8 ? M - (kWeightShift - (float)E) : M;
             lS[wid][ilane] = S;
         }
         if (r_of(ilane) < 2) {
@@ -1585,7 +1820,7 @@ q8kv_decode_kernel(const DecodeArgs a) {
 
         // merge the waves' states (same rescale rule, wave order fixed); write
         // the output (one partition) or this partition's state
-        const size_t state0 = (((size_t)b * a.n_kv + kh) * a.n_parts + part) * G;
+        const size_t state0 = (((size_t)b * a.n_hk + ih) * (a.n_parts + a.n_runs) + part) * G;
         const __amdgpu_buffer_rsrc_t racc = state_rsrc(a.st_acc + state0 * HD, (uint32_t)(G * HD * 4));
         const __amdgpu_buffer_rsrc_t rms = state_rsrc(a.st_ms + state0 * 2, (uint32_t)(G * 8));
         for (int e4 = itid; e4 < G * Q4; e4 += NT) {
@@ -1609,19 +1844,69 @@ q8kv_decode_kernel(const DecodeArgs a) {
                 if (i4 == 0) state_store2(rms, (uint32_t)g * 8, make_float2(Mx, St));
             }
         }
-        if (a.arrive && np_b > 1) {
+        if (np_b > 1 && a.merge == 1) {
             // the workgroup storing the group's last state merges the group
             wait_stores();
             __syncthreads();
             if (itid == 0) {
-                int* c = a.arrive + (size_t)b * a.n_kv + kh;
+                int* c = a.arrive + (size_t)b * a.n_hk + ih;
                 const int prev = __hip_atomic_fetch_add(c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 const bool last = prev == np_b - 1;
                 if (last) __hip_atomic_store(c, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 lflag = last;
             }
             __syncthreads();
-            if (lflag) merge_group<HD, NT>(a, b, kh, np_b, out_rows, itid, lms, lred);
+            if (lflag) merge_group<HD, NT>(a, (size_t)b * a.n_hk + ih, np_b, out_rows, itid, lms, lred);
+        } else if (M2 && np_b > 1) {
+            // two levels: every arrival counts itself in its run's counter
+            // and in the group's word (one round trip for both); the last
+            // arrival of the group writes the output, the last arrival of
+            // any other run merges its run
+            wait_stores();
+            __syncthreads();
+            ConstArgs* ka = kernel_args();
+            const size_t gi = (size_t)b * ka->n_hk + ih;
+            const int k = part / ka->run;
+            const int nr_b = (np_b + ka->run - 1) / ka->run;
+            unsigned long long* word = reinterpret_cast<unsigned long long*>(ka->arrive) + gi;
+            if (itid == 0) {
+                int* rc = ka->arrive + 2 * (size_t)ka->batch * ka->n_hk + gi * ka->n_runs + k;
+                const int prev_r = __hip_atomic_fetch_add(rc, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const unsigned long long prev_w =
+                    __hip_atomic_fetch_add(word, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const bool last_run = prev_r == min(ka->run, np_b - k * ka->run) - 1;
+                if (last_run) __hip_atomic_store(rc, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const bool fin = (int)(prev_w & 0xffffu) + 1 == np_b;
+                const uint32_t mask = (uint32_t)(prev_w >> 32);
+                // the last arrival takes out every arrival and the run bits it
+                // has seen; a bit set later is taken out by its setter
+                if (fin)
+                    __hip_atomic_fetch_sub(word, (unsigned long long)np_b | ((unsigned long long)mask << 32),
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                lflag = fin ? 2 : last_run ? 1 : 0;
+                lmask = mask;
+            }
+            __syncthreads();
+            float* lf = &lacc[0][0][0];
+            float2* lrm = reinterpret_cast<float2*>(lred);
+            int* lslot = reinterpret_cast<int*>(lrm + kRunsMax * kHeadGroup);
+            if (lflag == 2) {
+                merge_runs<HD, NT, kMB>(gi, np_b, 0, nr_b, lmask, true, out_rows, itid, lf, lrm, lslot);
+            } else if (lflag == 1) {
+                merge_runs<HD, NT, kMB>(gi, np_b, k, k + 1, 0u, false, out_rows, itid, lf, lrm, lslot);
+                wait_stores();
+                __syncthreads();
+                if (itid == 0) {
+                    const unsigned long long bit = 1ull << (32 + k);
+                    const unsigned long long prev_w =
+                        __hip_atomic_fetch_add(word, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    const int arrived = (int)(prev_w & 0xffffu);
+                    // the group's last arrival has come (np_b) or has already
+                    // cleared the word (0): it will not read this bit
+                    if (arrived == np_b || arrived == 0)
+                        __hip_atomic_fetch_sub(word, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+            }
         }
         // next item (the barrier also keeps LDS from being reused too early)
         if (STATIC || !a.ticket) break;
@@ -1639,87 +1924,6 @@ q8kv_decode_kernel(const DecodeArgs a) {
             __hip_atomic_store(a.ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(a.ticket + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-    }
-}
-
-struct CombineArgs {
-    float* out;
-    const float* st_acc;
-    const float* st_ms;
-    const int32_t* lens;
-    int n_q, n_kv, group, cap, part_tokens, n_parts;
-};
-
-// Merge the partition states of one (sequence, query head) with the rescale
-// rule: M* = max M_p, S* = sum S_p 2^(M_p - M*), out = sum acc_p 2^(M_p - M*) / S*.
-// Thread (row r, slice i4) owns partitions p = r, r + R, ... and sums them in
-// increasing order; the R row sums are then added in row order, so the result
-// is deterministic.  All state loads are issued at once, together with the
-// length read (slots past the sequence's partitions are read but never used).
-template <int HD>
-__global__ __launch_bounds__(kThreads) void q8kv_combine_kernel(const CombineArgs a) {
-    constexpr int Q4 = HD / 4;          // float4 slices per head row
-    constexpr int R = kThreads / Q4;    // partitions summed in parallel
-    constexpr int PER = kMaxParts / R;  // partitions per thread at most
-    __shared__ f32x4 lpart[R][Q4];
-    __shared__ float lsp[R];
-    __shared__ float lmax[kWaves];
-    const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid >> 6;
-    const int h = blockIdx.x % a.n_q, b = blockIdx.x / a.n_q;
-    const int kh = h / a.group, g = h % a.group;
-    const size_t first = (((size_t)b * a.n_kv + kh) * a.n_parts) * a.group + g;  // state of p = 0
-    const size_t pstride = (size_t)a.group;                                        // states per partition
-    const int i4 = tid % Q4, r = tid / Q4;
-
-    f32x4 v[PER];
-    float2 ms[PER];
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-        const int p = r + k * R;
-        if (p < a.n_parts) {
-            v[k] = *reinterpret_cast<const f32x4*>(a.st_acc + (first + p * pstride) * HD + 4 * i4);
-            ms[k] = *reinterpret_cast<const float2*>(a.st_ms + (first + p * pstride) * 2);
-        }
-    }
-    const int L = min(a.lens[b], a.cap);
-    if (L <= 0) return;
-    const int np = (L + a.part_tokens - 1) / a.part_tokens;
-    if (np <= 1) return;
-
-    float mx = -INFINITY;
-#pragma unroll
-    for (int k = 0; k < PER; ++k)
-        if (r + k * R < np) mx = fmaxf(mx, ms[k].x);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-    if (lane == 0) lmax[wid] = mx;
-    __syncthreads();
-    float Mx = lmax[0];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) Mx = fmaxf(Mx, lmax[w]);
-
-    f32x4 at = {0.f, 0.f, 0.f, 0.f};
-    float sp = 0.0f;
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-        if (r + k * R < np) {
-            const float w = __builtin_amdgcn_exp2f(ms[k].x - Mx);
-            at += v[k] * w;
-            sp += ms[k].y * w;
-        }
-    }
-    lpart[r][i4] = at;
-    if (i4 == 0) lsp[r] = sp;
-    __syncthreads();
-    if (r == 0) {
-        f32x4 t = lpart[0][i4];
-        float St = lsp[0];
-#pragma unroll
-        for (int rr = 1; rr < R; ++rr) {
-            t += lpart[rr][i4];
-            St += lsp[rr];
-        }
-        *reinterpret_cast<f32x4*>(a.out + ((size_t)b * a.n_q + h) * HD + 4 * i4) = t / St;
     }
 }
 
@@ -2409,6 +2613,13 @@ __global__ __launch_bounds__(kThreads) void q8kv_debug_dots_kernel(const DotsArg
 
 __device__ unsigned g_stream_sink;
 
+// Clears library-owned counters (a kernel rather than a memset, so that a
+// caller may capture the call in a graph).
+__global__ __launch_bounds__(256) void q8kv_zero_kernel(int* p, size_t n) {
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = 0;
+}
+
 __global__ __launch_bounds__(256) void q8kv_stream_read_kernel(const u32x4* __restrict__ a, size_t a16,
                                                                const u32x4* __restrict__ b, size_t b16) {
     constexpr int L = 8;
@@ -2488,6 +2699,17 @@ int check_cache_shape(int num_blocks, int n_kv, int hd, int kv_bs) {
     return Q8KV_OK;
 }
 
+// Query heads per work item: a kv head's G query heads in hgs groups of g
+// heads, g the largest divisor of G that is at most kHeadGroup (the matrix-
+// core column set); each group is its own work item and reads the kv head's
+// K/V itself.
+void head_groups(int G, int* g, int* hgs) {
+    int d = std::min(G, kHeadGroup);
+    while (G % d) --d;
+    *g = d;
+    *hgs = G / d;
+}
+
 // Partition plan: a pure function of the shapes, so results never depend on
 // the device.  When the longest possible step spreads over about 512 work
 // items of at most 2048 tokens, use that (one item per workgroup: every
@@ -2518,9 +2740,10 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 // append of the new token, the FP8 codec.
 enum Variant { kVarQ8 = 0, kVarQ8New = 1, kVarFp8 = 2, kVarQ40 = 3 };
 
-template <int HD, int VAR, int MODE, int NW = kWaves>
+template <int HD, int VAR, int MODE, int NW = kWaves, bool M2 = true>
 constexpr auto decode_kernel_ptr() {
-    return q8kv_decode_kernel<HD, MODE, VAR == kVarQ8New, VAR == kVarFp8 ? kFp8 : VAR == kVarQ40 ? kQ40 : kQ8, NW>;
+    return q8kv_decode_kernel<HD, MODE, VAR == kVarQ8New, VAR == kVarFp8 ? kFp8 : VAR == kVarQ40 ? kQ40 : kQ8, NW,
+                              M2>;
 }
 
 // Wide (kWideWaves) workgroups serve static grids of at most one workgroup
@@ -2536,7 +2759,7 @@ int launch_info_hd(int dev, LaunchInfo& li) {
     if (e == hipSuccess) e = hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev);
     if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &per_cu, reinterpret_cast<const void*>(decode_kernel_ptr<HD, VAR, kPersistent>()), kThreads, 0);
+        &per_cu, reinterpret_cast<const void*>(decode_kernel_ptr<HD, VAR, kPersistent, kWaves, false>()), kThreads, 0);
     if (e != hipSuccess) return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
     li.resident = std::max(1, li.cus * std::max(1, per_cu));
     // A static grid of at most two workgroups per CU is spread evenly when a
@@ -2587,7 +2810,12 @@ int launch_info(int dev, int hd, int var, LaunchInfo* out) {
 template <int HD, int VAR>
 void launch_decode_hd(int mode, bool wide, unsigned grid, size_t lds, hipStream_t st, const DecodeArgs& da) {
     if (mode == kPersistent) {
-        hipLaunchKernelGGL((decode_kernel_ptr<HD, VAR, kPersistent>()), dim3(grid), dim3(kThreads), 0, st, da);
+        if (da.merge == 2)
+            hipLaunchKernelGGL((decode_kernel_ptr<HD, VAR, kPersistent, kWaves, true>()), dim3(grid), dim3(kThreads), 0,
+                               st, da);
+        else
+            hipLaunchKernelGGL((decode_kernel_ptr<HD, VAR, kPersistent, kWaves, false>()), dim3(grid), dim3(kThreads),
+                               0, st, da);
         return;
     }
     if constexpr (wide_hd(HD)) {
@@ -2615,6 +2843,12 @@ void launch_decode(int hd, int var, int mode, bool wide, unsigned grid, size_t l
     else launch_decode_var<kVarQ8>(hd, mode, wide, grid, lds, st, da);
 }
 
+hipError_t launch_zero(void* p, size_t n_words, hipStream_t st) {
+    hipLaunchKernelGGL(q8kv_zero_kernel, dim3((unsigned)((n_words + 255) / 256)), dim3(256), 0, st,
+                       static_cast<int*>(p), n_words);
+    return hipGetLastError();
+}
+
 int decode_impl(float* out, const float* q, const int8_t* kp, const int8_t* vp, const float* ks,
                 const float* vs, const int32_t* table, const int32_t* lens, int max_blocks,
                 int num_blocks, int batch, int n_q, int n_kv, int hd, int kv_bs, float scale,
@@ -2632,8 +2866,9 @@ int decode_impl(float* out, const float* q, const int8_t* kp, const int8_t* vp, 
     int rc = check_cache_shape(num_blocks, n_kv, hd, kv_bs);
     if (rc) return rc;
     if (n_q % n_kv) return fail(Q8KV_EINVAL, "n_q_heads (%d) is not a multiple of n_kv_heads (%d)", n_q, n_kv);
-    const int G = n_q / n_kv;
-    if (G > kHeadGroup) return fail(Q8KV_EINVAL, "query heads per kv head must be <= %d (got %d)", kHeadGroup, G);
+    int G, hgs;
+    head_groups(n_q / n_kv, &G, &hgs);
+    const int n_hk = n_kv * hgs;
     if (max_blocks <= 0) return fail(Q8KV_EINVAL, "max_blocks_per_seq must be positive (got %d)", max_blocks);
     if ((long long)max_blocks * kv_bs > (INT_MAX / 2)) return fail(Q8KV_EINVAL, "max_blocks_per_seq * kv_bs overflows");
     if (!std::isfinite(scale)) return fail(Q8KV_EINVAL, "scale must be finite");
@@ -2641,14 +2876,14 @@ int decode_impl(float* out, const float* q, const int8_t* kp, const int8_t* vp, 
     const int max_tokens = max_blocks * kv_bs;
     int pt, np;
     if (part_tokens == 0) {
-        plan(batch, n_kv, max_tokens, &pt, &np);
+        plan(batch, n_hk, max_tokens, &pt, &np);
     } else {
         pt = part_tokens;
         np = (max_tokens + pt - 1) / pt;
         if (np > kMaxParts)
             return fail(Q8KV_EINVAL, "part_tokens %d splits %d tokens into %d > %d partitions", pt, max_tokens, np, kMaxParts);
     }
-    const long long items = (long long)batch * n_kv * np;
+    const long long items = (long long)batch * n_hk * np;
     if ((long long)batch * n_q > INT_MAX || items > INT_MAX) return fail(Q8KV_EINVAL, "decode shape too large");
 
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -2661,7 +2896,7 @@ int decode_impl(float* out, const float* q, const int8_t* kp, const int8_t* vp, 
     if (rc) return rc;
     const unsigned grid = (unsigned)std::min<long long>(items, li.resident);
     DecodeArgs da{out, q, kp, vp, ks, vs, table, lens, nullptr, nullptr, nullptr, nullptr,
-                  batch, max_blocks, num_blocks, n_q, n_kv, kv_bs, G, pt, np, scale * kLog2e,
+                  0, 0, 0, batch, max_blocks, num_blocks, n_q, n_kv, kv_bs, G, pt, np, hgs, n_hk, scale * kLog2e,
                   knew, vnew, new_dtype, ks8, vs8, head_tables ? n_kv : 1};
     if (items > (long long)grid) {
         std::lock_guard<std::mutex> lock(g_mu);
@@ -2670,19 +2905,41 @@ int decode_impl(float* out, const float* q, const int8_t* kp, const int8_t* vp, 
             void* t = nullptr;
             e = hipMalloc(&t, 256);
             if (e != hipSuccess) return fail(Q8KV_ENOMEM, "hipMalloc of the work ticket: %s", hipGetErrorString(e));
-            e = hipMemsetAsync(t, 0, 256, st);
+            e = launch_zero(t, 64, st);
             if (e != hipSuccess) {
                 (void)hipFree(t);
-                return hip_fail(e, "hipMemsetAsync");
+                return hip_fail(e, "work ticket clear");
             }
             w.ticket = static_cast<int*>(t);
         }
         da.ticket = w.ticket;
     }
+    // every item in its own workgroup: static grid (two per CU at most when
+    // that is enough; wide workgroups when one per CU is)
+    const int mode = items > (long long)grid ? kPersistent : kStatic;
+    const bool wide = mode == kStatic && wide_hd(hd) && grid <= (unsigned)li.cus && g_wide.load() != 0;
+    const int nt = wide ? kWave * kWideWaves : kThreads;
+    // Partition states are merged inside the decode kernel: in one level
+    // when a group's states fit one workgroup's loads, else in two (runs of
+    // about sqrt(np) partitions, then the runs).
+    const int slices = G * hd / 4;
+    const int rows_par = slices >= nt ? 1 : nt / slices;
     if (np > 1) {
-        const size_t n_state = (size_t)batch * n_kv * np * G;
+        const bool one = np * G <= kFuseRows && (np + rows_par - 1) / rows_par <= kFusePer;
+        da.merge = one ? 1 : 2;
+        if (!one) {
+            int run = (int)std::ceil(std::sqrt((double)np));
+            run = std::max(run, (np + kRunsMax - 1) / kRunsMax);
+            da.run = std::min(run, kRunMax);
+            da.n_runs = (np + da.run - 1) / da.run;
+        }
+    }
+    if (np > 1) {
+        const size_t groups = (size_t)batch * n_hk;
+        const size_t n_state = groups * (size_t)(np + da.n_runs) * G;
         const size_t acc_bytes = align256(n_state * hd * sizeof(float));
         const size_t need = acc_bytes + n_state * 2 * sizeof(float);
+        const size_t need_arrive = da.merge == 1 ? groups : 2 * groups + groups * (size_t)da.n_runs;
         std::lock_guard<std::mutex> lock(g_mu);
         Workspace& w = g_ws[{dev, stream}];
         if (w.bytes < need) {
@@ -2703,21 +2960,7 @@ int decode_impl(float* out, const float* q, const int8_t* kp, const int8_t* vp, 
         }
         da.st_acc = static_cast<float*>(w.ptr);
         da.st_ms = reinterpret_cast<float*>(static_cast<char*>(w.ptr) + acc_bytes);
-    }
-    // every item in its own workgroup: static grid (two per CU at most when
-    // that is enough; wide workgroups when one per CU is)
-    const int mode = items > (long long)grid ? kPersistent : kStatic;
-    const bool wide = mode == kStatic && wide_hd(hd) && grid <= (unsigned)li.cus && g_wide.load() != 0;
-    const int nt = wide ? kWave * kWideWaves : kThreads;
-    // small groups of partition states are merged inside the decode kernel
-    const int slices = G * hd / 4;
-    const int rows_par = slices >= nt ? 1 : nt / slices;
-    const bool fuse = np > 1 && np * G <= kFuseRows && (np + rows_par - 1) / rows_par <= kFusePer;
-    if (fuse) {
-        const size_t need = (size_t)batch * n_kv;
-        std::lock_guard<std::mutex> lock(g_mu);
-        Workspace& w = g_ws[{dev, stream}];
-        if (w.arrive_n < need) {
+        if (w.arrive_n < need_arrive) {
             if (w.arrive) {
                 e = hipStreamSynchronize(st);
                 if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
@@ -2727,15 +2970,16 @@ int decode_impl(float* out, const float* q, const int8_t* kp, const int8_t* vp, 
                 if (e != hipSuccess) return hip_fail(e, "hipFree");
             }
             void* t = nullptr;
-            e = hipMalloc(&t, need * sizeof(int));
+            e = hipMalloc(&t, need_arrive * sizeof(int));
             if (e != hipSuccess) return fail(Q8KV_ENOMEM, "hipMalloc of the merge counters: %s", hipGetErrorString(e));
-            e = hipMemsetAsync(t, 0, need * sizeof(int), st);
+            // cleared by a kernel, not a memset node (callers may capture the call)
+            e = launch_zero(t, need_arrive, st);
             if (e != hipSuccess) {
                 (void)hipFree(t);
-                return hip_fail(e, "hipMemsetAsync");
+                return hip_fail(e, "merge counter clear");
             }
             w.arrive = static_cast<int*>(t);
-            w.arrive_n = need;
+            w.arrive_n = need_arrive;
         }
         da.arrive = w.arrive;
     }
@@ -2744,17 +2988,6 @@ int decode_impl(float* out, const float* q, const int8_t* kp, const int8_t* vp, 
     launch_decode(hd, var, mode, wide, grid, lds, st, da);
     e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
-    if (np > 1 && !fuse) {
-        CombineArgs ca{out, da.st_acc, da.st_ms, lens, n_q, n_kv, G, max_tokens, pt, np};
-        const unsigned cgrid = (unsigned)(batch * n_q);
-        switch (hd) {
-            case 64: hipLaunchKernelGGL(q8kv_combine_kernel<64>, dim3(cgrid), dim3(kThreads), 0, st, ca); break;
-            case 128: hipLaunchKernelGGL(q8kv_combine_kernel<128>, dim3(cgrid), dim3(kThreads), 0, st, ca); break;
-            default: hipLaunchKernelGGL(q8kv_combine_kernel<256>, dim3(cgrid), dim3(kThreads), 0, st, ca); break;
-        }
-        e = hipGetLastError();
-        if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
-    }
     return Q8KV_OK;
 }
 
@@ -2805,7 +3038,9 @@ int q8kv_plan(int batch, int n_q_heads, int n_kv_heads, int hd, int kv_bs, int m
     if (!valid_hd(hd) || !valid_kv_bs(kv_bs) || max_blocks_per_seq <= 0 ||
         (long long)max_blocks_per_seq * kv_bs > (INT_MAX / 2))
         return fail(Q8KV_EINVAL, "bad hd / kv_bs / max_blocks_per_seq");
-    plan(batch, n_kv_heads, max_blocks_per_seq * kv_bs, part_tokens, n_parts);
+    int G, hgs;
+    head_groups(n_q_heads / n_kv_heads, &G, &hgs);
+    plan(batch, n_kv_heads * hgs, max_blocks_per_seq * kv_bs, part_tokens, n_parts);
     return Q8KV_OK;
 }
 

@@ -46,7 +46,7 @@ def fp8_decode(**kw):
     (dict(sl=NUL), q8.Q8KV_ENULL),
     (dict(hd=96), q8.Q8KV_EINVAL),
     (dict(kv_bs=8), q8.Q8KV_EINVAL),
-    (dict(n_q=18, n_kv=1), q8.Q8KV_EINVAL),
+    (dict(n_q=18, n_kv=4), q8.Q8KV_EINVAL),
     (dict(scale=float("nan")), q8.Q8KV_EINVAL),
     (dict(part=48), q8.Q8KV_EINVAL),
 ])
@@ -114,7 +114,6 @@ def test_append_decode_rejects_before_any_hip_call(kw, code):
     (dict(n_q=0), q8.Q8KV_EINVAL),
     (dict(n_kv=0), q8.Q8KV_EINVAL),
     (dict(n_q=6, n_kv=4), q8.Q8KV_EINVAL),
-    (dict(n_q=18, n_kv=1), q8.Q8KV_EINVAL),
     (dict(hd=96), q8.Q8KV_EINVAL),
     (dict(hd=512), q8.Q8KV_EINVAL),
     (dict(kv_bs=8), q8.Q8KV_EINVAL),
@@ -168,6 +167,15 @@ def test_set_wide_accepts_only_0_and_1():
 def test_stream_read_rejects():
     assert L.q8kv_debug_stream_read(NUL, 16, FAKE, 16, NUL) == q8.Q8KV_ENULL
     assert L.q8kv_debug_stream_read(FAKE, 17, FAKE, 16, NUL) == q8.Q8KV_EINVAL
+
+
+def test_plan_counts_head_groups():
+    """More than 8 query heads per kv head run as several head-group work
+    items (the largest divisor of the group size up to 8 heads each), so the
+    plan sees n_kv * groups item heads: 64 / 4 heads plan like 64 / 8."""
+    assert q8.plan(1, 64, 4, 128, 64, 2048) == q8.plan(1, 64, 8, 128, 64, 2048)
+    assert q8.plan(2, 36, 2, 128, 16, 256) == q8.plan(2, 36, 6, 128, 16, 256)   # 18 = 3 x 6
+    assert q8.plan(1, 13, 1, 64, 16, 64) == q8.plan(1, 13, 13, 64, 16, 64)     # prime: 13 x 1
 
 
 def test_plan_is_shape_only_and_sane():

@@ -77,4 +77,22 @@ def test_cpu_baseline_leg_fields():
     cpu, parity = bench.cpu_baseline(w, g, out_fn, 0.2)
     assert cpu["kind"] == "oracle" and cpu["unit"] == "GB/s" and cpu["value"] > 0
     assert cpu["cores"] >= 1 and cpu["sample_seconds"] >= 0.2 and "whole step" in cpu["sample"]
-    assert parity["ok"] and parity["max_abs_err_vs_oracle"] == 0.0
+    assert parity["ok"] and parity["max_abs_err_vs_oracle"] == 0.0 and parity["ok_f64"]
+    # the single-threaded pass, bitwise equal to the OpenMP one, and the host
+    st = cpu["single_thread"]
+    assert st["cores"] == 1 and st["value"] > 0 and st["bitwise_equal_to_parallel"]
+    assert cpu["host_nproc"] >= 1 and isinstance(cpu["cpu_model"], str)
+
+
+def test_bench_defaults_name_the_gated_workloads():
+    """The headline is the ragged batch (the largest workload) and the 128K
+    step is timed in the same run."""
+    sys.path.insert(0, ROOT)
+    import bench
+    old = sys.argv
+    sys.argv = ["bench.py"]
+    try:
+        args = bench.parse()
+    finally:
+        sys.argv = old
+    assert args.workload == "ragged" and "long_gqa" in args.also.split(",")

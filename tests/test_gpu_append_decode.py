@@ -108,7 +108,8 @@ def edge_lens(batch, kv_bs, pt):
 
 
 @pytest.mark.parametrize("hd,G,kv_bs", [(64, 1, 16), (64, 8, 32), (128, 1, 16), (128, 4, 64),
-                                        (128, 8, 16), (256, 2, 32), (256, 8, 128), (128, 5, 256)])
+                                        (128, 8, 16), (256, 2, 32), (256, 8, 128), (128, 5, 256),
+                                        (128, 16, 16), (64, 10, 32)])  # head groups: one of them stores the token
 def test_append_decode_shapes(hd, G, kv_bs):
     batch = 14
     lens = edge_lens(batch, kv_bs, 0)
@@ -122,8 +123,8 @@ def test_append_decode_shapes(hd, G, kv_bs):
 @pytest.mark.parametrize("pt", [32, 64, 96, 128])
 def test_append_decode_split_and_merge(pt):
     """Split contexts: the new token falls in the last partition, whichever
-    wave owns its tile; in-kernel merge (few partitions) and the combine
-    kernel (many)."""
+    wave owns its tile; one-level merge (few partitions) and the two-level
+    merge (many)."""
     lens = edge_lens(12, 16, pt)
     w = workloads.Workload("fusedsplit", 12, 8, 2, 128, 16, max(lens), ragged=True, table="pool",
                            key=1100 + pt)

@@ -181,12 +181,12 @@ def test_decode_hd_kv_bs(hd, kv_bs):
                                   (256, 2), (256, 5), (256, 8)])
 def test_decode_split_merge_paths(hd, G):
     """Partition states of a (sequence, kv head) are merged inside the decode
-    kernel by the workgroup that stores the last one when there are at most
-    64 of them (partitions x query heads), else by the combine kernel.  The
-    partition lengths here give 3 to 19 partitions, so each shape takes one or
-    both paths, the in-kernel one with one or several float4 slices per
-    thread; each call is made twice, since the merge leaves its arrival
-    counters at zero for the next call."""
+    kernel by the workgroup that stores the last one: in one level when
+    there are at most 64 of them (partitions x query heads), else in two
+    (runs of partitions, then the runs).  The partition lengths here give 3
+    to 19 partitions, so each shape takes one or both paths, the one-level
+    one with one or several float4 slices per thread; each call is made
+    twice, since the merges leave their counters at zero for the next call."""
     w = workloads.Workload("merge", 3, 2 * G, 2, hd, 32, 600, ragged=True, table="pool",
                            key=800 + hd + G)
     c = build(w)
@@ -243,13 +243,126 @@ def test_decode_max_batch():
 
 @pytest.mark.parametrize("hd,G", [(64, 1), (128, 8), (256, 4)])
 def test_decode_max_partitions(hd, G):
-    """256 partitions of one sequence, the most a call plans: the combine
-    kernel's per-thread state arrays at their full length for every hd."""
+    """256 partitions of one sequence, the most a call plans: the two-level
+    merge at its widest (16 runs of 16 partitions) for every hd."""
     w = workloads.Workload("maxparts", 2, 2 * G, 2, hd, 32, 256 * 32, ragged=True, table="pool", key=960 + hd)
     c = build(w, lens=[256 * 32, 5000])
     say(f"max partitions hd={hd} G={G}")
     dev = gpu_cache(c)
     check_decode(c, dev, part_tokens=32)
+
+
+@pytest.mark.parametrize("hd,G,n_kv,lens,pt", [
+    (128, 8, 2, [256 * 32, 5000, 300, 0], 32),   # 256 partitions: runs of 16
+    (128, 8, 4, [128 * 64], 64),                 # the 128K step's plan: 512 static items, 128 partitions
+    (64, 1, 2, [100 * 32, 70 * 32 + 5, 64], 32),  # one head: 100 states, runs of 10
+    (256, 8, 1, [40 * 64 + 3, 9 * 64], 64),      # hd 256: two slices per thread
+    (128, 3, 2, [30 * 32, 23 * 32 - 1, 1, 0], 32),
+    (64, 8, 1, [9 * 32, 17 * 32 + 1], 32),       # just past the one-level limit
+])
+def test_decode_two_level_merge(hd, G, n_kv, lens, pt):
+    """Groups of more than 64 partition states: the last arrival of each run
+    of partitions stores the run's state, and the group's last arrival reads
+    the run states it finds stored and folds the other runs from their
+    partition states itself.  Which runs are stored when the last arrival
+    comes varies from call to call, so the output is checked against the
+    oracle and repeated bit for bit over several calls."""
+    w = workloads.Workload("merge2", len(lens), n_kv * G, n_kv, hd, 32 if pt == 32 else 64, max(lens),
+                           ragged=True, table="pool", key=1100 + hd + G + n_kv)
+    c = build(w, lens=lens)
+    say(f"two-level merge hd={hd} G={G} n_kv={n_kv} lens={lens} part_tokens={pt}")
+    dev = gpu_cache(c)
+    first = decode(c, dev, part_tokens=pt)
+    for _ in range(4):
+        again = decode(c, dev, part_tokens=pt)
+        assert np.array_equal(first.view(np.uint32), again.view(np.uint32))
+    check_decode(c, dev, part_tokens=pt)
+
+
+def test_decode_two_level_merge_persistent():
+    """The two-level merge on the persistent grid: 24 sequences of up to 6000
+    tokens in 32-token partitions are ~9000 items, more than fit at once."""
+    rng = np.random.default_rng(1200)
+    lens = [int(x) for x in rng.integers(1, 6001, size=24)]
+    lens[:4] = [6000, 0, 33, 64 * 32]
+    w = workloads.Workload("merge2p", 24, 16, 2, 128, 32, 6000, ragged=True, table="pool", key=1200)
+    c = build(w, lens=lens)
+    say(f"two-level merge, persistent grid, tokens={int(c.lens.sum())}")
+    dev = gpu_cache(c)
+    first = decode(c, dev, part_tokens=32)
+    assert not first[1].any()
+    again = decode(c, dev, part_tokens=32)
+    assert np.array_equal(first.view(np.uint32), again.view(np.uint32))
+    check_decode(c, dev, part_tokens=32)
+
+
+@pytest.mark.parametrize("hd,G,n_kv,pt", [
+    (128, 16, 2, 0), (128, 16, 2, 64),   # two groups of 8 heads per kv head
+    (64, 12, 1, 32),                     # two groups of 6
+    (256, 10, 1, 0),                     # two groups of 5
+    (128, 32, 1, 0),                     # one kv head for 32 query heads: four groups of 8
+    (128, 13, 1, 64),                    # a prime group size: thirteen groups of 1
+])
+def test_decode_large_groups(hd, G, n_kv, pt):
+    """More query heads per kv head than the matrix cores' 8-head column
+    set: the heads are split into equal groups (the largest divisor of G up
+    to 8 heads), each its own work item over the same K/V."""
+    lens = [1, 0, 31, 300, 700, 1500]
+    w = workloads.Workload("biggroup", len(lens), n_kv * G, n_kv, hd, 32, max(lens), ragged=True, table="pool",
+                           key=1400 + hd + G)
+    c = build(w, lens=lens)
+    say(f"large group hd={hd} G={G} n_kv={n_kv} part_tokens={pt}")
+    dev = gpu_cache(c)
+    got = decode(c, dev, part_tokens=pt)
+    assert not got[1].any()
+    check_decode(c, dev, part_tokens=pt)
+
+
+@pytest.mark.parametrize("amp", [1e-6, 1e-3, 1e3, 1e4, 1e6])
+def test_decode_v_amplitude(amp):
+    """V rows scaled by amp: V scales absmax / 127 from ~1e-8 to ~4e4.  The
+    P.V weights are carried as f16 (hi, lo) pairs of w * v_scale; they must
+    neither overflow (V scales of 256 and more once made whole rows NaN) nor
+    lose precision in the f16 subnormals (tiny V scales).  The output is
+    checked against the oracle's fp64 twin relative to the output's size."""
+    w = workloads.Workload("vamp", 3, 16, 2, 128, 32, 700, ragged=True, table="pool", key=1300)
+    c = build(w, lens=[700, 333, 64], with_cache=False)
+    for b in range(w.batch):
+        c.v_src[b] = (c.v_src[b] * np.float32(amp)).astype(np.float32)
+    from cases import host_cache
+    c.cache = host_cache(c)
+    say(f"V amplitude {amp:g}")
+    dev = gpu_cache(c)
+    for pt in (0, 64):
+        got = decode(c, dev, part_tokens=pt)
+        want64 = oracle.decode(c.q, c.cache, c.table, c.lens, c.scale, use_f64=True, threads=8)
+        assert np.all(np.isfinite(got))
+        ref = float(np.abs(want64).max())
+        err = float(np.abs(got - want64).max())
+        assert err <= 2e-5 * ref, f"amp {amp:g} split {pt}: max-abs error {err:.3g} vs output size {ref:.3g}"
+
+
+def test_decode_mixed_v_amplitudes():
+    """Tokens whose V rows span 2^-20 .. 2^20 in one sequence (the largest
+    V scale of each tile varies, so the kernel's V-scale exponent grows
+    mid-sequence): against the oracle's fp64 twin relative to the output."""
+    w = workloads.Workload("vmix", 2, 16, 2, 128, 32, 900, ragged=True, table="pool", key=1310)
+    c = build(w, lens=[900, 517], with_cache=False)
+    rng = np.random.default_rng(1310)
+    for b in range(w.batch):
+        f = np.exp2(rng.uniform(-20, 20, size=(c.v_src[b].shape[0], 1, 1))).astype(np.float32)
+        c.v_src[b] = (c.v_src[b] * f).astype(np.float32)
+    from cases import host_cache
+    c.cache = host_cache(c)
+    dev = gpu_cache(c)
+    got = decode(c, dev, part_tokens=64)
+    want64 = oracle.decode(c.q, c.cache, c.table, c.lens, c.scale, use_f64=True, threads=8)
+    assert np.all(np.isfinite(got))
+    for b in range(w.batch):
+        for h in range(w.n_q):
+            ref = float(np.abs(want64[b, h]).max())
+            err = float(np.abs(got[b, h] - want64[b, h]).max())
+            assert err <= 2e-5 * ref, f"seq {b} head {h}: {err:.3g} vs {ref:.3g}"
 
 
 def test_decode_long_peaked_tail_precision():

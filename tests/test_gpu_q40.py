@@ -127,7 +127,8 @@ def run_decode(c, dev, host, part_tokens=0):
 
 
 @pytest.mark.parametrize("hd,G,kv_bs", [(64, 1, 16), (64, 8, 32), (128, 3, 16), (128, 8, 128),
-                                        (256, 2, 64), (256, 8, 16), (128, 5, 256), (128, 4, 64)])
+                                        (256, 2, 64), (256, 8, 16), (128, 5, 256), (128, 4, 64),
+                                        (128, 16, 64), (64, 12, 16)])  # more heads than one MFMA column set
 def test_q40_decode_shapes(hd, G, kv_bs):
     lens = [1, 0, 16, 17, 33, kv_bs, kv_bs + 1, 2 * kv_bs + 7, 300]
     w = workloads.Workload("q40shape", len(lens), 2 * G, 2, hd, kv_bs, max(lens), ragged=True, table="pool",
