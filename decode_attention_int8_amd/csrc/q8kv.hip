@@ -33,9 +33,9 @@
 //     overflow nor sink into the subnormals whatever the V amplitude (the
 //     state's normalisation point moves with E, as it does with the max);
 //   * ranges longer than one partition are merged with the log-sum-exp rule
-//     in a fixed order (deterministic), inside the decode kernel: by the
-//     workgroup that stores a group's last state, in one level for small
-//     groups and in two (runs of partitions, then the runs) for large ones.
+//     in partition order (deterministic): inside the decode kernel by the
+//     workgroup that stores a group's last state when the group is small,
+//     else by a combine kernel.
 // Scores are kept in the log2 domain (softmax scale pre-multiplied by log2 e)
 // so every exponential is one v_exp_f32.
 //
@@ -352,10 +352,9 @@ __device__ __forceinline__ void v_dword_to_f16(const u32x4 (&vch)[2][Geo<HD>::NP
 // otherwise a persistent grid takes them from an atomic ticket (see
 // GridMode).  An item's arithmetic does not depend on which workgroup runs
 // it, so results are deterministic.  A sequence with one partition writes
-// its output directly; longer ones store each partition's state (M, S, acc)
-// and the workgroup that stores the last of them merges them in a fixed
-// order (one level for small groups, two levels -- runs of partitions, then
-// the runs -- for large ones).
+// its output directly; longer ones store each partition's state (M, S, acc),
+// merged in partition order by the workgroup that stores the last of them
+// when the group is small, else by q8kv_combine_kernel.
 constexpr int kMaxBatch = 2048;   // sequences per call (LDS prefix sums)
 constexpr int kClasses = 16;      // remainder classes of the persistent grid's item order
 constexpr int kNoPartial = 255;   // class of a sequence without a partial partition
@@ -370,23 +369,14 @@ struct DecodeArgs {
     const float* vs;
     const int32_t* table;
     const int32_t* lens;
-    // Partition states: accumulators [batch][n_kv][n_parts + n_runs][G][hd]
-    // and (max in log2 units, exp-sum) [batch][n_kv][n_parts + n_runs][G][2];
-    // a group's run states (two-level merge) follow its partition states.
+    // Partition states: accumulators [batch][n_hk][n_parts][G][hd] and
+    // (normalisation point in log2 units, exp-sum) [batch][n_hk][n_parts][G][2]
     float* st_acc;
     float* st_ms;
     int* ticket;    // [2]: next work item, workgroups done (zero between calls);
                     // NULL when every item has its own workgroup
-    // Merge counters, all zero between calls (every call leaves them zero).
-    // merge 1: arrive [batch][n_hk] int, partitions of a (sequence, head group)
-    // stored so far.  merge 2: arrive holds one 64-bit word per (sequence,
-    // head group) -- bits 0-15 partitions stored, bits 32-63 runs whose
-    // merged state is stored -- followed by int run counters
-    // [batch][n_hk][n_runs], partitions of the run stored so far.
-    int* arrive;
-    int merge;       // 0: no group spans several partitions; 1: one level; 2: two levels
-    int run;         // merge 2: partitions per run
-    int n_runs;      // merge 2: runs of the longest possible sequence (else 0)
+    int* arrive;    // [batch][n_hk]: partitions of a (sequence, head group) stored so far
+                    // (zero between calls); NULL when q8kv_combine_kernel merges
     int batch, max_blocks, num_blocks, n_q, n_kv, kv_bs, group, part_tokens, n_parts;
     // Query heads per kv head above kHeadGroup: they are split into hgs
     // groups of `group` heads, each its own work item (reading the kv head's
@@ -495,7 +485,7 @@ __device__ void merge_group(const DecodeArgs& a, size_t gi, int np, float* out_r
     constexpr int Q4 = HD / 4;
     const int G = a.group;
     const int slices = G * Q4;
-    const size_t first = gi * (a.n_parts + a.n_runs) * G;  // state of (partition 0, head 0)
+    const size_t first = gi * a.n_parts * G;  // state of (partition 0, head 0)
     const __amdgpu_buffer_rsrc_t racc = state_rsrc(a.st_acc + first * HD, (uint32_t)(np * G * HD * 4));
     const __amdgpu_buffer_rsrc_t rms = state_rsrc(a.st_ms + first * 2, (uint32_t)(np * G * 8));
     const uint32_t pstride = (uint32_t)(G * HD * 4);  // bytes between partitions
@@ -527,166 +517,6 @@ __device__ void merge_group(const DecodeArgs& a, size_t gi, int np, float* out_r
         group_max_sum(lms, G, e4 / Q4, np, Mx, St);
         at = weigh_slices(v, lms, G, e4 / Q4, Mx, 0, 1, np);
         *reinterpret_cast<f32x4*>(out_rows + (size_t)e4 * 4) = at / St;
-    }
-}
-
-// Two-level merge of large groups (more partition states than one workgroup
-// merges at once).  The partitions of a (sequence, kv head) form runs of
-// a.run consecutive partitions.  The workgroup that stores a run's last
-// partition state folds the run into a run state
-//   M_j = max_p M_p,  S_j = sum_p S_p f_p,  acc_j = sum_p acc_p f_p,
-//   f_p = 2^(M_p - M_j)   (partition order),
-// stores it and sets the run's bit in the group's word.  The workgroup that
-// stores the group's last partition state writes
-//   out = sum_j acc_j 2^(M_j - M*) / sum_j S_j 2^(M_j - M*),  M* = max_j M_j
-// (run order), reading the run states whose bits it saw and folding every
-// other run from its partition states itself, with the same code: every
-// sum is an explicit fused multiply-add, so a run state has the same bits
-// whichever workgroup folds it, and the output does not depend on which run
-// merges had finished.  This is the page's rescale rule applied to whole
-// partitions and runs.
-constexpr int kRunMax = 16;      // partitions per run
-constexpr int kRunsMax = 32;     // runs per group (the word's 32 mask bits)
-// State slices a thread has in flight in the two-level merge: static grids
-// run two waves per SIMD, so their kernels have registers for a batch that
-// covers a whole final merge; persistent grids (three waves per SIMD) take
-// smaller batches.
-constexpr int kMergeBatch = 24;
-constexpr int kMergeBatchPersistent = 8;
-constexpr int kSlotMerged = 1 << 30;  // slot word: a stored run state (else a partition state)
-constexpr int kSlotLast = 1 << 29;    // slot word: the run's last slot
-
-__device__ __forceinline__ f32x4 fma4(f32x4 x, float f, f32x4 y) {
-    return f32x4{__builtin_fmaf(x.x, f, y.x), __builtin_fmaf(x.y, f, y.y), __builtin_fmaf(x.z, f, y.z),
-                 __builtin_fmaf(x.w, f, y.w)};
-}
-
-// Merge runs j0 .. j1-1 of group gi (np_b partitions).  mask: runs whose
-// stored state may be read.  final: write the output rows; else (one run)
-// store the run's state.  LDS: lf [np_b][G] partition factors, lrm
-// [j1-j0][G] run (M, S), lslot [kMaxParts + 1] the slot list and its length.
-// Every load of a batch is issued unconditionally, so that all are in
-// flight at once (a load under a branch is preceded by a wait for the ones
-// before it); a slot past the list loads from past the buffer's end, which a
-// buffer load returns as zeros, and its value is not used.
-template <int B>
-__device__ __forceinline__ void load_slot_batch(f32x4 (&v)[B], __amdgpu_buffer_rsrc_t racc, const int* lslot,
-                                                int base, int nslot, uint32_t voff, uint32_t sstride, bool live) {
-#pragma unroll
-    for (int i = 0; i < B; ++i) {
-        const int sw = lslot[min(base + i, nslot - 1)];
-        v[i] = state_load4(racc, live && base + i < nslot ? voff + (uint32_t)(sw & 0xffff) * sstride : 0xfffffff0u, 0);
-    }
-}
-
-template <int HD, int NT, int B>
-__device__ __forceinline__ void merge_runs(size_t gi, int np_b, int j0, int j1, uint32_t mask, bool final,
-                                           float* out_rows, int tid, float* lf, float2* lrm, int* lslot) {
-    constexpr int Q4 = HD / 4;
-    ConstArgs& a = *kernel_args();
-    const int G = a.group, RUN = a.run;
-    const int nst = a.n_parts + a.n_runs;  // states per group: partitions, then runs
-    const size_t first = gi * nst * G;     // state (partition 0, head 0) of the group
-    const __amdgpu_buffer_rsrc_t racc = state_rsrc(a.st_acc + first * HD, (uint32_t)(nst * G * HD * 4));
-    const __amdgpu_buffer_rsrc_t rms = state_rsrc(a.st_ms + first * 2, (uint32_t)(nst * G * 8));
-    const int nrun = j1 - j0;
-    const int slices = G * Q4;
-    const uint32_t sstride = (uint32_t)(G * HD * 4);  // bytes between consecutive states
-    // The slot list (wave 0, one lane per run): a read run state is one slot,
-    // any other run one slot per partition, all in run order.  Slot word:
-    // bits 0-15 the state index, 16-23 the run (from j0), flags above.
-    if (tid < kWave) {
-        const int j = j0 + tid;
-        const bool live = tid < nrun;
-        const bool merged = live && ((mask >> j) & 1u);
-        const int c = !live ? 0 : merged ? 1 : min(RUN, np_b - j * RUN);
-        int incl = c;
-#pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) {
-            const int v = __shfl_up(incl, off);
-            if (tid >= off) incl += v;
-        }
-        const int start = incl - c;
-        if (merged) lslot[start] = kSlotMerged | kSlotLast | (tid << 16) | (a.n_parts + j);
-        else
-            for (int i = 0; i < c; ++i) lslot[start + i] = (i == c - 1 ? kSlotLast : 0) | (tid << 16) | (j * RUN + i);
-        if (tid == kWave - 1) lslot[kMaxParts] = incl;
-    }
-    __syncthreads();
-    const int nslot = __builtin_amdgcn_readfirstlane(lslot[kMaxParts]);
-    // The first slice's accumulator loads go out before the (M, S) round
-    // trip, so the two overlap.
-    auto slice_off = [&](int e4) {
-        const int g = e4 / Q4;
-        return (uint32_t)(g * HD * 4 + (e4 - g * Q4) * 16);  // the slice inside a state
-    };
-    f32x4 v[B];
-    load_slot_batch<B>(v, racc, lslot, 0, nslot, slice_off(min(tid, slices - 1)), sstride, tid < slices);
-    // Run (M_j, S_j) and partition factors: one thread per (run, head).
-    for (int t = tid; t < nrun * G; t += NT) {
-        const int j = j0 + t / G, g = t - (t / G) * G;
-        float Mj, Sj;
-        if ((mask >> j) & 1u) {
-            const float2 ms = state_load2(rms, (uint32_t)((a.n_parts + j) * G + g) * 8);
-            Mj = ms.x;
-            Sj = ms.y;
-        } else {
-            const int p0 = j * RUN, rs = min(RUN, np_b - p0);
-            float2 ms[kRunMax];
-#pragma unroll
-            for (int i = 0; i < kRunMax; ++i)
-                ms[i] = state_load2(rms, i < rs ? (uint32_t)((p0 + i) * G + g) * 8 : 0xfffffff0u);
-            Mj = -INFINITY;
-#pragma unroll
-            for (int i = 0; i < kRunMax; ++i) Mj = i < rs ? fmaxf(Mj, ms[i].x) : Mj;
-            Sj = 0.0f;
-#pragma unroll
-            for (int i = 0; i < kRunMax; ++i) {
-                const float f = __builtin_amdgcn_exp2f(ms[i].x - Mj);
-                Sj = i < rs ? __builtin_fmaf(ms[i].y, f, Sj) : Sj;
-                if (i < rs) lf[(p0 + i) * G + g] = f;
-            }
-        }
-        lrm[(j - j0) * G + g] = make_float2(Mj, Sj);
-    }
-    __syncthreads();
-    for (int e4 = tid; e4 < slices; e4 += NT) {
-        const int g = e4 / Q4;
-        const uint32_t voff = slice_off(e4);
-        float Mx = -INFINITY, St = 0.0f;
-        if (final) {
-            for (int j = 0; j < nrun; ++j) Mx = fmaxf(Mx, lrm[j * G + g].x);
-            for (int j = 0; j < nrun; ++j)
-                St = __builtin_fmaf(lrm[j * G + g].y, __builtin_amdgcn_exp2f(lrm[j * G + g].x - Mx), St);
-        }
-        f32x4 at = {0.f, 0.f, 0.f, 0.f}, accj = {0.f, 0.f, 0.f, 0.f};
-        for (int base = 0; base < nslot; base += B) {
-            if (base > 0 || e4 != tid) load_slot_batch<B>(v, racc, lslot, base, nslot, voff, sstride, true);
-#pragma unroll
-            for (int i = 0; i < B; ++i) {
-                // branch-free: the slot words are uniform, but held in vector registers
-                const int sw = lslot[min(base + i, nslot - 1)];
-                const bool use = base + i < nslot;
-                const int src = sw & 0xffff;
-                const bool merged = (sw & kSlotMerged) != 0;
-                const float f = lf[merged ? 0 : src * G + g];
-                const f32x4 na = merged ? v[i] : fma4(v[i], f, accj);
-                accj = use ? na : accj;
-                if (final) {
-                    const bool last = use && (sw & kSlotLast) != 0;
-                    const float e = __builtin_amdgcn_exp2f(lrm[((sw >> 16) & 0xff) * G + g].x - Mx);
-                    const f32x4 nat = fma4(accj, e, at);
-                    at = last ? nat : at;
-                    accj = last ? f32x4{0.f, 0.f, 0.f, 0.f} : accj;
-                }
-            }
-        }
-        if (final) {
-            *reinterpret_cast<f32x4*>(out_rows + (size_t)e4 * 4) = at / St;
-        } else {
-            state_store4(racc, voff + (uint32_t)(a.n_parts + j0) * sstride, accj);
-            if (e4 == g * Q4) state_store2(rms, (uint32_t)((a.n_parts + j0) * G + g) * 8, lrm[g]);
-        }
     }
 }
 
@@ -1487,17 +1317,12 @@ __device__ __forceinline__ void q4_offset_fix(f32x4 (&acc)[Geo<HD>::BPL], const 
 enum GridMode { kPersistent = 0, kStatic = 1 };
 enum CodecKind { kQ8 = 0, kFp8 = 1, kQ40 = 2 };
 
-// M2: the kernel carries the two-level merge (a persistent grid whose
-// groups all fit the one-level merge runs without it: its registers are
-// then allocated for the tile loop alone).
-template <int HD, int MODE, bool NEW, int CODEC = kQ8, int NW = kWaves, bool M2 = true>
-__global__ __launch_bounds__(kWave * NW)
-__attribute__((amdgpu_waves_per_eu(HD == 256 ? 1 : MODE == kStatic ? 2 : 3))) void
+template <int HD, int MODE, bool NEW, int CODEC = kQ8, int NW = kWaves>
+__global__ __launch_bounds__(kWave * NW) __attribute__((amdgpu_waves_per_eu(HD == 256 ? 1 : 3))) void
 q8kv_decode_kernel(const DecodeArgs a) {
     using GG = Geo<HD>;
     constexpr int NT = kWave * NW;  // threads per workgroup
     constexpr bool STATIC = MODE == kStatic;
-    constexpr int kMB = STATIC ? kMergeBatch : kMergeBatchPersistent;
     constexpr bool FP8 = CODEC == kFp8;
     constexpr bool Q40 = CODEC == kQ40;
     static_assert(!(NEW && CODEC != kQ8), "the fused append is an int8-codec path");
@@ -1518,15 +1343,8 @@ q8kv_decode_kernel(const DecodeArgs a) {
     __shared__ int lscan[NW];
     __shared__ int litem;
     __shared__ int lflag;
-    __shared__ uint32_t lmask;
     __shared__ float2 lms[kFuseRows];
     __shared__ f32x4 lred[NT];
-    // the two-level merge reuses LDS that is free once the partition state is
-    // stored: lacc for the partition factors, lred for the run (M, S) and
-    // the slot list
-    static_assert(sizeof(lacc) >= sizeof(float) * kMaxParts * kHeadGroup, "partition factors do not fit");
-    static_assert(sizeof(lred) >= sizeof(float2) * kRunsMax * kHeadGroup + sizeof(int) * (kMaxParts + 1),
-                  "run states and slots do not fit");
     // fused append: the new token's codes, factors and block
     __shared__ __attribute__((aligned(16))) int8_t lnew[NEW ? 2 * HD : 16];
     __shared__ float lnew_sc[2];
@@ -1820,7 +1638,7 @@ q8kv_decode_kernel(const DecodeArgs a) {
 
         // merge the waves' states (same rescale rule, wave order fixed); write
         // the output (one partition) or this partition's state
-        const size_t state0 = (((size_t)b * a.n_hk + ih) * (a.n_parts + a.n_runs) + part) * G;
+        const size_t state0 = (((size_t)b * a.n_hk + ih) * a.n_parts + part) * G;
         const __amdgpu_buffer_rsrc_t racc = state_rsrc(a.st_acc + state0 * HD, (uint32_t)(G * HD * 4));
         const __amdgpu_buffer_rsrc_t rms = state_rsrc(a.st_ms + state0 * 2, (uint32_t)(G * 8));
         for (int e4 = itid; e4 < G * Q4; e4 += NT) {
@@ -1844,7 +1662,7 @@ q8kv_decode_kernel(const DecodeArgs a) {
                 if (i4 == 0) state_store2(rms, (uint32_t)g * 8, make_float2(Mx, St));
             }
         }
-        if (np_b > 1 && a.merge == 1) {
+        if (a.arrive && np_b > 1) {
             // the workgroup storing the group's last state merges the group
             wait_stores();
             __syncthreads();
@@ -1857,56 +1675,6 @@ q8kv_decode_kernel(const DecodeArgs a) {
             }
             __syncthreads();
             if (lflag) merge_group<HD, NT>(a, (size_t)b * a.n_hk + ih, np_b, out_rows, itid, lms, lred);
-        } else if (M2 && np_b > 1) {
-            // two levels: every arrival counts itself in its run's counter
-            // and in the group's word (one round trip for both); the last
-            // arrival of the group writes the output, the last arrival of
-            // any other run merges its run
-            wait_stores();
-            __syncthreads();
-            ConstArgs* ka = kernel_args();
-            const size_t gi = (size_t)b * ka->n_hk + ih;
-            const int k = part / ka->run;
-            const int nr_b = (np_b + ka->run - 1) / ka->run;
-            unsigned long long* word = reinterpret_cast<unsigned long long*>(ka->arrive) + gi;
-            if (itid == 0) {
-                int* rc = ka->arrive + 2 * (size_t)ka->batch * ka->n_hk + gi * ka->n_runs + k;
-                const int prev_r = __hip_atomic_fetch_add(rc, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                const unsigned long long prev_w =
-                    __hip_atomic_fetch_add(word, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                const bool last_run = prev_r == min(ka->run, np_b - k * ka->run) - 1;
-                if (last_run) __hip_atomic_store(rc, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                const bool fin = (int)(prev_w & 0xffffu) + 1 == np_b;
-                const uint32_t mask = (uint32_t)(prev_w >> 32);
-                // the last arrival takes out every arrival and the run bits it
-                // has seen; a bit set later is taken out by its setter
-                if (fin)
-                    __hip_atomic_fetch_sub(word, (unsigned long long)np_b | ((unsigned long long)mask << 32),
-                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                lflag = fin ? 2 : last_run ? 1 : 0;
-                lmask = mask;
-            }
-            __syncthreads();
-            float* lf = &lacc[0][0][0];
-            float2* lrm = reinterpret_cast<float2*>(lred);
-            int* lslot = reinterpret_cast<int*>(lrm + kRunsMax * kHeadGroup);
-            if (lflag == 2) {
-                merge_runs<HD, NT, kMB>(gi, np_b, 0, nr_b, lmask, true, out_rows, itid, lf, lrm, lslot);
-            } else if (lflag == 1) {
-                merge_runs<HD, NT, kMB>(gi, np_b, k, k + 1, 0u, false, out_rows, itid, lf, lrm, lslot);
-                wait_stores();
-                __syncthreads();
-                if (itid == 0) {
-                    const unsigned long long bit = 1ull << (32 + k);
-                    const unsigned long long prev_w =
-                        __hip_atomic_fetch_add(word, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    const int arrived = (int)(prev_w & 0xffffu);
-                    // the group's last arrival has come (np_b) or has already
-                    // cleared the word (0): it will not read this bit
-                    if (arrived == np_b || arrived == 0)
-                        __hip_atomic_fetch_sub(word, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                }
-            }
         }
         // next item (the barrier also keeps LDS from being reused too early)
         if (STATIC || !a.ticket) break;
@@ -1924,6 +1692,87 @@ q8kv_decode_kernel(const DecodeArgs a) {
             __hip_atomic_store(a.ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(a.ticket + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
+    }
+}
+
+struct CombineArgs {
+    float* out;
+    const float* st_acc;
+    const float* st_ms;
+    const int32_t* lens;
+    int n_q, n_hk, group, cap, part_tokens, n_parts;
+};
+
+// Merge the partition states of one (sequence, query head) with the rescale
+// rule: M* = max M_p, S* = sum S_p 2^(M_p - M*), out = sum acc_p 2^(M_p - M*) / S*.
+// Thread (row r, slice i4) owns partitions p = r, r + R, ... and sums them in
+// increasing order; the R row sums are then added in row order, so the result
+// is deterministic.  All state loads are issued at once, together with the
+// length read (slots past the sequence's partitions are read but never used).
+template <int HD>
+__global__ __launch_bounds__(kThreads) void q8kv_combine_kernel(const CombineArgs a) {
+    constexpr int Q4 = HD / 4;          // float4 slices per head row
+    constexpr int R = kThreads / Q4;    // partitions summed in parallel
+    constexpr int PER = kMaxParts / R;  // partitions per thread at most
+    __shared__ f32x4 lpart[R][Q4];
+    __shared__ float lsp[R];
+    __shared__ float lmax[kWaves];
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid >> 6;
+    const int h = blockIdx.x % a.n_q, b = blockIdx.x / a.n_q;
+    const int ih = h / a.group, g = h % a.group;  // head group, head in it
+    const size_t first = (((size_t)b * a.n_hk + ih) * a.n_parts) * a.group + g;  // state of p = 0
+    const size_t pstride = (size_t)a.group;                                        // states per partition
+    const int i4 = tid % Q4, r = tid / Q4;
+
+    f32x4 v[PER];
+    float2 ms[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        const int p = r + k * R;
+        if (p < a.n_parts) {
+            v[k] = *reinterpret_cast<const f32x4*>(a.st_acc + (first + p * pstride) * HD + 4 * i4);
+            ms[k] = *reinterpret_cast<const float2*>(a.st_ms + (first + p * pstride) * 2);
+        }
+    }
+    const int L = min(a.lens[b], a.cap);
+    if (L <= 0) return;
+    const int np = (L + a.part_tokens - 1) / a.part_tokens;
+    if (np <= 1) return;
+
+    float mx = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < PER; ++k)
+        if (r + k * R < np) mx = fmaxf(mx, ms[k].x);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    if (lane == 0) lmax[wid] = mx;
+    __syncthreads();
+    float Mx = lmax[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) Mx = fmaxf(Mx, lmax[w]);
+
+    f32x4 at = {0.f, 0.f, 0.f, 0.f};
+    float sp = 0.0f;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        if (r + k * R < np) {
+            const float w = __builtin_amdgcn_exp2f(ms[k].x - Mx);
+            at += v[k] * w;
+            sp += ms[k].y * w;
+        }
+    }
+    lpart[r][i4] = at;
+    if (i4 == 0) lsp[r] = sp;
+    __syncthreads();
+    if (r == 0) {
+        f32x4 t = lpart[0][i4];
+        float St = lsp[0];
+#pragma unroll
+        for (int rr = 1; rr < R; ++rr) {
+            t += lpart[rr][i4];
+            St += lsp[rr];
+        }
+        *reinterpret_cast<f32x4*>(a.out + ((size_t)b * a.n_q + h) * HD + 4 * i4) = t / St;
     }
 }
 
@@ -2740,10 +2589,9 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 // append of the new token, the FP8 codec.
 enum Variant { kVarQ8 = 0, kVarQ8New = 1, kVarFp8 = 2, kVarQ40 = 3 };
 
-template <int HD, int VAR, int MODE, int NW = kWaves, bool M2 = true>
+template <int HD, int VAR, int MODE, int NW = kWaves>
 constexpr auto decode_kernel_ptr() {
-    return q8kv_decode_kernel<HD, MODE, VAR == kVarQ8New, VAR == kVarFp8 ? kFp8 : VAR == kVarQ40 ? kQ40 : kQ8, NW,
-                              M2>;
+    return q8kv_decode_kernel<HD, MODE, VAR == kVarQ8New, VAR == kVarFp8 ? kFp8 : VAR == kVarQ40 ? kQ40 : kQ8, NW>;
 }
 
 // Wide (kWideWaves) workgroups serve static grids of at most one workgroup
@@ -2759,7 +2607,7 @@ int launch_info_hd(int dev, LaunchInfo& li) {
     if (e == hipSuccess) e = hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev);
     if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &per_cu, reinterpret_cast<const void*>(decode_kernel_ptr<HD, VAR, kPersistent, kWaves, false>()), kThreads, 0);
+        &per_cu, reinterpret_cast<const void*>(decode_kernel_ptr<HD, VAR, kPersistent>()), kThreads, 0);
     if (e != hipSuccess) return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
     li.resident = std::max(1, li.cus * std::max(1, per_cu));
     // A static grid of at most two workgroups per CU is spread evenly when a
@@ -2810,12 +2658,7 @@ int launch_info(int dev, int hd, int var, LaunchInfo* out) {
 template <int HD, int VAR>
 void launch_decode_hd(int mode, bool wide, unsigned grid, size_t lds, hipStream_t st, const DecodeArgs& da) {
     if (mode == kPersistent) {
-        if (da.merge == 2)
-            hipLaunchKernelGGL((decode_kernel_ptr<HD, VAR, kPersistent, kWaves, true>()), dim3(grid), dim3(kThreads), 0,
-                               st, da);
-        else
-            hipLaunchKernelGGL((decode_kernel_ptr<HD, VAR, kPersistent, kWaves, false>()), dim3(grid), dim3(kThreads),
-                               0, st, da);
+        hipLaunchKernelGGL((decode_kernel_ptr<HD, VAR, kPersistent>()), dim3(grid), dim3(kThreads), 0, st, da);
         return;
     }
     if constexpr (wide_hd(HD)) {
@@ -2895,8 +2738,7 @@ int decode_impl(float* out, const float* q, const int8_t* kp, const int8_t* vp, 
     rc = launch_info(dev, hd, var, &li);
     if (rc) return rc;
     const unsigned grid = (unsigned)std::min<long long>(items, li.resident);
-    DecodeArgs da{out, q, kp, vp, ks, vs, table, lens, nullptr, nullptr, nullptr, nullptr,
-                  0, 0, 0, batch, max_blocks, num_blocks, n_q, n_kv, kv_bs, G, pt, np, hgs, n_hk, scale * kLog2e,
+    DecodeArgs da{out, q, kp, vp, ks, vs, table, lens, nullptr, nullptr, nullptr, nullptr, batch, max_blocks, num_blocks, n_q, n_kv, kv_bs, G, pt, np, hgs, n_hk, scale * kLog2e,
                   knew, vnew, new_dtype, ks8, vs8, head_tables ? n_kv : 1};
     if (items > (long long)grid) {
         std::lock_guard<std::mutex> lock(g_mu);
@@ -2919,27 +2761,15 @@ int decode_impl(float* out, const float* q, const int8_t* kp, const int8_t* vp, 
     const int mode = items > (long long)grid ? kPersistent : kStatic;
     const bool wide = mode == kStatic && wide_hd(hd) && grid <= (unsigned)li.cus && g_wide.load() != 0;
     const int nt = wide ? kWave * kWideWaves : kThreads;
-    // Partition states are merged inside the decode kernel: in one level
-    // when a group's states fit one workgroup's loads, else in two (runs of
-    // about sqrt(np) partitions, then the runs).
+    // small groups of partition states are merged inside the decode kernel
     const int slices = G * hd / 4;
     const int rows_par = slices >= nt ? 1 : nt / slices;
-    if (np > 1) {
-        const bool one = np * G <= kFuseRows && (np + rows_par - 1) / rows_par <= kFusePer;
-        da.merge = one ? 1 : 2;
-        if (!one) {
-            int run = (int)std::ceil(std::sqrt((double)np));
-            run = std::max(run, (np + kRunsMax - 1) / kRunsMax);
-            da.run = std::min(run, kRunMax);
-            da.n_runs = (np + da.run - 1) / da.run;
-        }
-    }
+    const bool fuse = np > 1 && np * G <= kFuseRows && (np + rows_par - 1) / rows_par <= kFusePer;
     if (np > 1) {
         const size_t groups = (size_t)batch * n_hk;
-        const size_t n_state = groups * (size_t)(np + da.n_runs) * G;
+        const size_t n_state = groups * (size_t)np * G;
         const size_t acc_bytes = align256(n_state * hd * sizeof(float));
         const size_t need = acc_bytes + n_state * 2 * sizeof(float);
-        const size_t need_arrive = da.merge == 1 ? groups : 2 * groups + groups * (size_t)da.n_runs;
         std::lock_guard<std::mutex> lock(g_mu);
         Workspace& w = g_ws[{dev, stream}];
         if (w.bytes < need) {
@@ -2960,7 +2790,7 @@ int decode_impl(float* out, const float* q, const int8_t* kp, const int8_t* vp, 
         }
         da.st_acc = static_cast<float*>(w.ptr);
         da.st_ms = reinterpret_cast<float*>(static_cast<char*>(w.ptr) + acc_bytes);
-        if (w.arrive_n < need_arrive) {
+        if (fuse && w.arrive_n < groups) {
             if (w.arrive) {
                 e = hipStreamSynchronize(st);
                 if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
@@ -2970,24 +2800,35 @@ int decode_impl(float* out, const float* q, const int8_t* kp, const int8_t* vp, 
                 if (e != hipSuccess) return hip_fail(e, "hipFree");
             }
             void* t = nullptr;
-            e = hipMalloc(&t, need_arrive * sizeof(int));
+            e = hipMalloc(&t, groups * sizeof(int));
             if (e != hipSuccess) return fail(Q8KV_ENOMEM, "hipMalloc of the merge counters: %s", hipGetErrorString(e));
             // cleared by a kernel, not a memset node (callers may capture the call)
-            e = launch_zero(t, need_arrive, st);
+            e = launch_zero(t, groups, st);
             if (e != hipSuccess) {
                 (void)hipFree(t);
                 return hip_fail(e, "merge counter clear");
             }
             w.arrive = static_cast<int*>(t);
-            w.arrive_n = need_arrive;
+            w.arrive_n = groups;
         }
-        da.arrive = w.arrive;
+        if (fuse) da.arrive = w.arrive;
     }
     const size_t lds = wide ? (size_t)li.wide_lds
                        : mode == kStatic && grid <= 2u * (unsigned)li.cus ? (size_t)li.static_lds : 0;
     launch_decode(hd, var, mode, wide, grid, lds, st, da);
     e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
+    if (np > 1 && !fuse) {
+        CombineArgs ca{out, da.st_acc, da.st_ms, lens, n_q, n_hk, G, max_tokens, pt, np};
+        const unsigned cgrid = (unsigned)(batch * n_q);
+        switch (hd) {
+            case 64: hipLaunchKernelGGL(q8kv_combine_kernel<64>, dim3(cgrid), dim3(kThreads), 0, st, ca); break;
+            case 128: hipLaunchKernelGGL(q8kv_combine_kernel<128>, dim3(cgrid), dim3(kThreads), 0, st, ca); break;
+            default: hipLaunchKernelGGL(q8kv_combine_kernel<256>, dim3(cgrid), dim3(kThreads), 0, st, ca); break;
+        }
+        e = hipGetLastError();
+        if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
+    }
     return Q8KV_OK;
 }
 

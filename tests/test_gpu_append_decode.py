@@ -123,8 +123,8 @@ def test_append_decode_shapes(hd, G, kv_bs):
 @pytest.mark.parametrize("pt", [32, 64, 96, 128])
 def test_append_decode_split_and_merge(pt):
     """Split contexts: the new token falls in the last partition, whichever
-    wave owns its tile; one-level merge (few partitions) and the two-level
-    merge (many)."""
+    wave owns its tile; in-kernel merge (few partitions) and the combine
+    kernel (many)."""
     lens = edge_lens(12, 16, pt)
     w = workloads.Workload("fusedsplit", 12, 8, 2, 128, 16, max(lens), ragged=True, table="pool",
                            key=1100 + pt)

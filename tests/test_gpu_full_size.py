@@ -1,6 +1,6 @@
 """GPU parity at the five workloads' full sizes, in the launch configuration
 the benchmark times (the default partition plan; static or persistent grid,
-one- or two-level merge as the shape decides), for the int8 codec
+in-kernel merge or combine kernel as the shape decides), for the int8 codec
 and the FP8 and q4_0 codecs, the fused append + decode and QUEST.
 
 The whole workload is appended on the GPU and decoded in one call.  The

@@ -2,7 +2,7 @@
 workspace, the persistent grid's work ticket, the in-kernel merge's arrival
 counters and the QUEST bounds buffer must all be left ready for any next
 call.  A sequence of calls of different shapes and entry points (static and
-persistent grids, one- and two-level merges, a workspace that has
+persistent grids, in-kernel and combine-kernel merges, a workspace that has
 to grow, the fused step, both codecs, QUEST) is run once, checked against the
 oracle, then run again in reverse order, on a second stream, on two streams
 at once and after q8kv_release: every output must repeat bit for bit.
@@ -29,7 +29,7 @@ def case(key, batch, G, hd, kv_bs, seq_len, lens=None):
 def test_mixed_calls_repeat_bitwise():
     small = case(4100, 3, 4, 128, 16, 300)                        # static grid, in-kernel merges
     wide = case(4101, 64, 8, 128, 32, 1024)                       # persistent grid
-    deep = case(4102, 2, 8, 64, 64, 9000, lens=[9000, 4500])      # two-level merge, large workspace
+    deep = case(4102, 2, 8, 64, 64, 9000, lens=[9000, 4500])      # combine kernel, large workspace
     caches = {id(c): gpu_cache(c) for c in (small, wide, deep)}
 
     def codec_cache(cls, c):
@@ -74,12 +74,12 @@ def test_mixed_calls_repeat_bitwise():
 
     calls = [
         ("small plain", lambda: plain(small, 0)),
-        ("deep plain (two-level)", lambda: plain(deep, 0)),
+        ("deep plain (combine)", lambda: plain(deep, 0)),
         ("wide plain (persistent)", lambda: plain(wide, 32)),
         ("small split 32", lambda: plain(small, 32)),
         ("deep split 64 (grows the workspace)", lambda: plain(deep, 64)),
         ("small fused", lambda: fused(small)),
-        ("deep fp8 (two-level)", lambda: codec(q8.fp8_decode_attn, fp8, deep, 0)),
+        ("deep fp8 (combine)", lambda: codec(q8.fp8_decode_attn, fp8, deep, 0)),
         ("small q4_0 split 32", lambda: codec(q8.q40_decode_attn, q40, small, 32)),
         ("wide quest", lambda: quest(wide)),
         ("deep q4_0 split 64", lambda: codec(q8.q40_decode_attn, q40, deep, 64)),
@@ -92,7 +92,7 @@ def test_mixed_calls_repeat_bitwise():
         say(f"mixed: {name}")
         first[name] = fn().cpu().numpy()
     # the plain decodes against the oracle
-    for name, c in (("small plain", small), ("deep plain (two-level)", deep), ("wide plain (persistent)", wide)):
+    for name, c in (("small plain", small), ("deep plain (combine)", deep), ("wide plain (persistent)", wide)):
         want = oracle.decode(c.q, c.cache, c.table, c.lens, c.scale, threads=8)
         assert float(np.abs(first[name] - want).max()) <= 2e-4, name
     # the same calls in reverse order, then on a second stream
@@ -112,7 +112,7 @@ def test_mixed_calls_repeat_bitwise():
     for _ in range(3):
         with torch.cuda.stream(s1):
             conc["wide plain (persistent)"] = plain(wide, 32)
-            conc["deep plain (two-level)"] = plain(deep, 0)
+            conc["deep plain (combine)"] = plain(deep, 0)
         with torch.cuda.stream(s2):
             conc["deep split 64 (grows the workspace)"] = plain(deep, 64)
             conc["small split 32"] = plain(small, 32)

@@ -180,13 +180,13 @@ def test_decode_hd_kv_bs(hd, kv_bs):
 @pytest.mark.parametrize("hd,G", [(64, 1), (64, 8), (128, 1), (128, 3), (128, 5), (128, 8),
                                   (256, 2), (256, 5), (256, 8)])
 def test_decode_split_merge_paths(hd, G):
-    """Partition states of a (sequence, kv head) are merged inside the decode
-    kernel by the workgroup that stores the last one: in one level when
-    there are at most 64 of them (partitions x query heads), else in two
-    (runs of partitions, then the runs).  The partition lengths here give 3
-    to 19 partitions, so each shape takes one or both paths, the one-level
-    one with one or several float4 slices per thread; each call is made
-    twice, since the merges leave their counters at zero for the next call."""
+    """Partition states of a (sequence, head group) are merged inside the
+    decode kernel by the workgroup that stores the last one when there are
+    at most 64 of them (partitions x query heads), else by the combine
+    kernel.  The partition lengths here give 3 to 19 partitions, so each
+    shape takes one or both paths, the in-kernel one with one or several
+    float4 slices per thread; each call is made twice, since the merge
+    leaves its arrival counters at zero for the next call."""
     w = workloads.Workload("merge", 3, 2 * G, 2, hd, 32, 600, ragged=True, table="pool",
                            key=800 + hd + G)
     c = build(w)
@@ -243,8 +243,8 @@ def test_decode_max_batch():
 
 @pytest.mark.parametrize("hd,G", [(64, 1), (128, 8), (256, 4)])
 def test_decode_max_partitions(hd, G):
-    """256 partitions of one sequence, the most a call plans: the two-level
-    merge at its widest (16 runs of 16 partitions) for every hd."""
+    """256 partitions of one sequence, the most a call plans: the combine
+    kernel's per-thread state arrays at their full length for every hd."""
     w = workloads.Workload("maxparts", 2, 2 * G, 2, hd, 32, 256 * 32, ragged=True, table="pool", key=960 + hd)
     c = build(w, lens=[256 * 32, 5000])
     say(f"max partitions hd={hd} G={G}")
@@ -260,17 +260,15 @@ def test_decode_max_partitions(hd, G):
     (128, 3, 2, [30 * 32, 23 * 32 - 1, 1, 0], 32),
     (64, 8, 1, [9 * 32, 17 * 32 + 1], 32),       # just past the one-level limit
 ])
-def test_decode_two_level_merge(hd, G, n_kv, lens, pt):
-    """Groups of more than 64 partition states: the last arrival of each run
-    of partitions stores the run's state, and the group's last arrival reads
-    the run states it finds stored and folds the other runs from their
-    partition states itself.  Which runs are stored when the last arrival
-    comes varies from call to call, so the output is checked against the
-    oracle and repeated bit for bit over several calls."""
+def test_decode_many_partition_states(hd, G, n_kv, lens, pt):
+    """Groups of more than 64 partition states (the 128K step's plan among
+    them) go to the combine kernel, static and persistent grids alike:
+    checked against the oracle and repeated bit for bit over several
+    calls."""
     w = workloads.Workload("merge2", len(lens), n_kv * G, n_kv, hd, 32 if pt == 32 else 64, max(lens),
                            ragged=True, table="pool", key=1100 + hd + G + n_kv)
     c = build(w, lens=lens)
-    say(f"two-level merge hd={hd} G={G} n_kv={n_kv} lens={lens} part_tokens={pt}")
+    say(f"many partition states hd={hd} G={G} n_kv={n_kv} lens={lens} part_tokens={pt}")
     dev = gpu_cache(c)
     first = decode(c, dev, part_tokens=pt)
     for _ in range(4):
@@ -279,15 +277,16 @@ def test_decode_two_level_merge(hd, G, n_kv, lens, pt):
     check_decode(c, dev, part_tokens=pt)
 
 
-def test_decode_two_level_merge_persistent():
-    """The two-level merge on the persistent grid: 24 sequences of up to 6000
-    tokens in 32-token partitions are ~9000 items, more than fit at once."""
+def test_decode_many_partition_states_persistent():
+    """Many partition states on the persistent grid: 24 sequences of up to
+    6000 tokens in 32-token partitions are ~9000 items, more than fit at
+    once."""
     rng = np.random.default_rng(1200)
     lens = [int(x) for x in rng.integers(1, 6001, size=24)]
     lens[:4] = [6000, 0, 33, 64 * 32]
     w = workloads.Workload("merge2p", 24, 16, 2, 128, 32, 6000, ragged=True, table="pool", key=1200)
     c = build(w, lens=lens)
-    say(f"two-level merge, persistent grid, tokens={int(c.lens.sum())}")
+    say(f"many partition states, persistent grid, tokens={int(c.lens.sum())}")
     dev = gpu_cache(c)
     first = decode(c, dev, part_tokens=32)
     assert not first[1].any()

@@ -3,7 +3,7 @@ one workgroup per CU at hd 64 and 128 runs 8-wave workgroups; other grids
 run 4-wave ones.  Each small case here fits such a grid, so it is decoded
 once with the 8-wave kernel and once, after q8kv_debug_set_wide(0), with the
 4-wave kernel, for every codec, the fused append + decode, and the three
-merge paths (one partition, one-level merge, two-level merge).  Both outputs
+merge paths (one partition, in-kernel merge, combine kernel).  Both outputs
 are checked against the oracle of their codec.
 """
 import numpy as np
@@ -50,7 +50,7 @@ def both(fn):
 
 
 # (part_tokens, what it exercises)
-SPLITS = [(0, "default plan"), (32, "one-level merge"), (None, "two-level merge")]
+SPLITS = [(0, "default plan"), (32, "in-kernel merge"), (None, "combine kernel")]
 
 
 @pytest.mark.parametrize("hd", [64, 128])
