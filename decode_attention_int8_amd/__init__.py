@@ -16,7 +16,9 @@ import re
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libq8kv.so")
+# Q8KV_LIBRARY names another build of the same library (the sanitizer test
+# loads one whose host code is instrumented); the default is the in-tree one.
+LIB_PATH = os.environ.get("Q8KV_LIBRARY") or os.path.join(_HERE, "libq8kv.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "q8kv.h")
 
 Q8KV_OK, Q8KV_EINVAL, Q8KV_ENULL, Q8KV_EHIP, Q8KV_ENOMEM = 0, -1, -2, -3, -4
@@ -48,6 +50,7 @@ def _load():
         "q8kv_decode_attn_heads": [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, P],
         "q8kv_fp8_decode_attn": [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, P],
         "q8kv_append": [P, P, P, P, P, P, I, P, I, I, I, I, I, P],
+        "q8kv_import_pages": [P, P, P, P, P, P, P, P, I, I, I, I, P],
         "q8kv_release": [],
         "q8kv_debug_quantize_q": [P, P, P, I, I, P],
         "q8kv_debug_block_dots": [P, I, P, P, P, P, I, I, I, I, I, I, I, P],
@@ -87,6 +90,16 @@ def _ptr(t):
 
 def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _call(dev, fn, args):
+    """One library call on device dev's current stream, with dev current
+    (the library keeps its workspaces per current device)."""
+    if torch.cuda.current_device() == dev:
+        _check(fn(*args, torch.cuda.current_stream(dev).cuda_stream))
+    else:
+        with torch.cuda.device(dev):
+            _check(fn(*args, torch.cuda.current_stream(dev).cuda_stream))
 
 
 def _ok(t, dtype, dev, ndim):
@@ -187,11 +200,31 @@ class PagedKVCache:
             raise ValueError("k_src/v_src must be [n_tokens][n_kv][hd] matching slot_mapping")
         args = (kp, vp, ks, vs, k_src.data_ptr(), v_src.data_ptr(), 1 if sd is torch.bfloat16 else 0,
                 slot_mapping.data_ptr(), n, self.num_blocks, self.n_kv, self.hd, self.kv_bs)
-        if torch.cuda.current_device() == dev:
-            _check(lib.q8kv_append(*args, torch.cuda.current_stream(dev).cuda_stream))
-        else:
-            with torch.cuda.device(dev):
-                _check(lib.q8kv_append(*args, torch.cuda.current_stream(dev).cuda_stream))
+        _call(dev, lib.q8kv_append, args)
+
+
+def import_pages(cache, k_rows, v_rows, k_row_scale, v_row_scale):
+    """Fill cache from an int8 cache in row order: k_rows, v_rows int8
+    [num_blocks][kv_bs][n_kv][hd], k_row_scale, v_row_scale fp32
+    [num_blocks][kv_bs][n_kv], on the cache's device.  Every page and scale
+    of cache is rewritten, bit for bit.  Returns cache."""
+    if not isinstance(cache, PagedKVCache) or cache.k_pages.dtype != torch.int8:
+        raise TypeError("import_pages fills an int8 PagedKVCache")
+    dev, kp, vp, ks, vs = cache._pointers()
+    d = cache.device
+    nb, n_kv, kv_bs, hd = cache.num_blocks, cache.n_kv, cache.kv_bs, cache.hd
+    for t, name in ((k_rows, "k_rows"), (v_rows, "v_rows")):
+        _need(t, name, torch.int8, d, 4)
+        if tuple(t.shape) != (nb, kv_bs, n_kv, hd):
+            raise ValueError(f"{name} must be [num_blocks][kv_bs][n_kv][hd] = {(nb, kv_bs, n_kv, hd)}")
+    for t, name in ((k_row_scale, "k_row_scale"), (v_row_scale, "v_row_scale")):
+        _need(t, name, torch.float32, d, 3)
+        if tuple(t.shape) != (nb, kv_bs, n_kv):
+            raise ValueError(f"{name} must be [num_blocks][kv_bs][n_kv] = {(nb, kv_bs, n_kv)}")
+    args = (kp, vp, ks, vs, k_rows.data_ptr(), v_rows.data_ptr(), k_row_scale.data_ptr(),
+            v_row_scale.data_ptr(), nb, n_kv, hd, kv_bs)
+    _call(dev, lib.q8kv_import_pages, args)
+    return cache
 
 
 def decode_attn(q, cache, block_table, seq_lens, scale, out=None, part_tokens=0):
@@ -219,12 +252,7 @@ def decode_attn(q, cache, block_table, seq_lens, scale, out=None, part_tokens=0)
     args = (out.data_ptr(), q.data_ptr(), kp, vp, ks, vs, block_table.data_ptr(), seq_lens.data_ptr(),
             block_table.shape[1], cache.num_blocks, batch, n_q, cache.n_kv, hd, cache.kv_bs, float(scale),
             int(part_tokens))
-    # the library allocates its workspace on the current device
-    if torch.cuda.current_device() == dev:
-        _check(lib.q8kv_decode_attn_split(*args, torch.cuda.current_stream(dev).cuda_stream))
-    else:
-        with torch.cuda.device(dev):
-            _check(lib.q8kv_decode_attn_split(*args, torch.cuda.current_stream(dev).cuda_stream))
+    _call(dev, lib.q8kv_decode_attn_split, args)
     return out
 
 
@@ -265,11 +293,7 @@ def append_decode_attn(q, cache, k_new, v_new, block_table, seq_lens, scale, out
             1 if nd is torch.bfloat16 else 0, kp, vp, ks, vs, block_table.data_ptr(),
             seq_lens.data_ptr(), block_table.shape[1], cache.num_blocks, batch, n_q, cache.n_kv, hd,
             cache.kv_bs, float(scale), int(part_tokens))
-    if torch.cuda.current_device() == dev:
-        _check(lib.q8kv_append_decode_attn(*args, torch.cuda.current_stream(dev).cuda_stream))
-    else:
-        with torch.cuda.device(dev):
-            _check(lib.q8kv_append_decode_attn(*args, torch.cuda.current_stream(dev).cuda_stream))
+    _call(dev, lib.q8kv_append_decode_attn, args)
     return out
 
 
@@ -328,8 +352,7 @@ class Fp8KVCache(PagedKVCache):
             raise ValueError("k_src/v_src must be [n_tokens][n_kv][hd] matching slot_mapping")
         args = (kp, vp, ks, vs, k_src.data_ptr(), v_src.data_ptr(), 1 if sd is torch.bfloat16 else 0,
                 slot_mapping.data_ptr(), n, self.num_blocks, self.n_kv, self.hd, self.kv_bs)
-        with torch.cuda.device(dev):
-            _check(lib.q8kv_fp8_append(*args, torch.cuda.current_stream(dev).cuda_stream))
+        _call(dev, lib.q8kv_fp8_append, args)
 
 
 class Q40KVCache(PagedKVCache):
@@ -388,8 +411,7 @@ class Q40KVCache(PagedKVCache):
             raise ValueError("k_src/v_src must be [n_tokens][n_kv][hd] matching slot_mapping")
         args = (kp, vp, ks, vs, k_src.data_ptr(), v_src.data_ptr(), 1 if sd is torch.bfloat16 else 0,
                 slot_mapping.data_ptr(), n, self.num_blocks, self.n_kv, self.hd, self.kv_bs)
-        with torch.cuda.device(dev):
-            _check(lib.q8kv_q40_append(*args, torch.cuda.current_stream(dev).cuda_stream))
+        _call(dev, lib.q8kv_q40_append, args)
 
 
 def q40_decode_attn(q, cache, block_table, seq_lens, scale, out=None, part_tokens=0):
@@ -414,11 +436,7 @@ def q40_decode_attn(q, cache, block_table, seq_lens, scale, out=None, part_token
     args = (out.data_ptr(), q.data_ptr(), kp, vp, ks, vs, block_table.data_ptr(), seq_lens.data_ptr(),
             block_table.shape[1], cache.num_blocks, batch, n_q, cache.n_kv, hd, cache.kv_bs, float(scale),
             int(part_tokens))
-    if torch.cuda.current_device() == dev:
-        _check(lib.q8kv_q40_decode_attn(*args, torch.cuda.current_stream(dev).cuda_stream))
-    else:
-        with torch.cuda.device(dev):
-            _check(lib.q8kv_q40_decode_attn(*args, torch.cuda.current_stream(dev).cuda_stream))
+    _call(dev, lib.q8kv_q40_decode_attn, args)
     return out
 
 
@@ -445,11 +463,7 @@ def fp8_decode_attn(q, cache, block_table, seq_lens, scale, out=None, part_token
     args = (out.data_ptr(), q.data_ptr(), kp, vp, ks, vs, block_table.data_ptr(), seq_lens.data_ptr(),
             block_table.shape[1], cache.num_blocks, batch, n_q, cache.n_kv, hd, cache.kv_bs, float(scale),
             int(part_tokens))
-    if torch.cuda.current_device() == dev:
-        _check(lib.q8kv_fp8_decode_attn(*args, torch.cuda.current_stream(dev).cuda_stream))
-    else:
-        with torch.cuda.device(dev):
-            _check(lib.q8kv_fp8_decode_attn(*args, torch.cuda.current_stream(dev).cuda_stream))
+    _call(dev, lib.q8kv_fp8_decode_attn, args)
     return out
 
 
@@ -535,11 +549,7 @@ def decode_attn_heads(q, cache, head_table, seq_lens, scale, out=None, part_toke
     args = (out.data_ptr(), q.data_ptr(), kp, vp, ks, vs, head_table.data_ptr(), seq_lens.data_ptr(),
             head_table.shape[2], cache.num_blocks, batch, n_q, cache.n_kv, hd, cache.kv_bs, float(scale),
             int(part_tokens))
-    if torch.cuda.current_device() == dev:
-        _check(lib.q8kv_decode_attn_heads(*args, torch.cuda.current_stream(dev).cuda_stream))
-    else:
-        with torch.cuda.device(dev):
-            _check(lib.q8kv_decode_attn_heads(*args, torch.cuda.current_stream(dev).cuda_stream))
+    _call(dev, lib.q8kv_decode_attn_heads, args)
     return out
 
 

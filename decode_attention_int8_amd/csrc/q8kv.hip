@@ -623,9 +623,12 @@ __device__ __forceinline__ int uniform_read(const int32_t* p, int idx) {
     return ((const_i32*)p)[idx];
 }
 
-// Physical blocks of the two sub-tiles of the tile at token ts (the table
-// index is clamped into the row, so the read is always in bounds; an entry
-// is only used when its sub-tile holds valid tokens).
+// Physical blocks of the two sub-tiles of the tile at token ts.  The table
+// index is clamped into the row, so the read stays inside the table, but it
+// may read entries past the sequence's last block (a wave with no tile left,
+// or a tile whose second sub-tile is empty); such an entry's value is never
+// used: a block number only addresses pages when its sub-tile holds valid
+// tokens.
 // kv_bs is a power of two (checked on the host), so token positions split
 // into (block, row) with a shift and a mask.
 __device__ __forceinline__ int log2_pow2(int x) { return 31 - __builtin_clz(x); }
@@ -1812,6 +1815,61 @@ __global__ __launch_bounds__(256) void q8kv_append_kernel(const AppendArgs a) {
     row_store<HD, true>(a.vp, a.vs, dst_row, rr, pv, dv, lane);
 }
 
+// ----------------------------------------------------------------------------
+// import of a row-order int8 cache: pages [block][row][kv head][HD] (a block
+// holds kv_bs token rows of every kv head, as the page "Day 9-2:
+// flash_attn_single_q_q8_neon" (trdm.cn) addresses its int8 K/V blocks in its
+// function-signature section: row t % kv_bs of block t / kv_bs, kv head at
+// offset kh * HD inside the row) and scales [block][row][kv head], rewritten
+// into the library's pages and scales.  A pure byte permutation: one thread
+// per 16-byte piece of a source row, read in source order (coalesced); the
+// piece lands whole (K) or as 16 / BPL runs of BPL bytes (V).
+
+struct ImportArgs {
+    int8_t* kp;
+    int8_t* vp;
+    float* ks;
+    float* vs;
+    const int8_t* ksrc;
+    const int8_t* vsrc;
+    const float* kssrc;
+    const float* vssrc;
+    size_t n_pieces;  // num_blocks * kv_bs * n_kv * HD / 16
+    int n_kv, kv_bs;
+};
+
+template <int HD>
+__global__ __launch_bounds__(256) void q8kv_import_kernel(const ImportArgs a) {
+    constexpr int PPR = HD / 16, BPL = Geo<HD>::BPL;
+    const bool V = blockIdx.y != 0;
+    const int8_t* src = V ? a.vsrc : a.ksrc;
+    int8_t* pages = V ? a.vp : a.kp;
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < a.n_pieces; i += (size_t)gridDim.x * 256) {
+        const int c16 = (int)(i % PPR);
+        const size_t src_row = i / PPR;  // (block * kv_bs + row) * n_kv + kh
+        const int kh = (int)(src_row % a.n_kv);
+        const size_t br = src_row / a.n_kv;
+        const int rr = (int)(br % a.kv_bs);
+        const size_t blk = br / a.kv_bs;
+        const size_t dst_row = (blk * a.n_kv + kh) * a.kv_bs + rr;
+        const int row = rr % kSub, col = 16 * c16;
+        const u32x4 x = *reinterpret_cast<const u32x4*>(src + 16 * i);
+        int8_t* sub = pages + (dst_row - row) * HD;
+        if (!V) {
+            *reinterpret_cast<u32x4*>(sub + k_swizzle(row, col)) = x;
+        } else if constexpr (BPL == 16) {
+            *reinterpret_cast<u32x4*>(sub + v_swizzle<HD>(row, col)) = x;
+        } else if constexpr (BPL == 8) {
+            *reinterpret_cast<u32x2*>(sub + v_swizzle<HD>(row, col)) = u32x2{x[0], x[1]};
+            *reinterpret_cast<u32x2*>(sub + v_swizzle<HD>(row, col + 8)) = u32x2{x[2], x[3]};
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) *reinterpret_cast<uint32_t*>(sub + v_swizzle<HD>(row, col + 4 * k)) = x[k];
+        }
+        if (c16 == 0) (V ? a.vs : a.ks)[dst_row] = (V ? a.vssrc : a.kssrc)[src_row];
+    }
+}
+
 // FP8 append: one wave per (token, kv head) row, EPL = HD / 64 elements per
 // lane, so one 64-element scale block spans 64 / EPL lanes.  Per block: the
 // absmax, e = ceil(log2(absmax / 448)) read off the bits of the fp32
@@ -2909,6 +2967,45 @@ int q8kv_append(int8_t* k_pages, int8_t* v_pages, float* k_scale, float* v_scale
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "append kernel launch");
+    return Q8KV_OK;
+}
+
+static bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
+int q8kv_import_pages(int8_t* k_pages, int8_t* v_pages, float* k_scale, float* v_scale, const int8_t* k_rows,
+                      const int8_t* v_rows, const float* k_row_scale, const float* v_row_scale, int num_blocks,
+                      int n_kv_heads, int hd, int kv_bs, void* stream) {
+    g_err.clear();
+    if (!k_pages || !v_pages || !k_scale || !v_scale || !k_rows || !v_rows || !k_row_scale || !v_row_scale)
+        return fail(Q8KV_ENULL, "a tensor pointer is NULL");
+    int rc = check_cache_shape(num_blocks, n_kv_heads, hd, kv_bs);
+    if (rc) return rc;
+    const size_t rows = (size_t)num_blocks * n_kv_heads * kv_bs;
+    const size_t pb = rows * hd, sb = rows * sizeof(float);
+    const void* dst[4] = {k_pages, v_pages, k_scale, v_scale};
+    const void* src[4] = {k_rows, v_rows, k_row_scale, v_row_scale};
+    const size_t len[4] = {pb, pb, sb, sb};
+    for (int i = 0; i < 4; ++i) {
+        if (((uintptr_t)dst[i] | (uintptr_t)src[i]) % 16)
+            return fail(Q8KV_EINVAL, "pages and scales must be 16-byte aligned");
+        for (int j = 0; j < 4; ++j)
+            if (ranges_overlap(dst[i], len[i], src[j], len[j]))
+                return fail(Q8KV_EINVAL, "the destination cache overlaps the source rows");
+    }
+    ImportArgs ia{k_pages, v_pages, k_scale, v_scale, k_rows, v_rows, k_row_scale, v_row_scale,
+                  pb / 16, n_kv_heads, kv_bs};
+    const unsigned grid = (unsigned)std::min<size_t>((ia.n_pieces + 255) / 256, 16384);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    switch (hd) {
+        case 64: hipLaunchKernelGGL(q8kv_import_kernel<64>, dim3(grid, 2), dim3(256), 0, st, ia); break;
+        case 128: hipLaunchKernelGGL(q8kv_import_kernel<128>, dim3(grid, 2), dim3(256), 0, st, ia); break;
+        default: hipLaunchKernelGGL(q8kv_import_kernel<256>, dim3(grid, 2), dim3(256), 0, st, ia); break;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "import kernel launch");
     return Q8KV_OK;
 }
 

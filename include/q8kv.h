@@ -33,7 +33,9 @@
  *                       factor absmax * fp32(1/127) of that row
  *   block_table   int32 [batch][max_blocks_per_seq]  physical block of each
  *                       logical block of a sequence; entries past a
- *                       sequence's last block are never read (-1 by convention)
+ *                       sequence's last block may be read (the whole row
+ *                       must be readable) but never address a page (-1 by
+ *                       convention)
  *   seq_lens      int32 [batch]  tokens cached for each sequence
  * Token t of sequence b lives in physical block block_table[b][t / kv_bs] at
  * row t % kv_bs.  Query head h reads kv head h / (n_q_heads / n_kv_heads).
@@ -176,6 +178,31 @@ int q8kv_append(int8_t* k_pages, int8_t* v_pages, float* k_scale, float* v_scale
                 const void* k_src, const void* v_src, int src_dtype,
                 const int32_t* slot_mapping, int n_tokens, int num_blocks,
                 int n_kv_heads, int hd, int kv_bs, void* stream);
+
+/*
+ * Rewrite an int8 cache held in row order into the layout above, on the
+ * device, bit for bit.  Row order is the addressing of the int8 K/V blocks
+ * on the page "Day 9-2: flash_attn_single_q_q8_neon" (trdm.cn), section 2
+ * (the function signature and the per-token K row pointer): a block holds
+ * kv_bs token rows, each row the hd bytes of every kv head in turn (row
+ * stride n_kv_heads * hd), and the per-row scales sit beside them, one fp32
+ * per (row, kv head).  (The page indexes its scales by sequence position;
+ * here they are laid out per block, which is the same array when each
+ * sequence owns consecutive blocks.)
+ *
+ * k_rows, v_rows           int8 [num_blocks][kv_bs][n_kv_heads][hd]
+ * k_row_scale, v_row_scale fp32 [num_blocks][kv_bs][n_kv_heads]
+ * k_pages, v_pages, k_scale, v_scale  the destination cache, as for
+ *              q8kv_append; every byte and scale of it is written.
+ * All eight buffers are caller-owned device memory, 16-byte aligned; the
+ * destination must not overlap the source (Q8KV_EINVAL otherwise, checked
+ * on the host from the pointers and sizes).  Shape limits as for
+ * q8kv_append.  The scales are copied as bit patterns, NaN included.
+ */
+int q8kv_import_pages(int8_t* k_pages, int8_t* v_pages, float* k_scale, float* v_scale,
+                      const int8_t* k_rows, const int8_t* v_rows,
+                      const float* k_row_scale, const float* v_row_scale,
+                      int num_blocks, int n_kv_heads, int hd, int kv_bs, void* stream);
 
 /*
  * FP8 KV codec (page "deepseek-attention-div64" (beaiera.top), section on the

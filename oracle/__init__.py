@@ -59,11 +59,15 @@ def _configure(lib):
 
 
 def _load():
+    """The oracle library: oracle/liboracle_q8kv.so (built on first use), or
+    the build named by Q8KV_ORACLE_LIB (the sanitizer test points it at an
+    instrumented copy)."""
     global _LIB
     if _LIB is None:
-        if not os.path.exists(_build.LIB):
+        path = os.environ.get("Q8KV_ORACLE_LIB") or _build.LIB
+        if path == _build.LIB and not os.path.exists(path):
             _build.build()
-        _LIB = _configure(ctypes.CDLL(_build.LIB))
+        _LIB = _configure(ctypes.CDLL(path))
     return _LIB
 
 

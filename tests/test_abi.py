@@ -14,7 +14,7 @@ NUL = ctypes.c_void_p(0)
 
 def test_exports_every_declared_symbol():
     names = q8.header_symbols()
-    assert len(names) == 18
+    assert len(names) == 19
     for n in names:
         assert hasattr(L, n), n
 
@@ -238,3 +238,32 @@ def test_decode_heads_rejects_before_any_hip_call():
     rc = L.q8kv_decode_attn_heads(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 16, 2, 8, 2, 100, 16,
                                   0.088, 0, NUL)
     assert rc == q8.Q8KV_EINVAL
+
+
+def import_pages(**kw):
+    # destination at 0x100000.., sources 1 MB further on: 2 blocks x 2 kv heads
+    # x 16 rows x 128 bytes = 8 KB of pages, 256 B of scales each
+    a = dict(kp=0x100000, vp=0x110000, ks=0x120000, vs=0x130000,
+             kr=0x200000, vr=0x210000, ksr=0x220000, vsr=0x230000,
+             num_blocks=2, n_kv=2, hd=128, kv_bs=16)
+    a.update(kw)
+    p = [ctypes.c_void_p(a[k]) for k in ("kp", "vp", "ks", "vs", "kr", "vr", "ksr", "vsr")]
+    return L.q8kv_import_pages(*p, a["num_blocks"], a["n_kv"], a["hd"], a["kv_bs"], NUL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kp=0), q8.Q8KV_ENULL),
+    (dict(vsr=0), q8.Q8KV_ENULL),
+    (dict(hd=96), q8.Q8KV_EINVAL),
+    (dict(kv_bs=8), q8.Q8KV_EINVAL),
+    (dict(num_blocks=0), q8.Q8KV_EINVAL),
+    (dict(n_kv=0), q8.Q8KV_EINVAL),
+    (dict(kr=0x100008), q8.Q8KV_EINVAL),        # misaligned source
+    (dict(ks=0x120004), q8.Q8KV_EINVAL),        # misaligned destination
+    (dict(kr=0x101000), q8.Q8KV_EINVAL),        # source inside k_pages
+    (dict(vs=0x211f80), q8.Q8KV_EINVAL),        # v_scale runs into the end of v_rows
+    (dict(ksr=0x1100f0), q8.Q8KV_EINVAL),       # k_row_scale inside v_pages
+])
+def test_import_pages_rejects_before_any_hip_call(kw, code):
+    assert import_pages(**kw) == code
+    assert q8.last_error() != ""

@@ -10,6 +10,13 @@ query heads of the first and the last kv head.  It runs on a host cache that
 holds only the sampled rows of one kv head, addressed through the same block
 table; the other sequences are given length 0 there.
 
+At the same sizes the quantised cache and the integer scoring are checked
+bit for bit on the sampled sequences: their device pages and scales (read
+back through the page byte order the header defines) against the oracle's
+quantisation of the same rows, and the decode kernel's int32 block dots
+(q8kv_debug_block_dots, over each sampled sequence's whole length) against
+the oracle's.
+
 The fused step re-stores every sequence's newest token with its own values,
 as the benchmark's fused leg does: the cache must come back unchanged and
 the output must be the plain decode's, bit for bit.  QUEST runs as the
@@ -26,7 +33,7 @@ import torch
 import decode_attention_int8_amd as q8
 import oracle
 import workloads
-from gpu_cases import DEV, say, to_dev
+from gpu_cases import DEV, natural_pages, say, to_dev
 from oracle import fp8kv, q40, quest
 from test_oracle_quest import quest_decode
 
@@ -89,6 +96,17 @@ def full_case(name):
     scale = workloads.softmax_scale(w.hd)
     qd, td, ld = to_dev(q), to_dev(table), to_dev(lens)
     outs = {}
+    # the sampled sequences' pages and scales, and the int32 block dots of a
+    # decode over just those sequences (their table rows and lengths)
+    c8 = caches["q8"]
+    pages = {}
+    for b in seqs:
+        blocks = torch.from_numpy(table[b, :-(-int(lens[b]) // w.kv_bs)].astype(np.int64)).to(DEV)
+        pages[b] = tuple(t.index_select(0, blocks).cpu().numpy() for t in (c8.k_pages, c8.v_pages, c8.k_scale, c8.v_scale))
+    sub = np.array(seqs)
+    max_tok = int(lens[sub].max())
+    dots = q8.debug_block_dots(to_dev(q[sub]), c8, to_dev(table[sub]), to_dev(lens[sub]), max_tok).cpu().numpy()
+    outs["bits"] = dict(pages=pages, dots=dots)
     for codec, (_, fn) in CODECS.items():
         outs[codec] = fn(qd, caches[codec], td, ld, scale).cpu().numpy()
     # the fused step, storing each sequence's newest token again
@@ -130,12 +148,14 @@ def sampled_reference(codec, w, lens, table, nb, seqs, rows, q, scale, kh):
 
 
 # one list ordered by workload, so each workload is built once
-CHECKS = [(n, c) for n in workloads.ORDER for c in list(CODECS) + ["fused", "quest"]]
+CHECKS = [(n, c) for n in workloads.ORDER for c in ["bits"] + list(CODECS) + ["fused", "quest"]]
 
 
 @pytest.mark.parametrize("name,check", CHECKS)
 def test_full_size(name, check):
-    if check == "fused":
+    if check == "bits":
+        full_size_bits(name)
+    elif check == "fused":
         full_size_fused_append_decode(name)
     elif check == "quest":
         full_size_quest(name)
@@ -160,6 +180,37 @@ def full_size_sampled(name, codec):
     # sequences of length 0 give zero rows
     for b in np.flatnonzero(lens == 0):
         assert not got[b].any()
+
+
+def full_size_bits(name):
+    """Pages, scales and int32 block dots of the sampled sequences, bit for
+    bit.  The oracle quantises the sampled rows into a host pool of just
+    their blocks (the same logical order, renumbered)."""
+    w, lens, table, nb, seqs, rows, q, scale, outs = full_case(name)
+    pages, dots = outs["bits"]["pages"], outs["bits"]["dots"]
+    nblk = [-(-int(lens[b]) // w.kv_bs) for b in seqs]
+    host = oracle.Cache(sum(nblk), w.n_kv, w.kv_bs, w.hd)
+    sub_table = np.full((len(seqs), max(nblk)), -1, np.int32)
+    first = 0
+    for i, b in enumerate(seqs):
+        sub_table[i, :nblk[i]] = np.arange(first, first + nblk[i], dtype=np.int32)
+        k, v, _ = rows[b]
+        t = np.arange(int(lens[b]))
+        host.append(k, v, (sub_table[i, t // w.kv_bs] * w.kv_bs + t % w.kv_bs).astype(np.int32))
+        first += nblk[i]
+    first = 0
+    for i, b in enumerate(seqs):
+        say(f"  {name} bits: sequence {b}, {int(lens[b])} tokens")
+        kp, vp, ks, vs = pages[b]
+        sl = slice(first, first + nblk[i])
+        assert np.array_equal(natural_pages(kp, "k"), host.k_pages[sl]), f"{name} seq {b}: K pages"
+        assert np.array_equal(natural_pages(vp, "v"), host.v_pages[sl]), f"{name} seq {b}: V pages"
+        assert np.array_equal(ks.view(np.uint32), host.k_scale[sl].view(np.uint32)), f"{name} seq {b}: K scales"
+        assert np.array_equal(vs.view(np.uint32), host.v_scale[sl].view(np.uint32)), f"{name} seq {b}: V scales"
+        first += nblk[i]
+    sub = np.array(seqs)
+    want = oracle.block_dots(q[sub], host, sub_table, lens[sub], dots.shape[2])
+    assert np.array_equal(dots, want), f"{name}: int32 block dots differ"
 
 
 def full_size_fused_append_decode(name):

@@ -152,6 +152,32 @@ def test_decode_small_workloads(name):
         check_decode(c, dev, part_tokens=pt)
 
 
+@pytest.mark.parametrize("name", ["gqa_batch", "ragged"])
+def test_decode_attn_entry_point(name):
+    """q8kv_decode_attn itself, called through the C ABI with raw pointers
+    (the binding's decode goes through q8kv_decode_attn_split): the oracle's
+    parity bar, and bit for bit what the split entry gives with the automatic
+    plan (part_tokens 0)."""
+    c = build(SMALL[name])
+    say(f"q8kv_decode_attn {name}")
+    dev = gpu_cache(c)
+    q, bt, sl = dev_inputs(c)
+    out = torch.full_like(q, float("nan"))
+    st = torch.cuda.current_stream(DEV).cuda_stream
+    rc = q8.lib.q8kv_decode_attn(out.data_ptr(), q.data_ptr(), dev.k_pages.data_ptr(), dev.v_pages.data_ptr(),
+                                 dev.k_scale.data_ptr(), dev.v_scale.data_ptr(), bt.data_ptr(), sl.data_ptr(),
+                                 bt.shape[1], dev.num_blocks, c.w.batch, c.w.n_q, c.w.n_kv, c.w.hd, c.w.kv_bs,
+                                 c.scale, st)
+    assert rc == q8.Q8KV_OK, q8.last_error()
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), decode(c, dev).view(np.uint32))
+    want = oracle.decode(c.q, c.cache, c.table, c.lens, c.scale, threads=8)
+    want64 = oracle.decode(c.q, c.cache, c.table, c.lens, c.scale, use_f64=True, threads=8)
+    assert float(np.abs(got - want).max()) <= TOL
+    assert float(np.abs(got - want64).max()) <= TOL64
+
+
 @pytest.mark.parametrize("G", [1, 2, 4, 8])
 def test_decode_edge_lengths(G):
     lens = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257, 300]
