@@ -40,6 +40,7 @@ def _load():
     sig = {
         "q8kv_decode_attn": [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, P],
         "q8kv_decode_attn_split": [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, P],
+        "q8kv_decode_attn_noalloc": [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, P],
         "q8kv_append_decode_attn": [P, P, P, P, I, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, P],
         "q8kv_plan": [I, I, I, I, I, I, P, P],
         "q8kv_fp8_append": [P, P, P, P, P, P, I, P, I, I, I, I, I, P],
@@ -253,6 +254,31 @@ def decode_attn(q, cache, block_table, seq_lens, scale, out=None, part_tokens=0)
             block_table.shape[1], cache.num_blocks, batch, n_q, cache.n_kv, hd, cache.kv_bs, float(scale),
             int(part_tokens))
     _call(dev, lib.q8kv_decode_attn_split, args)
+    return out
+
+
+def decode_attn_noalloc(q, cache, block_table, seq_lens, scale, out, part_tokens=0):
+    """decode_attn through q8kv_decode_attn_noalloc: the same result, bit for
+    bit, with no device allocation by the library or this binding (out is
+    required).  The library's one scratch array per device is shared by
+    every such call: calls that overlap on one device race."""
+    dev, kp, vp, ks, vs = cache._pointers()
+    if not (_ok(q, torch.float32, dev, 3) and _ok(block_table, torch.int32, dev, 2)
+            and _ok(seq_lens, torch.int32, dev, 1) and _ok(out, torch.float32, dev, 3)):
+        d = cache.device
+        _need(q, "q", torch.float32, d, 3)
+        _need(block_table, "block_table", torch.int32, d, 2)
+        _need(seq_lens, "seq_lens", torch.int32, d, 1)
+        _need(out, "out", torch.float32, d, 3)
+    batch, n_q, hd = q.shape
+    if hd != cache.hd or block_table.shape[0] != batch or seq_lens.shape[0] != batch:
+        raise ValueError("q / block_table / seq_lens / cache shapes disagree")
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    args = (out.data_ptr(), q.data_ptr(), kp, vp, ks, vs, block_table.data_ptr(), seq_lens.data_ptr(),
+            block_table.shape[1], cache.num_blocks, batch, n_q, cache.n_kv, hd, cache.kv_bs, float(scale),
+            int(part_tokens))
+    _call(dev, lib.q8kv_decode_attn_noalloc, args)
     return out
 
 

@@ -2643,6 +2643,38 @@ void plan(int batch, int n_kv, int max_tokens, int* part_tokens, int* n_parts) {
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
+// Scratch of the allocation-free decode entry (q8kv_decode_attn_noalloc):
+// bytes [0, 256) the persistent grid's work ticket, then the merge arrival
+// counters (one int per (sequence, head group), 256-byte aligned), then the
+// partition states (accumulators, then (max, sum) pairs).  Held by every
+// device the library runs on until the process ends.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+}  // namespace
+
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+namespace {
+std::map<int, char*> g_scratch;  // device -> scratch's device address on it
+
+// scratch's address on device dev (the current device), looked up once per
+// device.  The array's name in host code is a host-side stand-in; kernels
+// must be given this address instead.
+int scratch_address(int dev, char** out) {
+    std::lock_guard<std::mutex> lock(g_mu);
+    auto it = g_scratch.find(dev);
+    if (it != g_scratch.end()) {
+        *out = it->second;
+        return Q8KV_OK;
+    }
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (p == nullptr) return fail(Q8KV_EHIP, "hipGetSymbolAddress(scratch) gave NULL");
+    g_scratch[dev] = static_cast<char*>(p);
+    *out = static_cast<char*>(p);
+    return Q8KV_OK;
+}
+
 // Decode kernel variants: the int8 codec, the int8 codec with the fused
 // append of the new token, the FP8 codec.
 enum Variant { kVarQ8 = 0, kVarQ8New = 1, kVarFp8 = 2, kVarQ40 = 3 };
@@ -2755,7 +2787,7 @@ int decode_impl(float* out, const float* q, const int8_t* kp, const int8_t* vp, 
                 int num_blocks, int batch, int n_q, int n_kv, int hd, int kv_bs, float scale,
                 int part_tokens, void* stream, const void* knew = nullptr, const void* vnew = nullptr,
                 int new_dtype = 0, const uint8_t* ks8 = nullptr, const uint8_t* vs8 = nullptr,
-                bool head_tables = false, bool q40 = false) {
+                bool head_tables = false, bool q40 = false, bool no_alloc = false) {
     const bool fp8 = ks8 != nullptr || vs8 != nullptr;
     if (!out || !q || !kp || !vp || !table || !lens || (fp8 ? (!ks8 || !vs8) : (!ks || !vs)))
         return fail(Q8KV_ENULL, "a tensor pointer is NULL");
@@ -2786,11 +2818,23 @@ int decode_impl(float* out, const float* q, const int8_t* kp, const int8_t* vp, 
     }
     const long long items = (long long)batch * n_hk * np;
     if ((long long)batch * n_q > INT_MAX || items > INT_MAX) return fail(Q8KV_EINVAL, "decode shape too large");
+    const size_t groups = (size_t)batch * n_hk;
+    const size_t n_state = np > 1 ? groups * (size_t)np * G : 0;
+    const size_t acc_bytes = align256(n_state * hd * sizeof(float));
+    const size_t arrive_off = 256, state_off = arrive_off + align256(groups * sizeof(int));
+    if (no_alloc && state_off + acc_bytes + n_state * 2 * sizeof(float) > kScratchBytes)
+        return fail(Q8KV_EINVAL, "this shape needs %zu bytes of scratch (%zu states of %d floats), above the %zu-byte maximum",
+                    state_off + acc_bytes + n_state * 2 * sizeof(float), n_state, hd + 2, kScratchBytes);
 
     hipStream_t st = static_cast<hipStream_t>(stream);
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    char* sp = nullptr;
+    if (no_alloc) {
+        rc = scratch_address(dev, &sp);
+        if (rc) return rc;
+    }
     LaunchInfo li;
     const int var = q40 ? kVarQ40 : fp8 ? kVarFp8 : knew ? kVarQ8New : kVarQ8;
     rc = launch_info(dev, hd, var, &li);
@@ -2798,7 +2842,9 @@ int decode_impl(float* out, const float* q, const int8_t* kp, const int8_t* vp, 
     const unsigned grid = (unsigned)std::min<long long>(items, li.resident);
     DecodeArgs da{out, q, kp, vp, ks, vs, table, lens, nullptr, nullptr, nullptr, nullptr, batch, max_blocks, num_blocks, n_q, n_kv, kv_bs, G, pt, np, hgs, n_hk, scale * kLog2e,
                   knew, vnew, new_dtype, ks8, vs8, head_tables ? n_kv : 1};
-    if (items > (long long)grid) {
+    if (items > (long long)grid && no_alloc) {
+        da.ticket = reinterpret_cast<int*>(sp);
+    } else if (items > (long long)grid) {
         std::lock_guard<std::mutex> lock(g_mu);
         Workspace& w = g_ws[{dev, stream}];
         if (!w.ticket) {
@@ -2823,10 +2869,11 @@ int decode_impl(float* out, const float* q, const int8_t* kp, const int8_t* vp, 
     const int slices = G * hd / 4;
     const int rows_par = slices >= nt ? 1 : nt / slices;
     const bool fuse = np > 1 && np * G <= kFuseRows && (np + rows_par - 1) / rows_par <= kFusePer;
-    if (np > 1) {
-        const size_t groups = (size_t)batch * n_hk;
-        const size_t n_state = groups * (size_t)np * G;
-        const size_t acc_bytes = align256(n_state * hd * sizeof(float));
+    if (np > 1 && no_alloc) {
+        da.st_acc = reinterpret_cast<float*>(sp + state_off);
+        da.st_ms = reinterpret_cast<float*>(sp + state_off + acc_bytes);
+        if (fuse) da.arrive = reinterpret_cast<int*>(sp + arrive_off);
+    } else if (np > 1) {
         const size_t need = acc_bytes + n_state * 2 * sizeof(float);
         std::lock_guard<std::mutex> lock(g_mu);
         Workspace& w = g_ws[{dev, stream}];
@@ -2871,6 +2918,12 @@ int decode_impl(float* out, const float* q, const int8_t* kp, const int8_t* vp, 
         }
         if (fuse) da.arrive = w.arrive;
     }
+    if (no_alloc && (da.ticket || da.arrive)) {
+        // the scratch keeps whatever the last call left: clear the ticket
+        // and the arrival counters (a kernel, not a memset node)
+        e = launch_zero(sp, (arrive_off + (da.arrive ? groups * sizeof(int) : 0)) / sizeof(int), st);
+        if (e != hipSuccess) return hip_fail(e, "scratch counter clear");
+    }
     const size_t lds = wide ? (size_t)li.wide_lds
                        : mode == kStatic && grid <= 2u * (unsigned)li.cus ? (size_t)li.static_lds : 0;
     launch_decode(hd, var, mode, wide, grid, lds, st, da);
@@ -2913,6 +2966,17 @@ int q8kv_decode_attn_split(float* out, const float* q, const int8_t* k_pages, co
     return decode_impl(out, q, k_pages, v_pages, k_scale, v_scale, block_table, seq_lens,
                        max_blocks_per_seq, num_blocks, batch, n_q_heads, n_kv_heads, hd, kv_bs,
                        scale, part_tokens, stream);
+}
+
+int q8kv_decode_attn_noalloc(float* out, const float* q, const int8_t* k_pages, const int8_t* v_pages,
+                             const float* k_scale, const float* v_scale, const int32_t* block_table,
+                             const int32_t* seq_lens, int max_blocks_per_seq, int num_blocks, int batch,
+                             int n_q_heads, int n_kv_heads, int hd, int kv_bs, float scale,
+                             int part_tokens, void* stream) {
+    g_err.clear();
+    return decode_impl(out, q, k_pages, v_pages, k_scale, v_scale, block_table, seq_lens,
+                       max_blocks_per_seq, num_blocks, batch, n_q_heads, n_kv_heads, hd, kv_bs,
+                       scale, part_tokens, stream, nullptr, nullptr, 0, nullptr, nullptr, false, false, true);
 }
 
 int q8kv_append_decode_attn(float* out, const float* q, const void* k_new, const void* v_new,

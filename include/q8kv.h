@@ -125,6 +125,34 @@ int q8kv_decode_attn_split(float* out, const float* q,
                            float scale, int part_tokens, void* stream);
 
 /*
+ * q8kv_decode_attn_split for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, kernels and results (bit for bit); it never
+ * calls hipMalloc or hipFree.  Its partition states, merge counters and
+ * work ticket live in one library-owned 32 MiB device array (a file-scope
+ * __device__ variable, one copy per device, held until the process ends),
+ * whose counters it clears with a kernel at the start of every call.
+ * Every call on a device shares that array: calls that overlap on one
+ * device (on different streams, or from different threads) race and give
+ * undefined results.  A call needs 256 bytes, plus 4 bytes per (sequence,
+ * group of at most 8 query heads of one kv head) rounded up to a multiple of
+ * 256, plus, when contexts are split into n_parts > 1 partitions (the
+ * q8kv_plan count, or the one part_tokens gives), S = batch * n_q_heads *
+ * n_parts states of 4 * hd bytes (all S rounded up to a multiple of 256) and
+ * 8 bytes each.  A shape that needs more than 32 MiB is rejected with
+ * Q8KV_EINVAL before any HIP call; q8kv_last_error() gives the bytes needed.
+ * (Every one of the five benchmark workloads fits: the largest, 64
+ * sequences of 64 query heads split in 8, needs about 17 MB.)
+ */
+int q8kv_decode_attn_noalloc(float* out, const float* q,
+                             const int8_t* k_pages, const int8_t* v_pages,
+                             const float* k_scale, const float* v_scale,
+                             const int32_t* block_table, const int32_t* seq_lens,
+                             int max_blocks_per_seq, int num_blocks,
+                             int batch, int n_q_heads, int n_kv_heads, int hd, int kv_bs,
+                             float scale, int part_tokens, void* stream);
+
+/*
  * Append the step's new token and attend to it in one launch: for every
  * sequence b with 1 <= seq_lens[b] <= max_blocks_per_seq * kv_bs, the new
  * token's K and V rows are quantised exactly as q8kv_append does and written

@@ -14,7 +14,7 @@ NUL = ctypes.c_void_p(0)
 
 def test_exports_every_declared_symbol():
     names = q8.header_symbols()
-    assert len(names) == 19
+    assert len(names) == 20
     for n in names:
         assert hasattr(L, n), n
 
@@ -267,3 +267,29 @@ def import_pages(**kw):
 def test_import_pages_rejects_before_any_hip_call(kw, code):
     assert import_pages(**kw) == code
     assert q8.last_error() != ""
+
+
+def test_noalloc_rejects_shapes_beyond_its_scratch():
+    """2048 sequences x 64 heads x 256 partitions of hd 256 need far more than
+    the allocation-free entry's 32 MiB: rejected on the host, saying so."""
+    rc = L.q8kv_decode_attn_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 64, 131072, 2048, 64, 8,
+                                    256, 256, 0.0625, 64, NUL)
+    assert rc == q8.Q8KV_EINVAL
+    assert "scratch" in q8.last_error()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kp=NUL), q8.Q8KV_ENULL),
+    (dict(hd=96), q8.Q8KV_EINVAL),
+    (dict(n_q=18, n_kv=4), q8.Q8KV_EINVAL),
+    (dict(part=48), q8.Q8KV_EINVAL),
+    (dict(scale=float("inf")), q8.Q8KV_EINVAL),
+])
+def test_noalloc_validates_like_split(kw, code):
+    a = dict(out=FAKE, q=FAKE, kp=FAKE, vp=FAKE, ks=FAKE, vs=FAKE, bt=FAKE, sl=FAKE,
+             max_blocks=8, num_blocks=16, batch=2, n_q=8, n_kv=2, hd=128, kv_bs=16, scale=0.088, part=0)
+    a.update(kw)
+    rc = L.q8kv_decode_attn_noalloc(a["out"], a["q"], a["kp"], a["vp"], a["ks"], a["vs"], a["bt"], a["sl"],
+                                    a["max_blocks"], a["num_blocks"], a["batch"], a["n_q"], a["n_kv"], a["hd"],
+                                    a["kv_bs"], a["scale"], a["part"], NUL)
+    assert rc == code == decode(**kw)
