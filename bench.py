@@ -72,6 +72,9 @@ def parse():
     p.add_argument("--no-q40", action="store_true", help="skip the q4_0-codec leg")
     p.add_argument("--no-quest", action="store_true", help="skip the QUEST metadata / selection leg")
     p.add_argument("--part-tokens", type=int, default=0, help="override the split plan (0: automatic)")
+    p.add_argument("--stage", action="store_true",
+                   help="time the LDS-staged variant of the int8 static-grid kernels (same results; "
+                        "not the default kernels)")
     p.add_argument("--copy-mb", type=float, default=0.0,
                    help="after timing, run one device-to-device copy of this many MiB (a known-size "
                         "kernel that scales hardware byte counters)")
@@ -560,6 +563,8 @@ def decode_record(w, g, args):
               "seq_len": ("U{1..%d}" % w.seq_len) if w.ragged else w.seq_len,
               "tokens": int(lens.sum()), "kv_bytes_per_step": kvb, "algorithmic_bytes_per_step": algo,
               "part_tokens": pt, "n_parts": npart, "cold_cache_copies": len(g["caches"])}
+    if args.stage:
+        config["kernel_variant"] = "lds_staged"
     rec = {"us_per_step": round(loop_ms * 1e3, 3), "kv_gbs": round(kv_gbs, 2),
            "hbm_frac": round(kv_gbs / HBM_PEAK_GBS, 4), "config": config,
            "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -580,6 +585,7 @@ def main():
         sys.exit(2)
     import torch
     import decode_attention_int8_amd as q8
+    q8.debug_set_stage(args.stage)
     w = workloads.WORKLOADS[args.workload]
     dev = torch.device("cuda", 0)
     log(f"workload {w.name}: batch {w.batch}, heads {w.n_q}/{w.n_kv}, hd {w.hd}, kv_bs {w.kv_bs}, "

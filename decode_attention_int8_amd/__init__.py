@@ -57,6 +57,7 @@ def _load():
         "q8kv_debug_block_dots": [P, I, P, P, P, P, I, I, I, I, I, I, I, P],
         "q8kv_debug_stream_read": [P, ctypes.c_size_t, P, ctypes.c_size_t, P],
         "q8kv_debug_set_wide": [I],
+        "q8kv_debug_set_stage": [I],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -607,6 +608,12 @@ def debug_set_wide(enable):
     """Test export: allow (True, the default) or forbid the 8-wave workgroups
     of static grids of at most one workgroup per CU."""
     _check(lib.q8kv_debug_set_wide(1 if enable else 0))
+
+
+def debug_set_stage(enable):
+    """Test export: use (True) or not (False, the default) the LDS-staged
+    int8 static-grid kernels; same results, bit for bit."""
+    _check(lib.q8kv_debug_set_stage(1 if enable else 0))
 
 
 def debug_quantize_q(q):

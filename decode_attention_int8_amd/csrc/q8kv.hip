@@ -158,6 +158,12 @@ __device__ __forceinline__ void load_q_rows(QRows<HD, NT>& Q, const float* __res
     }
 }
 
+// The same chunks loaded straight into LDS (chunk slot tid + i NT at 16 bytes
+// each), for kernels whose other loads all go to LDS: a register load among
+// them would make the compiler wait for every one of them before its use.
+template <int HD, int NT>
+__device__ __forceinline__ void dma_q_rows(int8_t* lraw, const float* __restrict__ q, int G, int tid, int wid);
+
 template <int HD, int NT>
 __device__ __forceinline__ void quantize_q_regs(const QRows<HD, NT>& Q, int8_t* lq, float* lqsc, int tid,
                                                 int* lqsum = nullptr) {
@@ -614,7 +620,7 @@ struct Tile {
 // Partitions start on multiples of 32 and kv_bs is a multiple of 16, so each
 // 16-token sub-tile lies inside one page and is read whole (rows past t1 are
 // masked in tile_compute).  An empty second sub-tile re-reads the first one,
-// so no table entry past the sequence is read.
+// so no page past the sequence is read.
 // Wave-uniform read of a table that the kernel never writes, through the
 // constant address space so that it is a scalar load: a vector load would
 // queue behind the in-flight tile loads and wait for all of them.
@@ -658,6 +664,147 @@ __device__ __forceinline__ void tile_load(Tile<HD>& T, const DecodeArgs& a, cons
         const int8_t* vsub = a.vp + base * HD;  // wave-uniform
 #pragma unroll
         for (int c = 0; c < Geo<HD>::NPAIR; ++c) T.v[st][c] = stream_load<u32x4>(vsub + 1024 * c + 16 * lane);
+    }
+}
+
+// Tiles staged through LDS.  A wave keeps kRing tiles in flight in its own
+// LDS ring: the loads go straight from memory into LDS (global_load_lds, no
+// registers held while they are in flight), and the wave reads a tile into
+// registers -- the same Tile the direct loads give, lane for lane -- only
+// when it is about to compute it, then refills that slot with the tile
+// kRing strides ahead.  A slot holds the K sub-tiles (2 x 16 HD bytes), the
+// V sub-tiles, then 256 bytes of scales: lane l carries the scale of row
+// l % 16 of sub-tile (l / 16) % 2, K for l < 32 and V above.
+constexpr int kRing = 2;
+
+template <int HD>
+struct Stage {
+    static constexpr int SUB = kSub * HD;             // bytes of one K or V sub-tile
+    static constexpr int SCALES = 4 * SUB;            // offset of the scales
+    static constexpr int SLOT = 4 * SUB + 4 * kWave;  // bytes per slot
+    static constexpr int NDMA = 4 * Geo<HD>::NPAIR + 1;  // loads per tile (one vmcnt each)
+};
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// One 16-byte (or 4-byte) piece per lane from global memory into LDS at
+// dst + 16 * lane (4 * lane), non-temporal.  dst is wave-uniform.
+__device__ __forceinline__ void dma16(const void* src, int8_t* dst) {
+    __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, 2);
+}
+__device__ __forceinline__ void dma4(const void* src, int8_t* dst) {
+    __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 4, 0, 2);
+}
+
+// 16 bytes of LDS written by the wave's own DMA, after its wait: read in
+// asm (waiting in the same block), since the compiler would put a wait for
+// every DMA in flight ahead of a plain LDS read that it cannot tell apart
+// from them.
+__device__ __forceinline__ f32x4 lds_read16(const int8_t* p) {
+    f32x4 v;
+    const uint32_t addr = (uint32_t)(uintptr_t)(lds_void*)p;
+    asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
+    return v;
+}
+
+template <int HD, int NT>
+__device__ __forceinline__ void dma_q_rows(int8_t* lraw, const float* __restrict__ q, int G, int tid, int wid) {
+#pragma unroll
+    for (int i = 0; i < QRows<HD, NT>::kPer; ++i) {
+        const int c = min(tid + i * NT, QRows<HD, NT>::kChunks - 1);
+        const int g = c / (HD / 4);
+        const int e = (c % (HD / 4)) * 4;
+        dma16(q + (size_t)min(g, G - 1) * HD + e, lraw + 16 * (i * NT + kWave * wid));
+    }
+}
+
+template <int HD>
+__device__ __forceinline__ void tile_issue(int8_t* slot, const DecodeArgs& a, const int (&tblk)[2], int kh, int ts,
+                                           int t1, int lane, bool& bad) {
+    using SG = Stage<HD>;
+    size_t base[2];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+        const bool val = t1 - (ts + kSub * st) > 0;
+        const int tst = val ? ts + kSub * st : ts;
+        int blk = (st == 1 && val) ? tblk[1] : tblk[0];
+        if ((unsigned)blk >= (unsigned)a.num_blocks) {
+            bad = true;
+            blk = 0;
+        }
+        base[st] = (((size_t)blk * a.n_kv + kh) << log2_pow2(a.kv_bs)) + (size_t)(tst & (a.kv_bs - 1));
+    }
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+#pragma unroll
+        for (int c = 0; c < Geo<HD>::NPAIR; ++c) {
+            dma16(a.kp + base[st] * HD + 1024 * c + 16 * lane, slot + st * SG::SUB + 1024 * c);
+            dma16(a.vp + base[st] * HD + 1024 * c + 16 * lane, slot + (2 + st) * SG::SUB + 1024 * c);
+        }
+    }
+    const int sst = (lane >> 4) & 1;
+    const float* sc = lane < 32 ? a.ks : a.vs;
+    dma4(sc + (sst ? base[1] : base[0]) + (lane & 15), slot + SG::SCALES);
+}
+
+// Wait until the slot's loads have landed: `later` tiles were issued after
+// it (their loads may stay in flight; memory loads complete in order).
+template <int HD>
+__device__ __forceinline__ void tile_wait(bool later) {
+    if (later) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(Stage<HD>::NDMA) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// The slot's tile into registers.  The reads are one asm block that waits
+// for them itself: the compiler, unable to tell the slot from the slots
+// still being filled, would otherwise wait for every load in flight first.
+// The outputs are early-clobber: a read that returns while later reads of
+// the block are still to be issued must not land on their address
+// registers.
+template <int HD>
+__device__ __forceinline__ void tile_read(Tile<HD>& T, const int8_t* slot, int ts, int t1, int lane) {
+    static_assert(HD == 64 || HD == 128, "staged tiles are hd 64 or 128");
+    const uint32_t akv = (uint32_t)(uintptr_t)(lds_void*)(slot + 16 * lane);
+    const uint32_t asc = (uint32_t)(uintptr_t)(lds_void*)(slot + Stage<HD>::SCALES + 16 * (lane >> 4));
+#pragma unroll
+    for (int st = 0; st < 2; ++st) T.nval[st] = min(max(t1 - (ts + kSub * st), 0), kSub);
+    if constexpr (HD == 128) {
+        // K sub-tile st chunk c at 2048 st + 1024 c, V at 4096 + 2048 st + 1024 c
+        asm volatile(
+            "ds_read_b128 %0, %12\n\t"
+            "ds_read_b128 %1, %12 offset:1024\n\t"
+            "ds_read_b128 %2, %12 offset:2048\n\t"
+            "ds_read_b128 %3, %12 offset:3072\n\t"
+            "ds_read_b128 %4, %12 offset:4096\n\t"
+            "ds_read_b128 %5, %12 offset:5120\n\t"
+            "ds_read_b128 %6, %12 offset:6144\n\t"
+            "ds_read_b128 %7, %12 offset:7168\n\t"
+            "ds_read_b128 %8, %13\n\t"
+            "ds_read_b128 %9, %13 offset:64\n\t"
+            "ds_read_b128 %10, %13 offset:128\n\t"
+            "ds_read_b128 %11, %13 offset:192\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(T.k[0][0]), "=&v"(T.k[0][1]), "=&v"(T.k[1][0]), "=&v"(T.k[1][1]), "=&v"(T.v[0][0]),
+              "=&v"(T.v[0][1]), "=&v"(T.v[1][0]), "=&v"(T.v[1][1]), "=&v"(T.ks[0]), "=&v"(T.ks[1]), "=&v"(T.vs[0]),
+              "=&v"(T.vs[1])
+            : "v"(akv), "v"(asc)
+            : "memory");
+    } else {
+        // K sub-tile st at 1024 st, V at 2048 + 1024 st
+        asm volatile(
+            "ds_read_b128 %0, %8\n\t"
+            "ds_read_b128 %1, %8 offset:1024\n\t"
+            "ds_read_b128 %2, %8 offset:2048\n\t"
+            "ds_read_b128 %3, %8 offset:3072\n\t"
+            "ds_read_b128 %4, %9\n\t"
+            "ds_read_b128 %5, %9 offset:64\n\t"
+            "ds_read_b128 %6, %9 offset:128\n\t"
+            "ds_read_b128 %7, %9 offset:192\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(T.k[0][0]), "=&v"(T.k[1][0]), "=&v"(T.v[0][0]), "=&v"(T.v[1][0]), "=&v"(T.ks[0]), "=&v"(T.ks[1]),
+              "=&v"(T.vs[0]), "=&v"(T.vs[1])
+            : "v"(akv), "v"(asc)
+            : "memory");
     }
 }
 
@@ -1320,8 +1467,8 @@ __device__ __forceinline__ void q4_offset_fix(f32x4 (&acc)[Geo<HD>::BPL], const 
 enum GridMode { kPersistent = 0, kStatic = 1 };
 enum CodecKind { kQ8 = 0, kFp8 = 1, kQ40 = 2 };
 
-template <int HD, int MODE, bool NEW, int CODEC = kQ8, int NW = kWaves>
-__global__ __launch_bounds__(kWave * NW) __attribute__((amdgpu_waves_per_eu(HD == 256 ? 1 : 3))) void
+template <int HD, int MODE, bool NEW, int CODEC = kQ8, int NW = kWaves, bool STG = false>
+__global__ __launch_bounds__(kWave * NW) __attribute__((amdgpu_waves_per_eu(HD == 256 ? 1 : STG ? 2 : 3))) void
 q8kv_decode_kernel(const DecodeArgs a) {
     using GG = Geo<HD>;
     constexpr int NT = kWave * NW;  // threads per workgroup
@@ -1330,13 +1477,27 @@ q8kv_decode_kernel(const DecodeArgs a) {
     constexpr bool Q40 = CODEC == kQ40;
     static_assert(!(NEW && CODEC != kQ8), "the fused append is an int8-codec path");
     using TileT = std::conditional_t<FP8, Fp8Tile<HD>, std::conditional_t<Q40, Q4Tile<HD>, Tile<HD>>>;
+    // STG: the int8 static kernels' variant that stages its tiles through an
+    // LDS ring (hd 64 / 128; chosen by the host only when asked for)
+    constexpr bool STAGE = STG;
+    static_assert(!STG || (CODEC == kQ8 && STATIC && HD <= 128), "staged tiles: int8 static grids at hd 64 / 128");
+    using SG = Stage<HD>;
     __shared__ __attribute__((aligned(16))) int8_t lq[FP8 ? 16 : kHeadGroup * HD];
     __shared__ float lqsc[FP8 ? 1 : kHeadGroup * GG::NB];
     __shared__ int lqsum[Q40 ? kHeadGroup * GG::NB : 1];  // q4_0: query block code sums
     __shared__ __attribute__((aligned(16))) _Float16 lq16[FP8 ? 2 * kHeadGroup * HD : 8];  // FP8: query hi, lo rows
     __shared__ float lM[NW][kHeadGroup];
     __shared__ float lS[NW][kHeadGroup];
-    __shared__ float lacc[NW][kHeadGroup][HD];
+    // the waves' final accumulators: in the staged kernels, each wave's sits
+    // in the wave's own ring, which is idle once its tile loop has ended
+    __shared__ __attribute__((aligned(16))) int8_t lring[STAGE ? NW * kRing * SG::SLOT : 16];
+    __shared__ float lacc[STAGE ? 1 : NW][kHeadGroup][HD];
+    __shared__ __attribute__((aligned(16))) int8_t lqraw[STAGE ? 16 * QRows<HD, NT>::kPer * NT : 16];
+    static_assert(!STAGE || kHeadGroup * HD * 4 <= kRing * SG::SLOT, "a wave's accumulator must fit its ring");
+    auto lacc_w = [&](int w) -> float* {
+        if constexpr (STAGE) return reinterpret_cast<float*>(lring + w * kRing * SG::SLOT);
+        else return &lacc[w][0][0];
+    };
     // persistent grids: exclusive prefix of full-partition items per sequence,
     // the sequences that end in a partial partition (longest remainder
     // first) and each sequence's remainder class
@@ -1493,7 +1654,8 @@ q8kv_decode_kernel(const DecodeArgs a) {
         // the query rows' loads go out first: the quantisation then waits for
         // them alone, not for the first tile queued behind them
         QRows<HD, NT> qrows;
-        load_q_rows<HD, NT>(qrows, a.q + ((size_t)b * a.n_q + (size_t)ih * G) * HD, G, itid);
+        if constexpr (STAGE) dma_q_rows<HD, NT>(lqraw, a.q + ((size_t)b * a.n_q + (size_t)ih * G) * HD, G, itid, wid);
+        else load_q_rows<HD, NT>(qrows, a.q + ((size_t)b * a.n_q + (size_t)ih * G) * HD, G, itid);
         const int32_t* trow = a.table + ((size_t)b * a.table_rows + (a.table_rows > 1 ? kh : 0)) * a.max_blocks;
         const int t0 = part * a.part_tokens;
         // The first tile's table reads, those of the item's first tile (a
@@ -1548,9 +1710,27 @@ q8kv_decode_kernel(const DecodeArgs a) {
             }
         }
 
-        // Start streaming the wave's first tile before the query prologue.
+        // Start streaming the wave's first tile (staged: its first kRing
+        // tiles) before the query prologue.
         TileT A;
-        {
+        int8_t* const ring = lring + wid * kRing * SG::SLOT;  // staged: the wave's ring
+        int slot = 0;
+        if constexpr (STAGE) {
+            // every wave issues kRing tiles' loads: a slot with no tile of
+            // its own loads the item's first tile, unused (as above, so that
+            // the compiler's wait for the query rows counts the same loads
+            // on every path)
+            const bool own = ts < t1;
+            const int blk0[2] = {own ? blk_first[0] : blk_t0[0], own ? blk_first[1] : blk_t0[1]};
+            tile_issue<HD>(ring, a, blk0, kh, own ? ts : t0, t1, ilane, bad);
+#pragma unroll
+            for (int k = 1; k < kRing; ++k) {
+                const int tk = ts + k * kStride < t1 ? ts + k * kStride : t0;
+                int blk[2];
+                tile_blocks(trow, tk, a.kv_bs, a.max_blocks, blk);
+                tile_issue<HD>(ring + k * SG::SLOT, a, blk, kh, tk, t1, ilane, bad);
+            }
+        } else {
             const bool own = ts < t1;
             const int blk0[2] = {own ? blk_first[0] : blk_t0[0], own ? blk_first[1] : blk_t0[1]};
             if constexpr (FP8) fp8_tile_load<HD>(A, a, blk0, kh, own ? ts : t0, t1, ilane, bad);
@@ -1568,8 +1748,28 @@ q8kv_decode_kernel(const DecodeArgs a) {
 
         if constexpr (FP8) split_q_regs<HD, NT>(qrows, lq16, itid);
         else if constexpr (Q40) quantize_q_regs<HD, NT>(qrows, lq, lqsc, itid, lqsum);
-        else quantize_q_regs<HD, NT>(qrows, lq, lqsc, itid);
-        __syncthreads();
+        else {
+            if constexpr (STAGE) {
+                // the query chunks have landed once at most the kRing tiles'
+                // loads issued after them are in flight
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kRing * SG::NDMA) : "memory");
+#pragma unroll
+                for (int i = 0; i < QRows<HD, NT>::kPer; ++i) {
+                    const int c = itid + i * NT;
+                    qrows.x[i] = lds_read16(lqraw + 16 * c);
+                    qrows.keep[i] = c / (HD / 4) < G;
+                }
+            }
+            quantize_q_regs<HD, NT>(qrows, lq, lqsc, itid);
+        }
+        if constexpr (STAGE) {
+            // the quantised query is in LDS once this wave's LDS writes are
+            // done; a full __syncthreads would also wait for the tiles in
+            // flight
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        } else {
+            __syncthreads();
+        }
         // static grids: the tail wave quantises the new rows (which arrive
         // with its first tile) while its second tile is in flight, or here
         // when the new token is in its first tile
@@ -1587,6 +1787,22 @@ q8kv_decode_kernel(const DecodeArgs a) {
         f32x4 wsums = {0.f, 0.f, 0.f, 0.f};  // q4_0: per-block weight sums
 
         while (ts < t1) {
+            if constexpr (STAGE) {
+                // the slot's tile, once its loads have landed (those of the
+                // tiles issued after it may stay in flight); the slot is
+                // refilled with the tile kRing strides ahead once read
+                static_assert(kRing == 2, "tile_wait counts one later tile");
+                tile_wait<HD>(ts + kStride < t1);
+                int8_t* sl = ring + slot * SG::SLOT;
+                tile_read<HD>(A, sl, ts, t1, ilane);
+                const int tn = ts + kRing * kStride;
+                if (tn < t1) {
+                    int blk[2];
+                    tile_blocks(trow, tn, a.kv_bs, a.max_blocks, blk);
+                    tile_issue<HD>(sl, a, blk, kh, tn, t1, ilane, bad);
+                }
+                slot = slot + 1 == kRing ? 0 : slot + 1;
+            }
             if constexpr (NEW) {
                 if (ts == tail_ts) tile_patch<HD>(A, lnew, lnew + HD, lnew_sc[0], lnew_sc[1], L - 1 - ts, ilane);
             }
@@ -1594,7 +1810,11 @@ q8kv_decode_kernel(const DecodeArgs a) {
             else if constexpr (Q40) q4_tile_compute<HD>(A, lq, lqsc, lqsum, a.scale_log2, acc, wsums, M, S, ilane);
             else tile_compute<HD>(A, lq, lqsc, a.scale_log2, acc, M, S, E, ilane);
             ts += kStride;
-            if (ts < t1) {
+            if constexpr (STAGE && NEW) {
+                if (tail_ts != INT_MIN && ts == ts_second)
+                    prepare_new_token<HD>(nk, nv, tail_blk, lnew, lnew_sc, &lnew_blk, ilane);
+            }
+            if (!STAGE && ts < t1) {
                 int blk[2];
                 tile_blocks(trow, ts, a.kv_bs, a.max_blocks, blk);
                 if constexpr (FP8) fp8_tile_load<HD>(A, a, blk, kh, ts, t1, ilane, bad);
@@ -1615,6 +1835,8 @@ q8kv_decode_kernel(const DecodeArgs a) {
         if constexpr (Q40) q4_offset_fix<HD>(acc, wsums, ilane);
 
         // wave state -> LDS: exp-sum over the four row groups, hi + lo rows
+        // (staged: into the wave's ring, once no load into it is in flight)
+        if constexpr (STAGE) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         S = swap16_sum(S);
         S = swap32_sum(S);
 #pragma unroll
@@ -1634,7 +1856,7 @@ q8kv_decode_kernel(const DecodeArgs a) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
 #pragma unroll
-                for (int s = 0; s < GG::BPL; ++s) lacc[wid][4 * r + j][CODEC != kQ8 ? 16 * s + n : GG::BPL * n + s] = acc[s][j];
+                for (int s = 0; s < GG::BPL; ++s) lacc_w(wid)[(4 * r + j) * HD + (CODEC != kQ8 ? 16 * s + n : GG::BPL * n + s)] = acc[s][j];
             }
         }
         const bool any_bad = __syncthreads_or(bad);
@@ -1655,7 +1877,7 @@ q8kv_decode_kernel(const DecodeArgs a) {
             for (int w = 0; w < NW; ++w) {
                 const float ew = __builtin_amdgcn_exp2f(lM[w][g] - Mx);
                 St += lS[w][g] * ew;
-                at += *reinterpret_cast<const f32x4*>(&lacc[w][g][4 * i4]) * ew;
+                at += *reinterpret_cast<const f32x4*>(lacc_w(w) + g * HD + 4 * i4) * ew;
             }
             if (any_bad) at = f32x4{NAN, NAN, NAN, NAN};
             if (np_b == 1) {
@@ -2593,6 +2815,7 @@ struct LaunchInfo {
 };
 std::map<std::pair<int, int>, LaunchInfo> g_launch;  // (device, hd * 4 + kernel variant)
 std::atomic<int> g_wide{1};  // wide workgroups allowed (a test export turns them off)
+std::atomic<int> g_stage{0};  // LDS-staged int8 static kernels (a test export turns them on)
 
 bool valid_hd(int hd) { return hd == 64 || hd == 128 || hd == 256; }
 bool valid_kv_bs(int bs) { return bs == 16 || bs == 32 || bs == 64 || bs == 128 || bs == 256; }
@@ -2679,9 +2902,9 @@ int scratch_address(int dev, char** out) {
 // append of the new token, the FP8 codec.
 enum Variant { kVarQ8 = 0, kVarQ8New = 1, kVarFp8 = 2, kVarQ40 = 3 };
 
-template <int HD, int VAR, int MODE, int NW = kWaves>
+template <int HD, int VAR, int MODE, int NW = kWaves, bool STG = false>
 constexpr auto decode_kernel_ptr() {
-    return q8kv_decode_kernel<HD, MODE, VAR == kVarQ8New, VAR == kVarFp8 ? kFp8 : VAR == kVarQ40 ? kQ40 : kQ8, NW>;
+    return q8kv_decode_kernel<HD, MODE, VAR == kVarQ8New, VAR == kVarFp8 ? kFp8 : VAR == kVarQ40 ? kQ40 : kQ8, NW, STG>;
 }
 
 // Wide (kWideWaves) workgroups serve static grids of at most one workgroup
@@ -2746,10 +2969,24 @@ int launch_info(int dev, int hd, int var, LaunchInfo* out) {
 }
 
 template <int HD, int VAR>
-void launch_decode_hd(int mode, bool wide, unsigned grid, size_t lds, hipStream_t st, const DecodeArgs& da) {
+void launch_decode_hd(int mode, bool wide, bool stage, unsigned grid, size_t lds, hipStream_t st,
+                      const DecodeArgs& da) {
     if (mode == kPersistent) {
         hipLaunchKernelGGL((decode_kernel_ptr<HD, VAR, kPersistent>()), dim3(grid), dim3(kThreads), 0, st, da);
         return;
+    }
+    if constexpr ((VAR == kVarQ8 || VAR == kVarQ8New) && HD <= 128) {
+        // the staged kernels' LDS already keeps them at two (wide: one) per CU
+        if (stage && wide) {
+            hipLaunchKernelGGL((decode_kernel_ptr<HD, VAR, kStatic, kWideWaves, true>()), dim3(grid),
+                               dim3(kWave * kWideWaves), 0, st, da);
+            return;
+        }
+        if (stage) {
+            hipLaunchKernelGGL((decode_kernel_ptr<HD, VAR, kStatic, kWaves, true>()), dim3(grid), dim3(kThreads), 0,
+                               st, da);
+            return;
+        }
     }
     if constexpr (wide_hd(HD)) {
         if (wide) {
@@ -2762,18 +2999,19 @@ void launch_decode_hd(int mode, bool wide, unsigned grid, size_t lds, hipStream_
 }
 
 template <int VAR>
-void launch_decode_var(int hd, int mode, bool wide, unsigned grid, size_t lds, hipStream_t st, const DecodeArgs& da) {
-    if (hd == 64) launch_decode_hd<64, VAR>(mode, wide, grid, lds, st, da);
-    else if (hd == 128) launch_decode_hd<128, VAR>(mode, wide, grid, lds, st, da);
-    else launch_decode_hd<256, VAR>(mode, wide, grid, lds, st, da);
+void launch_decode_var(int hd, int mode, bool wide, bool stage, unsigned grid, size_t lds, hipStream_t st,
+                       const DecodeArgs& da) {
+    if (hd == 64) launch_decode_hd<64, VAR>(mode, wide, stage, grid, lds, st, da);
+    else if (hd == 128) launch_decode_hd<128, VAR>(mode, wide, stage, grid, lds, st, da);
+    else launch_decode_hd<256, VAR>(mode, wide, stage, grid, lds, st, da);
 }
 
-void launch_decode(int hd, int var, int mode, bool wide, unsigned grid, size_t lds, hipStream_t st,
+void launch_decode(int hd, int var, int mode, bool wide, bool stage, unsigned grid, size_t lds, hipStream_t st,
                    const DecodeArgs& da) {
-    if (var == kVarQ8New) launch_decode_var<kVarQ8New>(hd, mode, wide, grid, lds, st, da);
-    else if (var == kVarFp8) launch_decode_var<kVarFp8>(hd, mode, wide, grid, lds, st, da);
-    else if (var == kVarQ40) launch_decode_var<kVarQ40>(hd, mode, wide, grid, lds, st, da);
-    else launch_decode_var<kVarQ8>(hd, mode, wide, grid, lds, st, da);
+    if (var == kVarQ8New) launch_decode_var<kVarQ8New>(hd, mode, wide, stage, grid, lds, st, da);
+    else if (var == kVarFp8) launch_decode_var<kVarFp8>(hd, mode, wide, stage, grid, lds, st, da);
+    else if (var == kVarQ40) launch_decode_var<kVarQ40>(hd, mode, wide, stage, grid, lds, st, da);
+    else launch_decode_var<kVarQ8>(hd, mode, wide, stage, grid, lds, st, da);
 }
 
 hipError_t launch_zero(void* p, size_t n_words, hipStream_t st) {
@@ -2861,8 +3099,13 @@ int decode_impl(float* out, const float* q, const int8_t* kp, const int8_t* vp, 
         da.ticket = w.ticket;
     }
     // every item in its own workgroup: static grid (two per CU at most when
-    // that is enough; wide workgroups when one per CU is)
-    const int mode = items > (long long)grid ? kPersistent : kStatic;
+    // that is enough; wide workgroups when one per CU is).  The LDS-staged
+    // variant (test export q8kv_debug_set_stage) holds a tile ring that
+    // leaves room for two workgroups per CU; larger grids then run the
+    // persistent kernel (one item per workgroup, no ticket).
+    const bool stage_ok = g_stage.load() != 0 && (var == kVarQ8 || var == kVarQ8New) && hd <= 128;
+    const int mode = items > (long long)grid || (stage_ok && grid > 2u * (unsigned)li.cus) ? kPersistent : kStatic;
+    const bool stage = stage_ok && mode == kStatic;
     const bool wide = mode == kStatic && wide_hd(hd) && grid <= (unsigned)li.cus && g_wide.load() != 0;
     const int nt = wide ? kWave * kWideWaves : kThreads;
     // small groups of partition states are merged inside the decode kernel
@@ -2926,7 +3169,7 @@ int decode_impl(float* out, const float* q, const int8_t* kp, const int8_t* vp, 
     }
     const size_t lds = wide ? (size_t)li.wide_lds
                        : mode == kStatic && grid <= 2u * (unsigned)li.cus ? (size_t)li.static_lds : 0;
-    launch_decode(hd, var, mode, wide, grid, lds, st, da);
+    launch_decode(hd, var, mode, wide, stage, grid, lds, st, da);
     e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
     if (np > 1 && !fuse) {
@@ -3317,6 +3560,13 @@ int q8kv_debug_block_dots(int32_t* dots, int max_tok, const float* q, const int8
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "dots kernel launch");
+    return Q8KV_OK;
+}
+
+int q8kv_debug_set_stage(int enable) {
+    g_err.clear();
+    if (enable != 0 && enable != 1) return fail(Q8KV_EINVAL, "enable must be 0 or 1 (got %d)", enable);
+    g_stage.store(enable);
     return Q8KV_OK;
 }
 

@@ -416,6 +416,19 @@ int q8kv_debug_block_dots(int32_t* dots, int max_tok, const float* q, const int8
 int q8kv_debug_set_wide(int enable);
 
 /*
+ * Test and measurement export: enable (1) or disable (0, the default) the
+ * LDS-staged variant of the int8 decode kernels for static grids at hd 64
+ * and 128 (q8kv_decode_attn, _split, _noalloc and q8kv_append_decode_attn).
+ * Each wave then keeps two tiles in flight in an LDS ring, loaded with
+ * global_load_lds, and reads a tile into registers only to compute it; the
+ * arithmetic is unchanged, so outputs are bit for bit those of the default
+ * kernels.  A static grid of more than two workgroups per CU runs the
+ * persistent kernel instead.  Applies to every later call in the process;
+ * Q8KV_EINVAL for other values.
+ */
+int q8kv_debug_set_stage(int enable);
+
+/*
  * Measurement export: read a_bytes of device buffer a and b_bytes of device
  * buffer b (both multiples of 16) in one launch with plain linear
  * non-temporal loads and discard the data.  A benchmark times it over a

@@ -14,7 +14,7 @@ NUL = ctypes.c_void_p(0)
 
 def test_exports_every_declared_symbol():
     names = q8.header_symbols()
-    assert len(names) == 20
+    assert len(names) == 21
     for n in names:
         assert hasattr(L, n), n
 
@@ -162,6 +162,13 @@ def test_set_wide_accepts_only_0_and_1():
     assert L.q8kv_debug_set_wide(-1) == q8.Q8KV_EINVAL
     assert L.q8kv_debug_set_wide(0) == q8.Q8KV_OK
     assert L.q8kv_debug_set_wide(1) == q8.Q8KV_OK  # the default again
+
+
+def test_set_stage_accepts_only_0_and_1():
+    assert L.q8kv_debug_set_stage(2) == q8.Q8KV_EINVAL
+    assert L.q8kv_debug_set_stage(-1) == q8.Q8KV_EINVAL
+    assert L.q8kv_debug_set_stage(1) == q8.Q8KV_OK
+    assert L.q8kv_debug_set_stage(0) == q8.Q8KV_OK  # the default again
 
 
 def test_stream_read_rejects():

@@ -10,6 +10,13 @@ source, built here with the library's flags).
   scalar-register spill reloads (v_readlane_b32) inside the static-grid and
   plain persistent-grid tile loops, the blocks that hold the Q.K and P.V
   matrix-core instructions.
+* The LDS-staged kernels' multi-read asm blocks (a tile's LDS reads, issued
+  together and waited for once) never write a read's destination over the
+  address register of a later read in the same block: a read that returns
+  early would otherwise redirect the reads still to be issued.
+* The staged tile loops hold no compiler-inserted wait for every load in
+  flight (vmcnt(0)) ahead of their LDS reads other than the kernel's own
+  waits in asm.
 """
 import os
 import re
@@ -60,8 +67,45 @@ def tile_loop_blocks(body):
 
 @pytest.mark.parametrize("mode", ["1", "0"])
 def test_int8_tile_loop_has_no_scalar_reloads(device_asm, mode):
-    name = f"_ZN12_GLOBAL__N_118q8kv_decode_kernelILi128ELi{mode}ELb0ELi0ELi4EEEvNS_10DecodeArgsE"
+    name = f"_ZN12_GLOBAL__N_118q8kv_decode_kernelILi128ELi{mode}ELb0ELi0ELi4ELb0EEEvNS_10DecodeArgsE"
     blocks = tile_loop_blocks(device_asm[name])
     assert blocks
     for lab, txt in blocks:
         assert "v_readlane_b32" not in txt, f"{name}: scalar spill reload in {lab}"
+
+
+def _vregs(tok):
+    m = re.match(r"v\[(\d+):(\d+)\]", tok)
+    if m:
+        return set(range(int(m.group(1)), int(m.group(2)) + 1))
+    m = re.match(r"v(\d+)", tok)
+    return {int(m.group(1))}
+
+
+def test_multi_read_asm_blocks_keep_their_addresses(device_asm):
+    checked = 0
+    for name, body in device_asm.items():
+        for blk in re.findall(r";;#ASMSTART\n(.*?);;#ASMEND", body, re.S):
+            reads = [l.strip().replace(",", " ").split() for l in blk.split("\n")
+                     if l.strip().startswith("ds_read_b128")]
+            if len(reads) < 2:
+                continue
+            checked += 1
+            for k, r in enumerate(reads):
+                dst = _vregs(r[1])
+                for later in reads[k + 1:]:
+                    assert not dst & _vregs(later[2]), f"{name}: {' '.join(r)} overwrites the address of {' '.join(later)}"
+    assert checked >= 8
+
+
+@pytest.mark.parametrize("hd,nw", [("128", "4"), ("128", "8"), ("64", "4")])
+def test_staged_tile_loop_waits_are_its_own(device_asm, hd, nw):
+    """Up to the last matrix-core instruction (the end of the tile loop),
+    every wait for all loads in flight is one of the kernel's own asm waits."""
+    name = f"_ZN12_GLOBAL__N_118q8kv_decode_kernelILi{hd}ELi1ELb0ELi0ELi{nw}ELb1EEEvNS_10DecodeArgsE"
+    lines = device_asm[name].split("\n")
+    assert any("global_load_lds_dwordx4" in l for l in lines)
+    last_mfma = max(i for i, l in enumerate(lines) if "v_mfma" in l)
+    for i in range(last_mfma):
+        if "s_waitcnt vmcnt(0)" in lines[i]:
+            assert ";;#ASMSTART" in lines[i - 1], f"{name}: compiler wait for every load at line {i}: {lines[i]}"
