@@ -1930,30 +1930,40 @@ struct CombineArgs {
 
 // Merge the partition states of one (sequence, query head) with the rescale
 // rule: M* = max M_p, S* = sum S_p 2^(M_p - M*), out = sum acc_p 2^(M_p - M*) / S*.
-// Thread (row r, slice i4) owns partitions p = r, r + R, ... and sums them in
-// increasing order; the R row sums are then added in row order, so the result
+// A head's row is split over kCombineSplit<HD> workgroups of kCombineCols
+// float4 slices each, so that a long context's states are read by many CUs
+// at once.  Thread (row r, column c) owns partitions p = r, r + ROWS, ... and
+// sums them in increasing order; the ROWS row sums are then added by a fixed
+// tree (lane shuffles inside a wave, then the waves in order), so the result
 // is deterministic.  All state loads are issued at once, together with the
 // length read (slots past the sequence's partitions are read but never used).
+constexpr int kCombineCols = 4;
+template <int HD>
+constexpr int kCombineSplit = HD / 4 / kCombineCols;
+
 template <int HD>
 __global__ __launch_bounds__(kThreads) void q8kv_combine_kernel(const CombineArgs a) {
-    constexpr int Q4 = HD / 4;          // float4 slices per head row
-    constexpr int R = kThreads / Q4;    // partitions summed in parallel
-    constexpr int PER = kMaxParts / R;  // partitions per thread at most
-    __shared__ f32x4 lpart[R][Q4];
-    __shared__ float lsp[R];
+    constexpr int CS = kCombineCols;
+    constexpr int ROWS = kThreads / CS;     // partition rows (64)
+    constexpr int PER = kMaxParts / ROWS;   // partitions per thread at most
+    constexpr int RPW = kWave / CS;         // rows per wave
+    __shared__ f32x4 lpart[kWaves][CS];
+    __shared__ float lsp[kWaves];
     __shared__ float lmax[kWaves];
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid >> 6;
-    const int h = blockIdx.x % a.n_q, b = blockIdx.x / a.n_q;
+    const int sl = blockIdx.x % kCombineSplit<HD>, bh = blockIdx.x / kCombineSplit<HD>;
+    const int h = bh % a.n_q, b = bh / a.n_q;
     const int ih = h / a.group, g = h % a.group;  // head group, head in it
     const size_t first = (((size_t)b * a.n_hk + ih) * a.n_parts) * a.group + g;  // state of p = 0
     const size_t pstride = (size_t)a.group;                                        // states per partition
-    const int i4 = tid % Q4, r = tid / Q4;
+    const int c = tid % CS, r = tid / CS;
+    const int i4 = sl * CS + c;
 
     f32x4 v[PER];
     float2 ms[PER];
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
-        const int p = r + k * R;
+        const int p = r + k * ROWS;
         if (p < a.n_parts) {
             v[k] = *reinterpret_cast<const f32x4*>(a.st_acc + (first + p * pstride) * HD + 4 * i4);
             ms[k] = *reinterpret_cast<const float2*>(a.st_ms + (first + p * pstride) * 2);
@@ -1967,7 +1977,7 @@ __global__ __launch_bounds__(kThreads) void q8kv_combine_kernel(const CombineArg
     float mx = -INFINITY;
 #pragma unroll
     for (int k = 0; k < PER; ++k)
-        if (r + k * R < np) mx = fmaxf(mx, ms[k].x);
+        if (r + k * ROWS < np) mx = fmaxf(mx, ms[k].x);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
     if (lane == 0) lmax[wid] = mx;
@@ -1980,22 +1990,30 @@ __global__ __launch_bounds__(kThreads) void q8kv_combine_kernel(const CombineArg
     float sp = 0.0f;
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
-        if (r + k * R < np) {
+        if (r + k * ROWS < np) {
             const float w = __builtin_amdgcn_exp2f(ms[k].x - Mx);
             at += v[k] * w;
             sp += ms[k].y * w;
         }
     }
-    lpart[r][i4] = at;
-    if (i4 == 0) lsp[r] = sp;
+    // the wave's RPW rows (lanes c, c + CS, ...) by a fixed xor tree
+#pragma unroll
+    for (int off = CS; off < kWave; off <<= 1) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) at[e] += __shfl_xor(at[e], off);
+        sp += __shfl_xor(sp, off);
+    }
+    static_assert(RPW * CS == kWave, "a wave holds whole rows");
+    if (lane < CS) lpart[wid][lane] = at;
+    if (lane == 0) lsp[wid] = sp;
     __syncthreads();
-    if (r == 0) {
-        f32x4 t = lpart[0][i4];
+    if (tid < CS) {
+        f32x4 t = lpart[0][tid];
         float St = lsp[0];
 #pragma unroll
-        for (int rr = 1; rr < R; ++rr) {
-            t += lpart[rr][i4];
-            St += lsp[rr];
+        for (int w = 1; w < kWaves; ++w) {
+            t += lpart[w][tid];
+            St += lsp[w];
         }
         *reinterpret_cast<f32x4*>(a.out + ((size_t)b * a.n_q + h) * HD + 4 * i4) = t / St;
     }
@@ -3174,11 +3192,11 @@ int decode_impl(float* out, const float* q, const int8_t* kp, const int8_t* vp, 
     if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
     if (np > 1 && !fuse) {
         CombineArgs ca{out, da.st_acc, da.st_ms, lens, n_q, n_hk, G, max_tokens, pt, np};
-        const unsigned cgrid = (unsigned)(batch * n_q);
+        const unsigned bq = (unsigned)(batch * n_q);
         switch (hd) {
-            case 64: hipLaunchKernelGGL(q8kv_combine_kernel<64>, dim3(cgrid), dim3(kThreads), 0, st, ca); break;
-            case 128: hipLaunchKernelGGL(q8kv_combine_kernel<128>, dim3(cgrid), dim3(kThreads), 0, st, ca); break;
-            default: hipLaunchKernelGGL(q8kv_combine_kernel<256>, dim3(cgrid), dim3(kThreads), 0, st, ca); break;
+            case 64: hipLaunchKernelGGL(q8kv_combine_kernel<64>, dim3(bq * kCombineSplit<64>), dim3(kThreads), 0, st, ca); break;
+            case 128: hipLaunchKernelGGL(q8kv_combine_kernel<128>, dim3(bq * kCombineSplit<128>), dim3(kThreads), 0, st, ca); break;
+            default: hipLaunchKernelGGL(q8kv_combine_kernel<256>, dim3(bq * kCombineSplit<256>), dim3(kThreads), 0, st, ca); break;
         }
         e = hipGetLastError();
         if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
