@@ -2203,13 +2203,14 @@ __device__ __forceinline__ float row16_reduce_xor(float (&v)[16]) {
 
 // Metadata: one wave per (sequence, logical block, kv head).  The wave reads
 // the page's 16-row sub-tiles (lane 16 r + n: row n, columns 64 c + 16 r ..
-// +16 of chunk c), puts column 64 c + 16 r + (s ^ n) in slot s (a dword
-// exchange and a byte permute per dword), dequantises each element as
-// float(code) * k_scale of its row, keeps running maxima and minima per slot
-// over its rows (rows past the sequence's length repeat its last row), reduces them
-// over the 16 rows of a DPP row (row16_reduce_xor), and lane n of each row
-// writes column 64 c + 16 r + n.
-template <int HD>
+// +16 of chunk c), NSUB of them at once (all of a page of up to 64 rows), puts
+// column 64 c + 16 r + (s ^ n) in slot s (a dword exchange and a byte permute
+// per dword), dequantises each element as float(code) * k_scale of its row,
+// keeps running maxima and minima per slot over its rows, reduces them over
+// the 16 rows of a DPP row (row16_reduce_xor), and lane n of each row writes
+// column 64 c + 16 r + n.  Rows past the sequence's length read its last row
+// again (every load is issued, and a repeat changes no maximum or minimum).
+template <int HD, int NSUB>
 __global__ __launch_bounds__(256) void q8kv_quest_metadata_kernel(const QuestArgs a) {
     constexpr int NPAIR = Geo<HD>::NPAIR;
     const int lane = threadIdx.x & (kWave - 1);
@@ -2226,6 +2227,7 @@ __global__ __launch_bounds__(256) void q8kv_quest_metadata_kernel(const QuestArg
     if (j * a.kv_bs >= L) return;
     if ((unsigned)p >= (unsigned)a.num_blocks) return;
     const int rows = min(a.kv_bs, L - j * a.kv_bs);
+    const int last_sub = (rows - 1) & ~(kSub - 1);  // first row of the last sub-tile in use
     const int n = lane & 15, r = lane >> 4;
     const uint32_t bsel = 0x03020100u ^ ((uint32_t)(n & 3) * 0x01010101u);  // byte e <- byte e ^ (n & 3)
     const bool dx1 = (n & 4) != 0, dx2 = (n & 8) != 0;                         // dword D <- dword D ^ (n >> 2)
@@ -2239,41 +2241,52 @@ __global__ __launch_bounds__(256) void q8kv_quest_metadata_kernel(const QuestArg
         }
     }
     const size_t page_row = ((size_t)p * a.n_kv + kh) * a.kv_bs;
-    // rows past the sequence's length (only in its last sub-tile) read the
-    // last valid row again: a repeat changes no maximum or minimum.  The next
-    // sub-tile's loads go out before the current one is reduced.
-    i32x4 ch[NPAIR];
-    int rn = min(n, rows - 1);
-    float sc = a.ks[page_row + rn];
-    load_k_subtile<HD>(ch, a.kp, page_row, 16 * r + rn);
-    for (int r0 = 0; r0 < rows; r0 += kSub) {
-        uint32_t cu[NPAIR][4];
+    for (int r0 = 0; r0 < rows; r0 += NSUB * kSub) {
+        i32x4 ch[NSUB][NPAIR];
+        float sc[NSUB];
+#pragma unroll
+        for (int u = 0; u < NSUB; ++u) {
+            const int rs = min(r0 + u * kSub, last_sub);  // a sub-tile past the rows repeats the last one
+            const int rn = min(n, rows - 1 - rs);
+            sc[u] = a.ks[page_row + rs + rn];
+            load_k_subtile<HD>(ch[u], a.kp, page_row + rs, 16 * r + rn);
+        }
+        float off[NSUB];
+#pragma unroll
+        for (int u = 0; u < NSUB; ++u) off[u] = -128.0f * sc[u];  // exact
 #pragma unroll
         for (int c = 0; c < NPAIR; ++c) {
-            uint32_t t[4];
+            uint32_t cu[NSUB][4];
 #pragma unroll
-            for (int d = 0; d < 4; ++d) t[d] = dx1 ? (uint32_t)ch[c][d ^ 1] : (uint32_t)ch[c][d];
+            for (int u = 0; u < NSUB; ++u) {
+                uint32_t t[4];
 #pragma unroll
-            for (int d = 0; d < 4; ++d) cu[c][d] = __builtin_amdgcn_perm(0u, dx2 ? t[d ^ 2] : t[d], bsel);
-        }
-        const float sc_cur = sc;
-        if (r0 + kSub < rows) {
-            rn = min(n, rows - 1 - (r0 + kSub));
-            sc = a.ks[page_row + r0 + kSub + rn];
-            load_k_subtile<HD>(ch, a.kp, page_row + r0 + kSub, 16 * r + rn);
-        }
-        const float off = -128.0f * sc_cur;  // exact
-        // code * sc as fma(code + 128, sc, -128 sc): the byte with its sign
-        // bit flipped converts to code + 128 in one instruction, and the
-        // fused result rounds the exact product once, as the product does
+                for (int d = 0; d < 4; ++d) t[d] = dx1 ? (uint32_t)ch[u][c][d ^ 1] : (uint32_t)ch[u][c][d];
 #pragma unroll
-        for (int c = 0; c < NPAIR; ++c) {
+                for (int d = 0; d < 4; ++d)
+                    cu[u][d] = __builtin_amdgcn_perm(0u, dx2 ? t[d ^ 2] : t[d], bsel) ^ 0x80808080u;
+            }
+            // code * sc as fma(code + 128, sc, -128 sc): the byte with its
+            // sign bit flipped converts to code + 128 in one instruction, and
+            // the fused result rounds the exact product once, as the product
+            // does.  The sub-tiles' values of a slot are folded in pairs
+            // (three-operand max / min).
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const uint32_t u = (cu[c][i >> 2] ^ 0x80808080u) >> (8 * (i & 3));
-                const float v = __builtin_fmaf((float)(uint8_t)u, sc_cur, off);
-                mx[c][i] = fmaxf(mx[c][i], v);
-                mn[c][i] = fminf(mn[c][i], v);
+                float v[NSUB];
+#pragma unroll
+                for (int u = 0; u < NSUB; ++u)
+                    v[u] = __builtin_fmaf((float)(uint8_t)(cu[u][i >> 2] >> (8 * (i & 3))), sc[u], off[u]);
+#pragma unroll
+                for (int u = 0; u < NSUB; u += 2) {
+                    if (u + 1 < NSUB) {
+                        mx[c][i] = fmaxf(fmaxf(mx[c][i], v[u]), v[u + 1]);
+                        mn[c][i] = fminf(fminf(mn[c][i], v[u]), v[u + 1]);
+                    } else {
+                        mx[c][i] = fmaxf(mx[c][i], v[u]);
+                        mn[c][i] = fminf(mn[c][i], v[u]);
+                    }
+                }
             }
         }
     }
@@ -3038,6 +3051,14 @@ hipError_t launch_zero(void* p, size_t n_words, hipStream_t st) {
     return hipGetLastError();
 }
 
+// Sub-tiles a metadata wave keeps in flight: a whole page of up to 64 rows.
+template <int HD>
+void launch_metadata(int kv_bs, unsigned grid, hipStream_t st, const QuestArgs& qa) {
+    if (kv_bs <= 16) hipLaunchKernelGGL((q8kv_quest_metadata_kernel<HD, 1>), dim3(grid), dim3(256), 0, st, qa);
+    else if (kv_bs == 32) hipLaunchKernelGGL((q8kv_quest_metadata_kernel<HD, 2>), dim3(grid), dim3(256), 0, st, qa);
+    else hipLaunchKernelGGL((q8kv_quest_metadata_kernel<HD, 4>), dim3(grid), dim3(256), 0, st, qa);
+}
+
 int decode_impl(float* out, const float* q, const int8_t* kp, const int8_t* vp, const float* ks,
                 const float* vs, const int32_t* table, const int32_t* lens, int max_blocks,
                 int num_blocks, int batch, int n_q, int n_kv, int hd, int kv_bs, float scale,
@@ -3443,9 +3464,9 @@ int q8kv_quest_metadata(float* kmax, float* kmin, const int8_t* k_pages, const f
                  batch, max_blocks_per_seq, num_blocks, 0, n_kv_heads, kv_bs, 0};
     hipStream_t st = static_cast<hipStream_t>(stream);
     switch (hd) {
-        case 64: hipLaunchKernelGGL(q8kv_quest_metadata_kernel<64>, dim3((unsigned)grid), dim3(256), 0, st, qa); break;
-        case 128: hipLaunchKernelGGL(q8kv_quest_metadata_kernel<128>, dim3((unsigned)grid), dim3(256), 0, st, qa); break;
-        default: hipLaunchKernelGGL(q8kv_quest_metadata_kernel<256>, dim3((unsigned)grid), dim3(256), 0, st, qa); break;
+        case 64: launch_metadata<64>(kv_bs, (unsigned)grid, st, qa); break;
+        case 128: launch_metadata<128>(kv_bs, (unsigned)grid, st, qa); break;
+        default: launch_metadata<256>(kv_bs, (unsigned)grid, st, qa); break;
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "metadata kernel launch");
