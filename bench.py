@@ -72,6 +72,10 @@ def parse():
     p.add_argument("--no-q40", action="store_true", help="skip the q4_0-codec leg")
     p.add_argument("--no-quest", action="store_true", help="skip the QUEST metadata / selection leg")
     p.add_argument("--part-tokens", type=int, default=0, help="override the split plan (0: automatic)")
+    p.add_argument("--timeline", action="store_true",
+                   help="instead of the benchmark: build a copy of the library whose decode kernel "
+                        "stamps each workgroup's start, end of streaming and CU, and report the "
+                        "timeline of one call after idle and of the last of 30 back-to-back calls")
     p.add_argument("--stage", action="store_true",
                    help="time the LDS-staged variant of the int8 static-grid kernels (same results; "
                         "not the default kernels)")
@@ -577,6 +581,107 @@ def decode_record(w, g, args):
     return rec, loop_ms, out
 
 
+# Per-workgroup wall-clock stamps (s_memrealtime, 100 MHz) for --timeline:
+# inserted into a copy of the kernel source at these points, each of which
+# must occur exactly once (tests/test_bench_contract.py checks that).
+TIMELINE_EDITS = [
+    ("struct DecodeArgs {",
+     "__device__ unsigned long long g_stamp[4096 * 8];\n"
+     "#define STAMP(k, val) do { if (threadIdx.x == 0 && blockIdx.x < 4096) "
+     "g_stamp[blockIdx.x * 8 + (k)] = (val); } while (0)\n"
+     "struct DecodeArgs {"),
+    ("    const int tid = threadIdx.x;\n    const int lane = tid & (kWave - 1);\n"
+     "    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);\n    const int G = a.group;",
+     "    STAMP(0, __builtin_amdgcn_s_memrealtime());\n"
+     "    const int tid = threadIdx.x;\n    const int lane = tid & (kWave - 1);\n"
+     "    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);\n    const int G = a.group;"),
+    ("        const bool any_bad = __syncthreads_or(bad);",
+     "        const bool any_bad = __syncthreads_or(bad);\n"
+     "        STAMP(1, __builtin_amdgcn_s_memrealtime());\n"
+     "        STAMP(2, (unsigned long long)__smid());"),
+    ('extern "C" {\n',
+     'extern "C" {\n'
+     "int q8kv_timeline_read(unsigned long long* host, int n) {\n"
+     "    return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(g_stamp), sizeof(unsigned long long) * (size_t)n, 0,"
+     " hipMemcpyDeviceToHost);\n}\n"
+     "int q8kv_timeline_clear() {\n"
+     "    static unsigned long long z[4096 * 8];\n"
+     "    return (int)hipMemcpyToSymbol(HIP_SYMBOL(g_stamp), z, sizeof(z), 0, hipMemcpyHostToDevice);\n}\n"),
+]
+
+
+def timeline_source(src):
+    for a, b in TIMELINE_EDITS:
+        if src.count(a) != 1:
+            raise RuntimeError(f"timeline anchor not found exactly once: {a[:40]!r}")
+        src = src.replace(a, b)
+    return src
+
+
+def run_timeline(w, args):
+    """Build the stamped copy of the library, run the workload's decode, and
+    return the per-workgroup timeline (µs from the first workgroup's start)."""
+    import ctypes
+    import importlib.util
+    import subprocess
+    import tempfile
+    import torch
+    import decode_attention_int8_amd as q8
+    spec = importlib.util.spec_from_file_location("_q8kv_build_tl", os.path.join(ROOT, "decode_attention_int8_amd", "build.py"))
+    b = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(b)
+    d = tempfile.mkdtemp(prefix="q8kv_timeline_")
+    srcp, libp = os.path.join(d, "q8kv_timeline.hip"), os.path.join(d, "libq8kv_timeline.so")
+    open(srcp, "w").write(timeline_source(open(b.SRC).read()))
+    log("building the stamped library copy")
+    subprocess.run([b.HIPCC] + b.FLAGS + [srcp, "-o", libp], check=True, capture_output=True)
+    q8.LIB_PATH = libp
+    q8.lib = q8._load()
+    T = ctypes.CDLL(libp)
+    g = build_gpu(w, torch.device("cuda", 0), args.cold_bytes, codecs=())
+    scale = workloads.softmax_scale(w.hd)
+    out = torch.empty_like(g["q"])
+    R = len(g["caches"])
+    state = {"i": 0}
+
+    def call():
+        q8.decode_attn(g["q"], g["caches"][state["i"] % R], g["table_d"], g["lens_d"], scale, out=out,
+                       part_tokens=args.part_tokens)
+        state["i"] += 1
+
+    def read():
+        st = np.zeros(4096 * 8, np.uint64)
+        if T.q8kv_timeline_read(st.ctypes.data_as(ctypes.c_void_p), 4096 * 8) != 0:
+            raise RuntimeError("stamp read failed")
+        st = st.reshape(4096, 8).astype(np.int64)
+        s_ = st[st[:, 0] > 0]
+        t0 = s_[:, 0].min()
+        start, end = (s_[:, 0] - t0) / 100.0, (s_[:, 1] - t0) / 100.0
+        xcd = s_[:, 2] >> 6
+        q = lambda x, p: round(float(np.percentile(x, p)), 2)
+        return {"workgroups": int(len(s_)),
+                "start_us": {"median": q(start, 50), "max": q(start, 100)},
+                "stream_end_us": {"min": q(end, 0), "median": q(end, 50), "p90": q(end, 90), "max": q(end, 100)},
+                "duration_us": {"median": q(end - start, 50), "max": q(end - start, 100)},
+                "by_cu_group": {int(x): {"workgroups": int((xcd == x).sum()), "start_median": q(start[xcd == x], 50),
+                                         "end_median": q(end[xcd == x], 50), "end_max": q(end[xcd == x], 100)}
+                                for x in np.unique(xcd)}}
+
+    for _ in range(50):
+        call()
+    torch.cuda.synchronize()
+    res = {}
+    for mode, n in (("after_idle", 1), ("back_to_back_last_of_30", 30)):
+        if T.q8kv_timeline_clear() != 0:
+            raise RuntimeError("stamp clear failed")
+        torch.cuda.synchronize()
+        for _ in range(n):
+            call()
+        torch.cuda.synchronize()
+        res[mode] = read()
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -588,6 +693,11 @@ def main():
     q8.debug_set_stage(args.stage)
     w = workloads.WORKLOADS[args.workload]
     dev = torch.device("cuda", 0)
+    if args.timeline:
+        print(json.dumps({"timeline": run_timeline(w, args), "workload": w.name,
+                          "note": "µs from the first workgroup's start; stream_end = after the tile loop, "
+                                  "before the wave merge; CU groups are __smid() >> 6"}), flush=True)
+        return
     log(f"workload {w.name}: batch {w.batch}, heads {w.n_q}/{w.n_kv}, hd {w.hd}, kv_bs {w.kv_bs}, "
         f"seq_len {'U{1..%d}' % w.seq_len if w.ragged else w.seq_len}")
     codecs = tuple(c for c in CODECS if not (c == "fp8" and args.no_fp8) and not (c == "q40" and args.no_q40))

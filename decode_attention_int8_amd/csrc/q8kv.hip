@@ -8,8 +8,9 @@
 // the end.  Here it is laid out for CDNA4 matrix cores:
 //
 //   * one workgroup (4 waves; 8 for a static grid of one workgroup per CU)
-//     owns (sequence b, kv head kh, token partition); the G = n_q / n_kv
-//     query heads of kh share every K/V byte it loads;
+//     owns (sequence b, head group of kv head kh, token partition); the
+//     group's g <= 8 query heads (g the largest divisor of n_q / n_kv that
+//     is at most 8) share every K/V byte it loads;
 //   * a wave walks tiles of 32 tokens.  Q.K^T runs on v_mfma_i32_16x16x64_i8
 //     with A = 16 K rows x 64 bytes (two 32-blocks) and B = the quantised
 //     queries: columns 0-7 carry head g's even block with zeros under the odd
@@ -35,7 +36,11 @@
 //   * ranges longer than one partition are merged with the log-sum-exp rule
 //     in partition order (deterministic): inside the decode kernel by the
 //     workgroup that stores a group's last state when the group is small,
-//     else by a combine kernel.
+//     else by a combine kernel whose workgroups each take 16 output floats of
+//     one query head over every partition;
+//   * a test export switches the int8 static grids to a variant that stages
+//     each wave's tiles through an LDS ring (global_load_lds, two tiles in
+//     flight); same arithmetic, slower here, kept for measurement.
 // Scores are kept in the log2 domain (softmax scale pre-multiplied by log2 e)
 // so every exponential is one v_exp_f32.
 //

@@ -87,20 +87,32 @@ enum {
  * num_blocks   physical blocks in the page pool (bounds table entries).
  * hd           64, 128 or 256.
  * kv_bs        tokens per page: 16, 32, 64, 128 or 256.
- * n_q_heads / n_kv_heads must be an integer group size of 1 to 8.
+ * n_q_heads / n_kv_heads must be a positive integer G.  The query heads of
+ *              a kv head are taken in head groups of g heads, g the largest
+ *              divisor of G that is at most 8 (the matrix cores' column
+ *              set); each head group is its own work item and reads the kv
+ *              head's K/V itself, so G above 8 costs G/g reads of the cache.
  * batch        1 to 2048 sequences per call.
  * scale        softmax scale (normally 1/sqrt(hd)), finite.
+ * K and V scales are any finite non-negative fp32 values (q8kv_append
+ *              writes absmax/127).  The P.V weights carry a power-of-two
+ *              offset that follows the largest V scale seen so far (up to
+ *              2^126), so scales far above 1 do not overflow the f16 weight
+ *              operands and scales far below 1 do not sink into their
+ *              subnormals; outputs are checked for V amplitudes from 1e-6 to
+ *              1e6.
  *
  * Contexts longer than one partition are split into fixed ranges of tokens
  * whose (max, sum, accumulator) states are merged in range order: inside the
- * decode kernel, by the workgroup that stores a (sequence, kv head)'s last
- * state, when there are at most 64 states (partitions x query heads), else
- * by a second kernel.  The plan depends only on the shapes, so results are
+ * decode kernel, by the workgroup that stores a (sequence, head group)'s
+ * last state, when there are at most 64 states (partitions x query heads),
+ * else by a second kernel (one workgroup per 16 output floats of a query
+ * head, over every partition).  The plan depends only on the shapes, so results are
  * deterministic.  Split contexts use a library-owned device workspace (grown
  * on demand with hipMalloc, one per device and stream, freed by
  * q8kv_release, which waits for the device first).  Calls on one stream run
  * in order; calls on different streams use different workspaces.  The
- * workspace holds per-(sequence, kv head) arrival counters that each call
+ * workspace holds per-(sequence, head group) arrival counters that each call
  * leaves at zero, so a call that is aborted mid-kernel leaves the workspace
  * unusable until q8kv_release.
  */

@@ -96,3 +96,13 @@ def test_bench_defaults_name_the_gated_workloads():
     finally:
         sys.argv = old
     assert args.workload == "ragged" and "long_gqa" in args.also.split(",")
+
+
+def test_timeline_edits_apply_to_the_kernel_source():
+    """bench.py --timeline stamps a copy of the kernel source at fixed
+    points; each must still occur exactly once."""
+    sys.path.insert(0, ROOT)
+    import bench
+    src = open(os.path.join(ROOT, "decode_attention_int8_amd", "csrc", "q8kv.hip")).read()
+    out = bench.timeline_source(src)
+    assert out.count("STAMP(") == 4 and "q8kv_timeline_read" in out
