@@ -8,8 +8,11 @@
  * may load it.  It shares no code, header, constant or helper with the HIP
  * library; neither side includes or links the other.
  *
- * Source of every step: the page "Day 9-2: flash_attn_single_q_q8_neon"
- * (trdm.cn news 511694), section 2, the segment-by-segment code walkthrough:
+ * Source of every rule: the page "Day 9-2: flash_attn_single_q_q8_neon"
+ * (trdm.cn news 511694), section 2 (segments 1-3).  The code is organised
+ * around those rules -- a generic absmax quantiser, a score function and an
+ * online-softmax state with init / raise / push -- and keeps the rounding
+ * order the rules fix:
  *   - segment 1 (Q -> int8, one absmax scale per 32 elements, same shape as
  *     Q8_0): per block  a = max|q|,  a < 1e-6 -> a = 1,  qsc = a * (1/127),
  *     iq = 127 / a,  qi = (int8) clamp(q * iq, -128, 127);
@@ -159,44 +162,75 @@ typedef struct {
     float* w;   /* weight given to token t when it arrived */
 } orc_trace;
 
-/* The page's recurrence over tokens [t0, t1) of (b, h), in fp32, in the
- * page's order.  qi/qsc hold the already quantised query row. */
+/* Score of one K row (section 2, segment 2): one int32 dot per 32-block,
+ * each times its query block's scale, added in block order; the sum times
+ * the row's K factor, then times the softmax scale. */
+static float orc_score(const int8_t* qi, const float* qsc, const int8_t* k, int nb, float ks, float scale) {
+    float s = 0.0f;
+    for (int blk = 0; blk < nb; ++blk) s = s + (float)orc_block_dot(qi, k, blk) * qsc[blk];
+    return (s * ks) * scale;
+}
+
+/* The online-softmax state of one query head (section 2, segment 2): the
+ * largest score so far M, the sum S of exp(s_t - M) over the tokens so far,
+ * and acc = sum_t exp(s_t - M) * vs_t * V_t over the int8 V codes.  It starts
+ * at the page's M = -1e9, S = 0, acc = 0. */
+typedef struct {
+    float M, S;
+    float* acc;
+    int hd;
+} orc_state;
+
+static void orc_state_init(orc_state* st, float* acc, int hd) {
+    st->M = ORC_M_INIT;
+    st->S = 0.0f;
+    st->acc = acc;
+    st->hd = hd;
+    for (int i = 0; i < hd; ++i) acc[i] = 0.0f;
+}
+
+/* A score s above M moves the normalisation point to s: S and acc are
+ * multiplied by exp(M - s). */
+static void orc_state_raise(orc_state* st, float s) {
+    float m = expf(st->M - s);
+    st->S = st->S * m;
+    for (int i = 0; i < st->hd; ++i) st->acc[i] = st->acc[i] * m;
+    st->M = s;
+}
+
+/* Fold in one token of score s whose V row has codes v and factor vs; the
+ * token's weight is exp(s - M) after any raise (exactly 1 when it raised M).
+ * Returns that weight. */
+static float orc_state_push(orc_state* st, float s, const int8_t* v, float vs) {
+    float w;
+    if (s > st->M) {
+        orc_state_raise(st, s);
+        w = 1.0f;
+    } else {
+        w = expf(s - st->M);
+    }
+    st->S = st->S + w;
+    float f = w * vs;
+    for (int i = 0; i < st->hd; ++i) st->acc[i] = st->acc[i] + (float)v[i] * f;
+    return w;
+}
+
+/* The recurrence over tokens [t0, t1) of (b, h), in fp32, token by token.
+ * qi/qsc hold the already quantised query row. */
 static void orc_run_f32(const orc_args* a, int b, int h, const int8_t* qi, const float* qsc,
-                        int t0, int t1, float* M_out, float* S_out, float* acc,
-                        const orc_trace* tr) {
+                        int t0, int t1, orc_state* st, const orc_trace* tr) {
     int G = a->n_q / a->n_kv, kh = h / G, nb = a->hd / ORC_QBLOCK;
-    float M = ORC_M_INIT, S = 0.0f;
-    for (int i = 0; i < a->hd; ++i) acc[i] = 0.0f;
     for (int t = t0; t < t1; ++t) {
         size_t row = orc_row(a, b, kh, t);
-        const int8_t* k = a->k_pages + row * a->hd;
-        const int8_t* v = a->v_pages + row * a->hd;
-        float ks = a->k_scale[row], vs = a->v_scale[row];
-        float s = 0.0f;
-        for (int blk = 0; blk < nb; ++blk) s = s + (float)orc_block_dot(qi, k, blk) * qsc[blk];
-        s = (s * ks) * a->scale;
-        float w;
-        if (s > M) {
-            float m = expf(M - s);
-            S = S * m;
-            for (int i = 0; i < a->hd; ++i) acc[i] = acc[i] * m;
-            M = s;
-            w = 1.0f;
-        } else {
-            w = expf(s - M);
-        }
-        S = S + w;
-        float f = w * vs;
-        for (int i = 0; i < a->hd; ++i) acc[i] = acc[i] + (float)v[i] * f;
+        float s = orc_score(qi, qsc, a->k_pages + row * a->hd, nb, a->k_scale[row], a->scale);
+        float w = orc_state_push(st, s, a->v_pages + row * a->hd, a->v_scale[row]);
         if (tr) {
             tr->s[t - t0] = s;
-            tr->m[t - t0] = M;
-            tr->sum[t - t0] = S;
+            tr->m[t - t0] = st->M;
+            tr->sum[t - t0] = st->S;
             tr->w[t - t0] = w;
         }
     }
-    *M_out = M;
-    *S_out = S;
 }
 
 /* The same recurrence with every float quantity held in double; it reads the
@@ -211,22 +245,20 @@ static void orc_run_f64(const orc_args* a, int b, int h, const int8_t* qi, const
         size_t row = orc_row(a, b, kh, t);
         const int8_t* k = a->k_pages + row * a->hd;
         const int8_t* v = a->v_pages + row * a->hd;
-        double ks = a->k_scale[row], vs = a->v_scale[row];
         double s = 0.0;
         for (int blk = 0; blk < nb; ++blk) s = s + (double)orc_block_dot(qi, k, blk) * (double)qsc[blk];
-        s = (s * ks) * (double)a->scale;
-        double w;
+        s = (s * (double)a->k_scale[row]) * (double)a->scale;
+        double w = 1.0;
         if (s > M) {
             double m = exp(M - s);
             S = S * m;
             for (int i = 0; i < a->hd; ++i) acc[i] = acc[i] * m;
             M = s;
-            w = 1.0;
         } else {
             w = exp(s - M);
         }
         S = S + w;
-        double f = w * vs;
+        double f = w * (double)a->v_scale[row];
         for (int i = 0; i < a->hd; ++i) acc[i] = acc[i] + (double)v[i] * f;
     }
     *M_out = M;
@@ -260,9 +292,10 @@ static void orc_head(const orc_args* a, int b, int h, int part_tokens, int use_f
         goto done;
     }
     if (part_tokens <= 0 || part_tokens >= L) {
-        float M, S;
-        orc_run_f32(a, b, h, qi, qsc, 0, L, &M, &S, acc, tr);
-        for (int i = 0; i < hd; ++i) out[i] = acc[i] / S;
+        orc_state st;
+        orc_state_init(&st, acc, hd);
+        orc_run_f32(a, b, h, qi, qsc, 0, L, &st, tr);
+        for (int i = 0; i < hd; ++i) out[i] = acc[i] / st.S;
         goto done;
     }
     {
@@ -272,7 +305,11 @@ static void orc_head(const orc_args* a, int b, int h, int part_tokens, int use_f
         float* accp = (float*)malloc(sizeof(float) * (size_t)np * hd);
         for (int p = 0; p < np; ++p) {
             int t0 = p * part_tokens, t1 = t0 + part_tokens < L ? t0 + part_tokens : L;
-            orc_run_f32(a, b, h, qi, qsc, t0, t1, &Mp[p], &Sp[p], accp + (size_t)p * hd, NULL);
+            orc_state st;
+            orc_state_init(&st, accp + (size_t)p * hd, hd);
+            orc_run_f32(a, b, h, qi, qsc, t0, t1, &st, NULL);
+            Mp[p] = st.M;
+            Sp[p] = st.S;
         }
         float Mx = ORC_M_INIT;
         for (int p = 0; p < np; ++p) Mx = fmaxf(Mx, Mp[p]);

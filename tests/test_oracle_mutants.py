@@ -26,23 +26,22 @@ MUTANTS = {
     "scale_divides": ("*scale_out = a * ORC_INV127;", "*scale_out = a / 127.0f;"),
     "drop_qsc": ("s = s + (float)orc_block_dot(qi, k, blk) * qsc[blk];",
                  "s = s + (float)orc_block_dot(qi, k, blk);"),
-    "drop_ks": ("s = (s * ks) * a->scale;", "s = s * a->scale;"),
-    "no_acc_rescale": ("float m = expf(M - s);\n            S = S * m;\n"
-                       "            for (int i = 0; i < a->hd; ++i) acc[i] = acc[i] * m;",
-                       "float m = expf(M - s);\n            S = S * m;"),
-    "no_sum_rescale": ("float m = expf(M - s);\n            S = S * m;", "float m = expf(M - s);"),
-    "exp_sign": ("w = expf(s - M);", "w = expf(M - s);"),
+    "drop_ks": ("return (s * ks) * scale;", "return s * scale;"),
+    "no_acc_rescale": ("    for (int i = 0; i < st->hd; ++i) st->acc[i] = st->acc[i] * m;\n", ""),
+    "no_sum_rescale": ("    st->S = st->S * m;\n", ""),
+    "exp_sign": ("w = expf(s - st->M);", "w = expf(st->M - s);"),
     "drop_vs": ("float f = w * vs;", "float f = w;"),
-    "no_final_divide": ("for (int i = 0; i < hd; ++i) out[i] = acc[i] / S;",
+    "no_final_divide": ("for (int i = 0; i < hd; ++i) out[i] = acc[i] / st.S;",
                         "for (int i = 0; i < hd; ++i) out[i] = acc[i];"),
-    "kv_head_modulo": ("int G = a->n_q / a->n_kv, kh = h / G, nb = a->hd / ORC_QBLOCK;\n    float M",
-                       "int G = a->n_q / a->n_kv, kh = h % a->n_kv, nb = a->hd / ORC_QBLOCK; (void)G;\n    float M"),
+    "kv_head_modulo": ("int G = a->n_q / a->n_kv, kh = h / G, nb = a->hd / ORC_QBLOCK;\n    for (int t = t0;",
+                       "int G = a->n_q / a->n_kv, kh = h % a->n_kv, nb = a->hd / ORC_QBLOCK; (void)G;\n"
+                       "    for (int t = t0;"),
     "row_index": ("(size_t)(t % a->kv_bs);", "(size_t)((t + 1) % a->kv_bs);"),
     "transposed_dot": ("d += (int32_t)qi[blk * ORC_QBLOCK + i] * (int32_t)k[blk * ORC_QBLOCK + i];",
                        "d += (int32_t)qi[blk * ORC_QBLOCK + i] * (int32_t)k[i * 4 % 128 + blk];"),
     "merge_unweighted": ("St = St + Sp[p] * e;", "St = St + Sp[p];"),
-    "max_hysteresis": ("if (s > M) {\n            float m", "if (s > M - 0.5f) {\n            float m"),
-    "max_not_updated": ("            M = s;\n            w = 1.0f;", "            w = 1.0f;"),
+    "max_hysteresis": ("if (s > st->M) {", "if (s > st->M - 0.5f) {"),
+    "max_not_updated": ("    st->M = s;\n", ""),
 }
 
 
