@@ -124,10 +124,16 @@ def _need(t, name, dtype, device, ndim):
         raise ValueError(f"{name} must be contiguous")
 
 
+def page_hd(hd):
+    """Width of an int8 page row for head size hd (a multiple of 32 up to
+    256): hd rounded up to 64, 128 or 256; the pad columns hold zero codes."""
+    return 64 if hd <= 64 else 128 if hd <= 128 else 256
+
+
 class PagedKVCache:
     """Device page pool of one layer's q8 KV cache.
 
-    k_pages, v_pages int8 [num_blocks][n_kv][kv_bs][hd];
+    k_pages, v_pages int8 [num_blocks][n_kv][kv_bs][hp], hp = page_hd(hd);
     k_scale, v_scale fp32 [num_blocks][n_kv][kv_bs].
     """
 
@@ -142,17 +148,23 @@ class PagedKVCache:
     def __init__(self, num_blocks, n_kv, kv_bs, hd, device="cuda"):
         dev = torch.device(device)
         self.num_blocks, self.n_kv, self.kv_bs, self.hd = num_blocks, n_kv, kv_bs, hd
-        self.k_pages = torch.empty((num_blocks, n_kv, kv_bs, hd), dtype=torch.int8, device=dev)
+        self.hp = page_hd(hd)
+        self.k_pages = torch.empty((num_blocks, n_kv, kv_bs, self.hp), dtype=torch.int8, device=dev)
         self.v_pages = torch.empty_like(self.k_pages)
         self.k_scale = torch.empty((num_blocks, n_kv, kv_bs), dtype=torch.float32, device=dev)
         self.v_scale = torch.empty_like(self.k_scale)
 
     @classmethod
-    def wrap(cls, k_pages, v_pages, k_scale, v_scale):
+    def wrap(cls, k_pages, v_pages, k_scale, v_scale, hd=None):
+        """Use existing tensors as the pool; hd (default: the page width)
+        is the head size the pages hold."""
         self = cls.__new__(cls)
         object.__setattr__(self, "_meta", None)
         self.k_pages, self.v_pages, self.k_scale, self.v_scale = k_pages, v_pages, k_scale, v_scale
-        self.num_blocks, self.n_kv, self.kv_bs, self.hd = k_pages.shape
+        self.num_blocks, self.n_kv, self.kv_bs, self.hp = k_pages.shape
+        self.hd = self.hp if hd is None else hd
+        if page_hd(self.hd) != self.hp:
+            raise ValueError(f"pages {self.hp} wide cannot hold head size {self.hd}")
         return self
 
     @property
@@ -161,7 +173,7 @@ class PagedKVCache:
 
     def validate(self):
         d = self.device
-        shp = (self.num_blocks, self.n_kv, self.kv_bs, self.hd)
+        shp = (self.num_blocks, self.n_kv, self.kv_bs, getattr(self, "hp", self.hd))
         for name in ("k_pages", "v_pages"):
             t = getattr(self, name)
             _need(t, name, torch.int8, d, 4)

@@ -150,16 +150,19 @@ struct QRows {
 };
 
 // Every thread issues its loads unconditionally (rows past G re-read row
-// G - 1), so no branch makes a later wait conservative.
+// G - 1, columns past the row's hdr re-read its first ones), so no branch
+// makes a later wait conservative.  q rows are hdr floats apart; hdr <= HD
+// (a head size padded to HD in the pages: the pad columns are zero).
 template <int HD, int NT>
-__device__ __forceinline__ void load_q_rows(QRows<HD, NT>& Q, const float* __restrict__ q, int G, int tid) {
+__device__ __forceinline__ void load_q_rows(QRows<HD, NT>& Q, const float* __restrict__ q, int G, int hdr,
+                                            int tid) {
 #pragma unroll
     for (int i = 0; i < QRows<HD, NT>::kPer; ++i) {
         const int c = min(tid + i * NT, QRows<HD, NT>::kChunks - 1);
         const int g = c / (HD / 4);
         const int e = (c % (HD / 4)) * 4;
-        Q.x[i] = *reinterpret_cast<const f32x4*>(q + (size_t)min(g, G - 1) * HD + e);
-        Q.keep[i] = g < G;
+        Q.x[i] = *reinterpret_cast<const f32x4*>(q + (size_t)min(g, G - 1) * hdr + (e < hdr ? e : 0));
+        Q.keep[i] = g < G && e < hdr;
     }
 }
 
@@ -167,7 +170,7 @@ __device__ __forceinline__ void load_q_rows(QRows<HD, NT>& Q, const float* __res
 // each), for kernels whose other loads all go to LDS: a register load among
 // them would make the compiler wait for every one of them before its use.
 template <int HD, int NT>
-__device__ __forceinline__ void dma_q_rows(int8_t* lraw, const float* __restrict__ q, int G, int tid, int wid);
+__device__ __forceinline__ void dma_q_rows(int8_t* lraw, const float* __restrict__ q, int G, int hdr, int tid, int wid);
 
 template <int HD, int NT>
 __device__ __forceinline__ void quantize_q_regs(const QRows<HD, NT>& Q, int8_t* lq, float* lqsc, int tid,
@@ -201,9 +204,10 @@ __device__ __forceinline__ void quantize_q_regs(const QRows<HD, NT>& Q, int8_t* 
 }
 
 template <int HD, int NT>
-__device__ __forceinline__ void quantize_q_rows(const float* __restrict__ q, int G, int8_t* lq, float* lqsc, int tid) {
+__device__ __forceinline__ void quantize_q_rows(const float* __restrict__ q, int G, int hdr, int8_t* lq, float* lqsc,
+                                                int tid) {
     QRows<HD, NT> Q;
-    load_q_rows<HD, NT>(Q, q, G, tid);
+    load_q_rows<HD, NT>(Q, q, G, hdr, tid);
     quantize_q_regs<HD, NT>(Q, lq, lqsc, tid);
 }
 
@@ -408,6 +412,10 @@ struct DecodeArgs {
     // 1: block_table is [batch][max_blocks]; n_kv: [batch][n_kv][max_blocks]
     // (a block list per kv head, as the QUEST selection produces)
     int table_rows;
+    // The caller's head size (a multiple of 32); HD is it rounded up to a
+    // multiple of 64, the width of the pages and of every internal row.
+    // q and out rows are hdr floats long.
+    int hdr;
 };
 
 // The kernel's arguments read afresh from the kernel argument segment, for
@@ -490,6 +498,15 @@ __device__ __forceinline__ void group_max_sum(const float2* lms, int G, int g, i
 // 2^(M_p - M*), out = sum acc_p 2^(M_p - M*) / S*.  Thread (row r, slice e4) sums partitions r, r + R, ...
 // in order; the R row sums are then added in row order, so the result does
 // not depend on which workgroup merges.
+// Store output slice e4 (head e4 / (HD / 4), columns 4 (e4 % (HD / 4)) ..
+// + 3) into rows hdr floats apart; slices in a padded head's pad columns are
+// dropped.
+template <int HD>
+__device__ __forceinline__ void store_out_slice(float* out_rows, int e4, int hdr, f32x4 v) {
+    const int g = e4 / (HD / 4), e = 4 * (e4 % (HD / 4));
+    if (e < hdr) *reinterpret_cast<f32x4*>(out_rows + (size_t)g * hdr + e) = v;
+}
+
 template <int HD, int NT>
 __device__ void merge_group(const DecodeArgs& a, size_t gi, int np, float* out_rows, int tid, float2* lms,
                             f32x4* lred) {
@@ -517,17 +534,17 @@ __device__ void merge_group(const DecodeArgs& a, size_t gi, int np, float* out_r
         __syncthreads();
         if (r == 0) {
             for (int rr = 1; rr < R; ++rr) at += lred[rr * slices + e4];
-            *reinterpret_cast<f32x4*>(out_rows + (size_t)e4 * 4) = at / St;
+            store_out_slice<HD>(out_rows, e4, a.hdr, at / St);
         }
         return;
     }
-    if (active) *reinterpret_cast<f32x4*>(out_rows + (size_t)e4 * 4) = at / St;
+    if (active) store_out_slice<HD>(out_rows, e4, a.hdr, at / St);
     // slices > NT (hd 256 with five or more heads): further slices
     for (e4 += NT; active && e4 < slices; e4 += NT) {
         load_slices(v, racc, pstride, e4, 0, 1, np);
         group_max_sum(lms, G, e4 / Q4, np, Mx, St);
         at = weigh_slices(v, lms, G, e4 / Q4, Mx, 0, 1, np);
-        *reinterpret_cast<f32x4*>(out_rows + (size_t)e4 * 4) = at / St;
+        store_out_slice<HD>(out_rows, e4, a.hdr, at / St);
     }
 }
 
@@ -553,20 +570,23 @@ struct NewRow {
     float x[EPL];
 };
 
-// The lane's EPL elements of source row `row` ([rows][HD], fp32, or bf16
-// widened exactly).
+// The lane's EPL elements of source row `row` ([rows][hdr], fp32, or bf16
+// widened exactly).  Rows shorter than HD (hdr a multiple of 32, so a lane's
+// elements are all inside or all outside) are zero-padded: zeros change
+// neither the row's absmax nor any dot product.
 template <int HD>
-__device__ __forceinline__ void row_load(NewRow<HD>& r, const void* src, size_t row, int bf16, int lane) {
+__device__ __forceinline__ void row_load(NewRow<HD>& r, const void* src, size_t row, int bf16, int lane, int hdr) {
     constexpr int EPL = NewRow<HD>::EPL;
-    const size_t off = row * HD + (size_t)lane * EPL;
+    const bool in = lane * EPL < hdr;
+    const size_t off = row * hdr + (in ? (size_t)lane * EPL : 0);
     if (bf16) {
         const uint16_t* s16 = static_cast<const uint16_t*>(src) + off;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) r.x[e] = __uint_as_float((uint32_t)s16[e] << 16);
+        for (int e = 0; e < EPL; ++e) r.x[e] = in ? __uint_as_float((uint32_t)s16[e] << 16) : 0.0f;
     } else {
         const float* s32 = static_cast<const float*>(src) + off;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) r.x[e] = s32[e];
+        for (int e = 0; e < EPL; ++e) r.x[e] = in ? s32[e] : 0.0f;
     }
 }
 
@@ -713,13 +733,13 @@ __device__ __forceinline__ f32x4 lds_read16(const int8_t* p) {
 }
 
 template <int HD, int NT>
-__device__ __forceinline__ void dma_q_rows(int8_t* lraw, const float* __restrict__ q, int G, int tid, int wid) {
+__device__ __forceinline__ void dma_q_rows(int8_t* lraw, const float* __restrict__ q, int G, int hdr, int tid, int wid) {
 #pragma unroll
     for (int i = 0; i < QRows<HD, NT>::kPer; ++i) {
         const int c = min(tid + i * NT, QRows<HD, NT>::kChunks - 1);
         const int g = c / (HD / 4);
         const int e = (c % (HD / 4)) * 4;
-        dma16(q + (size_t)min(g, G - 1) * HD + e, lraw + 16 * (i * NT + kWave * wid));
+        dma16(q + (size_t)min(g, G - 1) * hdr + (e < hdr ? e : 0), lraw + 16 * (i * NT + kWave * wid));
     }
 }
 
@@ -865,10 +885,10 @@ __device__ __forceinline__ void tile_patch(Tile<HD>& T, const int8_t* lk, const 
 
 template <int HD>
 __device__ __forceinline__ void load_new_rows(NewRow<HD>& nk, NewRow<HD>& nv, const void* knew, const void* vnew,
-                                              int bf16, int b, int n_kv, int kh, int lane) {
+                                              int bf16, int b, int n_kv, int kh, int lane, int hdr) {
     const size_t src_row = (size_t)b * n_kv + kh;
-    row_load<HD>(nk, knew, src_row, bf16, lane);
-    row_load<HD>(nv, vnew, src_row, bf16, lane);
+    row_load<HD>(nk, knew, src_row, bf16, lane, hdr);
+    row_load<HD>(nv, vnew, src_row, bf16, lane, hdr);
 }
 
 // lnew [2][HD] codes, lsc [2] factors, *lblk the new token's physical block.
@@ -1603,8 +1623,8 @@ q8kv_decode_kernel(const DecodeArgs a) {
         // empty sequences get zero rows; sequence b is zeroed by workgroup b mod grid
         for (int bb = blockIdx.x; bb < a.batch; bb += gridDim.x) {
             if (lfull[bb + 1] == lfull[bb] && lcls[bb] == kNoPartial) {
-                float* o = a.out + (size_t)bb * a.n_q * HD;
-                for (int e = tid; e < a.n_q * HD; e += NT) o[e] = 0.0f;
+                float* o = a.out + (size_t)bb * a.n_q * a.hdr;
+                for (int e = tid; e < a.n_q * a.hdr; e += NT) o[e] = 0.0f;
             }
         }
     }
@@ -1659,8 +1679,8 @@ q8kv_decode_kernel(const DecodeArgs a) {
         // the query rows' loads go out first: the quantisation then waits for
         // them alone, not for the first tile queued behind them
         QRows<HD, NT> qrows;
-        if constexpr (STAGE) dma_q_rows<HD, NT>(lqraw, a.q + ((size_t)b * a.n_q + (size_t)ih * G) * HD, G, itid, wid);
-        else load_q_rows<HD, NT>(qrows, a.q + ((size_t)b * a.n_q + (size_t)ih * G) * HD, G, itid);
+        if constexpr (STAGE) dma_q_rows<HD, NT>(lqraw, a.q + ((size_t)b * a.n_q + (size_t)ih * G) * a.hdr, G, a.hdr, itid, wid);
+        else load_q_rows<HD, NT>(qrows, a.q + ((size_t)b * a.n_q + (size_t)ih * G) * a.hdr, G, a.hdr, itid);
         const int32_t* trow = a.table + ((size_t)b * a.table_rows + (a.table_rows > 1 ? kh : 0)) * a.max_blocks;
         const int t0 = part * a.part_tokens;
         // The first tile's table reads, those of the item's first tile (a
@@ -1678,13 +1698,13 @@ q8kv_decode_kernel(const DecodeArgs a) {
             L = cap;
             bad = true;
         }
-        float* out_rows = a.out + ((size_t)b * a.n_q + (size_t)ih * G) * HD;
+        float* out_rows = a.out + ((size_t)b * a.n_q + (size_t)ih * G) * a.hdr;
         if constexpr (STATIC) {
             // a slot past the sequence's end has nothing to do; an empty
             // sequence's rows are zeroed by its partition-0 slots
             if (t0 >= L) {
                 if (part == 0)
-                    for (int e = itid; e < G * HD; e += NT) out_rows[e] = 0.0f;
+                    for (int e = itid; e < G * a.hdr; e += NT) out_rows[e] = 0.0f;
                 return;
             }
         }
@@ -1710,7 +1730,7 @@ q8kv_decode_kernel(const DecodeArgs a) {
             // registers are live (the item loop leaves few to spare)
             if (tail_ts != INT_MIN) {
                 ConstArgs* ka = kernel_args();
-                load_new_rows<HD>(nk, nv, ka->knew, ka->vnew, ka->new_bf16, b, a.n_kv, kh, ilane);
+                load_new_rows<HD>(nk, nv, ka->knew, ka->vnew, ka->new_bf16, b, a.n_kv, kh, ilane, a.hdr);
                 prepare_new_token<HD>(nk, nv, tail_blk, lnew, lnew_sc, &lnew_blk, ilane);
             }
         }
@@ -1744,7 +1764,7 @@ q8kv_decode_kernel(const DecodeArgs a) {
         }
         if constexpr (NEW && STATIC) {
             // static grids: the new rows' loads go out behind the first tile
-            if (tail_ts != INT_MIN) load_new_rows<HD>(nk, nv, a.knew, a.vnew, a.new_bf16, b, a.n_kv, kh, ilane);
+            if (tail_ts != INT_MIN) load_new_rows<HD>(nk, nv, a.knew, a.vnew, a.new_bf16, b, a.n_kv, kh, ilane, a.hdr);
         }
         // keep the query quantisation (which waits for the query rows) behind
         // the tile loads: the scheduler would otherwise fill the address
@@ -1762,7 +1782,7 @@ q8kv_decode_kernel(const DecodeArgs a) {
                 for (int i = 0; i < QRows<HD, NT>::kPer; ++i) {
                     const int c = itid + i * NT;
                     qrows.x[i] = lds_read16(lqraw + 16 * c);
-                    qrows.keep[i] = c / (HD / 4) < G;
+                    qrows.keep[i] = c / (HD / 4) < G && (c % (HD / 4)) * 4 < a.hdr;
                 }
             }
             quantize_q_regs<HD, NT>(qrows, lq, lqsc, itid);
@@ -1886,7 +1906,7 @@ q8kv_decode_kernel(const DecodeArgs a) {
             }
             if (any_bad) at = f32x4{NAN, NAN, NAN, NAN};
             if (np_b == 1) {
-                *reinterpret_cast<f32x4*>(out_rows + (size_t)e4 * 4) = at / St;
+                store_out_slice<HD>(out_rows, e4, a.hdr, at / St);
             } else {
                 state_store4(racc, (uint32_t)e4 * 16, at);
                 if (i4 == 0) state_store2(rms, (uint32_t)g * 8, make_float2(Mx, St));
@@ -1931,20 +1951,19 @@ struct CombineArgs {
     const float* st_ms;
     const int32_t* lens;
     int n_q, n_hk, group, cap, part_tokens, n_parts;
+    int hdr;  // output row length (the head size; HD is it padded to 64)
 };
 
 // Merge the partition states of one (sequence, query head) with the rescale
 // rule: M* = max M_p, S* = sum S_p 2^(M_p - M*), out = sum acc_p 2^(M_p - M*) / S*.
-// A head's row is split over kCombineSplit<HD> workgroups of kCombineCols
-// float4 slices each, so that a long context's states are read by many CUs
+// A head's row is split over hdr / 16 workgroups of kCombineCols float4
+// slices each (a padded head's pad columns get none), so that a long context's states are read by many CUs
 // at once.  Thread (row r, column c) owns partitions p = r, r + ROWS, ... and
 // sums them in increasing order; the ROWS row sums are then added by a fixed
 // tree (lane shuffles inside a wave, then the waves in order), so the result
 // is deterministic.  All state loads are issued at once, together with the
 // length read (slots past the sequence's partitions are read but never used).
 constexpr int kCombineCols = 4;
-template <int HD>
-constexpr int kCombineSplit = HD / 4 / kCombineCols;
 
 template <int HD>
 __global__ __launch_bounds__(kThreads) void q8kv_combine_kernel(const CombineArgs a) {
@@ -1956,7 +1975,8 @@ __global__ __launch_bounds__(kThreads) void q8kv_combine_kernel(const CombineArg
     __shared__ float lsp[kWaves];
     __shared__ float lmax[kWaves];
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid >> 6;
-    const int sl = blockIdx.x % kCombineSplit<HD>, bh = blockIdx.x / kCombineSplit<HD>;
+    const int nsplit = a.hdr / (4 * CS);
+    const int sl = blockIdx.x % nsplit, bh = blockIdx.x / nsplit;
     const int h = bh % a.n_q, b = bh / a.n_q;
     const int ih = h / a.group, g = h % a.group;  // head group, head in it
     const size_t first = (((size_t)b * a.n_hk + ih) * a.n_parts) * a.group + g;  // state of p = 0
@@ -2020,7 +2040,7 @@ __global__ __launch_bounds__(kThreads) void q8kv_combine_kernel(const CombineArg
             t += lpart[w][tid];
             St += lsp[w];
         }
-        *reinterpret_cast<f32x4*>(a.out + ((size_t)b * a.n_q + h) * HD + 4 * i4) = t / St;
+        *reinterpret_cast<f32x4*>(a.out + ((size_t)b * a.n_q + h) * a.hdr + 4 * i4) = t / St;
     }
 }
 
@@ -2037,6 +2057,7 @@ struct AppendArgs {
     const int32_t* slots;
     int n_tokens, n_kv, kv_bs, src_bf16;
     long long n_slots;
+    int hdr;  // source row length (the head size; the pages are HD wide)
 };
 
 template <int HD>
@@ -2051,8 +2072,8 @@ __global__ __launch_bounds__(256) void q8kv_append_kernel(const AppendArgs a) {
     const size_t dst_row = ((size_t)blk * a.n_kv + kh) * a.kv_bs + rr;
     const size_t src_row = (size_t)t * a.n_kv + kh;
     NewRow<HD> k, v;
-    row_load<HD>(k, a.ksrc, src_row, a.src_bf16, lane);
-    row_load<HD>(v, a.vsrc, src_row, a.src_bf16, lane);
+    row_load<HD>(k, a.ksrc, src_row, a.src_bf16, lane, a.hdr);
+    row_load<HD>(v, a.vsrc, src_row, a.src_bf16, lane, a.hdr);
     float dk, dv;
     const uint32_t pk = row_quantize<HD>(k, dk);
     const uint32_t pv = row_quantize<HD>(v, dv);
@@ -2061,14 +2082,15 @@ __global__ __launch_bounds__(256) void q8kv_append_kernel(const AppendArgs a) {
 }
 
 // ----------------------------------------------------------------------------
-// import of a row-order int8 cache: pages [block][row][kv head][HD] (a block
+// import of a row-order int8 cache: pages [block][row][kv head][hdr] (a block
 // holds kv_bs token rows of every kv head, as the page "Day 9-2:
 // flash_attn_single_q_q8_neon" (trdm.cn) addresses its int8 K/V blocks in its
 // function-signature section: row t % kv_bs of block t / kv_bs, kv head at
-// offset kh * HD inside the row) and scales [block][row][kv head], rewritten
+// offset kh * hdr inside the row) and scales [block][row][kv head], rewritten
 // into the library's pages and scales.  A pure byte permutation: one thread
-// per 16-byte piece of a source row, read in source order (coalesced); the
-// piece lands whole (K) or as 16 / BPL runs of BPL bytes (V).
+// per 16-byte piece of a library row (HD bytes: the head size padded to 64),
+// read in source order (coalesced); the piece lands whole (K) or as 16 / BPL
+// runs of BPL bytes (V).  Pieces in a padded head's pad columns are zeros.
 
 struct ImportArgs {
     int8_t* kp;
@@ -2081,6 +2103,7 @@ struct ImportArgs {
     const float* vssrc;
     size_t n_pieces;  // num_blocks * kv_bs * n_kv * HD / 16
     int n_kv, kv_bs;
+    int hdr;  // source row length (the head size)
 };
 
 template <int HD>
@@ -2098,7 +2121,7 @@ __global__ __launch_bounds__(256) void q8kv_import_kernel(const ImportArgs a) {
         const size_t blk = br / a.kv_bs;
         const size_t dst_row = (blk * a.n_kv + kh) * a.kv_bs + rr;
         const int row = rr % kSub, col = 16 * c16;
-        const u32x4 x = *reinterpret_cast<const u32x4*>(src + 16 * i);
+        const u32x4 x = col < a.hdr ? *reinterpret_cast<const u32x4*>(src + src_row * a.hdr + col) : u32x4{0u, 0u, 0u, 0u};
         int8_t* sub = pages + (dst_row - row) * HD;
         if (!V) {
             *reinterpret_cast<u32x4*>(sub + k_swizzle(row, col)) = x;
@@ -2673,8 +2696,8 @@ __global__ __launch_bounds__(256) void q8kv_q40_append_kernel(const Q4AppendArgs
     const size_t dst_row = ((size_t)blk * a.n_kv + kh) * a.kv_bs + rr;
     const size_t src_row = (size_t)t * a.n_kv + kh;
     NewRow<HD> k, v;
-    row_load<HD>(k, a.ksrc, src_row, a.src_bf16, lane);
-    row_load<HD>(v, a.vsrc, src_row, a.src_bf16, lane);
+    row_load<HD>(k, a.ksrc, src_row, a.src_bf16, lane, HD);
+    row_load<HD>(v, a.vsrc, src_row, a.src_bf16, lane, HD);
     q4_row_store<HD, false>(a.kp, a.ks, dst_row, rr, k, lane);
     q4_row_store<HD, true>(a.vp, a.vs, dst_row, rr, v, lane);
 }
@@ -2703,8 +2726,8 @@ __global__ __launch_bounds__(256) void q8kv_fp8_append_kernel(const Fp8AppendArg
     const size_t dst_row = ((size_t)blk * a.n_kv + kh) * a.kv_bs + rr;
     const size_t src_row = (size_t)t * a.n_kv + kh;
     NewRow<HD> k, v;
-    row_load<HD>(k, a.ksrc, src_row, a.src_bf16, lane);
-    row_load<HD>(v, a.vsrc, src_row, a.src_bf16, lane);
+    row_load<HD>(k, a.ksrc, src_row, a.src_bf16, lane, HD);
+    row_load<HD>(v, a.vsrc, src_row, a.src_bf16, lane, HD);
     fp8_row_store<HD, false>(a.kp, a.ks, dst_row, rr, k, lane);
     fp8_row_store<HD, true>(a.vp, a.vs, dst_row, rr, v, lane);
 }
@@ -2719,7 +2742,7 @@ __global__ __launch_bounds__(kThreads) void q8kv_debug_quantize_kernel(int8_t* q
     __shared__ float lqsc[kHeadGroup * Geo<HD>::NB];
     const int r0 = blockIdx.x * kHeadGroup;
     const int G = min(kHeadGroup, rows - r0);
-    quantize_q_rows<HD, kThreads>(q + (size_t)r0 * HD, G, lq, lqsc, threadIdx.x);
+    quantize_q_rows<HD, kThreads>(q + (size_t)r0 * HD, G, HD, lq, lqsc, threadIdx.x);
     __syncthreads();
     for (int e = threadIdx.x; e < G * HD; e += kThreads) qi[(size_t)r0 * HD + e] = lq[e];
     for (int e = threadIdx.x; e < G * Geo<HD>::NB; e += kThreads) qsc[(size_t)r0 * Geo<HD>::NB + e] = lqsc[e];
@@ -2744,7 +2767,7 @@ __global__ __launch_bounds__(kThreads) void q8kv_debug_dots_kernel(const DotsArg
     const int kh = blockIdx.x % a.n_kv, b = blockIdx.x / a.n_kv;
     const int G = a.group;
     const int Lm = min(min(a.lens[b], a.max_blocks * a.kv_bs), a.max_tok);
-    quantize_q_rows<HD, kThreads>(a.q + ((size_t)b * a.n_q + (size_t)kh * G) * HD, G, lq, lqsc, tid);
+    quantize_q_rows<HD, kThreads>(a.q + ((size_t)b * a.n_q + (size_t)kh * G) * HD, G, HD, lq, lqsc, tid);
     __syncthreads();
     QOperand<HD> Q;
     load_q_operand<HD>(Q, lq, lqsc, lane);
@@ -2853,12 +2876,18 @@ std::map<std::pair<int, int>, LaunchInfo> g_launch;  // (device, hd * 4 + kernel
 std::atomic<int> g_wide{1};  // wide workgroups allowed (a test export turns them off)
 std::atomic<int> g_stage{0};  // LDS-staged int8 static kernels (a test export turns them on)
 
-bool valid_hd(int hd) { return hd == 64 || hd == 128 || hd == 256; }
+// int8 caches take any head size that is a multiple of 32 up to 256 and
+// store it padded to page_hd(hd) columns; the FP8, q4_0 and QUEST kernels
+// take 64, 128 or 256 only.
+bool valid_hd(int hd) { return hd >= 32 && hd <= 256 && hd % 32 == 0; }
+bool full_hd(int hd) { return hd == 64 || hd == 128 || hd == 256; }
+int page_hd(int hd) { return hd <= 64 ? 64 : hd <= 128 ? 128 : 256; }
 bool valid_kv_bs(int bs) { return bs == 16 || bs == 32 || bs == 64 || bs == 128 || bs == 256; }
 
-int check_cache_shape(int num_blocks, int n_kv, int hd, int kv_bs) {
+int check_cache_shape(int num_blocks, int n_kv, int hd, int kv_bs, bool full = false) {
     if (num_blocks <= 0 || n_kv <= 0) return fail(Q8KV_EINVAL, "num_blocks (%d) and n_kv_heads (%d) must be positive", num_blocks, n_kv);
-    if (!valid_hd(hd)) return fail(Q8KV_EINVAL, "hd must be 64, 128 or 256 (got %d)", hd);
+    if (full && !full_hd(hd)) return fail(Q8KV_EINVAL, "hd must be 64, 128 or 256 (got %d)", hd);
+    if (!valid_hd(hd)) return fail(Q8KV_EINVAL, "hd must be a multiple of 32 from 32 to 256 (got %d)", hd);
     if (!valid_kv_bs(kv_bs)) return fail(Q8KV_EINVAL, "kv_bs must be 16, 32, 64, 128 or 256 (got %d)", kv_bs);
     const long long rows = (long long)num_blocks * n_kv * kv_bs;
     if (rows > INT_MAX) return fail(Q8KV_EINVAL, "page pool of %lld rows exceeds 2^31-1", rows);
@@ -3078,8 +3107,9 @@ int decode_impl(float* out, const float* q, const int8_t* kp, const int8_t* vp, 
     if (knew && head_tables) return fail(Q8KV_EINVAL, "the fused append takes a per-sequence block table");
     if (batch <= 0 || n_q <= 0) return fail(Q8KV_EINVAL, "batch (%d) and n_q_heads (%d) must be positive", batch, n_q);
     if (batch > kMaxBatch) return fail(Q8KV_EINVAL, "batch (%d) exceeds %d sequences per call", batch, kMaxBatch);
-    int rc = check_cache_shape(num_blocks, n_kv, hd, kv_bs);
+    int rc = check_cache_shape(num_blocks, n_kv, hd, kv_bs, fp8 || q40);
     if (rc) return rc;
+    const int hp = page_hd(hd);  // page width: every kernel template is instantiated for it
     if (n_q % n_kv) return fail(Q8KV_EINVAL, "n_q_heads (%d) is not a multiple of n_kv_heads (%d)", n_q, n_kv);
     int G, hgs;
     head_groups(n_q / n_kv, &G, &hgs);
@@ -3102,11 +3132,11 @@ int decode_impl(float* out, const float* q, const int8_t* kp, const int8_t* vp, 
     if ((long long)batch * n_q > INT_MAX || items > INT_MAX) return fail(Q8KV_EINVAL, "decode shape too large");
     const size_t groups = (size_t)batch * n_hk;
     const size_t n_state = np > 1 ? groups * (size_t)np * G : 0;
-    const size_t acc_bytes = align256(n_state * hd * sizeof(float));
+    const size_t acc_bytes = align256(n_state * hp * sizeof(float));
     const size_t arrive_off = 256, state_off = arrive_off + align256(groups * sizeof(int));
     if (no_alloc && state_off + acc_bytes + n_state * 2 * sizeof(float) > kScratchBytes)
         return fail(Q8KV_EINVAL, "this shape needs %zu bytes of scratch (%zu states of %d floats), above the %zu-byte maximum",
-                    state_off + acc_bytes + n_state * 2 * sizeof(float), n_state, hd + 2, kScratchBytes);
+                    state_off + acc_bytes + n_state * 2 * sizeof(float), n_state, hp + 2, kScratchBytes);
 
     hipStream_t st = static_cast<hipStream_t>(stream);
     int dev = 0;
@@ -3119,11 +3149,11 @@ int decode_impl(float* out, const float* q, const int8_t* kp, const int8_t* vp, 
     }
     LaunchInfo li;
     const int var = q40 ? kVarQ40 : fp8 ? kVarFp8 : knew ? kVarQ8New : kVarQ8;
-    rc = launch_info(dev, hd, var, &li);
+    rc = launch_info(dev, hp, var, &li);
     if (rc) return rc;
     const unsigned grid = (unsigned)std::min<long long>(items, li.resident);
     DecodeArgs da{out, q, kp, vp, ks, vs, table, lens, nullptr, nullptr, nullptr, nullptr, batch, max_blocks, num_blocks, n_q, n_kv, kv_bs, G, pt, np, hgs, n_hk, scale * kLog2e,
-                  knew, vnew, new_dtype, ks8, vs8, head_tables ? n_kv : 1};
+                  knew, vnew, new_dtype, ks8, vs8, head_tables ? n_kv : 1, hd};
     if (items > (long long)grid && no_alloc) {
         da.ticket = reinterpret_cast<int*>(sp);
     } else if (items > (long long)grid) {
@@ -3147,13 +3177,13 @@ int decode_impl(float* out, const float* q, const int8_t* kp, const int8_t* vp, 
     // variant (test export q8kv_debug_set_stage) holds a tile ring that
     // leaves room for two workgroups per CU; larger grids then run the
     // persistent kernel (one item per workgroup, no ticket).
-    const bool stage_ok = g_stage.load() != 0 && (var == kVarQ8 || var == kVarQ8New) && hd <= 128;
+    const bool stage_ok = g_stage.load() != 0 && (var == kVarQ8 || var == kVarQ8New) && hp <= 128;
     const int mode = items > (long long)grid || (stage_ok && grid > 2u * (unsigned)li.cus) ? kPersistent : kStatic;
     const bool stage = stage_ok && mode == kStatic;
-    const bool wide = mode == kStatic && wide_hd(hd) && grid <= (unsigned)li.cus && g_wide.load() != 0;
+    const bool wide = mode == kStatic && wide_hd(hp) && grid <= (unsigned)li.cus && g_wide.load() != 0;
     const int nt = wide ? kWave * kWideWaves : kThreads;
     // small groups of partition states are merged inside the decode kernel
-    const int slices = G * hd / 4;
+    const int slices = G * hp / 4;
     const int rows_par = slices >= nt ? 1 : nt / slices;
     const bool fuse = np > 1 && np * G <= kFuseRows && (np + rows_par - 1) / rows_par <= kFusePer;
     if (np > 1 && no_alloc) {
@@ -3213,16 +3243,16 @@ int decode_impl(float* out, const float* q, const int8_t* kp, const int8_t* vp, 
     }
     const size_t lds = wide ? (size_t)li.wide_lds
                        : mode == kStatic && grid <= 2u * (unsigned)li.cus ? (size_t)li.static_lds : 0;
-    launch_decode(hd, var, mode, wide, stage, grid, lds, st, da);
+    launch_decode(hp, var, mode, wide, stage, grid, lds, st, da);
     e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
     if (np > 1 && !fuse) {
-        CombineArgs ca{out, da.st_acc, da.st_ms, lens, n_q, n_hk, G, max_tokens, pt, np};
-        const unsigned bq = (unsigned)(batch * n_q);
-        switch (hd) {
-            case 64: hipLaunchKernelGGL(q8kv_combine_kernel<64>, dim3(bq * kCombineSplit<64>), dim3(kThreads), 0, st, ca); break;
-            case 128: hipLaunchKernelGGL(q8kv_combine_kernel<128>, dim3(bq * kCombineSplit<128>), dim3(kThreads), 0, st, ca); break;
-            default: hipLaunchKernelGGL(q8kv_combine_kernel<256>, dim3(bq * kCombineSplit<256>), dim3(kThreads), 0, st, ca); break;
+        CombineArgs ca{out, da.st_acc, da.st_ms, lens, n_q, n_hk, G, max_tokens, pt, np, hd};
+        const dim3 cgrid((unsigned)(batch * n_q) * (unsigned)(hd / (4 * kCombineCols)));
+        switch (hp) {
+            case 64: hipLaunchKernelGGL(q8kv_combine_kernel<64>, cgrid, dim3(kThreads), 0, st, ca); break;
+            case 128: hipLaunchKernelGGL(q8kv_combine_kernel<128>, cgrid, dim3(kThreads), 0, st, ca); break;
+            default: hipLaunchKernelGGL(q8kv_combine_kernel<256>, cgrid, dim3(kThreads), 0, st, ca); break;
         }
         e = hipGetLastError();
         if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
@@ -3309,9 +3339,9 @@ int q8kv_append(int8_t* k_pages, int8_t* v_pages, float* k_scale, float* v_scale
     const long long grid = (rows + 3) / 4;
     if (grid > INT_MAX) return fail(Q8KV_EINVAL, "too many rows (%lld)", rows);
     AppendArgs aa{k_pages, v_pages, k_scale, v_scale, k_src, v_src, slot_mapping, n_tokens,
-                  n_kv_heads, kv_bs, src_dtype, (long long)num_blocks * kv_bs};
+                  n_kv_heads, kv_bs, src_dtype, (long long)num_blocks * kv_bs, hd};
     hipStream_t st = static_cast<hipStream_t>(stream);
-    switch (hd) {
+    switch (page_hd(hd)) {
         case 64: hipLaunchKernelGGL(q8kv_append_kernel<64>, dim3((unsigned)grid), dim3(256), 0, st, aa); break;
         case 128: hipLaunchKernelGGL(q8kv_append_kernel<128>, dim3((unsigned)grid), dim3(256), 0, st, aa); break;
         default: hipLaunchKernelGGL(q8kv_append_kernel<256>, dim3((unsigned)grid), dim3(256), 0, st, aa); break;
@@ -3334,23 +3364,24 @@ int q8kv_import_pages(int8_t* k_pages, int8_t* v_pages, float* k_scale, float* v
         return fail(Q8KV_ENULL, "a tensor pointer is NULL");
     int rc = check_cache_shape(num_blocks, n_kv_heads, hd, kv_bs);
     if (rc) return rc;
+    const int hp = page_hd(hd);
     const size_t rows = (size_t)num_blocks * n_kv_heads * kv_bs;
-    const size_t pb = rows * hd, sb = rows * sizeof(float);
+    const size_t pb = rows * hp, rb = rows * hd, sb = rows * sizeof(float);
     const void* dst[4] = {k_pages, v_pages, k_scale, v_scale};
     const void* src[4] = {k_rows, v_rows, k_row_scale, v_row_scale};
-    const size_t len[4] = {pb, pb, sb, sb};
+    const size_t dlen[4] = {pb, pb, sb, sb}, slen[4] = {rb, rb, sb, sb};
     for (int i = 0; i < 4; ++i) {
         if (((uintptr_t)dst[i] | (uintptr_t)src[i]) % 16)
             return fail(Q8KV_EINVAL, "pages and scales must be 16-byte aligned");
         for (int j = 0; j < 4; ++j)
-            if (ranges_overlap(dst[i], len[i], src[j], len[j]))
+            if (ranges_overlap(dst[i], dlen[i], src[j], slen[j]))
                 return fail(Q8KV_EINVAL, "the destination cache overlaps the source rows");
     }
     ImportArgs ia{k_pages, v_pages, k_scale, v_scale, k_rows, v_rows, k_row_scale, v_row_scale,
-                  pb / 16, n_kv_heads, kv_bs};
+                  pb / 16, n_kv_heads, kv_bs, hd};
     const unsigned grid = (unsigned)std::min<size_t>((ia.n_pieces + 255) / 256, 16384);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    switch (hd) {
+    switch (hp) {
         case 64: hipLaunchKernelGGL(q8kv_import_kernel<64>, dim3(grid, 2), dim3(256), 0, st, ia); break;
         case 128: hipLaunchKernelGGL(q8kv_import_kernel<128>, dim3(grid, 2), dim3(256), 0, st, ia); break;
         default: hipLaunchKernelGGL(q8kv_import_kernel<256>, dim3(grid, 2), dim3(256), 0, st, ia); break;
@@ -3367,7 +3398,7 @@ int q8kv_fp8_append(uint8_t* k_pages, uint8_t* v_pages, uint8_t* k_scale, uint8_
     if (!k_pages || !v_pages || !k_scale || !v_scale || !k_src || !v_src || !slot_mapping)
         return fail(Q8KV_ENULL, "a tensor pointer is NULL");
     if (n_tokens < 0) return fail(Q8KV_EINVAL, "n_tokens must be >= 0 (got %d)", n_tokens);
-    int rc = check_cache_shape(num_blocks, n_kv_heads, hd, kv_bs);
+    int rc = check_cache_shape(num_blocks, n_kv_heads, hd, kv_bs, true);
     if (rc) return rc;
     if (src_dtype != 0 && src_dtype != 1) return fail(Q8KV_EINVAL, "src_dtype must be 0 (fp32) or 1 (bf16)");
     if (n_tokens == 0) return Q8KV_OK;
@@ -3406,7 +3437,7 @@ int q8kv_q40_append(uint8_t* k_pages, uint8_t* v_pages, uint16_t* k_scale, uint1
     if (!k_pages || !v_pages || !k_scale || !v_scale || !k_src || !v_src || !slot_mapping)
         return fail(Q8KV_ENULL, "a tensor pointer is NULL");
     if (n_tokens < 0) return fail(Q8KV_EINVAL, "n_tokens must be >= 0 (got %d)", n_tokens);
-    int rc = check_cache_shape(num_blocks, n_kv_heads, hd, kv_bs);
+    int rc = check_cache_shape(num_blocks, n_kv_heads, hd, kv_bs, true);
     if (rc) return rc;
     if (src_dtype != 0 && src_dtype != 1) return fail(Q8KV_EINVAL, "src_dtype must be 0 (fp32) or 1 (bf16)");
     if (n_tokens == 0) return Q8KV_OK;
@@ -3458,7 +3489,7 @@ int q8kv_quest_metadata(float* kmax, float* kmin, const int8_t* k_pages, const f
     if (!kmax || !kmin || !k_pages || !k_scale || !block_table || !seq_lens)
         return fail(Q8KV_ENULL, "a tensor pointer is NULL");
     if (batch <= 0) return fail(Q8KV_EINVAL, "batch must be positive (got %d)", batch);
-    int rc = check_cache_shape(num_blocks, n_kv_heads, hd, kv_bs);
+    int rc = check_cache_shape(num_blocks, n_kv_heads, hd, kv_bs, true);
     if (rc) return rc;
     if (max_blocks_per_seq <= 0 || (long long)max_blocks_per_seq * kv_bs > (INT_MAX / 2))
         return fail(Q8KV_EINVAL, "bad max_blocks_per_seq (%d)", max_blocks_per_seq);
@@ -3486,7 +3517,7 @@ int q8kv_quest_select(int32_t* sel_table, int32_t* sel_lens, const float* q, con
     if (!sel_table || !sel_lens || !q || !kmax || !kmin || !block_table || !seq_lens)
         return fail(Q8KV_ENULL, "a tensor pointer is NULL");
     if (batch <= 0 || n_q_heads <= 0) return fail(Q8KV_EINVAL, "batch and n_q_heads must be positive");
-    int rc = check_cache_shape(num_blocks, n_kv_heads, hd, kv_bs);
+    int rc = check_cache_shape(num_blocks, n_kv_heads, hd, kv_bs, true);
     if (rc) return rc;
     if (n_q_heads % n_kv_heads) return fail(Q8KV_EINVAL, "n_q_heads (%d) is not a multiple of n_kv_heads (%d)", n_q_heads, n_kv_heads);
     if (max_blocks_per_seq <= 0 || (long long)max_blocks_per_seq * kv_bs > (INT_MAX / 2))
@@ -3567,7 +3598,7 @@ int q8kv_release(void) {
 int q8kv_debug_quantize_q(int8_t* qi, float* qsc, const float* q, int rows, int hd, void* stream) {
     g_err.clear();
     if (!qi || !qsc || !q) return fail(Q8KV_ENULL, "a tensor pointer is NULL");
-    if (rows < 0 || !valid_hd(hd)) return fail(Q8KV_EINVAL, "bad rows (%d) or hd (%d)", rows, hd);
+    if (rows < 0 || !full_hd(hd)) return fail(Q8KV_EINVAL, "bad rows (%d) or hd (%d)", rows, hd);
     if (rows == 0) return Q8KV_OK;
     const unsigned grid = (unsigned)((rows + kHeadGroup - 1) / kHeadGroup);
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -3587,7 +3618,7 @@ int q8kv_debug_block_dots(int32_t* dots, int max_tok, const float* q, const int8
                           void* stream) {
     g_err.clear();
     if (!dots || !q || !k_pages || !block_table || !seq_lens) return fail(Q8KV_ENULL, "a tensor pointer is NULL");
-    int rc = check_cache_shape(num_blocks, n_kv_heads, hd, kv_bs);
+    int rc = check_cache_shape(num_blocks, n_kv_heads, hd, kv_bs, true);
     if (rc) return rc;
     if (batch <= 0 || n_q_heads <= 0 || n_q_heads % n_kv_heads || n_q_heads / n_kv_heads > kHeadGroup ||
         max_tok < 0 || max_blocks_per_seq <= 0 || (long long)max_blocks_per_seq * kv_bs > (INT_MAX / 2))

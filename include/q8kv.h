@@ -22,9 +22,9 @@
  * packed, naturally aligned -- 16 bytes for pages and scales):
  *   q, out        fp32  [batch][n_q_heads][hd] row-major
  *   k_pages,
- *   v_pages       int8  [num_blocks][n_kv_heads][kv_bs / 16][16 * hd]: each
+ *   v_pages       int8  [num_blocks][n_kv_heads][kv_bs / 16][16 * hp]: each
  *                       page (block, kv head) is a run of 16-row sub-tiles,
- *                       and a sub-tile's 16 x hd bytes are stored in the
+ *                       and a sub-tile's 16 x hp bytes are stored in the
  *                       matrix-core operand order below, so that one 16-byte
  *                       load per lane of a 64-lane wave reads 1 KB of
  *                       consecutive bytes;
@@ -40,11 +40,18 @@
  * Token t of sequence b lives in physical block block_table[b][t / kv_bs] at
  * row t % kv_bs.  Query head h reads kv head h / (n_q_heads / n_kv_heads).
  *
- * Sub-tile byte order.  A sub-tile is hd / 64 chunks of 1024 bytes; byte
+ * Page width.  hp, the bytes of one page row, is the head size hd rounded
+ * up to 64, 128 or 256 (hd 32 -> 64, 96 -> 128, 160 / 192 / 224 -> 256):
+ * the matrix-core steps contract 64 bytes at a time.  Columns hd .. hp - 1
+ * of every written row hold zero codes, which add nothing to a dot product
+ * and leave each row's absmax unchanged; q8kv_append and q8kv_import_pages
+ * write them.  q and out rows stay hd floats long.
+ *
+ * Sub-tile byte order.  A sub-tile is hp / 64 chunks of 1024 bytes; byte
  * 16 * l + i of chunk c belongs to lane slot l = 16 * r + n (r in 0..3, n in
- * 0..15) and is, for row t (0..15) and column x (0..hd-1) of the sub-tile:
+ * 0..15) and is, for row t (0..15) and column x (0..hp-1) of the sub-tile:
  *   K: t = n, x = 64 * c + 16 * r + i;
- *   V: with BPL = hd / 16, slot l holds rows 4r..4r+3, columns
+ *   V: with BPL = hp / 16, slot l holds rows 4r..4r+3, columns
  *      BPL*n .. BPL*n + BPL - 1, as 4 * BPL bytes in (row, column) order;
  *      byte j * BPL + e of that run (row 4r + j, column BPL*n + e) is byte
  *      i of chunk c where c * 16 + i = j * BPL + e.
@@ -85,7 +92,8 @@ enum {
  * q            [batch][n_q_heads][hd] fp32 query (already rotated).
  * max_blocks_per_seq  row stride of block_table; bounds every sequence.
  * num_blocks   physical blocks in the page pool (bounds table entries).
- * hd           64, 128 or 256.
+ * hd           head size: a multiple of 32 from 32 to 256 (pages are hp
+ *              wide, see "Page width").
  * kv_bs        tokens per page: 16, 32, 64, 128 or 256.
  * n_q_heads / n_kv_heads must be a positive integer G.  The query heads of
  *              a kv head are taken in head groups of g heads, g the largest
@@ -150,7 +158,7 @@ int q8kv_decode_attn_split(float* out, const float* q,
  * group of at most 8 query heads of one kv head) rounded up to a multiple of
  * 256, plus, when contexts are split into n_parts > 1 partitions (the
  * q8kv_plan count, or the one part_tokens gives), S = batch * n_q_heads *
- * n_parts states of 4 * hd bytes (all S rounded up to a multiple of 256) and
+ * n_parts states of 4 * hp bytes (all S rounded up to a multiple of 256) and
  * 8 bytes each.  A shape that needs more than 32 MiB is rejected with
  * Q8KV_EINVAL before any HIP call; q8kv_last_error() gives the bytes needed.
  * (Every one of the five benchmark workloads fits: the largest, 64
@@ -225,7 +233,7 @@ int q8kv_append(int8_t* k_pages, int8_t* v_pages, float* k_scale, float* v_scale
  * on the page "Day 9-2: flash_attn_single_q_q8_neon" (trdm.cn), section 2
  * (the function signature and the per-token K row pointer): a block holds
  * kv_bs token rows, each row the hd bytes of every kv head in turn (row
- * stride n_kv_heads * hd), and the per-row scales sit beside them, one fp32
+ * stride n_kv_heads * hd; no padding), and the per-row scales sit beside them, one fp32
  * per (row, kv head).  (The page indexes its scales by sequence position;
  * here they are laid out per block, which is the same array when each
  * sequence owns consecutive blocks.)
@@ -233,7 +241,8 @@ int q8kv_append(int8_t* k_pages, int8_t* v_pages, float* k_scale, float* v_scale
  * k_rows, v_rows           int8 [num_blocks][kv_bs][n_kv_heads][hd]
  * k_row_scale, v_row_scale fp32 [num_blocks][kv_bs][n_kv_heads]
  * k_pages, v_pages, k_scale, v_scale  the destination cache, as for
- *              q8kv_append; every byte and scale of it is written.
+ *              q8kv_append; every byte and scale of it is written (the
+ *              pad columns of a head size below hp with zeros).
  * All eight buffers are caller-owned device memory, 16-byte aligned; the
  * destination must not overlap the source (Q8KV_EINVAL otherwise, checked
  * on the host from the pointers and sizes).  Shape limits as for
@@ -268,7 +277,8 @@ int q8kv_import_pages(int8_t* k_pages, int8_t* v_pages, float* k_scale, float* v
  *             order, dword s lying in chunk s / 4 at bytes 4 (s % 4) ..;
  *   k_scale,
  *   v_scale   uint8 [num_blocks][n_kv_heads][kv_bs][hd / 64] UE8M0 bytes.
- * Other arguments, errors and behaviour as for q8kv_append and
+ * hd is 64, 128 or 256 (no padded widths: Q8KV_EINVAL otherwise).  Other
+ * arguments, errors and behaviour as for q8kv_append and
  * q8kv_decode_attn_split.
  */
 int q8kv_fp8_append(uint8_t* k_pages, uint8_t* v_pages, uint8_t* k_scale, uint8_t* v_scale,
@@ -317,8 +327,9 @@ int q8kv_fp8_decode_attn(float* out, const float* q, const uint8_t* k_pages,
  * (codes qi, scales qsc); a token's score is scale * sum over blocks b of
  * qsc[b] * d_K[b] * sum_{i in b} qi[i] * (c_K[i] - 8), and the output is the
  * softmax-weighted sum of the dequantised V rows, one pass as in
- * q8kv_decode_attn_split.  Other arguments, errors and behaviour as for
- * q8kv_append and q8kv_decode_attn_split.
+ * q8kv_decode_attn_split.  hd is 64, 128 or 256 (Q8KV_EINVAL otherwise).
+ * Other arguments, errors and behaviour as for q8kv_append and
+ * q8kv_decode_attn_split.
  */
 int q8kv_q40_append(uint8_t* k_pages, uint8_t* v_pages, uint16_t* k_scale, uint16_t* v_scale,
                     const void* k_src, const void* v_src, int src_dtype,
@@ -343,8 +354,9 @@ int q8kv_q40_decode_attn(float* out, const float* q, const uint8_t* k_pages,
  *             rows r < min(kv_bs, L - j kv_bs) of float(k code) * k_scale
  *             of that row (an fp32 product).  Other blocks, and table entries
  *             outside [0, num_blocks), are left untouched.
- * Other arguments as for q8kv_decode_attn.  A block shared by several
- * sequences must cover the same rows in each.
+ * Other arguments as for q8kv_decode_attn, except that hd is 64, 128 or
+ * 256 (for both QUEST calls).  A block shared by several sequences must
+ * cover the same rows in each.
  */
 int q8kv_quest_metadata(float* kmax, float* kmin, const int8_t* k_pages, const float* k_scale,
                         const int32_t* block_table, const int32_t* seq_lens,

@@ -116,7 +116,8 @@ def q40_codes(pages, which):
 
 
 def natural_pages(pages, which):
-    """Device pages [nb][n_kv][kv_bs][hd] in chunk order -> row-major rows."""
+    """Device pages [nb][n_kv][kv_bs][hp] in chunk order -> row-major rows
+    (hp wide: a padded head's pad columns included)."""
     nb, n_kv, kv_bs, hd = pages.shape
     sub = pages.reshape(nb, n_kv, kv_bs // 16, 16 * hd)
     return sub[..., chunk_offsets(hd, which).reshape(-1)].reshape(nb, n_kv, kv_bs, hd)
@@ -124,7 +125,9 @@ def natural_pages(pages, which):
 
 def assert_cache_equal(host, dev, blocks=None):
     """Bitwise equality of pages (in row order) and scales (NaN == NaN for
-    poisoned rows)."""
+    poisoned rows).  Pages wider than the head size hold zero codes in the
+    pad columns of every written row (a row whose host scale is a number)
+    and the pool's fill in the rest."""
     for f in ("k_pages", "v_pages", "k_scale", "v_scale"):
         a = getattr(host, f)
         b = getattr(dev, f).cpu().numpy()
@@ -132,6 +135,14 @@ def assert_cache_equal(host, dev, blocks=None):
             b = natural_pages(b, f[0])
         if blocks is not None:
             a, b = a[blocks], b[blocks]
+        if f.endswith("pages") and b.shape[-1] > a.shape[-1]:
+            written = ~np.isnan(getattr(host, f[0] + "_scale"))
+            if blocks is not None:
+                written = written[blocks]
+            pad = b[..., a.shape[-1]:]
+            want = np.where(written[..., None], np.int8(0), a[..., :1])
+            assert np.array_equal(pad, np.broadcast_to(want, pad.shape)), f + " pad columns"
+            b = b[..., :a.shape[-1]]
         if a.dtype == np.float32:
             assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), f
         else:

@@ -92,7 +92,7 @@ def append_decode(**kw):
     (dict(out=NUL), q8.Q8KV_ENULL),
     (dict(dt=2), q8.Q8KV_EINVAL),
     (dict(dt=-1), q8.Q8KV_EINVAL),
-    (dict(hd=96), q8.Q8KV_EINVAL),
+    (dict(hd=80), q8.Q8KV_EINVAL),
     (dict(n_q=6, n_kv=4), q8.Q8KV_EINVAL),
     (dict(batch=0), q8.Q8KV_EINVAL),
     (dict(part=48), q8.Q8KV_EINVAL),
@@ -114,7 +114,9 @@ def test_append_decode_rejects_before_any_hip_call(kw, code):
     (dict(n_q=0), q8.Q8KV_EINVAL),
     (dict(n_kv=0), q8.Q8KV_EINVAL),
     (dict(n_q=6, n_kv=4), q8.Q8KV_EINVAL),
-    (dict(hd=96), q8.Q8KV_EINVAL),
+    (dict(hd=80), q8.Q8KV_EINVAL),     # not a multiple of 32
+    (dict(hd=0), q8.Q8KV_EINVAL),
+    (dict(hd=288), q8.Q8KV_EINVAL),
     (dict(hd=512), q8.Q8KV_EINVAL),
     (dict(kv_bs=8), q8.Q8KV_EINVAL),
     (dict(kv_bs=48), q8.Q8KV_EINVAL),
@@ -144,6 +146,8 @@ def test_append_rejects():
     assert ap(dt=2) == q8.Q8KV_EINVAL
     assert ap(n=-1) == q8.Q8KV_EINVAL
     assert ap(hd=100) == q8.Q8KV_EINVAL
+    assert ap(hd=16) == q8.Q8KV_EINVAL
+    assert ap(hd=288) == q8.Q8KV_EINVAL
     assert ap(kv_bs=24) == q8.Q8KV_EINVAL
     assert ap(nb=0) == q8.Q8KV_EINVAL
     assert ap(n=0) == q8.Q8KV_OK  # nothing to do: no launch
@@ -152,6 +156,7 @@ def test_append_rejects():
 def test_debug_exports_reject():
     assert L.q8kv_debug_quantize_q(NUL, FAKE, FAKE, 4, 128, NUL) == q8.Q8KV_ENULL
     assert L.q8kv_debug_quantize_q(FAKE, FAKE, FAKE, 4, 100, NUL) == q8.Q8KV_EINVAL
+    assert L.q8kv_debug_quantize_q(FAKE, FAKE, FAKE, 4, 96, NUL) == q8.Q8KV_EINVAL
     assert L.q8kv_debug_quantize_q(FAKE, FAKE, FAKE, 0, 128, NUL) == q8.Q8KV_OK
     assert L.q8kv_debug_block_dots(FAKE, 4, FAKE, FAKE, FAKE, FAKE, 4, 8, 1, 3, 2, 128, 16, NUL) == q8.Q8KV_EINVAL
     assert L.q8kv_debug_block_dots(NUL, 4, FAKE, FAKE, FAKE, FAKE, 4, 8, 1, 2, 2, 128, 16, NUL) == q8.Q8KV_ENULL
@@ -227,6 +232,7 @@ def test_quest_select_rejects_before_any_hip_call(kw, code):
     (dict(batch=0), q8.Q8KV_EINVAL),
     (dict(max_blocks=0), q8.Q8KV_EINVAL),
     (dict(kv_bs=24), q8.Q8KV_EINVAL),
+    (dict(hd=96), q8.Q8KV_EINVAL),   # the QUEST kernels take 64, 128 or 256
 ])
 def test_quest_metadata_rejects_before_any_hip_call(kw, code):
     a = dict(kmax=FAKE, kmin=FAKE, kp=FAKE, ks=FAKE, bt=FAKE, sl=FAKE, max_blocks=8, num_blocks=16, batch=2,
@@ -261,7 +267,7 @@ def import_pages(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(kp=0), q8.Q8KV_ENULL),
     (dict(vsr=0), q8.Q8KV_ENULL),
-    (dict(hd=96), q8.Q8KV_EINVAL),
+    (dict(hd=80), q8.Q8KV_EINVAL),
     (dict(kv_bs=8), q8.Q8KV_EINVAL),
     (dict(num_blocks=0), q8.Q8KV_EINVAL),
     (dict(n_kv=0), q8.Q8KV_EINVAL),
@@ -287,7 +293,7 @@ def test_noalloc_rejects_shapes_beyond_its_scratch():
 
 @pytest.mark.parametrize("kw,code", [
     (dict(kp=NUL), q8.Q8KV_ENULL),
-    (dict(hd=96), q8.Q8KV_EINVAL),
+    (dict(hd=80), q8.Q8KV_EINVAL),
     (dict(n_q=18, n_kv=4), q8.Q8KV_EINVAL),
     (dict(part=48), q8.Q8KV_EINVAL),
     (dict(scale=float("inf")), q8.Q8KV_EINVAL),
@@ -300,3 +306,30 @@ def test_noalloc_validates_like_split(kw, code):
                                     a["max_blocks"], a["num_blocks"], a["batch"], a["n_q"], a["n_kv"], a["hd"],
                                     a["kv_bs"], a["scale"], a["part"], NUL)
     assert rc == code == decode(**kw)
+
+
+def test_codec_paths_take_full_head_sizes_only():
+    """The int8 cache takes any multiple of 32 up to 256 (padded pages); the
+    FP8 and q4_0 kernels take 64, 128 or 256 and reject the rest on the host."""
+    args = (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 16, 2, 8, 2, 96, 16, 0.088, 0, NUL)
+    assert L.q8kv_q40_decode_attn(*args) == q8.Q8KV_EINVAL and "64, 128 or 256" in q8.last_error()
+    assert L.q8kv_fp8_decode_attn(*args) == q8.Q8KV_EINVAL
+    app = (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, 4, 16, 2, 96, 16, NUL)
+    assert L.q8kv_q40_append(*app) == q8.Q8KV_EINVAL
+    assert L.q8kv_fp8_append(*app) == q8.Q8KV_EINVAL
+    assert L.q8kv_append(*app[:11], 80, 16, NUL) == q8.Q8KV_EINVAL
+    assert "multiple of 32" in q8.last_error()
+
+
+def test_padded_page_width():
+    """int8 pages are the head size rounded up to 64, 128 or 256 wide; a
+    wrapped pool names the head size it holds (host logic only)."""
+    import torch
+    assert [q8.page_hd(h) for h in (32, 64, 96, 128, 160, 192, 224, 256)] == [64, 64, 128, 128, 256, 256, 256, 256]
+    kp = torch.zeros((2, 2, 16, 128), dtype=torch.int8)
+    ks = torch.zeros((2, 2, 16), dtype=torch.float32)
+    c = q8.PagedKVCache.wrap(kp, kp.clone(), ks, ks.clone(), hd=96)
+    assert (c.hd, c.hp) == (96, 128)
+    assert q8.PagedKVCache.wrap(kp, kp.clone(), ks, ks.clone()).hd == 128
+    with pytest.raises(ValueError):
+        q8.PagedKVCache.wrap(kp, kp.clone(), ks, ks.clone(), hd=64)

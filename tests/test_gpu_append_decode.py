@@ -63,7 +63,8 @@ def history(c, src_dtype=torch.float32):
 
 
 def clone(dev):
-    return q8.PagedKVCache.wrap(dev.k_pages.clone(), dev.v_pages.clone(), dev.k_scale.clone(), dev.v_scale.clone())
+    return q8.PagedKVCache.wrap(dev.k_pages.clone(), dev.v_pages.clone(), dev.k_scale.clone(), dev.v_scale.clone(),
+                                hd=dev.hd)
 
 
 def run_case(c, part_tokens=0, src_dtype=torch.float32, reps=1):
@@ -109,7 +110,8 @@ def edge_lens(batch, kv_bs, pt):
 
 @pytest.mark.parametrize("hd,G,kv_bs", [(64, 1, 16), (64, 8, 32), (128, 1, 16), (128, 4, 64),
                                         (128, 8, 16), (256, 2, 32), (256, 8, 128), (128, 5, 256),
-                                        (128, 16, 16), (64, 10, 32)])  # head groups: one of them stores the token
+                                        (128, 16, 16), (64, 10, 32),  # head groups: one of them stores the token
+                                        (96, 8, 16), (160, 4, 32), (32, 2, 64)])  # padded pages
 def test_append_decode_shapes(hd, G, kv_bs):
     batch = 14
     lens = edge_lens(batch, kv_bs, 0)

@@ -33,6 +33,7 @@ def import_rows(nb, n_kv, kv_bs, hd, k_rows, v_rows, ks_rows, vs_rows):
 
 @pytest.mark.parametrize("hd,kv_bs,n_kv,nb", [
     (64, 16, 3, 5), (128, 64, 8, 3), (256, 32, 2, 4), (128, 256, 1, 2), (64, 128, 5, 1), (256, 16, 7, 6),
+    (96, 16, 3, 2), (160, 32, 2, 3), (32, 64, 1, 2), (224, 16, 2, 2),  # padded pages
 ])
 def test_import_is_a_permutation(hd, kv_bs, n_kv, nb):
     rng = np.random.default_rng(hd * 1000 + kv_bs * 10 + n_kv)
@@ -44,8 +45,11 @@ def test_import_is_a_permutation(hd, kv_bs, n_kv, nb):
     ks_rows, vs_rows = bits[0].view(np.float32), bits[1].view(np.float32)
     say(f"import hd={hd} kv_bs={kv_bs} n_kv={n_kv} nb={nb}")
     c = import_rows(nb, n_kv, kv_bs, hd, k_rows, v_rows, ks_rows, vs_rows)
-    assert np.array_equal(natural_pages(c.k_pages.cpu().numpy(), "k"), k_rows.transpose(0, 2, 1, 3))
-    assert np.array_equal(natural_pages(c.v_pages.cpu().numpy(), "v"), v_rows.transpose(0, 2, 1, 3))
+    kn = natural_pages(c.k_pages.cpu().numpy(), "k")
+    vn = natural_pages(c.v_pages.cpu().numpy(), "v")
+    assert np.array_equal(kn[..., :hd], k_rows.transpose(0, 2, 1, 3))
+    assert np.array_equal(vn[..., :hd], v_rows.transpose(0, 2, 1, 3))
+    assert not kn[..., hd:].any() and not vn[..., hd:].any()  # pad columns of a padded head
     assert np.array_equal(c.k_scale.cpu().numpy().view(np.uint32), bits[0].transpose(0, 2, 1))
     assert np.array_equal(c.v_scale.cpu().numpy().view(np.uint32), bits[1].transpose(0, 2, 1))
 

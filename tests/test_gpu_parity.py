@@ -55,6 +55,9 @@ def check_decode(c, cache=None, part_tokens=0, tol=TOL, tol64=TOL64):
 @pytest.mark.parametrize("hd,kv_bs,n_kv,dtype", [
     (128, 16, 2, torch.float32), (128, 64, 8, torch.float32), (64, 16, 1, torch.float32),
     (256, 32, 7, torch.float32), (128, 16, 2, torch.bfloat16), (256, 128, 3, torch.bfloat16),
+    # head sizes stored in padded pages (hd rounded up to 64, 128 or 256)
+    (32, 16, 3, torch.float32), (96, 64, 2, torch.float32), (160, 32, 2, torch.bfloat16),
+    (192, 16, 5, torch.float32), (224, 128, 1, torch.float32),
 ])
 def test_append_bit_exact(hd, kv_bs, n_kv, dtype):
     w = workloads.Workload("app", 3, n_kv, n_kv, hd, kv_bs, 5 * kv_bs + 3, ragged=True,
@@ -203,8 +206,44 @@ def test_decode_hd_kv_bs(hd, kv_bs):
     check_decode(c, dev, part_tokens=64)
 
 
+@pytest.mark.parametrize("hd,kv_bs", [(32, 16), (32, 256), (96, 16), (96, 64), (160, 32), (192, 128),
+                                      (224, 16), (224, 256)])
+def test_decode_padded_head_sizes(hd, kv_bs):
+    """Head sizes that are multiples of 32 but not of 64, 128 or 256 live in
+    pages hd rounded up to 64, 128 or 256 wide whose pad columns hold zero
+    codes: q and out stay hd floats a row, and the results are those of the
+    unpadded oracle."""
+    w = workloads.Workload("padhd", 3, 8, 2, hd, kv_bs, 2 * kv_bs + 37, ragged=True, table="pool",
+                           spare_blocks=2, k_outlier_p=0.05, k_outlier_amp=6.0,
+                           key=1600 + hd + kv_bs)
+    c = build(w)
+    say(f"decode padded hd={hd} kv_bs={kv_bs} lens={c.lens.tolist()}")
+    dev = gpu_cache(c)
+    assert dev.k_pages.shape[-1] == q8.page_hd(hd) > hd
+    check_decode(c, dev)
+    check_decode(c, dev, part_tokens=64)
+
+
+def test_decode_padded_persistent_grid():
+    """A padded head size on the persistent grid with the in-kernel merge
+    and the combine kernel."""
+    rng = np.random.default_rng(1700)
+    lens = rng.integers(1, 1025, size=64)
+    lens[:6] = [0, 1, 31, 32, 33, 1024]
+    w = workloads.Workload("padpersist", 64, 8, 2, 96, 32, 1024, ragged=True, table="pool",
+                           spare_blocks=3, key=1700)
+    c = build(w, lens=[int(x) for x in lens])
+    say(f"persistent grid hd=96 tokens={int(c.lens.sum())}")
+    dev = gpu_cache(c)
+    for pt in (32, 128):
+        got = decode(c, dev, part_tokens=pt)
+        assert not got[0].any()
+        check_decode(c, dev, part_tokens=pt)
+
+
 @pytest.mark.parametrize("hd,G", [(64, 1), (64, 8), (128, 1), (128, 3), (128, 5), (128, 8),
-                                  (256, 2), (256, 5), (256, 8)])
+                                  (256, 2), (256, 5), (256, 8),
+                                  (32, 8), (96, 3), (96, 8), (160, 5), (192, 8), (224, 2)])
 def test_decode_split_merge_paths(hd, G):
     """Partition states of a (sequence, head group) are merged inside the
     decode kernel by the workgroup that stores the last one when there are
@@ -327,6 +366,7 @@ def test_decode_many_partition_states_persistent():
     (256, 10, 1, 0),                     # two groups of 5
     (128, 32, 1, 0),                     # one kv head for 32 query heads: four groups of 8
     (128, 13, 1, 64),                    # a prime group size: thirteen groups of 1
+    (96, 12, 1, 32),                     # a padded head size in groups of 6
 ])
 def test_decode_large_groups(hd, G, n_kv, pt):
     """More query heads per kv head than the matrix cores' 8-head column

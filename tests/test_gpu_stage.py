@@ -52,6 +52,8 @@ CASES = [
     (64, 1, 16, [1, 0, 16, 17, 32, 33, 31, 129, 128, 65, 64], 0, True),
     (64, 8, 128, [1000, 513, 2], 64, False),
     (128, 16, 64, [2000, 77], 0, False),                   # two head groups per kv head
+    (96, 8, 16, [1, 16, 17, 33, 129, 300], 0, True),       # padded pages
+    (32, 4, 32, [700, 1, 0, 257], 32, False),
 ]
 
 

@@ -71,6 +71,9 @@ PAIRS = {
     # hd 64 and 256, then an unsplit call (one partition)
     "hd_mix": ((3, 4, 2, 256, 64, [1500, 700, 64], 64),
                (2, 2, 3, 64, 16, [40, 17], 64)),
+    # padded pages (hd 160 and 96), in-kernel merge then combine kernel
+    "hd_pad": ((3, 8, 2, 160, 32, [900, 300, 33], 64),
+               (2, 4, 2, 96, 16, [3000, 17], 32)),
 }
 
 
