@@ -72,6 +72,8 @@ def parse():
     p.add_argument("--no-q40", action="store_true", help="skip the q4_0-codec leg")
     p.add_argument("--no-quest", action="store_true", help="skip the QUEST metadata / selection leg")
     p.add_argument("--part-tokens", type=int, default=0, help="override the split plan (0: automatic)")
+    p.add_argument("--load-probe", action="store_true",
+                   help="also time the decode kernel's loads alone in three load orders (q8kv_debug_load_probe)")
     p.add_argument("--timeline", action="store_true",
                    help="instead of the benchmark: build a copy of the library whose decode kernel "
                         "stamps each workgroup's start, end of streaming and CU, and report the "
@@ -359,6 +361,40 @@ def time_stream_read(g, steps):
     e1.record(stream)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) * 1e3 / steps, nbytes
+
+
+LOAD_PATTERNS = {0: "page layout (1 KB operand chunks) + scale loads",
+                 1: "page layout, no scale loads",
+                 2: "row-major pages read into the same operands + scale loads"}
+
+
+def time_load_probe(w, g, steps, part_tokens):
+    """The decode kernel's loads without its arithmetic over the same pools
+    (q8kv_debug_load_probe), one item per partition of the plan, for each
+    load pattern: us per launch and the rate of the bytes it loads."""
+    import torch
+    import decode_attention_int8_amd as q8
+    caches = g["caches"]
+    item_pages = max(part_tokens // w.kv_bs, -(-128 // w.kv_bs))
+    num_pages = caches[0].num_blocks * w.n_kv // item_pages * item_pages
+    stream = torch.cuda.current_stream()
+    res = {"item_pages": item_pages, "num_pages": num_pages, "patterns": {}}
+    for pat, what in LOAD_PATTERNS.items():
+        for i in range(3):
+            q8.debug_load_probe(caches[i % len(caches)], item_pages, pat, num_pages)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(steps):
+            q8.debug_load_probe(caches[i % len(caches)], item_pages, pat, num_pages)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        nbytes = num_pages * w.kv_bs * (2 * w.hd + (0 if pat == 1 else 8))
+        res["patterns"][str(pat)] = {"what": what, "us": round(us, 3), "bytes": nbytes,
+                                     "gbs": round(nbytes / (us * 1e-6) / 1e9, 1)}
+        log(f"load probe {pat} ({what}): {us:.2f} us, {nbytes / (us * 1e-6) / 1e9:.0f} GB/s")
+    return res
 
 
 def profiled_traffic(w, key=None):
@@ -705,6 +741,7 @@ def main():
     lens = g["lens"]
     algo = workloads.step_bytes(w, lens)
     head, loop_ms, _ = decode_record(w, g, args)
+    probe = time_load_probe(w, g, args.steps, head["config"]["part_tokens"]) if args.load_probe else None
     rec = {
         "metric": METRIC,
         "value": head["kv_gbs"],
@@ -726,6 +763,8 @@ def main():
         "stream_read_ceiling": head["stream_read_ceiling"],
         "cpu_baseline": None,
     }
+    if probe:
+        rec["load_probe"] = probe
     for name in codecs:
         c_us = time_codec(w, g, name, args.steps, args.warmup, args.part_tokens)
         c_algo = workloads.step_bytes(w, lens, codec=name)

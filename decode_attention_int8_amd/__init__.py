@@ -56,6 +56,7 @@ def _load():
         "q8kv_debug_quantize_q": [P, P, P, I, I, P],
         "q8kv_debug_block_dots": [P, I, P, P, P, P, I, I, I, I, I, I, I, P],
         "q8kv_debug_stream_read": [P, ctypes.c_size_t, P, ctypes.c_size_t, P],
+        "q8kv_debug_load_probe": [P, P, P, P, I, I, I, I, I, P],
         "q8kv_debug_set_wide": [I],
         "q8kv_debug_set_stage": [I],
     }
@@ -197,6 +198,8 @@ class PagedKVCache:
             object.__setattr__(self, "_meta", meta)
         return meta
 
+    _APPEND = "q8kv_append"  # the codec's append entry point
+
     def append(self, k_src, v_src, slot_mapping):
         """Quantise k_src/v_src [n_tokens][n_kv][hd] (fp32 or bf16) into slots."""
         dev, kp, vp, ks, vs = self._pointers()
@@ -214,7 +217,7 @@ class PagedKVCache:
             raise ValueError("k_src/v_src must be [n_tokens][n_kv][hd] matching slot_mapping")
         args = (kp, vp, ks, vs, k_src.data_ptr(), v_src.data_ptr(), 1 if sd is torch.bfloat16 else 0,
                 slot_mapping.data_ptr(), n, self.num_blocks, self.n_kv, self.hd, self.kv_bs)
-        _call(dev, lib.q8kv_append, args)
+        _call(dev, getattr(lib, self._APPEND), args)
 
 
 def import_pages(cache, k_rows, v_rows, k_row_scale, v_row_scale):
@@ -241,6 +244,41 @@ def import_pages(cache, k_rows, v_rows, k_row_scale, v_row_scale):
     return cache
 
 
+def _decode_io(cache, q, table, seq_lens, out, table_ndim=2):
+    """Check q, the block table (table_ndim 2: per sequence; 3: per kv head),
+    seq_lens and out against cache; returns (cache pointers, out)."""
+    meta = cache._pointers()
+    dev = meta[0]
+    if not (_ok(q, torch.float32, dev, 3) and _ok(table, torch.int32, dev, table_ndim)
+            and _ok(seq_lens, torch.int32, dev, 1)):
+        d = cache.device
+        _need(q, "q", torch.float32, d, 3)
+        _need(table, "block_table", torch.int32, d, table_ndim)
+        _need(seq_lens, "seq_lens", torch.int32, d, 1)
+    batch, n_q, hd = q.shape
+    if (hd != cache.hd or table.shape[0] != batch or seq_lens.shape[0] != batch
+            or (table_ndim == 3 and table.shape[1] != cache.n_kv)):
+        raise ValueError("q / block_table / seq_lens / cache shapes disagree")
+    if out is None:
+        out = torch.empty_like(q)
+    elif not (_ok(out, torch.float32, dev, 3) and out.shape == q.shape):
+        _need(out, "out", torch.float32, cache.device, 3)
+        raise ValueError("out must have q's shape")
+    return meta, out
+
+
+def _decode(fn, q, cache, table, seq_lens, scale, out, part_tokens, table_ndim=2):
+    """The decode entry points' common call: (out, q, pages and scales,
+    table, lengths, table row length, shape, scale, part_tokens)."""
+    (dev, kp, vp, ks, vs), out = _decode_io(cache, q, table, seq_lens, out, table_ndim)
+    batch, n_q, hd = q.shape
+    args = (out.data_ptr(), q.data_ptr(), kp, vp, ks, vs, table.data_ptr(), seq_lens.data_ptr(),
+            table.shape[-1], cache.num_blocks, batch, n_q, cache.n_kv, hd, cache.kv_bs, float(scale),
+            int(part_tokens))
+    _call(dev, fn, args)
+    return out
+
+
 def decode_attn(q, cache, block_table, seq_lens, scale, out=None, part_tokens=0):
     """out[b][h] = softmax(q8 scores) @ q8 V for every sequence b and head h.
 
@@ -248,26 +286,7 @@ def decode_attn(q, cache, block_table, seq_lens, scale, out=None, part_tokens=0)
     seq_lens int32 [batch]; all on the cache's device.  part_tokens 0 picks the
     automatic split plan.  Returns out (fp32 [batch][n_q][hd]).
     """
-    dev, kp, vp, ks, vs = cache._pointers()
-    if not (_ok(q, torch.float32, dev, 3) and _ok(block_table, torch.int32, dev, 2)
-            and _ok(seq_lens, torch.int32, dev, 1)):
-        d = cache.device
-        _need(q, "q", torch.float32, d, 3)
-        _need(block_table, "block_table", torch.int32, d, 2)
-        _need(seq_lens, "seq_lens", torch.int32, d, 1)
-    batch, n_q, hd = q.shape
-    if hd != cache.hd or block_table.shape[0] != batch or seq_lens.shape[0] != batch:
-        raise ValueError("q / block_table / seq_lens / cache shapes disagree")
-    if out is None:
-        out = torch.empty_like(q)
-    elif not (_ok(out, torch.float32, dev, 3) and out.shape == q.shape):
-        _need(out, "out", torch.float32, cache.device, 3)
-        raise ValueError("out must have q's shape")
-    args = (out.data_ptr(), q.data_ptr(), kp, vp, ks, vs, block_table.data_ptr(), seq_lens.data_ptr(),
-            block_table.shape[1], cache.num_blocks, batch, n_q, cache.n_kv, hd, cache.kv_bs, float(scale),
-            int(part_tokens))
-    _call(dev, lib.q8kv_decode_attn_split, args)
-    return out
+    return _decode(lib.q8kv_decode_attn_split, q, cache, block_table, seq_lens, scale, out, part_tokens)
 
 
 def decode_attn_noalloc(q, cache, block_table, seq_lens, scale, out, part_tokens=0):
@@ -275,24 +294,9 @@ def decode_attn_noalloc(q, cache, block_table, seq_lens, scale, out, part_tokens
     bit, with no device allocation by the library or this binding (out is
     required).  The library's one scratch array per device is shared by
     every such call: calls that overlap on one device race."""
-    dev, kp, vp, ks, vs = cache._pointers()
-    if not (_ok(q, torch.float32, dev, 3) and _ok(block_table, torch.int32, dev, 2)
-            and _ok(seq_lens, torch.int32, dev, 1) and _ok(out, torch.float32, dev, 3)):
-        d = cache.device
-        _need(q, "q", torch.float32, d, 3)
-        _need(block_table, "block_table", torch.int32, d, 2)
-        _need(seq_lens, "seq_lens", torch.int32, d, 1)
-        _need(out, "out", torch.float32, d, 3)
-    batch, n_q, hd = q.shape
-    if hd != cache.hd or block_table.shape[0] != batch or seq_lens.shape[0] != batch:
-        raise ValueError("q / block_table / seq_lens / cache shapes disagree")
-    if out.shape != q.shape:
-        raise ValueError("out must have q's shape")
-    args = (out.data_ptr(), q.data_ptr(), kp, vp, ks, vs, block_table.data_ptr(), seq_lens.data_ptr(),
-            block_table.shape[1], cache.num_blocks, batch, n_q, cache.n_kv, hd, cache.kv_bs, float(scale),
-            int(part_tokens))
-    _call(dev, lib.q8kv_decode_attn_noalloc, args)
-    return out
+    if out is None:
+        raise ValueError("out is required (the call allocates nothing)")
+    return _decode(lib.q8kv_decode_attn_noalloc, q, cache, block_table, seq_lens, scale, out, part_tokens)
 
 
 def append_decode_attn(q, cache, k_new, v_new, block_table, seq_lens, scale, out=None, part_tokens=0):
@@ -305,29 +309,16 @@ def append_decode_attn(q, cache, k_new, v_new, block_table, seq_lens, scale, out
     Same result, cache bytes and output bits, as cache.append at those slots
     followed by decode_attn.  Returns out (fp32 [batch][n_q][hd]).
     """
-    dev, kp, vp, ks, vs = cache._pointers()
+    (dev, kp, vp, ks, vs), out = _decode_io(cache, q, block_table, seq_lens, out)
     nd = k_new.dtype if isinstance(k_new, torch.Tensor) else None
-    if not (_ok(q, torch.float32, dev, 3) and _ok(block_table, torch.int32, dev, 2)
-            and _ok(seq_lens, torch.int32, dev, 1) and nd in (torch.float32, torch.bfloat16)
-            and _ok(k_new, nd, dev, 3) and _ok(v_new, nd, dev, 3)):
-        d = cache.device
-        _need(q, "q", torch.float32, d, 3)
-        _need(block_table, "block_table", torch.int32, d, 2)
-        _need(seq_lens, "seq_lens", torch.int32, d, 1)
+    if not (nd in (torch.float32, torch.bfloat16) and _ok(k_new, nd, dev, 3) and _ok(v_new, nd, dev, 3)):
         if nd not in (torch.float32, torch.bfloat16):
             raise TypeError("k_new must be a float32 or bfloat16 tensor")
-        _need(k_new, "k_new", nd, d, 3)
-        _need(v_new, "v_new", nd, d, 3)
+        _need(k_new, "k_new", nd, cache.device, 3)
+        _need(v_new, "v_new", nd, cache.device, 3)
     batch, n_q, hd = q.shape
-    if hd != cache.hd or block_table.shape[0] != batch or seq_lens.shape[0] != batch:
-        raise ValueError("q / block_table / seq_lens / cache shapes disagree")
     if tuple(k_new.shape) != (batch, cache.n_kv, hd) or v_new.shape != k_new.shape:
         raise ValueError("k_new / v_new must be [batch][n_kv][hd]")
-    if out is None:
-        out = torch.empty_like(q)
-    elif not (_ok(out, torch.float32, dev, 3) and out.shape == q.shape):
-        _need(out, "out", torch.float32, cache.device, 3)
-        raise ValueError("out must have q's shape")
     args = (out.data_ptr(), q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
             1 if nd is torch.bfloat16 else 0, kp, vp, ks, vs, block_table.data_ptr(),
             seq_lens.data_ptr(), block_table.shape[1], cache.num_blocks, batch, n_q, cache.n_kv, hd,
@@ -343,6 +334,8 @@ class Fp8KVCache(PagedKVCache):
     k_pages, v_pages uint8 [num_blocks][n_kv][kv_bs][hd] (sub-tile byte order);
     k_scale, v_scale uint8 [num_blocks][n_kv][kv_bs][hd/64].
     """
+
+    _APPEND = "q8kv_fp8_append"
 
     def __init__(self, num_blocks, n_kv, kv_bs, hd, device="cuda"):
         dev = torch.device(device)
@@ -374,25 +367,6 @@ class Fp8KVCache(PagedKVCache):
             if tuple(t.shape) != shp[:3] + (self.hd // 64,):
                 raise ValueError(f"{name} shape {tuple(t.shape)} != {shp[:3] + (self.hd // 64,)}")
 
-    def append(self, k_src, v_src, slot_mapping):
-        """Quantise k_src/v_src [n_tokens][n_kv][hd] (fp32 or bf16) into slots."""
-        dev, kp, vp, ks, vs = self._pointers()
-        sd = k_src.dtype if isinstance(k_src, torch.Tensor) else None
-        if not (sd in (torch.float32, torch.bfloat16) and _ok(k_src, sd, dev, 3) and _ok(v_src, sd, dev, 3)
-                and _ok(slot_mapping, torch.int32, dev, 1)):
-            d = self.device
-            if sd not in (torch.float32, torch.bfloat16):
-                raise TypeError("k_src must be a float32 or bfloat16 tensor")
-            _need(k_src, "k_src", sd, d, 3)
-            _need(v_src, "v_src", sd, d, 3)
-            _need(slot_mapping, "slot_mapping", torch.int32, d, 1)
-        n = slot_mapping.shape[0]
-        if tuple(k_src.shape) != (n, self.n_kv, self.hd) or v_src.shape != k_src.shape:
-            raise ValueError("k_src/v_src must be [n_tokens][n_kv][hd] matching slot_mapping")
-        args = (kp, vp, ks, vs, k_src.data_ptr(), v_src.data_ptr(), 1 if sd is torch.bfloat16 else 0,
-                slot_mapping.data_ptr(), n, self.num_blocks, self.n_kv, self.hd, self.kv_bs)
-        _call(dev, lib.q8kv_fp8_append, args)
-
 
 class Q40KVCache(PagedKVCache):
     """Device page pool of one layer's q4_0 KV cache (4-bit codes, one fp16
@@ -401,6 +375,8 @@ class Q40KVCache(PagedKVCache):
     k_pages, v_pages uint8 [num_blocks][n_kv][kv_bs][hd/2] (sub-tile nibble order);
     k_scale, v_scale float16 [num_blocks][n_kv][kv_bs][hd/32].
     """
+
+    _APPEND = "q8kv_q40_append"
 
     def __init__(self, num_blocks, n_kv, kv_bs, hd, device="cuda"):
         dev = torch.device(device)
@@ -433,50 +409,12 @@ class Q40KVCache(PagedKVCache):
             if tuple(t.shape) != shp + (self.hd // 32,):
                 raise ValueError(f"{name} shape {tuple(t.shape)} != {shp + (self.hd // 32,)}")
 
-    def append(self, k_src, v_src, slot_mapping):
-        """Quantise k_src/v_src [n_tokens][n_kv][hd] (fp32 or bf16) into slots."""
-        dev, kp, vp, ks, vs = self._pointers()
-        sd = k_src.dtype if isinstance(k_src, torch.Tensor) else None
-        if not (sd in (torch.float32, torch.bfloat16) and _ok(k_src, sd, dev, 3) and _ok(v_src, sd, dev, 3)
-                and _ok(slot_mapping, torch.int32, dev, 1)):
-            d = self.device
-            if sd not in (torch.float32, torch.bfloat16):
-                raise TypeError("k_src must be a float32 or bfloat16 tensor")
-            _need(k_src, "k_src", sd, d, 3)
-            _need(v_src, "v_src", sd, d, 3)
-            _need(slot_mapping, "slot_mapping", torch.int32, d, 1)
-        n = slot_mapping.shape[0]
-        if tuple(k_src.shape) != (n, self.n_kv, self.hd) or v_src.shape != k_src.shape:
-            raise ValueError("k_src/v_src must be [n_tokens][n_kv][hd] matching slot_mapping")
-        args = (kp, vp, ks, vs, k_src.data_ptr(), v_src.data_ptr(), 1 if sd is torch.bfloat16 else 0,
-                slot_mapping.data_ptr(), n, self.num_blocks, self.n_kv, self.hd, self.kv_bs)
-        _call(dev, lib.q8kv_q40_append, args)
-
 
 def q40_decode_attn(q, cache, block_table, seq_lens, scale, out=None, part_tokens=0):
     """decode_attn over a Q40KVCache.  Returns out (fp32 [batch][n_q][hd])."""
     if not isinstance(cache, Q40KVCache):
         raise TypeError("cache must be a Q40KVCache")
-    dev, kp, vp, ks, vs = cache._pointers()
-    if not (_ok(q, torch.float32, dev, 3) and _ok(block_table, torch.int32, dev, 2)
-            and _ok(seq_lens, torch.int32, dev, 1)):
-        d = cache.device
-        _need(q, "q", torch.float32, d, 3)
-        _need(block_table, "block_table", torch.int32, d, 2)
-        _need(seq_lens, "seq_lens", torch.int32, d, 1)
-    batch, n_q, hd = q.shape
-    if hd != cache.hd or block_table.shape[0] != batch or seq_lens.shape[0] != batch:
-        raise ValueError("q / block_table / seq_lens / cache shapes disagree")
-    if out is None:
-        out = torch.empty_like(q)
-    elif not (_ok(out, torch.float32, dev, 3) and out.shape == q.shape):
-        _need(out, "out", torch.float32, cache.device, 3)
-        raise ValueError("out must have q's shape")
-    args = (out.data_ptr(), q.data_ptr(), kp, vp, ks, vs, block_table.data_ptr(), seq_lens.data_ptr(),
-            block_table.shape[1], cache.num_blocks, batch, n_q, cache.n_kv, hd, cache.kv_bs, float(scale),
-            int(part_tokens))
-    _call(dev, lib.q8kv_q40_decode_attn, args)
-    return out
+    return _decode(lib.q8kv_q40_decode_attn, q, cache, block_table, seq_lens, scale, out, part_tokens)
 
 
 def fp8_decode_attn(q, cache, block_table, seq_lens, scale, out=None, part_tokens=0):
@@ -484,26 +422,7 @@ def fp8_decode_attn(q, cache, block_table, seq_lens, scale, out=None, part_token
     the dequantised E4M3 K and V.  Returns out (fp32 [batch][n_q][hd])."""
     if not isinstance(cache, Fp8KVCache):
         raise TypeError("cache must be an Fp8KVCache")
-    dev, kp, vp, ks, vs = cache._pointers()
-    if not (_ok(q, torch.float32, dev, 3) and _ok(block_table, torch.int32, dev, 2)
-            and _ok(seq_lens, torch.int32, dev, 1)):
-        d = cache.device
-        _need(q, "q", torch.float32, d, 3)
-        _need(block_table, "block_table", torch.int32, d, 2)
-        _need(seq_lens, "seq_lens", torch.int32, d, 1)
-    batch, n_q, hd = q.shape
-    if hd != cache.hd or block_table.shape[0] != batch or seq_lens.shape[0] != batch:
-        raise ValueError("q / block_table / seq_lens / cache shapes disagree")
-    if out is None:
-        out = torch.empty_like(q)
-    elif not (_ok(out, torch.float32, dev, 3) and out.shape == q.shape):
-        _need(out, "out", torch.float32, cache.device, 3)
-        raise ValueError("out must have q's shape")
-    args = (out.data_ptr(), q.data_ptr(), kp, vp, ks, vs, block_table.data_ptr(), seq_lens.data_ptr(),
-            block_table.shape[1], cache.num_blocks, batch, n_q, cache.n_kv, hd, cache.kv_bs, float(scale),
-            int(part_tokens))
-    _call(dev, lib.q8kv_fp8_decode_attn, args)
-    return out
+    return _decode(lib.q8kv_fp8_decode_attn, q, cache, block_table, seq_lens, scale, out, part_tokens)
 
 
 def quest_metadata(cache, block_table, seq_lens, kmax=None, kmin=None):
@@ -569,27 +488,7 @@ def decode_attn_heads(q, cache, head_table, seq_lens, scale, out=None, part_toke
     """decode_attn with one block list per kv head: head_table int32
     [batch][n_kv][max_blocks] (e.g. quest_select's sel_table), seq_lens int32
     [batch].  Returns out (fp32 [batch][n_q][hd])."""
-    dev, kp, vp, ks, vs = cache._pointers()
-    if not (_ok(q, torch.float32, dev, 3) and _ok(head_table, torch.int32, dev, 3)
-            and _ok(seq_lens, torch.int32, dev, 1)):
-        d = cache.device
-        _need(q, "q", torch.float32, d, 3)
-        _need(head_table, "head_table", torch.int32, d, 3)
-        _need(seq_lens, "seq_lens", torch.int32, d, 1)
-    batch, n_q, hd = q.shape
-    if (hd != cache.hd or head_table.shape[0] != batch or head_table.shape[1] != cache.n_kv
-            or seq_lens.shape[0] != batch):
-        raise ValueError("q / head_table / seq_lens / cache shapes disagree")
-    if out is None:
-        out = torch.empty_like(q)
-    elif not (_ok(out, torch.float32, dev, 3) and out.shape == q.shape):
-        _need(out, "out", torch.float32, cache.device, 3)
-        raise ValueError("out must have q's shape")
-    args = (out.data_ptr(), q.data_ptr(), kp, vp, ks, vs, head_table.data_ptr(), seq_lens.data_ptr(),
-            head_table.shape[2], cache.num_blocks, batch, n_q, cache.n_kv, hd, cache.kv_bs, float(scale),
-            int(part_tokens))
-    _call(dev, lib.q8kv_decode_attn_heads, args)
-    return out
+    return _decode(lib.q8kv_decode_attn_heads, q, cache, head_table, seq_lens, scale, out, part_tokens, 3)
 
 
 def plan(batch, n_q, n_kv, hd, kv_bs, max_blocks):
@@ -610,6 +509,15 @@ def debug_stream_read(a, b):
     with torch.cuda.device(a.device):
         _check(lib.q8kv_debug_stream_read(a.data_ptr(), nb(a), b.data_ptr(), nb(b),
                                           torch.cuda.current_stream(a.device).cuda_stream))
+
+
+def debug_load_probe(cache, item_pages, pattern, num_pages=None):
+    """Issue the decode kernel's loads over cache's pools without its
+    arithmetic (q8kv_debug_load_probe; pattern 0, 1 or 2)."""
+    dev, kp, vp, ks, vs = cache._pointers()
+    if num_pages is None:
+        num_pages = cache.num_blocks * cache.n_kv // item_pages * item_pages
+    _call(dev, lib.q8kv_debug_load_probe, (kp, vp, ks, vs, num_pages, cache.hp, cache.kv_bs, item_pages, pattern))
 
 
 def release():

@@ -670,25 +670,53 @@ __device__ __forceinline__ void tile_blocks(const int32_t* trow, int ts, int kv_
     blk[1] = uniform_read(trow, min((ts + kSub) >> sh, max_blocks - 1));
 }
 
-template <int HD>
+// PART 0 loads the whole tile.  PART 1 loads its K chunks and K scales,
+// PART 2 its V scales, valid counts and V chunks (scales first), so that a
+// wave can issue the next tile's K half as soon as the current tile's scores
+// are formed and its V half once the current P.V is issued (tile_scores /
+// tile_accumulate): the next scores then wait for the K half and the V
+// scales only, with the V chunks still in flight.
+template <int HD, int PART = 0>
 __device__ __forceinline__ void tile_load(Tile<HD>& T, const DecodeArgs& a, const int (&tblk)[2], int kh,
                                           int ts, int t1, int lane, bool& bad) {
+    size_t base[2];
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
-        T.nval[st] = min(max(t1 - (ts + kSub * st), 0), kSub);
-        const int tst = T.nval[st] > 0 ? ts + kSub * st : ts;
-        int blk = (st == 1 && T.nval[1] > 0) ? tblk[1] : tblk[0];
+        const int nval = min(max(t1 - (ts + kSub * st), 0), kSub);
+        const int tst = nval > 0 ? ts + kSub * st : ts;
+        int blk = (st == 1 && nval > 0) ? tblk[1] : tblk[0];
         if ((unsigned)blk >= (unsigned)a.num_blocks) {
             bad = true;
             blk = 0;
         }
-        const size_t base = (((size_t)blk * a.n_kv + kh) << log2_pow2(a.kv_bs)) + (size_t)(tst & (a.kv_bs - 1));
-        T.ks[st] = stream_load<f32x4>(a.ks + base + 4 * (lane >> 4));
-        T.vs[st] = stream_load<f32x4>(a.vs + base + 4 * (lane >> 4));
-        load_k_subtile<HD>(T.k[st], a.kp, base, lane);
-        const int8_t* vsub = a.vp + base * HD;  // wave-uniform
+        base[st] = (((size_t)blk * a.n_kv + kh) << log2_pow2(a.kv_bs)) + (size_t)(tst & (a.kv_bs - 1));
+        if constexpr (PART != 1) T.nval[st] = nval;
+    }
+    if constexpr (PART == 0) {
 #pragma unroll
-        for (int c = 0; c < Geo<HD>::NPAIR; ++c) T.v[st][c] = stream_load<u32x4>(vsub + 1024 * c + 16 * lane);
+        for (int st = 0; st < 2; ++st) {
+            T.ks[st] = stream_load<f32x4>(a.ks + base[st] + 4 * (lane >> 4));
+            T.vs[st] = stream_load<f32x4>(a.vs + base[st] + 4 * (lane >> 4));
+            load_k_subtile<HD>(T.k[st], a.kp, base[st], lane);
+            const int8_t* vsub = a.vp + base[st] * HD;  // wave-uniform
+#pragma unroll
+            for (int c = 0; c < Geo<HD>::NPAIR; ++c) T.v[st][c] = stream_load<u32x4>(vsub + 1024 * c + 16 * lane);
+        }
+    } else if constexpr (PART == 1) {
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            T.ks[st] = stream_load<f32x4>(a.ks + base[st] + 4 * (lane >> 4));
+            load_k_subtile<HD>(T.k[st], a.kp, base[st], lane);
+        }
+    } else {
+#pragma unroll
+        for (int st = 0; st < 2; ++st) T.vs[st] = stream_load<f32x4>(a.vs + base[st] + 4 * (lane >> 4));
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            const int8_t* vsub = a.vp + base[st] * HD;  // wave-uniform
+#pragma unroll
+            for (int c = 0; c < Geo<HD>::NPAIR; ++c) T.v[st][c] = stream_load<u32x4>(vsub + 1024 * c + 16 * lane);
+        }
     }
 }
 
@@ -933,15 +961,21 @@ __device__ __forceinline__ void store_new_token(const DecodeArgs& a, int kh, int
 // 2^(M_old - M_new), weights 2^(s - M_new + kWeightShift), P.V on the matrix
 // cores.  E: the wave's V-scale exponent (S and the accumulator are
 // normalised at P = M - kWeightShift + E).
+// The tile's scores (the part that reads K and the K scales) ...
+struct TileScores {
+    float sc[2][4];
+    float mx, vmx;  // this lane's largest score and valid V scale
+};
+
 template <int HD>
-__device__ __forceinline__ void tile_compute(const Tile<HD>& T, const int8_t* lq, const float* lqsc, float score_scale,
-                                             f32x4 (&acc)[Geo<HD>::BPL], float& M, float& S, int& E, int lane) {
+__device__ __forceinline__ void tile_scores(const Tile<HD>& T, const int8_t* lq, const float* lqsc, float score_scale,
+                                            TileScores& ts, int lane) {
     using GG = Geo<HD>;
-    const int r = lane >> 4, n = lane & 15;
+    const int r = lane >> 4;
     // the query operand is re-read from LDS each tile rather than pinned in registers
     QOperand<HD> Q;
     load_q_operand<HD>(Q, lq, lqsc, lane, score_scale);
-    float sc[2][4];
+    float (&sc)[2][4] = ts.sc;
     float mx = -INFINITY;
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
@@ -967,6 +1001,18 @@ __device__ __forceinline__ void tile_compute(const Tile<HD>& T, const int8_t* lq
 #pragma unroll
         for (int j = 0; j < 4; ++j) vmx = fmaxf(vmx, (4 * r + j) < T.nval[st] ? T.vs[st][j] : 0.0f);
     }
+    ts.mx = mx;
+    ts.vmx = vmx;
+}
+
+// ... and the rest of the step (the part that reads V and the V scales).
+template <int HD>
+__device__ __forceinline__ void tile_accumulate(const Tile<HD>& T, const TileScores& ts,
+                                                f32x4 (&acc)[Geo<HD>::BPL], float& M, float& S, int& E, int lane) {
+    using GG = Geo<HD>;
+    const int r = lane >> 4, n = lane & 15;
+    const float (&sc)[2][4] = ts.sc;
+    float mx = ts.mx, vmx = ts.vmx;
     mx = swap16_max(mx);
     vmx = swap16_max(vmx);
     mx = swap32_max(mx);
@@ -1022,6 +1068,14 @@ __device__ __forceinline__ void tile_compute(const Tile<HD>& T, const int8_t* lq
             acc[4 * d + b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, bv[b], acc[4 * d + b], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
     }
+}
+
+template <int HD>
+__device__ __forceinline__ void tile_compute(const Tile<HD>& T, const int8_t* lq, const float* lqsc, float score_scale,
+                                             f32x4 (&acc)[Geo<HD>::BPL], float& M, float& S, int& E, int lane) {
+    TileScores ts;
+    tile_scores<HD>(T, lq, lqsc, score_scale, ts, lane);
+    tile_accumulate<HD>(T, ts, acc, M, S, E, lane);
 }
 
 // ----------------------------------------------------------------------------
@@ -1487,13 +1541,29 @@ __device__ __forceinline__ void q4_offset_fix(f32x4 (&acc)[Geo<HD>::BPL], const 
 // the shape's upper bound, read straight off blockIdx; a slot past its
 // sequence's end exits at once.  Each wave holds one register tile; latency
 // is hidden by the other resident waves (one wave's loads overlap the
-// others' compute).  3 waves per SIMD fit hd 64 and 128 without spills; hd
-// 256 keeps a whole register file.
+// others' compute) and, on persistent int8 grids, by the rolling tile order
+// below.  3 waves per SIMD fit hd 64 and 128 without spills; hd 256 keeps a
+// whole register file.
 enum GridMode { kPersistent = 0, kStatic = 1 };
 enum CodecKind { kQ8 = 0, kFp8 = 1, kQ40 = 2 };
 
+// Persistent int8 grids on the direct path roll their tiles (the next tile's
+// K half is issued around the current P.V, see the tile loop); at hd 128 the
+// K registers in flight then need more than a third of a SIMD's registers,
+// so those kernels run at two waves per SIMD.  Static grids keep the plain
+// order, which measured as fast or faster for them.
+constexpr bool kRollPersistent = true;
+constexpr bool kRollStatic = false;
+constexpr int kRollWavesPerEu = 2;
+constexpr bool decode_rolls(int mode, int codec, bool stg) {
+    return !stg && codec == kQ8 && (mode == kStatic ? kRollStatic : kRollPersistent);
+}
+constexpr int decode_waves_per_eu(int hd, int mode, int codec, bool stg) {
+    return hd == 256 ? 1 : stg ? 2 : (hd == 128 && decode_rolls(mode, codec, stg)) ? kRollWavesPerEu : 3;
+}
+
 template <int HD, int MODE, bool NEW, int CODEC = kQ8, int NW = kWaves, bool STG = false>
-__global__ __launch_bounds__(kWave * NW) __attribute__((amdgpu_waves_per_eu(HD == 256 ? 1 : STG ? 2 : 3))) void
+__global__ __launch_bounds__(kWave * NW) __attribute__((amdgpu_waves_per_eu(decode_waves_per_eu(HD, MODE, CODEC, STG)))) void
 q8kv_decode_kernel(const DecodeArgs a) {
     using GG = Geo<HD>;
     constexpr int NT = kWave * NW;  // threads per workgroup
@@ -1758,9 +1828,16 @@ q8kv_decode_kernel(const DecodeArgs a) {
         } else {
             const bool own = ts < t1;
             const int blk0[2] = {own ? blk_first[0] : blk_t0[0], own ? blk_first[1] : blk_t0[1]};
-            if constexpr (FP8) fp8_tile_load<HD>(A, a, blk0, kh, own ? ts : t0, t1, ilane, bad);
-            else if constexpr (Q40) q4_tile_load<HD>(A, a, blk0, kh, own ? ts : t0, t1, ilane, bad);
-            else tile_load<HD>(A, a, blk0, kh, own ? ts : t0, t1, ilane, bad);
+            if constexpr (FP8) {
+                fp8_tile_load<HD>(A, a, blk0, kh, own ? ts : t0, t1, ilane, bad);
+            } else if constexpr (Q40) {
+                q4_tile_load<HD>(A, a, blk0, kh, own ? ts : t0, t1, ilane, bad);
+            } else {
+                // K half first, as the tile loop issues them (the first
+                // scores then wait for the same count of later loads)
+                tile_load<HD, 1>(A, a, blk0, kh, own ? ts : t0, t1, ilane, bad);
+                tile_load<HD, 2>(A, a, blk0, kh, own ? ts : t0, t1, ilane, bad);
+            }
         }
         if constexpr (NEW && STATIC) {
             // static grids: the new rows' loads go out behind the first tile
@@ -1811,7 +1888,39 @@ q8kv_decode_kernel(const DecodeArgs a) {
         int E = kVsEInit;  // int8 codec: the V-scale exponent offset
         f32x4 wsums = {0.f, 0.f, 0.f, 0.f};  // q4_0: per-block weight sums
 
-        while (ts < t1) {
+        // Rolling order (persistent int8 grids): the next tile's K half is
+        // issued once the current scores are formed (its K registers are
+        // free), its V half once the current P.V is issued, so that a wave
+        // keeps loads in flight while it computes without a second set of
+        // tile registers.  Each branch ends in its own path (the last tile's
+        // arm breaks out), so the compiler's waits count the loads exactly.
+        constexpr bool ROLL = decode_rolls(MODE, CODEC, STAGE);
+        if constexpr (ROLL) {
+            while (ts < t1) {
+                if constexpr (NEW) {
+                    if (ts == tail_ts) tile_patch<HD>(A, lnew, lnew + HD, lnew_sc[0], lnew_sc[1], L - 1 - ts, ilane);
+                }
+                const int tn = ts + kStride;
+                int blk[2];
+                tile_blocks(trow, tn, a.kv_bs, a.max_blocks, blk);
+                TileScores tsc;
+                tile_scores<HD>(A, lq, lqsc, a.scale_log2, tsc, ilane);
+                if (tn < t1) {
+                    tile_load<HD, 1>(A, a, blk, kh, tn, t1, ilane, bad);
+                    tile_accumulate<HD>(A, tsc, acc, M, S, E, ilane);
+                    tile_load<HD, 2>(A, a, blk, kh, tn, t1, ilane, bad);
+                    if constexpr (NEW && STATIC) {
+                        if (tail_ts != INT_MIN && tn == ts_second)
+                            prepare_new_token<HD>(nk, nv, tail_blk, lnew, lnew_sc, &lnew_blk, ilane);
+                    }
+                    ts = tn;
+                } else {
+                    tile_accumulate<HD>(A, tsc, acc, M, S, E, ilane);
+                    break;
+                }
+            }
+        }
+        while (!ROLL && ts < t1) {
             if constexpr (STAGE) {
                 // the slot's tile, once its loads have landed (those of the
                 // tiles issued after it may stay in flight); the slot is
@@ -2831,6 +2940,126 @@ __global__ __launch_bounds__(256) void q8kv_stream_read_kernel(const u32x4* __re
     if (acc == 0x9e3779b9u) *reinterpret_cast<volatile unsigned*>(&g_stream_sink) = acc;
 }
 
+// Load-pattern probe: the int8 decode kernel's K, V and scale loads over a
+// static grid of items (item_pages consecutive pages of the flattened pool
+// each, four waves per workgroup, at most two workgroups per CU, wave w
+// taking tiles w, w + 4, ... of 32 tokens with the next tile's loads issued
+// before the current one is folded), without the arithmetic.  Patterns:
+//   0  the pages' operand order: one dwordx4 per lane per 1 KB chunk of K
+//      and of V, plus the per-row-group K and V scale loads;
+//   1  pattern 0 without the scale loads;
+//   2  row-major pages ([row][HD] bytes, the token-major order of a row
+//      cache) read into the same operands: K as 16-byte pieces (a wave load
+//      covers 16 rows x 64 bytes), V as four BPL-byte pieces per lane and
+//      sub-tile (rows 4r .. 4r + 3), plus the scale loads.
+// Every loaded word is folded into one value that is stored only if it
+// equals a constant, so that no load is dropped.
+template <int HD>
+struct ProbeTile {
+    u32x4 k[2][HD / 64];
+    u32x4 v[2][HD / 64];
+    f32x4 ks[2], vs[2];
+};
+
+template <int N>
+__device__ __forceinline__ void probe_words(uint32_t* w, const int8_t* p) {
+    if constexpr (N == 1) {
+        w[0] = stream_load<uint32_t>(p);
+    } else if constexpr (N == 2) {
+        const u32x2 x = stream_load<u32x2>(p);
+        w[0] = x[0];
+        w[1] = x[1];
+    } else {
+        const u32x4 x = stream_load<u32x4>(p);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = x[i];
+    }
+}
+
+template <int HD, int PAT>
+__device__ __forceinline__ void probe_issue(ProbeTile<HD>& T, const int8_t* kp, const int8_t* vp, const float* ks,
+                                            const float* vs, size_t page0, int kv_bs, int tile, int lane) {
+    constexpr int NC = HD / 64, BPL = HD / 16;
+    const int r = lane >> 4, n = lane & 15;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        const int tok = 32 * tile + 16 * s;
+        const size_t row = (page0 + (size_t)(tok / kv_bs)) * kv_bs + (size_t)(tok % kv_bs);  // first row of the sub-tile
+        const int8_t* ksub = kp + row * HD;
+        const int8_t* vsub = vp + row * HD;
+        if constexpr (PAT == 2) {
+#pragma unroll
+            for (int c = 0; c < NC; ++c) T.k[s][c] = stream_load<u32x4>(ksub + (size_t)n * HD + 64 * c + 16 * r);
+            uint32_t* w = reinterpret_cast<uint32_t*>(&T.v[s][0]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) probe_words<BPL / 4>(w + j * (BPL / 4), vsub + (size_t)(4 * r + j) * HD + BPL * n);
+        } else {
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                T.k[s][c] = stream_load<u32x4>(ksub + 1024 * c + 16 * lane);
+                T.v[s][c] = stream_load<u32x4>(vsub + 1024 * c + 16 * lane);
+            }
+        }
+        if constexpr (PAT != 1) {
+            T.ks[s] = stream_load<f32x4>(ks + row + 4 * r);
+            T.vs[s] = stream_load<f32x4>(vs + row + 4 * r);
+        }
+    }
+}
+
+template <int HD, int PAT>
+__device__ __forceinline__ uint32_t probe_fold(const ProbeTile<HD>& T) {
+    uint32_t x = 0;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+#pragma unroll
+        for (int c = 0; c < HD / 64; ++c) {
+            const u32x4 y = T.k[s][c] ^ T.v[s][c];
+            x ^= y[0] ^ y[1] ^ y[2] ^ y[3];
+        }
+        if constexpr (PAT != 1) {
+            const u32x4 y = __builtin_bit_cast(u32x4, T.ks[s]) ^ __builtin_bit_cast(u32x4, T.vs[s]);
+            x ^= y[0] ^ y[1] ^ y[2] ^ y[3];
+        }
+    }
+    return x;
+}
+
+template <int HD, int PAT>
+__global__ __launch_bounds__(256) void q8kv_load_probe_kernel(const int8_t* __restrict__ kp,
+                                                              const int8_t* __restrict__ vp,
+                                                              const float* __restrict__ ks,
+                                                              const float* __restrict__ vs, int kv_bs,
+                                                              int item_pages) {
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const size_t page0 = (size_t)blockIdx.x * item_pages;
+    const int steps = item_pages * kv_bs / (32 * kWaves);  // tiles per wave (the host checks divisibility)
+    // two register sets in turn (no copies, so that no load waits for the
+    // previous tile); the scheduling barriers keep each fold behind the
+    // next tile's loads
+    ProbeTile<HD> x, y;
+    probe_issue<HD, PAT>(x, kp, vp, ks, vs, page0, kv_bs, wid, lane);
+    uint32_t acc = 0;
+    int i = 1;
+    for (; i + 1 < steps; i += 2) {
+        probe_issue<HD, PAT>(y, kp, vp, ks, vs, page0, kv_bs, wid + kWaves * i, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        acc ^= probe_fold<HD, PAT>(x);
+        probe_issue<HD, PAT>(x, kp, vp, ks, vs, page0, kv_bs, wid + kWaves * (i + 1), lane);
+        __builtin_amdgcn_sched_barrier(0);
+        acc ^= probe_fold<HD, PAT>(y);
+    }
+    if (i < steps) {
+        probe_issue<HD, PAT>(y, kp, vp, ks, vs, page0, kv_bs, wid + kWaves * i, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        acc ^= probe_fold<HD, PAT>(x) ^ probe_fold<HD, PAT>(y);
+    } else {
+        acc ^= probe_fold<HD, PAT>(x);
+    }
+    if (acc == 0x9e3779b9u) *reinterpret_cast<volatile unsigned*>(&g_stream_sink) = acc;
+}
+
 // ----------------------------------------------------------------------------
 // host side
 
@@ -3260,6 +3489,14 @@ int decode_impl(float* out, const float* q, const int8_t* kp, const int8_t* vp, 
     return Q8KV_OK;
 }
 
+template <int HD>
+void launch_probe(int pattern, unsigned grid, size_t lds, hipStream_t st, const int8_t* kp, const int8_t* vp,
+                  const float* ks, const float* vs, int kv_bs, int item_pages) {
+    if (pattern == 0) hipLaunchKernelGGL((q8kv_load_probe_kernel<HD, 0>), dim3(grid), dim3(256), lds, st, kp, vp, ks, vs, kv_bs, item_pages);
+    else if (pattern == 1) hipLaunchKernelGGL((q8kv_load_probe_kernel<HD, 1>), dim3(grid), dim3(256), lds, st, kp, vp, ks, vs, kv_bs, item_pages);
+    else hipLaunchKernelGGL((q8kv_load_probe_kernel<HD, 2>), dim3(grid), dim3(256), lds, st, kp, vp, ks, vs, kv_bs, item_pages);
+}
+
 }  // namespace
 
 extern "C" {
@@ -3649,6 +3886,31 @@ int q8kv_debug_set_wide(int enable) {
     g_err.clear();
     if (enable != 0 && enable != 1) return fail(Q8KV_EINVAL, "enable must be 0 or 1 (got %d)", enable);
     g_wide.store(enable);
+    return Q8KV_OK;
+}
+
+int q8kv_debug_load_probe(const int8_t* k_pages, const int8_t* v_pages, const float* k_scale, const float* v_scale,
+                          int num_pages, int hd, int kv_bs, int item_pages, int pattern, void* stream) {
+    g_err.clear();
+    if (!k_pages || !v_pages || !k_scale || !v_scale) return fail(Q8KV_ENULL, "a buffer pointer is NULL");
+    if (!full_hd(hd) || !valid_kv_bs(kv_bs)) return fail(Q8KV_EINVAL, "bad hd (%d) or kv_bs (%d)", hd, kv_bs);
+    if (pattern < 0 || pattern > 2) return fail(Q8KV_EINVAL, "pattern must be 0, 1 or 2 (got %d)", pattern);
+    if (num_pages <= 0 || item_pages <= 0 || num_pages % item_pages ||
+        ((long long)item_pages * kv_bs) % (32 * kWaves) || (long long)item_pages * kv_bs > (INT_MAX / 2))
+        return fail(Q8KV_EINVAL, "num_pages (%d) must be a multiple of item_pages (%d), whose tokens a multiple of %d",
+                    num_pages, item_pages, 32 * kWaves);
+    // a dynamic LDS request that leaves room for two workgroups per CU, as
+    // the decode kernel's static grids have
+    const size_t lds = 64 * 1024;
+    const unsigned grid = (unsigned)(num_pages / item_pages);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    switch (hd) {
+        case 64: launch_probe<64>(pattern, grid, lds, st, k_pages, v_pages, k_scale, v_scale, kv_bs, item_pages); break;
+        case 128: launch_probe<128>(pattern, grid, lds, st, k_pages, v_pages, k_scale, v_scale, kv_bs, item_pages); break;
+        default: launch_probe<256>(pattern, grid, lds, st, k_pages, v_pages, k_scale, v_scale, kv_bs, item_pages); break;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "load probe launch");
     return Q8KV_OK;
 }
 

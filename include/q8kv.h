@@ -462,6 +462,25 @@ int q8kv_debug_set_stage(int enable);
  */
 int q8kv_debug_stream_read(const void* a, size_t a_bytes, const void* b, size_t b_bytes, void* stream);
 
+/*
+ * Measurement export: the int8 decode kernel's loads without its arithmetic,
+ * over the first num_pages pages (block, kv head) of a page pool taken as
+ * one flat array, to compare load orders on the same device.  Items of
+ * item_pages consecutive pages, one per workgroup of four waves (at most
+ * two per CU), each wave loading 32-token tiles as the decode kernel does.
+ * pattern 0: the page layout above (one 16-byte load per lane per 1 KB
+ * chunk of K and V) plus the per-row K and V scale loads; 1: the same
+ * without the scale loads; 2: the same bytes taken as row-major pages
+ * ([row][hd] bytes per page, the token-major order of a row cache) loaded
+ * into the same matrix-core operands (K 16-byte pieces of 16 rows, V
+ * hd/16-byte pieces of four rows per lane) plus the scale loads.  hd 64,
+ * 128 or 256; item_pages * kv_bs a multiple of 128; num_pages a multiple of
+ * item_pages.  No output; never writes the pool.
+ */
+int q8kv_debug_load_probe(const int8_t* k_pages, const int8_t* v_pages, const float* k_scale,
+                          const float* v_scale, int num_pages, int hd, int kv_bs, int item_pages,
+                          int pattern, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

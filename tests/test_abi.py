@@ -14,7 +14,7 @@ NUL = ctypes.c_void_p(0)
 
 def test_exports_every_declared_symbol():
     names = q8.header_symbols()
-    assert len(names) == 21
+    assert len(names) == 22
     for n in names:
         assert hasattr(L, n), n
 
@@ -333,3 +333,16 @@ def test_padded_page_width():
     assert q8.PagedKVCache.wrap(kp, kp.clone(), ks, ks.clone()).hd == 128
     with pytest.raises(ValueError):
         q8.PagedKVCache.wrap(kp, kp.clone(), ks, ks.clone(), hd=64)
+
+
+def test_load_probe_rejects_before_any_hip_call():
+    p = lambda **kw: L.q8kv_debug_load_probe(*[kw.get(k, FAKE) for k in ("kp", "vp", "ks", "vs")],
+                                             kw.get("n", 64), kw.get("hd", 128), kw.get("bs", 64),
+                                             kw.get("item", 16), kw.get("pat", 0), NUL)
+    assert p(kp=NUL) == q8.Q8KV_ENULL
+    assert p(hd=96) == q8.Q8KV_EINVAL      # full page widths only
+    assert p(bs=48) == q8.Q8KV_EINVAL
+    assert p(pat=3) == q8.Q8KV_EINVAL
+    assert p(n=60) == q8.Q8KV_EINVAL       # not a multiple of item_pages
+    assert p(bs=16, item=4) == q8.Q8KV_EINVAL  # 64 tokens an item: not a multiple of 128
+    assert p(n=0) == q8.Q8KV_EINVAL
