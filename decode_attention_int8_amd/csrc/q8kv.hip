@@ -1144,26 +1144,50 @@ struct Fp8Tile {
     int nval[2];
 };
 
-template <int HD>
+// PART as for the int8 tile_load: 0 the whole tile, 1 the K chunks and K
+// scale bytes, 2 the V scale bytes, valid counts and V chunks.
+template <int HD, int PART = 0>
 __device__ __forceinline__ void fp8_tile_load(Fp8Tile<HD>& T, const DecodeArgs& a, const int (&tblk)[2], int kh,
                                               int ts, int t1, int lane, bool& bad) {
     constexpr int NB = Fp8Tile<HD>::NB;
+    size_t base[2];
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
-        T.nval[st] = min(max(t1 - (ts + kSub * st), 0), kSub);
-        const int tst = T.nval[st] > 0 ? ts + kSub * st : ts;
-        int blk = (st == 1 && T.nval[1] > 0) ? tblk[1] : tblk[0];
+        const int nval = min(max(t1 - (ts + kSub * st), 0), kSub);
+        const int tst = nval > 0 ? ts + kSub * st : ts;
+        int blk = (st == 1 && nval > 0) ? tblk[1] : tblk[0];
         if ((unsigned)blk >= (unsigned)a.num_blocks) {
             bad = true;
             blk = 0;
         }
-        const size_t base = (((size_t)blk * a.n_kv + kh) << log2_pow2(a.kv_bs)) + (size_t)(tst & (a.kv_bs - 1));
-        load_scale_bytes<NB>(T.ke[st], a.ks8 + (base + 4 * (lane >> 4)) * NB);
-        load_scale_bytes<NB>(T.ve[st], a.vs8 + (base + 4 * (lane >> 4)) * NB);
-        load_k_subtile<HD>(T.k[st], a.kp, base, lane);
-        const int8_t* vsub = a.vp + base * HD;
+        base[st] = (((size_t)blk * a.n_kv + kh) << log2_pow2(a.kv_bs)) + (size_t)(tst & (a.kv_bs - 1));
+        if constexpr (PART != 1) T.nval[st] = nval;
+    }
+    if constexpr (PART == 0) {
 #pragma unroll
-        for (int c = 0; c < Geo<HD>::NPAIR; ++c) T.v[st][c] = stream_load<u32x4>(vsub + 1024 * c + 16 * lane);
+        for (int st = 0; st < 2; ++st) {
+            load_scale_bytes<NB>(T.ke[st], a.ks8 + (base[st] + 4 * (lane >> 4)) * NB);
+            load_scale_bytes<NB>(T.ve[st], a.vs8 + (base[st] + 4 * (lane >> 4)) * NB);
+            load_k_subtile<HD>(T.k[st], a.kp, base[st], lane);
+            const int8_t* vsub = a.vp + base[st] * HD;
+#pragma unroll
+            for (int c = 0; c < Geo<HD>::NPAIR; ++c) T.v[st][c] = stream_load<u32x4>(vsub + 1024 * c + 16 * lane);
+        }
+    } else if constexpr (PART == 1) {
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            load_scale_bytes<NB>(T.ke[st], a.ks8 + (base[st] + 4 * (lane >> 4)) * NB);
+            load_k_subtile<HD>(T.k[st], a.kp, base[st], lane);
+        }
+    } else {
+#pragma unroll
+        for (int st = 0; st < 2; ++st) load_scale_bytes<NB>(T.ve[st], a.vs8 + (base[st] + 4 * (lane >> 4)) * NB);
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            const int8_t* vsub = a.vp + base[st] * HD;
+#pragma unroll
+            for (int c = 0; c < Geo<HD>::NPAIR; ++c) T.v[st][c] = stream_load<u32x4>(vsub + 1024 * c + 16 * lane);
+        }
     }
 }
 
@@ -1211,13 +1235,12 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t x0, uint32_t x1) {
 // One tile of the recurrence over FP8 K/V (same softmax steps as
 // tile_compute; acc[s] holds output columns 16 s + n).
 template <int HD>
-__device__ __forceinline__ void fp8_tile_compute(const Fp8Tile<HD>& T, const _Float16* lq16, float score_scale,
-                                                 f32x4 (&acc)[Geo<HD>::BPL], float& M, float& S, int lane) {
-    using GG = Geo<HD>;
+__device__ __forceinline__ void fp8_tile_scores(const Fp8Tile<HD>& T, const _Float16* lq16, float score_scale,
+                                                TileScores& ts, int lane) {
     constexpr int NB = Fp8Tile<HD>::NB;
     const int r = lane >> 4, n = lane & 15;
     const _Float16* qrow = lq16 + ((n >> 3) * kHeadGroup + (n & 7)) * HD + 16 * r;
-    float sc[2][4];
+    float (&sc)[2][4] = ts.sc;
     float mx = -INFINITY;
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
@@ -1242,6 +1265,17 @@ __device__ __forceinline__ void fp8_tile_compute(const Fp8Tile<HD>& T, const _Fl
             mx = fmaxf(mx, sc[st][j]);
         }
     }
+    ts.mx = mx;
+}
+
+template <int HD>
+__device__ __forceinline__ void fp8_tile_accumulate(const Fp8Tile<HD>& T, const TileScores& ts,
+                                                    f32x4 (&acc)[Geo<HD>::BPL], float& M, float& S, int lane) {
+    using GG = Geo<HD>;
+    constexpr int NB = Fp8Tile<HD>::NB;
+    const int r = lane >> 4, n = lane & 15;
+    const float (&sc)[2][4] = ts.sc;
+    float mx = ts.mx;
     mx = swap16_max(mx);
     mx = swap32_max(mx);
     const float m_new = fmaxf(M, mx);
@@ -1298,6 +1332,14 @@ __device__ __forceinline__ void fp8_tile_compute(const Fp8Tile<HD>& T, const _Fl
             acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw, bv, acc[s], 0, 0, 0);
         }
     }
+}
+
+template <int HD>
+__device__ __forceinline__ void fp8_tile_compute(const Fp8Tile<HD>& T, const _Float16* lq16, float score_scale,
+                                                 f32x4 (&acc)[Geo<HD>::BPL], float& M, float& S, int lane) {
+    TileScores ts;
+    fp8_tile_scores<HD>(T, lq16, score_scale, ts, lane);
+    fp8_tile_accumulate<HD>(T, ts, acc, M, S, lane);
 }
 
 // ----------------------------------------------------------------------------
@@ -1360,25 +1402,41 @@ struct Q4Tile {
     }
 };
 
-template <int HD>
+// PART as for the int8 tile_load: 0 the whole tile, 1 the K codes and K
+// scales, 2 the V scales, valid counts and V codes.
+template <int HD, int PART = 0>
 __device__ __forceinline__ void q4_tile_load(Q4Tile<HD>& T, const DecodeArgs& a, const int (&tblk)[2], int kh,
                                              int ts, int t1, int lane, bool& bad) {
     using QG = Q4Geo<HD>;
+    size_t base[2];
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
-        T.nval[st] = min(max(t1 - (ts + kSub * st), 0), kSub);
-        const int tst = T.nval[st] > 0 ? ts + kSub * st : ts;
-        int blk = (st == 1 && T.nval[1] > 0) ? tblk[1] : tblk[0];
+        const int nval = min(max(t1 - (ts + kSub * st), 0), kSub);
+        const int tst = nval > 0 ? ts + kSub * st : ts;
+        int blk = (st == 1 && nval > 0) ? tblk[1] : tblk[0];
         if ((unsigned)blk >= (unsigned)a.num_blocks) {
             bad = true;
             blk = 0;
         }
-        const size_t base = (((size_t)blk * a.n_kv + kh) << log2_pow2(a.kv_bs)) + (size_t)(tst & (a.kv_bs - 1));
-        const size_t srow = (base + 4 * (lane >> 4)) * QG::NB * 2;  // byte offset of row 4r's scales
-        load_dwords<QG::SCW>(T.kd[st], a.ks8 + srow);
-        load_dwords<QG::SCW>(T.vd[st], a.vs8 + srow);
-        load_dwords<QG::SW>(T.k[st], a.kp + base * (HD / 2) + (size_t)lane * QG::SLOT);
-        load_dwords<QG::SW>(T.v[st], a.vp + base * (HD / 2) + (size_t)lane * QG::SLOT);
+        base[st] = (((size_t)blk * a.n_kv + kh) << log2_pow2(a.kv_bs)) + (size_t)(tst & (a.kv_bs - 1));
+        if constexpr (PART != 1) T.nval[st] = nval;
+    }
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+        const size_t srow = (base[st] + 4 * (lane >> 4)) * QG::NB * 2;  // byte offset of row 4r's scales
+        if constexpr (PART != 2) load_dwords<QG::SCW>(T.kd[st], a.ks8 + srow);
+        if constexpr (PART != 1) load_dwords<QG::SCW>(T.vd[st], a.vs8 + srow);
+        if constexpr (PART == 0) {
+            load_dwords<QG::SW>(T.k[st], a.kp + base[st] * (HD / 2) + (size_t)lane * QG::SLOT);
+            load_dwords<QG::SW>(T.v[st], a.vp + base[st] * (HD / 2) + (size_t)lane * QG::SLOT);
+        }
+    }
+    if constexpr (PART != 0) {
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            if constexpr (PART == 1) load_dwords<QG::SW>(T.k[st], a.kp + base[st] * (HD / 2) + (size_t)lane * QG::SLOT);
+            else load_dwords<QG::SW>(T.v[st], a.vp + base[st] * (HD / 2) + (size_t)lane * QG::SLOT);
+        }
     }
 }
 
@@ -1398,11 +1456,9 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float x, float y) {
 constexpr float kQ4Offset = 136.0f;
 
 template <int HD>
-__device__ __forceinline__ void q4_tile_compute(Q4Tile<HD>& T, const int8_t* lq, const float* lqsc,
-                                                const int* lqsum, float score_scale, f32x4 (&acc)[Geo<HD>::BPL],
-                                                f32x4& wsums, float& M, float& S, int lane) {
+__device__ __forceinline__ void q4_tile_scores(const Q4Tile<HD>& T, const int8_t* lq, const float* lqsc,
+                                               const int* lqsum, float score_scale, TileScores& ts, int lane) {
     using GG = Geo<HD>;
-    using QG = Q4Geo<HD>;
     const int r = lane >> 4, n = lane & 15, bp = n >> 3, g = n & 7;
     QOperand<HD> Q;
     load_q_operand<HD>(Q, lq, lqsc, lane, score_scale);
@@ -1410,7 +1466,7 @@ __device__ __forceinline__ void q4_tile_compute(Q4Tile<HD>& T, const int8_t* lq,
     int qs8[GG::NPAIR];
 #pragma unroll
     for (int p = 0; p < GG::NPAIR; ++p) qs8[p] = -8 * lqsum[g * GG::NB + 2 * p + bp];
-    float sc[2][4];
+    float (&sc)[2][4] = ts.sc;
     float mx = -INFINITY;
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
@@ -1433,6 +1489,17 @@ __device__ __forceinline__ void q4_tile_compute(Q4Tile<HD>& T, const int8_t* lq,
             mx = fmaxf(mx, sc[st][j]);
         }
     }
+    ts.mx = mx;
+}
+
+template <int HD>
+__device__ __forceinline__ void q4_tile_accumulate(Q4Tile<HD>& T, const TileScores& ts, f32x4 (&acc)[Geo<HD>::BPL],
+                                                   f32x4& wsums, float& M, float& S, int lane) {
+    using GG = Geo<HD>;
+    using QG = Q4Geo<HD>;
+    const int r = lane >> 4, n = lane & 15;
+    const float (&sc)[2][4] = ts.sc;
+    float mx = ts.mx;
     mx = swap16_max(mx);
     mx = swap32_max(mx);
     const float m_new = fmaxf(M, mx);
@@ -1518,6 +1585,15 @@ __device__ __forceinline__ void q4_tile_compute(Q4Tile<HD>& T, const int8_t* lq,
     }
 }
 
+template <int HD>
+__device__ __forceinline__ void q4_tile_compute(Q4Tile<HD>& T, const int8_t* lq, const float* lqsc,
+                                                const int* lqsum, float score_scale, f32x4 (&acc)[Geo<HD>::BPL],
+                                                f32x4& wsums, float& M, float& S, int lane) {
+    TileScores ts;
+    q4_tile_scores<HD>(T, lq, lqsc, lqsum, score_scale, ts, lane);
+    q4_tile_accumulate<HD>(T, ts, acc, wsums, M, S, lane);
+}
+
 // acc holds sum_k w_k (128 + c_k) per block; the weight sums of block b sit
 // in column b of wsums (lane 16 r + b): subtract 136 times them.
 template <int HD>
@@ -1541,22 +1617,24 @@ __device__ __forceinline__ void q4_offset_fix(f32x4 (&acc)[Geo<HD>::BPL], const 
 // the shape's upper bound, read straight off blockIdx; a slot past its
 // sequence's end exits at once.  Each wave holds one register tile; latency
 // is hidden by the other resident waves (one wave's loads overlap the
-// others' compute) and, on persistent int8 grids, by the rolling tile order
-// below.  3 waves per SIMD fit hd 64 and 128 without spills; hd 256 keeps a
+// others' compute) and, on persistent int8 and FP8 grids, by the rolling
+// tile order below.  3 waves per SIMD fit hd 64 and 128 without spills; hd 256 keeps a
 // whole register file.
 enum GridMode { kPersistent = 0, kStatic = 1 };
 enum CodecKind { kQ8 = 0, kFp8 = 1, kQ40 = 2 };
 
-// Persistent int8 grids on the direct path roll their tiles (the next tile's
-// K half is issued around the current P.V, see the tile loop); at hd 128 the
-// K registers in flight then need more than a third of a SIMD's registers,
-// so those kernels run at two waves per SIMD.  Static grids keep the plain
-// order, which measured as fast or faster for them.
+// Persistent int8 and FP8 grids on the direct path roll their tiles (the
+// next tile's K half is issued around the current P.V, see the tile loop);
+// at hd 128 the K registers in flight then need more than a third of a
+// SIMD's registers, so those kernels run at two waves per SIMD.  Static
+// grids keep the plain order, which measured as fast or faster for them;
+// so does the q4_0 codec, whose instruction-bound tile loop lost more to
+// the lower occupancy than it gained from the overlap.
 constexpr bool kRollPersistent = true;
 constexpr bool kRollStatic = false;
 constexpr int kRollWavesPerEu = 2;
 constexpr bool decode_rolls(int mode, int codec, bool stg) {
-    return !stg && codec == kQ8 && (mode == kStatic ? kRollStatic : kRollPersistent);
+    return !stg && (codec == kQ8 || codec == kFp8) && (mode == kStatic ? kRollStatic : kRollPersistent);
 }
 constexpr int decode_waves_per_eu(int hd, int mode, int codec, bool stg) {
     return hd == 256 ? 1 : stg ? 2 : (hd == 128 && decode_rolls(mode, codec, stg)) ? kRollWavesPerEu : 3;
@@ -1829,9 +1907,11 @@ q8kv_decode_kernel(const DecodeArgs a) {
             const bool own = ts < t1;
             const int blk0[2] = {own ? blk_first[0] : blk_t0[0], own ? blk_first[1] : blk_t0[1]};
             if constexpr (FP8) {
-                fp8_tile_load<HD>(A, a, blk0, kh, own ? ts : t0, t1, ilane, bad);
+                fp8_tile_load<HD, 1>(A, a, blk0, kh, own ? ts : t0, t1, ilane, bad);
+                fp8_tile_load<HD, 2>(A, a, blk0, kh, own ? ts : t0, t1, ilane, bad);
             } else if constexpr (Q40) {
-                q4_tile_load<HD>(A, a, blk0, kh, own ? ts : t0, t1, ilane, bad);
+                q4_tile_load<HD, 1>(A, a, blk0, kh, own ? ts : t0, t1, ilane, bad);
+                q4_tile_load<HD, 2>(A, a, blk0, kh, own ? ts : t0, t1, ilane, bad);
             } else {
                 // K half first, as the tile loop issues them (the first
                 // scores then wait for the same count of later loads)
@@ -1888,7 +1968,7 @@ q8kv_decode_kernel(const DecodeArgs a) {
         int E = kVsEInit;  // int8 codec: the V-scale exponent offset
         f32x4 wsums = {0.f, 0.f, 0.f, 0.f};  // q4_0: per-block weight sums
 
-        // Rolling order (persistent int8 grids): the next tile's K half is
+        // Rolling order (persistent int8 and FP8 grids): the next tile's K half is
         // issued once the current scores are formed (its K registers are
         // free), its V half once the current P.V is issued, so that a wave
         // keeps loads in flight while it computes without a second set of
@@ -1904,18 +1984,26 @@ q8kv_decode_kernel(const DecodeArgs a) {
                 int blk[2];
                 tile_blocks(trow, tn, a.kv_bs, a.max_blocks, blk);
                 TileScores tsc;
-                tile_scores<HD>(A, lq, lqsc, a.scale_log2, tsc, ilane);
+                if constexpr (FP8) fp8_tile_scores<HD>(A, lq16, a.scale_log2, tsc, ilane);
+                else tile_scores<HD>(A, lq, lqsc, a.scale_log2, tsc, ilane);
                 if (tn < t1) {
-                    tile_load<HD, 1>(A, a, blk, kh, tn, t1, ilane, bad);
-                    tile_accumulate<HD>(A, tsc, acc, M, S, E, ilane);
-                    tile_load<HD, 2>(A, a, blk, kh, tn, t1, ilane, bad);
+                    if constexpr (FP8) {
+                        fp8_tile_load<HD, 1>(A, a, blk, kh, tn, t1, ilane, bad);
+                        fp8_tile_accumulate<HD>(A, tsc, acc, M, S, ilane);
+                        fp8_tile_load<HD, 2>(A, a, blk, kh, tn, t1, ilane, bad);
+                    } else {
+                        tile_load<HD, 1>(A, a, blk, kh, tn, t1, ilane, bad);
+                        tile_accumulate<HD>(A, tsc, acc, M, S, E, ilane);
+                        tile_load<HD, 2>(A, a, blk, kh, tn, t1, ilane, bad);
+                    }
                     if constexpr (NEW && STATIC) {
                         if (tail_ts != INT_MIN && tn == ts_second)
                             prepare_new_token<HD>(nk, nv, tail_blk, lnew, lnew_sc, &lnew_blk, ilane);
                     }
                     ts = tn;
                 } else {
-                    tile_accumulate<HD>(A, tsc, acc, M, S, E, ilane);
+                    if constexpr (FP8) fp8_tile_accumulate<HD>(A, tsc, acc, M, S, ilane);
+                    else tile_accumulate<HD>(A, tsc, acc, M, S, E, ilane);
                     break;
                 }
             }

@@ -17,9 +17,9 @@ source, built here with the library's flags).
 * The staged tile loops hold no compiler-inserted wait for every load in
   flight (vmcnt(0)) ahead of their LDS reads other than the kernel's own
   waits in asm.
-* No int8 decode kernel at hd 64 or 128 spills to scratch memory, and the
-  persistent int8 kernels' rolled tile loop issues a tile's P.V behind the
-  next tile's K loads without waiting for them.
+* No int8 or FP8 decode kernel at hd 64 or 128 spills to scratch memory, and the
+  persistent int8 and FP8 kernels' rolled tile loop issues a tile's P.V
+  behind the next tile's K loads without waiting for them.
 """
 import os
 import re
@@ -114,23 +114,26 @@ def test_staged_tile_loop_waits_are_its_own(device_asm, hd, nw):
             assert ";;#ASMSTART" in lines[i - 1], f"{name}: compiler wait for every load at line {i}: {lines[i]}"
 
 
-def test_int8_decode_kernels_do_not_spill(device_asm):
-    """No int8-codec decode kernel at hd 64 or 128 keeps a value in scratch
-    memory (the rolled persistent kernels run at two waves per SIMD at hd
-    128 for that reason)."""
-    names = [n for n in device_asm if re.search(r"q8kv_decode_kernelILi(64|128)ELi\dELb\dELi0E", n)]
+def test_int8_and_fp8_decode_kernels_do_not_spill(device_asm):
+    """No int8- or FP8-codec decode kernel at hd 64 or 128 keeps a value in
+    scratch memory (the rolled persistent kernels run at two waves per SIMD
+    at hd 128 for that reason)."""
+    names = [n for n in device_asm if re.search(r"q8kv_decode_kernelILi(64|128)ELi\dELb\dELi[01]E", n)]
     assert len(names) >= 10
     for n in names:
         assert "scratch_" not in device_asm[n], f"{n}: scratch (spill) access"
 
 
-@pytest.mark.parametrize("new", ["0", "1"])
-def test_rolled_tile_loop_keeps_the_next_k_half_in_flight(device_asm, new):
-    """In the persistent int8 kernel the P.V matrix-core instructions of a
-    tile are issued behind loads of the next tile that they do not wait
-    for: between the last load before them and the P.V instruction every
-    wait leaves at least the next tile's four K chunks in flight."""
-    name = f"_ZN12_GLOBAL__N_118q8kv_decode_kernelILi128ELi0ELb{new}ELi0ELi4ELb0EEEvNS_10DecodeArgsE"
+@pytest.mark.parametrize("new,codec,pv", [("0", "0", "v_mfma_f32_16x16x32_f16"),
+                                          ("1", "0", "v_mfma_f32_16x16x32_f16"),
+                                          ("0", "1", "v_mfma_f32_16x16x32_bf16")])
+def test_rolled_tile_loop_keeps_the_next_k_half_in_flight(device_asm, new, codec, pv):
+    """In the persistent int8 and FP8 kernels the P.V matrix-core
+    instructions of a tile are issued behind loads of the next tile that
+    they do not wait for: between the last load before them and the P.V
+    instruction every wait leaves at least the next tile's four K chunks in
+    flight."""
+    name = f"_ZN12_GLOBAL__N_118q8kv_decode_kernelILi128ELi0ELb{new}ELi{codec}ELi4ELb0EEEvNS_10DecodeArgsE"
     lines = device_asm[name].split("\n")
     found = False
     since_load, low = None, None
@@ -140,7 +143,7 @@ def test_rolled_tile_loop_keeps_the_next_k_half_in_flight(device_asm, new):
             since_load, low = True, 63
         elif since_load and t.startswith("s_waitcnt") and "vmcnt(" in t:
             low = min(low, int(re.search(r"vmcnt\((\d+)\)", t).group(1)))
-        elif since_load and t.startswith("v_mfma_f32_16x16x32_f16"):
+        elif since_load and t.startswith(pv):
             found = found or low >= 4
             since_load = None
     assert found, f"{name}: every P.V waits for all loads in flight"
