@@ -135,13 +135,15 @@ def test_append_decode_split_and_merge(pt):
     run_case(c, part_tokens=pt, reps=2)
 
 
-def test_append_decode_persistent_grid():
-    """More items than resident workgroups: the persistent grid's item order."""
-    rng = np.random.default_rng(1200)
+@pytest.mark.parametrize("hd", [128, 64, 256])
+def test_append_decode_persistent_grid(hd):
+    """More items than resident workgroups: the persistent grid's item order
+    and its rolled tile loop, at every page width."""
+    rng = np.random.default_rng(1200 + hd)
     lens = [int(x) for x in rng.integers(1, 700, size=64)]
     lens[:6] = [0, 1, 32, 33, 64, 65]
-    w = workloads.Workload("fusedpersist", 64, 8, 2, 128, 16, 700, ragged=True, table="pool",
-                           key=1200)
+    w = workloads.Workload("fusedpersist", 64, 8, 2, hd, 16, 700, ragged=True, table="pool",
+                           key=1200 + hd)
     c = build(w, lens=lens, with_cache=False)
     say(f"fused persistent tokens={sum(lens)}")
     run_case(c, part_tokens=32)

@@ -178,11 +178,14 @@ def test_fp8_decode_shapes(hd, G, kv_bs):
         run_decode(c, dev, host, part_tokens=pt)
 
 
-def test_fp8_decode_persistent_grid():
-    rng = np.random.default_rng(2500)
+@pytest.mark.parametrize("hd", [128, 64, 256])
+def test_fp8_decode_persistent_grid(hd):
+    """More items than resident workgroups (the persistent kernel's rolled
+    tile loop) at every page width."""
+    rng = np.random.default_rng(2500 + hd)
     lens = [int(x) for x in rng.integers(1, 600, size=64)]
     lens[:5] = [0, 1, 32, 33, 64]
-    w = workloads.Workload("fp8persist", 64, 8, 2, 128, 16, 600, ragged=True, table="pool", key=2500)
+    w = workloads.Workload("fp8persist", 64, 8, 2, hd, 16, 600, ragged=True, table="pool", key=2500 + hd)
     c = build(w, lens=lens, with_cache=False)
     dev, host = dev_cache(c), host_cache(c)
     for pt in (32, 64):
