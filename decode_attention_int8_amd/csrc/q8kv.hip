@@ -1618,8 +1618,9 @@ __device__ __forceinline__ void q4_offset_fix(f32x4 (&acc)[Geo<HD>::BPL], const 
 // sequence's end exits at once.  Each wave holds one register tile; latency
 // is hidden by the other resident waves (one wave's loads overlap the
 // others' compute) and, on persistent int8 and FP8 grids, by the rolling
-// tile order below.  3 waves per SIMD fit hd 64 and 128 without spills; hd 256 keeps a
-// whole register file.
+// tile order below.  3 waves per SIMD fit hd 64 and the plain-order hd 128
+// kernels without spills (the q4_0 one with a few outside its tile loop);
+// hd 256 keeps a whole register file.
 enum GridMode { kPersistent = 0, kStatic = 1 };
 enum CodecKind { kQ8 = 0, kFp8 = 1, kQ40 = 2 };
 
