@@ -142,7 +142,7 @@ def _decimal_reference(c, b, h):
     return np.array(out)
 
 
-@pytest.mark.parametrize("hd,L,G", [(32, 1, 1), (32, 5, 2), (64, 8, 1), (64, 7, 2), (32, 8, 2)])
+@pytest.mark.parametrize("hd,L,G", [(32, 1, 1), (32, 5, 2), (64, 8, 1), (64, 7, 2), (32, 8, 2), (96, 6, 2)])
 def test_c6_brute_force_tiny(hd, L, G):
     w = workloads.Workload("bf", 2, 2 * G, 2, hd, 4, L, key=900 + hd + L + G)
     c = build(w, with_cache=False)

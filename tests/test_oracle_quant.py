@@ -174,7 +174,7 @@ def test_quantize_q_is_per_32_block():
     assert F(qsc[1, 2, 1]) == F(oracle.inv127()) and not qi[1, 2, 32:64].any()
 
 
-@pytest.mark.parametrize("hd,kv_bs,n_kv", [(128, 16, 2), (64, 64, 3), (256, 32, 1)])
+@pytest.mark.parametrize("hd,kv_bs,n_kv", [(128, 16, 2), (64, 64, 3), (256, 32, 1), (96, 16, 2)])
 def test_append_places_rows(hd, kv_bs, n_kv):
     rng = np.random.default_rng(4)
     nb, n = 7, 20
