@@ -146,3 +146,36 @@ def test_quest_max_blocks():
     check_selection(c, kmax, kmin, sel, sel_lens, 64)
     want = quest_decode(c.q, c.cache, sel, sel_lens, c.scale)
     assert float(np.abs(out - want).max()) <= TOL
+
+
+@pytest.mark.parametrize("hd", [96, 160])
+def test_decode_heads_padded_head_size(hd):
+    """q8kv_decode_attn_heads over per-kv-head block lists at head sizes
+    stored in padded pages (the QUEST selection itself takes 64, 128 or
+    256): each kv head keeps its own subset of the sequence's blocks, the
+    last block always kept, against the oracle over the same lists."""
+    lens = [300, 65, 1, 0, 130]
+    w = workloads.Workload("headspad", len(lens), 8, 2, hd, 16, max(lens), ragged=True, table="pool",
+                           key=3500 + hd)
+    c = build(w, lens=lens)
+    say(f"decode over per-head block lists hd={hd}")
+    cache = gpu_cache(c)
+    rng = np.random.default_rng(3500 + hd)
+    top = 8
+    sel = np.full((w.batch, w.n_kv, top), -1, np.int32)
+    sel_lens = np.zeros(w.batch, np.int32)
+    for b in range(w.batch):
+        nblk = -(-max(int(c.lens[b]), 0) // w.kv_bs)
+        if nblk == 0:
+            continue
+        keep = min(nblk, top)
+        last = (int(c.lens[b]) - 1) % w.kv_bs + 1
+        sel_lens[b] = (keep - 1) * w.kv_bs + last
+        for kh in range(w.n_kv):
+            js = sorted(rng.choice(nblk - 1, keep - 1, replace=False).tolist()) + [nblk - 1]
+            sel[b, kh, :keep] = c.table[b, js]
+    want = quest_decode(c.q, c.cache, sel, sel_lens, c.scale)
+    for pt in (0, 32):
+        got = q8.decode_attn_heads(to_dev(c.q), cache, to_dev(sel), to_dev(sel_lens), c.scale,
+                                   part_tokens=pt).cpu().numpy()
+        assert float(np.abs(got - want).max()) <= TOL
