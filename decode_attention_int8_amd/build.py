@@ -7,7 +7,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SRC = os.path.join(HERE, "csrc", "q8kv.hip")
 LIB = os.path.join(HERE, "libq8kv.so")
-HIPCC = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
+EXAMPLE_SRC = os.path.join(HERE, "csrc", "q8kv_example.c")
+EXAMPLE = os.path.join(HERE, "q8kv_example")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+HIPCC = os.path.join(ROCM, "bin", "hipcc")
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
@@ -39,5 +42,29 @@ def build(verbose=False):
     return LIB
 
 
+def example_command(out=EXAMPLE):
+    """The host compiler line of the plain C caller (csrc/q8kv_example.c),
+    linked against libq8kv.so (found next to the binary at run time) and the
+    HIP runtime."""
+    return ["gcc", "-std=c11", "-O2", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+            "-I", os.path.join(ROCM, "include"), "-I", os.path.join(ROOT, "include"), EXAMPLE_SRC,
+            "-L", os.path.join(ROCM, "lib"), "-lamdhip64", "-L", HERE, "-lq8kv",
+            "-Wl,-rpath," + os.path.join(ROCM, "lib"), "-Wl,-rpath,$ORIGIN", "-o", out]
+
+
+def build_example(verbose=False):
+    """Compile the C example against the built library (always recompiles)."""
+    tmp = EXAMPLE + ".tmp"
+    cmd = example_command(tmp)
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"gcc failed ({res.returncode}):\n{res.stderr}")
+    os.replace(tmp, EXAMPLE)
+    return EXAMPLE
+
+
 if __name__ == "__main__":
     build(verbose=True)
+    build_example(verbose=True)

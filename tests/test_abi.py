@@ -346,3 +346,20 @@ def test_load_probe_rejects_before_any_hip_call():
     assert p(n=60) == q8.Q8KV_EINVAL       # not a multiple of item_pages
     assert p(bs=16, item=4) == q8.Q8KV_EINVAL  # 64 tokens an item: not a multiple of 128
     assert p(n=0) == q8.Q8KV_EINVAL
+
+
+def test_header_and_c_caller_compile_as_c(tmp_path):
+    """include/q8kv.h is plain C: the C example that calls the library
+    compiles and links with gcc -std=c11 -Wall -Wextra -Werror."""
+    import importlib.util
+    import os
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not installed")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    spec = importlib.util.spec_from_file_location("_q8kv_build_c", os.path.join(root, "decode_attention_int8_amd", "build.py"))
+    b = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(b)
+    r = subprocess.run(b.example_command(str(tmp_path / "q8kv_example")), capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
