@@ -162,7 +162,10 @@ int q8kv_decode_attn_split(float* out, const float* q,
  * 8 bytes each.  A shape that needs more than 32 MiB is rejected with
  * Q8KV_EINVAL before any HIP call; q8kv_last_error() gives the bytes needed.
  * (Every one of the five benchmark workloads fits: the largest, 64
- * sequences of 64 query heads split in 8, needs about 17 MB.)
+ * sequences of 64 query heads split in 8, needs about 17 MB.)  After one
+ * call on a device (which looks up the array and the kernels' launch
+ * limits), the call can be captured into a HIP graph and replayed: it
+ * records kernels only.
  */
 int q8kv_decode_attn_noalloc(float* out, const float* q,
                              const int8_t* k_pages, const int8_t* v_pages,
