@@ -74,6 +74,9 @@ def parse():
     p.add_argument("--part-tokens", type=int, default=0, help="override the split plan (0: automatic)")
     p.add_argument("--load-probe", action="store_true",
                    help="also time the decode kernel's loads alone in three load orders (q8kv_debug_load_probe)")
+    p.add_argument("--item-timeline", action="store_true",
+                   help="per-item phases of the decode kernel (prologue, tile loop, end, gaps) from a stamped "
+                        "copy of the library")
     p.add_argument("--timeline", action="store_true",
                    help="instead of the benchmark: build a copy of the library whose decode kernel "
                         "stamps each workgroup's start, end of streaming and CU, and report the "
@@ -646,34 +649,152 @@ TIMELINE_EDITS = [
 ]
 
 
-def timeline_source(src):
-    for a, b in TIMELINE_EDITS:
+# Per-item wall-clock stamps for --item-timeline: the start of each of a
+# workgroup's first eight items, the end of its query prologue, the end of
+# its tile loop and the end of its merge, plus the item's number.
+ITEM_EDITS = [
+    ("struct DecodeArgs {",
+     "__device__ unsigned long long g_items[4096 * 8 * 6];\n"
+     "#define ISTAMP(p, val) do { if (threadIdx.x == 0 && blockIdx.x < 4096 && kst < 8) "
+     "g_items[(blockIdx.x * 8 + kst) * 6 + (p)] = (val); } while (0)\n"
+     "struct DecodeArgs {"),
+    ("    int item = blockIdx.x;\n", "    int item = blockIdx.x;\n    int kst = 0;\n"),
+    ("        int itid = tid;\n",
+     "        int itid = tid;\n        ISTAMP(0, __builtin_amdgcn_s_memrealtime());\n"
+     "        ISTAMP(5, (unsigned long long)item);\n"),
+    ("        } else {\n            __syncthreads();\n        }\n        // static grids: the tail wave quantises",
+     "        } else {\n            __syncthreads();\n        }\n        ISTAMP(1, __builtin_amdgcn_s_memrealtime());\n"
+     "        // static grids: the tail wave quantises"),
+    ("        const bool any_bad = __syncthreads_or(bad);\n",
+     "        const bool any_bad = __syncthreads_or(bad);\n        ISTAMP(2, __builtin_amdgcn_s_memrealtime());\n"),
+    ("        // next item (the barrier also keeps LDS from being reused too early)\n",
+     "        ISTAMP(3, __builtin_amdgcn_s_memrealtime());\n        ++kst;\n"
+     "        // next item (the barrier also keeps LDS from being reused too early)\n"),
+    ('extern "C" {\n',
+     'extern "C" {\n'
+     "int q8kv_items_read(unsigned long long* host, int n) {\n"
+     "    return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(g_items), sizeof(unsigned long long) * (size_t)n, 0,"
+     " hipMemcpyDeviceToHost);\n}\n"
+     "int q8kv_items_clear() {\n"
+     "    static unsigned long long z[4096 * 8 * 6];\n"
+     "    return (int)hipMemcpyToSymbol(HIP_SYMBOL(g_items), z, sizeof(z), 0, hipMemcpyHostToDevice);\n}\n"),
+]
+
+
+def stamped_source(src, edits):
+    for a, b in edits:
         if src.count(a) != 1:
-            raise RuntimeError(f"timeline anchor not found exactly once: {a[:40]!r}")
+            raise RuntimeError(f"stamp anchor not found exactly once: {a[:40]!r}")
         src = src.replace(a, b)
     return src
+
+
+def timeline_source(src):
+    return stamped_source(src, TIMELINE_EDITS)
+
+
+def items_source(src):
+    return stamped_source(src, ITEM_EDITS)
+
+
+def stamped_library(make_source):
+    """Build a copy of the library from make_source(kernel source) in a
+    temporary directory and make the binding call it; returns its handle."""
+    import ctypes
+    import importlib.util
+    import subprocess
+    import tempfile
+    import decode_attention_int8_amd as q8
+    spec = importlib.util.spec_from_file_location("_q8kv_build_tl", os.path.join(ROOT, "decode_attention_int8_amd", "build.py"))
+    b = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(b)
+    d = tempfile.mkdtemp(prefix="q8kv_stamped_")
+    srcp, libp = os.path.join(d, "q8kv_stamped.hip"), os.path.join(d, "libq8kv_stamped.so")
+    open(srcp, "w").write(make_source(open(b.SRC).read()))
+    log("building the stamped library copy")
+    subprocess.run([b.HIPCC] + b.FLAGS + [srcp, "-o", libp], check=True, capture_output=True)
+    q8.LIB_PATH = libp
+    q8.lib = q8._load()
+    return ctypes.CDLL(libp)
+
+
+def run_items(w, args):
+    """Per-item phases of the decode kernel from the stamped library copy:
+    for the last of 30 back-to-back calls, each item's query prologue, tile
+    loop and end (wave merge, state store, merge) and each workgroup's gap
+    between items, with the share of all workgroup time each takes."""
+    import ctypes
+    import torch
+    import decode_attention_int8_amd as q8
+    T = stamped_library(items_source)
+    g = build_gpu(w, torch.device("cuda", 0), args.cold_bytes, codecs=())
+    scale = workloads.softmax_scale(w.hd)
+    out = torch.empty_like(g["q"])
+    R = len(g["caches"])
+
+    def call(i):
+        q8.decode_attn(g["q"], g["caches"][i % R], g["table_d"], g["lens_d"], scale, out=out,
+                       part_tokens=args.part_tokens)
+
+    for i in range(50):
+        call(i)
+    torch.cuda.synchronize()
+    if T.q8kv_items_clear() != 0:
+        raise RuntimeError("stamp clear failed")
+    torch.cuda.synchronize()
+    for i in range(30):
+        call(i)
+    torch.cuda.synchronize()
+    n = 4096 * 8 * 6
+    st = np.zeros(n, np.uint64)
+    if T.q8kv_items_read(st.ctypes.data_as(ctypes.c_void_p), n) != 0:
+        raise RuntimeError("stamp read failed")
+    st = st.reshape(4096, 8, 6).astype(np.int64)
+    # slot 0 of a workgroup holds its first item of the last call; a later
+    # slot belongs to that call when it starts after the previous item ended
+    # and its four stamps are in order (the persistent loop stamps the start
+    # of the check that finds no item left, then leaves)
+    items = {}
+    for wg in range(4096):
+        if st[wg, 0, 0] <= 0:
+            continue
+        lst = []
+        for k in range(8):
+            s_ = st[wg, k]
+            ok = s_[0] <= s_[1] <= s_[2] <= s_[3] and (k == 0 or s_[0] >= lst[-1][3])
+            if not ok:
+                break
+            lst.append(s_[:4])
+        items[wg] = np.array(lst)
+    t0 = min(v[0, 0] for v in items.values())
+    ph = np.concatenate([np.diff(v, axis=1) for v in items.values()]) / 100.0
+    gaps = np.concatenate([(v[1:, 0] - v[:-1, 3]) for v in items.values() if len(v) > 1] or [np.zeros(0)]) / 100.0
+    ends = np.array([v[-1, 3] - t0 for v in items.values()]) / 100.0
+    starts = np.array([v[0, 0] - t0 for v in items.values()]) / 100.0
+    span = float(ends.max())
+    total = span * len(items)
+    q = lambda x, p: round(float(np.percentile(x, p)), 2) if len(x) else None
+    dist = lambda x: {"min": q(x, 0), "median": q(x, 50), "p90": q(x, 90), "max": q(x, 100)}
+    return {"workgroups": len(items), "items": int(len(ph)), "span_us": round(span, 2),
+            "items_per_workgroup": np.bincount([len(v) for v in items.values()]).tolist(),
+            "prologue_us": dist(ph[:, 0]), "tile_loop_us": dist(ph[:, 1]), "end_us": dist(ph[:, 2]),
+            "gap_us": dist(gaps), "workgroup_end_us": dist(ends),
+            "share_of_workgroup_time": {
+                "before_first_item": round(float(starts.sum()) / total, 4),
+                "prologue": round(float(ph[:, 0].sum()) / total, 4),
+                "tile_loop": round(float(ph[:, 1].sum()) / total, 4),
+                "end": round(float(ph[:, 2].sum()) / total, 4),
+                "gaps": round(float(gaps.sum()) / total, 4),
+                "idle_after_last_item": round(float((span - ends).sum()) / total, 4)}}
 
 
 def run_timeline(w, args):
     """Build the stamped copy of the library, run the workload's decode, and
     return the per-workgroup timeline (µs from the first workgroup's start)."""
     import ctypes
-    import importlib.util
-    import subprocess
-    import tempfile
     import torch
     import decode_attention_int8_amd as q8
-    spec = importlib.util.spec_from_file_location("_q8kv_build_tl", os.path.join(ROOT, "decode_attention_int8_amd", "build.py"))
-    b = importlib.util.module_from_spec(spec)
-    spec.loader.exec_module(b)
-    d = tempfile.mkdtemp(prefix="q8kv_timeline_")
-    srcp, libp = os.path.join(d, "q8kv_timeline.hip"), os.path.join(d, "libq8kv_timeline.so")
-    open(srcp, "w").write(timeline_source(open(b.SRC).read()))
-    log("building the stamped library copy")
-    subprocess.run([b.HIPCC] + b.FLAGS + [srcp, "-o", libp], check=True, capture_output=True)
-    q8.LIB_PATH = libp
-    q8.lib = q8._load()
-    T = ctypes.CDLL(libp)
+    T = stamped_library(timeline_source)
     g = build_gpu(w, torch.device("cuda", 0), args.cold_bytes, codecs=())
     scale = workloads.softmax_scale(w.hd)
     out = torch.empty_like(g["q"])
@@ -729,6 +850,11 @@ def main():
     q8.debug_set_stage(args.stage)
     w = workloads.WORKLOADS[args.workload]
     dev = torch.device("cuda", 0)
+    if args.item_timeline:
+        print(json.dumps({"items": run_items(w, args), "workload": w.name,
+                          "note": "µs; one workgroup's items of the last of 30 back-to-back calls (its first eight)"}),
+              flush=True)
+        return
     if args.timeline:
         print(json.dumps({"timeline": run_timeline(w, args), "workload": w.name,
                           "note": "µs from the first workgroup's start; stream_end = after the tile loop, "

@@ -106,3 +106,13 @@ def test_timeline_edits_apply_to_the_kernel_source():
     src = open(os.path.join(ROOT, "decode_attention_int8_amd", "csrc", "q8kv.hip")).read()
     out = bench.timeline_source(src)
     assert out.count("STAMP(") == 4 and "q8kv_timeline_read" in out
+
+
+def test_item_timeline_edits_apply_to_the_kernel_source():
+    """bench.py --item-timeline stamps a copy of the kernel source at fixed
+    points; each must still occur exactly once."""
+    sys.path.insert(0, ROOT)
+    import bench
+    src = open(os.path.join(ROOT, "decode_attention_int8_amd", "csrc", "q8kv.hip")).read()
+    out = bench.items_source(src)
+    assert out.count("ISTAMP(") == 6 and "q8kv_items_read" in out
