@@ -256,6 +256,19 @@ struct QOperand {
     float scl[Geo<HD>::NPAIR];  // scale of block 2p+bp of head g (times score_scale)
 };
 
+// Whether a tile has rows past the range (sub-tile 1 is never fuller than
+// sub-tile 0); the counts are wave-uniform, so the masking of such tiles is
+// a branch that whole tiles skip.
+__device__ __forceinline__ bool tile_is_partial(const int (&nval)[2]) {
+    return __builtin_amdgcn_readfirstlane(nval[1]) < kSub;
+}
+
+// The quantised query rows in LDS (kHeadGroup rows of HD codes) are followed
+// by kQZero zero bytes: a lane whose quarter of K lies in the other block of
+// the pair reads its operand from there, so every lane issues the same
+// unconditional 16-byte read.
+constexpr int kQZero = 16;
+
 template <int HD>
 __device__ __forceinline__ void load_q_operand(QOperand<HD>& Q, const int8_t* lq, const float* lqsc,
                                                int lane, float score_scale = 1.0f) {
@@ -263,12 +276,15 @@ __device__ __forceinline__ void load_q_operand(QOperand<HD>& Q, const int8_t* lq
 #pragma unroll
     for (int p = 0; p < Geo<HD>::NPAIR; ++p) {
         const int blk = 2 * p + bp;
-        if ((r >> 1) == bp)
-            Q.op[p] = *reinterpret_cast<const i32x4*>(lq + g * HD + kQBlock * blk + 16 * (r & 1));
-        else
-            Q.op[p] = i32x4{0, 0, 0, 0};
+        const int off = (r >> 1) == bp ? g * HD + kQBlock * blk + 16 * (r & 1) : kHeadGroup * HD;
+        Q.op[p] = *reinterpret_cast<const i32x4*>(lq + off);
         Q.scl[p] = lqsc[g * Geo<HD>::NB + blk] * score_scale;
     }
+}
+
+// zero the kQZero bytes after the query rows (before the first barrier)
+__device__ __forceinline__ void clear_q_zero(int8_t* lq_end, int tid) {
+    if (tid < kQZero / 4) reinterpret_cast<int*>(lq_end)[tid] = 0;
 }
 
 // Page byte order.  Each page (one physical block of one kv head, kv_bs
@@ -987,19 +1003,35 @@ __device__ __forceinline__ void tile_scores(const Tile<HD>& T, const int8_t* lq,
 #pragma unroll
             for (int p = 0; p < GG::NPAIR; ++p) part_s += (float)c[p][j] * Q.scl[p];
             const float full = part_s + dpp_row_ror8(part_s);  // add the other block parity
-            const float ksj = T.ks[st][j];
-            const float sv = full * ksj;
-            sc[st][j] = (4 * r + j) < T.nval[st] ? sv : -INFINITY;
-            mx = fmaxf(mx, sc[st][j]);
+            sc[st][j] = full * T.ks[st][j];
         }
     }
-    // the tile's largest V scale (valid rows; the 16 lanes of a row group
-    // share its rows) -> the exponent offset E
+    // the tile's largest V scale (the 16 lanes of a row group share its
+    // rows) -> the exponent offset E
     float vmx = 0.0f;
+    if (tile_is_partial(T.nval)) {
+        // rows past the range: score -inf, and their scale bytes (any bits)
+        // stay out of the maximum
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const bool in = (4 * r + j) < T.nval[st];
+                sc[st][j] = in ? sc[st][j] : -INFINITY;
+                vmx = fmaxf(vmx, in ? T.vs[st][j] : 0.0f);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) vmx = fmaxf(vmx, T.vs[st][j]);
+        }
+    }
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) vmx = fmaxf(vmx, (4 * r + j) < T.nval[st] ? T.vs[st][j] : 0.0f);
+        for (int j = 0; j < 4; ++j) mx = fmaxf(mx, sc[st][j]);
     }
     ts.mx = mx;
     ts.vmx = vmx;
@@ -1025,7 +1057,7 @@ __device__ __forceinline__ void tile_accumulate(const Tile<HD>& T, const TileSco
     M = m_new;
     E = e_new;
 
-    f16x8 aw;
+    float W[8];
     float wsum = 0.0f;
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
@@ -1033,12 +1065,23 @@ __device__ __forceinline__ void tile_accumulate(const Tile<HD>& T, const TileSco
         for (int j = 0; j < 4; ++j) {
             const float w = __builtin_amdgcn_exp2f(sc[st][j] - m_shift);
             wsum += w;
-            const float vsj = T.vs[st][j];
-            const float W = (4 * r + j) < T.nval[st] ? w * vsj : 0.0f;
-            const _Float16 hi = (_Float16)W;
-            const _Float16 lo = (_Float16)(W - (float)hi);
-            aw[4 * st + j] = n < 8 ? hi : lo;
+            W[4 * st + j] = w * T.vs[st][j];
         }
+    }
+    // rows past the range have w = 0 but may hold any scale bits
+    if (tile_is_partial(T.nval)) {
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) W[4 * st + j] = (4 * r + j) < T.nval[st] ? W[4 * st + j] : 0.0f;
+        }
+    }
+    f16x8 aw;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const _Float16 hi = (_Float16)W[k];
+        const _Float16 lo = (_Float16)(W[k] - (float)hi);
+        aw[k] = n < 8 ? hi : lo;
     }
     S = S * alpha + wsum;
 
@@ -1390,12 +1433,14 @@ template <int HD>
 struct Q4Tile {
     uint32_t k[2][Q4Geo<HD>::SW];
     uint32_t v[2][Q4Geo<HD>::SW];
-    uint32_t kd[2][Q4Geo<HD>::SCW];  // fp16 scales of rows 4r .. 4r+3, row-major
-    uint32_t vd[2][Q4Geo<HD>::SCW];
+    uint32_t kd[2][Q4Geo<HD>::SCW];  // fp16 K scales of rows 4r .. 4r+3, row-major
+    // fp16 V scales of rows 4r .. 4r+3 of the lane's own sub-tile: sub-tile 0
+    // for lanes n < 8, sub-tile 1 for lanes n >= 8 (see q4_tile_accumulate)
+    uint32_t vd[Q4Geo<HD>::SCW];
     int nval[2];
     // the fp16 scale of row 4r + j, 32-block blk, widened to fp32
     __device__ __forceinline__ float kscale(int st, int j, int blk) const { return half_at(kd[st], j, blk); }
-    __device__ __forceinline__ float vscale(int st, int j, int blk) const { return half_at(vd[st], j, blk); }
+    __device__ __forceinline__ float vscale(int j, int blk) const { return half_at(vd, j, blk); }
     static __device__ __forceinline__ float half_at(const uint32_t (&d)[Q4Geo<HD>::SCW], int j, int blk) {
         const int i = j * Q4Geo<HD>::NB + blk;
         return (float)__builtin_bit_cast(_Float16, (uint16_t)(d[i >> 1] >> (16 * (i & 1))));
@@ -1421,12 +1466,18 @@ __device__ __forceinline__ void q4_tile_load(Q4Tile<HD>& T, const DecodeArgs& a,
         base[st] = (((size_t)blk * a.n_kv + kh) << log2_pow2(a.kv_bs)) + (size_t)(tst & (a.kv_bs - 1));
         if constexpr (PART != 1) T.nval[st] = nval;
     }
+    if constexpr (PART != 2) {
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-        const size_t srow = (base[st] + 4 * (lane >> 4)) * QG::NB * 2;  // byte offset of row 4r's scales
-        if constexpr (PART != 2) load_dwords<QG::SCW>(T.kd[st], a.ks8 + srow);
-        if constexpr (PART != 1) load_dwords<QG::SCW>(T.vd[st], a.vs8 + srow);
-        if constexpr (PART == 0) {
+        for (int st = 0; st < 2; ++st)  // byte offset of row 4r's scales
+            load_dwords<QG::SCW>(T.kd[st], a.ks8 + (base[st] + 4 * (lane >> 4)) * QG::NB * 2);
+    }
+    if constexpr (PART != 1) {
+        const size_t vrow = (lane & 8) ? base[1] : base[0];  // the lane's own sub-tile
+        load_dwords<QG::SCW>(T.vd, a.vs8 + (vrow + 4 * (lane >> 4)) * QG::NB * 2);
+    }
+    if constexpr (PART == 0) {
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
             load_dwords<QG::SW>(T.k[st], a.kp + base[st] * (HD / 2) + (size_t)lane * QG::SLOT);
             load_dwords<QG::SW>(T.v[st], a.vp + base[st] * (HD / 2) + (size_t)lane * QG::SLOT);
         }
@@ -1484,10 +1535,20 @@ __device__ __forceinline__ void q4_tile_scores(const Q4Tile<HD>& T, const int8_t
 #pragma unroll
             for (int p = 0; p < GG::NPAIR; ++p)
                 part += (float)c[p][j] * __builtin_fmaf(Q.scl[p], T.kscale(st, j, 2 * p + bp), 0.0f);
-            const float full = part + dpp_row_ror8(part);  // add the other block parity
-            sc[st][j] = (4 * r + j) < T.nval[st] ? full : -INFINITY;
-            mx = fmaxf(mx, sc[st][j]);
+            sc[st][j] = part + dpp_row_ror8(part);  // add the other block parity
         }
+    }
+    if (tile_is_partial(T.nval)) {
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sc[st][j] = (4 * r + j) < T.nval[st] ? sc[st][j] : -INFINITY;
+        }
+    }
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mx = fmaxf(mx, sc[st][j]);
     }
     ts.mx = mx;
 }
@@ -1507,18 +1568,19 @@ __device__ __forceinline__ void q4_tile_accumulate(Q4Tile<HD>& T, const TileScor
     M = m_new;
     const float m_shift = m_new - kWeightShift;
 
-    // rows past the range have weight exactly 0 (exp2 of -inf)
-    float W[8];
-    float wsum = 0.0f;
+    // Lanes n and n + 8 carry the same head.  Each forms the weights of one
+    // sub-tile only (its own: 0 for n < 8, 1 for n >= 8) and the pair
+    // exchanges them below; rows past the range have weight exactly 0 (exp2
+    // of -inf).  Both lanes add the two sub-tiles' sums, so S stays equal.
+    const bool up = n >= 8;
+    float W[4];
+    float wown = 0.0f;
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            W[4 * st + j] = __builtin_amdgcn_exp2f(sc[st][j] - m_shift);
-            wsum += W[4 * st + j];
-        }
+    for (int j = 0; j < 4; ++j) {
+        W[j] = __builtin_amdgcn_exp2f((up ? sc[1][j] : sc[0][j]) - m_shift);
+        wown += W[j];
     }
-    S = S * alpha + wsum;
+    S = S * alpha + (wown + dpp_row_ror8(wown));
 
     if (__any(alpha != 1.0f)) {
         float arow[4];
@@ -1537,33 +1599,38 @@ __device__ __forceinline__ void q4_tile_accumulate(Q4Tile<HD>& T, const TileScor
     // sub-tile, which re-reads the first one's rows) may hold any scale
     // bytes: zero their V scales in the tile so that their zero weights stay
     // zero.
+    if (tile_is_partial(T.nval)) {
+        const int nv = up ? T.nval[1] : T.nval[0];
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-        if (T.nval[st] < kSub) {
-#pragma unroll
-            for (int i = 0; i < QG::SCW; ++i) {
-                const int j = 2 * i / QG::NB;  // row 4r + j of dword i
-                T.vd[st][i] = (4 * r + j) < T.nval[st] ? T.vd[st][i] : 0u;
-            }
+        for (int i = 0; i < QG::SCW; ++i) {
+            const int j = 2 * i / QG::NB;  // row 4r + j of dword i
+            T.vd[i] = (4 * r + j) < nv ? T.vd[i] : 0u;
         }
     }
 
-    // weight rows: lanes n < 8 carry bf16(x), lanes n >= 8 the remainder
-    // bf16(x - bf16(x)); a lane of the first kind subtracts zero
-    const uint32_t lo_sel = n < 8 ? 0x0c0c0c0cu : 0x01000c0cu;  // v_perm: (t << 16) or 0
-    const uint32_t lo_mask = n < 8 ? 0u : 0xffff0000u;
+    // A rows of the P.V matrices: lanes n < 8 carry the bf16 weights x of
+    // both sub-tiles (dwords 0-1: sub-tile 0, rows 4r .. 4r+3 in pairs;
+    // dwords 2-3: sub-tile 1), lanes n >= 8 the remainders bf16(x - bf16(x)).
+    // A lane rounds its own sub-tile's x both ways; a DPP move (row rotation
+    // by 8, written only to the lanes of the other half) fetches the
+    // partner's half of the operand.
 #pragma unroll
     for (int b = 0; b < QG::NB; ++b) {
+        uint32_t hi[2], lo[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const float x0 = __builtin_fmaf(W[2 * i], T.vscale(2 * i, b), 0.0f);
+            const float x1 = __builtin_fmaf(W[2 * i + 1], T.vscale(2 * i + 1, b), 0.0f);
+            hi[i] = pack_bf16x2(x0, x1);
+            lo[i] = pack_bf16x2(x0 - __uint_as_float(hi[i] << 16), x1 - __uint_as_float(hi[i] & 0xffff0000u));
+        }
         uint32_t aw[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int k0 = 2 * i, k1 = 2 * i + 1;
-            const float x0 = __builtin_fmaf(W[k0], T.vscale(k0 >> 2, k0 & 3, b), 0.0f);
-            const float x1 = __builtin_fmaf(W[k1], T.vscale(k1 >> 2, k1 & 3, b), 0.0f);
-            const uint32_t t = pack_bf16x2(x0, x1);
-            const float h0 = __uint_as_float(__builtin_amdgcn_perm(t, t, lo_sel));
-            const float h1 = __uint_as_float(t & lo_mask);
-            aw[i] = pack_bf16x2(x0 - h0, x1 - h1);
+        for (int i = 0; i < 2; ++i) {
+            // banks 2-3 (lanes 8-15 of each row) take the partner's remainder
+            aw[i] = __builtin_amdgcn_update_dpp(hi[i], lo[i], 0x128, 0xf, 0xc, false);
+            // banks 0-1 (lanes 0-7) take the partner's hi weights
+            aw[2 + i] = __builtin_amdgcn_update_dpp(lo[i], hi[i], 0x128, 0xf, 0x3, false);
         }
         const bf16x8 awv = __builtin_bit_cast(bf16x8, aw);
         // this block's weight sums go to column b of the sums matrix
@@ -1656,7 +1723,7 @@ q8kv_decode_kernel(const DecodeArgs a) {
     constexpr bool STAGE = STG;
     static_assert(!STG || (CODEC == kQ8 && STATIC && HD <= 128), "staged tiles: int8 static grids at hd 64 / 128");
     using SG = Stage<HD>;
-    __shared__ __attribute__((aligned(16))) int8_t lq[FP8 ? 16 : kHeadGroup * HD];
+    __shared__ __attribute__((aligned(16))) int8_t lq[FP8 ? 16 : kHeadGroup * HD + kQZero];
     __shared__ float lqsc[FP8 ? 1 : kHeadGroup * GG::NB];
     __shared__ int lqsum[Q40 ? kHeadGroup * GG::NB : 1];  // q4_0: query block code sums
     __shared__ __attribute__((aligned(16))) _Float16 lq16[FP8 ? 2 * kHeadGroup * HD : 8];  // FP8: query hi, lo rows
@@ -1693,6 +1760,7 @@ q8kv_decode_kernel(const DecodeArgs a) {
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int G = a.group;
     const int cap = a.max_blocks * a.kv_bs;
+    if constexpr (!FP8) clear_q_zero(lq + kHeadGroup * HD, tid);
 
     // Persistent grids number their items longest first, so that the ones
     // handed out last are short and the grid drains evenly: every full
@@ -2958,9 +3026,10 @@ struct DotsArgs {
 template <int HD>
 __global__ __launch_bounds__(kThreads) void q8kv_debug_dots_kernel(const DotsArgs a) {
     using GG = Geo<HD>;
-    __shared__ __attribute__((aligned(16))) int8_t lq[kHeadGroup * HD];
+    __shared__ __attribute__((aligned(16))) int8_t lq[kHeadGroup * HD + kQZero];
     __shared__ float lqsc[kHeadGroup * GG::NB];
     const int tid = threadIdx.x, lane = tid & 63;
+    clear_q_zero(lq + kHeadGroup * HD, tid);
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int kh = blockIdx.x % a.n_kv, b = blockIdx.x / a.n_kv;
     const int G = a.group;
