@@ -1438,12 +1438,30 @@ struct Q4Tile {
     // for lanes n < 8, sub-tile 1 for lanes n >= 8 (see q4_tile_accumulate)
     uint32_t vd[Q4Geo<HD>::SCW];
     int nval[2];
-    // the fp16 scale of row 4r + j, 32-block blk, widened to fp32
-    __device__ __forceinline__ float kscale(int st, int j, int blk) const { return half_at(kd[st], j, blk); }
+    // the fp16 V scale of row 4r + j, 32-block blk, widened to fp32
     __device__ __forceinline__ float vscale(int j, int blk) const { return half_at(vd, j, blk); }
     static __device__ __forceinline__ float half_at(const uint32_t (&d)[Q4Geo<HD>::SCW], int j, int blk) {
         const int i = j * Q4Geo<HD>::NB + blk;
         return (float)__builtin_bit_cast(_Float16, (uint16_t)(d[i >> 1] >> (16 * (i & 1))));
+    }
+    // The K scales of row 4r + j, sub-tile st, for the blocks 2p + bp (p =
+    // 0 .. NB/2 - 1) of the lane's block parity bp.  Row j's scales are NB/2
+    // dwords, dword p holding blocks 2p and 2p + 1; one v_perm (sel
+    // 0x05040100 for bp = 0, 0x07060302 for bp = 1) gathers the lane's two
+    // halves from dwords p and p + 1, so the conversions read fixed halves.
+    __device__ __forceinline__ void kscales(int st, int j, int bp, uint32_t sel,
+                                            float (&ks)[Q4Geo<HD>::NB / 2]) const {
+        constexpr int W = Q4Geo<HD>::NB / 2;
+        if constexpr (W == 1) {
+            ks[0] = half_at(kd[st], j, bp);
+        } else {
+#pragma unroll
+            for (int p = 0; p < W; p += 2) {
+                const uint32_t d = __builtin_amdgcn_perm(kd[st][j * W + p + 1], kd[st][j * W + p], sel);
+                ks[p] = (float)__builtin_bit_cast(_Float16, (uint16_t)d);
+                ks[p + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(d >> 16));
+            }
+        }
     }
 };
 
@@ -1517,6 +1535,7 @@ __device__ __forceinline__ void q4_tile_scores(const Q4Tile<HD>& T, const int8_t
     int qs8[GG::NPAIR];
 #pragma unroll
     for (int p = 0; p < GG::NPAIR; ++p) qs8[p] = -8 * lqsum[g * GG::NB + 2 * p + bp];
+    const uint32_t ksel = bp ? 0x07060302u : 0x05040100u;
     float (&sc)[2][4] = ts.sc;
     float mx = -INFINITY;
 #pragma unroll
@@ -1531,10 +1550,11 @@ __device__ __forceinline__ void q4_tile_scores(const Q4Tile<HD>& T, const int8_t
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
+            float ks[GG::NPAIR];
+            T.kscales(st, j, bp, ksel, ks);
             float part = 0.0f;
 #pragma unroll
-            for (int p = 0; p < GG::NPAIR; ++p)
-                part += (float)c[p][j] * __builtin_fmaf(Q.scl[p], T.kscale(st, j, 2 * p + bp), 0.0f);
+            for (int p = 0; p < GG::NPAIR; ++p) part += (float)c[p][j] * __builtin_fmaf(Q.scl[p], ks[p], 0.0f);
             sc[st][j] = part + dpp_row_ror8(part);  // add the other block parity
         }
     }
@@ -1682,10 +1702,10 @@ __device__ __forceinline__ void q4_offset_fix(f32x4 (&acc)[Geo<HD>::BPL], const 
 // LDS from seq_lens, and each workgroup takes its next item from an atomic
 // ticket.  kStatic: one workgroup per (sequence, kv head, partition) slot of
 // the shape's upper bound, read straight off blockIdx; a slot past its
-// sequence's end exits at once.  Each wave holds one register tile; latency
-// is hidden by the other resident waves (one wave's loads overlap the
-// others' compute) and, on persistent int8 and FP8 grids, by the rolling
-// tile order below.  3 waves per SIMD fit hd 64 and the plain-order hd 128
+// sequence's end exits at once.  Each wave holds one register tile (two on
+// static q4_0 grids, below); latency is hidden by the other resident waves
+// (one wave's loads overlap the others' compute) and, on persistent int8 and
+// FP8 grids, by the rolling tile order below.  3 waves per SIMD fit hd 64 and the plain-order hd 128
 // kernels without spills (the q4_0 one with a few outside its tile loop);
 // hd 256 keeps a whole register file.
 enum GridMode { kPersistent = 0, kStatic = 1 };
@@ -1704,12 +1724,27 @@ constexpr int kRollWavesPerEu = 2;
 constexpr bool decode_rolls(int mode, int codec, bool stg) {
     return !stg && (codec == kQ8 || codec == kFp8) && (mode == kStatic ? kRollStatic : kRollPersistent);
 }
-constexpr int decode_waves_per_eu(int hd, int mode, int codec, bool stg) {
-    return hd == 256 ? 1 : stg ? 2 : (hd == 128 && decode_rolls(mode, codec, stg)) ? kRollWavesPerEu : 3;
+// Static q4_0 grids of 4-wave workgroups at hd 64 and 128 keep two register
+// tiles per wave: tile ts is computed while tile ts + stride streams, and
+// its registers are refilled with tile ts + 2 strides right after.  The
+// second tile takes the hd-128 kernel to two waves per SIMD.  Measured
+// against the plain order at three: GQA batch 37.7 -> 34.6 us, 128K 25.1 ->
+// 24.2 us; the persistent grid (ragged) was unchanged and the 8-wave grid
+// of the 7B-like step slower (12.1 -> 12.6 us), so both keep the plain order.
+constexpr bool kQ4DeepPersistent = false;
+constexpr bool kQ4DeepStatic = true;
+constexpr bool decode_deep(int hd, int mode, int codec, bool stg, int nw) {
+    return !stg && codec == kQ40 && hd <= 128 && nw == 4 && (mode == kStatic ? kQ4DeepStatic : kQ4DeepPersistent);
+}
+constexpr int decode_waves_per_eu(int hd, int mode, int codec, bool stg, int nw) {
+    return hd == 256 ? 1
+           : stg     ? 2
+           : (hd == 128 && (decode_rolls(mode, codec, stg) || decode_deep(hd, mode, codec, stg, nw))) ? kRollWavesPerEu
+                                                                                                       : 3;
 }
 
 template <int HD, int MODE, bool NEW, int CODEC = kQ8, int NW = kWaves, bool STG = false>
-__global__ __launch_bounds__(kWave * NW) __attribute__((amdgpu_waves_per_eu(decode_waves_per_eu(HD, MODE, CODEC, STG)))) void
+__global__ __launch_bounds__(kWave * NW) __attribute__((amdgpu_waves_per_eu(decode_waves_per_eu(HD, MODE, CODEC, STG, NW)))) void
 q8kv_decode_kernel(const DecodeArgs a) {
     using GG = Geo<HD>;
     constexpr int NT = kWave * NW;  // threads per workgroup
@@ -1953,8 +1988,10 @@ q8kv_decode_kernel(const DecodeArgs a) {
         }
 
         // Start streaming the wave's first tile (staged: its first kRing
-        // tiles) before the query prologue.
+        // tiles; q4_0 deep pipeline: its first two) before the query prologue.
+        constexpr bool DEEP = decode_deep(HD, MODE, CODEC, STAGE, NW);
         TileT A;
+        TileT B;  // the deep pipeline's second tile
         int8_t* const ring = lring + wid * kRing * SG::SLOT;  // staged: the wave's ring
         int slot = 0;
         if constexpr (STAGE) {
@@ -1981,6 +2018,15 @@ q8kv_decode_kernel(const DecodeArgs a) {
             } else if constexpr (Q40) {
                 q4_tile_load<HD, 1>(A, a, blk0, kh, own ? ts : t0, t1, ilane, bad);
                 q4_tile_load<HD, 2>(A, a, blk0, kh, own ? ts : t0, t1, ilane, bad);
+                if constexpr (DEEP) {
+                    // (a wave with fewer than two tiles loads the item's
+                    // first one here, unused, so that every path has the
+                    // same loads in flight)
+                    const int tb = ts + kStride < t1 ? ts + kStride : t0;
+                    int blk[2];
+                    tile_blocks(trow, tb, a.kv_bs, a.max_blocks, blk);
+                    q4_tile_load<HD>(B, a, blk, kh, tb, t1, ilane, bad);
+                }
             } else {
                 // K half first, as the tile loop issues them (the first
                 // scores then wait for the same count of later loads)
@@ -2077,7 +2123,40 @@ q8kv_decode_kernel(const DecodeArgs a) {
                 }
             }
         }
-        while (!ROLL && ts < t1) {
+        if constexpr (DEEP) {
+            // Two tiles in flight: A holds the wave's tile i, B tile i + 1.
+            // While four or more remain, compute A and refill it with tile
+            // i + 2, then the same for B; every load in the loop is
+            // unconditional, so each compute waits only for its own tile.
+            int n = ts < t1 ? (t1 - ts + kStride - 1) / kStride : 0;
+            while (n >= 4) {
+                q4_tile_compute<HD>(A, lq, lqsc, lqsum, a.scale_log2, acc, wsums, M, S, ilane);
+                int blk[2];
+                tile_blocks(trow, ts + 2 * kStride, a.kv_bs, a.max_blocks, blk);
+                q4_tile_load<HD>(A, a, blk, kh, ts + 2 * kStride, t1, ilane, bad);
+                // (keep the scheduler from starting B's compute, which waits
+                // for B's loads, ahead of A's refill)
+                __builtin_amdgcn_sched_barrier(0);
+                q4_tile_compute<HD>(B, lq, lqsc, lqsum, a.scale_log2, acc, wsums, M, S, ilane);
+                tile_blocks(trow, ts + 3 * kStride, a.kv_bs, a.max_blocks, blk);
+                q4_tile_load<HD>(B, a, blk, kh, ts + 3 * kStride, t1, ilane, bad);
+                __builtin_amdgcn_sched_barrier(0);
+                ts += 2 * kStride;
+                n -= 2;
+            }
+            // the last one to three tiles
+            if (n >= 1) {
+                q4_tile_compute<HD>(A, lq, lqsc, lqsum, a.scale_log2, acc, wsums, M, S, ilane);
+                if (n == 3) {
+                    int blk[2];
+                    tile_blocks(trow, ts + 2 * kStride, a.kv_bs, a.max_blocks, blk);
+                    q4_tile_load<HD>(A, a, blk, kh, ts + 2 * kStride, t1, ilane, bad);
+                }
+            }
+            if (n >= 2) q4_tile_compute<HD>(B, lq, lqsc, lqsum, a.scale_log2, acc, wsums, M, S, ilane);
+            if (n == 3) q4_tile_compute<HD>(A, lq, lqsc, lqsum, a.scale_log2, acc, wsums, M, S, ilane);
+        }
+        while (!ROLL && !DEEP && ts < t1) {
             if constexpr (STAGE) {
                 // the slot's tile, once its loads have landed (those of the
                 // tiles issued after it may stay in flight); the slot is
