@@ -1731,20 +1731,26 @@ constexpr bool decode_rolls(int mode, int codec, bool stg) {
 // against the plain order at three: GQA batch 37.7 -> 34.6 us, 128K 25.1 ->
 // 24.2 us; the persistent grid (ragged) was unchanged and the 8-wave grid
 // of the 7B-like step slower (12.1 -> 12.6 us), so both keep the plain order.
+// The int8 static kernels were slower with the second tile (128K 29.8 ->
+// 30.2-30.6 us, GQA batch 50.8 -> 51.2-51.4 us): their streaming already
+// runs at a plain read's pace.
 constexpr bool kQ4DeepPersistent = false;
 constexpr bool kQ4DeepStatic = true;
-constexpr bool decode_deep(int hd, int mode, int codec, bool stg, int nw) {
-    return !stg && codec == kQ40 && hd <= 128 && nw == 4 && (mode == kStatic ? kQ4DeepStatic : kQ4DeepPersistent);
+constexpr bool kI8DeepStatic = false;
+constexpr bool decode_deep(int hd, int mode, int codec, bool stg, int nw, bool knew) {
+    return !stg && hd <= 128 && nw == 4 && mode == kStatic &&
+           ((codec == kQ40 && kQ4DeepStatic) || (codec == kQ8 && !knew && kI8DeepStatic));
 }
-constexpr int decode_waves_per_eu(int hd, int mode, int codec, bool stg, int nw) {
+constexpr int decode_waves_per_eu(int hd, int mode, int codec, bool stg, int nw, bool knew) {
     return hd == 256 ? 1
            : stg     ? 2
-           : (hd == 128 && (decode_rolls(mode, codec, stg) || decode_deep(hd, mode, codec, stg, nw))) ? kRollWavesPerEu
-                                                                                                       : 3;
+           : (hd == 128 && (decode_rolls(mode, codec, stg) || decode_deep(hd, mode, codec, stg, nw, knew)))
+               ? kRollWavesPerEu
+               : 3;
 }
 
 template <int HD, int MODE, bool NEW, int CODEC = kQ8, int NW = kWaves, bool STG = false>
-__global__ __launch_bounds__(kWave * NW) __attribute__((amdgpu_waves_per_eu(decode_waves_per_eu(HD, MODE, CODEC, STG, NW)))) void
+__global__ __launch_bounds__(kWave * NW) __attribute__((amdgpu_waves_per_eu(decode_waves_per_eu(HD, MODE, CODEC, STG, NW, NEW)))) void
 q8kv_decode_kernel(const DecodeArgs a) {
     using GG = Geo<HD>;
     constexpr int NT = kWave * NW;  // threads per workgroup
@@ -1989,7 +1995,7 @@ q8kv_decode_kernel(const DecodeArgs a) {
 
         // Start streaming the wave's first tile (staged: its first kRing
         // tiles; q4_0 deep pipeline: its first two) before the query prologue.
-        constexpr bool DEEP = decode_deep(HD, MODE, CODEC, STAGE, NW);
+        constexpr bool DEEP = decode_deep(HD, MODE, CODEC, STAGE, NW, NEW);
         TileT A;
         TileT B;  // the deep pipeline's second tile
         int8_t* const ring = lring + wid * kRing * SG::SLOT;  // staged: the wave's ring
@@ -2018,20 +2024,21 @@ q8kv_decode_kernel(const DecodeArgs a) {
             } else if constexpr (Q40) {
                 q4_tile_load<HD, 1>(A, a, blk0, kh, own ? ts : t0, t1, ilane, bad);
                 q4_tile_load<HD, 2>(A, a, blk0, kh, own ? ts : t0, t1, ilane, bad);
-                if constexpr (DEEP) {
-                    // (a wave with fewer than two tiles loads the item's
-                    // first one here, unused, so that every path has the
-                    // same loads in flight)
-                    const int tb = ts + kStride < t1 ? ts + kStride : t0;
-                    int blk[2];
-                    tile_blocks(trow, tb, a.kv_bs, a.max_blocks, blk);
-                    q4_tile_load<HD>(B, a, blk, kh, tb, t1, ilane, bad);
-                }
             } else {
                 // K half first, as the tile loop issues them (the first
                 // scores then wait for the same count of later loads)
                 tile_load<HD, 1>(A, a, blk0, kh, own ? ts : t0, t1, ilane, bad);
                 tile_load<HD, 2>(A, a, blk0, kh, own ? ts : t0, t1, ilane, bad);
+            }
+            if constexpr (DEEP) {
+                // (a wave with fewer than two tiles loads the item's first
+                // one here, unused, so that every path has the same loads in
+                // flight)
+                const int tb = ts + kStride < t1 ? ts + kStride : t0;
+                int blk[2];
+                tile_blocks(trow, tb, a.kv_bs, a.max_blocks, blk);
+                if constexpr (Q40) q4_tile_load<HD>(B, a, blk, kh, tb, t1, ilane, bad);
+                else tile_load<HD>(B, a, blk, kh, tb, t1, ilane, bad);
             }
         }
         if constexpr (NEW && STATIC) {
@@ -2128,33 +2135,36 @@ q8kv_decode_kernel(const DecodeArgs a) {
             // While four or more remain, compute A and refill it with tile
             // i + 2, then the same for B; every load in the loop is
             // unconditional, so each compute waits only for its own tile.
+            auto compute = [&](TileT& T) {
+                if constexpr (Q40) q4_tile_compute<HD>(T, lq, lqsc, lqsum, a.scale_log2, acc, wsums, M, S, ilane);
+                else tile_compute<HD>(T, lq, lqsc, a.scale_log2, acc, M, S, E, ilane);
+            };
+            auto refill = [&](TileT& T, int t) {
+                int blk[2];
+                tile_blocks(trow, t, a.kv_bs, a.max_blocks, blk);
+                if constexpr (Q40) q4_tile_load<HD>(T, a, blk, kh, t, t1, ilane, bad);
+                else tile_load<HD>(T, a, blk, kh, t, t1, ilane, bad);
+            };
             int n = ts < t1 ? (t1 - ts + kStride - 1) / kStride : 0;
             while (n >= 4) {
-                q4_tile_compute<HD>(A, lq, lqsc, lqsum, a.scale_log2, acc, wsums, M, S, ilane);
-                int blk[2];
-                tile_blocks(trow, ts + 2 * kStride, a.kv_bs, a.max_blocks, blk);
-                q4_tile_load<HD>(A, a, blk, kh, ts + 2 * kStride, t1, ilane, bad);
+                compute(A);
+                refill(A, ts + 2 * kStride);
                 // (keep the scheduler from starting B's compute, which waits
                 // for B's loads, ahead of A's refill)
                 __builtin_amdgcn_sched_barrier(0);
-                q4_tile_compute<HD>(B, lq, lqsc, lqsum, a.scale_log2, acc, wsums, M, S, ilane);
-                tile_blocks(trow, ts + 3 * kStride, a.kv_bs, a.max_blocks, blk);
-                q4_tile_load<HD>(B, a, blk, kh, ts + 3 * kStride, t1, ilane, bad);
+                compute(B);
+                refill(B, ts + 3 * kStride);
                 __builtin_amdgcn_sched_barrier(0);
                 ts += 2 * kStride;
                 n -= 2;
             }
             // the last one to three tiles
             if (n >= 1) {
-                q4_tile_compute<HD>(A, lq, lqsc, lqsum, a.scale_log2, acc, wsums, M, S, ilane);
-                if (n == 3) {
-                    int blk[2];
-                    tile_blocks(trow, ts + 2 * kStride, a.kv_bs, a.max_blocks, blk);
-                    q4_tile_load<HD>(A, a, blk, kh, ts + 2 * kStride, t1, ilane, bad);
-                }
+                compute(A);
+                if (n == 3) refill(A, ts + 2 * kStride);
             }
-            if (n >= 2) q4_tile_compute<HD>(B, lq, lqsc, lqsum, a.scale_log2, acc, wsums, M, S, ilane);
-            if (n == 3) q4_tile_compute<HD>(A, lq, lqsc, lqsum, a.scale_log2, acc, wsums, M, S, ilane);
+            if (n >= 2) compute(B);
+            if (n == 3) compute(A);
         }
         while (!ROLL && !DEEP && ts < t1) {
             if constexpr (STAGE) {
