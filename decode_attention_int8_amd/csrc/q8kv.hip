@@ -2593,6 +2593,15 @@ __device__ __forceinline__ float row16_reduce_xor(float (&v)[16]) {
 // the 16 rows of a DPP row (row16_reduce_xor), and lane n of each row writes
 // column 64 c + 16 r + n.  Rows past the sequence's length read its last row
 // again (every load is issued, and a repeat changes no maximum or minimum).
+// (x & m) | (y & ~m) as one v_bfi_b32.  Written out, a select between two
+// elements of a register vector under a lane mask is turned by the compiler
+// into a four-way choice over the whole vector (three selects per dword).
+__device__ __forceinline__ uint32_t bit_select(uint32_t m, uint32_t x, uint32_t y) {
+    uint32_t r;
+    asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "v"(m), "v"(x), "v"(y));
+    return r;
+}
+
 template <int HD, int NSUB>
 __global__ __launch_bounds__(256) void q8kv_quest_metadata_kernel(const QuestArgs a) {
     constexpr int NPAIR = Geo<HD>::NPAIR;
@@ -2612,8 +2621,11 @@ __global__ __launch_bounds__(256) void q8kv_quest_metadata_kernel(const QuestArg
     const int rows = min(a.kv_bs, L - j * a.kv_bs);
     const int last_sub = (rows - 1) & ~(kSub - 1);  // first row of the last sub-tile in use
     const int n = lane & 15, r = lane >> 4;
-    const uint32_t bsel = 0x03020100u ^ ((uint32_t)(n & 3) * 0x01010101u);  // byte e <- byte e ^ (n & 3)
-    const bool dx1 = (n & 4) != 0, dx2 = (n & 8) != 0;                         // dword D <- dword D ^ (n >> 2)
+    // slot s of a lane's 16 columns <- column s ^ n: dword D <- dword D ^ (n >> 2) (bit 3 of n by
+    // selects, bit 2 by the choice of v_perm operand) and byte e <- byte e ^ (n & 3)
+    const uint32_t psel = (0x03020100u ^ ((uint32_t)(n & 3) * 0x01010101u)) + ((n & 4) ? 0x04040404u : 0u);
+    // all ones where bit 3 of n is set: the mask of the bitfield selects below
+    const uint32_t dx2 = (n & 8) ? 0xffffffffu : 0u;
     float mx[NPAIR][16], mn[NPAIR][16];
 #pragma unroll
     for (int c = 0; c < NPAIR; ++c) {
@@ -2644,10 +2656,10 @@ __global__ __launch_bounds__(256) void q8kv_quest_metadata_kernel(const QuestArg
             for (int u = 0; u < NSUB; ++u) {
                 uint32_t t[4];
 #pragma unroll
-                for (int d = 0; d < 4; ++d) t[d] = dx1 ? (uint32_t)ch[u][c][d ^ 1] : (uint32_t)ch[u][c][d];
+                for (int d = 0; d < 4; ++d) t[d] = bit_select(dx2, (uint32_t)ch[u][c][d ^ 2], (uint32_t)ch[u][c][d]);
+                // perm(x, y, sel): selector bytes 0-3 pick bytes of y, 4-7 bytes of x
 #pragma unroll
-                for (int d = 0; d < 4; ++d)
-                    cu[u][d] = __builtin_amdgcn_perm(0u, dx2 ? t[d ^ 2] : t[d], bsel) ^ 0x80808080u;
+                for (int d = 0; d < 4; ++d) cu[u][d] = __builtin_amdgcn_perm(t[d ^ 1], t[d], psel) ^ 0x80808080u;
             }
             // code * sc as fma(code + 128, sc, -128 sc): the byte with its
             // sign bit flipped converts to code + 128 in one instruction, and
