@@ -2602,96 +2602,173 @@ __device__ __forceinline__ uint32_t bit_select(uint32_t m, uint32_t x, uint32_t 
     return r;
 }
 
+// A metadata wave's registers for NSUB sub-tiles of one page: each lane holds
+// row n's 16 columns of every 64-column chunk (the decode kernel's K loads)
+// and that row's scale.
 template <int HD, int NSUB>
-__global__ __launch_bounds__(256) void q8kv_quest_metadata_kernel(const QuestArgs a) {
-    constexpr int NPAIR = Geo<HD>::NPAIR;
-    const int lane = threadIdx.x & (kWave - 1);
-    const long long wave = (long long)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (wave >= (long long)a.batch * a.max_blocks * a.n_kv) return;
-    const int kh = (int)(wave % a.n_kv);
-    const int j = (int)((wave / a.n_kv) % a.max_blocks);
-    const int b = (int)(wave / ((long long)a.n_kv * a.max_blocks));
-    // the length and the table entry are read together (j < max_blocks, so
-    // the entry is inside the table whether or not the block is in use)
-    const int len = uniform_read(a.lens, b);
-    const int p = uniform_read(a.table + (size_t)b * a.max_blocks, j);
-    const int L = min(len, a.max_blocks * a.kv_bs);
-    if (j * a.kv_bs >= L) return;
-    if ((unsigned)p >= (unsigned)a.num_blocks) return;
-    const int rows = min(a.kv_bs, L - j * a.kv_bs);
-    const int last_sub = (rows - 1) & ~(kSub - 1);  // first row of the last sub-tile in use
+struct MetaPage {
+    i32x4 ch[NSUB][Geo<HD>::NPAIR];
+    float sc[NSUB];
+};
+
+// Rows r0 .. r0 + 16 NSUB - 1 of a page whose first `rows` rows are in use;
+// a sub-tile past them repeats the last one (a repeat changes no maximum or
+// minimum), and rows past them inside it re-read the last row.
+template <int HD, int NSUB>
+__device__ __forceinline__ void meta_load(MetaPage<HD, NSUB>& P, const QuestArgs& a, size_t page_row, int rows,
+                                          int r0, int lane) {
     const int n = lane & 15, r = lane >> 4;
-    // slot s of a lane's 16 columns <- column s ^ n: dword D <- dword D ^ (n >> 2) (bit 3 of n by
-    // selects, bit 2 by the choice of v_perm operand) and byte e <- byte e ^ (n & 3)
-    const uint32_t psel = (0x03020100u ^ ((uint32_t)(n & 3) * 0x01010101u)) + ((n & 4) ? 0x04040404u : 0u);
-    // all ones where bit 3 of n is set: the mask of the bitfield selects below
-    const uint32_t dx2 = (n & 8) ? 0xffffffffu : 0u;
-    float mx[NPAIR][16], mn[NPAIR][16];
+    const int last_sub = (rows - 1) & ~(kSub - 1);  // first row of the last sub-tile in use
 #pragma unroll
-    for (int c = 0; c < NPAIR; ++c) {
+    for (int u = 0; u < NSUB; ++u) {
+        const int rs = min(r0 + u * kSub, last_sub);
+        const int rn = min(n, rows - 1 - rs);
+        P.sc[u] = a.ks[page_row + rs + rn];
+        load_k_subtile<HD>(P.ch[u], a.kp, page_row + rs, 16 * r + rn);
+    }
+}
+
+// Folds the loaded rows into the running column maxima and minima.  Slot s
+// of a lane's 16 columns takes column s ^ n: dword D <- dword D ^ (n >> 2)
+// (bit 3 of n by bitfield selects under the mask dx2, bit 2 by the choice of
+// v_perm operand) and byte e <- byte e ^ (n & 3) (the selector psel).
+template <int HD, int NSUB>
+__device__ __forceinline__ void meta_fold(const MetaPage<HD, NSUB>& P, float (&mx)[Geo<HD>::NPAIR][16],
+                                          float (&mn)[Geo<HD>::NPAIR][16], uint32_t psel, uint32_t dx2) {
+    float off[NSUB];
+#pragma unroll
+    for (int u = 0; u < NSUB; ++u) off[u] = -128.0f * P.sc[u];  // exact
+#pragma unroll
+    for (int c = 0; c < Geo<HD>::NPAIR; ++c) {
+        uint32_t cu[NSUB][4];
+#pragma unroll
+        for (int u = 0; u < NSUB; ++u) {
+            uint32_t t[4];
+#pragma unroll
+            for (int d = 0; d < 4; ++d) t[d] = bit_select(dx2, (uint32_t)P.ch[u][c][d ^ 2], (uint32_t)P.ch[u][c][d]);
+            // perm(x, y, sel): selector bytes 0-3 pick bytes of y, 4-7 bytes of x
+#pragma unroll
+            for (int d = 0; d < 4; ++d) cu[u][d] = __builtin_amdgcn_perm(t[d ^ 1], t[d], psel) ^ 0x80808080u;
+        }
+        // code * sc as fma(code + 128, sc, -128 sc): the byte with its sign
+        // bit flipped converts to code + 128 in one instruction, and the
+        // fused result rounds the exact product once, as the product does.
+        // The sub-tiles' values of a slot are folded in pairs (three-operand
+        // max / min).
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            float v[NSUB];
+#pragma unroll
+            for (int u = 0; u < NSUB; ++u)
+                v[u] = __builtin_fmaf((float)(uint8_t)(cu[u][i >> 2] >> (8 * (i & 3))), P.sc[u], off[u]);
+#pragma unroll
+            for (int u = 0; u < NSUB; u += 2) {
+                if (u + 1 < NSUB) {
+                    mx[c][i] = fmaxf(fmaxf(mx[c][i], v[u]), v[u + 1]);
+                    mn[c][i] = fminf(fminf(mn[c][i], v[u]), v[u + 1]);
+                } else {
+                    mx[c][i] = fmaxf(mx[c][i], v[u]);
+                    mn[c][i] = fminf(mn[c][i], v[u]);
+                }
+            }
+        }
+    }
+}
+
+template <int HD>
+__device__ __forceinline__ void meta_reset(float (&mx)[Geo<HD>::NPAIR][16], float (&mn)[Geo<HD>::NPAIR][16]) {
+#pragma unroll
+    for (int c = 0; c < Geo<HD>::NPAIR; ++c) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             mx[c][i] = -INFINITY;
             mn[c][i] = INFINITY;
         }
     }
-    const size_t page_row = ((size_t)p * a.n_kv + kh) * a.kv_bs;
-    for (int r0 = 0; r0 < rows; r0 += NSUB * kSub) {
-        i32x4 ch[NSUB][NPAIR];
-        float sc[NSUB];
-#pragma unroll
-        for (int u = 0; u < NSUB; ++u) {
-            const int rs = min(r0 + u * kSub, last_sub);  // a sub-tile past the rows repeats the last one
-            const int rn = min(n, rows - 1 - rs);
-            sc[u] = a.ks[page_row + rs + rn];
-            load_k_subtile<HD>(ch[u], a.kp, page_row + rs, 16 * r + rn);
-        }
-        float off[NSUB];
-#pragma unroll
-        for (int u = 0; u < NSUB; ++u) off[u] = -128.0f * sc[u];  // exact
-#pragma unroll
-        for (int c = 0; c < NPAIR; ++c) {
-            uint32_t cu[NSUB][4];
-#pragma unroll
-            for (int u = 0; u < NSUB; ++u) {
-                uint32_t t[4];
-#pragma unroll
-                for (int d = 0; d < 4; ++d) t[d] = bit_select(dx2, (uint32_t)ch[u][c][d ^ 2], (uint32_t)ch[u][c][d]);
-                // perm(x, y, sel): selector bytes 0-3 pick bytes of y, 4-7 bytes of x
-#pragma unroll
-                for (int d = 0; d < 4; ++d) cu[u][d] = __builtin_amdgcn_perm(t[d ^ 1], t[d], psel) ^ 0x80808080u;
-            }
-            // code * sc as fma(code + 128, sc, -128 sc): the byte with its
-            // sign bit flipped converts to code + 128 in one instruction, and
-            // the fused result rounds the exact product once, as the product
-            // does.  The sub-tiles' values of a slot are folded in pairs
-            // (three-operand max / min).
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                float v[NSUB];
-#pragma unroll
-                for (int u = 0; u < NSUB; ++u)
-                    v[u] = __builtin_fmaf((float)(uint8_t)(cu[u][i >> 2] >> (8 * (i & 3))), sc[u], off[u]);
-#pragma unroll
-                for (int u = 0; u < NSUB; u += 2) {
-                    if (u + 1 < NSUB) {
-                        mx[c][i] = fmaxf(fmaxf(mx[c][i], v[u]), v[u + 1]);
-                        mn[c][i] = fminf(fminf(mn[c][i], v[u]), v[u + 1]);
-                    } else {
-                        mx[c][i] = fmaxf(mx[c][i], v[u]);
-                        mn[c][i] = fminf(mn[c][i], v[u]);
-                    }
-                }
-            }
-        }
-    }
+}
+
+// The row reductions and the stores of physical block p's metadata.
+template <int HD>
+__device__ __forceinline__ void meta_store(const QuestArgs& a, int p, int kh, float (&mx)[Geo<HD>::NPAIR][16],
+                                           float (&mn)[Geo<HD>::NPAIR][16], int lane) {
+    const int n = lane & 15, r = lane >> 4;
     const size_t out = ((size_t)p * a.n_kv + kh) * HD;
 #pragma unroll
-    for (int c = 0; c < NPAIR; ++c) {
+    for (int c = 0; c < Geo<HD>::NPAIR; ++c) {
         const float vx = row16_reduce_xor<true>(mx[c]);
         const float vn = row16_reduce_xor<false>(mn[c]);
         a.kmax[out + 64 * c + 16 * r + n] = vx;
         a.kmin[out + 64 * c + 16 * r + n] = vn;
+    }
+}
+
+// One wave per (sequence, PPW consecutive logical blocks, kv head).  With
+// PPW = 2 (pages of at most 16 NSUB rows) both pages' loads go out before
+// either is folded, so a wave has twice the bytes in flight and the launch,
+// index arithmetic and table round trip are shared by two pages.
+template <int HD, int NSUB, int PPW>
+__global__ __launch_bounds__(256) void q8kv_quest_metadata_kernel(const QuestArgs a) {
+    static_assert(PPW == 1 || PPW == 2, "pages per wave");
+    constexpr int NPAIR = Geo<HD>::NPAIR;
+    const int lane = threadIdx.x & (kWave - 1);
+    const long long wave = (long long)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int ngroups = (a.max_blocks + PPW - 1) / PPW;
+    if (wave >= (long long)a.batch * ngroups * a.n_kv) return;
+    const int kh = (int)(wave % a.n_kv);
+    const int j0 = (int)((wave / a.n_kv) % ngroups) * PPW;
+    const int b = (int)(wave / ((long long)a.n_kv * ngroups));
+    // the length and the table entries are read together (an entry is read
+    // only below max_blocks, so inside the table whether or not in use)
+    const int len = uniform_read(a.lens, b);
+    int pg[PPW];
+#pragma unroll
+    for (int k = 0; k < PPW; ++k)
+        pg[k] = j0 + k < a.max_blocks ? uniform_read(a.table + (size_t)b * a.max_blocks, j0 + k) : -1;
+    const int L = min(len, a.max_blocks * a.kv_bs);
+    bool ok[PPW];
+    int rows[PPW];
+#pragma unroll
+    for (int k = 0; k < PPW; ++k) {
+        ok[k] = (j0 + k) * a.kv_bs < L && (unsigned)pg[k] < (unsigned)a.num_blocks;
+        rows[k] = min(a.kv_bs, L - (j0 + k) * a.kv_bs);
+    }
+    const int n = lane & 15;
+    const uint32_t psel = (0x03020100u ^ ((uint32_t)(n & 3) * 0x01010101u)) + ((n & 4) ? 0x04040404u : 0u);
+    const uint32_t dx2 = (n & 8) ? 0xffffffffu : 0u;  // all ones where bit 3 of n is set
+    float mx[NPAIR][16], mn[NPAIR][16];
+    if constexpr (PPW == 1) {
+        if (!ok[0]) return;
+        meta_reset<HD>(mx, mn);
+        const size_t page_row = ((size_t)pg[0] * a.n_kv + kh) * a.kv_bs;
+        for (int r0 = 0; r0 < rows[0]; r0 += NSUB * kSub) {
+            MetaPage<HD, NSUB> P;
+            meta_load<HD, NSUB>(P, a, page_row, rows[0], r0, lane);
+            meta_fold<HD, NSUB>(P, mx, mn, psel, dx2);
+        }
+        meta_store<HD>(a, pg[0], kh, mx, mn, lane);
+    } else {
+        if (!ok[0] && !ok[1]) return;
+        // a page not in use loads the other one again, so that both loads
+        // always go out and the first fold waits for its own page only
+        // (opaque, so that the compiler does not turn the two cases into
+        // branches with the loads inside)
+        int p0 = ok[0] ? pg[0] : pg[1], n0 = ok[0] ? rows[0] : rows[1];
+        int p1 = ok[1] ? pg[1] : pg[0], n1 = ok[1] ? rows[1] : rows[0];
+        asm volatile("" : "+s"(p0), "+s"(n0), "+s"(p1), "+s"(n1));
+        MetaPage<HD, NSUB> P0, P1;
+        meta_load<HD, NSUB>(P0, a, ((size_t)p0 * a.n_kv + kh) * a.kv_bs, n0, 0, lane);
+        meta_load<HD, NSUB>(P1, a, ((size_t)p1 * a.n_kv + kh) * a.kv_bs, n1, 0, lane);
+        __builtin_amdgcn_sched_barrier(0);  // (both pages' loads out before the first fold)
+        // Both pages are folded and stored unconditionally (a page not in
+        // use stands for the other one, whose metadata is then written twice
+        // with the same values): work under a branch would let the compiler
+        // sink that page's loads into it, behind the other page's.
+        meta_reset<HD>(mx, mn);
+        meta_fold<HD, NSUB>(P0, mx, mn, psel, dx2);
+        meta_store<HD>(a, p0, kh, mx, mn, lane);
+        meta_reset<HD>(mx, mn);
+        meta_fold<HD, NSUB>(P1, mx, mn, psel, dx2);
+        meta_store<HD>(a, p1, kh, mx, mn, lane);
     }
 }
 
@@ -3573,12 +3650,22 @@ hipError_t launch_zero(void* p, size_t n_words, hipStream_t st) {
     return hipGetLastError();
 }
 
-// Sub-tiles a metadata wave keeps in flight: a whole page of up to 64 rows.
+template <int HD, int NSUB, int PPW>
+void launch_meta(hipStream_t st, const QuestArgs& qa) {
+    const long long waves = (long long)qa.batch * ((qa.max_blocks + PPW - 1) / PPW) * qa.n_kv;
+    hipLaunchKernelGGL((q8kv_quest_metadata_kernel<HD, NSUB, PPW>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st,
+                       qa);
+}
+
+// Sub-tiles a metadata wave keeps in flight: a whole page of up to 64 rows;
+// at hd 64 and 128 two such pages per wave.
 template <int HD>
-void launch_metadata(int kv_bs, unsigned grid, hipStream_t st, const QuestArgs& qa) {
-    if (kv_bs <= 16) hipLaunchKernelGGL((q8kv_quest_metadata_kernel<HD, 1>), dim3(grid), dim3(256), 0, st, qa);
-    else if (kv_bs == 32) hipLaunchKernelGGL((q8kv_quest_metadata_kernel<HD, 2>), dim3(grid), dim3(256), 0, st, qa);
-    else hipLaunchKernelGGL((q8kv_quest_metadata_kernel<HD, 4>), dim3(grid), dim3(256), 0, st, qa);
+void launch_metadata(int kv_bs, hipStream_t st, const QuestArgs& qa) {
+    constexpr int PPW = HD <= 128 ? 2 : 1;
+    if (kv_bs <= 16) launch_meta<HD, 1, PPW>(st, qa);
+    else if (kv_bs == 32) launch_meta<HD, 2, PPW>(st, qa);
+    else if (kv_bs == 64) launch_meta<HD, 4, PPW>(st, qa);
+    else launch_meta<HD, 4, 1>(st, qa);
 }
 
 int decode_impl(float* out, const float* q, const int8_t* kp, const int8_t* vp, const float* ks,
@@ -3989,6 +4076,7 @@ int q8kv_quest_metadata(float* kmax, float* kmin, const int8_t* k_pages, const f
     if (rc) return rc;
     if (max_blocks_per_seq <= 0 || (long long)max_blocks_per_seq * kv_bs > (INT_MAX / 2))
         return fail(Q8KV_EINVAL, "bad max_blocks_per_seq (%d)", max_blocks_per_seq);
+    // (the grid at one page per wave bounds every launch's)
     const long long waves = (long long)batch * max_blocks_per_seq * n_kv_heads;
     const long long grid = (waves + 3) / 4;
     if (grid > INT_MAX) return fail(Q8KV_EINVAL, "metadata shape too large");
@@ -3996,9 +4084,9 @@ int q8kv_quest_metadata(float* kmax, float* kmin, const int8_t* k_pages, const f
                  batch, max_blocks_per_seq, num_blocks, 0, n_kv_heads, kv_bs, 0};
     hipStream_t st = static_cast<hipStream_t>(stream);
     switch (hd) {
-        case 64: launch_metadata<64>(kv_bs, (unsigned)grid, st, qa); break;
-        case 128: launch_metadata<128>(kv_bs, (unsigned)grid, st, qa); break;
-        default: launch_metadata<256>(kv_bs, (unsigned)grid, st, qa); break;
+        case 64: launch_metadata<64>(kv_bs, st, qa); break;
+        case 128: launch_metadata<128>(kv_bs, st, qa); break;
+        default: launch_metadata<256>(kv_bs, st, qa); break;
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "metadata kernel launch");
