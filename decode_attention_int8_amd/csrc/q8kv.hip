@@ -2703,12 +2703,12 @@ __device__ __forceinline__ void meta_store(const QuestArgs& a, int p, int kh, fl
 }
 
 // One wave per (sequence, PPW consecutive logical blocks, kv head).  With
-// PPW = 2 (pages of at most 16 NSUB rows) both pages' loads go out before
-// either is folded, so a wave has twice the bytes in flight and the launch,
-// index arithmetic and table round trip are shared by two pages.
+// PPW > 1 (pages of at most 16 NSUB rows) every page's loads go out before
+// the first is folded, so a wave has PPW times the bytes in flight and the
+// launch, index arithmetic and table round trip are shared by PPW pages.
 template <int HD, int NSUB, int PPW>
 __global__ __launch_bounds__(256) void q8kv_quest_metadata_kernel(const QuestArgs a) {
-    static_assert(PPW == 1 || PPW == 2, "pages per wave");
+    static_assert(PPW == 1 || PPW == 2 || PPW == 4, "pages per wave");
     constexpr int NPAIR = Geo<HD>::NPAIR;
     const int lane = threadIdx.x & (kWave - 1);
     const long long wave = (long long)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -2747,28 +2747,33 @@ __global__ __launch_bounds__(256) void q8kv_quest_metadata_kernel(const QuestArg
         }
         meta_store<HD>(a, pg[0], kh, mx, mn, lane);
     } else {
-        if (!ok[0] && !ok[1]) return;
-        // a page not in use loads the other one again, so that both loads
-        // always go out and the first fold waits for its own page only
-        // (opaque, so that the compiler does not turn the two cases into
-        // branches with the loads inside)
-        int p0 = ok[0] ? pg[0] : pg[1], n0 = ok[0] ? rows[0] : rows[1];
-        int p1 = ok[1] ? pg[1] : pg[0], n1 = ok[1] ? rows[1] : rows[0];
-        asm volatile("" : "+s"(p0), "+s"(n0), "+s"(p1), "+s"(n1));
-        MetaPage<HD, NSUB> P0, P1;
-        meta_load<HD, NSUB>(P0, a, ((size_t)p0 * a.n_kv + kh) * a.kv_bs, n0, 0, lane);
-        meta_load<HD, NSUB>(P1, a, ((size_t)p1 * a.n_kv + kh) * a.kv_bs, n1, 0, lane);
-        __builtin_amdgcn_sched_barrier(0);  // (both pages' loads out before the first fold)
-        // Both pages are folded and stored unconditionally (a page not in
-        // use stands for the other one, whose metadata is then written twice
-        // with the same values): work under a branch would let the compiler
-        // sink that page's loads into it, behind the other page's.
-        meta_reset<HD>(mx, mn);
-        meta_fold<HD, NSUB>(P0, mx, mn, psel, dx2);
-        meta_store<HD>(a, p0, kh, mx, mn, lane);
-        meta_reset<HD>(mx, mn);
-        meta_fold<HD, NSUB>(P1, mx, mn, psel, dx2);
-        meta_store<HD>(a, p1, kh, mx, mn, lane);
+        // the first page in use; a page not in use loads that one again, so
+        // that every load always goes out and each fold waits for its own
+        // page only, and is folded and stored with it (the same values written
+        // twice): work under a branch would let the compiler sink that page's
+        // loads into it, behind the others'
+        int first = -1;
+#pragma unroll
+        for (int k = PPW - 1; k >= 0; --k) first = ok[k] ? k : first;
+        if (first < 0) return;
+        int sp[PPW], sn[PPW];
+#pragma unroll
+        for (int k = 0; k < PPW; ++k) {
+            sp[k] = ok[k] ? pg[k] : pg[first];
+            sn[k] = ok[k] ? rows[k] : rows[first];
+            asm volatile("" : "+s"(sp[k]), "+s"(sn[k]));  // (opaque: no branches around the loads)
+        }
+        MetaPage<HD, NSUB> P[PPW];
+#pragma unroll
+        for (int k = 0; k < PPW; ++k)
+            meta_load<HD, NSUB>(P[k], a, ((size_t)sp[k] * a.n_kv + kh) * a.kv_bs, sn[k], 0, lane);
+        __builtin_amdgcn_sched_barrier(0);  // (every page's loads out before the first fold)
+#pragma unroll
+        for (int k = 0; k < PPW; ++k) {
+            meta_reset<HD>(mx, mn);
+            meta_fold<HD, NSUB>(P[k], mx, mn, psel, dx2);
+            meta_store<HD>(a, sp[k], kh, mx, mn, lane);
+        }
     }
 }
 
@@ -3658,7 +3663,9 @@ void launch_meta(hipStream_t st, const QuestArgs& qa) {
 }
 
 // Sub-tiles a metadata wave keeps in flight: a whole page of up to 64 rows;
-// at hd 64 and 128 two such pages per wave.
+// at hd 64 and 128 two such pages per wave (against one: ragged 256 -> 223
+// us, GQA batch 62 -> 44 us; four were slower again, ragged 221 -> 242 us,
+// GQA batch 42 -> 44 us, with fewer waves per SIMD).
 template <int HD>
 void launch_metadata(int kv_bs, hipStream_t st, const QuestArgs& qa) {
     constexpr int PPW = HD <= 128 ? 2 : 1;
