@@ -7,8 +7,9 @@
   code multiples, bf16 sources.
 * Decode: against the oracle's fp64 definition within 2e-4 max-abs on every
   hd, group sizes 1-8, kv_bs 16-256, split plans on both merge paths, the
-  persistent grid (bitwise repeatable), empty sequences and an out-of-pool
-  table entry (NaN row for that sequence only).
+  persistent grid (bitwise repeatable), static grids whose waves walk 0-10
+  tiles (every tail of the two-tile pipeline), empty sequences and an
+  out-of-pool table entry (NaN row for that sequence only).
 """
 import numpy as np
 import pytest
@@ -165,6 +166,21 @@ def test_q40_decode_small_workload_shapes():
         dev, host = dev_cache(c), host_cache(c)
         run_decode(c, dev, host)
         run_decode(c, dev, host, part_tokens=64)
+
+
+@pytest.mark.parametrize("hd,kv_bs", [(128, 64), (128, 16), (64, 32)])
+def test_q40_decode_static_tile_counts(hd, kv_bs):
+    """One partition per sequence on a static grid, so that the waves walk 0 to
+    10 tiles each: the two-tile pipeline's steady loop and every tail after it
+    (one, two or three tiles), and waves with no tile."""
+    lens = [1, 33, 100, 129, 300, 555, 700, 1000, 1153, 0, 1280]
+    w = workloads.Workload("q40tiles", len(lens), 8, 2, hd, kv_bs, max(lens), ragged=True, table="pool",
+                           key=4500 + hd + kv_bs)
+    c = build(w, lens=lens, with_cache=False)
+    say(f"q40 static tile counts hd={hd} kv_bs={kv_bs}")
+    dev, host = dev_cache(c), host_cache(c)
+    got = run_decode(c, dev, host, part_tokens=2048)
+    assert not got[9].any()
 
 
 def test_q40_decode_bad_table_entry():
