@@ -21,6 +21,9 @@ FLAGS = [
     # cross-lane reduction only adds a wait for each atomic's result before
     # the next one can go out
     "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
+    # leading scalar kernel arguments arrive preloaded in SGPRs (the decode
+    # kernel's first dependent loads then need no argument-block round trip)
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-I", os.path.join(ROOT, "include"),
 ]
 

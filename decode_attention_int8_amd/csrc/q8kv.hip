@@ -441,9 +441,21 @@ struct DecodeArgs {
 // through the scalar cache; the empty asm keeps them where they are used.
 // The segment's address is defined only in the kernel itself: every caller
 // must be inlined into it.
+// The decode kernel's argument block follows the scalar arguments it takes
+// ahead of it (laid out in the segment in parameter order, each at its own
+// alignment, as in this struct), at the block's alignment.
+struct LeadArgs {
+    const int32_t* table;
+    const int32_t* lens;
+    int batch, max_blocks, kv_bs, part_tokens, n_parts, hgs, n_hk, table_rows;
+};
+constexpr size_t kArgsOffset = (sizeof(LeadArgs) + alignof(DecodeArgs) - 1) / alignof(DecodeArgs) * alignof(DecodeArgs);
+static_assert(kArgsOffset == 48, "argument block offset");
 typedef const __attribute__((address_space(4))) DecodeArgs ConstArgs;
 __device__ __forceinline__ ConstArgs* kernel_args() {
-    ConstArgs* ka = (ConstArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+    const __attribute__((address_space(4))) char* seg =
+        (const __attribute__((address_space(4))) char*)__builtin_amdgcn_kernarg_segment_ptr();
+    ConstArgs* ka = (ConstArgs*)(seg + kArgsOffset);
     asm volatile("" : "+s"(ka));
     return ka;
 }
@@ -1738,8 +1750,9 @@ constexpr bool kQ4DeepPersistent = false;
 constexpr bool kQ4DeepStatic = true;
 constexpr bool kI8DeepStatic = false;
 constexpr bool decode_deep(int hd, int mode, int codec, bool stg, int nw, bool knew) {
-    return !stg && hd <= 128 && nw == 4 && mode == kStatic &&
-           ((codec == kQ40 && kQ4DeepStatic) || (codec == kQ8 && !knew && kI8DeepStatic));
+    return !stg && hd <= 128 && nw == 4 &&
+           ((codec == kQ40 && (mode == kStatic ? kQ4DeepStatic : kQ4DeepPersistent)) ||
+            (codec == kQ8 && !knew && mode == kStatic && kI8DeepStatic));
 }
 constexpr int decode_waves_per_eu(int hd, int mode, int codec, bool stg, int nw, bool knew) {
     return hd == 256 ? 1
@@ -1751,7 +1764,26 @@ constexpr int decode_waves_per_eu(int hd, int mode, int codec, bool stg, int nw,
 
 template <int HD, int MODE, bool NEW, int CODEC = kQ8, int NW = kWaves, bool STG = false>
 __global__ __launch_bounds__(kWave * NW) __attribute__((amdgpu_waves_per_eu(decode_waves_per_eu(HD, MODE, CODEC, STG, NW, NEW)))) void
-q8kv_decode_kernel(const DecodeArgs a) {
+q8kv_decode_kernel(const int32_t* hot_table, const int32_t* hot_lens, int hot_batch, int hot_max_blocks,
+                   int hot_kv_bs, int hot_part_tokens, int hot_n_parts, int hot_hgs, int hot_n_hk, int hot_table_rows,
+                   const DecodeArgs args) {
+    // (these leading parameters are LeadArgs, field for field: kernel_args()
+    // finds the argument block behind them)
+    // The fields that the first dependent loads (lengths, block table) need
+    // also come as leading scalar arguments, which are preloaded into SGPRs:
+    // those loads then go out without waiting for the argument block, whose
+    // other fields are read from memory meanwhile.
+    DecodeArgs a = args;
+    a.table = hot_table;
+    a.lens = hot_lens;
+    a.batch = hot_batch;
+    a.max_blocks = hot_max_blocks;
+    a.kv_bs = hot_kv_bs;
+    a.part_tokens = hot_part_tokens;
+    a.n_parts = hot_n_parts;
+    a.hgs = hot_hgs;
+    a.n_hk = hot_n_hk;
+    a.table_rows = hot_table_rows;
     using GG = Geo<HD>;
     constexpr int NT = kWave * NW;  // threads per workgroup
     constexpr bool STATIC = MODE == kStatic;
@@ -1934,11 +1966,19 @@ q8kv_decode_kernel(const DecodeArgs a) {
             }
         }
         const int kh = a.hgs == 1 ? ih : ih / a.hgs;
-        // the query rows' loads go out first: the quantisation then waits for
-        // them alone, not for the first tile queued behind them
+        // The query rows' loads go out before the tile loads: the quantisation
+        // then waits for them alone, not for the first tile queued behind
+        // them.  Persistent grids issue them before the item's table reads
+        // (the argument block was read once, at the start); static grids
+        // after, so that the table reads, whose operands arrive preloaded,
+        // overlap the argument-block read the query address needs.
         QRows<HD, NT> qrows;
-        if constexpr (STAGE) dma_q_rows<HD, NT>(lqraw, a.q + ((size_t)b * a.n_q + (size_t)ih * G) * a.hdr, G, a.hdr, itid, wid);
-        else load_q_rows<HD, NT>(qrows, a.q + ((size_t)b * a.n_q + (size_t)ih * G) * a.hdr, G, a.hdr, itid);
+        auto issue_q_rows = [&]() {
+            const float* qsrc = a.q + ((size_t)b * a.n_q + (size_t)ih * G) * a.hdr;
+            if constexpr (STAGE) dma_q_rows<HD, NT>(lqraw, qsrc, G, a.hdr, itid, wid);
+            else load_q_rows<HD, NT>(qrows, qsrc, G, a.hdr, itid);
+        };
+        if constexpr (!STATIC) issue_q_rows();
         const int32_t* trow = a.table + ((size_t)b * a.table_rows + (a.table_rows > 1 ? kh : 0)) * a.max_blocks;
         const int t0 = part * a.part_tokens;
         // The first tile's table reads, those of the item's first tile (a
@@ -1951,6 +1991,7 @@ q8kv_decode_kernel(const DecodeArgs a) {
         tile_blocks(trow, t0, a.kv_bs, a.max_blocks, blk_t0);
         int L = uniform_read(a.lens, b);
         asm volatile("" : "+s"(blk_first[0]), "+s"(blk_first[1]), "+s"(blk_t0[0]), "+s"(blk_t0[1]), "+s"(L));
+        if constexpr (STATIC) issue_q_rows();
         bool bad = false;
         if (L > cap) {
             L = cap;
@@ -3542,6 +3583,14 @@ constexpr auto decode_kernel_ptr() {
     return q8kv_decode_kernel<HD, MODE, VAR == kVarQ8New, VAR == kVarFp8 ? kFp8 : VAR == kVarQ40 ? kQ40 : kQ8, NW, STG>;
 }
 
+// A decode kernel launch: the argument block, after the fields the kernel
+// takes again as leading scalar arguments (preloaded into SGPRs).
+template <typename Kernel>
+void launch_decode(Kernel kernel, dim3 grid, dim3 block, size_t lds, hipStream_t st, const DecodeArgs& da) {
+    hipLaunchKernelGGL(kernel, grid, block, lds, st, da.table, da.lens, da.batch, da.max_blocks, da.kv_bs,
+                       da.part_tokens, da.n_parts, da.hgs, da.n_hk, da.table_rows, da);
+}
+
 // Wide (kWideWaves) workgroups serve static grids of at most one workgroup
 // per CU at hd 64 and 128: with 4 waves such a grid leaves one wave per SIMD,
 // too few loads in flight to cover the memory latency.  (At hd 256 the wave
@@ -3607,30 +3656,30 @@ template <int HD, int VAR>
 void launch_decode_hd(int mode, bool wide, bool stage, unsigned grid, size_t lds, hipStream_t st,
                       const DecodeArgs& da) {
     if (mode == kPersistent) {
-        hipLaunchKernelGGL((decode_kernel_ptr<HD, VAR, kPersistent>()), dim3(grid), dim3(kThreads), 0, st, da);
+        launch_decode(decode_kernel_ptr<HD, VAR, kPersistent>(), dim3(grid), dim3(kThreads), 0, st, da);
         return;
     }
     if constexpr ((VAR == kVarQ8 || VAR == kVarQ8New) && HD <= 128) {
         // the staged kernels' LDS already keeps them at two (wide: one) per CU
         if (stage && wide) {
-            hipLaunchKernelGGL((decode_kernel_ptr<HD, VAR, kStatic, kWideWaves, true>()), dim3(grid),
-                               dim3(kWave * kWideWaves), 0, st, da);
+            launch_decode(decode_kernel_ptr<HD, VAR, kStatic, kWideWaves, true>(), dim3(grid),
+                          dim3(kWave * kWideWaves), 0, st, da);
             return;
         }
         if (stage) {
-            hipLaunchKernelGGL((decode_kernel_ptr<HD, VAR, kStatic, kWaves, true>()), dim3(grid), dim3(kThreads), 0,
-                               st, da);
+            launch_decode(decode_kernel_ptr<HD, VAR, kStatic, kWaves, true>(), dim3(grid), dim3(kThreads), 0,
+                          st, da);
             return;
         }
     }
     if constexpr (wide_hd(HD)) {
         if (wide) {
-            hipLaunchKernelGGL((decode_kernel_ptr<HD, VAR, kStatic, kWideWaves>()), dim3(grid), dim3(kWave * kWideWaves),
-                               lds, st, da);
+            launch_decode(decode_kernel_ptr<HD, VAR, kStatic, kWideWaves>(), dim3(grid), dim3(kWave * kWideWaves),
+                          lds, st, da);
             return;
         }
     }
-    hipLaunchKernelGGL((decode_kernel_ptr<HD, VAR, kStatic>()), dim3(grid), dim3(kThreads), lds, st, da);
+    launch_decode(decode_kernel_ptr<HD, VAR, kStatic>(), dim3(grid), dim3(kThreads), lds, st, da);
 }
 
 template <int VAR>

@@ -54,6 +54,14 @@ def device_asm():
     return funcs
 
 
+def kernel_body(device_asm, prefix):
+    """The body of the one kernel whose mangled name starts with prefix (the
+    template arguments; the parameter list follows)."""
+    names = [n for n in device_asm if n.startswith(prefix)]
+    assert len(names) == 1, (prefix, names)
+    return names[0], device_asm[names[0]]
+
+
 def test_no_device_function_calls(device_asm):
     kernels = [n for n in device_asm if "q8kv_decode_kernel" in n]
     assert len(kernels) >= 30
@@ -70,8 +78,8 @@ def tile_loop_blocks(body):
 
 @pytest.mark.parametrize("mode", ["1", "0"])
 def test_int8_tile_loop_has_no_scalar_reloads(device_asm, mode):
-    name = f"_ZN12_GLOBAL__N_118q8kv_decode_kernelILi128ELi{mode}ELb0ELi0ELi4ELb0EEEvNS_10DecodeArgsE"
-    blocks = tile_loop_blocks(device_asm[name])
+    name, body = kernel_body(device_asm, f"_ZN12_GLOBAL__N_118q8kv_decode_kernelILi128ELi{mode}ELb0ELi0ELi4ELb0EEEv")
+    blocks = tile_loop_blocks(body)
     assert blocks
     for lab, txt in blocks:
         assert "v_readlane_b32" not in txt, f"{name}: scalar spill reload in {lab}"
@@ -105,8 +113,8 @@ def test_multi_read_asm_blocks_keep_their_addresses(device_asm):
 def test_staged_tile_loop_waits_are_its_own(device_asm, hd, nw):
     """Up to the last matrix-core instruction (the end of the tile loop),
     every wait for all loads in flight is one of the kernel's own asm waits."""
-    name = f"_ZN12_GLOBAL__N_118q8kv_decode_kernelILi{hd}ELi1ELb0ELi0ELi{nw}ELb1EEEvNS_10DecodeArgsE"
-    lines = device_asm[name].split("\n")
+    name, body = kernel_body(device_asm, f"_ZN12_GLOBAL__N_118q8kv_decode_kernelILi{hd}ELi1ELb0ELi0ELi{nw}ELb1EEEv")
+    lines = body.split("\n")
     assert any("global_load_lds_dwordx4" in l for l in lines)
     last_mfma = max(i for i, l in enumerate(lines) if "v_mfma" in l)
     for i in range(last_mfma):
@@ -133,8 +141,8 @@ def test_rolled_tile_loop_keeps_the_next_k_half_in_flight(device_asm, new, codec
     they do not wait for: between the last load before them and the P.V
     instruction every wait leaves at least the next tile's four K chunks in
     flight."""
-    name = f"_ZN12_GLOBAL__N_118q8kv_decode_kernelILi128ELi0ELb{new}ELi{codec}ELi4ELb0EEEvNS_10DecodeArgsE"
-    lines = device_asm[name].split("\n")
+    name, body = kernel_body(device_asm, f"_ZN12_GLOBAL__N_118q8kv_decode_kernelILi128ELi0ELb{new}ELi{codec}ELi4ELb0EEEv")
+    lines = body.split("\n")
     found = False
     since_load, low = None, None
     for l in lines:
