@@ -17,6 +17,8 @@ source, built here with the library's flags).
 * The staged tile loops hold no compiler-inserted wait for every load in
   flight (vmcnt(0)) ahead of their LDS reads other than the kernel's own
   waits in asm.
+* Every decode kernel's argument block sits where kernel_args() reads it,
+  behind the leading scalar arguments (the kernel metadata's offsets).
 * No int8 or FP8 decode kernel at hd 64 or 128 spills to scratch memory, and the
   persistent int8 and FP8 kernels' rolled tile loop issues a tile's P.V
   behind the next tile's K loads without waiting for them.
@@ -51,6 +53,8 @@ def device_asm():
     funcs = {}
     for m in re.finditer(r"^(_Z\S+):\s*;.*?$(.*?)^\.Lfunc_end", text, re.M | re.S):
         funcs[m.group(1)] = m.group(2)
+    # the kernel metadata (argument offsets and sizes), under a key no kernel has
+    funcs["__metadata__"] = text[text.find("amdhsa.kernels:"):]
     return funcs
 
 
@@ -60,6 +64,23 @@ def kernel_body(device_asm, prefix):
     names = [n for n in device_asm if n.startswith(prefix)]
     assert len(names) == 1, (prefix, names)
     return names[0], device_asm[names[0]]
+
+
+def test_decode_argument_block_behind_the_leading_arguments(device_asm):
+    """kernel_args() reads a decode kernel's argument block kArgsOffset bytes
+    into the argument segment, behind the leading scalar arguments: every
+    decode kernel's metadata must place its by-value argument block there."""
+    off = int(re.search(r"static_assert\(kArgsOffset == (\d+)", open(SRC).read()).group(1))
+    n = 0
+    for entry in re.split(r"\n  - \.agpr_count:", device_asm["__metadata__"]):
+        m = re.search(r"\.name:\s+(\S*q8kv_decode_kernel\S*)", entry)
+        if not m:
+            continue
+        args = re.findall(r"\.offset:\s+(\d+)\s+\.size:\s+(\d+)\s+\.value_kind:\s+by_value", entry)
+        blocks = [(int(o), int(sz)) for o, sz in args if int(sz) > 8]
+        assert len(blocks) == 1 and blocks[0][0] == off, (m.group(1), blocks, off)
+        n += 1
+    assert n >= 30
 
 
 def test_no_device_function_calls(device_asm):
